@@ -1,0 +1,194 @@
+"""CPU float64 oracle for streaming log-domain Sinkhorn (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg; the product package never imports it. The
+arithmetic lives in ``sk_oracle.c`` (plain float64 loops, OpenMP over rows);
+this file only marshals numpy arrays and builds the shared object.
+
+Every function takes the stored point values exactly (float32, or bf16 decoded
+exactly) promoted to float64, and weights as stored (float32) promoted to
+float64. Conventions (see sk_oracle.c for the formulas and their sources):
+  F(g)_i = -eps * LSE_j(log b_j + (g_j - C_ij)/eps), G symmetric,
+  P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps), C_ij = |x_i - y_j|^2.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sk_oracle.c")
+_LIB = os.path.join(_HERE, "libskoracle.so")
+
+ALTERNATING, SYMMETRIC = 0, 1
+_MODES = {"alternating": ALTERNATING, "symmetric": SYMMETRIC}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile sk_oracle.c with gcc (IEEE float64: no fast-math) into libskoracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    D = ctypes.c_double
+    INT = ctypes.c_int
+    sig = {
+        "sko_F": [P, P, I64, I64, I64, P, P, D, P],
+        "sko_G": [P, P, I64, I64, I64, P, P, D, P],
+        "sko_solve": [P, P, I64, I64, I64, P, P, D, INT, INT, P, P, P],
+        "sko_grad_x": [P, P, I64, I64, I64, P, P, P, D, P],
+        "sko_grad_x_plan": [P, P, I64, I64, I64, P, P, P, P, D, P],
+        "sko_apply": [P, P, I64, I64, I64, P, P, P, P, D, INT, P, I64, P],
+        "sko_marginals": [P, P, I64, I64, I64, P, P, P, P, D, P, P],
+        "sko_objectives": [P, P, I64, I64, I64, P, P, P, P, D, P, P],
+        "sko_set_threads": [INT],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = None
+    lib.sko_threads.restype = INT
+    lib.sko_version.restype = INT
+    _lib = lib
+    return lib
+
+
+def _c(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _shapes(x, y):
+    x = _c(x)
+    y = _c(y)
+    if x.ndim == 1:
+        x = x[:, None]
+    if y.ndim == 1:
+        y = y[:, None]
+    assert x.shape[1] == y.shape[1], "x and y must have the same dimension"
+    return x, y, x.shape[0], y.shape[0], x.shape[1]
+
+
+def set_threads(t: int) -> None:
+    _load().sko_set_threads(int(t))
+
+
+def threads() -> int:
+    return int(_load().sko_threads())
+
+
+def F(x, y, b, g, eps):
+    """F(g)_i = -eps * LSE_j(log b_j + (g_j - C_ij)/eps)."""
+    x, y, n, m, d = _shapes(x, y)
+    b, g = _c(b), _c(g)
+    out = np.empty(n)
+    _load().sko_F(_p(x), _p(y), n, m, d, _p(b), _p(g), float(eps), _p(out))
+    return out
+
+
+def G(x, y, a, f, eps):
+    """G(f)_j = -eps * LSE_i(log a_i + (f_i - C_ij)/eps)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, f = _c(a), _c(f)
+    out = np.empty(m)
+    _load().sko_G(_p(x), _p(y), n, m, d, _p(a), _p(f), float(eps), _p(out))
+    return out
+
+
+def solve(x, y, a, b, eps, iters, mode="alternating", f0=None, g0=None):
+    """Fixed-budget Sinkhorn from (f0, g0) (zeros by default). Returns (f, g, cost)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b = _c(a), _c(b)
+    f = np.zeros(n) if f0 is None else _c(f0).copy()
+    g = np.zeros(m) if g0 is None else _c(g0).copy()
+    cost = ctypes.c_double(0.0)
+    _load().sko_solve(_p(x), _p(y), n, m, d, _p(a), _p(b), float(eps), int(iters),
+                      _MODES[mode] if isinstance(mode, str) else int(mode),
+                      _p(f), _p(g), ctypes.byref(cost))
+    return f, g, cost.value
+
+
+def grad_x(x, y, a, b, g, eps):
+    """grad_i = 2 a_i (x_i - sum_j softmax_j(log b_j + (g_j - C_ij)/eps) y_j)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b, g = _c(a), _c(b), _c(g)
+    out = np.empty((n, d))
+    _load().sko_grad_x(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(g), float(eps), _p(out))
+    return out
+
+
+def grad_x_plan(x, y, a, b, f, g, eps):
+    """Diagnostic: 2 (r_i x_i - (P Y)_i) with P at (f, g)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b, f, g = _c(a), _c(b), _c(f), _c(g)
+    out = np.empty((n, d))
+    _load().sko_grad_x_plan(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps), _p(out))
+    return out
+
+
+def apply(x, y, a, b, f, g, eps, V, transpose=False):
+    """P V (V: m x k) or, with transpose, P^T V (V: n x k)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b, f, g = _c(a), _c(b), _c(f), _c(g)
+    V = _c(V)
+    squeeze = V.ndim == 1
+    if squeeze:
+        V = V[:, None]
+    k = V.shape[1]
+    rows = m if transpose else n
+    assert V.shape[0] == (n if transpose else m)
+    out = np.empty((rows, k))
+    _load().sko_apply(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps),
+                      int(bool(transpose)), _p(V), k, _p(out))
+    return out[:, 0] if squeeze else out
+
+
+def marginals(x, y, a, b, f, g, eps):
+    """(P 1, P^T 1)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b, f, g = _c(a), _c(b), _c(f), _c(g)
+    r = np.empty(n)
+    c = np.empty(m)
+    _load().sko_marginals(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps), _p(r), _p(c))
+    return r, c
+
+
+def objectives(x, y, a, b, f, g, eps):
+    """(primal, dual) objective values at (f, g)."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b, f, g = _c(a), _c(b), _c(f), _c(g)
+    pr = ctypes.c_double()
+    du = ctypes.c_double()
+    _load().sko_objectives(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps),
+                           ctypes.byref(pr), ctypes.byref(du))
+    return pr.value, du.value
+
+
+def time_row_map(x, y, w, pot, eps, repeats: int = 1) -> float:
+    """Wall seconds of one F-map evaluation (for the CPU-baseline timing)."""
+    t0 = time.perf_counter()
+    for _ in range(repeats):
+        F(x, y, w, pot, eps)
+    return (time.perf_counter() - t0) / repeats

@@ -1,0 +1,323 @@
+"""Pins of the CPU float64 oracle against facts it does not compute itself.
+
+Each test ties an oracle routine to an independent fact fixed by the pages or by
+the mathematics of entropic optimal transport:
+  * the primal matrix-scaling form of Sinkhorn (u = a / (K v), v = b / (K^T u)),
+    derived in "Fused & Furious: Sinkhorn Triton Kernels", section II.B, with
+    unit marginals there and general ones here;
+  * marginal constraints and primal/dual agreement at convergence;
+  * translation invariance and the swap symmetry of the averaged schedule;
+  * closed forms (one point per side; two points per side with uniform weights);
+  * the eps -> 0 limit against brute force over permutations, the extreme points
+    of the Birkhoff polytope (same page, section II);
+  * the eps-monotonicity and the product-coupling upper bound of OT_eps;
+  * finite differences of the gradient, including the envelope (Danskin) argument
+    named in the FlashSinkhorn replication review's Weaknesses paragraph;
+  * the plan-rescaling identity of the block-wise Sinkhorn attention explainer,
+    section 2.2 (plans at different potentials differ by diagonal scalings).
+None of these tests uses a GPU.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+from scipy.optimize import linprog
+
+import oracle
+
+
+def _cloud(seed, n, d, lo=0.0, hi=1.0):
+    return np.random.default_rng([seed, 7]).uniform(lo, hi, size=(n, d))
+
+
+def _weights(seed, n):
+    w = np.random.default_rng([seed, 8]).exponential(1.0, size=n)
+    return w / w.sum()
+
+
+def _pairwise_by_expansion(x, y):
+    """|x|^2 + |y|^2 - 2 x.y: a different evaluation from the oracle's differences."""
+    return (x * x).sum(1)[:, None] + (y * y).sum(1)[None, :] - 2.0 * x @ y.T
+
+
+def _scaling_iterates(K, a, b, iters, mode):
+    """Primal matrix-scaling Sinkhorn from f = g = 0, i.e. u = a, v = b."""
+    u, v = a.copy(), b.copy()
+    for _ in range(iters):
+        if mode == "alternating":
+            u = a / (K @ v)
+            v = b / (K.T @ u)
+        else:  # averaged potentials <=> geometric mean of the scalings
+            u, v = np.sqrt(u * a / (K @ v)), np.sqrt(v * b / (K.T @ u))
+    return u, v
+
+
+def _converge(x, y, a, b, eps, tol=1e-12, max_iters=200000):
+    """Alternating oracle iterations until both marginals hold to tol."""
+    f = np.zeros(len(a))
+    g = np.zeros(len(b))
+    done = 0
+    step = 200
+    while done < max_iters:
+        f, g, cost = oracle.solve(x, y, a, b, eps, step, "alternating", f, g)
+        done += step
+        r, c = oracle.marginals(x, y, a, b, f, g, eps)
+        if max(np.abs(r - a).max(), np.abs(c - b).max()) < tol:
+            return f, g, cost
+    raise AssertionError("no convergence")
+
+
+# ---------------------------------------------------------------- P1 scaling form
+@pytest.mark.parametrize("mode", ["alternating", "symmetric"])
+def test_log_domain_matches_primal_scaling(mode):
+    x, y = _cloud(1, 7, 3), _cloud(2, 5, 3)
+    a, b = _weights(3, 7), _weights(4, 5) * 1.3  # unequal masses are allowed
+    eps = 0.15
+    K = np.exp(-_pairwise_by_expansion(x, y) / eps)
+    for iters in (1, 2, 5, 17):
+        u, v = _scaling_iterates(K, a, b, iters, mode)
+        f, g, _ = oracle.solve(x, y, a, b, eps, iters, mode)
+        np.testing.assert_allclose(f, eps * np.log(u / a), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(g, eps * np.log(v / b), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P2 marginals
+def test_half_step_marginals_are_exact():
+    x, y = _cloud(5, 9, 2), _cloud(6, 11, 2)
+    a, b = _weights(7, 9), _weights(8, 11)
+    eps = 0.2
+    f, g, _ = oracle.solve(x, y, a, b, eps, 3, "alternating")
+    r, c = oracle.marginals(x, y, a, b, f, g, eps)
+    np.testing.assert_allclose(c, b, rtol=1e-13)          # g = G(f) makes P^T 1 = b
+    f2 = oracle.F(x, y, b, g, eps)
+    r2, _ = oracle.marginals(x, y, a, b, f2, g, eps)
+    np.testing.assert_allclose(r2, a, rtol=1e-13)         # f = F(g) makes P 1 = a
+
+
+def test_marginals_at_convergence_and_primal_equals_dual():
+    x, y = _cloud(9, 8, 3), _cloud(10, 6, 3)
+    a, b = _weights(11, 8), _weights(12, 6)
+    eps = 0.1
+    f, g, cost = _converge(x, y, a, b, eps, tol=1e-12)
+    r, c = oracle.marginals(x, y, a, b, f, g, eps)
+    assert np.abs(r - a).max() < 1e-10 and np.abs(c - b).max() < 1e-10
+    primal, dual = oracle.objectives(x, y, a, b, f, g, eps)
+    assert abs(primal - dual) <= 1e-10 * abs(primal)
+    assert abs(cost - dual) <= 1e-10 * abs(primal)
+
+
+def test_cost_equals_full_dual_after_each_alternating_iteration():
+    x, y = _cloud(13, 6, 2), _cloud(14, 7, 2)
+    a, b = _weights(15, 6), _weights(16, 7)
+    eps = 0.3
+    for iters in (1, 2, 4):
+        f, g, cost = oracle.solve(x, y, a, b, eps, iters)
+        _, dual = oracle.objectives(x, y, a, b, f, g, eps)
+        assert abs(cost - dual) < 1e-13 * max(1.0, abs(cost))
+
+
+# ---------------------------------------------------------------- P4 / P5 invariances
+def test_translation_invariance():
+    x, y = _cloud(17, 10, 3), _cloud(18, 12, 3)
+    a, b = _weights(19, 10), _weights(20, 12)
+    eps = 0.05
+    t = np.array([0.3, -1.7, 2.2])
+    f1, g1, c1 = oracle.solve(x, y, a, b, eps, 30)
+    f2, g2, c2 = oracle.solve(x + t, y + t, a, b, eps, 30)
+    np.testing.assert_allclose(f2, f1, atol=1e-11)
+    np.testing.assert_allclose(g2, g1, atol=1e-11)
+    assert abs(c2 - c1) < 1e-11
+    gr1 = oracle.grad_x(x, y, a, b, g1, eps)
+    gr2 = oracle.grad_x(x + t, y + t, a, b, g2, eps)
+    np.testing.assert_allclose(gr2, gr1, atol=1e-9)
+
+
+def test_symmetric_schedule_is_swap_symmetric():
+    x, y = _cloud(21, 9, 2), _cloud(22, 6, 2)
+    a, b = _weights(23, 9), _weights(24, 6)
+    eps = 0.1
+    f, g, c = oracle.solve(x, y, a, b, eps, 13, "symmetric")
+    f_s, g_s, c_s = oracle.solve(y, x, b, a, eps, 13, "symmetric")
+    assert np.array_equal(f_s, g) and np.array_equal(g_s, f)
+    assert abs(c_s - c) < 1e-14
+    # the alternating schedule is not symmetric: this guards the test itself
+    fa, ga, _ = oracle.solve(x, y, a, b, eps, 3, "alternating")
+    fb, gb, _ = oracle.solve(y, x, b, a, eps, 3, "alternating")
+    assert not np.allclose(fb, ga)
+
+
+# ---------------------------------------------------------------- P6 closed forms
+def test_single_point_each_side():
+    x = np.array([[0.0, 0.0]])
+    y = np.array([[3.0, 4.0]])          # C = 25
+    one = np.ones(1)
+    eps = 0.7
+    f, g, cost = oracle.solve(x, y, one, one, eps, 1, "alternating")
+    assert f[0] == pytest.approx(25.0, abs=1e-12) and g[0] == pytest.approx(0.0, abs=1e-12)
+    assert cost == pytest.approx(25.0, abs=1e-12)
+    f, g, cost = oracle.solve(x, y, one, one, eps, 1, "symmetric")
+    assert f[0] == pytest.approx(12.5, abs=1e-12) and g[0] == pytest.approx(12.5, abs=1e-12)
+    # unit weights other than 1: F(0) = C - eps log b
+    f, g, _ = oracle.solve(x, y, np.array([2.0]), np.array([0.5]), eps, 1, "alternating")
+    assert f[0] == pytest.approx(25.0 - eps * math.log(0.5), abs=1e-12)
+    # then G(f) = C - eps log a - f, so f + g = C - eps log a
+    assert f[0] + g[0] == pytest.approx(25.0 - eps * math.log(2.0), abs=1e-12)
+
+
+def test_two_by_two_closed_form_plan_and_cost():
+    # Uniform 2x2: the optimal plan is [[p, 1/2-p], [1/2-p, p]] with
+    # p / (1/2 - p) = exp(-(C11 + C22 - C12 - C21) / (2 eps)).
+    x = np.array([[0.0, 0.0], [1.0, 0.5]])
+    y = np.array([[0.2, 0.1], [0.7, 0.9]])
+    C = _pairwise_by_expansion(x, y)
+    a = b = np.array([0.5, 0.5])
+    for eps in (0.15, 0.3, 2.0):
+        kappa = math.exp(-(C[0, 0] + C[1, 1] - C[0, 1] - C[1, 0]) / (2 * eps))
+        p = kappa / (2 * (1 + kappa))
+        P = np.array([[p, 0.5 - p], [0.5 - p, p]])
+        ot = (P * C).sum() + eps * (P * np.log(P / 0.25)).sum()
+        f, g, cost = _converge(x, y, a, b, eps, tol=1e-14 if eps > 0.2 else 1e-13)
+        assert cost == pytest.approx(ot, rel=1e-11, abs=1e-13)
+        cols = oracle.apply(x, y, a, b, f, g, eps, np.eye(2))   # P @ I
+        np.testing.assert_allclose(cols, P, rtol=1e-10, atol=1e-14)
+
+
+# ---------------------------------------------------------------- P7 / P8 eps limits
+def _lp_ot(C, a, b):
+    n, m = C.shape
+    A_eq = np.zeros((n + m, n * m))
+    for i in range(n):
+        A_eq[i, i * m:(i + 1) * m] = 1.0
+    for j in range(m):
+        A_eq[n + j, j::m] = 1.0
+    res = linprog(C.ravel(), A_eq=A_eq, b_eq=np.concatenate([a, b]), bounds=(0, None), method="highs")
+    assert res.status == 0
+    return res.fun
+
+
+def test_eps_monotone_and_bounded_by_product_coupling():
+    x, y = _cloud(31, 6, 2), _cloud(32, 5, 2)
+    a, b = _weights(33, 6), _weights(34, 5)
+    C = _pairwise_by_expansion(x, y)
+    ot0 = _lp_ot(C, a, b)
+    # <a (x) b, C> = sum a|x|^2 + sum b|y|^2 - 2 <sum a x, sum b y> for unit masses
+    prod = a @ (x * x).sum(1) + b @ (y * y).sum(1) - 2.0 * (a @ x) @ (b @ y)
+    prev = -np.inf
+    for eps in (0.05, 0.1, 0.3, 1.0, 3.0):
+        _, _, c = _converge(x, y, a, b, eps, tol=1e-11)
+        assert ot0 - 1e-9 <= c <= prod + 1e-12
+        assert c >= prev - 1e-12
+        prev = c
+    _, _, c_big = _converge(x, y, a, b, 1e4, tol=1e-13)
+    assert c_big == pytest.approx(prod, rel=1e-4)
+
+
+@pytest.mark.parametrize("n", [4, 6])
+def test_small_eps_against_brute_force_permutations(n):
+    x, y = _cloud(40 + n, n, 2), _cloud(50 + n, n, 2)
+    a = b = np.full(n, 1.0 / n)
+    C = _pairwise_by_expansion(x, y)
+    ot0 = min(sum(C[i, s[i]] for i in range(n)) for s in itertools.permutations(range(n))) / n
+    for eps in (0.02, 0.05, 0.2):
+        _, _, c = _converge(x, y, a, b, eps, tol=1e-11)
+        # a permutation plan divided by n has KL(P | a (x) b) = log n
+        assert ot0 - 1e-9 <= c <= ot0 + eps * math.log(n) + 1e-9
+
+
+# ---------------------------------------------------------------- P9 gradient
+def test_gradient_matches_finite_differences_at_fixed_g():
+    x, y = _cloud(61, 5, 3), _cloud(62, 7, 3)
+    a, b = _weights(63, 5), _weights(64, 7)
+    eps = 0.2
+    _, g, _ = oracle.solve(x, y, a, b, eps, 4)           # any iterate will do
+    grad = oracle.grad_x(x, y, a, b, g, eps)
+
+    def obj(xx):
+        return a @ oracle.F(xx, y, b, g, eps) + b @ g
+
+    h = 1e-5
+    fd = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        for k in range(x.shape[1]):
+            xp, xm = x.copy(), x.copy()
+            xp[i, k] += h
+            xm[i, k] -= h
+            fd[i, k] = (obj(xp) - obj(xm)) / (2 * h)
+    np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-9)
+
+
+def test_gradient_envelope_at_convergence_and_plan_form():
+    x, y = _cloud(65, 4, 2), _cloud(66, 5, 2)
+    a, b = _weights(67, 4), _weights(68, 5)
+    eps = 0.25
+    f, g, _ = _converge(x, y, a, b, eps, tol=1e-13)
+    grad = oracle.grad_x(x, y, a, b, g, eps)
+    h = 1e-5
+    for i, k in [(0, 0), (2, 1), (3, 0)]:
+        xp, xm = x.copy(), x.copy()
+        xp[i, k] += h
+        xm[i, k] -= h
+        cp = _converge(xp, y, a, b, eps, tol=1e-13)[2]
+        cm = _converge(xm, y, a, b, eps, tol=1e-13)[2]
+        assert (cp - cm) / (2 * h) == pytest.approx(grad[i, k], rel=1e-5, abs=1e-8)
+    # with f = F(g) the plan form 2 (r_i x_i - (P y)_i) equals the normalized form
+    f_exact = oracle.F(x, y, b, g, eps)
+    np.testing.assert_allclose(oracle.grad_x_plan(x, y, a, b, f_exact, g, eps), grad, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- P10 apply
+def test_apply_identities():
+    x, y = _cloud(71, 9, 3), _cloud(72, 8, 3)
+    a, b = _weights(73, 9), _weights(74, 8)
+    eps = 0.15
+    rng = np.random.default_rng(75)
+    f, g = rng.standard_normal(9) * 0.1, rng.standard_normal(8) * 0.1
+    V, U = rng.standard_normal((8, 4)), rng.standard_normal((9, 4))
+    PV = oracle.apply(x, y, a, b, f, g, eps, V)
+    PtU = oracle.apply(x, y, a, b, f, g, eps, U, transpose=True)
+    # adjointness <U, P V> = <P^T U, V>
+    assert (U * PV).sum() == pytest.approx((PtU * V).sum(), rel=1e-12)
+    # linearity in V
+    np.testing.assert_allclose(oracle.apply(x, y, a, b, f, g, eps, 2.0 * V - U[:8]),
+                               2.0 * PV - oracle.apply(x, y, a, b, f, g, eps, U[:8]), rtol=1e-11, atol=1e-14)
+    # rescaling: P(f + delta, g) = diag(exp(delta/eps)) P(f, g)
+    delta = rng.standard_normal(9) * 0.05
+    np.testing.assert_allclose(oracle.apply(x, y, a, b, f + delta, g, eps, V),
+                               np.exp(delta / eps)[:, None] * PV, rtol=1e-11)
+    # after f = F(g) the row sums are exactly a; after g = G(f) the column sums are b
+    f1 = oracle.F(x, y, b, g, eps)
+    np.testing.assert_allclose(oracle.apply(x, y, a, b, f1, g, eps, np.ones(8)), a, rtol=1e-13)
+    g1 = oracle.G(x, y, a, f, eps)
+    np.testing.assert_allclose(oracle.apply(x, y, a, b, f, g1, eps, np.ones(9), transpose=True), b, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- maps: gauge and contraction
+def test_map_gauge_and_nonexpansive():
+    x, y = _cloud(81, 10, 2), _cloud(82, 12, 2)
+    a, b = _weights(83, 10), _weights(84, 12)
+    eps = 0.1
+    rng = np.random.default_rng(85)
+    g1, g2 = rng.standard_normal(12), rng.standard_normal(12)
+    F1, F2 = oracle.F(x, y, b, g1, eps), oracle.F(x, y, b, g2, eps)
+    np.testing.assert_allclose(oracle.F(x, y, b, g1 + 0.37, eps), F1 - 0.37, rtol=1e-13, atol=1e-13)
+
+    def osc(v):
+        return v.max() - v.min()
+    # the log-domain map is an average (softmin), so it cannot expand oscillations
+    assert osc(F1 - F2) <= osc(g1 - g2) + 1e-13
+    assert np.all(F1 - F2 <= (g2 - g1).max() + 1e-13) and np.all(F1 - F2 >= (g2 - g1).min() - 1e-13)
+
+
+def test_zero_weights_drop_out():
+    x, y = _cloud(91, 6, 2), _cloud(92, 7, 2)
+    a, b = _weights(93, 6), _weights(94, 7)
+    b0 = b.copy()
+    b0[[1, 4]] = 0.0
+    eps = 0.2
+    f, g, cost = oracle.solve(x, y, a, b0, eps, 5)
+    keep = [0, 2, 3, 5, 6]
+    fk, gk, ck = oracle.solve(x, y[keep], a, b0[keep], eps, 5)
+    np.testing.assert_allclose(f, fk, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g[keep], gk, rtol=1e-12, atol=1e-14)
+    assert cost == pytest.approx(ck, rel=1e-12)
