@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the streaming log-domain Sinkhorn hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+a fixed-budget solve (prep, `iters` iterations of an F and a G half-pass, the
+cost), the barycentric gradient with respect to x, and the transport
+applications P V and P^T U with k = 16. The reported value is Sinkhorn
+iterations per second of the whole step (iterations per step / seconds per
+step), so the gradient and applications count against it.
+
+Default workload: n = m = 50,000, d = 64, bf16 points, Dirichlet weights,
+eps = 0.1, 100 alternating iterations. The same JSON line carries the d = 3
+point of the metric (n = m = 50,000, 8-Gaussian mixture, eps = 0.01,
+100 alternating iterations) under "d3".
+
+Timing: W untimed warm-up steps, then exactly K steps between two device
+synchronizations. Inside the timed region every call is bracketed by HIP
+events on the stream the library launches on (torch's current stream); the
+average half-pass duration is (solve time - prep/cost time) / (2 iters).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "Sinkhorn iters/s at n=m=50k (d=3, d=64) + % of gfx950 roofline"
+CU, CLK = 256, 2.4e9
+# v_exp_f32 issues at half the 64-lane VALU rate: 32 lanes per CU per clock.
+EXP_PEAK = CU * 32 * CLK            # exp2 evaluations per second
+VALU_PEAK = CU * 64 * CLK           # fp32 VALU lane-operations per second (no packed math)
+BF16_MFMA_PEAK = 2.5e15             # dense bf16 MFMA flop/s
+F32_MFMA_PEAK = 157.3e12
+HBM_PEAK = 8.0e12
+
+WORKLOADS = {w.name: key for key, w in W.CONFIGS.items()}
+
+
+def _dev_points(arr, dtype, torch, dev):
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(arr).to(dev)
+
+
+class Case:
+    def __init__(self, key, torch, sk, dev, k=16):
+        self.w = w = W.CONFIGS[key]
+        inp = W.make_inputs(w, k=k)
+        self.inp = inp
+        self.x = _dev_points(inp.x, w.dtype, torch, dev)
+        self.y = _dev_points(inp.y, w.dtype, torch, dev)
+        self.a = torch.from_numpy(inp.a).to(dev)
+        self.b = torch.from_numpy(inp.b).to(dev)
+        self.V = torch.from_numpy(inp.V).to(dev)
+        self.U = torch.from_numpy(inp.U).to(dev)
+        self.k = k
+        self.sk = sk
+        self.torch = torch
+        dt = sk.SK_BF16 if w.dtype == "bf16" else sk.SK_F32
+        nbytes = max(sk.workspace_bytes(sk.SK_OP_SOLVE, dt, w.n, w.m, w.d),
+                     sk.workspace_bytes(sk.SK_OP_GRAD, dt, w.n, w.m, w.d),
+                     sk.workspace_bytes(sk.SK_OP_APPLY, dt, w.n, w.m, w.d, k))
+        self.ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+
+    def step(self, ev=None):
+        """One pass of the hot path; with ev, records (start, end) events per call."""
+        sk, w, t = self.sk, self.w, self.torch
+
+        def rec():
+            if ev is None:
+                return None
+            e = t.cuda.Event(enable_timing=True)
+            e.record()
+            return e
+
+        e0 = rec()
+        f, g, cost = sk.solve(self.x, self.y, self.a, self.b, w.eps, w.iters, w.mode, workspace=self.ws)
+        e1 = rec()
+        grad = sk.eot_grad_x(self.x, self.y, self.a, self.b, g, w.eps, workspace=self.ws)
+        e2 = rec()
+        pv = sk.transport_apply(self.x, self.y, self.a, self.b, f, g, w.eps, self.V, workspace=self.ws)
+        e3 = rec()
+        ptu = sk.transport_apply(self.x, self.y, self.a, self.b, f, g, w.eps, self.U, transpose=True,
+                                 workspace=self.ws)
+        e4 = rec()
+        if ev is not None:
+            ev.append((e0, e1, e2, e3, e4))
+        return f, g, cost, grad, pv, ptu
+
+    def overhead_ms(self, reps=5):
+        """Duration of a solve with zero iterations (prep and cost only)."""
+        t = self.torch
+        out = []
+        for _ in range(reps):
+            s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            s.record()
+            self.sk.solve(self.x, self.y, self.a, self.b, self.w.eps, 0, self.w.mode, workspace=self.ws)
+            e.record()
+            e.synchronize()
+            out.append(s.elapsed_time(e))
+        return statistics.median(out)
+
+
+def pass_roofline(w, pass_ms):
+    """Roofline of the half-pass kernel: per pair one exp2 is irreducible."""
+    pairs = w.n * w.m
+    sec = pass_ms * 1e-3
+    exp_rate = pairs / sec
+    mfma_flops = 2.0 * w.d * pairs
+    if w.d >= 32:
+        peak = BF16_MFMA_PEAK if w.dtype == "bf16" else F32_MFMA_PEAK
+        alu_frac = exp_rate / EXP_PEAK
+        mfma_frac = mfma_flops / sec / peak
+        # the binding roof is whichever ideal time is longer
+        if mfma_flops / peak >= pairs / EXP_PEAK:
+            return {"bound": "mfma", "achieved": mfma_flops / sec / 1e12, "peak": peak / 1e12,
+                    "unit": "TFLOP/s", "frac": mfma_frac, "traffic": None,
+                    "also": {"exp_frac": alu_frac}}
+        return {"bound": "alu", "achieved": exp_rate / 1e9, "peak": EXP_PEAK / 1e9, "unit": "Gexp/s",
+                "frac": alu_frac, "traffic": None,
+                "also": {"mfma_frac": mfma_frac, "mfma_TFLOPs": mfma_flops / sec / 1e12}}
+    return {"bound": "alu", "achieved": exp_rate / 1e9, "peak": EXP_PEAK / 1e9, "unit": "Gexp/s",
+            "frac": exp_rate / EXP_PEAK, "traffic": None}
+
+
+def measure(case, steps, warmup):
+    torch = case.torch
+    for _ in range(warmup):
+        case.step()
+    torch.cuda.synchronize()
+    ov = case.overhead_ms()
+    torch.cuda.synchronize()
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        case.step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    solve_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    grad_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    pv_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    ptu_ms = [e[3].elapsed_time(e[4]) for e in ev]
+    w = case.w
+    pass_ms = (statistics.median(solve_ms) - ov) / (2 * w.iters)
+    return {
+        "wall_s": wall,
+        "ms_per_step": 1e3 * wall / steps,
+        "iters_per_s": w.iters * steps / wall,
+        "solve_ms_median": statistics.median(solve_ms),
+        "solve_ms_q01_q99": [float(np.quantile(solve_ms, 0.01)), float(np.quantile(solve_ms, 0.99))],
+        "prep_cost_ms": ov,
+        "half_pass_ms": pass_ms,
+        "grad_ms": statistics.median(grad_ms),
+        "apply_PV_ms": statistics.median(pv_ms),
+        "apply_PtU_ms": statistics.median(ptu_ms),
+        "solve_only_iters_per_s": w.iters / (statistics.median(solve_ms) * 1e-3),
+        "nmd_iters_per_s": w.n * w.m * w.d * w.iters * steps / wall,
+        "roofline": pass_roofline(w, pass_ms),
+    }
+
+
+def cpu_baseline(case, target_s=12.0):
+    """The float64 oracle on the host cores, on a bounded sample of the workload:
+    the F map on R rows of x and the G map on R rows of y (all columns each),
+    scaled to one full iteration (n rows of F, m rows of G)."""
+    import oracle
+
+    oracle.build(force=False)
+    w, inp = case.w, case.inp
+    x64, y64 = inp.x64(), inp.y64()
+    g = np.zeros(w.m)
+    f = np.zeros(w.n)
+    r0 = 16
+    t = time.perf_counter()
+    oracle.F(x64[:r0], y64, inp.b, g, w.eps)
+    oracle.G(x64, y64[:r0], inp.a, f, w.eps)
+    per_row = (time.perf_counter() - t) / (2 * r0)
+    R = int(max(r0, min(w.n, w.m, target_s / (2 * per_row))))
+    t = time.perf_counter()
+    oracle.F(x64[:R], y64, inp.b, g, w.eps)
+    tf = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.G(x64, y64[:R], inp.a, f, w.eps)
+    tg = time.perf_counter() - t
+    sec_per_iter = tf * w.n / R + tg * w.m / R
+    return {"value": 1.0 / sec_per_iter, "unit": "iters/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"F map on {R} rows of x and G map on {R} rows of y (all {w.m} and {w.n} columns), "
+                      f"float64, scaled by n/{R} and m/{R} to one iteration; {tf + tg:.1f} s measured"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="embed_d64_50k_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-d3", action="store_true", help="skip the d=3 point")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import streaming_sinkhorn_solver_log_amd as sk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    key = WORKLOADS[args.workload]
+    print(f"[bench] workload {args.workload}: building inputs", file=sys.stderr, flush=True)
+    case = Case(key, torch, sk, dev)
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    r = measure(case, args.steps, args.warmup)
+    w = case.w
+    out = {
+        "metric": METRIC,
+        "value": r["iters_per_s"],
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "point_dtype": w.dtype,
+                   "eps": w.eps, "iters": w.iters, "mode": w.mode, "weights": w.weights,
+                   "step": f"solve({w.iters} iters) + eot_grad_x + P.V + P^T.U (k=16)"},
+        "roofline": r["roofline"],
+        "detail": {k: v for k, v in r.items() if k != "roofline"},
+    }
+    if not args.no_d3 and key != 6:
+        print("[bench] d=3 point", file=sys.stderr, flush=True)
+        c3 = Case(6, torch, sk, dev)
+        r3 = measure(c3, args.steps, args.warmup)
+        out["d3"] = {"workload": c3.w.name, "iters_per_s": r3["iters_per_s"], "ms_per_step": r3["ms_per_step"],
+                     "roofline": r3["roofline"], "detail": {k: v for k, v in r3.items() if k != "roofline"}}
+        del c3
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * flashsk.h -- C ABI of the streaming log-domain Sinkhorn library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Problem (entropic optimal transport between weighted point clouds under the
+ * squared Euclidean cost; "FlashSinkhorn: IO-Aware Entropic Optimal Transport
+ * on GPU", abstract, and its replication review, Summary):
+ *
+ *   x_i (i < n), y_j (j < m) in R^d, weights a_i >= 0, b_j >= 0, eps > 0
+ *   C_ij = |x_i - y_j|^2 = |x_i|^2 + |y_j|^2 - 2 x_i.y_j
+ *   P_ij = a_i b_j exp((f_i + g_j - C_ij) / eps)                 (transport plan)
+ *   F(g)_i = -eps LSE_j( log b_j + (g_j - |y_j|^2 + 2 x_i.y_j)/eps ) + |x_i|^2
+ *   G(f)_j = -eps LSE_i( log a_i + (f_i - |x_i|^2 + 2 x_i.y_j)/eps ) + |y_j|^2
+ *
+ * F and G are the stabilized log-domain Sinkhorn updates written as row-wise
+ * log-sum-exp reductions of biased dot-product scores (review, Summary: the
+ * cost has the form alpha_i + beta_j - Q_i.K_j). The library evaluates them
+ * tile by tile on the GPU; the n x m cost and plan matrices are never stored.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless stated otherwise. Arrays are dense and
+ *    row-major: x is n x d, y is m x d, V/U/out are (rows x k), grad_x is n x d.
+ *    x and y are float32 (SK_F32) or bfloat16 bit patterns (SK_BF16); every
+ *    other array is float32. x, y, V need 16-byte alignment.
+ *  - The caller owns all memory. The library allocates nothing and keeps no
+ *    state between calls apart from loaded code objects and a thread-local
+ *    error string. Scratch memory is the caller's workspace `ws` of at least
+ *    sk_workspace_bytes(...) bytes (256-byte aligned); its contents on entry
+ *    are ignored and on exit are unspecified.
+ *  - `stream` is a hipStream_t (NULL: the default stream). All work is enqueued
+ *    on it asynchronously; outputs are valid once the stream has synchronized.
+ *    Calls on the same workspace must not overlap.
+ *  - Return value: SK_OK (0) or a negative SK_ERR_* code. Arguments are
+ *    validated on the host before anything is enqueued; on a validation error
+ *    nothing is enqueued and no output is touched. sk_last_error() gives the
+ *    message of the calling thread's last failure.
+ *  - NaN or Inf inputs propagate to the outputs; they are not detected.
+ *    A weight vector that sums to zero makes the potentials +Inf.
+ */
+#ifndef FLASHSK_H
+#define FLASHSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SK_VERSION 1
+
+/* return codes */
+#define SK_OK 0
+#define SK_ERR_INVALID_ARG (-1) /* a size, pointer, eps, mode or flag is invalid  */
+#define SK_ERR_UNSUPPORTED (-2) /* a valid combination this build does not handle */
+#define SK_ERR_WORKSPACE (-3)   /* ws is NULL, misaligned or too small            */
+#define SK_ERR_HIP (-4)         /* the HIP runtime reported an error              */
+
+/* storage type of x and y */
+#define SK_F32 0
+#define SK_BF16 1
+
+/* schedules (review, Strengths: "symmetric-vs-alternating comparisons") */
+#define SK_ALTERNATING 0 /* f <- F(g); then g <- G(f) with the new f            */
+#define SK_SYMMETRIC 1   /* (f, g) <- ((f + F(g))/2, (g + G(f))/2) at the old pair */
+
+/* solve flags */
+#define SK_WARM_START 1u /* f and g hold the starting potentials (else zeros)  */
+#define SK_NO_CENTER 2u  /* do not translate float32 clouds to a common origin */
+
+/* operations, for sk_workspace_bytes */
+#define SK_OP_SOLVE 0
+#define SK_OP_APPLY 1
+#define SK_OP_GRAD 2
+
+/*
+ * Fixed-budget Sinkhorn solve (FlashSinkhorn abstract; review, Summary and
+ * Weaknesses: fixed iteration budgets).
+ *   iters      number of full iterations (each is an F half-pass and a G
+ *              half-pass); iters = 0 returns the starting potentials and
+ *              their cost.
+ *   mode       SK_ALTERNATING or SK_SYMMETRIC.
+ *   flags      SK_WARM_START, SK_NO_CENTER.
+ *   f, g       out (in/out with SK_WARM_START): n and m float32 potentials.
+ *   cost       out: one double, <a, f> + <b, g> at the final pair.
+ * Requirements: n, m, d >= 1; eps finite and > 0; iters >= 0.
+ */
+int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                      const float* a, const float* b, double eps, int32_t iters, int mode,
+                      uint32_t flags, float* f, float* g, double* cost, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * Matrix-free transport application (review, Summary item ii: transport-vector
+ * and transport-matrix applications): with the plan P formed from the given
+ * (f, g) as they are (no renormalization),
+ *   transpose = 0:  out (n x k) = P V,    V is m x k
+ *   transpose = 1:  out (m x k) = P^T V,  V is n x k
+ * Requirements: 1 <= k <= 64 (SK_ERR_UNSUPPORTED above), as for the solve otherwise.
+ */
+int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                       const float* a, const float* b, const float* f, const float* g, double eps,
+                       int transpose, const float* V, int64_t k, float* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * Gradient of the EOT cost with respect to x as a barycentric projection (the
+ * review's Summary item i: the gradient as a residual attention output):
+ *   grad_x_i = 2 a_i (x_i - sum_j pi_ij y_j),
+ *   pi_ij = softmax over j of (log b_j + (g_j - C_ij)/eps),
+ * using g only. This is the exact derivative of x -> <a, F_x(g)> + <b, g>;
+ * it equals the derivative of the cost at a converged pair.
+ * Requirements as for the solve.
+ */
+int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                  const float* a, const float* b, const float* g, double eps, float* grad_x,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by `op` for these sizes (0 on invalid sizes). */
+size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, int64_t k);
+
+/* Message of the calling thread's last failed call ("" if none). Never NULL. */
+const char* sk_last_error(void);
+
+/* SK_VERSION of the loaded library. */
+int sk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHSK_H */

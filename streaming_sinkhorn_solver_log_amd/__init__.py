@@ -1,0 +1,189 @@
+"""Streaming log-domain Sinkhorn on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libflashsk.so`` (include/flashsk.h).
+It only marshals arguments: checks tensor devices, dtypes and shapes,
+allocates outputs and the workspace with PyTorch, and passes raw device
+pointers plus the current HIP stream. Every step of the computation runs in
+the library's HIP kernels; there is no Python or CPU fallback, and importing
+the package fails loudly if the shared library is missing.
+
+    f, g, cost = solve(x, y, a, b, eps, iters, mode="alternating")
+    out = transport_apply(x, y, a, b, f, g, eps, V)                  # P V
+    out = transport_apply(x, y, a, b, f, g, eps, U, transpose=True)  # P^T U
+    grad = eot_grad_x(x, y, a, b, g, eps)
+
+x, y: (n, d) and (m, d) float32 or bfloat16 CUDA tensors; a, b, f, g, V, U:
+float32. Plans, potentials and costs follow the conventions of flashsk.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflashsk.so")
+
+SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0, -1, -2, -3, -4
+SK_F32, SK_BF16 = 0, 1
+SK_ALTERNATING, SK_SYMMETRIC = 0, 1
+SK_WARM_START, SK_NO_CENTER = 1, 2
+SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD = 0, 1, 2
+
+_ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
+              SK_ERR_WORKSPACE: "SK_ERR_WORKSPACE", SK_ERR_HIP: "SK_ERR_HIP"}
+
+
+class SinkhornError(RuntimeError):
+    """A non-zero return code of the C ABI."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _load_library() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m streaming_sinkhorn_solver_log_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, U32, D, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                               ctypes.c_double, ctypes.c_size_t)
+    INT = ctypes.c_int
+    lib.sk_sinkhorn_solve.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, SZ, P]
+    lib.sk_sinkhorn_solve.restype = INT
+    lib.sk_transport_apply.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, I64, P, P, SZ, P]
+    lib.sk_transport_apply.restype = INT
+    lib.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
+    lib.sk_eot_grad_x.restype = INT
+    lib.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
+    lib.sk_workspace_bytes.restype = SZ
+    lib.sk_last_error.argtypes = []
+    lib.sk_last_error.restype = ctypes.c_char_p
+    lib.sk_version.argtypes = []
+    lib.sk_version.restype = INT
+    return lib
+
+
+_lib = _load_library()
+EXPORTS = ("sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x", "sk_workspace_bytes",
+           "sk_last_error", "sk_version")
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != SK_OK:
+        raise SinkhornError(rc, _lib.sk_last_error().decode(errors="replace"))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SK_F32
+    if t.dtype == torch.bfloat16:
+        return SK_BF16
+    raise TypeError(f"points must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _vec(t: torch.Tensor, n: int, name: str, device) -> torch.Tensor:
+    if t.dtype != torch.float32 or t.device != device or t.shape != (n,) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape ({n},) on {device}")
+    return t
+
+
+def _points(x: torch.Tensor, y: torch.Tensor):
+    if not (x.is_cuda and y.is_cuda):
+        raise ValueError("x and y must be GPU tensors")
+    if x.dim() != 2 or y.dim() != 2 or x.shape[1] != y.shape[1]:
+        raise ValueError("x must be (n, d) and y (m, d) with the same d")
+    if x.dtype != y.dtype or x.device != y.device:
+        raise ValueError("x and y must share dtype and device")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("x and y must be contiguous")
+    return x.shape[0], y.shape[0], x.shape[1], _dtype_code(x)
+
+
+def workspace_bytes(op: int, dtype: int, n: int, m: int, d: int, k: int = 0) -> int:
+    return int(_lib.sk_workspace_bytes(op, dtype, n, m, d, k))
+
+
+def _workspace(op, dtype, n, m, d, k, device, ws):
+    need = workspace_bytes(op, dtype, n, m, d, k)
+    if need == 0:
+        need = 256  # invalid sizes: the library reports the reason
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws, ws.data_ptr() + off, ws.numel() - off
+
+
+def solve(x, y, a, b, eps: float, iters: int, mode: str = "alternating", f0=None, g0=None,
+          center: bool = True, workspace=None):
+    """Fixed-budget Sinkhorn; returns (f, g, cost) with cost a 0-d float64 tensor."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    _vec(a, n, "a", dev)
+    _vec(b, m, "b", dev)
+    mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
+    flags = 0 if center else SK_NO_CENTER
+    if (f0 is None) != (g0 is None):
+        raise ValueError("give both f0 and g0 for a warm start, or neither")
+    if f0 is not None:
+        f = _vec(f0, n, "f0", dev).clone()
+        g = _vec(g0, m, "g0", dev).clone()
+        flags |= SK_WARM_START
+    else:
+        f = torch.empty(n, dtype=torch.float32, device=dev)
+        g = torch.empty(m, dtype=torch.float32, device=dev)
+    cost = torch.empty((), dtype=torch.float64, device=dev)
+    _, wptr, wbytes = _workspace(SK_OP_SOLVE, dt, n, m, d, 0, dev, workspace)
+    _check(_lib.sk_sinkhorn_solve(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
+                                  int(iters), mode_code, flags, _ptr(f), _ptr(g), _ptr(cost),
+                                  ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return f, g, cost
+
+
+def transport_apply(x, y, a, b, f, g, eps: float, V, transpose: bool = False, workspace=None):
+    """P V (V: m x k), or P^T V (V: n x k) with transpose=True."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    for t, cnt, name in ((a, n, "a"), (b, m, "b"), (f, n, "f"), (g, m, "g")):
+        _vec(t, cnt, name, dev)
+    squeeze = V.dim() == 1
+    V2 = V[:, None] if squeeze else V
+    rows_in = n if transpose else m
+    if V2.dtype != torch.float32 or V2.device != dev or V2.dim() != 2 or V2.shape[0] != rows_in:
+        raise ValueError(f"V must be float32 of shape ({rows_in}, k) on {dev}")
+    V2 = V2.contiguous()
+    k = V2.shape[1]
+    out = torch.empty((m if transpose else n, k), dtype=torch.float32, device=dev)
+    _, wptr, wbytes = _workspace(SK_OP_APPLY, dt, n, m, d, k, dev, workspace)
+    _check(_lib.sk_transport_apply(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(f), _ptr(g),
+                                   float(eps), int(bool(transpose)), _ptr(V2), k, _ptr(out),
+                                   ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return out[:, 0] if squeeze else out
+
+
+def eot_grad_x(x, y, a, b, g, eps: float, workspace=None):
+    """Barycentric-projection gradient of the EOT cost with respect to x (n x d)."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    for t, cnt, name in ((a, n, "a"), (b, m, "b"), (g, m, "g")):
+        _vec(t, cnt, name, dev)
+    out = torch.empty((n, d), dtype=torch.float32, device=dev)
+    _, wptr, wbytes = _workspace(SK_OP_GRAD, dt, n, m, d, 0, dev, workspace)
+    _check(_lib.sk_eot_grad_x(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(g), float(eps),
+                              _ptr(out), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return out

@@ -1,0 +1,126 @@
+// prep.hip -- once-per-call preparation and the final cost reduction.
+//
+// The cost decomposes as C_ij = alpha_i + beta_j - 2 p_i.q_j with alpha, beta the
+// squared norms (FlashSinkhorn replication review, Summary and Weaknesses: the
+// fused update needs a cost of the form alpha_i + beta_j - Q_i.K_j). The prep
+// kernels compute, for each side, the packed points, the norms, the natural-log
+// weights and the column biases of the starting potentials. Float clouds are
+// first translated by the midpoint of their two centroids: C is invariant
+// under a common translation, and smaller norms make the expansion better
+// conditioned in float32.
+#include "sk_internal.h"
+
+#include <math.h>
+
+namespace sk {
+namespace {
+
+__device__ inline float load_point(const void* pts, int dtype, int64_t idx) {
+  if (dtype == 0) return static_cast<const float*>(pts)[idx];
+  const unsigned short bits = static_cast<const unsigned short*>(pts)[idx];
+  return __uint_as_float(static_cast<unsigned>(bits) << 16);
+}
+
+// Partial coordinate sums (float64) of both clouds: part[b][0..d) for x, part[b][d..2d) for y.
+__global__ __launch_bounds__(256) void k_centroid_partial(const void* x, int64_t n, const void* y,
+                                                           int64_t m, int dtype, int d,
+                                                           double* part) {
+  const int b = blockIdx.x;
+  for (int side = 0; side < 2; ++side) {
+    const void* pts = side ? y : x;
+    const int64_t cnt = side ? m : n;
+    const int64_t per = (cnt + gridDim.x - 1) / gridDim.x;
+    const int64_t r0 = b * per, r1 = min(cnt, r0 + per);
+    for (int k = threadIdx.x; k < d; k += blockDim.x) {
+      double s = 0.0;
+      for (int64_t r = r0; r < r1; ++r) s += load_point(pts, dtype, r * d + k);
+      part[((int64_t)b * 2 + side) * d + k] = s;
+    }
+  }
+}
+
+// shift_k = (mean_x + mean_y)_k / 2, summed over the partials in a fixed order.
+__global__ __launch_bounds__(256) void k_centroid_final(const double* part, int nb, int64_t n,
+                                                        int64_t m, int d, float* shift) {
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    double sx = 0.0, sy = 0.0;
+    for (int b = 0; b < nb; ++b) {
+      sx += part[((int64_t)b * 2 + 0) * d + k];
+      sy += part[((int64_t)b * 2 + 1) * d + k];
+    }
+    shift[k] = static_cast<float>(0.5 * (sx / (double)n + sy / (double)m));
+  }
+}
+
+// One thread per point of either side: packed float32 point (row stride dp,
+// zero padded), |p|^2, ln w, and the bias of the starting potential.
+__global__ __launch_bounds__(256) void k_prep_f32(PrepSide xs, PrepSide ys, int dtype, int d,
+                                                  int dp, const float* shift,
+                                                  float log2e_over_eps, unsigned* counters,
+                                                  int n_counters) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid < n_counters) counters[gid] = 0u;
+  const bool is_x = gid < xs.n;
+  const PrepSide& s = is_x ? xs : ys;
+  const int64_t r = is_x ? gid : gid - xs.n;
+  if (r >= s.n) return;
+  float nrm = 0.0f;
+  for (int k = 0; k < dp; ++k) {
+    float v = 0.0f;
+    if (k < d) {
+      v = load_point(s.pts, dtype, r * d + k);
+      if (shift) v -= shift[k];
+    }
+    s.packed[r * dp + k] = v;
+    nrm = fmaf(v, v, nrm);
+  }
+  const float lw = logf(s.w[r]);
+  const float pot = s.pot ? s.pot[r] : 0.0f;
+  if (s.pot_init) s.pot_init[r] = 0.0f;
+  s.alpha[r] = nrm;
+  s.lw[r] = lw;
+  s.h[r] = kLog2e * lw + (pot - nrm) * log2e_over_eps;
+}
+
+// cost = sum_i a_i f_i + sum_j b_j g_j in float64, one workgroup, fixed order.
+__global__ __launch_bounds__(1024) void k_cost(const float* a, const float* f, int64_t n,
+                                               const float* b, const float* g, int64_t m,
+                                               double* cost) {
+  __shared__ double red[1024];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s += (double)a[i] * (double)f[i];
+  for (int64_t j = threadIdx.x; j < m; j += blockDim.x) s += (double)b[j] * (double)g[j];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *cost = red[0];
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepSide& xs, const PrepSide& ys, int dtype, int d, int dp,
+                       bool center, double* centroid_part, float* shift, unsigned* counters,
+                       int n_counters, float log2e_over_eps, hipStream_t s) {
+  if (center) {
+    k_centroid_partial<<<kCentroidBlocks, 256, 0, s>>>(xs.pts, xs.n, ys.pts, ys.n, dtype, d,
+                                                       centroid_part);
+    k_centroid_final<<<1, 256, 0, s>>>(centroid_part, kCentroidBlocks, xs.n, ys.n, d, shift);
+  }
+  const int64_t total = xs.n + ys.n;
+  const int64_t work = total > n_counters ? total : n_counters;
+  const int blocks = (int)((work + 255) / 256);
+  k_prep_f32<<<blocks, 256, 0, s>>>(xs, ys, dtype, d, dp, center ? shift : nullptr,
+                                    log2e_over_eps, counters, n_counters);
+  return hipGetLastError();
+}
+
+hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
+                       int64_t m, double* cost, hipStream_t s) {
+  k_cost<<<1, 1024, 0, s>>>(a, f, n, b, g, m, cost);
+  return hipGetLastError();
+}
+
+}  // namespace sk

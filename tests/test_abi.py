@@ -1,0 +1,119 @@
+"""The C-ABI library loads, exports every symbol include/flashsk.h declares, and
+rejects invalid arguments on the host before anything reaches a GPU.
+
+No test here makes a compute call: every call below fails validation, which
+happens before the first HIP call, so the suite runs on machines without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashsk.h")
+LIB = os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "libflashsk.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sk_[a-z_]+)\s*\(", src)))
+
+
+def _header_int(name):
+    m = re.search(r"#define\s+%s\s+\(?(-?\w+)u?\)?" % name, open(HEADER).read())
+    return int(m.group(1).rstrip("u"), 0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libflashsk.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    P, I64, I32, U32, D, SZ, INT = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                                    ctypes.c_double, ctypes.c_size_t, ctypes.c_int)
+    L.sk_sinkhorn_solve.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, SZ, P]
+    L.sk_transport_apply.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, I64, P, P, SZ, P]
+    L.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
+    L.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
+    L.sk_workspace_bytes.restype = SZ
+    L.sk_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x",
+                          "sk_workspace_bytes", "sk_last_error", "sk_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.sk_version() == _header_int("SK_VERSION")
+    assert lib.sk_last_error() is not None
+
+
+def test_workspace_sizes(lib):
+    solve, apply, grad = _header_int("SK_OP_SOLVE"), _header_int("SK_OP_APPLY"), _header_int("SK_OP_GRAD")
+    for d in (1, 3, 16):
+        for n, m in ((1, 1), (1024, 1024), (10_000, 777), (50_000, 50_000)):
+            s = lib.sk_workspace_bytes(solve, 0, n, m, d, 0)
+            assert s >= 4 * (n + m) * d
+            assert lib.sk_workspace_bytes(apply, 0, n, m, d, 16) > 0
+            assert lib.sk_workspace_bytes(grad, 0, n, m, d, 0) > 0
+    assert lib.sk_workspace_bytes(solve, 0, 0, 5, 3, 0) == 0
+    assert lib.sk_workspace_bytes(solve, 0, 5, 5, 0, 0) == 0
+    assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 0) == 0
+    assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 65) == 0
+    assert lib.sk_workspace_bytes(99, 0, 5, 5, 3, 0) == 0
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _solve(lib, **kw):
+    args = dict(x=FAKE, y=FAKE, dtype=0, n=10, m=12, d=3, a=FAKE, b=FAKE, eps=0.1, iters=3, mode=0,
+                flags=0, f=FAKE, g=FAKE, cost=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sk_sinkhorn_solve(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), "SK_ERR_INVALID_ARG"),
+    (dict(b=None), "SK_ERR_INVALID_ARG"),
+    (dict(f=None), "SK_ERR_INVALID_ARG"),
+    (dict(cost=None), "SK_ERR_INVALID_ARG"),
+    (dict(dtype=7), "SK_ERR_INVALID_ARG"),
+    (dict(n=0), "SK_ERR_INVALID_ARG"),
+    (dict(m=-3), "SK_ERR_INVALID_ARG"),
+    (dict(d=0), "SK_ERR_INVALID_ARG"),
+    (dict(eps=0.0), "SK_ERR_INVALID_ARG"),
+    (dict(eps=-1.0), "SK_ERR_INVALID_ARG"),
+    (dict(eps=float("nan")), "SK_ERR_INVALID_ARG"),
+    (dict(eps=float("inf")), "SK_ERR_INVALID_ARG"),
+    (dict(iters=-1), "SK_ERR_INVALID_ARG"),
+    (dict(mode=2), "SK_ERR_INVALID_ARG"),
+    (dict(flags=0x80), "SK_ERR_INVALID_ARG"),
+    (dict(x=FAKE + 4), "SK_ERR_INVALID_ARG"),
+    (dict(ws=None), "SK_ERR_WORKSPACE"),
+    (dict(ws=FAKE + 64), "SK_ERR_WORKSPACE"),
+    (dict(ws_bytes=16), "SK_ERR_WORKSPACE"),
+    (dict(n=1 << 31), "SK_ERR_UNSUPPORTED"),
+])
+def test_solve_rejects_invalid_arguments(lib, kw, code):
+    assert _solve(lib, **kw) == _header_int(code)
+    assert len(lib.sk_last_error()) > 0
+
+
+def test_apply_and_grad_reject_invalid_arguments(lib):
+    inv, uns, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_UNSUPPORTED"), _header_int("SK_ERR_WORKSPACE")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, FAKE, FAKE, 0.1, 0, FAKE, 4, FAKE, FAKE, 1 << 30, None]
+    for idx, val, code in [(11, 2, inv), (13, 0, inv), (13, 65, uns), (12, None, inv), (14, None, inv),
+                           (8, None, inv), (10, 0.0, inv), (15, None, wsp), (16, 8, wsp)]:
+        args = list(base)
+        args[idx] = val
+        assert lib.sk_transport_apply(*args) == code, (idx, val)
+    gbase = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, None]
+    for idx, val, code in [(8, None, inv), (10, None, inv), (2, 5, inv), (9, -0.5, inv), (11, None, wsp)]:
+        args = list(gbase)
+        args[idx] = val
+        assert lib.sk_eot_grad_x(*args) == code, (idx, val)

@@ -1,0 +1,230 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Both sides get identical seeded inputs (workloads/): the oracle reads the stored
+float32 or bf16 values exactly, promoted to float64. Tolerances (written per
+test) follow the arithmetic of the GPU path:
+  * fp32 points: potentials within 1e-4 * eps absolute, cost within 1e-5 relative;
+  * bf16 points: potentials within 1e-3 * max(|f_ref|_inf, eps), cost 1e-3 relative;
+  * gradient and transport application, both sides fed the same fp32 potentials:
+    |delta|_inf / |ref|_inf <= 1e-5 (fp32 points) or 1e-3 (bf16 points).
+Shapes span several workgroup tiles and column splits and end in ragged tails;
+the full-size workloads are checked on sampled rows that the oracle computes one
+by one, and through properties that hold at any size.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sk():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import streaming_sinkhorn_solver_log_amd as sk
+    return sk
+
+
+DEV = "cuda:0"
+
+
+def dev_points(arr, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(arr).to(DEV)
+
+
+def dev(inp):
+    return (dev_points(inp.x, inp.w.dtype), dev_points(inp.y, inp.w.dtype),
+            torch.from_numpy(inp.a).to(DEV), torch.from_numpy(inp.b).to(DEV))
+
+
+def tol_pot(w, ref):
+    if w.dtype == "bf16":
+        return 1e-3 * max(np.abs(ref).max(), w.eps)
+    return 1e-4 * w.eps
+
+
+def tol_rel(w):
+    return 1e-3 if w.dtype == "bf16" else 1e-5
+
+
+def bf16_variant(w, name="bf16"):
+    from dataclasses import replace
+    return replace(w, dtype="bf16", name=w.name + "_" + name)
+
+
+SOLVE_CASES = [
+    # (config key, n, m, iters or None for the config's own count)
+    (1, 1024, 1024, None),        # the tiny configuration at full size
+    (1, 1000, 333, 20),
+    (2, 1500, 2100, 40),          # symmetric schedule, eps = 0.01
+    (6, 2000, 1777, 30),          # alternating, eps = 0.01
+    (1, 1, 1, 5),
+    (1, 1, 700, 5),
+    (1, 700, 1, 5),
+    (1, 257, 4099, 10),
+]
+
+
+@pytest.mark.parametrize("key,n,m,iters", SOLVE_CASES)
+def test_solve_matches_oracle(sk, key, n, m, iters):
+    w = W.CONFIGS[key].scaled(n, m, iters)
+    say(f"solve cfg={key} n={n} m={m} d={w.d} iters={w.iters} mode={w.mode} eps={w.eps}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    torch.cuda.synchronize()
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    f, g = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    ef, eg = np.abs(f - fr).max(), np.abs(g - gr).max()
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} tol={tol_pot(w, fr):.3e} cost {float(cost):.9g} vs {cr:.9g}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * max(abs(cr), 1e-30)
+
+
+def test_solve_bf16_points_small_d(sk):
+    w = bf16_variant(W.CONFIGS[1].scaled(900, 1100, 20))
+    say("solve bf16 d=3")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    assert np.abs(f.cpu().numpy() - fr).max() <= tol_pot(w, fr)
+    assert np.abs(g.cpu().numpy() - gr).max() <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
+
+
+def test_zero_iterations_and_warm_start_resume(sk):
+    w = W.CONFIGS[6].scaled(1300, 1200, 12)
+    say("iters=0 and warm-start resume")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f0, g0, c0 = sk.solve(x, y, a, b, w.eps, 0)
+    assert torch.count_nonzero(f0) == 0 and torch.count_nonzero(g0) == 0 and float(c0) == 0.0
+    f, g, c = sk.solve(x, y, a, b, w.eps, 12)
+    f1, g1, _ = sk.solve(x, y, a, b, w.eps, 5)
+    f2, g2, c2 = sk.solve(x, y, a, b, w.eps, 7, f0=f1, g0=g1)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, 12)
+    for ff, gg, cc in ((f, g, c), (f2, g2, c2)):
+        assert np.abs(ff.cpu().numpy() - fr).max() <= tol_pot(w, fr)
+        assert np.abs(gg.cpu().numpy() - gr).max() <= tol_pot(w, gr)
+        assert abs(float(cc) - cr) <= 1e-5 * abs(cr)
+    # warm start from arbitrary potentials agrees with the oracle started there
+    fs, gs = W.random_potentials(1300, 1200, 0.05, seed=5)
+    f3, g3, _ = sk.solve(x, y, a, b, w.eps, 3, "symmetric", f0=torch.from_numpy(fs).to(DEV),
+                         g0=torch.from_numpy(gs).to(DEV))
+    fr3, gr3, _ = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, 3, "symmetric", fs, gs)
+    assert np.abs(f3.cpu().numpy() - fr3).max() <= tol_pot(w, fr3)
+    assert np.abs(g3.cpu().numpy() - gr3).max() <= tol_pot(w, gr3)
+
+
+def test_zero_weights(sk):
+    w = W.CONFIGS[1].scaled(600, 500, 10)
+    say("zero weights")
+    inp = W.make_inputs(w)
+    inp.a[::7] = 0.0
+    inp.b[3::11] = 0.0
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters)
+    assert np.abs(f.cpu().numpy() - fr).max() <= tol_pot(w, fr)
+    assert np.abs(g.cpu().numpy() - gr).max() <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= 1e-5 * abs(cr)
+
+
+def test_repeatable_and_swap_symmetric(sk):
+    w = W.CONFIGS[2].scaled(1200, 1200, 15)
+    say("bitwise repeatability, swap symmetry")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    r1 = sk.solve(x, y, a, b, w.eps, w.iters, "symmetric")
+    r2 = sk.solve(x, y, a, b, w.eps, w.iters, "symmetric")
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
+    fs, gs, _ = sk.solve(y, x, b, a, w.eps, w.iters, "symmetric")
+    assert torch.equal(fs, r1[1]) and torch.equal(gs, r1[0])
+
+
+def test_translation_invariance(sk):
+    w = W.CONFIGS[1].scaled(800, 900, 10)
+    say("translation invariance")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    t = torch.tensor([3.0, -7.0, 11.0], device=DEV)
+    f1, g1, c1 = sk.solve(x, y, a, b, w.eps, w.iters)
+    f2, g2, c2 = sk.solve(x + t, y + t, a, b, w.eps, w.iters)
+    assert (f1 - f2).abs().max().item() <= 1e-4 * w.eps
+    assert abs(float(c1) - float(c2)) <= 1e-5 * abs(float(c1))
+
+
+@pytest.mark.parametrize("key,n,m", [(2, 1500, 2100), (1, 1000, 333), (1, 1, 50)])
+def test_grad_matches_oracle(sk, key, n, m):
+    w = W.CONFIGS[key].scaled(n, m, 10)
+    say(f"grad cfg={key} n={n} m={m}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    _, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    grad = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()
+    ref = oracle.grad_x(inp.x64(), inp.y64(), inp.a, inp.b, g.cpu().numpy().astype(np.float64), w.eps)
+    err = np.abs(grad - ref).max() / np.abs(ref).max()
+    say(f"  rel err {err:.3e}")
+    assert err <= tol_rel(w)
+
+
+@pytest.mark.parametrize("key,n,m,k", [(1, 1000, 333, 16), (6, 1200, 1900, 5), (1, 1, 40, 3), (1, 64, 64, 64)])
+def test_apply_matches_oracle(sk, key, n, m, k):
+    w = W.CONFIGS[key].scaled(n, m, 10)
+    say(f"apply cfg={key} n={n} m={m} k={k}")
+    inp = W.make_inputs(w, k=k)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+    PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy()
+    PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy()
+    ref = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.V)
+    reft = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.U, transpose=True)
+    e1 = np.abs(PV - ref).max() / np.abs(ref).max()
+    e2 = np.abs(PtU - reft).max() / np.abs(reft).max()
+    say(f"  rel err P.V {e1:.3e}  P^T.U {e2:.3e}")
+    assert e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
+@pytest.mark.parametrize("key", [2, 6])
+def test_full_size_sampled_rows(sk, key):
+    """Full-size solve in the benchmark's launch configuration, checked on sampled rows."""
+    w = W.CONFIGS[key]
+    say(f"full size cfg={key} n={w.n} m={w.m} iters={w.iters} mode={w.mode}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    assert torch.isfinite(f).all() and torch.isfinite(g).all()
+    # one more alternating iteration from (f, g): its f is F(g) and its g is G(F(g))
+    f1, g1, _ = sk.solve(x, y, a, b, w.eps, 1, "alternating", f0=f, g0=g)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(w.n, 96, replace=False))
+    cols = np.sort(rng.choice(w.m, 96, replace=False))
+    gT = g.cpu().numpy().astype(np.float64)
+    f1n = f1.cpu().numpy().astype(np.float64)
+    x64, y64 = inp.x64(), inp.y64()
+    fr = oracle.F(x64[rows], y64, inp.b, gT, w.eps)
+    gr = oracle.G(x64, y64[cols], inp.a, f1n, w.eps)
+    ef = np.abs(f1n[rows] - fr).max()
+    eg = np.abs(g1.cpu().numpy()[cols] - gr).max()
+    say(f"  sampled max|df|={ef:.3e} max|dg|={eg:.3e} tol={1e-4 * w.eps:.3e}")
+    assert ef <= 1e-4 * w.eps and eg <= 1e-4 * w.eps
+    # the last half-pass was the g-pass: the plan's column sums are b
+    colsum = sk.transport_apply(x, y, a, b, f1, g1, w.eps, torch.ones(w.n, device=DEV), transpose=True)
+    rel = ((colsum - b).abs() / b).max().item()
+    say(f"  column-sum rel err {rel:.3e}")
+    assert rel <= 1e-4
