@@ -7,6 +7,8 @@
 
 #include "flashsk.h"
 #include "sk_internal.h"
+#include "sk_mfma.h"
+#include <stdlib.h>
 
 namespace sk {
 namespace {
@@ -44,16 +46,35 @@ struct Carve {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Which kernel family serves (dtype, d).
-enum class Path { Valu, None };
-Path choose_path(int dtype, int64_t d) {
-  (void)dtype;
-  if (d >= 1 && d <= 16) return Path::Valu;
+// Kernel family of a solve: the matrix-core pass when its register-resident
+// records fit (bf16: d <= 128, float32: d <= 21), else the vector-ALU pass.
+// FLASHSK_SOLVE_PATH=valu selects the vector-ALU pass wherever it applies
+// (for comparisons). Gradient and transport application use the vector-ALU
+// kernels (d <= 64).
+enum class Path { Valu, Mfma, None };
+
+bool force_valu() {
+  static const bool v = [] {
+    const char* e = getenv("FLASHSK_SOLVE_PATH");
+    return e && strcmp(e, "valu") == 0;
+  }();
+  return v;
+}
+
+Path solve_path(int dtype, int64_t d) {
+  if (d < 1) return Path::None;
+  if (!force_valu() && d <= 1024 && mfma_nkb(dtype, (int)d) > 0) return Path::Mfma;
+  if (d <= 64) return Path::Valu;
   return Path::None;
 }
 
+Path aux_path(int dtype, int64_t d) {
+  (void)dtype;
+  return (d >= 1 && d <= 64) ? Path::Valu : Path::None;
+}
+
 int check_common(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
-                 const float* a, const float* b, double eps) {
+                 const float* a, const float* b, double eps, Path path) {
   if (!x || !y || !a || !b) return fail(SK_ERR_INVALID_ARG, "null input pointer");
   if (dtype != SK_F32 && dtype != SK_BF16) return fail(SK_ERR_INVALID_ARG, "dtype %d is not SK_F32 or SK_BF16", dtype);
   if (n < 1 || m < 1 || d < 1) return fail(SK_ERR_INVALID_ARG, "sizes must be >= 1 (n=%lld m=%lld d=%lld)", (long long)n, (long long)m, (long long)d);
@@ -61,11 +82,12 @@ int check_common(const void* x, const void* y, int dtype, int64_t n, int64_t m, 
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(SK_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   if (n > kMaxRows || m > kMaxRows || n * d > ((int64_t)1 << 31) - 1 || m * d > ((int64_t)1 << 31) - 1)
     return fail(SK_ERR_UNSUPPORTED, "n*d and m*d must be below 2^31");
-  if (choose_path(dtype, d) == Path::None) return fail(SK_ERR_UNSUPPORTED, "dimension d=%lld is not supported by this build", (long long)d);
+  if (path == Path::None) return fail(SK_ERR_UNSUPPORTED, "dimension d=%lld is not supported by this build", (long long)d);
   return SK_OK;
 }
 
-// Workspace of one side (points + per-point vectors).
+// ---------------------------------------------------------------- workspace layouts
+// Vector-ALU layout of one side: packed float32 points and per-point vectors.
 struct Side {
   float* pts;
   float* alpha;
@@ -74,25 +96,22 @@ struct Side {
   float* L;
 };
 
-struct SolveLayout {
-  Side x, y;
+// Matrix-core layout of one side: row-form and column-form records, bias records.
+struct SideM {
+  bf16x8* row_rec;
+  bf16x8* col_rec;
+  float* alpha;
+  float* lw;
+  bf16x8* bias[2];
+  float* L;
+};
+
+struct Common {
   float2* part;
   unsigned* counters;
   double* centroid;
   float* shift;
-  size_t bytes;
 };
-
-struct Plans {
-  PassPlan f, g;
-};
-
-Plans make_plans(int64_t n, int64_t m, int64_t d) {
-  Plans p;
-  p.f = plan_valu_pass(n, m, (int)d);
-  p.g = plan_valu_pass(m, n, (int)d);
-  return p;
-}
 
 Side carve_side(Carve& c, int64_t cnt, int dp) {
   Side s;
@@ -105,49 +124,97 @@ Side carve_side(Carve& c, int64_t cnt, int dp) {
   return s;
 }
 
-SolveLayout layout_solve(void* ws, int64_t n, int64_t m, int64_t d, size_t part_elems_f2,
-                         int n_counters) {
+SideM carve_side_m(Carve& c, int64_t cnt, int nkb) {
+  SideM s;
+  s.row_rec = c.take<bf16x8>((size_t)cnt * nkb * 2);
+  s.col_rec = c.take<bf16x8>((size_t)cnt * nkb * 2);
+  s.alpha = c.take<float>(cnt);
+  s.lw = c.take<float>(cnt);
+  s.bias[0] = c.take<bf16x8>((size_t)cnt * 2);
+  s.bias[1] = c.take<bf16x8>((size_t)cnt * 2);
+  s.L = c.take<float>(cnt);
+  return s;
+}
+
+Common carve_common(Carve& c, size_t part_f2, int n_counters, int64_t d) {
+  Common k;
+  k.part = c.take<float2>(part_f2);
+  k.counters = c.take<unsigned>(n_counters > 0 ? n_counters : 1);
+  k.centroid = c.take<double>((size_t)kCentroidBlocks * 2 * d);
+  k.shift = c.take<float>(d);
+  return k;
+}
+
+size_t part_f2(const PassPlan& f, int64_t n, const PassPlan& g, int64_t m) {
+  const size_t pf = f.splits > 1 ? (size_t)f.splits * n : 0;
+  const size_t pg = g.splits > 1 ? (size_t)g.splits * m : 0;
+  return pf > pg ? pf : pg;
+}
+
+struct SolvePlan {
+  Path path;
+  int nkb;      // matrix-core records: K blocks per record
+  PassPlan f, g;
+};
+
+SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d) {
+  SolvePlan sp;
+  sp.path = solve_path(dtype, d);
+  sp.nkb = 0;
+  if (sp.path == Path::Mfma) {
+    sp.nkb = mfma_nkb(dtype, (int)d);
+    sp.f = plan_mfma_pass(n, m, sp.nkb);
+    sp.g = plan_mfma_pass(m, n, sp.nkb);
+  } else {
+    sp.f = plan_valu_pass(n, m, (int)d);
+    sp.g = plan_valu_pass(m, n, (int)d);
+  }
+  return sp;
+}
+
+struct SolveWs {
+  Side x, y;     // vector-ALU path
+  SideM xm, ym;  // matrix-core path
+  Common c;
+  size_t bytes;
+};
+
+SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_t d) {
   Carve c{static_cast<char*>(ws)};
-  SolveLayout L;
-  const int dp = valu_dp((int)d);
-  L.x = carve_side(c, n, dp);
-  L.y = carve_side(c, m, dp);
-  L.part = c.take<float2>(part_elems_f2);
-  L.counters = c.take<unsigned>(n_counters);
-  L.centroid = c.take<double>((size_t)kCentroidBlocks * 2 * d);
-  L.shift = c.take<float>(d);
+  SolveWs L{};
+  if (sp.path == Path::Mfma) {
+    L.xm = carve_side_m(c, n, sp.nkb);
+    L.ym = carve_side_m(c, m, sp.nkb);
+  } else {
+    L.x = carve_side(c, n, valu_dp((int)d));
+    L.y = carve_side(c, m, valu_dp((int)d));
+  }
+  const int ncnt = sp.f.row_blocks > sp.g.row_blocks ? sp.f.row_blocks : sp.g.row_blocks;
+  L.c = carve_common(c, part_f2(sp.f, n, sp.g, m), ncnt, d);
   L.bytes = c.off;
   return L;
 }
 
-size_t solve_part_elems(const Plans& p, int64_t n, int64_t m) {
-  const size_t pf = p.f.splits > 1 ? (size_t)p.f.splits * n : 0;
-  const size_t pg = p.g.splits > 1 ? (size_t)p.g.splits * m : 0;
-  return pf > pg ? pf : pg;
-}
-int n_counters_for(const Plans& p) { return p.f.row_blocks > p.g.row_blocks ? p.f.row_blocks : p.g.row_blocks; }
-
-size_t solve_bytes(int64_t n, int64_t m, int64_t d) {
-  const Plans p = make_plans(n, m, d);
-  return layout_solve(nullptr, n, m, d, solve_part_elems(p, n, m), n_counters_for(p)).bytes;
-}
-
-// Apply and gradient share the solve's side layout; their partial records are wider.
+// Gradient and transport application: vector-ALU layout plus wider partials.
 size_t wide_part_floats(const PassPlan& pl, int64_t nr, int64_t rec) {
   return pl.splits > 1 ? (size_t)pl.splits * nr * rec : 0;
 }
 
-size_t apply_bytes(int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
-  const int64_t nr = transpose ? m : n, nc = transpose ? n : m;
-  const PassPlan pl = plan_valu_pass(nr, nc, (int)d);
-  const size_t f2 = (wide_part_floats(pl, nr, k) + 1) / 2;
-  return layout_solve(nullptr, n, m, d, f2, pl.row_blocks).bytes;
-}
+struct AuxWs {
+  Side x, y;
+  Common c;
+  size_t bytes;
+};
 
-size_t grad_bytes(int64_t n, int64_t m, int64_t d) {
-  const PassPlan pl = plan_valu_pass(n, m, (int)d);
-  const size_t f2 = (wide_part_floats(pl, n, 2 + d) + 1) / 2;
-  return layout_solve(nullptr, n, m, d, f2, pl.row_blocks).bytes;
+AuxWs layout_aux(void* ws, int64_t n, int64_t m, int64_t d, const PassPlan& pl, int64_t nr,
+                 int64_t rec) {
+  Carve c{static_cast<char*>(ws)};
+  AuxWs L{};
+  L.x = carve_side(c, n, valu_dp((int)d));
+  L.y = carve_side(c, m, valu_dp((int)d));
+  L.c = carve_common(c, (wide_part_floats(pl, nr, rec) + 1) / 2, pl.row_blocks, d);
+  L.bytes = c.off;
+  return L;
 }
 
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -158,24 +225,89 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 struct Scalars {
-  float c2, neg_eps_ln2, log2e_over_eps;
+  float c2, inv_c2, neg_eps_ln2, log2e_over_eps;
 };
 Scalars scalars(double eps) {
   Scalars s;
   s.c2 = (float)(2.0 * 1.4426950408889634 / eps);
+  s.inv_c2 = (float)(eps / (2.0 * 1.4426950408889634));
   s.neg_eps_ln2 = (float)(-eps * 0.6931471805599453);
   s.log2e_over_eps = (float)(1.4426950408889634 / eps);
   return s;
 }
 
-hipError_t prep_sides(const SolveLayout& L, const void* x, const void* y, int dtype, int64_t n,
-                      int64_t m, int64_t d, const float* a, const float* b, const float* f_start,
-                      const float* g_start, float* f_zero, float* g_zero, bool center,
-                      int n_counters, const Scalars& sc, hipStream_t s) {
-  PrepSide px{x, a, f_start, f_zero, L.x.pts, L.x.alpha, L.x.lw, L.x.h[0], n};
-  PrepSide py{y, b, g_start, g_zero, L.y.pts, L.y.alpha, L.y.lw, L.y.h[0], m};
-  return launch_prep(px, py, dtype, (int)d, valu_dp((int)d), center, L.centroid, L.shift,
-                     L.counters, n_counters, sc.log2e_over_eps, s);
+hipError_t prep_valu(const Side& X, const Side& Y, const Common& C, const void* x, const void* y,
+                     int dtype, int64_t n, int64_t m, int64_t d, const float* a, const float* b,
+                     const float* f_start, const float* g_start, float* f_zero, float* g_zero,
+                     bool center, int n_counters, const Scalars& sc, hipStream_t s) {
+  PrepSide px{x, a, f_start, f_zero, X.pts, X.alpha, X.lw, X.h[0], n};
+  PrepSide py{y, b, g_start, g_zero, Y.pts, Y.alpha, Y.lw, Y.h[0], m};
+  return launch_prep(px, py, dtype, (int)d, valu_dp((int)d), center, C.centroid, C.shift,
+                     C.counters, n_counters, sc.log2e_over_eps, s);
+}
+
+int solve_valu(const SolveWs& L, const SolvePlan& sp, int64_t n, int64_t m, int64_t d,
+               int iters, bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
+  int cur = 0;
+  hipError_t e;
+  for (int t = 0; t < iters; ++t) {
+    const int nxt = sym ? 1 - cur : cur;
+    PassArgs pf{};
+    pf.rows = L.x.pts; pf.cols = L.y.pts; pf.hcol = L.y.h[cur];
+    pf.alpha = L.x.alpha; pf.lw = L.x.lw; pf.pot = f; pf.hout = L.x.h[nxt]; pf.Lout = L.x.L;
+    pf.part = L.c.part; pf.counters = L.c.counters; pf.nr = (int)n; pf.nc = (int)m;
+    pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
+    pf.c2 = sc.c2; pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps;
+    pf.symmetric = sym;
+    if ((e = launch_lse_valu(pf, (int)d, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
+    PassArgs pg = pf;
+    pg.rows = L.y.pts; pg.cols = L.x.pts; pg.hcol = L.x.h[cur];  // alternating: the new f's bias
+    pg.alpha = L.y.alpha; pg.lw = L.y.lw; pg.pot = g; pg.hout = L.y.h[nxt]; pg.Lout = L.y.L;
+    pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
+    if ((e = launch_lse_valu(pg, (int)d, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
+    cur = nxt;
+  }
+  return SK_OK;
+}
+
+int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int64_t m, int iters,
+               bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
+  int cur = 0;
+  hipError_t e;
+  for (int t = 0; t < iters; ++t) {
+    const int nxt = sym ? 1 - cur : cur;
+    MfmaPassArgs pf{};
+    pf.rows = L.xm.row_rec; pf.cols = L.ym.col_rec; pf.bias_col = L.ym.bias[cur];
+    pf.alpha = L.xm.alpha; pf.lw = L.xm.lw; pf.pot = f; pf.bias_out = L.xm.bias[nxt];
+    pf.Lout = L.xm.L; pf.part = L.c.part; pf.counters = L.c.counters;
+    pf.nr = (int)n; pf.nc = (int)m; pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
+    pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
+    pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
+    if ((e = launch_lse_mfma(pf, sp.nkb, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
+    MfmaPassArgs pg = pf;
+    pg.rows = L.ym.row_rec; pg.cols = L.xm.col_rec; pg.bias_col = L.xm.bias[cur];
+    pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt]; pg.Lout = L.ym.L;
+    pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
+    if ((e = launch_lse_mfma(pg, sp.nkb, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
+    cur = nxt;
+  }
+  return SK_OK;
+}
+
+size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  const SolvePlan sp = plan_solve(dtype, n, m, d);
+  return layout_solve(nullptr, sp, n, m, d).bytes;
+}
+
+size_t apply_bytes(int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
+  const int64_t nr = transpose ? m : n, nc = transpose ? n : m;
+  const PassPlan pl = plan_valu_pass(nr, nc, (int)d);
+  return layout_aux(nullptr, n, m, d, pl, nr, k).bytes;
+}
+
+size_t grad_bytes(int64_t n, int64_t m, int64_t d) {
+  const PassPlan pl = plan_valu_pass(n, m, (int)d);
+  return layout_aux(nullptr, n, m, d, pl, n, 2 + valu_dclass((int)d)).bytes;
 }
 
 }  // namespace
@@ -191,15 +323,19 @@ const char* sk_last_error(void) { return g_err; }
 
 size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, int64_t k) {
   if (n < 1 || m < 1 || d < 1 || n > kMaxRows || m > kMaxRows) return 0;
-  if (choose_path(dtype, d) == Path::None) return 0;
+  if (dtype != SK_F32 && dtype != SK_BF16) return 0;
   switch (op) {
-    case SK_OP_SOLVE: return solve_bytes(n, m, d);
+    case SK_OP_SOLVE:
+      if (solve_path(dtype, d) == Path::None) return 0;
+      return solve_bytes(dtype, n, m, d);
     case SK_OP_APPLY: {
-      if (k < 1 || k > 64) return 0;
+      if (aux_path(dtype, d) == Path::None || k < 1 || k > 64) return 0;
       const size_t a0 = apply_bytes(n, m, d, k, 0), a1 = apply_bytes(n, m, d, k, 1);
       return a0 > a1 ? a0 : a1;
     }
-    case SK_OP_GRAD: return grad_bytes(n, m, d);
+    case SK_OP_GRAD:
+      if (aux_path(dtype, d) == Path::None) return 0;
+      return grad_bytes(n, m, d);
     default: return 0;
   }
 }
@@ -209,45 +345,39 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
                       uint32_t flags, float* f, float* g, double* cost, void* ws, size_t ws_bytes,
                       void* stream) {
   g_err[0] = 0;
-  int rc = check_common(x, y, dtype, n, m, d, a, b, eps);
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, solve_path(dtype, d));
   if (rc) return rc;
   if (!f || !g || !cost) return fail(SK_ERR_INVALID_ARG, "null output pointer");
   if (iters < 0) return fail(SK_ERR_INVALID_ARG, "iters must be >= 0");
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
   if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
-  const Plans pl = make_plans(n, m, d);
-  const int ncnt = n_counters_for(pl);
-  const size_t need = layout_solve(nullptr, n, m, d, solve_part_elems(pl, n, m), ncnt).bytes;
+  const SolvePlan sp = plan_solve(dtype, n, m, d);
+  const size_t need = layout_solve(nullptr, sp, n, m, d).bytes;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const SolveLayout L = layout_solve(ws, n, m, d, solve_part_elems(pl, n, m), ncnt);
+  const SolveWs L = layout_solve(ws, sp, n, m, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Scalars sc = scalars(eps);
   const bool warm = (flags & SK_WARM_START) != 0;
   const bool center = (flags & SK_NO_CENTER) == 0;
-
-  hipError_t e = prep_sides(L, x, y, dtype, n, m, d, a, b, warm ? f : nullptr,
-                            warm ? g : nullptr, warm ? nullptr : f, warm ? nullptr : g, center,
-                            ncnt, sc, s);
-  if (e != hipSuccess) return hip_fail(e, "prep");
-
   const bool sym = (mode == SK_SYMMETRIC);
-  int cur = 0;
-  for (int t = 0; t < iters; ++t) {
-    const int nxt = sym ? 1 - cur : cur;
-    PassArgs pf{};
-    pf.rows = L.x.pts; pf.cols = L.y.pts; pf.hcol = L.y.h[cur];
-    pf.alpha = L.x.alpha; pf.lw = L.x.lw; pf.pot = f; pf.hout = L.x.h[nxt]; pf.Lout = L.x.L;
-    pf.part = L.part; pf.counters = L.counters; pf.nr = (int)n; pf.nc = (int)m;
-    pf.splits = pl.f.splits; pf.cols_per_split = pl.f.cols_per_split;
-    pf.c2 = sc.c2; pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps;
-    pf.symmetric = sym;
-    if ((e = launch_lse_valu(pf, (int)d, pl.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
-    PassArgs pg = pf;
-    pg.rows = L.y.pts; pg.cols = L.x.pts; pg.hcol = L.x.h[cur];  // alternating: the new f's bias
-    pg.alpha = L.y.alpha; pg.lw = L.y.lw; pg.pot = g; pg.hout = L.y.h[nxt]; pg.Lout = L.y.L;
-    pg.nr = (int)m; pg.nc = (int)n; pg.splits = pl.g.splits; pg.cols_per_split = pl.g.cols_per_split;
-    if ((e = launch_lse_valu(pg, (int)d, pl.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
-    cur = nxt;
+  const int ncnt = sp.f.row_blocks > sp.g.row_blocks ? sp.f.row_blocks : sp.g.row_blocks;
+  const float* f_start = warm ? f : nullptr;
+  const float* g_start = warm ? g : nullptr;
+  float* f_zero = warm ? nullptr : f;
+  float* g_zero = warm ? nullptr : g;
+  hipError_t e;
+  if (sp.path == Path::Mfma) {
+    MfmaPrepSide px{x, a, f_start, f_zero, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw, L.xm.bias[0], n};
+    MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw, L.ym.bias[0], m};
+    e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, center, L.c.centroid, L.c.shift,
+                         L.c.counters, ncnt, sc.log2e_over_eps, sc.c2, s);
+    if (e != hipSuccess) return hip_fail(e, "prep");
+    if ((rc = solve_mfma(L, sp, dtype, n, m, iters, sym, f, g, sc, s))) return rc;
+  } else {
+    e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, f_start, g_start, f_zero, g_zero,
+                  center, ncnt, sc, s);
+    if (e != hipSuccess) return hip_fail(e, "prep");
+    if ((rc = solve_valu(L, sp, n, m, d, iters, sym, f, g, sc, s))) return rc;
   }
   if ((e = launch_cost(a, f, n, b, g, m, cost, s)) != hipSuccess) return hip_fail(e, "cost");
   return SK_OK;
@@ -258,7 +388,7 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
                        int transpose, const float* V, int64_t k, float* out, void* ws,
                        size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  int rc = check_common(x, y, dtype, n, m, d, a, b, eps);
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
   if (rc) return rc;
   if (!f || !g || !V || !out) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
   if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
@@ -266,20 +396,19 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
   if (k > 64) return fail(SK_ERR_UNSUPPORTED, "k=%lld > 64 is not supported", (long long)k);
   const int64_t nr = transpose ? m : n, nc = transpose ? n : m;
   const PassPlan pl = plan_valu_pass(nr, nc, (int)d);
-  const size_t f2 = (wide_part_floats(pl, nr, k) + 1) / 2;
-  const size_t need = layout_solve(nullptr, n, m, d, f2, pl.row_blocks).bytes;
+  const size_t need = layout_aux(nullptr, n, m, d, pl, nr, k).bytes;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const SolveLayout L = layout_solve(ws, n, m, d, f2, pl.row_blocks);
+  const AuxWs L = layout_aux(ws, n, m, d, pl, nr, k);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Scalars sc = scalars(eps);
-  hipError_t e = prep_sides(L, x, y, dtype, n, m, d, a, b, f, g, nullptr, nullptr, true,
-                            pl.row_blocks, sc, s);
+  hipError_t e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, f, g, nullptr, nullptr, true,
+                           pl.row_blocks, sc, s);
   if (e != hipSuccess) return hip_fail(e, "prep");
   const Side& R = transpose ? L.y : L.x;
   const Side& Cs = transpose ? L.x : L.y;
   ApplyArgs aa{};
   aa.rows = R.pts; aa.cols = Cs.pts; aa.hrow = R.h[0]; aa.hcol = Cs.h[0]; aa.V = V; aa.out = out;
-  aa.part = reinterpret_cast<float*>(L.part); aa.counters = L.counters;
+  aa.part = reinterpret_cast<float*>(L.c.part); aa.counters = L.c.counters;
   aa.nr = (int)nr; aa.nc = (int)nc; aa.k = (int)k; aa.splits = pl.splits;
   aa.cols_per_split = pl.cols_per_split; aa.c2 = sc.c2;
   if ((e = launch_apply_valu(aa, (int)d, pl, s)) != hipSuccess) return hip_fail(e, "apply");
@@ -290,22 +419,22 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
                   const float* a, const float* b, const float* g, double eps, float* grad_x,
                   void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  int rc = check_common(x, y, dtype, n, m, d, a, b, eps);
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
   if (rc) return rc;
   if (!g || !grad_x) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
   const PassPlan pl = plan_valu_pass(n, m, (int)d);
-  const size_t f2 = (wide_part_floats(pl, n, 2 + d) + 1) / 2;
-  const size_t need = layout_solve(nullptr, n, m, d, f2, pl.row_blocks).bytes;
+  const int64_t rec = 2 + valu_dclass((int)d);
+  const size_t need = layout_aux(nullptr, n, m, d, pl, n, rec).bytes;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const SolveLayout L = layout_solve(ws, n, m, d, f2, pl.row_blocks);
+  const AuxWs L = layout_aux(ws, n, m, d, pl, n, rec);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Scalars sc = scalars(eps);
-  hipError_t e = prep_sides(L, x, y, dtype, n, m, d, a, b, nullptr, g, nullptr, nullptr, true,
-                            pl.row_blocks, sc, s);
+  hipError_t e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, nullptr, g, nullptr, nullptr,
+                           true, pl.row_blocks, sc, s);
   if (e != hipSuccess) return hip_fail(e, "prep");
   GradArgs ga{};
   ga.rows = L.x.pts; ga.cols = L.y.pts; ga.hcol = L.y.h[0]; ga.wrow = a; ga.out = grad_x;
-  ga.part = reinterpret_cast<float*>(L.part); ga.counters = L.counters;
+  ga.part = reinterpret_cast<float*>(L.c.part); ga.counters = L.c.counters;
   ga.nr = (int)n; ga.nc = (int)m; ga.d = (int)d; ga.splits = pl.splits;
   ga.cols_per_split = pl.cols_per_split; ga.c2 = sc.c2;
   if ((e = launch_grad_valu(ga, pl, s)) != hipSuccess) return hip_fail(e, "grad");

@@ -1,4 +1,5 @@
-// pass_valu.hip -- vector-ALU passes for small dimension (1 <= d <= 16).
+// pass_valu.hip -- vector-ALU passes for small dimension (1 <= d <= 64; d > 16 is
+// served by the padded classes 32 and 64).
 //
 // One half-pass of the stabilized log-domain Sinkhorn update, evaluated as a
 // row-wise log-sum-exp of biased dot-product scores that are formed on the fly
@@ -20,7 +21,11 @@
 namespace sk {
 namespace {
 
-constexpr int kChunk = 8;
+// Columns per online-max refresh: the chunk's column points are wave-uniform
+// (scalar) registers, so the chunk shrinks as d grows.
+template <int D>
+constexpr int chunk_for() { return D <= 4 ? 8 : (D <= 8 ? 4 : (D <= 16 ? 2 : 1)); }
+constexpr int kChunkMax = 8;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -71,6 +76,7 @@ __device__ __forceinline__ void load_col(const float* __restrict__ cols, int j, 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_lse_valu(const PassArgs p) {
   constexpr int DP = (D + 3) & ~3;
+  constexpr int kChunk = chunk_for<D>();
   const float* __restrict__ rows = static_cast<const float*>(p.rows);
   const float* __restrict__ cols = static_cast<const float*>(p.cols);
   const float* __restrict__ hcol = p.hcol;
@@ -141,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(const PassArgs p) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_grad_valu(const GradArgs p) {
   constexpr int DP = (D + 3) & ~3;
+  constexpr int kChunk = chunk_for<D>();
   const float* __restrict__ rows = static_cast<const float*>(p.rows);
   const float* __restrict__ cols = static_cast<const float*>(p.cols);
   const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void k_grad_valu(const GradArgs p) {
     const float tw = 2.0f * p.wrow[i];
 #pragma unroll
     for (int k = 0; k < D; ++k)
-      p.out[(int64_t)i * p.d + k] = tw * (rows[(int64_t)i * DP + k] - Ov[k] * inv);
+      if (k < p.d) p.out[(int64_t)i * p.d + k] = tw * (rows[(int64_t)i * DP + k] - Ov[k] * inv);
   };
   if (p.splits == 1) {
     if (i < p.nr) finish(S, O);
@@ -294,7 +301,10 @@ hipError_t dispatch_d(int d, A&&... args) {
     SK_CASE(1) SK_CASE(2) SK_CASE(3) SK_CASE(4) SK_CASE(5) SK_CASE(6) SK_CASE(7) SK_CASE(8)
     SK_CASE(9) SK_CASE(10) SK_CASE(11) SK_CASE(12) SK_CASE(13) SK_CASE(14) SK_CASE(15) SK_CASE(16)
 #undef SK_CASE
-    default: return hipErrorInvalidValue;
+    default:
+      if (d <= 32) return Fn<32>::run(args...);
+      if (d <= 64) return Fn<64>::run(args...);
+      return hipErrorInvalidValue;
   }
 }
 
@@ -326,7 +336,8 @@ struct ApplyRun {
 
 }  // namespace
 
-int valu_dp(int d) { return (d + 3) & ~3; }
+int valu_dclass(int d) { return d <= 16 ? d : (d <= 32 ? 32 : 64); }
+int valu_dp(int d) { return (valu_dclass(d) + 3) & ~3; }
 
 PassPlan plan_valu_pass(int64_t nr, int64_t nc, int d) {
   (void)d;
@@ -341,7 +352,7 @@ PassPlan plan_valu_pass(int64_t nr, int64_t nc, int d) {
   if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
   pl.cols_per_split = (int)((nc + splits - 1) / splits);
-  pl.cols_per_split = (pl.cols_per_split + kChunk - 1) / kChunk * kChunk;
+  pl.cols_per_split = (pl.cols_per_split + kChunkMax - 1) / kChunkMax * kChunkMax;
   pl.splits = (int)((nc + pl.cols_per_split - 1) / pl.cols_per_split);
   return pl;
 }

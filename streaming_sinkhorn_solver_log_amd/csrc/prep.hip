@@ -82,6 +82,11 @@ __global__ __launch_bounds__(256) void k_prep_f32(PrepSide xs, PrepSide ys, int 
   s.h[r] = kLog2e * lw + (pot - nrm) * log2e_over_eps;
 }
 
+__global__ __launch_bounds__(256) void k_zero_u32(unsigned* p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0u;
+}
+
 // cost = sum_i a_i f_i + sum_j b_j g_j in float64, one workgroup, fixed order.
 __global__ __launch_bounds__(1024) void k_cost(const float* a, const float* f, int64_t n,
                                                const float* b, const float* g, int64_t m,
@@ -101,14 +106,22 @@ __global__ __launch_bounds__(1024) void k_cost(const float* a, const float* f, i
 
 }  // namespace
 
+hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, int dtype, int d,
+                           double* centroid_part, float* shift, hipStream_t s) {
+  k_centroid_partial<<<kCentroidBlocks, 256, 0, s>>>(x, n, y, m, dtype, d, centroid_part);
+  k_centroid_final<<<1, 256, 0, s>>>(centroid_part, kCentroidBlocks, n, m, d, shift);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(unsigned* p, int64_t count, hipStream_t s) {
+  if (count > 0) k_zero_u32<<<(int)((count + 255) / 256), 256, 0, s>>>(p, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep(const PrepSide& xs, const PrepSide& ys, int dtype, int d, int dp,
                        bool center, double* centroid_part, float* shift, unsigned* counters,
                        int n_counters, float log2e_over_eps, hipStream_t s) {
-  if (center) {
-    k_centroid_partial<<<kCentroidBlocks, 256, 0, s>>>(xs.pts, xs.n, ys.pts, ys.n, dtype, d,
-                                                       centroid_part);
-    k_centroid_final<<<1, 256, 0, s>>>(centroid_part, kCentroidBlocks, xs.n, ys.n, d, shift);
-  }
+  if (center) (void)launch_centroid(xs.pts, xs.n, ys.pts, ys.n, dtype, d, centroid_part, shift, s);
   const int64_t total = xs.n + ys.n;
   const int64_t work = total > n_counters ? total : n_counters;
   const int blocks = (int)((work + 255) / 256);

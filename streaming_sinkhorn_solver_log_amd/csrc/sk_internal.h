@@ -84,7 +84,8 @@ struct PassPlan {
 };
 
 PassPlan plan_valu_pass(int64_t nr, int64_t nc, int d);
-int valu_dp(int d);
+int valu_dclass(int d);  // template dimension of the VALU kernels serving d (d <= 64)
+int valu_dp(int d);      // row stride of their packed float32 points
 
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_lse_valu(const PassArgs& a, int d, const PassPlan& pl, hipStream_t s);
@@ -107,6 +108,9 @@ struct PrepSide {
 hipError_t launch_prep(const PrepSide& xs, const PrepSide& ys, int dtype, int d, int dp,
                        bool center, double* centroid_part, float* shift, unsigned* counters,
                        int n_counters, float log2e_over_eps, hipStream_t s);
+hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, int dtype, int d,
+                           double* centroid_part, float* shift, hipStream_t s);
+hipError_t launch_zero_u32(unsigned* p, int64_t count, hipStream_t s);
 hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
                        int64_t m, double* cost, hipStream_t s);
 

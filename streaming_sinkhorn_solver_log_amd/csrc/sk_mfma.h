@@ -1,0 +1,59 @@
+// sk_mfma.h -- types and arguments of the matrix-core passes (library-internal).
+#pragma once
+
+#include "sk_internal.h"
+
+namespace sk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One half-pass on the matrix cores. Records are NKB * 32 bytes per point; a
+// bias record is two bf16x8 (half 0: the three bf16 parts of h~ = h / c2).
+struct MfmaPassArgs {
+  const void* rows;        // nr row-form records
+  const void* cols;        // nc column-form records
+  const bf16x8* bias_col;  // nc bias records of the columns
+  const float* alpha;      // nr squared norms of the rows
+  const float* lw;         // nr natural-log row weights
+  float* pot;              // nr potentials, updated in place
+  bf16x8* bias_out;        // nr bias records for the next pass of the other side
+  float* Lout;             // nr log2-sum-exp values (may be null)
+  float2* part;            // split partials (M, S) in log2 units: [split][nr]
+  unsigned* counters;      // one per row block, zero on entry and exit
+  int nr, nc;
+  int splits, cols_per_split;
+  // Exponent of a pair in log2 units = escale * (acc - M). float32 points have
+  // c2 folded into their row records (escale = 1, biases in log2 units); bf16
+  // points keep exact records (escale = c2, biases stored divided by c2).
+  float escale, bias_scale, neg_eps_ln2, log2e_over_eps;
+  int symmetric;
+};
+
+struct MfmaPrepSide {
+  const void* pts;   // n x d as stored
+  const float* w;    // weights
+  const float* pot;  // starting potential (null: zeros)
+  float* pot_zero;   // written with zeros if non-null
+  bf16x8* row_rec;   // n records (row form)
+  bf16x8* col_rec;   // n records (column form)
+  float* alpha;
+  float* lw;
+  bf16x8* bias;      // n bias records of the starting potential
+  int64_t n;
+};
+
+int mfma_nkb(int dtype, int d);  // K blocks per record, 0 if the resident kernel does not serve d
+int mfma_rb(int nkb);
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb);
+hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, const PassPlan& pl, hipStream_t s);
+hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
+                            int nkb, bool center, double* centroid_part, float* shift,
+                            unsigned* counters, int n_counters, float log2e_over_eps,
+                            float c2, hipStream_t s);
+// escale and bias_scale of a storage type (see MfmaPassArgs).
+inline float mfma_escale(int dtype, float c2) { return dtype == 1 ? c2 : 1.0f; }
+inline float mfma_bias_scale(int dtype, float c2) { return dtype == 1 ? 1.0f / c2 : 1.0f; }
+
+}  // namespace sk

@@ -74,6 +74,8 @@ SOLVE_CASES = [
     (1, 1, 700, 5),
     (1, 700, 1, 5),
     (1, 257, 4099, 10),
+    (3, 2000, 1500, 20),          # bf16 points, d = 64, Dirichlet weights
+    (3, 129, 2111, 5),
 ]
 
 
@@ -91,6 +93,24 @@ def test_solve_matches_oracle(sk, key, n, m, iters):
     say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} tol={tol_pot(w, fr):.3e} cost {float(cost):.9g} vs {cr:.9g}")
     assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
     assert abs(float(cost) - cr) <= tol_rel(w) * max(abs(cr), 1e-30)
+
+
+CUSTOM_DIMS = [("f32", 16), ("f32", 20), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7)]
+
+
+@pytest.mark.parametrize("dtype,d", CUSTOM_DIMS)
+def test_solve_other_dimensions(sk, dtype, d):
+    from dataclasses import replace
+    w = replace(W.CONFIGS[4], d=d, dtype=dtype, eps=0.2, name=f"gauss_d{d}_{dtype}").scaled(900, 1100, 10)
+    say(f"solve d={d} {dtype}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    ef, eg = np.abs(f.cpu().numpy() - fr).max(), np.abs(g.cpu().numpy() - gr).max()
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} tol={tol_pot(w, fr):.3e}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
 
 
 def test_solve_bf16_points_small_d(sk):
