@@ -61,6 +61,16 @@ bool force_valu() {
   return v;
 }
 
+// FLASHSK_DEBUG=1: after each matrix-core solve, synchronize the stream and
+// report how many workgroups fell back to the exact sweep.
+bool debug_enabled() {
+  static const bool v = [] {
+    const char* e = getenv("FLASHSK_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return v;
+}
+
 Path solve_path(int dtype, int64_t d) {
   if (d < 1) return Path::None;
   if (!force_valu() && d <= 1024 && mfma_nkb(dtype, (int)d) > 0) return Path::Mfma;
@@ -103,12 +113,15 @@ struct SideM {
   float* alpha;
   float* lw;
   bf16x8* bias[2];
+  float* hval[2];
+  float* dmax[2];
   float* L;
 };
 
 struct Common {
   float2* part;
   unsigned* counters;
+  unsigned* exact_count;
   double* centroid;
   float* shift;
 };
@@ -124,14 +137,19 @@ Side carve_side(Carve& c, int64_t cnt, int dp) {
   return s;
 }
 
-SideM carve_side_m(Carve& c, int64_t cnt, int nkb) {
+SideM carve_side_m(Carve& c, int64_t cnt, int nkb, int row_blocks) {
   SideM s;
+  const int64_t padded = mfma_padded_count(cnt);
   s.row_rec = c.take<bf16x8>((size_t)cnt * nkb * 2);
-  s.col_rec = c.take<bf16x8>((size_t)cnt * nkb * 2);
+  s.col_rec = c.take<bf16x8>((size_t)padded * nkb * 2);
   s.alpha = c.take<float>(cnt);
   s.lw = c.take<float>(cnt);
-  s.bias[0] = c.take<bf16x8>((size_t)cnt * 2);
-  s.bias[1] = c.take<bf16x8>((size_t)cnt * 2);
+  s.bias[0] = c.take<bf16x8>((size_t)padded * 2);
+  s.bias[1] = c.take<bf16x8>((size_t)padded * 2);
+  s.hval[0] = c.take<float>(cnt);
+  s.hval[1] = c.take<float>(cnt);
+  s.dmax[0] = c.take<float>(row_blocks);
+  s.dmax[1] = c.take<float>(row_blocks);
   s.L = c.take<float>(cnt);
   return s;
 }
@@ -139,7 +157,8 @@ SideM carve_side_m(Carve& c, int64_t cnt, int nkb) {
 Common carve_common(Carve& c, size_t part_f2, int n_counters, int64_t d) {
   Common k;
   k.part = c.take<float2>(part_f2);
-  k.counters = c.take<unsigned>(n_counters > 0 ? n_counters : 1);
+  k.counters = c.take<unsigned>((n_counters > 0 ? n_counters : 1) + 1);
+  k.exact_count = k.counters + (n_counters > 0 ? n_counters : 1);
   k.centroid = c.take<double>((size_t)kCentroidBlocks * 2 * d);
   k.shift = c.take<float>(d);
   return k;
@@ -183,8 +202,8 @@ SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_
   Carve c{static_cast<char*>(ws)};
   SolveWs L{};
   if (sp.path == Path::Mfma) {
-    L.xm = carve_side_m(c, n, sp.nkb);
-    L.ym = carve_side_m(c, m, sp.nkb);
+    L.xm = carve_side_m(c, n, sp.nkb, sp.f.row_blocks);
+    L.ym = carve_side_m(c, m, sp.nkb, sp.g.row_blocks);
   } else {
     L.x = carve_side(c, n, valu_dp((int)d));
     L.y = carve_side(c, m, valu_dp((int)d));
@@ -274,21 +293,29 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
                bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
   int cur = 0;
   hipError_t e;
+  const bool scaled = dtype == SK_BF16;
   for (int t = 0; t < iters; ++t) {
     const int nxt = sym ? 1 - cur : cur;
+    // Each side's first pass has no previous log-sum-exp to shift by: exact sweep.
+    const bool shifted = t > 0;
     MfmaPassArgs pf{};
     pf.rows = L.xm.row_rec; pf.cols = L.ym.col_rec; pf.bias_col = L.ym.bias[cur];
     pf.alpha = L.xm.alpha; pf.lw = L.xm.lw; pf.pot = f; pf.bias_out = L.xm.bias[nxt];
-    pf.Lout = L.xm.L; pf.part = L.c.part; pf.counters = L.c.counters;
+    pf.Lout = L.xm.L; pf.Lin = L.xm.L; pf.hval_in = L.xm.hval[cur]; pf.hval_out = L.xm.hval[nxt];
+    pf.dmax_in = L.ym.dmax[cur]; pf.n_dmax_in = sp.g.row_blocks; pf.dmax_out = L.xm.dmax[nxt];
+    pf.exact_count = L.c.exact_count;
+    pf.part = L.c.part; pf.counters = L.c.counters;
     pf.nr = (int)n; pf.nc = (int)m; pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
     pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
     pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
-    if ((e = launch_lse_mfma(pf, sp.nkb, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
+    if ((e = launch_lse_mfma(pf, sp.nkb, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
     MfmaPassArgs pg = pf;
     pg.rows = L.ym.row_rec; pg.cols = L.xm.col_rec; pg.bias_col = L.xm.bias[cur];
-    pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt]; pg.Lout = L.ym.L;
+    pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt];
+    pg.Lout = L.ym.L; pg.Lin = L.ym.L; pg.hval_in = L.ym.hval[cur]; pg.hval_out = L.ym.hval[nxt];
+    pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
-    if ((e = launch_lse_mfma(pg, sp.nkb, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
+    if ((e = launch_lse_mfma(pg, sp.nkb, shifted, scaled, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
     cur = nxt;
   }
   return SK_OK;
@@ -367,12 +394,22 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   float* g_zero = warm ? nullptr : g;
   hipError_t e;
   if (sp.path == Path::Mfma) {
-    MfmaPrepSide px{x, a, f_start, f_zero, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw, L.xm.bias[0], n};
-    MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw, L.ym.bias[0], m};
+    MfmaPrepSide px{x, a, f_start, f_zero, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw,
+                    L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
+    MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw,
+                    L.ym.bias[0], L.ym.bias[1], L.ym.hval[0], m};
+    // counters and the exact-fallback count are zeroed together (adjacent)
     e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, center, L.c.centroid, L.c.shift,
-                         L.c.counters, ncnt, sc.log2e_over_eps, sc.c2, s);
+                         L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);
     if (e != hipSuccess) return hip_fail(e, "prep");
     if ((rc = solve_mfma(L, sp, dtype, n, m, iters, sym, f, g, sc, s))) return rc;
+    if (debug_enabled()) {
+      unsigned cnt = 0;
+      if (hipMemcpyAsync(&cnt, L.c.exact_count, sizeof(cnt), hipMemcpyDeviceToHost, s) == hipSuccess &&
+          hipStreamSynchronize(s) == hipSuccess)
+        fprintf(stderr, "[flashsk] solve n=%lld m=%lld d=%lld iters=%d: %u workgroup(s) used the exact fallback\n",
+                (long long)n, (long long)m, (long long)d, iters, cnt);
+    }
   } else {
     e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, f_start, g_start, f_zero, g_zero,
                   center, ncnt, sc, s);

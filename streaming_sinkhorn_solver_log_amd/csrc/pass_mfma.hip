@@ -32,18 +32,18 @@
 // (s mod 8) of K block (s / 8) mod NKB in half s / (8 NKB): each lane loads its
 // half of a record with contiguous 16-byte loads.
 //
-// Column records (and their bias blocks) are staged through LDS, double
-// buffered, 64 columns per stage; each wave keeps RB blocks of 32 row records
-// in registers for the whole pass.
+// Each wave keeps RB blocks of 32 row records in registers for the whole pass
+// and streams the column records of its range from memory.
 #include "sk_internal.h"
 #include "sk_mfma.h"
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace sk {
 namespace {
 
-constexpr int kStageCols = 64;
 constexpr float kMaskedBias = -1.0e30f;  // bias of a column that contributes nothing
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -73,7 +73,8 @@ __device__ __forceinline__ void split3(float v, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)(r1 - (float)mid);
 }
 
-// Bias record of one column: half 0 = (hi, mid, lo, 0...), half 1 = zeros.
+// Bias record of one column: half 0 = (hi, mid, lo, 1, 1, 1, 0, 0), half 1 = zeros.
+// The three ones meet the row side's (-M) parts in the shifted sweep.
 __device__ __forceinline__ void write_bias_record(bf16x8* rec, float htilde) {
   float v = htilde < kMaskedBias ? kMaskedBias : htilde;  // -inf (zero weight) -> masked; NaN kept
   bf16x8 h0 = {}, h1 = {};
@@ -82,22 +83,44 @@ __device__ __forceinline__ void write_bias_record(bf16x8* rec, float htilde) {
   h0[0] = a;
   h0[1] = b;
   h0[2] = c;
+  h0[3] = (__bf16)1.0f;
+  h0[4] = (__bf16)1.0f;
+  h0[5] = (__bf16)1.0f;
   rec[0] = h0;
   rec[1] = h1;
 }
 
-__device__ __forceinline__ void finish_row_mfma(const MfmaPassArgs& p, int i, float L) {
+// Row-side bias block: (1, 1, 1, -M parts) in half 0, zeros in half 1.
+__device__ __forceinline__ bf16x8 row_aug(int half, float neg_m) {
+  bf16x8 r = {};
+  if (half == 0) {
+    r[0] = (__bf16)1.0f;
+    r[1] = (__bf16)1.0f;
+    r[2] = (__bf16)1.0f;
+    __bf16 a, b, c;
+    split3(neg_m, a, b, c);
+    r[3] = a;
+    r[4] = b;
+    r[5] = c;
+  }
+  return r;
+}
+
+// Potential update of row i from its log2-sum-exp L; returns the change of the
+// row's bias (log2 units) since the previous pass of this side.
+__device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, float L) {
   const float al = p.alpha[i];
   float v = fmaf(p.neg_eps_ln2, L, al);
   if (p.symmetric) v = 0.5f * (p.pot[i] + v);
   p.pot[i] = v;
   const float h = fmaf(kLog2e, p.lw[i], (v - al) * p.log2e_over_eps);
   write_bias_record(p.bias_out + 2 * (int64_t)i, h * p.bias_scale);
-  if (p.Lout) p.Lout[i] = L;
+  const float dh = h - p.hval_in[i];
+  p.hval_out[i] = h;
+  p.Lout[i] = L;
+  return dh;
 }
 
-// Online update of a lane's running (M, S) with one 32x32 tile (16 scores per lane).
-// M is in accumulator units; the exponent of a score is e * (acc - M).
 // max(a, b, c) in one instruction. Written as inline assembly because the
 // compiler otherwise quiets each MFMA result before a max (IEEE mode), which
 // costs an extra instruction per score; a NaN score still reaches the sum
@@ -108,8 +131,9 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
-__device__ __forceinline__ void lse_update(const f32x16& acc, float c2, float& M, float& S) {
-  // c2 here is the exponent scale e
+// Online update of a lane's running (M, S) with one 32x32 tile (16 scores per lane).
+// M is in accumulator units; the exponent of a score is e * (acc - M).
+__device__ __forceinline__ void lse_update(const f32x16& acc, float e, float& M, float& S) {
   const float m1 = max3(acc[0], acc[1], acc[2]);
   const float m2 = max3(acc[3], acc[4], acc[5]);
   const float m3 = max3(acc[6], acc[7], acc[8]);
@@ -118,24 +142,130 @@ __device__ __forceinline__ void lse_update(const f32x16& acc, float c2, float& M
   const float Mn = max3(max3(m1, m2, m3), max3(m4, m5, acc[15]), M);
   const bool valid = Mn > 0.5f * kMaskedBias;  // some real (unmasked) column seen
   const float Me = valid ? Mn : 0.0f;
-  const float off = -c2 * Me;
-  const float scale = fast_exp2(fmaf(M, c2, off));  // M = -inf -> 0
-  float s0 = fast_exp2(fmaf(acc[0], c2, off));
-  float s1 = fast_exp2(fmaf(acc[1], c2, off));
-  float s2 = fast_exp2(fmaf(acc[2], c2, off));
-  float s3 = fast_exp2(fmaf(acc[3], c2, off));
+  const float off = -e * Me;
+  const float scale = fast_exp2(fmaf(M, e, off));  // M = -inf -> 0
+  float s0 = fast_exp2(fmaf(acc[0], e, off));
+  float s1 = fast_exp2(fmaf(acc[1], e, off));
+  float s2 = fast_exp2(fmaf(acc[2], e, off));
+  float s3 = fast_exp2(fmaf(acc[3], e, off));
 #pragma unroll
   for (int r = 4; r < 16; r += 4) {
-    s0 += fast_exp2(fmaf(acc[r + 0], c2, off));
-    s1 += fast_exp2(fmaf(acc[r + 1], c2, off));
-    s2 += fast_exp2(fmaf(acc[r + 2], c2, off));
-    s3 += fast_exp2(fmaf(acc[r + 3], c2, off));
+    s0 += fast_exp2(fmaf(acc[r + 0], e, off));
+    s1 += fast_exp2(fmaf(acc[r + 1], e, off));
+    s2 += fast_exp2(fmaf(acc[r + 2], e, off));
+    s3 += fast_exp2(fmaf(acc[r + 3], e, off));
   }
   S = fmaf(S, scale, (s0 + s1) + (s2 + s3));
   M = valid ? Mn : M;
 }
 
-// Registers holding one stage of column records in flight (global -> LDS).
+// Shifted update: the row shift is already inside acc (bias block), so every
+// term is exp2(e * acc) with no running maximum. SCALED: e != 1 (bf16 points).
+template <bool SCALED>
+__device__ __forceinline__ void sum_update(const f32x16& acc, float e, float& S) {
+  auto ex = [&](float a) { return fast_exp2(SCALED ? a * e : a); };
+  float s0 = ex(acc[0]), s1 = ex(acc[1]), s2 = ex(acc[2]), s3 = ex(acc[3]);
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    s0 += ex(acc[r + 0]);
+    s1 += ex(acc[r + 1]);
+    s2 += ex(acc[r + 2]);
+    s3 += ex(acc[r + 3]);
+  }
+  S += (s0 + s1) + (s2 + s3);
+}
+
+// Column operands of one 32-column tile for this lane: its half of the record
+// of column (tile start + li), NKB data chunks plus the bias chunk.
+template <int NKB>
+struct ColTile {
+  bf16x8 a[NKB];
+  bf16x8 aug;
+};
+
+// Record and bias arrays are padded past the last column with masked columns
+// (zero data, masked bias) for five extra tiles, so a tile load needs no
+// bounds test: the loads are plain and can be issued well ahead of use.
+template <int NKB>
+__device__ __attribute__((always_inline)) inline void load_tile(
+    ColTile<NKB>& ct, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
+    int jt, int li, int half) {
+  const int j = jt + li;
+  const bf16x8* rec = reinterpret_cast<const bf16x8*>(cols + (int64_t)j * (NKB * 32)) + half * NKB;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = rec[kb];
+  ct.aug = bias[2 * (int64_t)j + half];
+}
+
+// MFMA products of one 32-column tile against the RB row blocks.
+template <int NKB, int RB>
+__device__ __attribute__((always_inline)) inline void tile_mfma(
+    const ColTile<NKB>& ct, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB], f32x16 (&acc)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    f32x16 a = {};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.a[kb], B[rb][kb], a, 0, 0, 0);
+    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.aug, Baug[rb], a, 0, 0, 0);
+  }
+}
+
+template <int RB, bool SHIFTED, bool SCALED>
+__device__ __attribute__((always_inline)) inline void tile_valu(const f32x16 (&acc)[RB], float e,
+                                                                float (&M)[RB], float (&S)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (SHIFTED) sum_update<SCALED>(acc[rb], e, S[rb]);
+    else lse_update(acc[rb], e, M[rb], S[rb]);
+  }
+}
+
+// One sweep of a wave over columns [j0, j1). SHIFTED: the row shift is folded
+// into Baug and the sums need no running maximum; otherwise online
+// max/sum-exp. Each wave streams its column records straight from memory (the
+// four waves of a workgroup read the same columns, so the L1 cache serves the
+// reuse), keeps two tiles of loads in flight ahead of use, and issues the
+// MFMAs of tile t+1 before the exp/sum work of tile t. There is no LDS staging
+// and no barrier, so waves never wait for each other.
+template <int NKB, int RB, bool SHIFTED, bool SCALED>
+__device__ __attribute__((always_inline)) inline void sweep(
+    const MfmaPassArgs& p, int j0, int j1, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB],
+    float (&M)[RB], float (&S)[RB], int li, int half) {
+  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
+  const bf16x8* __restrict__ bias = p.bias_col;
+  const int ntiles = (j1 - j0 + 31) / 32;
+  ColTile<NKB> c0, c1;
+  f32x16 acc0[RB], acc1[RB];
+  // Prefetch loads run up to four tiles past the range: they read the next
+  // range's columns or the padding, and their products are never summed.
+  load_tile<NKB>(c0, cols, bias, j0, li, half);
+  load_tile<NKB>(c1, cols, bias, j0 + 32, li, half);
+  tile_mfma<NKB, RB>(c0, B, Baug, acc0);
+  load_tile<NKB>(c0, cols, bias, j0 + 64, li, half);
+  for (int t = 0; t < ntiles; t += 2) {
+    // here: acc0 = tile t (issued), c1 = tile t+1, c0 = tile t+2 (loads in flight)
+    tile_mfma<NKB, RB>(c1, B, Baug, acc1);
+    load_tile<NKB>(c1, cols, bias, j0 + (t + 3) * 32, li, half);
+    tile_valu<RB, SHIFTED, SCALED>(acc0, p.escale, M, S);
+    tile_mfma<NKB, RB>(c0, B, Baug, acc0);
+    load_tile<NKB>(c0, cols, bias, j0 + (t + 4) * 32, li, half);
+    if (t + 1 < ntiles) tile_valu<RB, SHIFTED, SCALED>(acc1, p.escale, M, S);
+  }
+}
+
+// LDS-staged variant of the sweep for wide records (NKB >= 4): the workgroup
+// stages 64 columns at a time through LDS (double buffered, one barrier per
+// stage), so the four waves share one copy of each column record instead of
+// each pulling it through the L1 cache.
+constexpr int kStageCols = 64;
+
+template <int NKB>
+struct StageLds {
+  static constexpr int kRow = NKB * 32 + 16;  // padded record row (bytes) against bank conflicts
+  unsigned char dat[2][kStageCols * kRow];
+  bf16x8 aug[2][2 * kStageCols];             // [buffer][half * 64 + column]
+};
+
 template <int CPT>
 struct StageRegs {
   u32x4 d[CPT];
@@ -143,64 +273,108 @@ struct StageRegs {
 };
 
 // Thread t moves data chunks t, t + 256, ... and bias chunk t % 128 of a stage.
-// Loads are unconditional (indices clamped into range) so the staged values
-// stay in registers while the current stage is computed; a column past the end
-// of the range gets the masked bias, which makes its terms zero.
+// Columns past the range read the padding or the next range (never summed).
 template <int NKB, int CPT>
 __device__ __attribute__((always_inline)) inline void load_stage(
-    StageRegs<CPT>& sr, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
-    int s0, int j1, const bf16x8& masked) {
-  constexpr int RSB = NKB * 32;
+    StageRegs<CPT>& sr, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias, int s0) {
   constexpr int CHUNKS = kStageCols * NKB * 2;
-  constexpr int ACHUNKS = kStageCols * 2;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     int ch = threadIdx.x + c * kThreads;
     if constexpr (CHUNKS % kThreads != 0) ch = min(ch, CHUNKS - 1);
     const int col = ch / (NKB * 2), part = ch % (NKB * 2);
-    const int j = min(s0 + col, j1 - 1);
-    sr.d[c] = *reinterpret_cast<const u32x4*>(cols + (int64_t)j * RSB + part * 16);
+    sr.d[c] = *reinterpret_cast<const u32x4*>(cols + (int64_t)(s0 + col) * (NKB * 32) + part * 16);
   }
-  const int ach = threadIdx.x & (ACHUNKS - 1);
-  const int j = s0 + (ach >> 1);
-  const bf16x8 v = bias[2 * (int64_t)min(j, j1 - 1) + (ach & 1)];
-  sr.aug = (j < j1) ? v : masked;
+  const int ach = threadIdx.x & (2 * kStageCols - 1);
+  sr.aug = bias[2 * (int64_t)(s0 + (ach >> 1)) + (ach & 1)];
 }
 
 template <int NKB, int CPT>
 __device__ __attribute__((always_inline)) inline void store_stage(const StageRegs<CPT>& sr,
-                                                                  unsigned char* dat, bf16x8* aug) {
-  constexpr int LDS_ROW = NKB * 32 + 16;
+                                                                  StageLds<NKB>& L, int buf) {
   constexpr int CHUNKS = kStageCols * NKB * 2;
-  constexpr int ACHUNKS = kStageCols * 2;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = threadIdx.x + c * kThreads;
     if (CHUNKS % kThreads == 0 || ch < CHUNKS) {
       const int col = ch / (NKB * 2), part = ch % (NKB * 2);
-      *reinterpret_cast<u32x4*>(dat + col * LDS_ROW + part * 16) = sr.d[c];
+      *reinterpret_cast<u32x4*>(&L.dat[buf][col * StageLds<NKB>::kRow + part * 16]) = sr.d[c];
     }
   }
-  if (threadIdx.x < ACHUNKS) aug[threadIdx.x] = sr.aug;
+  if (threadIdx.x < 2 * kStageCols)
+    L.aug[buf][(threadIdx.x & 1) * kStageCols + (threadIdx.x >> 1)] = sr.aug;
 }
 
-template <int NKB, int RB>
-__global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
-  constexpr int RS = NKB * 16;                 // bf16 slots per record (both halves)
-  constexpr int RSB = RS * 2;                  // bytes per record
-  constexpr int LDS_ROW = RSB + 16;            // padded LDS row (bytes) against bank conflicts
-  constexpr int CHUNKS = kStageCols * NKB * 2; // 16-byte chunks of column data per stage
-  constexpr int ACHUNKS = kStageCols * 2;      // 16-byte chunks of bias records per stage
-  constexpr int CPT = (CHUNKS + kThreads - 1) / kThreads;
-  static_assert(ACHUNKS <= kThreads, "bias chunks: one per thread");
+template <int NKB, int RB, bool SHIFTED, bool SCALED>
+__device__ __attribute__((always_inline)) inline void sweep_lds(
+    const MfmaPassArgs& p, StageLds<NKB>& L, int j0, int j1, const bf16x8 (&B)[RB][NKB],
+    const bf16x8 (&Baug)[RB], float (&M)[RB], float (&S)[RB], int li, int half) {
+  constexpr int CPT = (kStageCols * NKB * 2 + kThreads - 1) / kThreads;
+  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
+  StageRegs<CPT> sr;
+  const int nstages = (j1 - j0 + kStageCols - 1) / kStageCols;
+  load_stage<NKB, CPT>(sr, cols, p.bias_col, j0);
+  store_stage<NKB, CPT>(sr, L, 0);
+  __syncthreads();
+  for (int st = 0; st < nstages; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nstages) load_stage<NKB, CPT>(sr, cols, p.bias_col, j0 + (st + 1) * kStageCols);
+#pragma unroll
+    for (int t = 0; t < kStageCols / 32; ++t) {
+      const int col = t * 32 + li;
+      ColTile<NKB> ct;
+      const bf16x8* arow = reinterpret_cast<const bf16x8*>(&L.dat[buf][col * StageLds<NKB>::kRow]) + half * NKB;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = arow[kb];
+      ct.aug = L.aug[buf][half * kStageCols + col];
+      f32x16 acc[RB];
+      tile_mfma<NKB, RB>(ct, B, Baug, acc);
+      tile_valu<RB, SHIFTED, SCALED>(acc, p.escale, M, S);
+    }
+    if (st + 1 < nstages) store_stage<NKB, CPT>(sr, L, buf ^ 1);
+    __syncthreads();
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds_dat[2][kStageCols * LDS_ROW];
-  __shared__ __attribute__((aligned(16))) bf16x8 lds_aug[2][kStageCols * 2];
+// Per record width, the sweep that serves it best: narrow records stream
+// per wave, wide records are staged through LDS.
+template <int NKB>
+constexpr bool kUseLds = NKB >= 4;
+
+template <int NKB>
+struct SweepLds {
+  StageLds<NKB> s;
+};
+struct NoLds {};
+
+// Block-wide max of v (every thread of the workgroup must call it).
+__device__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+constexpr float kShiftedFloor = 0x1p-60f;  // below this a shifted sum is recomputed exactly
+
+// One half-pass. SHIFTED (every pass after a side's first): the row shift
+// M_i = L_i(previous pass) + max_j (change of h_j since then) bounds every
+// term by 1, so the sum cannot overflow; a row whose sum falls below 2^-60
+// (shift far too high) is recomputed by an exact online-max sweep over all
+// columns, done by the workgroup that completes the row's block.
+template <int NKB, int RB, bool SHIFTED, bool SCALED>
+__global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
+  constexpr int RSB = NKB * 32;
+  constexpr int ROWS = 4 * RB * 32;
+  __shared__ float red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) std::conditional_t<kUseLds<NKB>, StageLds<NKB>, NoLds> lds;
 
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
-  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
-  const bf16x8* __restrict__ bias = p.bias_col;
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
@@ -208,9 +382,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
   const int sp = blockIdx.y;
   const int j0 = sp * p.cols_per_split;
   const int j1 = min(p.nc, j0 + p.cols_per_split);
-  const int row_base = blockIdx.x * (4 * RB * 32) + wave * (RB * 32);
+  const int row_base = blockIdx.x * ROWS + wave * (RB * 32);
 
-  // Row operands (B): this lane's half of the records of rows row_base + rb*32 + li.
   bf16x8 B[RB][NKB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -219,97 +392,128 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
   }
-  bf16x8 Baug = {};
-  if (half == 0) {
-    Baug[0] = (__bf16)1.0f;
-    Baug[1] = (__bf16)1.0f;
-    Baug[2] = (__bf16)1.0f;
-  }
   float M[RB], S[RB];
+  bf16x8 Baug[RB];
+  float shift_row[RB];
+  if constexpr (SHIFTED) {
+    // largest change of a column bias since this side's previous pass
+    float dm = -INFINITY;
+    for (int q = threadIdx.x; q < p.n_dmax_in; q += kThreads) dm = fmaxf(dm, p.dmax_in[q]);
+    const float dmax = block_max(dm, red);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    M[rb] = -INFINITY;
-    S[rb] = 0.0f;
-  }
-
-  StageRegs<CPT> sr;
-  bf16x8 masked = {};
-  if ((threadIdx.x & 1) == 0) masked[0] = (__bf16)kMaskedBias;
-
-  const int nstages = (j1 - j0 + kStageCols - 1) / kStageCols;
-  load_stage<NKB, CPT>(sr, cols, bias, j0, j1, masked);
-  store_stage<NKB, CPT>(sr, &lds_dat[0][0], &lds_aug[0][0]);
-  __syncthreads();
-  for (int st = 0; st < nstages; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstages) load_stage<NKB, CPT>(sr, cols, bias, j0 + (st + 1) * kStageCols, j1, masked);
-#pragma unroll
-    for (int t = 0; t < kStageCols / 32; ++t) {
-      const int col = t * 32 + li;
-      bf16x8 A[NKB];
-      const bf16x8* arow = reinterpret_cast<const bf16x8*>(&lds_dat[buf][col * LDS_ROW]) + half * NKB;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) A[kb] = arow[kb];
-      const bf16x8 Aaug = lds_aug[buf][2 * col + half];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb], B[rb][kb], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aaug, Baug, acc, 0, 0, 0);
-        lse_update(acc, p.escale, M[rb], S[rb]);
-      }
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = min(row_base + rb * 32 + li, p.nr - 1);
+      shift_row[rb] = p.Lin[i] + dmax;  // log2 units
+      Baug[rb] = row_aug(half, -shift_row[rb] / p.escale);
+      M[rb] = 0.0f;
+      S[rb] = 0.0f;
     }
-    if (st + 1 < nstages) store_stage<NKB, CPT>(sr, &lds_dat[buf ^ 1][0], &lds_aug[buf ^ 1][0]);
-    __syncthreads();
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      Baug[rb] = row_aug(half, 0.0f);
+      M[rb] = -INFINITY;
+      S[rb] = 0.0f;
+      shift_row[rb] = 0.0f;
+    }
   }
 
-  // Merge the two halves of each row (lanes li and li + 32), convert to log2 units.
+  if constexpr (kUseLds<NKB>) sweep_lds<NKB, RB, SHIFTED, SCALED>(p, lds, j0, j1, B, Baug, M, S, li, half);
+  else sweep<NKB, RB, SHIFTED, SCALED>(p, j0, j1, B, Baug, M, S, li, half);
+
+  // Per row (lanes of half 0): (Lm, Ls) with L = Lm + log2 Ls, Lm in log2 units.
   float Lm[RB], Ls[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float Mo = __shfl_xor(M[rb], 32);
     const float So = __shfl_xor(S[rb], 32);
-    const float Mt = fmaxf(M[rb], Mo);
-    const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
-    Ls[rb] = S[rb] * fast_exp2(p.escale * (M[rb] - Me)) + So * fast_exp2(p.escale * (Mo - Me));
-    Lm[rb] = p.escale * Mt;
+    if constexpr (SHIFTED) {
+      Ls[rb] = S[rb] + So;
+      Lm[rb] = shift_row[rb];
+    } else {
+      const float Mo = __shfl_xor(M[rb], 32);
+      const float Mt = fmaxf(M[rb], Mo);
+      const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
+      Ls[rb] = S[rb] * fast_exp2(p.escale * (M[rb] - Me)) + So * fast_exp2(p.escale * (Mo - Me));
+      Lm[rb] = p.escale * Mt;
+    }
   }
 
+  float dh = -INFINITY;  // this thread's largest bias change over the rows it finishes
+  bool need_exact = false;
   if (p.splits == 1) {
+    bool bad = false;
+    if constexpr (SHIFTED) {
+      if (half == 0)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          bad |= (row_base + rb * 32 + li < p.nr) && !(Ls[rb] >= kShiftedFloor);
+      need_exact = __syncthreads_or(bad);
+    }
+    if (!need_exact && half == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int i = row_base + rb * 32 + li;
+        if (i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, Lm[rb] + fast_log2(Ls[rb])));
+      }
+    }
+  } else {
     if (half == 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int i = row_base + rb * 32 + li;
-        if (i < p.nr) finish_row_mfma(p, i, Lm[rb] + fast_log2(Ls[rb]));
+        if (i < p.nr) p.part[(int64_t)sp * p.nr + i] = make_float2(Lm[rb], Ls[rb]);
       }
     }
-    return;
+    if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
+    // The completing workgroup merges the splits of its rows in split order.
+    float Lr = 0.0f;
+    bool bad = false;
+    const int i = blockIdx.x * ROWS + (int)threadIdx.x;
+    const bool mine = (int)threadIdx.x < ROWS && i < p.nr;
+    if (mine) {
+      float Mt = -INFINITY;
+      for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
+      const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
+      float St = 0.0f;
+      for (int s2 = 0; s2 < p.splits; ++s2) {
+        const float Mp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].x);
+        const float Sp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].y);
+        St = fmaf(Sp, fast_exp2(Mp - Me), St);
+      }
+      Lr = Mt + fast_log2(St);
+      bad = SHIFTED && !(St >= kShiftedFloor);
+    }
+    if constexpr (SHIFTED) need_exact = __syncthreads_or(bad);
+    if (!need_exact && mine) dh = finish_row_mfma(p, i, Lr);
+    if (threadIdx.x == 0) atomicExch(p.counters + blockIdx.x, 0u);
   }
-  if (half == 0) {
+
+  if constexpr (SHIFTED) {
+    if (need_exact) {
+      // Exact recomputation of this workgroup's rows over all columns.
+      if (threadIdx.x == 0 && p.exact_count) atomicAdd(p.exact_count, 1u);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = row_base + rb * 32 + li;
-      if (i < p.nr) p.part[(int64_t)sp * p.nr + i] = make_float2(Lm[rb], Ls[rb]);
+      for (int rb = 0; rb < RB; ++rb) {
+        Baug[rb] = row_aug(half, 0.0f);
+        M[rb] = -INFINITY;
+        S[rb] = 0.0f;
+      }
+      if constexpr (kUseLds<NKB>) sweep_lds<NKB, RB, false, SCALED>(p, lds, 0, p.nc, B, Baug, M, S, li, half);
+      else sweep<NKB, RB, false, SCALED>(p, 0, p.nc, B, Baug, M, S, li, half);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float So = __shfl_xor(S[rb], 32);
+        const float Mo = __shfl_xor(M[rb], 32);
+        const float Mt = fmaxf(M[rb], Mo);
+        const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
+        const float St = S[rb] * fast_exp2(p.escale * (M[rb] - Me)) + So * fast_exp2(p.escale * (Mo - Me));
+        const int i = row_base + rb * 32 + li;
+        if (half == 0 && i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, p.escale * Mt + fast_log2(St)));
+      }
     }
   }
-  if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
-  // The completing workgroup merges the splits of its 4 * RB * 32 rows in split order.
-  for (int r = threadIdx.x; r < 4 * RB * 32; r += kThreads) {
-    const int i = blockIdx.x * (4 * RB * 32) + r;
-    if (i >= p.nr) continue;
-    float Mt = -INFINITY;
-    for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
-    const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
-    float St = 0.0f;
-    for (int s2 = 0; s2 < p.splits; ++s2) {
-      const float Mp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].x);
-      const float Sp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].y);
-      St = fmaf(Sp, fast_exp2(Mp - Me), St);
-    }
-    finish_row_mfma(p, i, Mt + fast_log2(St));
-  }
-  if (threadIdx.x == 0) atomicExch(p.counters + blockIdx.x, 0u);
+  const float bmax = block_max(dh, red);
+  if (threadIdx.x == 0) p.dmax_out[blockIdx.x] = bmax;
 }
 
 // ---------------------------------------------------------------- record prep
@@ -358,7 +562,8 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
                                                         const float* shift, const float* w,
                                                         const float* pot, float* pot_zero,
                                                         float* alpha, float* lw, bf16x8* bias,
-                                                        float log2e_over_eps, float bias_scale) {
+                                                        float* hval, float log2e_over_eps,
+                                                        float bias_scale) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n) return;
   float nrm = 0.0f;
@@ -378,12 +583,41 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
   if (pot_zero) pot_zero[r] = 0.0f;
   alpha[r] = nrm;
   lw[r] = l;
-  write_bias_record(bias + 2 * r, (kLog2e * l + (pv - nrm) * log2e_over_eps) * bias_scale);
+  const float h = kLog2e * l + (pv - nrm) * log2e_over_eps;
+  hval[r] = h;
+  write_bias_record(bias + 2 * r, h * bias_scale);
+}
+
+// Masked padding columns [n, n_pad) of a side: zero records, masked bias in both buffers.
+__global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, int nkb, bf16x8* col_rec,
+                                                     bf16x8* bias0, bf16x8* bias1) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = (int64_t)nkb * 2;
+  if (t < (n_pad - n) * per) col_rec[n * per + t] = bf16x8{};
+  if (t < (n_pad - n) * 2) {
+    const int64_t q = n * 2 + t;
+    bf16x8 v = {};
+    if ((q & 1) == 0) {
+      v[0] = (__bf16)kMaskedBias;
+      v[3] = (__bf16)1.0f;
+      v[4] = (__bf16)1.0f;
+      v[5] = (__bf16)1.0f;
+    }
+    bias0[q] = v;
+    bias1[q] = v;
+  }
 }
 
 template <int NKB, int RB>
-hipError_t run_lse(const MfmaPassArgs& a, const PassPlan& pl, hipStream_t s) {
-  k_lse_mfma<NKB, RB><<<dim3(pl.row_blocks, pl.splits), kThreads, 0, s>>>(a);
+hipError_t run_lse(const MfmaPassArgs& a, bool shifted, bool scaled, const PassPlan& pl, hipStream_t s) {
+  const dim3 grid(pl.row_blocks, pl.splits);
+  if (shifted) {
+    if (scaled) k_lse_mfma<NKB, RB, true, true><<<grid, kThreads, 0, s>>>(a);
+    else k_lse_mfma<NKB, RB, true, false><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    if (scaled) k_lse_mfma<NKB, RB, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_lse_mfma<NKB, RB, false, false><<<grid, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -401,6 +635,8 @@ int mfma_nkb(int dtype, int d) {
 
 int mfma_rb(int nkb) { return nkb <= 4 ? 2 : 1; }
 
+int64_t mfma_padded_count(int64_t n) { return (n + 31) / 32 * 32 + 5 * 32; }
+
 PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb) {
   PassPlan pl;
   pl.rows_per_block = 4 * mfma_rb(nkb) * 32;
@@ -412,18 +648,19 @@ PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb) {
   if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
   int64_t cps = (nc + splits - 1) / splits;
-  cps = (cps + kStageCols - 1) / kStageCols * kStageCols;
+  cps = (cps + 63) / 64 * 64;  // whole 64-column stages: a split never reads into the next one
   pl.cols_per_split = (int)cps;
   pl.splits = (int)((nc + cps - 1) / cps);
   return pl;
 }
 
-hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, const PassPlan& pl, hipStream_t s) {
+hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
+                           const PassPlan& pl, hipStream_t s) {
   switch (nkb) {
-    case 1: return run_lse<1, 2>(a, pl, s);
-    case 2: return run_lse<2, 2>(a, pl, s);
-    case 4: return run_lse<4, 2>(a, pl, s);
-    case 8: return run_lse<8, 1>(a, pl, s);
+    case 1: return run_lse<1, 2>(a, shifted, scaled, pl, s);
+    case 2: return run_lse<2, 2>(a, shifted, scaled, pl, s);
+    case 4: return run_lse<4, 2>(a, shifted, scaled, pl, s);
+    case 8: return run_lse<8, 1>(a, shifted, scaled, pl, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -445,9 +682,13 @@ hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int 
     const int blocks = (int)((chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096);
     k_pack_records<<<blocks, 256, 0, s>>>(side->pts, dtype, side->n, d, sh, nkb, c2,
                                           side->row_rec, side->col_rec);
+    const int64_t npad = mfma_padded_count(side->n);
+    const int64_t pad_work = (npad - side->n) * nkb * 2;
+    k_pad_columns<<<(int)((pad_work + 255) / 256), 256, 0, s>>>(side->n, npad, nkb, side->col_rec,
+                                                                side->bias, side->bias_alt);
     k_prep_side_mfma<<<(int)((side->n + 255) / 256), 256, 0, s>>>(
         side->pts, dtype, side->n, d, sh, side->w, side->pot, side->pot_zero, side->alpha, side->lw,
-        side->bias, log2e_over_eps, mfma_bias_scale(dtype, c2));
+        side->bias, side->hval, log2e_over_eps, mfma_bias_scale(dtype, c2));
   }
   return hipGetLastError();
 }

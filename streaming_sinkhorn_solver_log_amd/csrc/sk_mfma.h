@@ -19,7 +19,14 @@ struct MfmaPassArgs {
   const float* lw;         // nr natural-log row weights
   float* pot;              // nr potentials, updated in place
   bf16x8* bias_out;        // nr bias records for the next pass of the other side
-  float* Lout;             // nr log2-sum-exp values (may be null)
+  float* Lout;             // nr log2-sum-exp values of this pass
+  const float* Lin;        // nr log2-sum-exp values of this side's previous pass (shifted sweep)
+  const float* hval_in;    // nr biases (log2 units) this side had before this pass
+  float* hval_out;         // nr biases (log2 units) after this pass
+  const float* dmax_in;    // per-block maxima of the columns' bias change since this side's previous pass
+  int n_dmax_in;
+  float* dmax_out;         // one entry per row block: max bias change of its rows
+  unsigned* exact_count;   // workgroups that fell back to the exact sweep (may be null)
   float2* part;            // split partials (M, S) in log2 units: [split][nr]
   unsigned* counters;      // one per row block, zero on entry and exit
   int nr, nc;
@@ -41,13 +48,18 @@ struct MfmaPrepSide {
   float* alpha;
   float* lw;
   bf16x8* bias;      // n bias records of the starting potential
+  bf16x8* bias_alt;  // the second bias buffer (its padding is initialized too)
+  float* hval;       // n biases (log2 units) of the starting potential
   int64_t n;
 };
 
 int mfma_nkb(int dtype, int d);  // K blocks per record, 0 if the resident kernel does not serve d
 int mfma_rb(int nkb);
+// Points per side including the masked padding columns (records, bias buffers).
+int64_t mfma_padded_count(int64_t n);
 PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb);
-hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, const PassPlan& pl, hipStream_t s);
+hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
+                           const PassPlan& pl, hipStream_t s);
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
                             int nkb, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,
