@@ -46,12 +46,12 @@ struct Carve {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Kernel family of a solve: the matrix-core pass when its register-resident
-// records fit (bf16: d <= 128, float32: d <= 21), else the vector-ALU pass.
-// FLASHSK_SOLVE_PATH=valu selects the vector-ALU pass wherever it applies
-// (for comparisons). Gradient and transport application use the vector-ALU
-// kernels (d <= 64).
-enum class Path { Valu, Mfma, None };
+// Kernel family of a solve: the matrix-core pass with register-resident row
+// records when they fit (bf16: d <= 128, float32: d <= 21), else the GEMM-tiled
+// matrix-core pass (d <= 4096). FLASHSK_SOLVE_PATH=valu selects the
+// vector-ALU pass where it applies (d <= 64, for comparisons). Gradient and
+// transport application use the vector-ALU kernels (d <= 64).
+enum class Path { Valu, Mfma, Gemm, None };
 
 bool force_valu() {
   static const bool v = [] {
@@ -73,8 +73,9 @@ bool debug_enabled() {
 
 Path solve_path(int dtype, int64_t d) {
   if (d < 1) return Path::None;
-  if (!force_valu() && d <= 1024 && mfma_nkb(dtype, (int)d) > 0) return Path::Mfma;
-  if (d <= 64) return Path::Valu;
+  if (force_valu() && d <= 64) return Path::Valu;
+  if (d <= 4096 && mfma_nkb(dtype, (int)d) > 0) return Path::Mfma;
+  if (d <= 4096) return Path::Gemm;
   return Path::None;
 }
 
@@ -184,6 +185,10 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d) {
     sp.nkb = mfma_nkb(dtype, (int)d);
     sp.f = plan_mfma_pass(n, m, sp.nkb);
     sp.g = plan_mfma_pass(m, n, sp.nkb);
+  } else if (sp.path == Path::Gemm) {
+    sp.nkb = gemm_nkb(dtype, (int)d);
+    sp.f = plan_gemm_pass(n, m);
+    sp.g = plan_gemm_pass(m, n);
   } else {
     sp.f = plan_valu_pass(n, m, (int)d);
     sp.g = plan_valu_pass(m, n, (int)d);
@@ -201,7 +206,7 @@ struct SolveWs {
 SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_t d) {
   Carve c{static_cast<char*>(ws)};
   SolveWs L{};
-  if (sp.path == Path::Mfma) {
+  if (sp.path == Path::Mfma || sp.path == Path::Gemm) {
     L.xm = carve_side_m(c, n, sp.nkb, sp.f.row_blocks);
     L.ym = carve_side_m(c, m, sp.nkb, sp.g.row_blocks);
   } else {
@@ -289,6 +294,12 @@ int solve_valu(const SolveWs& L, const SolvePlan& sp, int64_t n, int64_t m, int6
   return SK_OK;
 }
 
+hipError_t launch_pass(const SolvePlan& sp, const MfmaPassArgs& a, bool shifted, bool scaled,
+                       const PassPlan& pl, hipStream_t s) {
+  if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, pl, s);
+  return launch_lse_mfma(a, sp.nkb, shifted, scaled, pl, s);
+}
+
 int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int64_t m, int iters,
                bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
   int cur = 0;
@@ -308,14 +319,14 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pf.nr = (int)n; pf.nc = (int)m; pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
     pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
     pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
-    if ((e = launch_lse_mfma(pf, sp.nkb, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
+    if ((e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
     MfmaPassArgs pg = pf;
     pg.rows = L.ym.row_rec; pg.cols = L.xm.col_rec; pg.bias_col = L.xm.bias[cur];
     pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt];
     pg.Lout = L.ym.L; pg.Lin = L.ym.L; pg.hval_in = L.ym.hval[cur]; pg.hval_out = L.ym.hval[nxt];
     pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
-    if ((e = launch_lse_mfma(pg, sp.nkb, shifted, scaled, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
+    if ((e = launch_pass(sp, pg, shifted, scaled, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
     cur = nxt;
   }
   return SK_OK;
@@ -393,7 +404,7 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   float* f_zero = warm ? nullptr : f;
   float* g_zero = warm ? nullptr : g;
   hipError_t e;
-  if (sp.path == Path::Mfma) {
+  if (sp.path == Path::Mfma || sp.path == Path::Gemm) {
     MfmaPrepSide px{x, a, f_start, f_zero, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw,
                     L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
     MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw,

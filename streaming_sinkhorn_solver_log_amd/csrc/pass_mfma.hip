@@ -36,6 +36,7 @@
 // and streams the column records of its range from memory.
 #include "sk_internal.h"
 #include "sk_mfma.h"
+#include "sk_mfma_dev.h"
 
 #include <math.h>
 
@@ -44,136 +45,7 @@
 namespace sk {
 namespace {
 
-constexpr float kMaskedBias = -1.0e30f;  // bias of a column that contributes nothing
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-template <typename T>
-__device__ __forceinline__ T load_coherent(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ bool arrive_last(unsigned* counter, int splits) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1u) == (unsigned)(splits - 1));
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
-
-// Three-part bf16 split of v (v ~= hi + mid + lo to float32 precision).
-__device__ __forceinline__ void split3(float v, __bf16& hi, __bf16& mid, __bf16& lo) {
-  hi = (__bf16)v;
-  const float r1 = v - (float)hi;
-  mid = (__bf16)r1;
-  lo = (__bf16)(r1 - (float)mid);
-}
-
-// Bias record of one column: half 0 = (hi, mid, lo, 1, 1, 1, 0, 0), half 1 = zeros.
-// The three ones meet the row side's (-M) parts in the shifted sweep.
-__device__ __forceinline__ void write_bias_record(bf16x8* rec, float htilde) {
-  float v = htilde < kMaskedBias ? kMaskedBias : htilde;  // -inf (zero weight) -> masked; NaN kept
-  bf16x8 h0 = {}, h1 = {};
-  __bf16 a, b, c;
-  split3(v, a, b, c);
-  h0[0] = a;
-  h0[1] = b;
-  h0[2] = c;
-  h0[3] = (__bf16)1.0f;
-  h0[4] = (__bf16)1.0f;
-  h0[5] = (__bf16)1.0f;
-  rec[0] = h0;
-  rec[1] = h1;
-}
-
-// Row-side bias block: (1, 1, 1, -M parts) in half 0, zeros in half 1.
-__device__ __forceinline__ bf16x8 row_aug(int half, float neg_m) {
-  bf16x8 r = {};
-  if (half == 0) {
-    r[0] = (__bf16)1.0f;
-    r[1] = (__bf16)1.0f;
-    r[2] = (__bf16)1.0f;
-    __bf16 a, b, c;
-    split3(neg_m, a, b, c);
-    r[3] = a;
-    r[4] = b;
-    r[5] = c;
-  }
-  return r;
-}
-
-// Potential update of row i from its log2-sum-exp L; returns the change of the
-// row's bias (log2 units) since the previous pass of this side.
-__device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, float L) {
-  const float al = p.alpha[i];
-  float v = fmaf(p.neg_eps_ln2, L, al);
-  if (p.symmetric) v = 0.5f * (p.pot[i] + v);
-  p.pot[i] = v;
-  const float h = fmaf(kLog2e, p.lw[i], (v - al) * p.log2e_over_eps);
-  write_bias_record(p.bias_out + 2 * (int64_t)i, h * p.bias_scale);
-  const float dh = h - p.hval_in[i];
-  p.hval_out[i] = h;
-  p.Lout[i] = L;
-  return dh;
-}
-
-// max(a, b, c) in one instruction. Written as inline assembly because the
-// compiler otherwise quiets each MFMA result before a max (IEEE mode), which
-// costs an extra instruction per score; a NaN score still reaches the sum
-// through exp2 and propagates.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Online update of a lane's running (M, S) with one 32x32 tile (16 scores per lane).
-// M is in accumulator units; the exponent of a score is e * (acc - M).
-__device__ __forceinline__ void lse_update(const f32x16& acc, float e, float& M, float& S) {
-  const float m1 = max3(acc[0], acc[1], acc[2]);
-  const float m2 = max3(acc[3], acc[4], acc[5]);
-  const float m3 = max3(acc[6], acc[7], acc[8]);
-  const float m4 = max3(acc[9], acc[10], acc[11]);
-  const float m5 = max3(acc[12], acc[13], acc[14]);
-  const float Mn = max3(max3(m1, m2, m3), max3(m4, m5, acc[15]), M);
-  const bool valid = Mn > 0.5f * kMaskedBias;  // some real (unmasked) column seen
-  const float Me = valid ? Mn : 0.0f;
-  const float off = -e * Me;
-  const float scale = fast_exp2(fmaf(M, e, off));  // M = -inf -> 0
-  float s0 = fast_exp2(fmaf(acc[0], e, off));
-  float s1 = fast_exp2(fmaf(acc[1], e, off));
-  float s2 = fast_exp2(fmaf(acc[2], e, off));
-  float s3 = fast_exp2(fmaf(acc[3], e, off));
-#pragma unroll
-  for (int r = 4; r < 16; r += 4) {
-    s0 += fast_exp2(fmaf(acc[r + 0], e, off));
-    s1 += fast_exp2(fmaf(acc[r + 1], e, off));
-    s2 += fast_exp2(fmaf(acc[r + 2], e, off));
-    s3 += fast_exp2(fmaf(acc[r + 3], e, off));
-  }
-  S = fmaf(S, scale, (s0 + s1) + (s2 + s3));
-  M = valid ? Mn : M;
-}
-
-// Shifted update: the row shift is already inside acc (bias block), so every
-// term is exp2(e * acc) with no running maximum. SCALED: e != 1 (bf16 points).
-template <bool SCALED>
-__device__ __forceinline__ void sum_update(const f32x16& acc, float e, float& S) {
-  auto ex = [&](float a) { return fast_exp2(SCALED ? a * e : a); };
-  float s0 = ex(acc[0]), s1 = ex(acc[1]), s2 = ex(acc[2]), s3 = ex(acc[3]);
-#pragma unroll
-  for (int r = 4; r < 16; r += 4) {
-    s0 += ex(acc[r + 0]);
-    s1 += ex(acc[r + 1]);
-    s2 += ex(acc[r + 2]);
-    s3 += ex(acc[r + 3]);
-  }
-  S += (s0 + s1) + (s2 + s3);
-}
+using namespace dev;
 
 // Column operands of one 32-column tile for this lane: its half of the record
 // of column (tile start + li), NKB data chunks plus the bias chunk.
@@ -346,21 +218,6 @@ struct SweepLds {
   StageLds<NKB> s;
 };
 struct NoLds {};
-
-// Block-wide max of v (every thread of the workgroup must call it).
-__device__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
-  __syncthreads();
-  return r;
-}
-
-constexpr float kShiftedFloor = 0x1p-60f;  // below this a shifted sum is recomputed exactly
 
 // One half-pass. SHIFTED (every pass after a side's first): the row shift
 // M_i = L_i(previous pass) + max_j (change of h_j since then) bounds every

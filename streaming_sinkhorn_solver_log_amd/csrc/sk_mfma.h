@@ -60,6 +60,11 @@ int64_t mfma_padded_count(int64_t n);
 PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb);
 hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
                            const PassPlan& pl, hipStream_t s);
+// GEMM-tiled half-pass for wide records (any NKB that is a multiple of 4).
+int gemm_nkb(int dtype, int d);
+PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
+hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
+                           const PassPlan& pl, hipStream_t s);
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
                             int nkb, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,

@@ -76,6 +76,9 @@ SOLVE_CASES = [
     (1, 257, 4099, 10),
     (3, 2000, 1500, 20),          # bf16 points, d = 64, Dirichlet weights
     (3, 129, 2111, 5),
+    (4, 600, 700, 5),             # float32 points, d = 512 (GEMM-tiled pass)
+    (7, 700, 333, 5),             # bf16 points, d = 512
+    (5, 300, 1300, 4),            # bf16 points, d = 1024, rectangular
 ]
 
 
@@ -95,7 +98,8 @@ def test_solve_matches_oracle(sk, key, n, m, iters):
     assert abs(float(cost) - cr) <= tol_rel(w) * max(abs(cr), 1e-30)
 
 
-CUSTOM_DIMS = [("f32", 16), ("f32", 20), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7)]
+CUSTOM_DIMS = [("f32", 16), ("f32", 20), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7),
+               ("f32", 64), ("bf16", 200), ("f32", 130)]
 
 
 @pytest.mark.parametrize("dtype,d", CUSTOM_DIMS)
