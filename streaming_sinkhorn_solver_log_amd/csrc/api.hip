@@ -46,16 +46,15 @@ struct Carve {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Kernel family of a solve: the matrix-core pass with register-resident row
+// Kernel family of a call: the matrix-core kernels with register-resident row
 // records when they fit (bf16: d <= 128, float32: d <= 21), else the GEMM-tiled
-// matrix-core pass (d <= 4096). FLASHSK_SOLVE_PATH=valu selects the
-// vector-ALU pass where it applies (d <= 64, for comparisons). Gradient and
-// transport application use the vector-ALU kernels (d <= 64).
+// matrix-core kernels (d <= 4096). FLASHSK_PATH=valu selects the vector-ALU
+// kernels where they apply (d <= 64, for comparisons).
 enum class Path { Valu, Mfma, Gemm, None };
 
 bool force_valu() {
   static const bool v = [] {
-    const char* e = getenv("FLASHSK_SOLVE_PATH");
+    const char* e = getenv("FLASHSK_PATH");
     return e && strcmp(e, "valu") == 0;
   }();
   return v;
@@ -79,10 +78,7 @@ Path solve_path(int dtype, int64_t d) {
   return Path::None;
 }
 
-Path aux_path(int dtype, int64_t d) {
-  (void)dtype;
-  return (d >= 1 && d <= 64) ? Path::Valu : Path::None;
-}
+Path aux_path(int dtype, int64_t d) { return solve_path(dtype, d); }
 
 int check_common(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                  const float* a, const float* b, double eps, Path path) {
@@ -241,13 +237,6 @@ AuxWs layout_aux(void* ws, int64_t n, int64_t m, int64_t d, const PassPlan& pl, 
   return L;
 }
 
-int check_ws(void* ws, size_t ws_bytes, size_t need) {
-  if (!ws) return fail(SK_ERR_WORKSPACE, "workspace pointer is null (%zu bytes needed)", need);
-  if (!aligned(ws, kAlign)) return fail(SK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (ws_bytes < need) return fail(SK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-  return SK_OK;
-}
-
 struct Scalars {
   float c2, inv_c2, neg_eps_ln2, log2e_over_eps;
 };
@@ -258,6 +247,109 @@ Scalars scalars(double eps) {
   s.neg_eps_ln2 = (float)(-eps * 0.6931471805599453);
   s.log2e_over_eps = (float)(1.4426950408889634 / eps);
   return s;
+}
+
+// Matrix-core gradient / transport application: records of both sides, value
+// fragments of the column side, split partials of (mu, S, values).
+struct AuxPlan {
+  Path path;
+  int nkb;
+  int kv, nobt, nob, nchunks, pp, vp;
+  int64_t nr, nc;
+  PassPlan pl;
+};
+
+AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool grad, int transpose) {
+  AuxPlan ap{};
+  ap.path = aux_path(dtype, d);
+  ap.nr = transpose ? m : n;
+  ap.nc = transpose ? n : m;
+  ap.kv = (int)kv;
+  if (ap.path == Path::Mfma || ap.path == Path::Gemm) {
+    const bool gemm = ap.path == Path::Gemm;
+    ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
+    pv_parts(dtype, grad, ap.pp, ap.vp);
+    const int blocks = (int)((kv + 31) / 32);
+    ap.nob = pv_nob(blocks);
+    ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
+    ap.nobt = ap.nchunks * ap.nob;
+    ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks);
+  } else {
+    ap.pl = plan_valu_pass(ap.nr, ap.nc, (int)d);
+  }
+  return ap;
+}
+
+struct AuxWsM {
+  SideM x, y;
+  bf16x8* vfrag;
+  int64_t vtiles;
+  Common c;
+  size_t bytes;
+};
+
+AuxWsM layout_aux_m(void* ws, const AuxPlan& ap, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  AuxWsM L{};
+  L.x = carve_side_m(c, n, ap.nkb, 1);
+  L.y = carve_side_m(c, m, ap.nkb, 1);
+  L.vtiles = mfma_padded_count(ap.nc) / 32;
+  L.vfrag = c.take<bf16x8>((size_t)L.vtiles * ap.nobt * ap.vp * 2 * 64);
+  // (mu, S) pairs, padded to 16 bytes, then the value partials
+  const size_t slots_rows = (size_t)ap.nchunks * ap.pl.splits * ap.nr;
+  const size_t part_floats = ap.pl.splits > 1
+      ? round_up(2 * slots_rows, 4) + slots_rows * 32 * ap.nob : 0;
+  L.c = carve_common(c, (part_floats + 1) / 2, ap.nchunks * ap.pl.row_blocks, d);
+  L.bytes = c.off;
+  return L;
+}
+
+// Workspace of a transport application (vector-ALU partials: k floats per split).
+size_t aux_bytes(const AuxPlan& ap, int64_t n, int64_t m, int64_t d, int64_t k) {
+  if (ap.path == Path::Valu) return layout_aux(nullptr, n, m, d, ap.pl, ap.nr, k).bytes;
+  return layout_aux_m(nullptr, ap, n, m, d).bytes;
+}
+
+// Prep of both sides (records, norms, log-weights, biases of the given
+// potentials, centering shift), value fragments of the column side, then the
+// P V / gradient launch.
+int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, int dtype, int64_t n,
+              int64_t m, int64_t d, const float* a, const float* b, const float* f, const float* g,
+              bool grad, int transpose, const void* vsrc, bool vsrc_bf16, float* out,
+              const Scalars& sc, hipStream_t s) {
+  const int ncnt = ap.nchunks * ap.pl.row_blocks;
+  MfmaPrepSide px{x, a, f, nullptr, L.x.row_rec, L.x.col_rec, L.x.alpha, L.x.lw,
+                  L.x.bias[0], L.x.bias[1], L.x.hval[0], n};
+  MfmaPrepSide py{y, b, g, nullptr, L.y.row_rec, L.y.col_rec, L.y.alpha, L.y.lw,
+                  L.y.bias[0], L.y.bias[1], L.y.hval[0], m};
+  hipError_t e = launch_prep_mfma(px, py, dtype, (int)d, ap.nkb, true, L.c.centroid, L.c.shift,
+                                  L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);
+  if (e != hipSuccess) return hip_fail(e, "prep");
+  const float* shift = dtype == SK_F32 ? L.c.shift : nullptr;
+  e = launch_pack_values(vsrc, vsrc_bf16, ap.nc, ap.kv, grad ? shift : nullptr, ap.vp, ap.nobt,
+                         L.vtiles, L.vfrag, s);
+  if (e != hipSuccess) return hip_fail(e, "value packing");
+  const SideM& R = transpose ? L.y : L.x;
+  const SideM& C = transpose ? L.x : L.y;
+  PvArgs pa{};
+  pa.rows = R.row_rec; pa.cols = C.col_rec; pa.bias_col = C.bias[0]; pa.vfrag = L.vfrag;
+  pa.nobt = ap.nobt; pa.kv = ap.kv; pa.out = out;
+  pa.hrow = R.hval[0]; pa.wrow = a; pa.xrow = x; pa.xbf16 = dtype == SK_BF16; pa.shift = shift;
+  pa.grad = grad ? 1 : 0;
+  pa.part = reinterpret_cast<float*>(L.c.part); pa.counters = L.c.counters;
+  pa.nr = (int)ap.nr; pa.nc = (int)ap.nc; pa.row_blocks = ap.pl.row_blocks; pa.nchunks = ap.nchunks;
+  pa.splits = ap.pl.splits; pa.cols_per_split = ap.pl.cols_per_split;
+  pa.escale = mfma_escale(dtype, sc.c2);
+  e = launch_pv(pa, ap.path == Path::Gemm, ap.nkb, ap.nob, ap.pp, ap.vp, ap.pl, s);
+  if (e != hipSuccess) return hip_fail(e, grad ? "grad" : "apply");
+  return SK_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(SK_ERR_WORKSPACE, "workspace pointer is null (%zu bytes needed)", need);
+  if (!aligned(ws, kAlign)) return fail(SK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(SK_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return SK_OK;
 }
 
 hipError_t prep_valu(const Side& X, const Side& Y, const Common& C, const void* x, const void* y,
@@ -337,15 +429,14 @@ size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
   return layout_solve(nullptr, sp, n, m, d).bytes;
 }
 
-size_t apply_bytes(int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
-  const int64_t nr = transpose ? m : n, nc = transpose ? n : m;
-  const PassPlan pl = plan_valu_pass(nr, nc, (int)d);
-  return layout_aux(nullptr, n, m, d, pl, nr, k).bytes;
+size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
+  return aux_bytes(plan_aux(dtype, n, m, d, k, false, transpose), n, m, d, k);
 }
 
-size_t grad_bytes(int64_t n, int64_t m, int64_t d) {
-  const PassPlan pl = plan_valu_pass(n, m, (int)d);
-  return layout_aux(nullptr, n, m, d, pl, n, 2 + valu_dclass((int)d)).bytes;
+size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  const AuxPlan ap = plan_aux(dtype, n, m, d, d, true, 0);
+  if (ap.path == Path::Valu) return layout_aux(nullptr, n, m, d, ap.pl, n, 2 + valu_dclass((int)d)).bytes;
+  return layout_aux_m(nullptr, ap, n, m, d).bytes;
 }
 
 }  // namespace
@@ -368,12 +459,12 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
       return solve_bytes(dtype, n, m, d);
     case SK_OP_APPLY: {
       if (aux_path(dtype, d) == Path::None || k < 1 || k > 64) return 0;
-      const size_t a0 = apply_bytes(n, m, d, k, 0), a1 = apply_bytes(n, m, d, k, 1);
+      const size_t a0 = apply_bytes(dtype, n, m, d, k, 0), a1 = apply_bytes(dtype, n, m, d, k, 1);
       return a0 > a1 ? a0 : a1;
     }
     case SK_OP_GRAD:
       if (aux_path(dtype, d) == Path::None) return 0;
-      return grad_bytes(n, m, d);
+      return grad_bytes(dtype, n, m, d);
     default: return 0;
   }
 }
@@ -442,13 +533,18 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
   if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
   if (k < 1) return fail(SK_ERR_INVALID_ARG, "k must be >= 1");
   if (k > 64) return fail(SK_ERR_UNSUPPORTED, "k=%lld > 64 is not supported", (long long)k);
-  const int64_t nr = transpose ? m : n, nc = transpose ? n : m;
-  const PassPlan pl = plan_valu_pass(nr, nc, (int)d);
-  const size_t need = layout_aux(nullptr, n, m, d, pl, nr, k).bytes;
+  const AuxPlan ap = plan_aux(dtype, n, m, d, k, false, transpose);
+  const size_t need = aux_bytes(ap, n, m, d, k);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const AuxWs L = layout_aux(ws, n, m, d, pl, nr, k);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Scalars sc = scalars(eps);
+  if (ap.path != Path::Valu) {
+    const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
+    return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, transpose, V, false, out, sc, s);
+  }
+  const PassPlan& pl = ap.pl;
+  const int64_t nr = ap.nr, nc = ap.nc;
+  const AuxWs L = layout_aux(ws, n, m, d, pl, nr, k);
   hipError_t e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, f, g, nullptr, nullptr, true,
                            pl.row_blocks, sc, s);
   if (e != hipSuccess) return hip_fail(e, "prep");
@@ -470,13 +566,19 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
   int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
   if (rc) return rc;
   if (!g || !grad_x) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
-  const PassPlan pl = plan_valu_pass(n, m, (int)d);
-  const int64_t rec = 2 + valu_dclass((int)d);
-  const size_t need = layout_aux(nullptr, n, m, d, pl, n, rec).bytes;
+  const AuxPlan ap = plan_aux(dtype, n, m, d, d, true, 0);
+  const size_t need = grad_bytes(dtype, n, m, d);
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const AuxWs L = layout_aux(ws, n, m, d, pl, n, rec);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Scalars sc = scalars(eps);
+  if (ap.path != Path::Valu) {
+    const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
+    return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, nullptr, g, true, 0, y, dtype == SK_BF16,
+                     grad_x, sc, s);
+  }
+  const PassPlan& pl = ap.pl;
+  const int64_t rec = 2 + valu_dclass((int)d);
+  const AuxWs L = layout_aux(ws, n, m, d, pl, n, rec);
   hipError_t e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, nullptr, g, nullptr, nullptr,
                            true, pl.row_blocks, sc, s);
   if (e != hipSuccess) return hip_fail(e, "prep");

@@ -47,41 +47,6 @@ namespace {
 
 using namespace dev;
 
-// Column operands of one 32-column tile for this lane: its half of the record
-// of column (tile start + li), NKB data chunks plus the bias chunk.
-template <int NKB>
-struct ColTile {
-  bf16x8 a[NKB];
-  bf16x8 aug;
-};
-
-// Record and bias arrays are padded past the last column with masked columns
-// (zero data, masked bias) for five extra tiles, so a tile load needs no
-// bounds test: the loads are plain and can be issued well ahead of use.
-template <int NKB>
-__device__ __attribute__((always_inline)) inline void load_tile(
-    ColTile<NKB>& ct, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
-    int jt, int li, int half) {
-  const int j = jt + li;
-  const bf16x8* rec = reinterpret_cast<const bf16x8*>(cols + (int64_t)j * (NKB * 32)) + half * NKB;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = rec[kb];
-  ct.aug = bias[2 * (int64_t)j + half];
-}
-
-// MFMA products of one 32-column tile against the RB row blocks.
-template <int NKB, int RB>
-__device__ __attribute__((always_inline)) inline void tile_mfma(
-    const ColTile<NKB>& ct, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB], f32x16 (&acc)[RB]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    f32x16 a = {};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.a[kb], B[rb][kb], a, 0, 0, 0);
-    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.aug, Baug[rb], a, 0, 0, 0);
-  }
-}
-
 template <int RB, bool SHIFTED, bool SCALED>
 __device__ __attribute__((always_inline)) inline void tile_valu(const f32x16 (&acc)[RB], float e,
                                                                 float (&M)[RB], float (&S)[RB]) {

@@ -1,0 +1,580 @@
+// pass_pv.hip -- matrix-core transport application (P V, P^T U) and
+// barycentric gradient.
+//
+// Both are weighted sums over columns of the half-pass scores (FlashSinkhorn
+// replication review, Summary: the released primitives apply the plan to a
+// matrix without forming it, and the gradient is the barycentric projection,
+// i.e. an attention output with the plan's row-softmax as weights):
+//
+//   apply: out_i = sum_j 2^{r_i + s_ij} V_j,   r_i = log2 a_i + (f_i - |x_i|^2) log2(e) / eps
+//   grad:  O_i   = sum_j 2^{s_ij} y_j / sum_j 2^{s_ij},   out_i = 2 a_i (x_i - O_i)
+//
+// with s_ij = e * acc_ij the score of the half-pass (column bias included,
+// no row shift). A score tile comes out of the MFMA as in the half-pass; its
+// entries are then the B operand of a second MFMA against the tile's values.
+// In lane l (h = l / 32) register r = 8 kb + e of a score accumulator holds
+// the entry of row l % 32 at tile column 16 kb + 8 (e / 4) + 4 h + e % 4, and
+// a 32x32x16 B operand wants, in the same lane, K slots 8 h + e of column
+// l % 32: so the accumulator, converted to bf16, IS the B operand of two K
+// blocks, provided the values (the A operand, value index l % 32) are stored
+// in that column order. pack_values writes them so, once per call.
+//
+// Precision: entries and values are split into bf16 parts (float32 points:
+// three and three, the six products of relative order up to 2^-16 give
+// float32 accuracy; bf16 points: two parts of the entries and two of the
+// values for P V, or one exact part of the bf16 points for the gradient).
+//
+// Stabilization: a running row maximum mu (acc units), raised only when a
+// tile's maximum exceeds it by more than 2^8 in value (lazy rescaling: terms
+// stay below 256, the accumulators are rescaled rarely). The maximum is taken
+// over both halves of the wave, so one shift holds for a whole MFMA sum.
+#include "sk_internal.h"
+#include "sk_mfma.h"
+#include "sk_mfma_dev.h"
+
+#include <math.h>
+
+namespace sk {
+namespace {
+
+using namespace dev;
+
+constexpr float kMuInit = -1.0e29f;  // no column seen yet (above any masked score)
+constexpr float kLazy = 8.0f;        // raise mu when a term would exceed 2^8
+
+template <int NOB, int VP>
+struct VTile {
+  bf16x8 v[NOB][VP][2];
+};
+
+__device__ __forceinline__ const bf16x8* vfrag_at(const PvArgs& p, int64_t tile, int ob, int vp_parts,
+                                                  int vp, int kb) {
+  return p.vfrag + ((((tile * p.nobt + ob) * vp_parts + vp) * 2 + kb) << 6);
+}
+
+template <int NOB, int VP>
+__device__ __attribute__((always_inline)) inline void load_vtile(VTile<NOB, VP>& vt, const PvArgs& p,
+                                                                 int64_t tile, int ob0, int lane) {
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int vp = 0; vp < VP; ++vp)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) vt.v[ob][vp][kb] = vfrag_at(p, tile, ob0 + ob, VP, vp, kb)[lane];
+}
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  const float m1 = max3(a[0], a[1], a[2]);
+  const float m2 = max3(a[3], a[4], a[5]);
+  const float m3 = max3(a[6], a[7], a[8]);
+  const float m4 = max3(a[9], a[10], a[11]);
+  const float m5 = max3(a[12], a[13], a[14]);
+  return max3(max3(m1, m2, m3), max3(m4, m5, a[15]), a[15]);
+}
+
+// Lazy running maximum of a row over NT score tiles; returns the exponent offset -e*mu.
+template <int NT, int NOB>
+__device__ __attribute__((always_inline)) inline float pv_shift(const f32x16 (&acc)[NT], float e, float& mu,
+                                                                float& S, f32x16 (&O)[NOB]) {
+  float tm = max16(acc[0]);
+#pragma unroll
+  for (int t = 1; t < NT; ++t) tm = max3(tm, max16(acc[t]), tm);
+  const float to = __shfl_xor(tm, 32);
+  tm = max3(tm, to, to);
+  const bool raise = e * (tm - mu) > kLazy;
+  if (__any(raise)) {
+    const float mn = raise ? tm : mu;
+    const float sc = fast_exp2(e * (mu - mn));
+    S *= sc;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[ob][r] *= sc;
+    mu = mn;
+  }
+  return -e * mu;
+}
+
+// Plan entries of one score tile (terms <= 2^8), their sum, and their bf16 parts
+// as the B operands of two K blocks.
+template <int PP>
+__device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& acc, float e, float off,
+                                                               bf16x8 (&P)[PP][2]) {
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float v = fast_exp2(fmaf(acc[r], e, off));
+    if ((r & 3) == 0) s0 += v;
+    else if ((r & 3) == 1) s1 += v;
+    else if ((r & 3) == 2) s2 += v;
+    else s3 += v;
+    const __bf16 a = (__bf16)v;
+    P[0][r >> 3][r & 7] = a;
+    if constexpr (PP >= 2) {
+      const float r1 = v - (float)a;
+      const __bf16 b = (__bf16)r1;
+      P[1][r >> 3][r & 7] = b;
+      if constexpr (PP >= 3) P[2][r >> 3][r & 7] = (__bf16)(r1 - (float)b);
+    }
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// O[ob] += V[ob] x P over the products (pp, vp) of combined order below max(PP, VP).
+template <int NOB, int PP, int VP>
+__device__ __attribute__((always_inline)) inline void pv_mfma(const VTile<NOB, VP>& vt, const bf16x8 (&P)[PP][2],
+                                                              f32x16 (&O)[NOB]) {
+  constexpr int KMAX = PP > VP ? PP : VP;
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+      for (int vp = 0; vp < VP; ++vp)
+        if (pp + vp < KMAX) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            O[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt.v[ob][vp][kb], P[pp][kb], O[ob], 0, 0, 0);
+        }
+}
+
+// Output element (row i, value index cc) from the merged (mu, S, T) of the row.
+__device__ __forceinline__ void pv_store(const PvArgs& p, int i, int cc, float mu, float S, float T) {
+  const int64_t o = (int64_t)i * p.kv + cc;
+  if (p.grad) {
+    float xv;
+    if (p.xbf16) {
+      xv = __uint_as_float((unsigned)static_cast<const unsigned short*>(p.xrow)[o] << 16);
+    } else {
+      xv = static_cast<const float*>(p.xrow)[o];
+      if (p.shift) xv -= p.shift[cc];
+    }
+    p.out[o] = 2.0f * p.wrow[i] * (xv - T / S);
+  } else {
+    p.out[o] = T * fast_exp2(fmaf(p.escale, mu, p.hrow[i]));
+  }
+}
+
+// End of a workgroup: with one split, every lane writes its rows' outputs;
+// otherwise the partials (mu, S, T) go to the split buffer and the last
+// workgroup of the row block merges them in split order (bitwise repeatable).
+// Lanes of inactive waves hold nothing but take part in the barriers.
+template <int RB, int NOB>
+__device__ __attribute__((always_inline)) inline void pv_finish(
+    const PvArgs& p, bool active, int row_base, int rows_per_wg, const f32x16 (&O)[RB][NOB],
+    const float (&mu)[RB], const float (&S)[RB], int li, int half) {
+  constexpr int CW = NOB * 32;
+  const int sp = blockIdx.y, z = blockIdx.z;
+  const int cbase = z * CW;
+  float St[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) St[rb] = S[rb] + __shfl_xor(S[rb], 32);
+  if (p.splits == 1) {
+    if (!active) return;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = row_base + rb * 32 + li;
+      if (i >= p.nr) continue;
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cc = cbase + ob * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (cc < p.kv) pv_store(p, i, cc, mu[rb], St[rb], O[rb][ob][r]);
+        }
+    }
+    return;
+  }
+  const int64_t nslots = (int64_t)p.nchunks * p.splits;
+  float2* part_ms = reinterpret_cast<float2*>(p.part);
+  float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);  // 16-byte aligned value partials
+  const int64_t slot = (int64_t)z * p.splits + sp;
+  if (active) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = row_base + rb * 32 + li;
+      if (i >= p.nr) continue;
+      if (half == 0) part_ms[slot * p.nr + i] = make_float2(mu[rb], St[rb]);
+      float* T = part_t + (slot * p.nr + i) * CW;
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(T + ob * 32 + 8 * q + 4 * half) =
+              make_float4(O[rb][ob][4 * q], O[rb][ob][4 * q + 1], O[rb][ob][4 * q + 2], O[rb][ob][4 * q + 3]);
+    }
+  }
+  unsigned* counter = p.counters + (int64_t)z * p.row_blocks + blockIdx.x;
+  if (!arrive_last(counter, p.splits)) return;
+  const int row0 = blockIdx.x * rows_per_wg;
+  for (int q = threadIdx.x; q < rows_per_wg * CW; q += kThreads) {
+    const int i = row0 + q / CW;
+    const int c = q % CW;
+    if (i >= p.nr || cbase + c >= p.kv) continue;
+    float Mt = kMuInit;
+    for (int s2 = 0; s2 < p.splits; ++s2)
+      Mt = fmaxf(Mt, load_coherent(&part_ms[((int64_t)z * p.splits + s2) * p.nr + i].x));
+    float St2 = 0.0f, Tt = 0.0f;
+    for (int s2 = 0; s2 < p.splits; ++s2) {
+      const int64_t sl = ((int64_t)z * p.splits + s2) * p.nr + i;
+      const float f = fast_exp2(p.escale * (load_coherent(&part_ms[sl].x) - Mt));
+      St2 = fmaf(load_coherent(&part_ms[sl].y), f, St2);
+      Tt = fmaf(load_coherent(&part_t[sl * CW + c]), f, Tt);
+    }
+    pv_store(p, i, cbase + c, Mt, St2, Tt);
+  }
+  if (threadIdx.x == 0) atomicExch(counter, 0u);
+}
+
+// Register-resident rows (record widths up to 8 K blocks): each wave keeps RB
+// blocks of 32 row records and streams column tiles and their value fragments
+// from memory, one tile ahead.
+template <int NKB, int RB, int NOB, int PP, int VP>
+__global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
+  constexpr int RSB = NKB * 32;
+  constexpr int ROWS = 4 * RB * 32;
+  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
+  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const int ob0 = blockIdx.z * NOB;
+  const int j0 = blockIdx.y * p.cols_per_split;
+  const int j1 = min(p.nc, j0 + p.cols_per_split);
+  const int row_base = blockIdx.x * ROWS + wave * (RB * 32);
+  const float e = p.escale;
+
+  bf16x8 B[RB][NKB], Baug[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = row_base + rb * 32 + li;
+    const bf16x8* rec = reinterpret_cast<const bf16x8*>(rows + (int64_t)min(i, p.nr - 1) * RSB) + half * NKB;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
+    Baug[rb] = row_aug(half, 0.0f);
+  }
+  float mu[RB], S[RB];
+  f32x16 O[RB][NOB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    mu[rb] = kMuInit;
+    S[rb] = 0.0f;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) O[rb][ob] = f32x16{};
+  }
+
+  auto tile_work = [&](const ColTile<NKB>& ct, const VTile<NOB, VP>& vt) {
+    f32x16 acc[RB];
+    tile_mfma<NKB, RB>(ct, B, Baug, acc);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x16 a1[1] = {acc[rb]};
+      const float off = pv_shift<1, NOB>(a1, e, mu[rb], S[rb], O[rb]);
+      bf16x8 P[PP][2];
+      S[rb] += pv_probs<PP>(acc[rb], e, off, P);
+      pv_mfma<NOB, PP, VP>(vt, P, O[rb]);
+    }
+  };
+
+  // Tiles past the range read the padding (masked columns, zero values) or the
+  // next range; the loop below reads at most one tile past its last one.
+  const int ntiles = (j1 - j0 + 31) / 32;
+  const int64_t t0 = j0 / 32;
+  ColTile<NKB> c0, c1;
+  VTile<NOB, VP> v0, v1;
+  load_tile<NKB>(c0, cols, p.bias_col, j0, li, half);
+  load_vtile<NOB, VP>(v0, p, t0, ob0, lane);
+  for (int t = 0; t < ntiles; t += 2) {
+    load_tile<NKB>(c1, cols, p.bias_col, j0 + (t + 1) * 32, li, half);
+    load_vtile<NOB, VP>(v1, p, t0 + t + 1, ob0, lane);
+    tile_work(c0, v0);
+    if (t + 1 < ntiles) {
+      load_tile<NKB>(c0, cols, p.bias_col, j0 + (t + 2) * 32, li, half);
+      load_vtile<NOB, VP>(v0, p, t0 + t + 2, ob0, lane);
+      tile_work(c1, v1);
+    }
+  }
+  pv_finish<RB, NOB>(p, true, row_base, ROWS, O, mu, S, li, half);
+}
+
+// GEMM-tiled variant for wide records: the score block of a 2 x 2-wave
+// workgroup (128 rows x 128 columns per block, K streamed through LDS) feeds
+// the value products of each wave's 64 x 64 quarter; the two column waves of
+// a row pair merge their partials through LDS at the end.
+template <int NOB, int PP, int VP>
+__global__ __launch_bounds__(kThreads, 2) void k_pv_gemm(const PvArgs p, int nkb) {
+  __shared__ __attribute__((aligned(16))) GemmLds lds;
+  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
+  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const int ob0 = blockIdx.z * NOB;
+  const int j0 = blockIdx.y * p.cols_per_split;
+  const int j1 = min(p.nc, j0 + p.cols_per_split);
+  const int r0 = blockIdx.x * kGRows;
+  const float e = p.escale;
+
+  bf16x8 Baug[2];
+  float mu[2], S[2];
+  f32x16 O[2][NOB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    Baug[rb] = row_aug(half, 0.0f);
+    mu[rb] = kMuInit;
+    S[rb] = 0.0f;
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob) O[rb][ob] = f32x16{};
+  }
+
+  const int nkc = nkb / kGKb;
+  const int nblocks = (j1 - j0 + kGCols - 1) / kGCols;
+  const int nstages = nblocks * nkc;
+  GemmRegs g;
+  gemm_load(g, rows, cols, nkb, p.nr, r0, j0, 0);
+  gemm_store(g, lds, 0);
+  __syncthreads();
+  f32x16 acc[2][2];
+  for (int st = 0; st < nstages; ++st) {
+    const int blk = st / nkc, kc = st % nkc;
+    const int buf = st & 1;
+    if (st + 1 < nstages) {
+      const int nb = (st + 1) / nkc, nk = (st + 1) % nkc;
+      gemm_load(g, rows, cols, nkb, p.nr, r0, j0 + nb * kGCols, nk);
+    }
+    if (kc == 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[rb][ct] = f32x16{};
+    }
+#pragma unroll
+    for (int kb = 0; kb < kGKb; ++kb) {
+      bf16x8 A[2], Bm[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        A[ct] = *reinterpret_cast<const bf16x8*>(&lds.cols[buf][(wc * 64 + ct * 32 + li) * kGRow + half * 64 + kb * 16]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        Bm[rb] = *reinterpret_cast<const bf16x8*>(&lds.rows[buf][(wr * 64 + rb * 32 + li) * kGRow + half * 64 + kb * 16]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ct], Bm[rb], acc[rb][ct], 0, 0, 0);
+    }
+    // The next stage's operands go to LDS before the value products, so their
+    // staging registers are free during them.
+    if (st + 1 < nstages) gemm_store(g, lds, buf ^ 1);
+    if (kc == nkc - 1) {
+      const int cb = j0 + blk * kGCols + wc * 64;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bf16x8 Aaug = p.bias_col[2 * (int64_t)(cb + ct * 32 + li) + half];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aaug, Baug[rb], acc[rb][ct], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float off = pv_shift<2, NOB>(acc[rb], e, mu[rb], S[rb], O[rb]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          bf16x8 P[PP][2];
+          S[rb] += pv_probs<PP>(acc[rb][ct], e, off, P);
+#pragma unroll
+          for (int ob = 0; ob < NOB; ++ob) {
+            VTile<1, VP> vt;
+            load_vtile<1, VP>(vt, p, (cb >> 5) + ct, ob0 + ob, lane);
+            f32x16 (&Oob)[1] = *reinterpret_cast<f32x16(*)[1]>(&O[rb][ob]);
+            pv_mfma<1, PP, VP>(vt, P, Oob);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Column wave 1 hands its partials to column wave 0 of the same rows (same
+  // lane layout); the staging buffers are free after the last barrier.
+  constexpr int PER = 2 * (2 + NOB * 16);
+  static_assert(2 * PER * 64 * 4 <= (int)sizeof(GemmLds), "merge area exceeds the staging buffers");
+  float* xl = reinterpret_cast<float*>(&lds) + wr * PER * 64 + lane;
+  if (wc == 1) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      xl[(rb * (2 + NOB * 16)) * 64] = mu[rb];
+      xl[(rb * (2 + NOB * 16) + 1) * 64] = S[rb];
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xl[(rb * (2 + NOB * 16) + 2 + ob * 16 + r) * 64] = O[rb][ob][r];
+    }
+  }
+  __syncthreads();
+  if (wc == 0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mo = xl[(rb * (2 + NOB * 16)) * 64];
+      const float so = xl[(rb * (2 + NOB * 16) + 1) * 64];
+      const float mt = fmaxf(mu[rb], mo);
+      const float f0 = fast_exp2(e * (mu[rb] - mt)), f1 = fast_exp2(e * (mo - mt));
+      S[rb] = S[rb] * f0 + so * f1;
+#pragma unroll
+      for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          O[rb][ob][r] = O[rb][ob][r] * f0 + xl[(rb * (2 + NOB * 16) + 2 + ob * 16 + r) * 64] * f1;
+      mu[rb] = mt;
+    }
+  }
+  pv_finish<2, NOB>(p, wc == 0, r0 + wr * 64, kGRows, O, mu, S, li, half);
+}
+
+// Value fragment (tile t, value block ob, part vp, K block kb) in lane l
+// (h = l / 32): the values of index 32 ob + l % 32 at the eight points
+// 32 t + 16 kb + 8 (e / 4) + 4 h + e % 4, e = 0..7 -- the column order of a
+// score accumulator. Part vp of the three-part bf16 split; zeros past nv / kv.
+__global__ __launch_bounds__(256) void k_pack_values(const void* src, int src_bf16, int64_t nv, int kv,
+                                                     const float* shift, int vp_parts, int nobt,
+                                                     int64_t ntiles, bf16x8* out) {
+  const int64_t total = ntiles * nobt * vp_parts * 2 * 64;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx & 63);
+    int64_t q = idx >> 6;
+    const int kb = (int)(q & 1);
+    q >>= 1;
+    const int vp = (int)(q % vp_parts);
+    q /= vp_parts;
+    const int ob = (int)(q % nobt);
+    const int64_t t = q / nobt;
+    const int h = lane >> 5;
+    const int cc = ob * 32 + (lane & 31);
+    bf16x8 r = {};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t j = t * 32 + kb * 16 + 8 * (e >> 2) + 4 * h + (e & 3);
+      float v = 0.0f;
+      if (j < nv && cc < kv) {
+        if (src_bf16) {
+          v = __uint_as_float((unsigned)static_cast<const unsigned short*>(src)[j * kv + cc] << 16);
+        } else {
+          v = static_cast<const float*>(src)[j * kv + cc];
+          if (shift) v -= shift[cc];
+        }
+      }
+      __bf16 a, b, c;
+      split3(v, a, b, c);
+      r[e] = vp == 0 ? a : (vp == 1 ? b : c);
+    }
+    out[idx] = r;
+  }
+}
+
+// Row blocks per wave of the resident kernel: two where registers allow.
+constexpr int pv_rb(int nkb, int nob, int vp) { return (nkb <= 4 && nob * vp <= 2) ? 2 : 1; }
+
+template <int NKB, int RB, int NOB, int PP, int VP>
+bool try_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t s) {
+  if constexpr (pv_rb(NKB, NOB, VP) != RB) {
+    return false;
+  } else {
+    if (pp != PP || vp != VP) return false;
+    k_pv_mfma<NKB, RB, NOB, PP, VP><<<grid, kThreads, 0, s>>>(a);
+    return true;
+  }
+}
+
+template <int NKB, int RB, int NOB>
+hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t s) {
+  if (try_pv_mfma<NKB, RB, NOB, 3, 3>(a, pp, vp, grid, s) || try_pv_mfma<NKB, RB, NOB, 2, 2>(a, pp, vp, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 2, 1>(a, pp, vp, grid, s))
+    return hipGetLastError();
+  return hipErrorInvalidValue;
+}
+
+template <int NOB>
+hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& grid, hipStream_t s) {
+  if (pp == 3 && vp == 3) k_pv_gemm<NOB, 3, 3><<<grid, kThreads, 0, s>>>(a, nkb);
+  else if (pp == 2 && vp == 2) k_pv_gemm<NOB, 2, 2><<<grid, kThreads, 0, s>>>(a, nkb);
+  else if (pp == 2 && vp == 1) k_pv_gemm<NOB, 2, 1><<<grid, kThreads, 0, s>>>(a, nkb);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void pv_parts(int dtype, bool grad, int& pp, int& vp) {
+  if (dtype == 0) {
+    pp = 3;
+    vp = 3;
+  } else {
+    pp = 2;
+    vp = grad ? 1 : 2;
+  }
+}
+
+int pv_nob(int nobt) { return nobt >= 2 ? 2 : 1; }
+
+PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks) {
+  PassPlan pl;
+  pl.rows_per_block = gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32;
+  pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
+  const int64_t target = (gemm ? 1024 : 2048) / (nchunks > 0 ? nchunks : 1);
+  int64_t splits = (target + pl.row_blocks - 1) / pl.row_blocks;
+  const int64_t min_cols = gemm ? 512 : 1024;
+  const int64_t max_splits = nc / min_cols > 1 ? nc / min_cols : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  const int64_t unit = gemm ? kGCols : 64;
+  int64_t cps = (nc + splits - 1) / splits;
+  cps = (cps + unit - 1) / unit * unit;
+  pl.cols_per_split = (int)cps;
+  pl.splits = (int)((nc + cps - 1) / cps);
+  return pl;
+}
+
+hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+                     const PassPlan& pl, hipStream_t s) {
+  const dim3 grid(pl.row_blocks, pl.splits, a.nchunks);
+  if (gemm) {
+    if (nob == 1) return run_pv_gemm<1>(a, nkb, pp, vp, grid, s);
+    if (nob == 2) return run_pv_gemm<2>(a, nkb, pp, vp, grid, s);
+    return hipErrorInvalidValue;
+  }
+  const int rb = pv_rb(nkb, nob, vp);
+  const int key = nkb * 100 + rb * 10 + nob;
+  switch (key) {
+    case 111: return run_pv_mfma<1, 1, 1>(a, pp, vp, grid, s);
+    case 121: return run_pv_mfma<1, 2, 1>(a, pp, vp, grid, s);
+    case 122: return run_pv_mfma<1, 2, 2>(a, pp, vp, grid, s);
+    case 112: return run_pv_mfma<1, 1, 2>(a, pp, vp, grid, s);
+    case 221: return run_pv_mfma<2, 2, 1>(a, pp, vp, grid, s);
+    case 222: return run_pv_mfma<2, 2, 2>(a, pp, vp, grid, s);
+    case 211: return run_pv_mfma<2, 1, 1>(a, pp, vp, grid, s);
+    case 212: return run_pv_mfma<2, 1, 2>(a, pp, vp, grid, s);
+    case 421: return run_pv_mfma<4, 2, 1>(a, pp, vp, grid, s);
+    case 422: return run_pv_mfma<4, 2, 2>(a, pp, vp, grid, s);
+    case 411: return run_pv_mfma<4, 1, 1>(a, pp, vp, grid, s);
+    case 412: return run_pv_mfma<4, 1, 2>(a, pp, vp, grid, s);
+    case 811: return run_pv_mfma<8, 1, 1>(a, pp, vp, grid, s);
+    case 812: return run_pv_mfma<8, 1, 2>(a, pp, vp, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
+                              int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s) {
+  const int64_t total = ntiles * nobt * vp * 2 * 64;
+  const int64_t blocks = (total + 255) / 256;
+  k_pack_values<<<(int)(blocks < 8192 ? blocks : 8192), 256, 0, s>>>(src, src_bf16 ? 1 : 0, nv, kv, shift,
+                                                                     vp, nobt, ntiles, out);
+  return hipGetLastError();
+}
+
+}  // namespace sk

@@ -38,6 +38,33 @@ struct MfmaPassArgs {
   int symmetric;
 };
 
+// Weighted sums over the columns of the half-pass scores, on the matrix cores:
+//   apply: out_i = sum_j 2^{hrow_i + e acc_ij} V_j                 (kv = k)
+//   grad:  out_i = 2 a_i (x_i - sum_j 2^{e acc_ij} q_j / sum_j 2^{e acc_ij})  (kv = d)
+// acc_ij = score + column bias, as in a half-pass with no row shift. Values
+// come as fragments (pack_values); a launch covers value blocks
+// [z * NOB, z * NOB + NOB) for z = blockIdx.z.
+struct PvArgs {
+  const void* rows;        // nr row-form records
+  const void* cols;        // nc column-form records (padded)
+  const bf16x8* bias_col;  // nc bias records of the columns (padded)
+  const bf16x8* vfrag;     // value fragments of the columns (padded)
+  int nobt;                // value blocks (of 32) per tile in vfrag
+  int kv;                  // value width; out is nr x kv, row-major
+  float* out;
+  const float* hrow;       // apply: nr row biases (log2 units)
+  const float* wrow;       // grad: nr row weights
+  const void* xrow;        // grad: nr x kv row points as stored
+  int xbf16;               // grad: row points are bf16
+  const float* shift;      // grad: centering shift of float32 points (or null)
+  int grad;
+  float* part;             // split partials: (mu, S) pairs then values, per (chunk, split)
+  unsigned* counters;      // chunks x row_blocks, zero on entry and exit
+  int nr, nc, row_blocks, nchunks;
+  int splits, cols_per_split;
+  float escale;
+};
+
 struct MfmaPrepSide {
   const void* pts;   // n x d as stored
   const float* w;    // weights
@@ -65,6 +92,16 @@ int gemm_nkb(int dtype, int d);
 PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
 hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
                            const PassPlan& pl, hipStream_t s);
+// Transport application / gradient kernels. pv_parts: bf16 parts of the plan
+// entries (pp) and of the values (vp) for a storage type and operation.
+void pv_parts(int dtype, bool grad, int& pp, int& vp);
+int pv_nob(int nobt);  // value blocks per launch chunk
+PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
+hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+                     const PassPlan& pl, hipStream_t s);
+// Value fragments of nv points (src nv x kv, float32 or bf16 bits) for vp parts.
+hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
+                              int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s);
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
                             int nkb, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,

@@ -155,6 +155,89 @@ __device__ inline float block_max(float v, float* red) {
 
 constexpr float kShiftedFloor = 0x1p-60f;  // below this a shifted sum is recomputed exactly
 
+// ---------------------------------------------------------------- column tiles
+// Column operands of one 32-column tile for this lane: its half of the record
+// of column (tile start + li), NKB data chunks plus the bias chunk.
+template <int NKB>
+struct ColTile {
+  bf16x8 a[NKB];
+  bf16x8 aug;
+};
+
+// Record and bias arrays are padded past the last column with masked columns
+// (zero data, masked bias) for five extra tiles, so a tile load needs no
+// bounds test: the loads are plain and can be issued well ahead of use.
+template <int NKB>
+__device__ __attribute__((always_inline)) inline void load_tile(
+    ColTile<NKB>& ct, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
+    int jt, int li, int half) {
+  const int j = jt + li;
+  const bf16x8* rec = reinterpret_cast<const bf16x8*>(cols + (int64_t)j * (NKB * 32)) + half * NKB;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = rec[kb];
+  ct.aug = bias[2 * (int64_t)j + half];
+}
+
+// MFMA products of one 32-column tile against the RB row blocks.
+template <int NKB, int RB>
+__device__ __attribute__((always_inline)) inline void tile_mfma(
+    const ColTile<NKB>& ct, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB], f32x16 (&acc)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    f32x16 a = {};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.a[kb], B[rb][kb], a, 0, 0, 0);
+    acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.aug, Baug[rb], a, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM-tiled staging
+// Workgroups of 2 x 2 waves own 128 rows and sweep columns in blocks of 128;
+// both operands stream through LDS in chunks of 4 K blocks.
+constexpr int kGRows = 128;   // rows per workgroup
+constexpr int kGCols = 128;   // columns per block
+constexpr int kGKb = 4;       // K blocks (16 slots) per LDS stage
+constexpr int kGRow = kGKb * 2 * 16 + 16;  // LDS bytes per record per stage (both halves + pad)
+
+struct GemmLds {
+  unsigned char rows[2][kGRows * kGRow];
+  unsigned char cols[2][kGCols * kGRow];
+};
+
+struct GemmRegs {
+  u32x4 r[4];  // 1024 row chunks / 256 threads
+  u32x4 c[4];  // 1024 column chunks / 256 threads
+};
+
+// Stage s of the flattened (column block, K chunk) sequence: chunk (kc) of the
+// K dimension for rows [r0, r0+128) and columns [c0, c0+128). A chunk is, per
+// record, 4 x 16 bytes in each half: record bytes [h*NKB*16 + kc*64, +64).
+__device__ __attribute__((always_inline)) inline void gemm_load(
+    GemmRegs& g, const unsigned char* __restrict__ rows, const unsigned char* __restrict__ cols,
+    int nkb, int nr, int r0, int c0, int kc) {
+  const int64_t rsb = (int64_t)nkb * 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ch = threadIdx.x + q * kThreads;  // 0..1023: record (ch >> 3), half ((ch >> 2) & 1), part (ch & 3)
+    const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+    const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
+    g.r[q] = *reinterpret_cast<const u32x4*>(rows + (int64_t)min(r0 + rec, nr - 1) * rsb + off);
+    g.c[q] = *reinterpret_cast<const u32x4*>(cols + (int64_t)(c0 + rec) * rsb + off);
+  }
+}
+
+__device__ __attribute__((always_inline)) inline void gemm_store(const GemmRegs& g, GemmLds& L, int buf) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ch = threadIdx.x + q * kThreads;
+    const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+    const int o = rec * kGRow + hh * 64 + part * 16;
+    *reinterpret_cast<u32x4*>(&L.rows[buf][o]) = g.r[q];
+    *reinterpret_cast<u32x4*>(&L.cols[buf][o]) = g.c[q];
+  }
+}
+
+
 
 }  // namespace dev
 }  // namespace sk

@@ -191,7 +191,18 @@ def test_translation_invariance(sk):
     assert abs(float(c1) - float(c2)) <= 1e-5 * abs(float(c1))
 
 
-@pytest.mark.parametrize("key,n,m", [(2, 1500, 2100), (1, 1000, 333), (1, 1, 50)])
+GRAD_CASES = [
+    (2, 1500, 2100),   # float32 d = 3, symmetric-schedule potentials
+    (1, 1000, 333),    # one column split
+    (1, 1, 50),
+    (6, 1200, 5000),   # several column splits
+    (3, 2000, 1500),   # bf16 d = 64: two value blocks
+    (4, 600, 700),     # float32 d = 512: GEMM-tiled, 16 value blocks in 8 chunks
+    (7, 500, 333),     # bf16 d = 512
+]
+
+
+@pytest.mark.parametrize("key,n,m", GRAD_CASES)
 def test_grad_matches_oracle(sk, key, n, m):
     w = W.CONFIGS[key].scaled(n, m, 10)
     say(f"grad cfg={key} n={n} m={m}")
@@ -205,7 +216,19 @@ def test_grad_matches_oracle(sk, key, n, m):
     assert err <= tol_rel(w)
 
 
-@pytest.mark.parametrize("key,n,m,k", [(1, 1000, 333, 16), (6, 1200, 1900, 5), (1, 1, 40, 3), (1, 64, 64, 64)])
+APPLY_CASES = [
+    (1, 1000, 333, 16),
+    (6, 1200, 1900, 5),
+    (1, 1, 40, 3),
+    (1, 64, 64, 64),     # two value blocks
+    (3, 1000, 1500, 64), # bf16 d = 64
+    (3, 500, 3000, 7),
+    (5, 300, 1300, 16),  # bf16 d = 1024, GEMM-tiled
+    (4, 600, 700, 40),   # float32 d = 512, two value blocks
+]
+
+
+@pytest.mark.parametrize("key,n,m,k", APPLY_CASES)
 def test_apply_matches_oracle(sk, key, n, m, k):
     w = W.CONFIGS[key].scaled(n, m, 10)
     say(f"apply cfg={key} n={n} m={m} k={k}")
@@ -222,6 +245,60 @@ def test_apply_matches_oracle(sk, key, n, m, k):
     e2 = np.abs(PtU - reft).max() / np.abs(reft).max()
     say(f"  rel err P.V {e1:.3e}  P^T.U {e2:.3e}")
     assert e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
+AUX_DIMS = [("f32", 16), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7), ("bf16", 200), ("f32", 130)]
+
+
+@pytest.mark.parametrize("dtype,d", AUX_DIMS)
+def test_grad_apply_other_dimensions(sk, dtype, d):
+    from dataclasses import replace
+    w = replace(W.CONFIGS[4], d=d, dtype=dtype, eps=0.2, name=f"gauss_d{d}_{dtype}").scaled(700, 1300, 5)
+    say(f"grad/apply d={d} {dtype}")
+    inp = W.make_inputs(w, k=40)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    grad = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()
+    ref = oracle.grad_x(inp.x64(), inp.y64(), inp.a, inp.b, g64, w.eps)
+    eg = np.abs(grad - ref).max() / np.abs(ref).max()
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+    PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy()
+    PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy()
+    ref1 = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.V)
+    ref2 = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.U, transpose=True)
+    e1 = np.abs(PV - ref1).max() / np.abs(ref1).max()
+    e2 = np.abs(PtU - ref2).max() / np.abs(ref2).max()
+    say(f"  rel err grad {eg:.3e}  P.V {e1:.3e}  P^T.U {e2:.3e}")
+    assert eg <= tol_rel(w) and e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
+@pytest.mark.parametrize("key,scale", [(1, 0.5), (3, 0.3), (4, 2.0)])
+def test_apply_arbitrary_potentials(sk, key, scale):
+    """Plan entries spread over many orders of magnitude (potentials not from a solve)."""
+    w = W.CONFIGS[key].scaled(700, 900, 1)
+    say(f"apply cfg={key} arbitrary potentials scale={scale}")
+    inp = W.make_inputs(w, k=16)
+    x, y, a, b = dev(inp)
+    fs, gs = W.random_potentials(w.n, w.m, scale, seed=11)
+    f, g = torch.from_numpy(fs).to(DEV), torch.from_numpy(gs).to(DEV)
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+    PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy()
+    PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy()
+    f64, g64 = fs.astype(np.float64), gs.astype(np.float64)
+    ref1 = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.V)
+    ref2 = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.U, transpose=True)
+    # row-wise relative error: each row of P V has its own scale here
+    r1 = np.abs(PV - ref1).max(axis=1) / np.maximum(np.abs(ref1).max(axis=1), 1e-300)
+    r2 = np.abs(PtU - ref2).max(axis=1) / np.maximum(np.abs(ref2).max(axis=1), 1e-300)
+    say(f"  worst row rel err P.V {r1.max():.3e}  P^T.U {r2.max():.3e}")
+    tol = 1e-3 if w.dtype == "bf16" else 1e-4
+    assert r1.max() <= tol and r2.max() <= tol
+    gr = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()
+    refg = oracle.grad_x(inp.x64(), inp.y64(), inp.a, inp.b, g64, w.eps)
+    eg = np.abs(gr - refg).max() / np.abs(refg).max()
+    say(f"  grad rel err {eg:.3e}")
+    assert eg <= tol_rel(w)
 
 
 @pytest.mark.parametrize("key", [2, 6])
