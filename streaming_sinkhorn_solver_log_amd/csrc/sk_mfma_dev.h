@@ -86,14 +86,11 @@ __device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, f
   return dh;
 }
 
-// max(a, b, c) in one instruction. Written as inline assembly because the
-// compiler otherwise quiets each MFMA result before a max (IEEE mode), which
-// costs an extra instruction per score; a NaN score still reaches the sum
-// through exp2 and propagates.
+// max(a, b, c): one v_maximum3_f32 (IEEE maximum: a NaN operand gives NaN, so
+// a NaN score still propagates to the sum). Plain builtins, so the compiler
+// places the wait states an MFMA result needs before a vector-ALU read.
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // Online update of a lane's running (M, S) with one 32x32 tile (16 scores per lane).

@@ -179,6 +179,28 @@ def test_repeatable_and_swap_symmetric(sk):
     assert torch.equal(fs, r1[1]) and torch.equal(gs, r1[0])
 
 
+@pytest.mark.parametrize("key,n,m", [(3, 6000, 5000), (7, 700, 900), (6, 3000, 2500)])
+def test_bitwise_repeatable_all_kernels(sk, key, n, m):
+    """Every kernel family (register-resident, LDS-staged, GEMM-tiled half-pass; gradient;
+    transport application) gives bitwise identical results on repeated calls."""
+    w = W.CONFIGS[key].scaled(n, m, 4)
+    say(f"repeatability cfg={key} n={n} m={m} d={w.d} {w.dtype}")
+    inp = W.make_inputs(w, k=16)
+    x, y, a, b = dev(inp)
+    V = torch.from_numpy(inp.V).to(DEV)
+    ref = None
+    for _ in range(4):
+        f, g, c = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+        gr = sk.eot_grad_x(x, y, a, b, g, w.eps)
+        pv = sk.transport_apply(x, y, a, b, f, g, w.eps, V)
+        cur = (f, g, c, gr, pv)
+        if ref is None:
+            ref = cur
+        else:
+            for r, t in zip(ref, cur):
+                assert torch.equal(r, t)
+
+
 def test_translation_invariance(sk):
     w = W.CONFIGS[1].scaled(800, 900, 10)
     say("translation invariance")
