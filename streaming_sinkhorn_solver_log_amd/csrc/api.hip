@@ -409,6 +409,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pf.exact_count = L.c.exact_count;
     pf.part = L.c.part; pf.counters = L.c.counters;
     pf.nr = (int)n; pf.nc = (int)m; pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
+    pf.row_blocks = sp.f.row_blocks; pf.stages = sp.f.stages;
     pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
     pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
     if ((e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
@@ -418,6 +419,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pg.Lout = L.ym.L; pg.Lin = L.ym.L; pg.hval_in = L.ym.hval[cur]; pg.hval_out = L.ym.hval[nxt];
     pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
+    pg.row_blocks = sp.g.row_blocks; pg.stages = sp.g.stages;
     if ((e = launch_pass(sp, pg, shifted, scaled, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
     cur = nxt;
   }

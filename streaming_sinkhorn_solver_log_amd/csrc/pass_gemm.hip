@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_gemm(const MfmaPassArgs p, 
 }  // namespace
 
 PassPlan plan_gemm_pass(int64_t nr, int64_t nc) {
-  PassPlan pl;
+  PassPlan pl{};
   pl.rows_per_block = kGRows;
   pl.row_blocks = (int)((nr + kGRows - 1) / kGRows);
   const int64_t target = 1024;  // two workgroups per CU (LDS bound), two waves of them

@@ -57,194 +57,141 @@ __device__ __attribute__((always_inline)) inline void tile_valu(const f32x16 (&a
   }
 }
 
-// One sweep of a wave over columns [j0, j1). SHIFTED: the row shift is folded
-// into Baug and the sums need no running maximum; otherwise online
-// max/sum-exp. Each wave streams its column records straight from memory (the
-// four waves of a workgroup read the same columns, so the L1 cache serves the
-// reuse), keeps two tiles of loads in flight ahead of use, and issues the
-// MFMAs of tile t+1 before the exp/sum work of tile t. There is no LDS staging
-// and no barrier, so waves never wait for each other.
+// ---------------------------------------------------------------- column staging
+// Column records stream into LDS by direct global-to-LDS loads
+// (global_load_lds_dwordx4), four tiles (128 columns) per stage, in a ring of
+// stages. A tile's image in LDS is NKB + 1 blocks of 1 KB; block kb holds, at
+// lane l's 16 bytes, exactly the A operand lane l needs (its half l / 32 of
+// K block kb of column tile + l % 32; block NKB is the bias chunk), so the
+// compute waves read it back with conflict-free 16-byte reads. The four waves
+// of the workgroup share the loads (one per block) and one barrier per stage.
+constexpr int kStageTiles = 4;
+constexpr int kStageCols = kStageTiles * 32;
+template <int NKB>
+constexpr int kRing = NKB >= 4 ? 2 : 3;  // stages in flight (LDS: ring x 4 x (NKB + 1) KB)
+
+template <int NKB>
+struct StageRing {
+  bf16x8 blk[kRing<NKB>][kStageTiles][NKB + 1][64];
+};
+
+// s_waitcnt vmcnt(N), other counters not waited on (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// One 16-byte-per-lane global-to-LDS load: lane l's 16 bytes land at
+// lds_addr + 16 l. Written as inline assembly so that the compiler does not
+// treat the in-flight load as aliasing every later LDS read (it would wait for
+// all of them); completion is waited for explicitly with vmcnt.
+__device__ __forceinline__ void load_to_lds(const void* src, const void* lds_dst) {
+  const unsigned m0 = (unsigned)(uintptr_t)lds_dst;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// This wave's share of stage [c0, c0 + 128): blocks wave, wave + 4, ... of the
+// 4 (NKB + 1) blocks. Columns past the range read the padding (masked) or the
+// next range; they are never summed.
+template <int NKB>
+__device__ __attribute__((always_inline)) inline void issue_stage(
+    StageRing<NKB>& L, int slot, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
+    int c0, int wave, int lane) {
+  constexpr int NB = kStageTiles * (NKB + 1);
+  static_assert(NB % 4 == 0, "blocks of a stage split evenly over four waves");
+  const int li = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int q = 0; q < NB / 4; ++q) {
+    const int b = wave + 4 * q;
+    const int tt = b / (NKB + 1), kb = b % (NKB + 1);
+    const int col = c0 + tt * 32 + li;
+    const void* src = (kb < NKB)
+        ? static_cast<const void*>(cols + (int64_t)col * (NKB * 32) + h * (NKB * 16) + kb * 16)
+        : static_cast<const void*>(bias + 2 * (int64_t)col + h);
+    load_to_lds(src, &L.blk[slot][tt][kb][0]);
+  }
+}
+
+// One sweep of the workgroup over columns [j0, j1), j0 a multiple of 128.
+// SHIFTED: the row shift is folded into Baug and the sums need no running
+// maximum; otherwise online max/sum-exp. Ends with a barrier (LDS reusable).
 template <int NKB, int RB, bool SHIFTED, bool SCALED>
 __device__ __attribute__((always_inline)) inline void sweep(
-    const MfmaPassArgs& p, int j0, int j1, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB],
-    float (&M)[RB], float (&S)[RB], int li, int half) {
+    const MfmaPassArgs& p, StageRing<NKB>& L, int j0, int j1, const bf16x8 (&B)[RB][NKB],
+    const bf16x8 (&Baug)[RB], float (&M)[RB], float (&S)[RB], int lane, int wave) {
+  constexpr int R = kRing<NKB>;
+  constexpr int PER = kStageTiles * (NKB + 1) / 4;  // loads per wave per stage
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
-  const bf16x8* __restrict__ bias = p.bias_col;
-  const int ntiles = (j1 - j0 + 31) / 32;
-  ColTile<NKB> c0, c1;
-  f32x16 acc0[RB], acc1[RB];
-  // Prefetch loads run up to four tiles past the range: they read the next
-  // range's columns or the padding, and their products are never summed.
-  load_tile<NKB>(c0, cols, bias, j0, li, half);
-  load_tile<NKB>(c1, cols, bias, j0 + 32, li, half);
-  tile_mfma<NKB, RB>(c0, B, Baug, acc0);
-  load_tile<NKB>(c0, cols, bias, j0 + 64, li, half);
-  for (int t = 0; t < ntiles; t += 2) {
-    // here: acc0 = tile t (issued), c1 = tile t+1, c0 = tile t+2 (loads in flight)
-    tile_mfma<NKB, RB>(c1, B, Baug, acc1);
-    load_tile<NKB>(c1, cols, bias, j0 + (t + 3) * 32, li, half);
-    tile_valu<RB, SHIFTED, SCALED>(acc0, p.escale, M, S);
-    tile_mfma<NKB, RB>(c0, B, Baug, acc0);
-    load_tile<NKB>(c0, cols, bias, j0 + (t + 4) * 32, li, half);
-    if (t + 1 < ntiles) tile_valu<RB, SHIFTED, SCALED>(acc1, p.escale, M, S);
-  }
-}
-
-// LDS-staged variant of the sweep for wide records (NKB >= 4): the workgroup
-// stages 64 columns at a time through LDS (double buffered, one barrier per
-// stage), so the four waves share one copy of each column record instead of
-// each pulling it through the L1 cache.
-constexpr int kStageCols = 64;
-
-template <int NKB>
-struct StageLds {
-  static constexpr int kRow = NKB * 32 + 16;  // padded record row (bytes) against bank conflicts
-  unsigned char dat[2][kStageCols * kRow];
-  bf16x8 aug[2][2 * kStageCols];             // [buffer][half * 64 + column]
-};
-
-template <int CPT>
-struct StageRegs {
-  u32x4 d[CPT];
-  bf16x8 aug;
-};
-
-// Thread t moves data chunks t, t + 256, ... and bias chunk t % 128 of a stage.
-// Columns past the range read the padding or the next range (never summed).
-template <int NKB, int CPT>
-__device__ __attribute__((always_inline)) inline void load_stage(
-    StageRegs<CPT>& sr, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias, int s0) {
-  constexpr int CHUNKS = kStageCols * NKB * 2;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    int ch = threadIdx.x + c * kThreads;
-    if constexpr (CHUNKS % kThreads != 0) ch = min(ch, CHUNKS - 1);
-    const int col = ch / (NKB * 2), part = ch % (NKB * 2);
-    sr.d[c] = *reinterpret_cast<const u32x4*>(cols + (int64_t)(s0 + col) * (NKB * 32) + part * 16);
-  }
-  const int ach = threadIdx.x & (2 * kStageCols - 1);
-  sr.aug = bias[2 * (int64_t)(s0 + (ach >> 1)) + (ach & 1)];
-}
-
-template <int NKB, int CPT>
-__device__ __attribute__((always_inline)) inline void store_stage(const StageRegs<CPT>& sr,
-                                                                  StageLds<NKB>& L, int buf) {
-  constexpr int CHUNKS = kStageCols * NKB * 2;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int ch = threadIdx.x + c * kThreads;
-    if (CHUNKS % kThreads == 0 || ch < CHUNKS) {
-      const int col = ch / (NKB * 2), part = ch % (NKB * 2);
-      *reinterpret_cast<u32x4*>(&L.dat[buf][col * StageLds<NKB>::kRow + part * 16]) = sr.d[c];
-    }
-  }
-  if (threadIdx.x < 2 * kStageCols)
-    L.aug[buf][(threadIdx.x & 1) * kStageCols + (threadIdx.x >> 1)] = sr.aug;
-}
-
-template <int NKB, int RB, bool SHIFTED, bool SCALED>
-__device__ __attribute__((always_inline)) inline void sweep_lds(
-    const MfmaPassArgs& p, StageLds<NKB>& L, int j0, int j1, const bf16x8 (&B)[RB][NKB],
-    const bf16x8 (&Baug)[RB], float (&M)[RB], float (&S)[RB], int li, int half) {
-  constexpr int CPT = (kStageCols * NKB * 2 + kThreads - 1) / kThreads;
-  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
-  StageRegs<CPT> sr;
   const int nstages = (j1 - j0 + kStageCols - 1) / kStageCols;
-  load_stage<NKB, CPT>(sr, cols, p.bias_col, j0);
-  store_stage<NKB, CPT>(sr, L, 0);
-  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < R - 1; ++q)
+    if (q < nstages) issue_stage<NKB>(L, q, cols, p.bias_col, j0 + q * kStageCols, wave, lane);
   for (int st = 0; st < nstages; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nstages) load_stage<NKB, CPT>(sr, cols, p.bias_col, j0 + (st + 1) * kStageCols);
-#pragma unroll
-    for (int t = 0; t < kStageCols / 32; ++t) {
-      const int col = t * 32 + li;
-      ColTile<NKB> ct;
-      const bf16x8* arow = reinterpret_cast<const bf16x8*>(&L.dat[buf][col * StageLds<NKB>::kRow]) + half * NKB;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = arow[kb];
-      ct.aug = L.aug[buf][half * kStageCols + col];
-      f32x16 acc[RB];
-      tile_mfma<NKB, RB>(ct, B, Baug, acc);
-      tile_valu<RB, SHIFTED, SCALED>(acc, p.escale, M, S);
+    // this wave's loads of stage st are done once at most the later stages'
+    // loads are outstanding; the barrier then covers every wave's loads
+    if constexpr (R == 3) {
+      if (st + 1 < nstages) wait_vmcnt<PER>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (st + 1 < nstages) store_stage<NKB, CPT>(sr, L, buf ^ 1);
     __syncthreads();
+    // slot (st - 1) % R is free: every wave finished stage st - 1 before the barrier
+    if (st + R - 1 < nstages)
+      issue_stage<NKB>(L, (st + R - 1) % R, cols, p.bias_col, j0 + (st + R - 1) * kStageCols, wave, lane);
+    const int slot = st % R;
+    auto stage_tile = [&](ColTile<NKB>& ct, int tt) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = L.blk[slot][tt][kb][lane];
+      ct.aug = L.blk[slot][tt][NKB][lane];
+    };
+    if constexpr (NKB <= 4) {
+      // MFMAs of tile tt + 1 are issued before the exp/sum work of tile tt
+      f32x16 acc[2][RB];
+      ColTile<NKB> ct;
+      stage_tile(ct, 0);
+      tile_mfma<NKB, RB>(ct, B, Baug, acc[0]);
+#pragma unroll
+      for (int tt = 0; tt < kStageTiles; ++tt) {
+        if (tt + 1 < kStageTiles) {
+          stage_tile(ct, tt + 1);
+          tile_mfma<NKB, RB>(ct, B, Baug, acc[(tt + 1) & 1]);
+        }
+        tile_valu<RB, SHIFTED, SCALED>(acc[tt & 1], p.escale, M, S);
+      }
+    } else {
+      // wide records: registers do not allow a second tile of accumulators
+#pragma unroll
+      for (int tt = 0; tt < kStageTiles; ++tt) {
+        ColTile<NKB> ct;
+        stage_tile(ct, tt);
+        f32x16 acc[RB];
+        tile_mfma<NKB, RB>(ct, B, Baug, acc);
+        tile_valu<RB, SHIFTED, SCALED>(acc, p.escale, M, S);
+      }
+    }
   }
+  __syncthreads();
 }
 
-// Per record width, the sweep that serves it best: narrow records stream
-// per wave, wide records are staged through LDS.
-template <int NKB>
-constexpr bool kUseLds = NKB >= 4;
+// ---------------------------------------------------------------- work split
+// The pass is R row blocks x T stages (128 columns) = U units. Workgroup w of
+// W takes units [w U / W, (w + 1) U / W) in row-block-major order: every
+// workgroup gets the same amount of work (within one unit) and the grid is
+// one wave of resident workgroups. A row block split between workgroups is
+// merged from per-workgroup partials by the last one to arrive, in
+// workgroup order, so results do not depend on timing.
+__device__ __forceinline__ int64_t unit_begin(int64_t w, int64_t W, int64_t U) { return w * U / W; }
+__device__ __forceinline__ int64_t unit_owner(int64_t u, int64_t W, int64_t U) {
+  return ((u + 1) * W - 1) / U;  // the workgroup whose range holds unit u
+}
 
-template <int NKB>
-struct SweepLds {
-  StageLds<NKB> s;
-};
-struct NoLds {};
-
-// One half-pass. SHIFTED (every pass after a side's first): the row shift
-// M_i = L_i(previous pass) + max_j (change of h_j since then) bounds every
-// term by 1, so the sum cannot overflow; a row whose sum falls below 2^-60
-// (shift far too high) is recomputed by an exact online-max sweep over all
-// columns, done by the workgroup that completes the row's block.
-template <int NKB, int RB, bool SHIFTED, bool SCALED>
-__global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
-  constexpr int RSB = NKB * 32;
-  constexpr int ROWS = 4 * RB * 32;
-  __shared__ float red[kThreads / 64];
-  __shared__ __attribute__((aligned(16))) std::conditional_t<kUseLds<NKB>, StageLds<NKB>, NoLds> lds;
-
-  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int li = lane & 31;
-  const int sp = blockIdx.y;
-  const int j0 = sp * p.cols_per_split;
-  const int j1 = min(p.nc, j0 + p.cols_per_split);
-  const int row_base = blockIdx.x * ROWS + wave * (RB * 32);
-
-  bf16x8 B[RB][NKB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int i = row_base + rb * 32 + li;
-    const bf16x8* rec = reinterpret_cast<const bf16x8*>(rows + (int64_t)min(i, p.nr - 1) * RSB) + half * NKB;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
-  }
-  float M[RB], S[RB];
-  bf16x8 Baug[RB];
-  float shift_row[RB];
-  if constexpr (SHIFTED) {
-    // largest change of a column bias since this side's previous pass
-    float dm = -INFINITY;
-    for (int q = threadIdx.x; q < p.n_dmax_in; q += kThreads) dm = fmaxf(dm, p.dmax_in[q]);
-    const float dmax = block_max(dm, red);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = min(row_base + rb * 32 + li, p.nr - 1);
-      shift_row[rb] = p.Lin[i] + dmax;  // log2 units
-      Baug[rb] = row_aug(half, -shift_row[rb] / p.escale);
-      M[rb] = 0.0f;
-      S[rb] = 0.0f;
-    }
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      Baug[rb] = row_aug(half, 0.0f);
-      M[rb] = -INFINITY;
-      S[rb] = 0.0f;
-      shift_row[rb] = 0.0f;
-    }
-  }
-
-  if constexpr (kUseLds<NKB>) sweep_lds<NKB, RB, SHIFTED, SCALED>(p, lds, j0, j1, B, Baug, M, S, li, half);
-  else sweep<NKB, RB, SHIFTED, SCALED>(p, j0, j1, B, Baug, M, S, li, half);
-
-  // Per row (lanes of half 0): (Lm, Ls) with L = Lm + log2 Ls, Lm in log2 units.
-  float Lm[RB], Ls[RB];
+// Row results of one row block: (Lm, Ls) per row with L = Lm + log2 Ls (log2
+// units), in lanes of half 0.
+template <int RB, bool SHIFTED>
+__device__ __forceinline__ void row_sums(const MfmaPassArgs& p, const float (&M)[RB], const float (&S)[RB],
+                                         const float (&shift_row)[RB], float (&Lm)[RB], float (&Ls)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float So = __shfl_xor(S[rb], 32);
@@ -259,83 +206,150 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
       Lm[rb] = p.escale * Mt;
     }
   }
+}
 
-  float dh = -INFINITY;  // this thread's largest bias change over the rows it finishes
-  bool need_exact = false;
-  if (p.splits == 1) {
-    bool bad = false;
-    if constexpr (SHIFTED) {
-      if (half == 0)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          bad |= (row_base + rb * 32 + li < p.nr) && !(Ls[rb] >= kShiftedFloor);
-      need_exact = __syncthreads_or(bad);
-    }
-    if (!need_exact && half == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int i = row_base + rb * 32 + li;
-        if (i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, Lm[rb] + fast_log2(Ls[rb])));
-      }
-    }
-  } else {
-    if (half == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int i = row_base + rb * 32 + li;
-        if (i < p.nr) p.part[(int64_t)sp * p.nr + i] = make_float2(Lm[rb], Ls[rb]);
-      }
-    }
-    if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
-    // The completing workgroup merges the splits of its rows in split order.
-    float Lr = 0.0f;
-    bool bad = false;
-    const int i = blockIdx.x * ROWS + (int)threadIdx.x;
-    const bool mine = (int)threadIdx.x < ROWS && i < p.nr;
-    if (mine) {
-      float Mt = -INFINITY;
-      for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
-      const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
-      float St = 0.0f;
-      for (int s2 = 0; s2 < p.splits; ++s2) {
-        const float Mp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].x);
-        const float Sp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].y);
-        St = fmaf(Sp, fast_exp2(Mp - Me), St);
-      }
-      Lr = Mt + fast_log2(St);
-      bad = SHIFTED && !(St >= kShiftedFloor);
-    }
-    if constexpr (SHIFTED) need_exact = __syncthreads_or(bad);
-    if (!need_exact && mine) dh = finish_row_mfma(p, i, Lr);
-    if (threadIdx.x == 0) atomicExch(p.counters + blockIdx.x, 0u);
+// One half-pass. SHIFTED (every pass after a side's first): the row shift
+// M_i = L_i(previous pass) + max_j (change of h_j since then) bounds every
+// term by 1, so the sum cannot overflow; a row block with a sum below 2^-60
+// (shift far too high) is recomputed by an exact online-max sweep over all
+// columns, by the workgroup that completes it.
+template <int NKB, int RB, bool SHIFTED, bool SCALED>
+__global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
+  constexpr int RSB = NKB * 32;
+  constexpr int ROWS = 4 * RB * 32;
+  __shared__ float red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) StageRing<NKB> lds;
+
+  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const int64_t W = gridDim.x, w = blockIdx.x;
+  const int64_t T = p.stages;
+  const int64_t U = (int64_t)p.row_blocks * T;
+  const int64_t u_end = unit_begin(w + 1, W, U);
+
+  float dmax = 0.0f;
+  if constexpr (SHIFTED) {
+    // largest change of a column bias since this side's previous pass
+    float dm = -INFINITY;
+    for (int q = threadIdx.x; q < p.n_dmax_in; q += kThreads) dm = fmaxf(dm, p.dmax_in[q]);
+    dmax = block_max(dm, red);
   }
 
-  if constexpr (SHIFTED) {
-    if (need_exact) {
-      // Exact recomputation of this workgroup's rows over all columns.
-      if (threadIdx.x == 0 && p.exact_count) atomicAdd(p.exact_count, 1u);
+  for (int64_t u = unit_begin(w, W, U); u < u_end;) {
+    const int r = (int)(u / T);
+    const int s0 = (int)(u - (int64_t)r * T);
+    const int64_t rest = u_end - (int64_t)r * T;
+    const int s1 = (int)(rest < T ? rest : T);
+    u = (int64_t)(r + 1) * T;
+    const int row_base = r * ROWS + wave * (RB * 32);
+
+    bf16x8 B[RB][NKB], Baug[RB];
+    float M[RB], S[RB], shift_row[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = min(row_base + rb * 32 + li, p.nr - 1);
+      const bf16x8* rec = reinterpret_cast<const bf16x8*>(rows + (int64_t)i * RSB) + half * NKB;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
+      if constexpr (SHIFTED) {
+        shift_row[rb] = p.Lin[i] + dmax;  // log2 units
+        Baug[rb] = row_aug(half, -shift_row[rb] / p.escale);
+        M[rb] = 0.0f;
+      } else {
+        shift_row[rb] = 0.0f;
         Baug[rb] = row_aug(half, 0.0f);
         M[rb] = -INFINITY;
-        S[rb] = 0.0f;
       }
-      if constexpr (kUseLds<NKB>) sweep_lds<NKB, RB, false, SCALED>(p, lds, 0, p.nc, B, Baug, M, S, li, half);
-      else sweep<NKB, RB, false, SCALED>(p, 0, p.nc, B, Baug, M, S, li, half);
+      S[rb] = 0.0f;
+    }
+
+    sweep<NKB, RB, SHIFTED, SCALED>(p, lds, s0 * kStageCols, min(p.nc, s1 * kStageCols), B, Baug, M, S,
+                                     lane, wave);
+    float Lm[RB], Ls[RB];
+    row_sums<RB, SHIFTED>(p, M, S, shift_row, Lm, Ls);
+
+    // Finish the row block here if this workgroup holds all of it, else leave
+    // a partial and let the last contributor merge.
+    float dh = -INFINITY;  // largest bias change over the rows this thread finishes
+    bool need_exact = false;
+    if (s0 == 0 && s1 == T) {
+      bool bad = false;
+      if constexpr (SHIFTED) {
+        if (half == 0)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float So = __shfl_xor(S[rb], 32);
-        const float Mo = __shfl_xor(M[rb], 32);
-        const float Mt = fmaxf(M[rb], Mo);
+          for (int rb = 0; rb < RB; ++rb)
+            bad |= (row_base + rb * 32 + li < p.nr) && !(Ls[rb] >= kShiftedFloor);
+        need_exact = __syncthreads_or(bad);
+      }
+      if (!need_exact && half == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = row_base + rb * 32 + li;
+          if (i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, Lm[rb] + fast_log2(Ls[rb])));
+        }
+      }
+    } else {
+      const int64_t first = unit_owner((int64_t)r * T, W, U);
+      const int64_t last = unit_owner((int64_t)(r + 1) * T - 1, W, U);
+      const int contributors = (int)(last - first + 1);
+      const int64_t slot = w - first;
+      if (half == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = row_base + rb * 32 + li;
+          if (i < p.nr) p.part[slot * p.nr + i] = make_float2(Lm[rb], Ls[rb]);
+        }
+      }
+      if (!arrive_last(p.counters + r, contributors)) continue;
+      // the last contributor merges the partials of the row block in workgroup order
+      float Lr = 0.0f;
+      bool bad = false;
+      const int i = r * ROWS + (int)threadIdx.x;
+      const bool mine = (int)threadIdx.x < ROWS && i < p.nr;
+      if (mine) {
+        float Mt = -INFINITY;
+        for (int s2 = 0; s2 < contributors; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
         const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
-        const float St = S[rb] * fast_exp2(p.escale * (M[rb] - Me)) + So * fast_exp2(p.escale * (Mo - Me));
-        const int i = row_base + rb * 32 + li;
-        if (half == 0 && i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, p.escale * Mt + fast_log2(St)));
+        float St = 0.0f;
+        for (int s2 = 0; s2 < contributors; ++s2) {
+          const float Mp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].x);
+          const float Sp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].y);
+          St = fmaf(Sp, fast_exp2(Mp - Me), St);
+        }
+        Lr = Mt + fast_log2(St);
+        bad = SHIFTED && !(St >= kShiftedFloor);
+      }
+      if constexpr (SHIFTED) need_exact = __syncthreads_or(bad);
+      if (!need_exact && mine) dh = finish_row_mfma(p, i, Lr);
+      if (threadIdx.x == 0) atomicExch(p.counters + r, 0u);
+    }
+
+    if constexpr (SHIFTED) {
+      if (need_exact) {
+        // exact recomputation of this row block over all columns
+        if (threadIdx.x == 0 && p.exact_count) atomicAdd(p.exact_count, 1u);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          Baug[rb] = row_aug(half, 0.0f);
+          M[rb] = -INFINITY;
+          S[rb] = 0.0f;
+        }
+        sweep<NKB, RB, false, SCALED>(p, lds, 0, p.nc, B, Baug, M, S, lane, wave);
+        row_sums<RB, false>(p, M, S, shift_row, Lm, Ls);
+        dh = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = row_base + rb * 32 + li;
+          if (half == 0 && i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, Lm[rb] + fast_log2(Ls[rb])));
+        }
       }
     }
+    const float bmax = block_max(dh, red);
+    if (threadIdx.x == 0) p.dmax_out[r] = bmax;
   }
-  const float bmax = block_max(dh, red);
-  if (threadIdx.x == 0) p.dmax_out[blockIdx.x] = bmax;
 }
 
 // ---------------------------------------------------------------- record prep
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, i
 
 template <int NKB, int RB>
 hipError_t run_lse(const MfmaPassArgs& a, bool shifted, bool scaled, const PassPlan& pl, hipStream_t s) {
-  const dim3 grid(pl.row_blocks, pl.splits);
+  const dim3 grid(pl.grid);
   if (shifted) {
     if (scaled) k_lse_mfma<NKB, RB, true, true><<<grid, kThreads, 0, s>>>(a);
     else k_lse_mfma<NKB, RB, true, false><<<grid, kThreads, 0, s>>>(a);
@@ -441,6 +455,29 @@ hipError_t run_lse(const MfmaPassArgs& a, bool shifted, bool scaled, const PassP
     else k_lse_mfma<NKB, RB, false, false><<<grid, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+// Workgroups of the shifted kernel of a record width that fit on the device at once.
+int resident_workgroups(int nkb) {
+  static int cached[9] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (nkb < 1 || nkb > 8) return 0;
+  if (cached[nkb] == 0) {
+    int per_cu = 0, cus = 0;
+    hipError_t e = hipErrorInvalidValue;
+    switch (nkb) {
+      case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true>, kThreads, 0); break;
+      case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false>, kThreads, 0); break;
+      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<4, 2, true, true>, kThreads, 0); break;
+      case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<8, 1, true, true>, kThreads, 0); break;
+      default: break;
+    }
+    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cached[nkb] = per_cu * cus;
+  }
+  return cached[nkb];
 }
 
 }  // namespace
@@ -460,19 +497,21 @@ int mfma_rb(int nkb) { return nkb <= 4 ? 2 : 1; }
 int64_t mfma_padded_count(int64_t n) { return (n + 31) / 32 * 32 + 5 * 32; }
 
 PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb) {
-  PassPlan pl;
+  PassPlan pl{};
   pl.rows_per_block = 4 * mfma_rb(nkb) * 32;
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
-  const int64_t target = 2048;
-  int64_t splits = (target + pl.row_blocks - 1) / pl.row_blocks;
-  const int64_t max_splits = nc / 1024 > 1 ? nc / 1024 : 1;
-  if (splits > max_splits) splits = max_splits;
-  if (splits > 64) splits = 64;
-  if (splits < 1) splits = 1;
-  int64_t cps = (nc + splits - 1) / splits;
-  cps = (cps + 63) / 64 * 64;  // whole 64-column stages: a split never reads into the next one
-  pl.cols_per_split = (int)cps;
-  pl.splits = (int)((nc + cps - 1) / cps);
+  pl.stages = (int)((nc + kStageCols - 1) / kStageCols);
+  const int64_t units = (int64_t)pl.row_blocks * pl.stages;
+  int64_t grid = resident_workgroups(nkb);
+  const int64_t min_units = 4;  // at least 512 columns of one row block per workgroup
+  if (grid > units / min_units) grid = units / min_units;
+  if (grid < 1) grid = 1;
+  pl.grid = (int)grid;
+  // partial slots per row: workgroups that can share one row block
+  const int64_t per_wg = units / grid;  // >= min_units unless units is small
+  pl.splits = (int)(per_wg > 0 ? (pl.stages + per_wg - 1) / per_wg + 1 : pl.stages + 1);
+  if (pl.splits > grid) pl.splits = (int)grid;
+  pl.cols_per_split = kStageCols;
   return pl;
 }
 

@@ -521,7 +521,7 @@ void pv_parts(int dtype, bool grad, int& pp, int& vp) {
 int pv_nob(int nobt) { return nobt >= 2 ? 2 : 1; }
 
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks) {
-  PassPlan pl;
+  PassPlan pl{};
   pl.rows_per_block = gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32;
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
   const int64_t target = (gemm ? 1024 : 2048) / (nchunks > 0 ? nchunks : 1);

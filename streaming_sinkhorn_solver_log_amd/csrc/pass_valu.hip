@@ -341,7 +341,7 @@ int valu_dp(int d) { return (valu_dclass(d) + 3) & ~3; }
 
 PassPlan plan_valu_pass(int64_t nr, int64_t nc, int d) {
   (void)d;
-  PassPlan pl;
+  PassPlan pl{};
   pl.rows_per_block = kThreads;
   pl.row_blocks = (int)((nr + kThreads - 1) / kThreads);
   // Aim for about 2048 workgroups (8 waves per SIMD) and at least 512 columns per split.

@@ -79,8 +79,10 @@ enum class Layout : int {
 struct PassPlan {
   int rows_per_block;
   int row_blocks;
-  int splits;
+  int splits;          // column splits (partial slots per row for the balanced plan)
   int cols_per_split;
+  int grid;            // balanced plan: workgroups (one resident wave of them)
+  int stages;          // balanced plan: 128-column stages per row block
 };
 
 PassPlan plan_valu_pass(int64_t nr, int64_t nc, int d);

@@ -30,7 +30,8 @@ struct MfmaPassArgs {
   float2* part;            // split partials (M, S) in log2 units: [split][nr]
   unsigned* counters;      // one per row block, zero on entry and exit
   int nr, nc;
-  int splits, cols_per_split;
+  int splits, cols_per_split;  // GEMM-tiled pass: column splits
+  int row_blocks, stages;      // register-resident pass: balanced split of row blocks x stages
   // Exponent of a pair in log2 units = escale * (acc - M). float32 points have
   // c2 folded into their row records (escale = 1, biases in log2 units); bf16
   // points keep exact records (escale = c2, biases stored divided by c2).
