@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_gemm(const MfmaPassArgs p, 
     if (mine) {
       float lm, ls;
       row_result(r, lm, ls);
-      p.part[(int64_t)sp * p.nr + i] = make_float2(lm, ls);
+      store_coherent(&p.part[(int64_t)sp * p.nr + i], make_float2(lm, ls));
     }
     if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
     if (mine) {

@@ -176,16 +176,38 @@ __device__ __attribute__((always_inline)) inline void sweep(
 }
 
 // ---------------------------------------------------------------- work split
-// The pass is R row blocks x T stages (128 columns) = U units. Workgroup w of
-// W takes units [w U / W, (w + 1) U / W) in row-block-major order: every
-// workgroup gets the same amount of work (within one unit) and the grid is
-// one wave of resident workgroups. A row block split between workgroups is
-// merged from per-workgroup partials by the last one to arrive, in
-// workgroup order, so results do not depend on timing.
-__device__ __forceinline__ int64_t unit_begin(int64_t w, int64_t W, int64_t U) { return w * U / W; }
-__device__ __forceinline__ int64_t unit_owner(int64_t u, int64_t W, int64_t U) {
-  return ((u + 1) * W - 1) / U;  // the workgroup whose range holds unit u
-}
+// The pass is R row blocks x T stages (128 columns) = U units, ordered chunk
+// by chunk: the columns are cut into C chunks, and within a chunk the units
+// run row block by row block. Workgroup v of W takes units [v U / W,
+// (v + 1) U / W): every workgroup gets the same amount of work (within one
+// unit) and the grid is one wave of resident workgroups. Workgroups are
+// dispatched to the 8 XCDs round robin; numbering them so that each XCD
+// holds a contiguous range of v makes the workgroups of one XCD share about
+// 1/C of the columns, which its L2 cache keeps. A row block is merged from
+// the partials of its contributors by the last one to arrive, in (chunk,
+// workgroup) order, so results do not depend on timing.
+struct UnitMap {
+  int64_t R, T, C, U, W;
+  __host__ __device__ int64_t cs(int64_t c) const { return c * T / C; }   // first stage of chunk c
+  __host__ __device__ int64_t off(int64_t c) const { return R * cs(c); }  // first unit of chunk c
+  __host__ __device__ int64_t begin(int64_t v) const { return v * U / W; }
+  __host__ __device__ int64_t owner(int64_t u) const { return ((u + 1) * W - 1) / U; }
+  __host__ __device__ int64_t chunk_of(int64_t u) const {
+    int64_t c = u * C / U;
+    while (c + 1 < C && off(c + 1) <= u) ++c;
+    while (c > 0 && off(c) > u) --c;
+    return c;
+  }
+  // workgroups that contribute to row block r within chunk c
+  __host__ __device__ int64_t contrib(int64_t c, int64_t r) const {
+    const int64_t tc = cs(c + 1) - cs(c);
+    if (tc == 0) return 0;
+    const int64_t a = off(c) + r * tc;
+    return owner(a + tc - 1) - owner(a) + 1;
+  }
+};
+
+__host__ __device__ inline int64_t chunks_for(int64_t T, int64_t W) { return (W % 8 == 0 && T >= 8) ? 8 : 1; }
 
 // Row results of one row block: (Lm, Ls) per row with L = Lm + log2 Ls (log2
 // units), in lanes of half 0.
@@ -227,8 +249,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
   const int li = lane & 31;
   const int64_t W = gridDim.x, w = blockIdx.x;
   const int64_t T = p.stages;
-  const int64_t U = (int64_t)p.row_blocks * T;
-  const int64_t u_end = unit_begin(w + 1, W, U);
+  const UnitMap um{p.row_blocks, T, chunks_for(T, W), (int64_t)p.row_blocks * T, W};
+  const int64_t v = (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;  // XCD-contiguous numbering
+  const int64_t u_end = um.begin(v + 1);
 
   float dmax = 0.0f;
   if constexpr (SHIFTED) {
@@ -238,12 +261,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
     dmax = block_max(dm, red);
   }
 
-  for (int64_t u = unit_begin(w, W, U); u < u_end;) {
-    const int r = (int)(u / T);
-    const int s0 = (int)(u - (int64_t)r * T);
-    const int64_t rest = u_end - (int64_t)r * T;
-    const int s1 = (int)(rest < T ? rest : T);
-    u = (int64_t)(r + 1) * T;
+  for (int64_t u = um.begin(v); u < u_end;) {
+    const int64_t c = um.chunk_of(u);
+    const int64_t tc = um.cs(c + 1) - um.cs(c);
+    const int64_t local = u - um.off(c);
+    const int r = (int)(local / tc);
+    const int s0 = (int)(um.cs(c) + local % tc);
+    const int64_t seg_end = min(u_end, um.off(c) + (int64_t)(r + 1) * tc);
+    const int s1 = (int)(s0 + (seg_end - u));
+    u = seg_end;
     const int row_base = r * ROWS + wave * (RB * 32);
 
     bf16x8 B[RB][NKB], Baug[RB];
@@ -292,15 +318,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
         }
       }
     } else {
-      const int64_t first = unit_owner((int64_t)r * T, W, U);
-      const int64_t last = unit_owner((int64_t)(r + 1) * T - 1, W, U);
-      const int contributors = (int)(last - first + 1);
-      const int64_t slot = w - first;
+      int contributors = 0;
+      int64_t slot = 0;
+      for (int64_t c2 = 0; c2 < um.C; ++c2) {
+        const int64_t n2 = um.contrib(c2, r);
+        if (c2 < c) slot += n2;
+        contributors += (int)n2;
+      }
+      slot += v - um.owner(um.off(c) + (int64_t)r * tc);
       if (half == 0) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int i = row_base + rb * 32 + li;
-          if (i < p.nr) p.part[slot * p.nr + i] = make_float2(Lm[rb], Ls[rb]);
+          if (i < p.nr) store_coherent(&p.part[slot * p.nr + i], make_float2(Lm[rb], Ls[rb]));
         }
       }
       if (!arrive_last(p.counters + r, contributors)) continue;
@@ -507,10 +537,15 @@ PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb) {
   if (grid > units / min_units) grid = units / min_units;
   if (grid < 1) grid = 1;
   pl.grid = (int)grid;
-  // partial slots per row: workgroups that can share one row block
-  const int64_t per_wg = units / grid;  // >= min_units unless units is small
-  pl.splits = (int)(per_wg > 0 ? (pl.stages + per_wg - 1) / per_wg + 1 : pl.stages + 1);
-  if (pl.splits > grid) pl.splits = (int)grid;
+  // partial slots per row: the most contributors any row block has
+  const UnitMap um{pl.row_blocks, pl.stages, chunks_for(pl.stages, grid), units, grid};
+  int64_t most = 1;
+  for (int64_t r = 0; r < pl.row_blocks; ++r) {
+    int64_t n = 0;
+    for (int64_t c = 0; c < um.C; ++c) n += um.contrib(c, r);
+    if (n > most) most = n;
+  }
+  pl.splits = (int)most;
   pl.cols_per_split = kStageCols;
   return pl;
 }

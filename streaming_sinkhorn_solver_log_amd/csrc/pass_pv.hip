@@ -194,14 +194,14 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
     for (int rb = 0; rb < RB; ++rb) {
       const int i = row_base + rb * 32 + li;
       if (i >= p.nr) continue;
-      if (half == 0) part_ms[slot * p.nr + i] = make_float2(mu[rb], St[rb]);
+      if (half == 0) store_coherent(&part_ms[slot * p.nr + i], make_float2(mu[rb], St[rb]));
       float* T = part_t + (slot * p.nr + i) * CW;
 #pragma unroll
       for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(T + ob * 32 + 8 * q + 4 * half) =
-              make_float4(O[rb][ob][4 * q], O[rb][ob][4 * q + 1], O[rb][ob][4 * q + 2], O[rb][ob][4 * q + 3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store_coherent(T + ob * 32 + 8 * q + 4 * half + e, O[rb][ob][4 * q + e]);
     }
   }
   unsigned* counter = p.counters + (int64_t)z * p.row_blocks + blockIdx.x;

@@ -15,6 +15,7 @@
 // with a device-scope atomic) combines the partials in split order, so the
 // result does not depend on which workgroup finishes last.
 #include "sk_internal.h"
+#include "sk_sync.h"
 
 #include <math.h>
 
@@ -30,25 +31,6 @@ constexpr int kChunkMax = 8;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-template <typename T>
-__device__ __forceinline__ T load_coherent(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Returns true in every thread of the workgroup that completes the row block.
-__device__ bool arrive_last(unsigned* counter, int splits) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned old = atomicAdd(counter, 1u);
-    s_last = (old == (unsigned)(splits - 1));
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
 
 __device__ __forceinline__ void finish_row(const PassArgs& p, int i, float M, float S) {
   const float L = M + fast_log2(S);
@@ -125,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_lse_valu(const PassArgs p) {
     if (i < p.nr) finish_row(p, i, M, S);
     return;
   }
-  if (i < p.nr) p.part[(int64_t)sp * p.nr + i] = make_float2(M, S);
+  if (i < p.nr) store_coherent(&p.part[(int64_t)sp * p.nr + i], make_float2(M, S));
   if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
   if (i < p.nr) {
     float Mt = -INFINITY;
@@ -212,10 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_grad_valu(const GradArgs p) {
   constexpr int R = 2 + D;
   if (i < p.nr) {
     float* rec = p.part + ((int64_t)sp * p.nr + i) * R;
-    rec[0] = M;
-    rec[1] = S;
+    store_coherent(rec, M);
+    store_coherent(rec + 1, S);
 #pragma unroll
-    for (int k = 0; k < D; ++k) rec[2 + k] = O[k];
+    for (int k = 0; k < D; ++k) store_coherent(rec + 2 + k, O[k]);
   }
   if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
   if (i < p.nr) {
@@ -281,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void k_apply_valu(const ApplyArgs p) {
   if (i < p.nr) {
 #pragma unroll
     for (int c = 0; c < K; ++c)
-      if (c < p.k) p.part[((int64_t)sp * p.nr + i) * p.k + c] = acc[c];
+      if (c < p.k) store_coherent(p.part + ((int64_t)sp * p.nr + i) * p.k + c, acc[c]);
   }
   if (!arrive_last(p.counters + blockIdx.x, p.splits)) return;
   if (i < p.nr) {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "sk_mfma.h"
+#include "sk_sync.h"
 
 #include <math.h>
 
@@ -13,22 +14,6 @@ constexpr float kMaskedBias = -1.0e30f;  // bias of a column that contributes no
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-template <typename T>
-__device__ __forceinline__ T load_coherent(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline bool arrive_last(unsigned* counter, int splits) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1u) == (unsigned)(splits - 1));
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
 
 // Three-part bf16 split of v (v ~= hi + mid + lo to float32 precision).
 __device__ __forceinline__ void split3(float v, __bf16& hi, __bf16& mid, __bf16& lo) {
