@@ -45,6 +45,84 @@ HBM_PEAK = 8.0e12
 
 WORKLOADS = {w.name: key for key, w in W.CONFIGS.items()}
 
+# HBM traffic of the half-pass kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# runs scaled by the same counters' reading for a device copy of known size
+# (written by --summarize-counters). It is reported only while the kernel
+# sources still hash to the digest the counters were taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+_CSRC = os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "csrc")
+KERNEL_SOURCES = ["pass_mfma.hip", "sk_mfma_dev.h", "sk_mfma.h", "sk_sync.h", "sk_internal.h"]
+# shifted half-pass kernel of each workload (the launch that dominates a solve)
+HALF_PASS_KERNEL = {"embed_d64_50k_bf16": "k_lse_mfma<4, 2, true, true>",
+                    "mix8_d3_50k": "k_lse_mfma<2, 2, true, false>"}
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_traffic(workload):
+    """HBM bytes per launch of the workload's half-pass kernel, or None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    k = t.get("kernels", {}).get(HALF_PASS_KERNEL.get(workload, ""))
+    if not k:
+        return None
+    return (k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def _pmc_means(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_counters(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """Write TRAFFIC_FILE from four rocprofv3 --pmc output folders and print a summary."""
+    fetch, nf = _pmc_means(fetch_dir)
+    write, _ = _pmc_means(write_dir)
+    cf, _ = _pmc_means(cfetch_dir)
+    cw, _ = _pmc_means(cwrite_dir)
+    copy_kib = (1 << 30) / 1024.0  # --copy-calibration moves 1 GiB per copy
+    name = next(k for k in cf if "copyBuffer" in k)
+    fs, ws = copy_kib / cf[name], copy_kib / cw[name]
+    kernels = {}
+    for full, v in fetch.items():
+        for stem in ("k_lse_mfma<", "k_pv_mfma<", "k_lse_gemm<", "k_pv_gemm<"):
+            i = full.find(stem)
+            if i >= 0:
+                short = full[i:full.index(">", i) + 1]
+                kernels[short] = {"fetch_kib": v, "write_kib": write.get(full, 0.0), "dispatches": nf[full]}
+    out = {"source_digest": source_digest(), "fetch_scale": fs, "write_scale": ws,
+           "copy_fetch_kib": cf[name], "copy_write_kib": cw[name], "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print(f"copy of {copy_kib:.0f} KiB: FETCH_SIZE {cf[name]:.0f} KiB (scale {fs:.3f}), "
+          f"WRITE_SIZE {cw[name]:.0f} KiB (scale {ws:.3f})")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written |")
+    print("|---|---|---|---|---|---|")
+    for k, v in sorted(kernels.items()):
+        print(f"| `{k}` | {v['dispatches']} | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | "
+              f"{v['fetch_kib'] * fs * 1.024e-3:.1f} | {v['write_kib'] * ws * 1.024e-3:.1f} |")
+
 
 def _dev_points(arr, dtype, torch, dev):
     if dtype == "bf16":
@@ -113,6 +191,12 @@ class Case:
 
 def pass_roofline(w, pass_ms):
     """Roofline of the half-pass kernel: per pair one exp2 is irreducible."""
+    r = _pass_roofline(w, pass_ms)
+    r["traffic"] = kernel_traffic(w.name)
+    return r
+
+
+def _pass_roofline(w, pass_ms):
     pairs = w.n * w.m
     sec = pass_ms * 1e-3
     exp_rate = pairs / sec
@@ -169,10 +253,11 @@ def measure(case, steps, warmup):
     }
 
 
-def cpu_baseline(case, target_s=12.0):
+def cpu_baseline(case, target_s=15.0):
     """The float64 oracle on the host cores, on a bounded sample of the workload:
     the F map on R rows of x and the G map on R rows of y (all columns each),
-    scaled to one full iteration (n rows of F, m rows of G)."""
+    scaled to one full iteration (n rows of F, m rows of G); when a whole
+    iteration takes less than the target, whole iterations are repeated."""
     import oracle
 
     oracle.build(force=False)
@@ -180,22 +265,35 @@ def cpu_baseline(case, target_s=12.0):
     x64, y64 = inp.x64(), inp.y64()
     g = np.zeros(w.m)
     f = np.zeros(w.n)
-    r0 = 16
-    t = time.perf_counter()
-    oracle.F(x64[:r0], y64, inp.b, g, w.eps)
-    oracle.G(x64, y64[:r0], inp.a, f, w.eps)
-    per_row = (time.perf_counter() - t) / (2 * r0)
-    R = int(max(r0, min(w.n, w.m, target_s / (2 * per_row))))
-    t = time.perf_counter()
-    oracle.F(x64[:R], y64, inp.b, g, w.eps)
-    tf = time.perf_counter() - t
-    t = time.perf_counter()
-    oracle.G(x64, y64[:R], inp.a, f, w.eps)
-    tg = time.perf_counter() - t
-    sec_per_iter = tf * w.n / R + tg * w.m / R
+    lim = min(w.n, w.m)
+    r0, t0 = 16, 0.0
+    while True:  # ramp up until the fixed costs are small against the sample
+        t = time.perf_counter()
+        oracle.F(x64[:r0], y64, inp.b, g, w.eps)
+        oracle.G(x64, y64[:r0], inp.a, f, w.eps)
+        t0 = time.perf_counter() - t
+        if t0 >= 0.1 * target_s or r0 >= lim:
+            break
+        r0 = min(lim, r0 * 8)
+    per_row = t0 / (2 * r0)
+    R = int(max(16, min(lim, target_s / (2 * per_row))))
+    reps = 1
+    if R >= min(w.n, w.m):
+        R = min(w.n, w.m)
+        reps = max(1, int(round(target_s / (per_row * (w.n + w.m)))))
+    tf = tg = 0.0
+    for _ in range(reps):
+        t = time.perf_counter()
+        oracle.F(x64[:R], y64, inp.b, g, w.eps)
+        tf += time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.G(x64, y64[:R], inp.a, f, w.eps)
+        tg += time.perf_counter() - t
+    sec_per_iter = (tf * w.n / R + tg * w.m / R) / reps
     return {"value": 1.0 / sec_per_iter, "unit": "iters/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"F map on {R} rows of x and G map on {R} rows of y (all {w.m} and {w.n} columns), "
-                      f"float64, scaled by n/{R} and m/{R} to one iteration; {tf + tg:.1f} s measured"}
+                      f"float64, {reps} time(s), scaled by n/{R} and m/{R} to one iteration; "
+                      f"{tf + tg:.1f} s measured"}
 
 
 def main():
@@ -206,10 +304,15 @@ def main():
     ap.add_argument("--workload", default="embed_d64_50k_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-d3", action="store_true", help="skip the d=3 point")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/hbm_traffic.json from four rocprofv3 --pmc output folders")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
