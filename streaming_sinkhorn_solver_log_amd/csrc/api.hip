@@ -170,17 +170,23 @@ size_t part_f2(const PassPlan& f, int64_t n, const PassPlan& g, int64_t m) {
 struct SolvePlan {
   Path path;
   int nkb;      // matrix-core records: K blocks per record
+  bool merged;  // register-resident pass with the bias chunk inside the column records
   PassPlan f, g;
 };
 
-SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d) {
+// The merged layout keeps one bias copy per side inside its column records, so
+// it serves the alternating schedule only (the averaged one reads the old
+// biases of both sides while writing the new ones).
+SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternating) {
   SolvePlan sp;
   sp.path = solve_path(dtype, d);
   sp.nkb = 0;
+  sp.merged = false;
   if (sp.path == Path::Mfma) {
     sp.nkb = mfma_nkb(dtype, (int)d);
-    sp.f = plan_mfma_pass(n, m, sp.nkb);
-    sp.g = plan_mfma_pass(m, n, sp.nkb);
+    sp.merged = alternating && mfma_merged(dtype, (int)d, sp.nkb);
+    sp.f = plan_mfma_pass(n, m, sp.nkb, sp.merged);
+    sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged);
   } else if (sp.path == Path::Gemm) {
     sp.nkb = gemm_nkb(dtype, (int)d);
     sp.f = plan_gemm_pass(n, m);
@@ -322,7 +328,7 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
                   L.x.bias[0], L.x.bias[1], L.x.hval[0], n};
   MfmaPrepSide py{y, b, g, nullptr, L.y.row_rec, L.y.col_rec, L.y.alpha, L.y.lw,
                   L.y.bias[0], L.y.bias[1], L.y.hval[0], m};
-  hipError_t e = launch_prep_mfma(px, py, dtype, (int)d, ap.nkb, true, L.c.centroid, L.c.shift,
+  hipError_t e = launch_prep_mfma(px, py, dtype, (int)d, ap.nkb, false, true, L.c.centroid, L.c.shift,
                                   L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);
   if (e != hipSuccess) return hip_fail(e, "prep");
   const float* shift = dtype == SK_F32 ? L.c.shift : nullptr;
@@ -389,7 +395,7 @@ int solve_valu(const SolveWs& L, const SolvePlan& sp, int64_t n, int64_t m, int6
 hipError_t launch_pass(const SolvePlan& sp, const MfmaPassArgs& a, bool shifted, bool scaled,
                        const PassPlan& pl, hipStream_t s) {
   if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, pl, s);
-  return launch_lse_mfma(a, sp.nkb, shifted, scaled, pl, s);
+  return launch_lse_mfma(a, sp.nkb, shifted, scaled, sp.merged, pl, s);
 }
 
 int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int64_t m, int iters,
@@ -403,7 +409,12 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     const bool shifted = t > 0;
     MfmaPassArgs pf{};
     pf.rows = L.xm.row_rec; pf.cols = L.ym.col_rec; pf.bias_col = L.ym.bias[cur];
-    pf.alpha = L.xm.alpha; pf.lw = L.xm.lw; pf.pot = f; pf.bias_out = L.xm.bias[nxt];
+    pf.alpha = L.xm.alpha; pf.lw = L.xm.lw; pf.pot = f; pf.bias_out = L.xm.bias[nxt]; pf.bias_stride = 2;
+    if (sp.merged) {  // the bias chunk is the last chunk of each column record
+      pf.bias_col = nullptr;
+      pf.bias_out = L.xm.col_rec + (2 * sp.nkb - 1);
+      pf.bias_stride = 2 * sp.nkb;
+    }
     pf.Lout = L.xm.L; pf.Lin = L.xm.L; pf.hval_in = L.xm.hval[cur]; pf.hval_out = L.xm.hval[nxt];
     pf.dmax_in = L.ym.dmax[cur]; pf.n_dmax_in = sp.g.row_blocks; pf.dmax_out = L.xm.dmax[nxt];
     pf.exact_count = L.c.exact_count;
@@ -415,7 +426,12 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     if ((e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
     MfmaPassArgs pg = pf;
     pg.rows = L.ym.row_rec; pg.cols = L.xm.col_rec; pg.bias_col = L.xm.bias[cur];
-    pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt];
+    pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt]; pg.bias_stride = 2;
+    if (sp.merged) {
+      pg.bias_col = nullptr;
+      pg.bias_out = L.ym.col_rec + (2 * sp.nkb - 1);
+      pg.bias_stride = 2 * sp.nkb;
+    }
     pg.Lout = L.ym.L; pg.Lin = L.ym.L; pg.hval_in = L.ym.hval[cur]; pg.hval_out = L.ym.hval[nxt];
     pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
@@ -427,8 +443,10 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
 }
 
 size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
-  const SolvePlan sp = plan_solve(dtype, n, m, d);
-  return layout_solve(nullptr, sp, n, m, d).bytes;
+  // the schedule is not known here: the larger of the two plans
+  const size_t a = layout_solve(nullptr, plan_solve(dtype, n, m, d, true), n, m, d).bytes;
+  const size_t b = layout_solve(nullptr, plan_solve(dtype, n, m, d, false), n, m, d).bytes;
+  return a > b ? a : b;
 }
 
 size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
@@ -482,7 +500,7 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   if (iters < 0) return fail(SK_ERR_INVALID_ARG, "iters must be >= 0");
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
   if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
-  const SolvePlan sp = plan_solve(dtype, n, m, d);
+  const SolvePlan sp = plan_solve(dtype, n, m, d, mode == SK_ALTERNATING);
   const size_t need = layout_solve(nullptr, sp, n, m, d).bytes;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const SolveWs L = layout_solve(ws, sp, n, m, d);
@@ -503,7 +521,7 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
     MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw,
                     L.ym.bias[0], L.ym.bias[1], L.ym.hval[0], m};
     // counters and the exact-fallback count are zeroed together (adjacent)
-    e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, center, L.c.centroid, L.c.shift,
+    e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, sp.merged, center, L.c.centroid, L.c.shift,
                          L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);
     if (e != hipSuccess) return hip_fail(e, "prep");
     if ((rc = solve_mfma(L, sp, dtype, n, m, iters, sym, f, g, sc, s))) return rc;

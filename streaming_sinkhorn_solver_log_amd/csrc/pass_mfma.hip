@@ -68,11 +68,16 @@ __device__ __attribute__((always_inline)) inline void tile_valu(const f32x16 (&a
 constexpr int kStageTiles = 4;
 constexpr int kStageCols = kStageTiles * 32;
 template <int NKB>
-constexpr int kRing = NKB >= 4 ? 2 : 3;  // stages in flight (LDS: ring x 4 x (NKB + 1) KB)
+constexpr int kRing = NKB >= 4 ? 2 : 3;  // stages in flight (LDS: ring x 4 x blocks KB)
 
-template <int NKB>
+// LDS blocks per tile: the record's K blocks, plus the bias chunk unless it
+// is merged into the record.
+template <int NKB, bool MERGED>
+constexpr int kBlocks = MERGED ? NKB : NKB + 1;
+
+template <int NKB, bool MERGED>
 struct StageRing {
-  bf16x8 blk[kRing<NKB>][kStageTiles][NKB + 1][64];
+  bf16x8 blk[kRing<NKB>][kStageTiles][kBlocks<NKB, MERGED>][64];
 };
 
 // s_waitcnt vmcnt(N), other counters not waited on (gfx9 encoding).
@@ -92,19 +97,20 @@ __device__ __forceinline__ void load_to_lds(const void* src, const void* lds_dst
 }
 
 // This wave's share of stage [c0, c0 + 128): blocks wave, wave + 4, ... of the
-// 4 (NKB + 1) blocks. Columns past the range read the padding (masked) or the
+// stage's blocks. Columns past the range read the padding (masked) or the
 // next range; they are never summed.
-template <int NKB>
+template <int NKB, bool MERGED>
 __device__ __attribute__((always_inline)) inline void issue_stage(
-    StageRing<NKB>& L, int slot, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
+    StageRing<NKB, MERGED>& L, int slot, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
     int c0, int wave, int lane) {
-  constexpr int NB = kStageTiles * (NKB + 1);
+  constexpr int NBT = kBlocks<NKB, MERGED>;
+  constexpr int NB = kStageTiles * NBT;
   static_assert(NB % 4 == 0, "blocks of a stage split evenly over four waves");
   const int li = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int q = 0; q < NB / 4; ++q) {
     const int b = wave + 4 * q;
-    const int tt = b / (NKB + 1), kb = b % (NKB + 1);
+    const int tt = b / NBT, kb = b % NBT;
     const int col = c0 + tt * 32 + li;
     const void* src = (kb < NKB)
         ? static_cast<const void*>(cols + (int64_t)col * (NKB * 32) + h * (NKB * 16) + kb * 16)
@@ -113,20 +119,39 @@ __device__ __attribute__((always_inline)) inline void issue_stage(
   }
 }
 
+// Score tile against the RB row blocks: data K blocks, then (separate layout)
+// the bias block.
+template <int NKB, int RB, bool MERGED>
+__device__ __attribute__((always_inline)) inline void tile_scores(
+    const ColTile<NKB>& ct, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB], f32x16 (&acc)[RB]) {
+  if constexpr (MERGED) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f32x16 a = {};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.a[kb], B[rb][kb], a, 0, 0, 0);
+      acc[rb] = a;
+    }
+  } else {
+    tile_mfma<NKB, RB>(ct, B, Baug, acc);
+  }
+}
+
 // One sweep of the workgroup over columns [j0, j1), j0 a multiple of 128.
-// SHIFTED: the row shift is folded into Baug and the sums need no running
-// maximum; otherwise online max/sum-exp. Ends with a barrier (LDS reusable).
-template <int NKB, int RB, bool SHIFTED, bool SCALED>
+// SHIFTED: the row shift is folded into the row side's bias block and the sums
+// need no running maximum; otherwise online max/sum-exp. Ends with a barrier
+// (LDS reusable).
+template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED>
 __device__ __attribute__((always_inline)) inline void sweep(
-    const MfmaPassArgs& p, StageRing<NKB>& L, int j0, int j1, const bf16x8 (&B)[RB][NKB],
+    const MfmaPassArgs& p, StageRing<NKB, MERGED>& L, int j0, int j1, const bf16x8 (&B)[RB][NKB],
     const bf16x8 (&Baug)[RB], float (&M)[RB], float (&S)[RB], int lane, int wave) {
   constexpr int R = kRing<NKB>;
-  constexpr int PER = kStageTiles * (NKB + 1) / 4;  // loads per wave per stage
+  constexpr int PER = kStageTiles * kBlocks<NKB, MERGED> / 4;  // loads per wave per stage
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
   const int nstages = (j1 - j0 + kStageCols - 1) / kStageCols;
 #pragma unroll
   for (int q = 0; q < R - 1; ++q)
-    if (q < nstages) issue_stage<NKB>(L, q, cols, p.bias_col, j0 + q * kStageCols, wave, lane);
+    if (q < nstages) issue_stage<NKB, MERGED>(L, q, cols, p.bias_col, j0 + q * kStageCols, wave, lane);
   for (int st = 0; st < nstages; ++st) {
     // this wave's loads of stage st are done once at most the later stages'
     // loads are outstanding; the barrier then covers every wave's loads
@@ -139,24 +164,24 @@ __device__ __attribute__((always_inline)) inline void sweep(
     __syncthreads();
     // slot (st - 1) % R is free: every wave finished stage st - 1 before the barrier
     if (st + R - 1 < nstages)
-      issue_stage<NKB>(L, (st + R - 1) % R, cols, p.bias_col, j0 + (st + R - 1) * kStageCols, wave, lane);
+      issue_stage<NKB, MERGED>(L, (st + R - 1) % R, cols, p.bias_col, j0 + (st + R - 1) * kStageCols, wave, lane);
     const int slot = st % R;
     auto stage_tile = [&](ColTile<NKB>& ct, int tt) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = L.blk[slot][tt][kb][lane];
-      ct.aug = L.blk[slot][tt][NKB][lane];
+      if constexpr (!MERGED) ct.aug = L.blk[slot][tt][NKB][lane];
     };
     if constexpr (NKB <= 4) {
       // MFMAs of tile tt + 1 are issued before the exp/sum work of tile tt
       f32x16 acc[2][RB];
       ColTile<NKB> ct;
       stage_tile(ct, 0);
-      tile_mfma<NKB, RB>(ct, B, Baug, acc[0]);
+      tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc[0]);
 #pragma unroll
       for (int tt = 0; tt < kStageTiles; ++tt) {
         if (tt + 1 < kStageTiles) {
           stage_tile(ct, tt + 1);
-          tile_mfma<NKB, RB>(ct, B, Baug, acc[(tt + 1) & 1]);
+          tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc[(tt + 1) & 1]);
         }
         tile_valu<RB, SHIFTED, SCALED>(acc[tt & 1], p.escale, M, S);
       }
@@ -167,7 +192,7 @@ __device__ __attribute__((always_inline)) inline void sweep(
         ColTile<NKB> ct;
         stage_tile(ct, tt);
         f32x16 acc[RB];
-        tile_mfma<NKB, RB>(ct, B, Baug, acc);
+        tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc);
         tile_valu<RB, SHIFTED, SCALED>(acc, p.escale, M, S);
       }
     }
@@ -235,12 +260,22 @@ __device__ __forceinline__ void row_sums(const MfmaPassArgs& p, const float (&M)
 // term by 1, so the sum cannot overflow; a row block with a sum below 2^-60
 // (shift far too high) is recomputed by an exact online-max sweep over all
 // columns, by the workgroup that completes it.
-template <int NKB, int RB, bool SHIFTED, bool SCALED>
+template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED>
 __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
   __shared__ float red[kThreads / 64];
-  __shared__ __attribute__((aligned(16))) StageRing<NKB> lds;
+  __shared__ __attribute__((aligned(16))) StageRing<NKB, MERGED> lds;
+  // Row side of the bias block: (1, 1, 1, -shift parts) meeting the column's
+  // (bias parts, 1, 1, 1). Separate layout: its own K block (Baug); merged
+  // layout: the free last chunk of the row record (half 1, K block NKB - 1).
+  auto set_row_aug = [&](bf16x8 (&Bx)[NKB], bf16x8& Baugx, float neg_m, int half_) {
+    if constexpr (MERGED) {
+      if (half_ == 1) Bx[NKB - 1] = row_aug(0, neg_m);
+    } else {
+      Baugx = row_aug(half_, neg_m);
+    }
+  };
 
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
   const int lane = threadIdx.x & 63;
@@ -282,18 +317,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
       for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
       if constexpr (SHIFTED) {
         shift_row[rb] = p.Lin[i] + dmax;  // log2 units
-        Baug[rb] = row_aug(half, -shift_row[rb] / p.escale);
+        set_row_aug(B[rb], Baug[rb], -shift_row[rb] / p.escale, half);
         M[rb] = 0.0f;
       } else {
         shift_row[rb] = 0.0f;
-        Baug[rb] = row_aug(half, 0.0f);
+        set_row_aug(B[rb], Baug[rb], 0.0f, half);
         M[rb] = -INFINITY;
       }
       S[rb] = 0.0f;
     }
 
-    sweep<NKB, RB, SHIFTED, SCALED>(p, lds, s0 * kStageCols, min(p.nc, s1 * kStageCols), B, Baug, M, S,
-                                     lane, wave);
+    sweep<NKB, RB, SHIFTED, SCALED, MERGED>(p, lds, s0 * kStageCols, min(p.nc, s1 * kStageCols), B, Baug, M,
+                                             S, lane, wave);
     float Lm[RB], Ls[RB];
     row_sums<RB, SHIFTED>(p, M, S, shift_row, Lm, Ls);
 
@@ -363,11 +398,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) 
         if (threadIdx.x == 0 && p.exact_count) atomicAdd(p.exact_count, 1u);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          Baug[rb] = row_aug(half, 0.0f);
+          set_row_aug(B[rb], Baug[rb], 0.0f, half);
           M[rb] = -INFINITY;
           S[rb] = 0.0f;
         }
-        sweep<NKB, RB, false, SCALED>(p, lds, 0, p.nc, B, Baug, M, S, lane, wave);
+        sweep<NKB, RB, false, SCALED, MERGED>(p, lds, 0, p.nc, B, Baug, M, S, lane, wave);
         row_sums<RB, false>(p, M, S, shift_row, Lm, Ls);
         dh = -INFINITY;
 #pragma unroll
@@ -423,12 +458,14 @@ __global__ __launch_bounds__(256) void k_pack_records(const void* pts, int dtype
 }
 
 // Norms (of the values the records represent), log-weights, starting potentials
-// and the initial bias records. One thread per point.
+// and the initial bias chunks (at bias + r * bias_stride). Separate layout
+// (bias_alt non-null): the half-1 chunks of both bias buffers are zeroed here
+// once; the passes only rewrite half-0 chunks. One thread per point.
 __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dtype, int64_t n, int d,
                                                         const float* shift, const float* w,
                                                         const float* pot, float* pot_zero,
-                                                        float* alpha, float* lw, bf16x8* bias,
-                                                        float* hval, float log2e_over_eps,
+                                                        float* alpha, float* lw, bf16x8* bias, int bias_stride,
+                                                        bf16x8* bias_alt, float* hval, float log2e_over_eps,
                                                         float bias_scale) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n) return;
@@ -451,63 +488,71 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
   lw[r] = l;
   const float h = kLog2e * l + (pv - nrm) * log2e_over_eps;
   hval[r] = h;
-  write_bias_record(bias + 2 * r, h * bias_scale);
+  write_bias_chunk(bias + r * bias_stride, h * bias_scale);
+  if (bias_alt) {
+    bias[r * bias_stride + 1] = bf16x8{};
+    bias_alt[2 * r + 1] = bf16x8{};
+  }
 }
 
-// Masked padding columns [n, n_pad) of a side: zero records, masked bias in both buffers.
-__global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, int nkb, bf16x8* col_rec,
-                                                     bf16x8* bias0, bf16x8* bias1) {
+// Masked padding columns [n, n_pad) of a side. Separate layout: zero records,
+// masked bias records in both buffers. Merged layout: zero records whose
+// last chunk is a masked bias chunk.
+__global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, int nkb, int merged,
+                                                     bf16x8* col_rec, bf16x8* bias0, bf16x8* bias1) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per = (int64_t)nkb * 2;
-  if (t < (n_pad - n) * per) col_rec[n * per + t] = bf16x8{};
-  if (t < (n_pad - n) * 2) {
+  bf16x8 masked = {};
+  masked[0] = (__bf16)kMaskedBias;
+  masked[3] = (__bf16)1.0f;
+  masked[4] = (__bf16)1.0f;
+  masked[5] = (__bf16)1.0f;
+  if (t < (n_pad - n) * per) col_rec[n * per + t] = (merged && t % per == per - 1) ? masked : bf16x8{};
+  if (!merged && t < (n_pad - n) * 2) {
     const int64_t q = n * 2 + t;
-    bf16x8 v = {};
-    if ((q & 1) == 0) {
-      v[0] = (__bf16)kMaskedBias;
-      v[3] = (__bf16)1.0f;
-      v[4] = (__bf16)1.0f;
-      v[5] = (__bf16)1.0f;
-    }
+    const bf16x8 v = ((q & 1) == 0) ? masked : bf16x8{};
     bias0[q] = v;
     bias1[q] = v;
   }
 }
 
-template <int NKB, int RB>
+template <int NKB, int RB, bool MERGED>
 hipError_t run_lse(const MfmaPassArgs& a, bool shifted, bool scaled, const PassPlan& pl, hipStream_t s) {
   const dim3 grid(pl.grid);
   if (shifted) {
-    if (scaled) k_lse_mfma<NKB, RB, true, true><<<grid, kThreads, 0, s>>>(a);
-    else k_lse_mfma<NKB, RB, true, false><<<grid, kThreads, 0, s>>>(a);
+    if (scaled) k_lse_mfma<NKB, RB, true, true, MERGED><<<grid, kThreads, 0, s>>>(a);
+    else k_lse_mfma<NKB, RB, true, false, MERGED><<<grid, kThreads, 0, s>>>(a);
   } else {
-    if (scaled) k_lse_mfma<NKB, RB, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_lse_mfma<NKB, RB, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (scaled) k_lse_mfma<NKB, RB, false, true, MERGED><<<grid, kThreads, 0, s>>>(a);
+    else k_lse_mfma<NKB, RB, false, false, MERGED><<<grid, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }
 
 // Workgroups of the shifted kernel of a record width that fit on the device at once.
-int resident_workgroups(int nkb) {
-  static int cached[9] = {};
+int resident_workgroups(int nkb, bool merged) {
+  static int cached[9][2] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (nkb < 1 || nkb > 8) return 0;
-  if (cached[nkb] == 0) {
+  int& slot = cached[nkb][merged ? 1 : 0];
+  if (slot == 0) {
     int per_cu = 0, cus = 0;
     hipError_t e = hipErrorInvalidValue;
-    switch (nkb) {
-      case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true>, kThreads, 0); break;
-      case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false>, kThreads, 0); break;
-      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<4, 2, true, true>, kThreads, 0); break;
-      case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<8, 1, true, true>, kThreads, 0); break;
+    switch (nkb * 2 + (merged ? 1 : 0)) {
+      case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true, false>, kThreads, 0); break;
+      case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true, true>, kThreads, 0); break;
+      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false, false>, kThreads, 0); break;
+      case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false, true>, kThreads, 0); break;
+      case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<4, 2, true, true, false>, kThreads, 0); break;
+      case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<8, 1, true, true, false>, kThreads, 0); break;
       default: break;
     }
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    cached[nkb] = per_cu * cus;
+    slot = per_cu * cus;
   }
-  return cached[nkb];
+  return slot;
 }
 
 }  // namespace
@@ -524,15 +569,21 @@ int mfma_nkb(int dtype, int d) {
 
 int mfma_rb(int nkb) { return nkb <= 4 ? 2 : 1; }
 
+bool mfma_merged(int dtype, int d, int nkb) {
+  const int slots = (dtype == 1) ? d : 6 * d;
+  const int data_chunks = (slots + 7) / 8;
+  return nkb <= 2 && data_chunks <= 2 * nkb - 1;
+}
+
 int64_t mfma_padded_count(int64_t n) { return (n + 31) / 32 * 32 + 5 * 32; }
 
-PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb) {
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged) {
   PassPlan pl{};
   pl.rows_per_block = 4 * mfma_rb(nkb) * 32;
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
   pl.stages = (int)((nc + kStageCols - 1) / kStageCols);
   const int64_t units = (int64_t)pl.row_blocks * pl.stages;
-  int64_t grid = resident_workgroups(nkb);
+  int64_t grid = resident_workgroups(nkb, merged);
   const int64_t min_units = 4;  // at least 512 columns of one row block per workgroup
   if (grid > units / min_units) grid = units / min_units;
   if (grid < 1) grid = 1;
@@ -550,19 +601,26 @@ PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb) {
   return pl;
 }
 
-hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
+hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, bool merged,
                            const PassPlan& pl, hipStream_t s) {
+  if (merged) {
+    switch (nkb) {
+      case 1: return run_lse<1, 2, true>(a, shifted, scaled, pl, s);
+      case 2: return run_lse<2, 2, true>(a, shifted, scaled, pl, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (nkb) {
-    case 1: return run_lse<1, 2>(a, shifted, scaled, pl, s);
-    case 2: return run_lse<2, 2>(a, shifted, scaled, pl, s);
-    case 4: return run_lse<4, 2>(a, shifted, scaled, pl, s);
-    case 8: return run_lse<8, 1>(a, shifted, scaled, pl, s);
+    case 1: return run_lse<1, 2, false>(a, shifted, scaled, pl, s);
+    case 2: return run_lse<2, 2, false>(a, shifted, scaled, pl, s);
+    case 4: return run_lse<4, 2, false>(a, shifted, scaled, pl, s);
+    case 8: return run_lse<8, 1, false>(a, shifted, scaled, pl, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
-                            int nkb, bool center, double* centroid_part, float* shift,
+                            int nkb, bool merged, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,
                             float c2, hipStream_t s) {
   const float* sh = nullptr;
@@ -580,11 +638,14 @@ hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int 
                                           side->row_rec, side->col_rec);
     const int64_t npad = mfma_padded_count(side->n);
     const int64_t pad_work = (npad - side->n) * nkb * 2;
-    k_pad_columns<<<(int)((pad_work + 255) / 256), 256, 0, s>>>(side->n, npad, nkb, side->col_rec,
-                                                                side->bias, side->bias_alt);
+    k_pad_columns<<<(int)((pad_work + 255) / 256), 256, 0, s>>>(side->n, npad, nkb, merged ? 1 : 0,
+                                                                side->col_rec, side->bias, side->bias_alt);
+    // merged: the bias chunk is the last chunk of the column record
+    bf16x8* bias0 = merged ? side->col_rec + (2 * nkb - 1) : side->bias;
     k_prep_side_mfma<<<(int)((side->n + 255) / 256), 256, 0, s>>>(
         side->pts, dtype, side->n, d, sh, side->w, side->pot, side->pot_zero, side->alpha, side->lw,
-        side->bias, side->hval, log2e_over_eps, mfma_bias_scale(dtype, c2));
+        bias0, merged ? 2 * nkb : 2, merged ? nullptr : side->bias_alt, side->hval, log2e_over_eps,
+        mfma_bias_scale(dtype, c2));
   }
   return hipGetLastError();
 }

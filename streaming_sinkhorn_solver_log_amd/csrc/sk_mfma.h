@@ -18,7 +18,8 @@ struct MfmaPassArgs {
   const float* alpha;      // nr squared norms of the rows
   const float* lw;         // nr natural-log row weights
   float* pot;              // nr potentials, updated in place
-  bf16x8* bias_out;        // nr bias records for the next pass of the other side
+  bf16x8* bias_out;        // bias chunk of row 0 for the next pass of the other side
+  int bias_stride;         // bf16x8 units between consecutive rows' bias chunks
   float* Lout;             // nr log2-sum-exp values of this pass
   const float* Lin;        // nr log2-sum-exp values of this side's previous pass (shifted sweep)
   const float* hval_in;    // nr biases (log2 units) this side had before this pass
@@ -75,18 +76,22 @@ struct MfmaPrepSide {
   bf16x8* col_rec;   // n records (column form)
   float* alpha;
   float* lw;
-  bf16x8* bias;      // n bias records of the starting potential
+  bf16x8* bias;      // n bias records of the starting potential (separate layout)
   bf16x8* bias_alt;  // the second bias buffer (its padding is initialized too)
   float* hval;       // n biases (log2 units) of the starting potential
   int64_t n;
 };
 
 int mfma_nkb(int dtype, int d);  // K blocks per record, 0 if the resident kernel does not serve d
+// Merged layout: the column bias chunk lives in the last (free) 16-byte chunk
+// of each column record instead of a separate bias record, saving one MFMA
+// and one LDS block per tile. Possible when the data leaves that chunk free.
+bool mfma_merged(int dtype, int d, int nkb);
 int mfma_rb(int nkb);
 // Points per side including the masked padding columns (records, bias buffers).
 int64_t mfma_padded_count(int64_t n);
-PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb);
-hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged);
+hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, bool merged,
                            const PassPlan& pl, hipStream_t s);
 // GEMM-tiled half-pass for wide records (any NKB that is a multiple of 4).
 int gemm_nkb(int dtype, int d);
@@ -104,7 +109,7 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
 hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
                               int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s);
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
-                            int nkb, bool center, double* centroid_part, float* shift,
+                            int nkb, bool merged, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,
                             float c2, hipStream_t s);
 // escale and bias_scale of a storage type (see MfmaPassArgs).

@@ -23,11 +23,11 @@ __device__ __forceinline__ void split3(float v, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)(r1 - (float)mid);
 }
 
-// Bias record of one column: half 0 = (hi, mid, lo, 1, 1, 1, 0, 0), half 1 = zeros.
-// The three ones meet the row side's (-M) parts in the shifted sweep.
-__device__ __forceinline__ void write_bias_record(bf16x8* rec, float htilde) {
+// Bias chunk of one column: (hi, mid, lo, 1, 1, 1, 0, 0). The three ones meet
+// the row side's (-M) parts in the shifted sweep.
+__device__ __forceinline__ void write_bias_chunk(bf16x8* dst, float htilde) {
   float v = htilde < kMaskedBias ? kMaskedBias : htilde;  // -inf (zero weight) -> masked; NaN kept
-  bf16x8 h0 = {}, h1 = {};
+  bf16x8 h0 = {};
   __bf16 a, b, c;
   split3(v, a, b, c);
   h0[0] = a;
@@ -36,8 +36,13 @@ __device__ __forceinline__ void write_bias_record(bf16x8* rec, float htilde) {
   h0[3] = (__bf16)1.0f;
   h0[4] = (__bf16)1.0f;
   h0[5] = (__bf16)1.0f;
-  rec[0] = h0;
-  rec[1] = h1;
+  *dst = h0;
+}
+
+// Separate bias record of one column: half 0 = the bias chunk, half 1 = zeros.
+__device__ __forceinline__ void write_bias_record(bf16x8* rec, float htilde) {
+  write_bias_chunk(rec, htilde);
+  rec[1] = bf16x8{};
 }
 
 // Row-side bias block: (1, 1, 1, -M parts) in half 0, zeros in half 1.
@@ -64,7 +69,7 @@ __device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, f
   if (p.symmetric) v = 0.5f * (p.pot[i] + v);
   p.pot[i] = v;
   const float h = fmaf(kLog2e, p.lw[i], (v - al) * p.log2e_over_eps);
-  write_bias_record(p.bias_out + 2 * (int64_t)i, h * p.bias_scale);
+  write_bias_chunk(p.bias_out + (int64_t)i * p.bias_stride, h * p.bias_scale);
   const float dh = h - p.hval_in[i];
   p.hval_out[i] = h;
   p.Lout[i] = L;
