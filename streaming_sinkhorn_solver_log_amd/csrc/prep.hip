@@ -22,19 +22,45 @@ __device__ inline float load_point(const void* pts, int dtype, int64_t idx) {
 }
 
 // Partial coordinate sums (float64) of both clouds: part[b][0..d) for x, part[b][d..2d) for y.
+// Block b sums a contiguous range of rows. For d <= 256 the block reads the
+// range as a flat, coalesced stream: thread t < T (T = the largest multiple of
+// d not above 256) owns coordinate t % d and every (T / d)-th row; the T
+// per-thread sums are then added per coordinate in a fixed order. Wider
+// points give each thread whole coordinates.
 __global__ __launch_bounds__(256) void k_centroid_partial(const void* x, int64_t n, const void* y,
                                                            int64_t m, int dtype, int d,
                                                            double* part) {
+  __shared__ double acc[256];
   const int b = blockIdx.x;
+  const int t = threadIdx.x;
   for (int side = 0; side < 2; ++side) {
     const void* pts = side ? y : x;
     const int64_t cnt = side ? m : n;
     const int64_t per = (cnt + gridDim.x - 1) / gridDim.x;
     const int64_t r0 = b * per, r1 = min(cnt, r0 + per);
-    for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    double* out = part + ((int64_t)b * 2 + side) * d;
+    if (d <= 256) {
+      const int T = (256 / d) * d;
+      const int step = T / d;  // rows advanced per sweep of the block
       double s = 0.0;
-      for (int64_t r = r0; r < r1; ++r) s += load_point(pts, dtype, r * d + k);
-      part[((int64_t)b * 2 + side) * d + k] = s;
+      if (t < T) {
+        const int k = t % d;
+        for (int64_t r = r0 + t / d; r < r1; r += step) s += load_point(pts, dtype, r * d + k);
+      }
+      acc[t] = s;
+      __syncthreads();
+      if (t < d) {
+        double tot = 0.0;
+        for (int q = t; q < T; q += d) tot += acc[q];
+        out[t] = tot;
+      }
+      __syncthreads();
+    } else {
+      for (int k = t; k < d; k += blockDim.x) {
+        double s = 0.0;
+        for (int64_t r = r0; r < r1; ++r) s += load_point(pts, dtype, r * d + k);
+        out[k] = s;
+      }
     }
   }
 }

@@ -323,6 +323,41 @@ def test_apply_arbitrary_potentials(sk, key, scale):
     assert eg <= tol_rel(w)
 
 
+SPLIT_SHAPES = [
+    (6, 200_000, 700),    # far more row blocks than resident workgroups; 6 stages -> one column chunk
+    (6, 700, 200_000),    # few row blocks, many stages: every row block merged from many partials
+    (3, 130_000, 900),    # bf16 d = 64, wide row range
+    (1, 300, 300),        # a single workgroup per side
+    (1, 33, 4000),
+]
+
+
+@pytest.mark.parametrize("key,n,m", SPLIT_SHAPES)
+def test_work_split_regimes(sk, key, n, m):
+    """Shapes at the edges of the balanced work split, checked on sampled rows of the
+    last half-pass: F(g) for rows of x and G(f) for rows of y."""
+    w = W.CONFIGS[key].scaled(n, m, 3)
+    say(f"work split cfg={key} n={n} m={m} d={w.d} {w.dtype}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, "alternating")
+    assert torch.isfinite(f).all() and torch.isfinite(g).all()
+    f1, g1, _ = sk.solve(x, y, a, b, w.eps, 1, "alternating", f0=f, g0=g)
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(n, min(n, 64), replace=False))
+    cols = np.sort(rng.choice(m, min(m, 64), replace=False))
+    x64, y64 = inp.x64(), inp.y64()
+    f1n = f1.cpu().numpy().astype(np.float64)
+    fr = oracle.F(x64[rows], y64, inp.b, g.cpu().numpy().astype(np.float64), w.eps)
+    gr = oracle.G(x64, y64[cols], inp.a, f1n, w.eps)
+    tf = 1e-3 * max(np.abs(fr).max(), w.eps) if w.dtype == "bf16" else 1e-4 * w.eps
+    tg = 1e-3 * max(np.abs(gr).max(), w.eps) if w.dtype == "bf16" else 1e-4 * w.eps
+    ef = np.abs(f1n[rows] - fr).max()
+    eg = np.abs(g1.cpu().numpy()[cols] - gr).max()
+    say(f"  sampled max|df|={ef:.3e} (tol {tf:.1e}) max|dg|={eg:.3e} (tol {tg:.1e})")
+    assert ef <= tf and eg <= tg
+
+
 @pytest.mark.parametrize("key", [2, 6])
 def test_full_size_sampled_rows(sk, key):
     """Full-size solve in the benchmark's launch configuration, checked on sampled rows."""
