@@ -276,7 +276,7 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
     pv_parts(dtype, grad, ap.pp, ap.vp);
     const int blocks = (int)((kv + 31) / 32);
-    ap.nob = pv_nob(blocks);
+    ap.nob = pv_nob(gemm, blocks);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
     ap.nobt = ap.nchunks * ap.nob;
     ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks);

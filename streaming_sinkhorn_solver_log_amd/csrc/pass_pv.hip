@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
 // the value products of each wave's 64 x 64 quarter; the two column waves of
 // a row pair merge their partials through LDS at the end.
 template <int NOB, int PP, int VP>
-__global__ __launch_bounds__(kThreads, 2) void k_pv_gemm(const PvArgs p, int nkb) {
+__global__ __launch_bounds__(kThreads, NOB >= 4 ? 1 : 2) void k_pv_gemm(const PvArgs p, int nkb) {
   __shared__ __attribute__((aligned(16))) GemmLds lds;
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
@@ -399,37 +399,48 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_gemm(const PvArgs p, int nkb
   }
 
   // Column wave 1 hands its partials to column wave 0 of the same rows (same
-  // lane layout); the staging buffers are free after the last barrier.
-  constexpr int PER = 2 * (2 + NOB * 16);
+  // lane layout) through the staging buffers, free after the last barrier:
+  // first (mu, S), then two value blocks per round.
+  constexpr int PER = 2 * (2 + 2 * 16);  // floats per lane per round
   static_assert(2 * PER * 64 * 4 <= (int)sizeof(GemmLds), "merge area exceeds the staging buffers");
   float* xl = reinterpret_cast<float*>(&lds) + wr * PER * 64 + lane;
-  if (wc == 1) {
+  float f0[2], f1[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      xl[(rb * (2 + NOB * 16)) * 64] = mu[rb];
-      xl[(rb * (2 + NOB * 16) + 1) * 64] = S[rb];
+  for (int ob0 = 0; ob0 < NOB; ob0 += 2) {
+    if (wc == 1) {
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob)
+      for (int rb = 0; rb < 2; ++rb) {
+        xl[(rb * 34) * 64] = mu[rb];
+        xl[(rb * 34 + 1) * 64] = S[rb];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xl[(rb * (2 + NOB * 16) + 2 + ob * 16 + r) * 64] = O[rb][ob][r];
+        for (int q = 0; q < 2; ++q)
+          if (ob0 + q < NOB)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xl[(rb * 34 + 2 + q * 16 + r) * 64] = O[rb][ob0 + q][r];
+      }
     }
-  }
-  __syncthreads();
-  if (wc == 0) {
+    __syncthreads();
+    if (wc == 0) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float mo = xl[(rb * (2 + NOB * 16)) * 64];
-      const float so = xl[(rb * (2 + NOB * 16) + 1) * 64];
-      const float mt = fmaxf(mu[rb], mo);
-      const float f0 = fast_exp2(e * (mu[rb] - mt)), f1 = fast_exp2(e * (mo - mt));
-      S[rb] = S[rb] * f0 + so * f1;
+      for (int rb = 0; rb < 2; ++rb) {
+        if (ob0 == 0) {
+          const float mo = xl[(rb * 34) * 64];
+          const float so = xl[(rb * 34 + 1) * 64];
+          const float mt = fmaxf(mu[rb], mo);
+          f0[rb] = fast_exp2(e * (mu[rb] - mt));
+          f1[rb] = fast_exp2(e * (mo - mt));
+          S[rb] = S[rb] * f0[rb] + so * f1[rb];
+          mu[rb] = mt;
+        }
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob)
+        for (int q = 0; q < 2; ++q)
+          if (ob0 + q < NOB)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          O[rb][ob][r] = O[rb][ob][r] * f0 + xl[(rb * (2 + NOB * 16) + 2 + ob * 16 + r) * 64] * f1;
-      mu[rb] = mt;
+            for (int r = 0; r < 16; ++r)
+              O[rb][ob0 + q][r] = O[rb][ob0 + q][r] * f0[rb] + xl[(rb * 34 + 2 + q * 16 + r) * 64] * f1[rb];
+      }
     }
+    __syncthreads();
   }
   pv_finish<2, NOB>(p, wc == 0, r0 + wr * 64, kGRows, O, mu, S, li, half);
 }
@@ -518,7 +529,13 @@ void pv_parts(int dtype, bool grad, int& pp, int& vp) {
   }
 }
 
-int pv_nob(int nobt) { return nobt >= 2 ? 2 : 1; }
+int pv_nob(bool gemm, int nobt) {
+  // The GEMM-tiled kernel recomputes the scores once per chunk of value blocks,
+  // so it carries up to 4 blocks per chunk (one workgroup per CU then; 8 would
+  // spill).
+  if (gemm) return nobt >= 4 ? 4 : (nobt >= 2 ? 2 : 1);
+  return nobt >= 2 ? 2 : 1;
+}
 
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks) {
   PassPlan pl{};
@@ -545,6 +562,7 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
   if (gemm) {
     if (nob == 1) return run_pv_gemm<1>(a, nkb, pp, vp, grid, s);
     if (nob == 2) return run_pv_gemm<2>(a, nkb, pp, vp, grid, s);
+    if (nob == 4) return run_pv_gemm<4>(a, nkb, pp, vp, grid, s);
     return hipErrorInvalidValue;
   }
   const int rb = pv_rb(nkb, nob, vp);

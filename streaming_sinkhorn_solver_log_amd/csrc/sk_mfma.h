@@ -101,7 +101,7 @@ hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool sc
 // Transport application / gradient kernels. pv_parts: bf16 parts of the plan
 // entries (pp) and of the values (vp) for a storage type and operation.
 void pv_parts(int dtype, bool grad, int& pp, int& vp);
-int pv_nob(int nobt);  // value blocks per launch chunk
+int pv_nob(bool gemm, int nobt);  // value blocks per launch chunk
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
                      const PassPlan& pl, hipStream_t s);
