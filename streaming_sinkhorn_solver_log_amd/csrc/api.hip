@@ -8,6 +8,7 @@
 #include "flashsk.h"
 #include "sk_internal.h"
 #include "sk_mfma.h"
+#include "sk_gemm.h"
 #include <stdlib.h>
 
 namespace sk {

@@ -16,7 +16,8 @@
 // M ~ 128 records per side in LDS).
 #include "sk_internal.h"
 #include "sk_mfma.h"
-#include "sk_mfma_dev.h"
+#include "sk_gemm.h"
+#include "sk_gemm_dev.h"
 
 #include <math.h>
 

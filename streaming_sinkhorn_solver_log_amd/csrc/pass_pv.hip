@@ -30,7 +30,8 @@
 // over both halves of the wave, so one shift holds for a whole MFMA sum.
 #include "sk_internal.h"
 #include "sk_mfma.h"
-#include "sk_mfma_dev.h"
+#include "sk_gemm.h"
+#include "sk_gemm_dev.h"
 
 #include <math.h>
 

@@ -1,0 +1,25 @@
+// sk_gemm.h -- GEMM-tiled half-pass and transport application / gradient
+// kernels (library-internal).
+#pragma once
+
+#include "sk_mfma.h"
+
+namespace sk {
+
+// GEMM-tiled half-pass for wide records (any NKB that is a multiple of 4).
+int gemm_nkb(int dtype, int d);
+PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
+hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled,
+                           const PassPlan& pl, hipStream_t s);
+// Transport application / gradient kernels. pv_parts: bf16 parts of the plan
+// entries (pp) and of the values (vp) for a storage type and operation.
+void pv_parts(int dtype, bool grad, int& pp, int& vp);
+int pv_nob(bool gemm, int nobt);  // value blocks per launch chunk
+PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
+hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+                     const PassPlan& pl, hipStream_t s);
+// Value fragments of nv points (src nv x kv, float32 or bf16 bits) for vp parts.
+hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
+                              int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s);
+
+}  // namespace sk
