@@ -20,6 +20,7 @@
 #include "sk_gemm_dev.h"
 
 #include <math.h>
+#include <stdint.h>
 
 namespace sk {
 namespace {
@@ -234,20 +235,58 @@ __global__ __launch_bounds__(kThreads, 2) void k_lse_gemm(const MfmaPassArgs p, 
 
 }  // namespace
 
+int64_t round_filling_splits(int64_t units, int64_t nc, int64_t unit_cols, int64_t max_splits,
+                             int64_t resident, int64_t& cols_per_split) {
+  // Workgroups run in rounds of `resident`; a round costs about one split's
+  // columns. Take the split count with the fewest column-rounds (ties: fewer
+  // splits), so the last round is not left mostly empty.
+  if (max_splits < 1) max_splits = 1;
+  if (resident < 1) resident = 1;
+  int64_t best = 1, best_cps = 0, best_cost = INT64_MAX;
+  for (int64_t s = 1; s <= max_splits; ++s) {
+    int64_t cps = (nc + s - 1) / s;
+    cps = (cps + unit_cols - 1) / unit_cols * unit_cols;
+    const int64_t se = (nc + cps - 1) / cps;
+    if (se < s) continue;  // same split as a smaller s
+    const int64_t rounds = (units * se + resident - 1) / resident;
+    const int64_t cost = rounds * cps;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = se;
+      best_cps = cps;
+    }
+  }
+  cols_per_split = best_cps;
+  return best;
+}
+
+namespace {
+int gemm_resident() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0, per_cu = 0, most = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    // the four instantiations share the LDS footprint that binds occupancy
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_gemm<true, true>, kThreads, 0) == hipSuccess)
+      most = per_cu;
+    if (most < 1) most = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    cached = most * cus;
+  }
+  return cached;
+}
+}  // namespace
+
 PassPlan plan_gemm_pass(int64_t nr, int64_t nc) {
   PassPlan pl{};
   pl.rows_per_block = kGRows;
   pl.row_blocks = (int)((nr + kGRows - 1) / kGRows);
-  const int64_t target = 1024;  // two workgroups per CU (LDS bound), two waves of them
-  int64_t splits = (target + pl.row_blocks - 1) / pl.row_blocks;
-  const int64_t max_splits = nc / 512 > 1 ? nc / 512 : 1;
-  if (splits > max_splits) splits = max_splits;
-  if (splits > 64) splits = 64;
-  if (splits < 1) splits = 1;
-  int64_t cps = (nc + splits - 1) / splits;
-  cps = (cps + kGCols - 1) / kGCols * kGCols;  // whole column blocks
+  int64_t max_splits = nc / 512 > 1 ? nc / 512 : 1;
+  if (max_splits > 64) max_splits = 64;
+  int64_t cps = 0;
+  pl.splits = (int)round_filling_splits(pl.row_blocks, nc, kGCols, max_splits, gemm_resident(), cps);
   pl.cols_per_split = (int)cps;
-  pl.splits = (int)((nc + cps - 1) / cps);
   return pl;
 }
 

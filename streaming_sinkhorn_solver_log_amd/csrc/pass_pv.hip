@@ -538,18 +538,49 @@ int pv_nob(bool gemm, int nobt) {
   return nobt >= 2 ? 2 : 1;
 }
 
+namespace {
+// Resident workgroups of the GEMM-tiled kernel carrying nob value blocks.
+int pv_gemm_resident(int nob) {
+  static int cached[5] = {};
+  if (nob < 1 || nob > 4) return 256;
+  int& slot = cached[nob];
+  if (slot == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    hipError_t e = hipErrorInvalidValue;
+    if (nob == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<1, 3, 3>, kThreads, 0);
+    if (nob == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<2, 3, 3>, kThreads, 0);
+    if (nob == 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<4, 3, 3>, kThreads, 0);
+    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    slot = per_cu * cus;
+  }
+  return slot;
+}
+}  // namespace
+
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks) {
   PassPlan pl{};
   pl.rows_per_block = gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32;
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
-  const int64_t target = (gemm ? 1024 : 2048) / (nchunks > 0 ? nchunks : 1);
+  if (gemm) {
+    int64_t max_splits = nc / 512 > 1 ? nc / 512 : 1;
+    if (max_splits > 64) max_splits = 64;
+    int64_t cps = 0;
+    const int64_t units = (int64_t)pl.row_blocks * (nchunks > 0 ? nchunks : 1);
+    pl.splits = (int)round_filling_splits(units, nc, kGCols, max_splits, pv_gemm_resident(nob), cps);
+    pl.cols_per_split = (int)cps;
+    return pl;
+  }
+  const int64_t target = 2048 / (nchunks > 0 ? nchunks : 1);
   int64_t splits = (target + pl.row_blocks - 1) / pl.row_blocks;
-  const int64_t min_cols = gemm ? 512 : 1024;
+  const int64_t min_cols = 1024;
   const int64_t max_splits = nc / min_cols > 1 ? nc / min_cols : 1;
   if (splits > max_splits) splits = max_splits;
   if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
-  const int64_t unit = gemm ? kGCols : 64;
+  const int64_t unit = 64;
   int64_t cps = (nc + splits - 1) / splits;
   cps = (cps + unit - 1) / unit * unit;
   pl.cols_per_split = (int)cps;

@@ -6,6 +6,11 @@
 
 namespace sk {
 
+// Column splits for `units` independent row units (row blocks, or row blocks x
+// value chunks) so that whole rounds of `resident` workgroups are filled;
+// writes the columns per split (a multiple of unit_cols).
+int64_t round_filling_splits(int64_t units, int64_t nc, int64_t unit_cols, int64_t max_splits,
+                             int64_t resident, int64_t& cols_per_split);
 // GEMM-tiled half-pass for wide records (any NKB that is a multiple of 4).
 int gemm_nkb(int dtype, int d);
 PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
