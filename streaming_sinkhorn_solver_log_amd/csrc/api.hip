@@ -172,6 +172,7 @@ struct SolvePlan {
   Path path;
   int nkb;      // matrix-core records: K blocks per record
   bool merged;  // register-resident pass with the bias chunk inside the column records
+  bool wide;    // GEMM-tiled pass with the 128 x 256 workgroup tile
   PassPlan f, g;
 };
 
@@ -183,6 +184,7 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
   sp.path = solve_path(dtype, d);
   sp.nkb = 0;
   sp.merged = false;
+  sp.wide = false;
   if (sp.path == Path::Mfma) {
     sp.nkb = mfma_nkb(dtype, (int)d);
     sp.merged = alternating && mfma_merged(dtype, (int)d, sp.nkb);
@@ -190,8 +192,9 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
     sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged);
   } else if (sp.path == Path::Gemm) {
     sp.nkb = gemm_nkb(dtype, (int)d);
-    sp.f = plan_gemm_pass(n, m);
-    sp.g = plan_gemm_pass(m, n);
+    sp.wide = dtype == SK_F32;
+    sp.f = plan_gemm_pass(n, m, sp.wide);
+    sp.g = plan_gemm_pass(m, n, sp.wide);
   } else {
     sp.f = plan_valu_pass(n, m, (int)d);
     sp.g = plan_valu_pass(m, n, (int)d);
@@ -395,7 +398,7 @@ int solve_valu(const SolveWs& L, const SolvePlan& sp, int64_t n, int64_t m, int6
 
 hipError_t launch_pass(const SolvePlan& sp, const MfmaPassArgs& a, bool shifted, bool scaled,
                        const PassPlan& pl, hipStream_t s) {
-  if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, pl, s);
+  if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, sp.wide, pl, s);
   return launch_lse_mfma(a, sp.nkb, shifted, scaled, sp.merged, pl, s);
 }
 
