@@ -53,15 +53,21 @@ __device__ __forceinline__ const bf16x8* vfrag_at(const PvArgs& p, int64_t tile,
   return p.vfrag + ((((tile * p.nobt + ob) * vp_parts + vp) * 2 + kb) << 6);
 }
 
+// Lane l supplies value index l % 32 of each block; lanes past the value
+// width hold zeros in the fragments, so they skip the load (for k = 16 half
+// the bytes, for the d = 3 gradient 29 of 32).
 template <int NOB, int VP>
 __device__ __attribute__((always_inline)) inline void load_vtile(VTile<NOB, VP>& vt, const PvArgs& p,
                                                                  int64_t tile, int ob0, int lane) {
 #pragma unroll
-  for (int ob = 0; ob < NOB; ++ob)
+  for (int ob = 0; ob < NOB; ++ob) {
+    const bool live = (ob0 + ob) * 32 + (lane & 31) < p.kv;
 #pragma unroll
     for (int vp = 0; vp < VP; ++vp)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) vt.v[ob][vp][kb] = vfrag_at(p, tile, ob0 + ob, VP, vp, kb)[lane];
+      for (int kb = 0; kb < 2; ++kb)
+        vt.v[ob][vp][kb] = live ? vfrag_at(p, tile, ob0 + ob, VP, vp, kb)[lane] : bf16x8{};
+  }
 }
 
 __device__ __forceinline__ float max16(const f32x16& a) {
