@@ -264,6 +264,7 @@ template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED>
 __global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
+  static_assert(ROWS <= kThreads, "the partial merge finishes one row per thread");
   __shared__ float red[kThreads / 64];
   __shared__ __attribute__((aligned(16))) StageRing<NKB, MERGED> lds;
   // Row side of the bias block: (1, 1, 1, -shift parts) meeting the column's
