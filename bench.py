@@ -228,6 +228,23 @@ def _pass_roofline(w, pass_ms):
             "frac": rate / alu_peak, "traffic": None, "also": also}
 
 
+def op_roofline(w, ms, value_width):
+    """Roofline of a gradient / application launch (n x m pairs): per pair the
+    scores (2d flops) and the weighted sum over the value width (2 * width
+    flops) on the matrix cores, and at least the half-pass's exp2 and add on
+    the VALU. The longer ideal time is the bound."""
+    pairs = w.n * w.m
+    sec = ms * 1e-3
+    peak = BF16_MFMA_PEAK if w.dtype == "bf16" else F32_MFMA_PEAK
+    flops = 2.0 * (w.d + value_width) * pairs
+    alu_peak = VALU_PEAK / alu_slots_per_pair(w)
+    t_mfma, t_alu = flops / peak, pairs / alu_peak
+    r = {"ms": ms, "mfma_frac": t_mfma / sec, "alu_frac": t_alu / sec}
+    r["bound"] = "mfma" if t_mfma >= t_alu else "alu"
+    r["frac"] = max(t_mfma, t_alu) / sec
+    return r
+
+
 def measure(case, steps, warmup):
     torch = case.torch
     for _ in range(warmup):
@@ -261,6 +278,16 @@ def measure(case, steps, warmup):
         "solve_only_iters_per_s": w.iters / (statistics.median(solve_ms) * 1e-3),
         "nmd_iters_per_s": w.n * w.m * w.d * w.iters * steps / wall,
         "roofline": pass_roofline(w, pass_ms),
+        # every step of the path against its own roof (prep and cost: one
+        # zero-iteration solve, O(n + m) work, launch bound)
+        "rows": {
+            "a1_a6_prep_and_cost_ms": ov,
+            "a3_a4_half_pass": {"ms": pass_ms, **{k: v for k, v in pass_roofline(w, pass_ms).items()
+                                                  if k in ("bound", "frac")}},
+            "a7_grad": op_roofline(w, statistics.median(grad_ms), w.d),
+            "a8_PV": op_roofline(w, statistics.median(pv_ms), case.k),
+            "a8_PtU": op_roofline(w, statistics.median(ptu_ms), case.k),
+        },
     }
 
 
