@@ -120,10 +120,16 @@ def workspace_bytes(op: int, dtype: int, n: int, m: int, d: int, k: int = 0) -> 
 
 
 def _workspace(op, dtype, n, m, d, k, device, ws):
+    """A 256-byte aligned region of at least the required size: the caller's
+    uint8 tensor if large enough, else a new one. A new tensor is allocated on
+    the current stream, which the library's launches use too, so the caching
+    allocator cannot hand it to other work before they finish."""
     need = workspace_bytes(op, dtype, n, m, d, k)
     if need == 0:
         need = 256  # invalid sizes: the library reports the reason
-    if ws is None or ws.numel() < need:
+    if ws is not None and (ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    if ws is None or ws.numel() < need + (-ws.data_ptr()) % 256:
         ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws, ws.data_ptr() + off, ws.numel() - off
@@ -148,10 +154,11 @@ def solve(x, y, a, b, eps: float, iters: int, mode: str = "alternating", f0=None
         f = torch.empty(n, dtype=torch.float32, device=dev)
         g = torch.empty(m, dtype=torch.float32, device=dev)
     cost = torch.empty((), dtype=torch.float64, device=dev)
-    _, wptr, wbytes = _workspace(SK_OP_SOLVE, dt, n, m, d, 0, dev, workspace)
-    _check(_lib.sk_sinkhorn_solve(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
-                                  int(iters), mode_code, flags, _ptr(f), _ptr(g), _ptr(cost),
-                                  ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    ws, wptr, wbytes = _workspace(SK_OP_SOLVE, dt, n, m, d, 0, dev, workspace)
+    with torch.cuda.device(dev):  # the library's HIP calls act on the current device
+        _check(_lib.sk_sinkhorn_solve(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
+                                      int(iters), mode_code, flags, _ptr(f), _ptr(g), _ptr(cost),
+                                      ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return f, g, cost
 
 
@@ -169,10 +176,11 @@ def transport_apply(x, y, a, b, f, g, eps: float, V, transpose: bool = False, wo
     V2 = V2.contiguous()
     k = V2.shape[1]
     out = torch.empty((m if transpose else n, k), dtype=torch.float32, device=dev)
-    _, wptr, wbytes = _workspace(SK_OP_APPLY, dt, n, m, d, k, dev, workspace)
-    _check(_lib.sk_transport_apply(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(f), _ptr(g),
-                                   float(eps), int(bool(transpose)), _ptr(V2), k, _ptr(out),
-                                   ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    ws, wptr, wbytes = _workspace(SK_OP_APPLY, dt, n, m, d, k, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_transport_apply(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(f), _ptr(g),
+                                       float(eps), int(bool(transpose)), _ptr(V2), k, _ptr(out),
+                                       ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return out[:, 0] if squeeze else out
 
 
@@ -183,7 +191,8 @@ def eot_grad_x(x, y, a, b, g, eps: float, workspace=None):
     for t, cnt, name in ((a, n, "a"), (b, m, "b"), (g, m, "g")):
         _vec(t, cnt, name, dev)
     out = torch.empty((n, d), dtype=torch.float32, device=dev)
-    _, wptr, wbytes = _workspace(SK_OP_GRAD, dt, n, m, d, 0, dev, workspace)
-    _check(_lib.sk_eot_grad_x(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(g), float(eps),
-                              _ptr(out), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    ws, wptr, wbytes = _workspace(SK_OP_GRAD, dt, n, m, d, 0, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_eot_grad_x(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(g), float(eps),
+                                  _ptr(out), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return out
