@@ -22,6 +22,7 @@
 #include "sk_gemm.h"
 #include "sk_gemm_dev.h"
 
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -382,11 +383,16 @@ int64_t round_filling_splits(int64_t units, int64_t nc, int64_t unit_cols, int64
 
 namespace {
 int gemm_resident(bool wide) {
-  static int cached[2] = {};
-  int& slot = cached[wide ? 1 : 0];
-  if (slot == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  // Per device and tile shape, computed once; concurrent first calls compute
+  // the same value.
+  constexpr int kDevices = 16;
+  static std::atomic<int> cached[kDevices][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev][wide ? 1 : 0] : nullptr;
+  int v = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    int cus = 0, per_cu = 0;
     // the instantiations of one shape share the LDS footprint that binds occupancy
     const hipError_t e =
         wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_gemm<true, false, 2, 4>, kThreads, 0)
@@ -394,9 +400,10 @@ int gemm_resident(bool wide) {
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    slot = per_cu * cus;
+    v = per_cu * cus;
+    if (slot) slot->store(v, std::memory_order_relaxed);
   }
-  return slot;
+  return v;
 }
 }  // namespace
 

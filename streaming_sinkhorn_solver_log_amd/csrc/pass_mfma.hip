@@ -38,6 +38,7 @@
 #include "sk_mfma.h"
 #include "sk_mfma_dev.h"
 
+#include <atomic>
 #include <math.h>
 
 #include <type_traits>
@@ -532,12 +533,16 @@ hipError_t run_lse(const MfmaPassArgs& a, bool shifted, bool scaled, const PassP
 
 // Workgroups of the shifted kernel of a record width that fit on the device at once.
 int resident_workgroups(int nkb, bool merged) {
-  static int cached[9][2] = {};
+  // Per device and record width, computed once; concurrent first calls
+  // compute the same value.
+  constexpr int kDevices = 16;
+  static std::atomic<int> cached[kDevices][9][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (nkb < 1 || nkb > 8) return 0;
-  int& slot = cached[nkb][merged ? 1 : 0];
-  if (slot == 0) {
+  std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev][nkb][merged ? 1 : 0] : nullptr;
+  int v = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
     int per_cu = 0, cus = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (nkb * 2 + (merged ? 1 : 0)) {
@@ -551,9 +556,10 @@ int resident_workgroups(int nkb, bool merged) {
     }
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    slot = per_cu * cus;
+    v = per_cu * cus;
+    if (slot) slot->store(v, std::memory_order_relaxed);
   }
-  return slot;
+  return v;
 }
 
 }  // namespace

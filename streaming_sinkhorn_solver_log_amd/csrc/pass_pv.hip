@@ -33,6 +33,7 @@
 #include "sk_gemm.h"
 #include "sk_gemm_dev.h"
 
+#include <atomic>
 #include <math.h>
 
 namespace sk {
@@ -547,12 +548,17 @@ int pv_nob(bool gemm, int nobt) {
 namespace {
 // Resident workgroups of the GEMM-tiled kernel carrying nob value blocks.
 int pv_gemm_resident(int nob) {
-  static int cached[5] = {};
+  // Per device and value blocks per chunk, computed once; concurrent first
+  // calls compute the same value.
+  constexpr int kDevices = 16;
+  static std::atomic<int> cached[kDevices][5];
   if (nob < 1 || nob > 4) return 256;
-  int& slot = cached[nob];
-  if (slot == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev][nob] : nullptr;
+  int v = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    int cus = 0, per_cu = 0;
     hipError_t e = hipErrorInvalidValue;
     if (nob == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<1, 3, 3>, kThreads, 0);
     if (nob == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<2, 3, 3>, kThreads, 0);
@@ -560,9 +566,10 @@ int pv_gemm_resident(int nob) {
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    slot = per_cu * cus;
+    v = per_cu * cus;
+    if (slot) slot->store(v, std::memory_order_relaxed);
   }
-  return slot;
+  return v;
 }
 }  // namespace
 
