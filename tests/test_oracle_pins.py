@@ -321,3 +321,59 @@ def test_zero_weights_drop_out():
     np.testing.assert_allclose(f, fk, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(g[keep], gk, rtol=1e-12, atol=1e-14)
     assert cost == pytest.approx(ck, rel=1e-12)
+
+
+# ---------------------------------------------------------------- debiased divergence
+# The review names a "debiased-Sinkhorn" sweep (Weaknesses, "Downstream drivers
+# absent"); S = OT(a,b) - OT(a,a)/2 - OT(b,b)/2 is the textbook form. Its pins:
+# it vanishes on identical inputs, is positive otherwise (the kernel
+# exp(-|x-y|^2/eps) is positive definite), is symmetric under swapping the two
+# measures, and its gradients match central differences of S itself.
+_DIV_ITERS = 3000
+
+
+def test_divergence_vanishes_on_identical_inputs_and_is_positive():
+    eps = 0.1
+    x, a = _cloud(101, 7, 2), _weights(102, 7)
+    assert abs(oracle.divergence(x, x, a, a, eps, _DIV_ITERS)[0]) < 1e-12
+    for seed in range(3):
+        y, b = _cloud(110 + seed, 6 + seed, 2, 0.2, 1.3), _weights(120 + seed, 6 + seed)
+        assert oracle.divergence(x, y, a, b, eps, _DIV_ITERS)[0] > 1e-4
+
+
+def test_divergence_is_swap_symmetric():
+    eps = 0.15
+    x, y = _cloud(131, 6, 3), _cloud(132, 8, 3, 0.1, 1.1)
+    a, b = _weights(133, 6), _weights(134, 8)
+    s1 = oracle.divergence(x, y, a, b, eps, _DIV_ITERS)[0]
+    s2 = oracle.divergence(y, x, b, a, eps, _DIV_ITERS)[0]
+    assert s1 == pytest.approx(s2, rel=1e-10)
+
+
+def test_divergence_gradients_match_finite_differences():
+    eps, h = 0.1, 1e-6
+    x, y = _cloud(141, 6, 2), _cloud(142, 7, 2, 0.2, 1.2)
+    a, b = _weights(143, 6), _weights(144, 7)
+
+    def S(x_, y_, a_, b_):
+        return oracle.divergence(x_, y_, a_, b_, eps, _DIV_ITERS)[0]
+
+    _, ga, gb, gx, gy = oracle.divergence(x, y, a, b, eps, _DIV_ITERS)
+    for (i, k) in [(0, 0), (3, 1), (5, 0)]:
+        xp, xm = x.copy(), x.copy()
+        xp[i, k] += h
+        xm[i, k] -= h
+        assert (S(xp, y, a, b) - S(xm, y, a, b)) / (2 * h) == pytest.approx(gx[i, k], rel=1e-6, abs=1e-8)
+    for (j, k) in [(1, 1), (6, 0)]:
+        yp, ym = y.copy(), y.copy()
+        yp[j, k] += h
+        ym[j, k] -= h
+        assert (S(x, yp, a, b) - S(x, ym, a, b)) / (2 * h) == pytest.approx(gy[j, k], rel=1e-6, abs=1e-8)
+    # weights: directions that keep the total mass (the gradients are defined
+    # up to an additive constant off the simplex)
+    da = np.zeros(6)
+    da[[1, 4]] = [1.0, -1.0]
+    db = np.zeros(7)
+    db[[0, 5]] = [1.0, -1.0]
+    assert (S(x, y, a + h * da, b) - S(x, y, a - h * da, b)) / (2 * h) == pytest.approx(ga @ da, rel=1e-6)
+    assert (S(x, y, a, b + h * db) - S(x, y, a, b - h * db)) / (2 * h) == pytest.approx(gb @ db, rel=1e-6)
