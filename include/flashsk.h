@@ -72,6 +72,7 @@ extern "C" {
 #define SK_OP_SOLVE 0
 #define SK_OP_APPLY 1
 #define SK_OP_GRAD 2
+#define SK_OP_DIVERGENCE 3
 
 /*
  * Fixed-budget Sinkhorn solve (FlashSinkhorn abstract; review, Summary and
@@ -115,6 +116,35 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
 int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                   const float* a, const float* b, const float* g, double eps, float* grad_x,
                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Debiased Sinkhorn divergence (the replication review names a
+ * "debiased-Sinkhorn" sweep among the OTDD drivers, Weaknesses, "Downstream
+ * drivers absent"; the pages print no formula, so the textbook form is used):
+ *   S = OT(x,a; y,b) - OT(x,a; x,a)/2 - OT(y,b; y,b)/2,
+ * each OT the cost <a,f> + <b,g> of a fixed-budget solve of `iters`
+ * iterations: the cross term with `mode`, the two self terms with
+ * SK_SYMMETRIC (which keeps their f = g).
+ *   flags      SK_NO_CENTER only (warm starts do not apply).
+ *   div        out: one double, S.
+ *   grad_a     out (n, or NULL): f_ab - f_aa, the gradient of S in a along
+ *              mass-preserving directions (off the simplex it holds up to an
+ *              additive constant).
+ *   grad_b     out (m, or NULL): g_ab - g_bb, likewise in b.
+ *   grad_x     out (n x d, or NULL): gradient of S in x, the barycentric
+ *              gradient of the cross term minus that of the self term
+ *              (x enters the self term on both sides: twice the one-sided
+ *              gradient, times 1/2).
+ *   grad_y     out (m x d, or NULL): likewise in y.
+ * The gradients are exact for the potentials the solves return (envelope
+ * argument); they are the gradients of S at converged potentials.
+ * Workspace: sk_workspace_bytes(SK_OP_DIVERGENCE, dtype, n, m, d, 0).
+ * Requirements as for the solve; x and y may be the same array.
+ */
+int sk_sinkhorn_divergence(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                           const float* a, const float* b, double eps, int32_t iters, int mode,
+                           uint32_t flags, double* div, float* grad_a, float* grad_b, float* grad_x,
+                           float* grad_y, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes needed by `op` for these sizes (0 on invalid sizes). */
 size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, int64_t k);

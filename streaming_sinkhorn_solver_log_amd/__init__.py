@@ -11,6 +11,7 @@ the package fails loudly if the shared library is missing.
     out = transport_apply(x, y, a, b, f, g, eps, V)                  # P V
     out = transport_apply(x, y, a, b, f, g, eps, U, transpose=True)  # P^T U
     grad = eot_grad_x(x, y, a, b, g, eps)
+    S, ga, gb, gx, gy = sinkhorn_divergence(x, y, a, b, eps, iters)  # debiased
 
 x, y: (n, d) and (m, d) float32 or bfloat16 CUDA tensors; a, b, f, g, V, U:
 float32. Plans, potentials and costs follow the conventions of flashsk.h.
@@ -29,7 +30,7 @@ SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0,
 SK_F32, SK_BF16 = 0, 1
 SK_ALTERNATING, SK_SYMMETRIC = 0, 1
 SK_WARM_START, SK_NO_CENTER = 1, 2
-SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD = 0, 1, 2
+SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE = 0, 1, 2, 3
 
 _ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
               SK_ERR_WORKSPACE: "SK_ERR_WORKSPACE", SK_ERR_HIP: "SK_ERR_HIP"}
@@ -58,6 +59,9 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_transport_apply.restype = INT
     lib.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
     lib.sk_eot_grad_x.restype = INT
+    lib.sk_sinkhorn_divergence.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, P, P,
+                                           SZ, P]
+    lib.sk_sinkhorn_divergence.restype = INT
     lib.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.sk_workspace_bytes.restype = SZ
     lib.sk_last_error.argtypes = []
@@ -68,8 +72,8 @@ def _load_library() -> ctypes.CDLL:
 
 
 _lib = _load_library()
-EXPORTS = ("sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x", "sk_workspace_bytes",
-           "sk_last_error", "sk_version")
+EXPORTS = ("sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x", "sk_sinkhorn_divergence",
+           "sk_workspace_bytes", "sk_last_error", "sk_version")
 
 
 def library() -> ctypes.CDLL:
@@ -196,3 +200,31 @@ def eot_grad_x(x, y, a, b, g, eps: float, workspace=None):
         _check(_lib.sk_eot_grad_x(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(g), float(eps),
                                   _ptr(out), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return out
+
+
+def sinkhorn_divergence(x, y, a, b, eps: float, iters: int, mode: str = "alternating", grads: bool = True,
+                        center: bool = True, workspace=None):
+    """Debiased Sinkhorn divergence S = OT(a,b) - OT(a,a)/2 - OT(b,b)/2 (flashsk.h).
+
+    Returns (S, grad_a, grad_b, grad_x, grad_y): S a 0-d float64 tensor, the
+    gradients float32 (None when grads=False).
+    """
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    _vec(a, n, "a", dev)
+    _vec(b, m, "b", dev)
+    mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
+    flags = 0 if center else SK_NO_CENTER
+    S = torch.empty((), dtype=torch.float64, device=dev)
+    ga = gb = gx = gy = None
+    if grads:
+        ga = torch.empty(n, dtype=torch.float32, device=dev)
+        gb = torch.empty(m, dtype=torch.float32, device=dev)
+        gx = torch.empty((n, d), dtype=torch.float32, device=dev)
+        gy = torch.empty((m, d), dtype=torch.float32, device=dev)
+    ws, wptr, wbytes = _workspace(SK_OP_DIVERGENCE, dt, n, m, d, 0, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_sinkhorn_divergence(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
+                                           int(iters), mode_code, flags, _ptr(S), _ptr(ga), _ptr(gb),
+                                           _ptr(gx), _ptr(gy), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return S, ga, gb, gx, gy

@@ -468,6 +468,67 @@ size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
 
 using namespace sk;
 
+// ---------------------------------------------------------------- divergence
+// Debiased Sinkhorn divergence S = OT(a,b) - OT(a,a)/2 - OT(b,b)/2 and its
+// gradients, composed from the solve and gradient entry points below (the
+// review names a "debiased-Sinkhorn" sweep among the OTDD drivers,
+// Weaknesses, "Downstream drivers absent"; the textbook form is used).
+
+__global__ void k_div_combine(const double* __restrict__ c, double* __restrict__ out) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) out[0] = c[0] - 0.5 * c[1] - 0.5 * c[2];
+}
+
+// out = p - q, elementwise (out may alias p)
+__global__ void k_sub(const float* p, const float* __restrict__ q, float* out, int64_t cnt) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = p[i] - q[i];
+}
+
+hipError_t launch_sub(const float* p, const float* q, float* out, int64_t cnt, hipStream_t s) {
+  const int64_t blocks = (cnt + 255) / 256;
+  k_sub<<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(p, q, out, cnt);
+  return hipGetLastError();
+}
+
+struct DivWs {
+  float *f_ab, *g_ab, *f_aa, *g_aa, *f_bb, *g_bb, *tmp;
+  double* costs;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+size_t div_inner_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  size_t need = 0;
+  auto take = [&](size_t v) { need = v > need ? v : need; };
+  take(solve_bytes(dtype, n, m, d));
+  take(solve_bytes(dtype, n, n, d));
+  take(solve_bytes(dtype, m, m, d));
+  if (aux_path(dtype, d) != Path::None) {
+    take(grad_bytes(dtype, n, m, d));
+    take(grad_bytes(dtype, n, n, d));
+    take(grad_bytes(dtype, m, n, d));
+    take(grad_bytes(dtype, m, m, d));
+  }
+  return need;
+}
+
+DivWs layout_div(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  DivWs L{};
+  L.f_ab = c.take<float>(n);
+  L.g_ab = c.take<float>(m);
+  L.f_aa = c.take<float>(n);
+  L.g_aa = c.take<float>(n);
+  L.f_bb = c.take<float>(m);
+  L.g_bb = c.take<float>(m);
+  L.tmp = c.take<float>((size_t)(n > m ? n : m) * d);
+  L.costs = c.take<double>(3);
+  L.inner_bytes = div_inner_bytes(dtype, n, m, d);
+  L.inner = c.take<char>(L.inner_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
 extern "C" {
 
 int sk_version(void) { return SK_VERSION; }
@@ -489,6 +550,9 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
     case SK_OP_GRAD:
       if (aux_path(dtype, d) == Path::None) return 0;
       return grad_bytes(dtype, n, m, d);
+    case SK_OP_DIVERGENCE:
+      if (solve_path(dtype, d) == Path::None) return 0;
+      return layout_div(nullptr, dtype, n, m, d).bytes;
     default: return 0;
   }
 }
@@ -612,6 +676,55 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
   ga.nr = (int)n; ga.nc = (int)m; ga.d = (int)d; ga.splits = pl.splits;
   ga.cols_per_split = pl.cols_per_split; ga.c2 = sc.c2;
   if ((e = launch_grad_valu(ga, pl, s)) != hipSuccess) return hip_fail(e, "grad");
+  return SK_OK;
+}
+
+int sk_sinkhorn_divergence(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                           const float* a, const float* b, double eps, int32_t iters, int mode,
+                           uint32_t flags, double* div, float* grad_a, float* grad_b, float* grad_x,
+                           float* grad_y, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, solve_path(dtype, d));
+  if (rc) return rc;
+  if (!div) return fail(SK_ERR_INVALID_ARG, "null output pointer");
+  if (iters < 0) return fail(SK_ERR_INVALID_ARG, "iters must be >= 0");
+  if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
+  if (flags & ~SK_NO_CENTER) return fail(SK_ERR_INVALID_ARG, "flags 0x%x: only SK_NO_CENTER applies", flags);
+  if ((grad_x || grad_y) && aux_path(dtype, d) == Path::None)
+    return fail(SK_ERR_UNSUPPORTED, "gradients at d=%lld are not supported by this build", (long long)d);
+  const DivWs L = layout_div(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // every sub-call below passes the same validation, so none fails before
+  // enqueuing anything unless the HIP runtime does
+  if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, iters, mode, flags, L.f_ab, L.g_ab,
+                              L.costs, L.inner, L.inner_bytes, stream)))
+    return rc;
+  if ((rc = sk_sinkhorn_solve(x, x, dtype, n, n, d, a, a, eps, iters, SK_SYMMETRIC, flags, L.f_aa, L.g_aa,
+                              L.costs + 1, L.inner, L.inner_bytes, stream)))
+    return rc;
+  if ((rc = sk_sinkhorn_solve(y, y, dtype, m, m, d, b, b, eps, iters, SK_SYMMETRIC, flags, L.f_bb, L.g_bb,
+                              L.costs + 2, L.inner, L.inner_bytes, stream)))
+    return rc;
+  k_div_combine<<<1, 64, 0, s>>>(L.costs, div);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "divergence");
+  if (grad_a && (e = launch_sub(L.f_ab, L.f_aa, grad_a, n, s)) != hipSuccess) return hip_fail(e, "grad_a");
+  if (grad_b && (e = launch_sub(L.g_ab, L.g_bb, grad_b, m, s)) != hipSuccess) return hip_fail(e, "grad_b");
+  if (grad_x) {
+    if ((rc = sk_eot_grad_x(x, y, dtype, n, m, d, a, b, L.g_ab, eps, grad_x, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((rc = sk_eot_grad_x(x, x, dtype, n, n, d, a, a, L.g_aa, eps, L.tmp, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((e = launch_sub(grad_x, L.tmp, grad_x, n * d, s)) != hipSuccess) return hip_fail(e, "grad_x");
+  }
+  if (grad_y) {
+    if ((rc = sk_eot_grad_x(y, x, dtype, m, n, d, b, a, L.f_ab, eps, grad_y, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((rc = sk_eot_grad_x(y, y, dtype, m, m, d, b, b, L.g_bb, eps, L.tmp, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((e = launch_sub(grad_y, L.tmp, grad_y, m * d, s)) != hipSuccess) return hip_fail(e, "grad_y");
+  }
   return SK_OK;
 }
 

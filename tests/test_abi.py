@@ -36,6 +36,8 @@ def lib():
     L.sk_sinkhorn_solve.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, SZ, P]
     L.sk_transport_apply.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, I64, P, P, SZ, P]
     L.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
+    L.sk_sinkhorn_divergence.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, P, P,
+                                         SZ, P]
     L.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     L.sk_workspace_bytes.restype = SZ
     L.sk_last_error.restype = ctypes.c_char_p
@@ -45,7 +47,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x",
-                          "sk_workspace_bytes", "sk_last_error", "sk_version"}
+                          "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.sk_version() == _header_int("SK_VERSION")
@@ -60,6 +62,10 @@ def test_workspace_sizes(lib):
             assert s >= 4 * (n + m) * d
             assert lib.sk_workspace_bytes(apply, 0, n, m, d, 16) > 0
             assert lib.sk_workspace_bytes(grad, 0, n, m, d, 0) > 0
+            # the divergence runs the three solves and four gradients in one workspace
+            dv = lib.sk_workspace_bytes(_header_int("SK_OP_DIVERGENCE"), 0, n, m, d, 0)
+            assert dv > max(s, lib.sk_workspace_bytes(solve, 0, n, n, d, 0),
+                            lib.sk_workspace_bytes(solve, 0, m, m, d, 0))
     assert lib.sk_workspace_bytes(solve, 0, 0, 5, 3, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 5, 5, 0, 0) == 0
     assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 0) == 0
@@ -117,3 +123,16 @@ def test_apply_and_grad_reject_invalid_arguments(lib):
         args = list(gbase)
         args[idx] = val
         assert lib.sk_eot_grad_x(*args) == code, (idx, val)
+
+
+def test_divergence_rejects_invalid_arguments(lib):
+    inv, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_WORKSPACE")
+    warm = _header_int("SK_WARM_START")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 3, 0, 0, FAKE, None, None, None, None, FAKE, 1 << 30,
+            None]
+    for idx, val, code in [(0, None, inv), (6, None, inv), (8, 0.0, inv), (9, -1, inv), (10, 5, inv),
+                           (11, warm, inv), (12, None, inv), (3, 0, inv), (17, None, wsp), (18, 64, wsp)]:
+        args = list(base)
+        args[idx] = val
+        assert lib.sk_sinkhorn_divergence(*args) == code, (idx, val)
+        assert len(lib.sk_last_error()) > 0

@@ -404,3 +404,54 @@ def test_full_size_sampled_rows(sk, key):
     e2 = np.abs(PtU - ref2).max() / np.abs(ref2).max()
     say(f"  sampled rel err grad {e_g:.3e}  P.V {e1:.3e}  P^T.U {e2:.3e} (tol {tol_rel(w):.0e})")
     assert e_g <= tol_rel(w) and e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
+DIV_CASES = [
+    # (config key, n, m, iters)
+    (2, 700, 900, 20),   # float32 d = 3, symmetric cross term
+    (6, 500, 1300, 15),  # float32 d = 3, alternating, merged records
+    (3, 600, 800, 10),   # bf16 d = 64
+    (4, 300, 400, 5),    # float32 d = 512 (GEMM-tiled)
+    (5, 200, 700, 4),    # bf16 d = 1024, rectangular
+]
+
+
+@pytest.mark.parametrize("key,n,m,iters", DIV_CASES)
+def test_divergence_matches_oracle(sk, key, n, m, iters):
+    """Debiased divergence: the device composition is checked exactly against the
+    same solves run through the solve entry point (bitwise repeatable), the
+    gradients in x and y against the oracle fed those potentials, and S and the
+    weight gradients end to end against the oracle's own solves."""
+    w = W.CONFIGS[key].scaled(n, m, iters)
+    say(f"divergence cfg={key} n={n} m={m} iters={iters} {w.dtype} d={w.d}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    S, ga, gb, gx, gy = sk.sinkhorn_divergence(x, y, a, b, w.eps, w.iters, w.mode)
+    f_ab, g_ab, c_ab = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    f_aa, g_aa, c_aa = sk.solve(x, x, a, a, w.eps, w.iters, "symmetric")
+    f_bb, g_bb, c_bb = sk.solve(y, y, b, b, w.eps, w.iters, "symmetric")
+    c = [float(v) for v in (c_ab, c_aa, c_bb)]
+    assert float(S) == c[0] - 0.5 * c[1] - 0.5 * c[2]
+    assert torch.equal(ga, f_ab - f_aa) and torch.equal(gb, g_ab - g_bb)
+    x64, y64 = inp.x64(), inp.y64()
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    cross_x = oracle.grad_x(x64, y64, inp.a, inp.b, t(g_ab), w.eps)
+    self_x = oracle.grad_x(x64, x64, inp.a, inp.a, t(g_aa), w.eps)
+    cross_y = oracle.grad_x(y64, x64, inp.b, inp.a, t(f_ab), w.eps)
+    self_y = oracle.grad_x(y64, y64, inp.b, inp.b, t(g_bb), w.eps)
+    ex = np.abs(t(gx) - (cross_x - self_x)).max() / max(np.abs(cross_x).max(), np.abs(self_x).max())
+    ey = np.abs(t(gy) - (cross_y - self_y)).max() / max(np.abs(cross_y).max(), np.abs(self_y).max())
+    S_ref, ga_ref, gb_ref, _, _ = oracle.divergence(x64, y64, inp.a, inp.b, w.eps, w.iters, w.mode)
+    # S is a difference of costs: its error bound is the cost tolerance times their magnitudes
+    tol_s = tol_rel(w) * (abs(c[0]) + 0.5 * abs(c[1]) + 0.5 * abs(c[2]))
+    es = abs(float(S) - S_ref)
+    ea = np.abs(t(ga) - ga_ref).max()
+    eb = np.abs(t(gb) - gb_ref).max()
+    ta, tb = 2 * tol_pot(w, ga_ref), 2 * tol_pot(w, gb_ref)
+    say(f"  S={float(S):.6e} ref={S_ref:.6e} |dS|={es:.2e} (tol {tol_s:.1e}); grad_a {ea:.2e} (tol {ta:.1e}) "
+        f"grad_b {eb:.2e} (tol {tb:.1e}); grad_x {ex:.2e} grad_y {ey:.2e} (tol {tol_rel(w):.0e})")
+    assert es <= tol_s and ea <= ta and eb <= tb
+    assert ex <= tol_rel(w) and ey <= tol_rel(w)
+    # without gradients only S is written
+    S2, *rest = sk.sinkhorn_divergence(x, y, a, b, w.eps, w.iters, w.mode, grads=False)
+    assert float(S2) == float(S) and all(r is None for r in rest)
