@@ -291,6 +291,36 @@ def measure(case, steps, warmup):
     }
 
 
+def measure_divergence(case, steps, warmup):
+    """Debiased divergence S = OT(a,b) - OT(a,a)/2 - OT(b,b)/2 with the gradients
+    in a, b, x and y: three solves of `iters` iterations and four gradients per
+    evaluation, timed with HIP events on the library's stream."""
+    sk, w, torch = case.sk, case.w, case.torch
+    dt = sk.SK_BF16 if w.dtype == "bf16" else sk.SK_F32
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_DIVERGENCE, dt, w.n, w.m, w.d) + 256, dtype=torch.uint8,
+                     device=case.x.device)
+    for _ in range(warmup):
+        sk.sinkhorn_divergence(case.x, case.y, case.a, case.b, w.eps, w.iters, w.mode, workspace=ws)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        S, *_ = sk.sinkhorn_divergence(case.x, case.y, case.a, case.b, w.eps, w.iters, w.mode, workspace=ws)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = statistics.median(ms)
+    return {"metric": "debiased Sinkhorn divergence evaluations/s (with gradients in a, b, x, y)",
+            "value": 1e3 / med, "unit": "evaluations/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_eval": med, "higher_is_better": True, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+            "data": "synthetic", "divergence": float(S),
+            "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "iters": w.iters,
+                       "mode": w.mode, "evaluation": "3 solves (n x m, n x n, m x m) + 4 gradients"},
+            "solve_iters_per_s": 3 * w.iters / (med * 1e-3)}
+
+
 def cpu_baseline(case, target_s=15.0):
     """The float64 oracle on the host cores, on a bounded sample of the workload:
     the F map on R rows of x and the G map on R rows of y (all columns each),
@@ -343,6 +373,8 @@ def main():
     ap.add_argument("--no-d3", action="store_true", help="skip the d=3 point")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--divergence", action="store_true",
+                    help="time the debiased Sinkhorn divergence with its four gradients instead of the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -373,6 +405,9 @@ def main():
     key = WORKLOADS[args.workload]
     print(f"[bench] workload {args.workload}: building inputs", file=sys.stderr, flush=True)
     case = Case(key, torch, sk, dev)
+    if args.divergence:
+        print(json.dumps(measure_divergence(case, args.steps, args.warmup)), flush=True)
+        return
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     r = measure(case, args.steps, args.warmup)
     w = case.w
