@@ -58,6 +58,7 @@ def _load():
         "sko_grad_x": [P, P, I64, I64, I64, P, P, P, D, P],
         "sko_grad_x_plan": [P, P, I64, I64, I64, P, P, P, P, D, P],
         "sko_apply": [P, P, I64, I64, I64, P, P, P, P, D, INT, P, I64, P],
+        "sko_apply_hadamard": [P, P, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64, P],
         "sko_marginals": [P, P, I64, I64, I64, P, P, P, P, D, P, P],
         "sko_objectives": [P, P, I64, I64, I64, P, P, P, P, D, P, P],
         "sko_set_threads": [INT],
@@ -189,6 +190,27 @@ def apply(x, y, a, b, f, g, eps, V, transpose=False):
     out = np.empty((rows, k))
     _load().sko_apply(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps),
                       int(bool(transpose)), _p(V), k, _p(out))
+    return out[:, 0] if squeeze else out
+
+
+def apply_hadamard(x, y, a, b, f, g, eps, A, B, V, transpose=False):
+    """(P o W) V (V: m x k) or, with transpose, (P o W)^T V (V: n x k), W = A B^T
+    with A (n x r), B (m x r); evaluated entry by entry from the definition."""
+    x, y, n, m, d = _shapes(x, y)
+    a, b, f, g = _c(a), _c(b), _c(f), _c(g)
+    A, B, V = _c(A), _c(B), _c(V)
+    if A.ndim == 1:
+        A = A[:, None]
+    if B.ndim == 1:
+        B = B[:, None]
+    squeeze = V.ndim == 1
+    if squeeze:
+        V = V[:, None]
+    r, k = A.shape[1], V.shape[1]
+    assert A.shape == (n, r) and B.shape == (m, r) and V.shape[0] == (n if transpose else m)
+    out = np.empty((m if transpose else n, k))
+    _load().sko_apply_hadamard(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps),
+                               int(bool(transpose)), _p(A), _p(B), r, _p(V), k, _p(out))
     return out[:, 0] if squeeze else out
 
 

@@ -220,6 +220,43 @@ void sko_apply(const double* x, const double* y, int64_t n, int64_t m, int64_t d
   }
 }
 
+/*
+ * Hadamard-weighted application (the replication review, Summary item ii,
+ * names Hadamard-weighted transport applications; W is not defined on the
+ * pages: here W = A B^T with A (n x r), B (m x r), the form that streams).
+ * Written from the definition, entry by entry: W_ij = sum_s A_is B_js and
+ *   transpose == 0: out (n x k) = (P o W) V,       V (m x k)
+ *   transpose == 1: out (m x k) = (P o W)^T V,     V (n x k)
+ */
+void sko_apply_hadamard(const double* x, const double* y, int64_t n, int64_t m, int64_t d,
+                        const double* a, const double* b, const double* f, const double* g, double eps,
+                        int transpose, const double* A, const double* B, int64_t r, const double* V,
+                        int64_t k, double* out) {
+  if (!transpose) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+      for (int64_t c = 0; c < k; ++c) out[i * k + c] = 0.0;
+      for (int64_t j = 0; j < m; ++j) {
+        double w = 0.0;
+        for (int64_t s2 = 0; s2 < r; ++s2) w += A[i * r + s2] * B[j * r + s2];
+        const double pw = plan_entry(x + i * d, y + j * d, d, a[i], b[j], f[i], g[j], eps) * w;
+        for (int64_t c = 0; c < k; ++c) out[i * k + c] += pw * V[j * k + c];
+      }
+    }
+  } else {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < m; ++j) {
+      for (int64_t c = 0; c < k; ++c) out[j * k + c] = 0.0;
+      for (int64_t i = 0; i < n; ++i) {
+        double w = 0.0;
+        for (int64_t s2 = 0; s2 < r; ++s2) w += A[i * r + s2] * B[j * r + s2];
+        const double pw = plan_entry(x + i * d, y + j * d, d, a[i], b[j], f[i], g[j], eps) * w;
+        for (int64_t c = 0; c < k; ++c) out[j * k + c] += pw * V[i * k + c];
+      }
+    }
+  }
+}
+
 /* Row and column sums of the plan: r = P 1 (n), c = P^T 1 (m). */
 void sko_marginals(const double* x, const double* y, int64_t n, int64_t m, int64_t d,
                    const double* a, const double* b, const double* f, const double* g, double eps,

@@ -377,3 +377,30 @@ def test_divergence_gradients_match_finite_differences():
     db[[0, 5]] = [1.0, -1.0]
     assert (S(x, y, a + h * da, b) - S(x, y, a - h * da, b)) / (2 * h) == pytest.approx(ga @ da, rel=1e-6)
     assert (S(x, y, a, b + h * db) - S(x, y, a, b - h * db)) / (2 * h) == pytest.approx(gb @ db, rel=1e-6)
+
+
+# ---------------------------------------------------------------- Hadamard-weighted transport
+# (P o W) V with W = A B^T (the review's Summary item ii names Hadamard-weighted
+# applications; W is not defined on the pages). Pins against the plain
+# application, which shares no code with it: W = 1 gives P V; a rank-one W =
+# u v^T gives diag(u) P diag(v) V; the result is linear in W (sum of ranks).
+def test_hadamard_apply_special_cases():
+    x, y = _cloud(151, 7, 3), _cloud(152, 9, 3)
+    a, b = _weights(153, 7), _weights(154, 9)
+    rng = np.random.default_rng(155)
+    f, g = rng.standard_normal(7) * 0.1, rng.standard_normal(9) * 0.1
+    eps = 0.3
+    V, U = rng.standard_normal((9, 4)), rng.standard_normal((7, 4))
+    ones_n, ones_m = np.ones((7, 1)), np.ones((9, 1))
+    np.testing.assert_allclose(oracle.apply_hadamard(x, y, a, b, f, g, eps, ones_n, ones_m, V),
+                               oracle.apply(x, y, a, b, f, g, eps, V), rtol=1e-13)
+    u, v = rng.standard_normal(7), rng.standard_normal(9)
+    ref = u[:, None] * oracle.apply(x, y, a, b, f, g, eps, v[:, None] * V)
+    np.testing.assert_allclose(oracle.apply_hadamard(x, y, a, b, f, g, eps, u, v, V), ref, rtol=1e-12, atol=1e-15)
+    reft = v[:, None] * oracle.apply(x, y, a, b, f, g, eps, u[:, None] * U, transpose=True)
+    np.testing.assert_allclose(oracle.apply_hadamard(x, y, a, b, f, g, eps, u, v, U, transpose=True), reft,
+                               rtol=1e-12, atol=1e-15)
+    A, B = rng.standard_normal((7, 3)), rng.standard_normal((9, 3))
+    parts = sum(oracle.apply_hadamard(x, y, a, b, f, g, eps, A[:, s], B[:, s], V) for s in range(3))
+    np.testing.assert_allclose(oracle.apply_hadamard(x, y, a, b, f, g, eps, A, B, V), parts, rtol=1e-12,
+                               atol=1e-15)
