@@ -73,6 +73,7 @@ extern "C" {
 #define SK_OP_APPLY 1
 #define SK_OP_GRAD 2
 #define SK_OP_DIVERGENCE 3
+#define SK_OP_APPLY_HADAMARD 4
 
 /*
  * Fixed-budget Sinkhorn solve (FlashSinkhorn abstract; review, Summary and
@@ -116,6 +117,25 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
 int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                   const float* a, const float* b, const float* g, double eps, float* grad_x,
                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Hadamard-weighted transport application (review, Summary item ii: the
+ * released primitives include Hadamard-weighted transport applications; the
+ * pages do not define the weight matrix, so it is taken in the low-rank form
+ * that streams): W = A B^T with A (n x r) and B (m x r), float32 row-major,
+ *   transpose = 0:  out (n x k) = (P o W) V,     V is m x k
+ *   transpose = 1:  out (m x k) = (P o W)^T V,   V is n x k
+ * where o is the entrywise product and P is formed from (f, g) as in
+ * sk_transport_apply. Evaluated as sum_s diag(A_s) P diag(B_s) V: ranks are
+ * taken in groups of floor(64 / k), one matrix-free application per group.
+ * Requirements: 1 <= k <= 64 (SK_ERR_UNSUPPORTED above), r >= 1, as for
+ * sk_transport_apply otherwise. Workspace: sk_workspace_bytes(SK_OP_APPLY_HADAMARD,
+ * dtype, n, m, d, k) (independent of r).
+ */
+int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                                const float* a, const float* b, const float* f, const float* g, double eps,
+                                int transpose, const float* A, const float* B, int64_t r, const float* V,
+                                int64_t k, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Debiased Sinkhorn divergence (the replication review names a

@@ -10,6 +10,7 @@ the package fails loudly if the shared library is missing.
     f, g, cost = solve(x, y, a, b, eps, iters, mode="alternating")
     out = transport_apply(x, y, a, b, f, g, eps, V)                  # P V
     out = transport_apply(x, y, a, b, f, g, eps, U, transpose=True)  # P^T U
+    out = transport_apply_hadamard(x, y, a, b, f, g, eps, A, B, V)   # (P o A B^T) V
     grad = eot_grad_x(x, y, a, b, g, eps)
     S, ga, gb, gx, gy = sinkhorn_divergence(x, y, a, b, eps, iters)  # debiased
 
@@ -30,7 +31,7 @@ SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0,
 SK_F32, SK_BF16 = 0, 1
 SK_ALTERNATING, SK_SYMMETRIC = 0, 1
 SK_WARM_START, SK_NO_CENTER = 1, 2
-SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE = 0, 1, 2, 3
+SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD = 0, 1, 2, 3, 4
 
 _ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
               SK_ERR_WORKSPACE: "SK_ERR_WORKSPACE", SK_ERR_HIP: "SK_ERR_HIP"}
@@ -62,6 +63,9 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_sinkhorn_divergence.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, P, P,
                                            SZ, P]
     lib.sk_sinkhorn_divergence.restype = INT
+    lib.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64,
+                                                P, P, SZ, P]
+    lib.sk_transport_apply_hadamard.restype = INT
     lib.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.sk_workspace_bytes.restype = SZ
     lib.sk_last_error.argtypes = []
@@ -72,8 +76,8 @@ def _load_library() -> ctypes.CDLL:
 
 
 _lib = _load_library()
-EXPORTS = ("sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x", "sk_sinkhorn_divergence",
-           "sk_workspace_bytes", "sk_last_error", "sk_version")
+EXPORTS = ("sk_sinkhorn_solve", "sk_transport_apply", "sk_transport_apply_hadamard", "sk_eot_grad_x",
+           "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version")
 
 
 def library() -> ctypes.CDLL:
@@ -228,3 +232,33 @@ def sinkhorn_divergence(x, y, a, b, eps: float, iters: int, mode: str = "alterna
                                            int(iters), mode_code, flags, _ptr(S), _ptr(ga), _ptr(gb),
                                            _ptr(gx), _ptr(gy), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return S, ga, gb, gx, gy
+
+
+def transport_apply_hadamard(x, y, a, b, f, g, eps: float, A, B, V, transpose: bool = False, workspace=None):
+    """(P o W) V with W = A B^T (A: n x r, B: m x r; V: m x k), or (P o W)^T V
+    (V: n x k) with transpose=True."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    for t, cnt, name in ((a, n, "a"), (b, m, "b"), (f, n, "f"), (g, m, "g")):
+        _vec(t, cnt, name, dev)
+    A2 = A[:, None] if A.dim() == 1 else A
+    B2 = B[:, None] if B.dim() == 1 else B
+    if (A2.dtype != torch.float32 or B2.dtype != torch.float32 or A2.device != dev or B2.device != dev
+            or A2.dim() != 2 or B2.dim() != 2 or A2.shape[0] != n or B2.shape[0] != m
+            or A2.shape[1] != B2.shape[1]):
+        raise ValueError(f"A and B must be float32 (n, r) and (m, r) on {dev} with the same r")
+    A2, B2 = A2.contiguous(), B2.contiguous()
+    squeeze = V.dim() == 1
+    V2 = V[:, None] if squeeze else V
+    rows_in = n if transpose else m
+    if V2.dtype != torch.float32 or V2.device != dev or V2.dim() != 2 or V2.shape[0] != rows_in:
+        raise ValueError(f"V must be float32 of shape ({rows_in}, k) on {dev}")
+    V2 = V2.contiguous()
+    k, r = V2.shape[1], A2.shape[1]
+    out = torch.empty((m if transpose else n, k), dtype=torch.float32, device=dev)
+    ws, wptr, wbytes = _workspace(SK_OP_APPLY_HADAMARD, dt, n, m, d, k, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_transport_apply_hadamard(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(f), _ptr(g),
+                                                float(eps), int(bool(transpose)), _ptr(A2), _ptr(B2), r, _ptr(V2),
+                                                k, _ptr(out), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return out[:, 0] if squeeze else out

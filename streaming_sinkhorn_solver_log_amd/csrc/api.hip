@@ -529,6 +529,68 @@ DivWs layout_div(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   return L;
 }
 
+// ---------------------------------------------------------------- Hadamard-weighted application
+// (P o W) V with W = A B^T (review, Summary item ii names Hadamard-weighted
+// transport applications; W is not defined on the pages, and the low-rank
+// form is the one that streams):
+//   ((P o W) V)_i = sum_s A_is sum_j P_ij (B_js V_j) = sum_s A_is (P U_s)_i,
+// U_s = diag(B_s) V. Ranks go in groups whose values fit one application
+// (group size x k <= 64 columns).
+
+constexpr int64_t kHadamardCols = 64;
+
+// U[row, q k + c] = Wv[row, s0 + q] * V[row, c] for q < gs
+__global__ void k_hadamard_values(const float* __restrict__ V, const float* __restrict__ Wv, int64_t rows,
+                                  int64_t r, int64_t k, int64_t s0, int64_t gs, float* __restrict__ U) {
+  const int64_t total = rows * gs * k;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / (gs * k), rem = t % (gs * k), q = rem / k, c = rem % k;
+    U[t] = Wv[row * r + s0 + q] * V[row * k + c];
+  }
+}
+
+// out[row, c] (+)= sum_q Wo[row, s0 + q] * Z[row, q k + c]
+__global__ void k_hadamard_combine(const float* __restrict__ Z, const float* __restrict__ Wo, int64_t rows,
+                                   int64_t r, int64_t k, int64_t s0, int64_t gs, int accumulate,
+                                   float* __restrict__ out) {
+  const int64_t total = rows * k;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / k, c = t % k;
+    float acc = accumulate ? out[t] : 0.0f;
+    for (int64_t q = 0; q < gs; ++q) acc = fmaf(Wo[row * r + s0 + q], Z[row * gs * k + q * k + c], acc);
+    out[t] = acc;
+  }
+}
+
+int grid_for(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
+}
+
+struct HadWs {
+  float *U, *Z;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+HadWs layout_hadamard(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  HadWs L{};
+  const int64_t big = n > m ? n : m;
+  L.U = c.take<float>((size_t)big * kHadamardCols);
+  L.Z = c.take<float>((size_t)big * kHadamardCols);
+  size_t need = 0;
+  for (int64_t kk = 1; kk <= kHadamardCols; ++kk) {  // any group width may occur
+    const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0), a1 = apply_bytes(dtype, n, m, d, kk, 1);
+    need = a0 > need ? a0 : need;
+    need = a1 > need ? a1 : need;
+  }
+  L.inner_bytes = need;
+  L.inner = c.take<char>(need);
+  L.bytes = c.off;
+  return L;
+}
+
 extern "C" {
 
 int sk_version(void) { return SK_VERSION; }
@@ -550,6 +612,9 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
     case SK_OP_GRAD:
       if (aux_path(dtype, d) == Path::None) return 0;
       return grad_bytes(dtype, n, m, d);
+    case SK_OP_APPLY_HADAMARD:
+      if (aux_path(dtype, d) == Path::None || k < 1 || k > kHadamardCols) return 0;
+      return layout_hadamard(nullptr, dtype, n, m, d).bytes;
     case SK_OP_DIVERGENCE:
       if (solve_path(dtype, d) == Path::None) return 0;
       return layout_div(nullptr, dtype, n, m, d).bytes;
@@ -676,6 +741,40 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
   ga.nr = (int)n; ga.nc = (int)m; ga.d = (int)d; ga.splits = pl.splits;
   ga.cols_per_split = pl.cols_per_split; ga.c2 = sc.c2;
   if ((e = launch_grad_valu(ga, pl, s)) != hipSuccess) return hip_fail(e, "grad");
+  return SK_OK;
+}
+
+int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                                const float* a, const float* b, const float* f, const float* g, double eps,
+                                int transpose, const float* A, const float* B, int64_t r, const float* V,
+                                int64_t k, float* out, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !A || !B || !V || !out) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
+  if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
+  if (k < 1 || r < 1) return fail(SK_ERR_INVALID_ARG, "k and r must be >= 1");
+  if (k > kHadamardCols) return fail(SK_ERR_UNSUPPORTED, "k=%lld > 64 is not supported", (long long)k);
+  if (!aligned(V, 16)) return fail(SK_ERR_INVALID_ARG, "V must be 16-byte aligned");
+  const HadWs L = layout_hadamard(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // value side: the points V is indexed by; output side: the other one
+  const int64_t vrows = transpose ? n : m, orows = transpose ? m : n;
+  const float* Wv = transpose ? A : B;
+  const float* Wo = transpose ? B : A;
+  const int64_t gmax = kHadamardCols / k;
+  for (int64_t s0 = 0; s0 < r; s0 += gmax) {
+    const int64_t gs = (r - s0) < gmax ? (r - s0) : gmax;
+    k_hadamard_values<<<grid_for(vrows * gs * k), 256, 0, s>>>(V, Wv, vrows, r, k, s0, gs, L.U);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "hadamard values");
+    if ((rc = sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, L.U, gs * k, L.Z, L.inner,
+                                 L.inner_bytes, stream)))
+      return rc;
+    k_hadamard_combine<<<grid_for(orows * k), 256, 0, s>>>(L.Z, Wo, orows, r, k, s0, gs, s0 > 0 ? 1 : 0, out);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hadamard combine");
+  }
   return SK_OK;
 }
 

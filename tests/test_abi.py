@@ -38,6 +38,8 @@ def lib():
     L.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
     L.sk_sinkhorn_divergence.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, P, P,
                                          SZ, P]
+    L.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64, P,
+                                              P, SZ, P]
     L.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     L.sk_workspace_bytes.restype = SZ
     L.sk_last_error.restype = ctypes.c_char_p
@@ -47,7 +49,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x",
-                          "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version"}
+                          "sk_sinkhorn_divergence", "sk_transport_apply_hadamard", "sk_workspace_bytes",
+                          "sk_last_error", "sk_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.sk_version() == _header_int("SK_VERSION")
@@ -66,6 +69,9 @@ def test_workspace_sizes(lib):
             dv = lib.sk_workspace_bytes(_header_int("SK_OP_DIVERGENCE"), 0, n, m, d, 0)
             assert dv > max(s, lib.sk_workspace_bytes(solve, 0, n, n, d, 0),
                             lib.sk_workspace_bytes(solve, 0, m, m, d, 0))
+            had = _header_int("SK_OP_APPLY_HADAMARD")
+            assert lib.sk_workspace_bytes(had, 0, n, m, d, 16) >= lib.sk_workspace_bytes(apply, 0, n, m, d, 16)
+            assert lib.sk_workspace_bytes(had, 0, n, m, d, 65) == 0
     assert lib.sk_workspace_bytes(solve, 0, 0, 5, 3, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 5, 5, 0, 0) == 0
     assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 0) == 0
@@ -136,3 +142,15 @@ def test_divergence_rejects_invalid_arguments(lib):
         args[idx] = val
         assert lib.sk_sinkhorn_divergence(*args) == code, (idx, val)
         assert len(lib.sk_last_error()) > 0
+
+
+def test_hadamard_apply_rejects_invalid_arguments(lib):
+    inv, uns, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_UNSUPPORTED"), _header_int("SK_ERR_WORKSPACE")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, FAKE, FAKE, 0.1, 0, FAKE, FAKE, 2, FAKE, 4, FAKE, FAKE, 1 << 30,
+            None]
+    for idx, val, code in [(12, None, inv), (13, None, inv), (14, 0, inv), (16, 0, inv), (16, 65, uns),
+                           (11, 3, inv), (15, None, inv), (17, None, inv), (10, -1.0, inv), (18, None, wsp),
+                           (19, 8, wsp)]:
+        args = list(base)
+        args[idx] = val
+        assert lib.sk_transport_apply_hadamard(*args) == code, (idx, val)

@@ -455,3 +455,39 @@ def test_divergence_matches_oracle(sk, key, n, m, iters):
     # without gradients only S is written
     S2, *rest = sk.sinkhorn_divergence(x, y, a, b, w.eps, w.iters, w.mode, grads=False)
     assert float(S2) == float(S) and all(r is None for r in rest)
+
+
+HADAMARD_CASES = [
+    # (config key, n, m, r, k)
+    (1, 300, 500, 3, 5),      # one group of ranks
+    (6, 700, 400, 20, 8),     # three groups (8 ranks of width 8 per application), the last partial
+    (3, 500, 900, 4, 16),     # bf16 d = 64
+    (4, 200, 300, 2, 33),     # float32 d = 512 (GEMM-tiled), two value blocks
+    (1, 1, 70, 1, 1),         # a single row
+]
+
+
+@pytest.mark.parametrize("key,n,m,r,k", HADAMARD_CASES)
+def test_hadamard_apply_matches_oracle(sk, key, n, m, r, k):
+    """(P o A B^T) V and its transpose against the oracle's entrywise definition,
+    both sides fed the same float32 potentials; the bound is relative to
+    |P| |W| |V| (signed weights may cancel)."""
+    w = W.CONFIGS[key].scaled(n, m, 8)
+    say(f"hadamard apply cfg={key} n={n} m={m} r={r} k={k}")
+    inp = W.make_inputs(w, k=k)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    rng = np.random.default_rng([key, n, r, k])
+    A = rng.standard_normal((n, r)).astype(np.float32)
+    B = rng.standard_normal((m, r)).astype(np.float32)
+    f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    args = (inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps)
+    At, Bt = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    for transpose, vals in ((False, inp.V), (True, inp.U)):
+        out = sk.transport_apply_hadamard(x, y, a, b, f, g, w.eps, At, Bt, torch.from_numpy(vals).to(DEV),
+                                          transpose=transpose).cpu().numpy()
+        ref = oracle.apply_hadamard(*args, A, B, vals, transpose=transpose)
+        scale = np.abs(oracle.apply_hadamard(*args, np.abs(A), np.abs(B), np.abs(vals), transpose=transpose)).max()
+        err = np.abs(out - ref).max() / scale
+        say(f"  transpose={int(transpose)} rel err {err:.3e} (tol {tol_rel(w):.0e})")
+        assert err <= tol_rel(w)
