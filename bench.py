@@ -321,6 +321,43 @@ def measure_divergence(case, steps, warmup):
             "solve_iters_per_s": 3 * w.iters / (med * 1e-3)}
 
 
+def measure_hadamard(case, r, steps, warmup):
+    """(P o A B^T) V and (P o A B^T)^T U with the workload's potentials (one
+    solve first) and k = 16: ceil(r / 4) matrix-free applications each."""
+    sk, w, torch = case.sk, case.w, case.torch
+    f, g, _ = sk.solve(case.x, case.y, case.a, case.b, w.eps, w.iters, w.mode, workspace=case.ws)
+    gen = torch.Generator(device=case.x.device).manual_seed(7)
+    A = torch.randn(w.n, r, generator=gen, device=case.x.device)
+    B = torch.randn(w.m, r, generator=gen, device=case.x.device)
+    dt = sk.SK_BF16 if w.dtype == "bf16" else sk.SK_F32
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_APPLY_HADAMARD, dt, w.n, w.m, w.d, case.k) + 256,
+                     dtype=torch.uint8, device=case.x.device)
+
+    def run():
+        sk.transport_apply_hadamard(case.x, case.y, case.a, case.b, f, g, w.eps, A, B, case.V, workspace=ws)
+        sk.transport_apply_hadamard(case.x, case.y, case.a, case.b, f, g, w.eps, A, B, case.U, transpose=True,
+                                    workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = statistics.median(ms)
+    return {"metric": "Hadamard-weighted applications/s ((P o W) V and (P o W)^T U, W = A B^T)",
+            "value": 2e3 / med, "unit": "applications/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_pair_of_applications": med, "higher_is_better": True,
+            "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+            "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "rank": r, "k": case.k,
+                       "applications_per_call": -(-r // max(1, 64 // case.k))}}
+
+
 def cpu_baseline(case, target_s=15.0):
     """The float64 oracle on the host cores, on a bounded sample of the workload:
     the F map on R rows of x and the G map on R rows of y (all columns each),
@@ -375,6 +412,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--divergence", action="store_true",
                     help="time the debiased Sinkhorn divergence with its four gradients instead of the step")
+    ap.add_argument("--hadamard", type=int, default=0, metavar="R",
+                    help="time the Hadamard-weighted applications (P o A B^T) V and their transposes, rank R")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -407,6 +446,9 @@ def main():
     case = Case(key, torch, sk, dev)
     if args.divergence:
         print(json.dumps(measure_divergence(case, args.steps, args.warmup)), flush=True)
+        return
+    if args.hadamard:
+        print(json.dumps(measure_hadamard(case, args.hadamard, args.steps, args.warmup)), flush=True)
         return
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     r = measure(case, args.steps, args.warmup)
