@@ -321,6 +321,26 @@ def measure_divergence(case, steps, warmup):
             "solve_iters_per_s": 3 * w.iters / (med * 1e-3)}
 
 
+def measure_tol(case, tol, check_every=10, max_iters=20000):
+    """Iterations and wall time to reach a marginal error of tol (blocking solve
+    with a check every `check_every` iterations)."""
+    sk, w, torch = case.sk, case.w, case.torch
+    dt = sk.SK_BF16 if w.dtype == "bf16" else sk.SK_F32
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_SOLVE_TOL, dt, w.n, w.m, w.d) + 256, dtype=torch.uint8,
+                     device=case.x.device)
+    sk.solve_tol(case.x, case.y, case.a, case.b, w.eps, tol, 20, w.mode, check_every, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, _, cost, done, err = sk.solve_tol(case.x, case.y, case.a, case.b, w.eps, tol, max_iters, w.mode,
+                                         check_every, workspace=ws)
+    sec = time.perf_counter() - t0
+    return {"metric": "iterations to a marginal error of tol", "value": done, "unit": "iterations",
+            "higher_is_better": False, "seconds": sec, "iters_per_s": done / sec, "err": err, "tol": tol,
+            "converged": err <= tol, "cost": float(cost), "check_every": check_every, "max_iters": max_iters,
+            "n_gpus": 1, "data": "synthetic",
+            "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "mode": w.mode}}
+
+
 def measure_hadamard(case, r, steps, warmup):
     """(P o A B^T) V and (P o A B^T)^T U with the workload's potentials (one
     solve first) and k = 16: ceil(r / 4) matrix-free applications each."""
@@ -414,6 +434,9 @@ def main():
                     help="time the debiased Sinkhorn divergence with its four gradients instead of the step")
     ap.add_argument("--hadamard", type=int, default=0, metavar="R",
                     help="time the Hadamard-weighted applications (P o A B^T) V and their transposes, rank R")
+    ap.add_argument("--tol", type=float, default=0.0,
+                    help="solve the workload to this marginal error (checked every 10 iterations, at most "
+                         "20000) and report the iterations and time it took")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -446,6 +469,9 @@ def main():
     case = Case(key, torch, sk, dev)
     if args.divergence:
         print(json.dumps(measure_divergence(case, args.steps, args.warmup)), flush=True)
+        return
+    if args.tol > 0:
+        print(json.dumps(measure_tol(case, args.tol)), flush=True)
         return
     if args.hadamard:
         print(json.dumps(measure_hadamard(case, args.hadamard, args.steps, args.warmup)), flush=True)

@@ -74,6 +74,7 @@ extern "C" {
 #define SK_OP_GRAD 2
 #define SK_OP_DIVERGENCE 3
 #define SK_OP_APPLY_HADAMARD 4
+#define SK_OP_SOLVE_TOL 5
 
 /*
  * Fixed-budget Sinkhorn solve (FlashSinkhorn abstract; review, Summary and
@@ -91,6 +92,33 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
                       const float* a, const float* b, double eps, int32_t iters, int mode,
                       uint32_t flags, float* f, float* g, double* cost, void* ws, size_t ws_bytes,
                       void* stream);
+
+/*
+ * Solve to a marginal tolerance (the review's Weaknesses note that iterations
+ * to convergence grow sharply at small eps, 2000-5000 in its Table 21).
+ * Runs iterations as sk_sinkhorn_solve does, and every `check_every`
+ * iterations measures the marginal error of the current pair (f, g),
+ *   err = ||P 1 - a||_1 + ||P^T 1 - b||_1,
+ * from the iteration that follows it (F(g) normalizes the rows exactly, so the
+ * row sums of P(f, g) are a_i exp((f_i - F(g)_i)/eps); after an alternating
+ * g-step the column sums are b, so in that schedule a check of the starting
+ * pair itself is skipped). It stops after that iteration once err <= tol, or
+ * after max_iters iterations (err is then the last one measured, or +Inf).
+ *   max_iters, check_every   >= 1.
+ *   tol        >= 0, finite. float32 potentials put a floor near
+ *              1e-7 * max|f| / eps under the measurable error.
+ *   iters_done out (host): iterations run.
+ *   err        out (host): the last error measured (of the pair before the
+ *              last iteration; the returned pair is one iteration further).
+ * BLOCKING: synchronizes `stream` at every check. Between checks the solve
+ * restarts from the current pair (SK_WARM_START), so the pairs differ from an
+ * uninterrupted sk_sinkhorn_solve of the same length by rounding only.
+ * Workspace: sk_workspace_bytes(SK_OP_SOLVE_TOL, dtype, n, m, d, 0).
+ */
+int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                          const float* a, const float* b, double eps, int32_t max_iters, int mode,
+                          uint32_t flags, double tol, int32_t check_every, float* f, float* g, double* cost,
+                          int32_t* iters_done, double* err, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Matrix-free transport application (review, Summary item ii: transport-vector

@@ -8,6 +8,7 @@ the library's HIP kernels; there is no Python or CPU fallback, and importing
 the package fails loudly if the shared library is missing.
 
     f, g, cost = solve(x, y, a, b, eps, iters, mode="alternating")
+    f, g, cost, iters_done, err = solve_tol(x, y, a, b, eps, tol, max_iters)   # blocking
     out = transport_apply(x, y, a, b, f, g, eps, V)                  # P V
     out = transport_apply(x, y, a, b, f, g, eps, U, transpose=True)  # P^T U
     out = transport_apply_hadamard(x, y, a, b, f, g, eps, A, B, V)   # (P o A B^T) V
@@ -31,7 +32,7 @@ SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0,
 SK_F32, SK_BF16 = 0, 1
 SK_ALTERNATING, SK_SYMMETRIC = 0, 1
 SK_WARM_START, SK_NO_CENTER = 1, 2
-SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD = 0, 1, 2, 3, 4
+SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD, SK_OP_SOLVE_TOL = 0, 1, 2, 3, 4, 5
 
 _ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
               SK_ERR_WORKSPACE: "SK_ERR_WORKSPACE", SK_ERR_HIP: "SK_ERR_HIP"}
@@ -66,6 +67,9 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64,
                                                 P, P, SZ, P]
     lib.sk_transport_apply_hadamard.restype = INT
+    lib.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, D, I32, P, P, P, P, P,
+                                          P, SZ, P]
+    lib.sk_sinkhorn_solve_tol.restype = INT
     lib.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.sk_workspace_bytes.restype = SZ
     lib.sk_last_error.argtypes = []
@@ -76,7 +80,7 @@ def _load_library() -> ctypes.CDLL:
 
 
 _lib = _load_library()
-EXPORTS = ("sk_sinkhorn_solve", "sk_transport_apply", "sk_transport_apply_hadamard", "sk_eot_grad_x",
+EXPORTS = ("sk_sinkhorn_solve", "sk_sinkhorn_solve_tol", "sk_transport_apply", "sk_transport_apply_hadamard", "sk_eot_grad_x",
            "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version")
 
 
@@ -262,3 +266,35 @@ def transport_apply_hadamard(x, y, a, b, f, g, eps: float, A, B, V, transpose: b
                                                 float(eps), int(bool(transpose)), _ptr(A2), _ptr(B2), r, _ptr(V2),
                                                 k, _ptr(out), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return out[:, 0] if squeeze else out
+
+
+def solve_tol(x, y, a, b, eps: float, tol: float, max_iters: int, mode: str = "alternating",
+              check_every: int = 10, f0=None, g0=None, center: bool = True, workspace=None):
+    """Sinkhorn until the marginal error ||P1 - a||_1 + ||P^T 1 - b||_1 of the
+    pair checked every `check_every` iterations is <= tol (or max_iters).
+    Blocking. Returns (f, g, cost, iters_done, err)."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    _vec(a, n, "a", dev)
+    _vec(b, m, "b", dev)
+    mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
+    flags = 0 if center else SK_NO_CENTER
+    if (f0 is None) != (g0 is None):
+        raise ValueError("give both f0 and g0 for a warm start, or neither")
+    if f0 is not None:
+        f = _vec(f0, n, "f0", dev).clone()
+        g = _vec(g0, m, "g0", dev).clone()
+        flags |= SK_WARM_START
+    else:
+        f = torch.empty(n, dtype=torch.float32, device=dev)
+        g = torch.empty(m, dtype=torch.float32, device=dev)
+    cost = torch.empty((), dtype=torch.float64, device=dev)
+    done = ctypes.c_int32(0)
+    err = ctypes.c_double(0.0)
+    ws, wptr, wbytes = _workspace(SK_OP_SOLVE_TOL, dt, n, m, d, 0, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_sinkhorn_solve_tol(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
+                                          int(max_iters), mode_code, flags, float(tol), int(check_every),
+                                          _ptr(f), _ptr(g), _ptr(cost), ctypes.byref(done), ctypes.byref(err),
+                                          ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return f, g, cost, done.value, err.value

@@ -529,6 +529,55 @@ DivWs layout_div(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   return L;
 }
 
+// ---------------------------------------------------------------- run to tolerance
+// Marginal error of a pair (f0, g0) from the next iteration (review,
+// Weaknesses: iterations to convergence grow sharply at small eps; the
+// survey's next step is a streamed marginal check). F(g0) normalizes the
+// rows exactly, so the row sums of P(f0, g0) are a_i exp((f0_i - F(g0)_i)/eps)
+// and ||P 1 - a||_1 = sum_i a_i |expm1((f0_i - F(g0)_i)/eps)|. The next
+// iteration computes F(g0): f1 itself (alternating) or 2 f1 - f0 (averaged,
+// whose G(f0) = 2 g1 - g0 gives the column term the same way; after an
+// alternating g-step the columns are exact).
+
+// out (+)= sum_i w_i |expm1((p0_i - M_i) inv_eps)|, M = p1 or 2 p1 - p0; one block
+__global__ __launch_bounds__(1024) void k_marginal_error(const float* __restrict__ w, const float* __restrict__ p0,
+                                                         const float* __restrict__ p1, int64_t cnt, double inv_eps,
+                                                         int averaged, int accumulate, double* __restrict__ out) {
+  __shared__ double red[16];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const float m = averaged ? 2.0f * p1[i] - p0[i] : p1[i];
+    acc += (double)w[i] * fabs(expm1((double)(p0[i] - m) * inv_eps));
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int q = 0; q < (int)(blockDim.x >> 6); ++q) t += red[q];
+    out[0] = accumulate ? out[0] + t : t;
+  }
+}
+
+struct TolWs {
+  float *f0, *g0;
+  double* err;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+TolWs layout_tol(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  TolWs L{};
+  L.f0 = c.take<float>(n);
+  L.g0 = c.take<float>(m);
+  L.err = c.take<double>(1);
+  L.inner_bytes = solve_bytes(dtype, n, m, d);
+  L.inner = c.take<char>(L.inner_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
 // ---------------------------------------------------------------- Hadamard-weighted application
 // (P o W) V with W = A B^T (review, Summary item ii names Hadamard-weighted
 // transport applications; W is not defined on the pages, and the low-rank
@@ -612,6 +661,9 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
     case SK_OP_GRAD:
       if (aux_path(dtype, d) == Path::None) return 0;
       return grad_bytes(dtype, n, m, d);
+    case SK_OP_SOLVE_TOL:
+      if (solve_path(dtype, d) == Path::None) return 0;
+      return layout_tol(nullptr, dtype, n, m, d).bytes;
     case SK_OP_APPLY_HADAMARD:
       if (aux_path(dtype, d) == Path::None || k < 1 || k > kHadamardCols) return 0;
       return layout_hadamard(nullptr, dtype, n, m, d).bytes;
@@ -741,6 +793,72 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
   ga.nr = (int)n; ga.nc = (int)m; ga.d = (int)d; ga.splits = pl.splits;
   ga.cols_per_split = pl.cols_per_split; ga.c2 = sc.c2;
   if ((e = launch_grad_valu(ga, pl, s)) != hipSuccess) return hip_fail(e, "grad");
+  return SK_OK;
+}
+
+int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                          const float* a, const float* b, double eps, int32_t max_iters, int mode,
+                          uint32_t flags, double tol, int32_t check_every, float* f, float* g, double* cost,
+                          int32_t* iters_done, double* err, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, solve_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !cost || !iters_done || !err) return fail(SK_ERR_INVALID_ARG, "null output pointer");
+  if (max_iters < 1) return fail(SK_ERR_INVALID_ARG, "max_iters must be >= 1");
+  if (check_every < 1) return fail(SK_ERR_INVALID_ARG, "check_every must be >= 1");
+  if (!(tol >= 0.0) || !isfinite(tol)) return fail(SK_ERR_INVALID_ARG, "tol must be finite and >= 0");
+  if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
+  if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  const TolWs L = layout_tol(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t keep = flags & SK_NO_CENTER;
+  const double inv_eps = 1.0 / eps;
+  int32_t done = 0;
+  double e_host = INFINITY;
+  uint32_t fl = flags;
+  hipError_t e;
+  while (done < max_iters) {
+    // iterations up to the next check, then the checking iteration itself
+    const int32_t left = max_iters - done;
+    const int32_t run = (check_every - 1 < left - 1) ? check_every - 1 : left - 1;
+    if (run > 0) {
+      if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, run, mode, fl, f, g, cost, L.inner,
+                                  L.inner_bytes, stream)))
+        return rc;
+      done += run;
+      fl = keep | SK_WARM_START;
+    }
+    if (done > 0 || (fl & SK_WARM_START)) {
+      if ((e = hipMemcpyAsync(L.f0, f, n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+          (e = hipMemcpyAsync(L.g0, g, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "copy");
+    } else {
+      // cold start: the starting pair is zero
+      if ((e = hipMemsetAsync(L.f0, 0, n * sizeof(float), s)) != hipSuccess ||
+          (e = hipMemsetAsync(L.g0, 0, m * sizeof(float), s)) != hipSuccess)
+        return hip_fail(e, "clear");
+    }
+    // alternating: the columns of the checked pair are exact only if this call's
+    // own g-step produced it, so a check on the starting pair is skipped
+    const bool measurable = mode == SK_SYMMETRIC || done > 0;
+    if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, 1, mode, fl, f, g, cost, L.inner,
+                                L.inner_bytes, stream)))
+      return rc;
+    done += 1;
+    fl = keep | SK_WARM_START;
+    if (!measurable) continue;
+    const int avg = mode == SK_SYMMETRIC ? 1 : 0;
+    k_marginal_error<<<1, 1024, 0, s>>>(a, L.f0, f, n, inv_eps, avg, 0, L.err);
+    if (avg) k_marginal_error<<<1, 1024, 0, s>>>(b, L.g0, g, m, inv_eps, 1, 1, L.err);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "marginal error");
+    if ((e = hipMemcpyAsync(&e_host, L.err, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "marginal error");
+    if (e_host <= tol) break;
+  }
+  *iters_done = done;
+  *err = e_host;
   return SK_OK;
 }
 

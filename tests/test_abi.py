@@ -38,6 +38,8 @@ def lib():
     L.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
     L.sk_sinkhorn_divergence.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, P, P,
                                          SZ, P]
+    L.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, D, I32, P, P, P, P, P, P,
+                                        SZ, P]
     L.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64, P,
                                               P, SZ, P]
     L.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
@@ -49,7 +51,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x",
-                          "sk_sinkhorn_divergence", "sk_transport_apply_hadamard", "sk_workspace_bytes",
+                          "sk_sinkhorn_divergence", "sk_transport_apply_hadamard", "sk_sinkhorn_solve_tol",
+                          "sk_workspace_bytes",
                           "sk_last_error", "sk_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -72,6 +75,7 @@ def test_workspace_sizes(lib):
             had = _header_int("SK_OP_APPLY_HADAMARD")
             assert lib.sk_workspace_bytes(had, 0, n, m, d, 16) >= lib.sk_workspace_bytes(apply, 0, n, m, d, 16)
             assert lib.sk_workspace_bytes(had, 0, n, m, d, 65) == 0
+            assert lib.sk_workspace_bytes(_header_int("SK_OP_SOLVE_TOL"), 0, n, m, d, 0) > s
     assert lib.sk_workspace_bytes(solve, 0, 0, 5, 3, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 5, 5, 0, 0) == 0
     assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 0) == 0
@@ -154,3 +158,15 @@ def test_hadamard_apply_rejects_invalid_arguments(lib):
         args = list(base)
         args[idx] = val
         assert lib.sk_transport_apply_hadamard(*args) == code, (idx, val)
+
+
+def test_solve_tol_rejects_invalid_arguments(lib):
+    inv, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_WORKSPACE")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 100, 0, 0, 1e-4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            1 << 30, None]
+    for idx, val, code in [(9, 0, inv), (13, 0, inv), (12, -1.0, inv), (12, float("nan"), inv), (10, 3, inv),
+                           (11, 0x40, inv), (17, None, inv), (18, None, inv), (14, None, inv), (19, None, wsp),
+                           (20, 32, wsp), (8, 0.0, inv)]:
+        args = list(base)
+        args[idx] = val
+        assert lib.sk_sinkhorn_solve_tol(*args) == code, (idx, val)

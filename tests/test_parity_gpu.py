@@ -491,3 +491,46 @@ def test_hadamard_apply_matches_oracle(sk, key, n, m, r, k):
         err = np.abs(out - ref).max() / scale
         say(f"  transpose={int(transpose)} rel err {err:.3e} (tol {tol_rel(w):.0e})")
         assert err <= tol_rel(w)
+
+
+@pytest.mark.parametrize("mode", ["symmetric", "alternating"])
+def test_solve_tol_error_matches_oracle(sk, mode):
+    """The marginal error the tolerance solve measures equals the oracle's
+    ||P1 - a||_1 + ||P^T 1 - b||_1 at the checked pair (far from convergence)."""
+    w = W.CONFIGS[6].scaled(900, 700, 3)
+    say(f"solve_tol error parity mode={mode}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, 3, mode)
+    if mode == "symmetric":
+        # the check runs on the starting pair itself
+        _, _, _, done, err = sk.solve_tol(x, y, a, b, w.eps, 0.0, 1, mode, check_every=1, f0=f, g0=g)
+        fc, gc = f, g
+    else:
+        # one iteration produces the checked pair (its columns exact), the next measures it
+        _, _, _, done, err = sk.solve_tol(x, y, a, b, w.eps, 0.0, 2, mode, check_every=2, f0=f, g0=g)
+        fc, gc, _ = sk.solve(x, y, a, b, w.eps, 1, mode, f0=f, g0=g)
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    r, c = oracle.marginals(inp.x64(), inp.y64(), inp.a, inp.b, t(fc), t(gc), w.eps)
+    ref = np.abs(r - inp.a).sum() + np.abs(c - inp.b).sum()
+    say(f"  iters {done} err {err:.6e} ref {ref:.6e}")
+    assert done == (1 if mode == "symmetric" else 2)
+    assert err == pytest.approx(ref, rel=1e-3, abs=1e-6)
+
+
+@pytest.mark.parametrize("key,n,m", [(1, 600, 500), (3, 400, 700), (6, 800, 700)])
+def test_solve_tol_reaches_tolerance(sk, key, n, m):
+    w = W.CONFIGS[key].scaled(n, m)
+    say(f"solve_tol convergence cfg={key} n={n} m={m} {w.dtype}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    tol = 1e-4
+    f, g, cost, done, err = sk.solve_tol(x, y, a, b, w.eps, tol, 5000, check_every=10)
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    r, c = oracle.marginals(inp.x64(), inp.y64(), inp.a, inp.b, t(f), t(g), w.eps)
+    ref = np.abs(r - inp.a).sum() + np.abs(c - inp.b).sum()
+    say(f"  iters {done} err {err:.3e}; oracle marginal error of the returned pair {ref:.3e}")
+    assert done < 5000 and done % 10 == 0 and err <= tol and ref <= tol
+    # with tol = 0 it runs to max_iters
+    _, _, _, done0, err0 = sk.solve_tol(x, y, a, b, w.eps, 0.0, 35, check_every=10)
+    assert done0 == 35 and np.isfinite(err0)
