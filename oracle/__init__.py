@@ -214,6 +214,45 @@ def apply_hadamard(x, y, a, b, f, g, eps, A, B, V, transpose=False):
     return out[:, 0] if squeeze else out
 
 
+def hvp_x(x, y, a, b, f, g, eps, V):
+    """Hessian-vector product of OT_eps with respect to x, dense (small n, m).
+
+    Implicit differentiation of the optimality conditions at the pair (f, g)
+    (the review's Summary and Strengths describe the HVP as a Schur solve over
+    streaming plan products, Theorem 5, checked against a dense Moore-Penrose
+    reference; the pages print no formula, so it is derived here). With
+    P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps), row and column sums r, c, and a
+    tangent V (n x d) of x:
+        dC_ij = 2 (x_i - y_j) . v_i
+        u = (P o dC) 1,  w = (P o dC)^T 1
+        [diag(r) P; P^T diag(c)] [df; dg] = [u; w]   (Moore-Penrose solution)
+        dP_ij = P_ij (df_i + dg_j - dC_ij) / eps
+        (H V)_i = 2 r_i v_i - 2 sum_j dP_ij y_j
+    the derivative of the gradient 2 sum_j P_ij (x_i - y_j) with the marginals
+    held fixed (sum_j dP_ij = 0 removes the x_i term). Returns n x d.
+    """
+    x, y = np.asarray(x, dtype=np.float64), np.asarray(y, dtype=np.float64)
+    a, b, f, g = (np.asarray(t, dtype=np.float64) for t in (a, b, f, g))
+    V = np.asarray(V, dtype=np.float64)
+    diff = x[:, None, :] - y[None, :, :]
+    C = (diff * diff).sum(-1)
+    with np.errstate(divide="ignore"):
+        P = np.exp(np.log(a)[:, None] + np.log(b)[None, :] + (f[:, None] + g[None, :] - C) / eps)
+    r, c = P.sum(1), P.sum(0)
+    dC = 2.0 * (diff * V[:, None, :]).sum(-1)
+    u, w = (P * dC).sum(1), (P * dC).sum(0)
+    n, m = P.shape
+    K = np.zeros((n + m, n + m))
+    K[:n, :n] = np.diag(r)
+    K[:n, n:] = P
+    K[n:, :n] = P.T
+    K[n:, n:] = np.diag(c)
+    sol = np.linalg.pinv(K) @ np.concatenate([u, w])
+    df, dg = sol[:n], sol[n:]
+    dP = P * (df[:, None] + dg[None, :] - dC) / eps
+    return 2.0 * r[:, None] * V - 2.0 * dP @ y
+
+
 def marginals(x, y, a, b, f, g, eps):
     """(P 1, P^T 1)."""
     x, y, n, m, d = _shapes(x, y)
