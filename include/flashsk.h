@@ -75,6 +75,7 @@ extern "C" {
 #define SK_OP_DIVERGENCE 3
 #define SK_OP_APPLY_HADAMARD 4
 #define SK_OP_SOLVE_TOL 5
+#define SK_OP_HVP 6
 
 /*
  * Fixed-budget Sinkhorn solve (FlashSinkhorn abstract; review, Summary and
@@ -164,6 +165,30 @@ int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t
                                 const float* a, const float* b, const float* f, const float* g, double eps,
                                 int transpose, const float* A, const float* B, int64_t r, const float* V,
                                 int64_t k, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Hessian-vector product of OT_eps with respect to x (the replication review,
+ * Summary and Strengths: Theorem 5 reduces the HVP to a Schur solve over
+ * streaming plan products, checked against a dense Moore-Penrose reference;
+ * the pages print no formula). At the pair (f, g), for a tangent V (n x d):
+ *   dC_ij = 2 (x_i - y_j).v_i; (df, dg) keep both marginals of P fixed:
+ *   [diag(r) P; P^T diag(c)] [df; dg] = [(P o dC) 1; (P o dC)^T 1],
+ *   r = P 1, c = P^T 1, solved by conjugate gradients on the Schur
+ *   complement diag(c) - P^T diag(1/r) P (relative residual cg_tol, at most
+ *   cg_max_iters iterations); dP_ij = P_ij (df_i + dg_j - dC_ij)/eps;
+ *   out_i = 2 r_i v_i - 2 sum_j dP_ij y_j.
+ * At a converged pair this is the Hessian of OT_eps in x applied to V. All
+ * plan products are matrix-free applications (O((n + m) d) memory).
+ *   V, out     n x d float32 (V 16-byte aligned).
+ *   cg_iters, cg_resid   out (host): CG iterations and final relative residual.
+ * BLOCKING: synchronizes `stream` once per CG iteration.
+ * Requirements: d <= 64 (SK_ERR_UNSUPPORTED above), as for the solve otherwise.
+ * Workspace: sk_workspace_bytes(SK_OP_HVP, dtype, n, m, d, 0).
+ */
+int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                const float* b, const float* f, const float* g, double eps, const float* V, float* out,
+                double cg_tol, int32_t cg_max_iters, int32_t* cg_iters, double* cg_resid, void* ws,
+                size_t ws_bytes, void* stream);
 
 /*
  * Debiased Sinkhorn divergence (the replication review names a

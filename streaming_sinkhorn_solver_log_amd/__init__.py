@@ -13,6 +13,7 @@ the package fails loudly if the shared library is missing.
     out = transport_apply(x, y, a, b, f, g, eps, U, transpose=True)  # P^T U
     out = transport_apply_hadamard(x, y, a, b, f, g, eps, A, B, V)   # (P o A B^T) V
     grad = eot_grad_x(x, y, a, b, g, eps)
+    HV, cg_iters, cg_resid = ot_hvp_x(x, y, a, b, f, g, eps, V)       # blocking
     S, ga, gb, gx, gy = sinkhorn_divergence(x, y, a, b, eps, iters)  # debiased
 
 x, y: (n, d) and (m, d) float32 or bfloat16 CUDA tensors; a, b, f, g, V, U:
@@ -32,7 +33,7 @@ SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0,
 SK_F32, SK_BF16 = 0, 1
 SK_ALTERNATING, SK_SYMMETRIC = 0, 1
 SK_WARM_START, SK_NO_CENTER = 1, 2
-SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD, SK_OP_SOLVE_TOL = 0, 1, 2, 3, 4, 5
+SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD, SK_OP_SOLVE_TOL, SK_OP_HVP = range(7)
 
 _ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
               SK_ERR_WORKSPACE: "SK_ERR_WORKSPACE", SK_ERR_HIP: "SK_ERR_HIP"}
@@ -70,6 +71,8 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, D, I32, P, P, P, P, P,
                                           P, SZ, P]
     lib.sk_sinkhorn_solve_tol.restype = INT
+    lib.sk_ot_hvp_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, P, P, D, I32, P, P, P, SZ, P]
+    lib.sk_ot_hvp_x.restype = INT
     lib.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.sk_workspace_bytes.restype = SZ
     lib.sk_last_error.argtypes = []
@@ -81,7 +84,7 @@ def _load_library() -> ctypes.CDLL:
 
 _lib = _load_library()
 EXPORTS = ("sk_sinkhorn_solve", "sk_sinkhorn_solve_tol", "sk_transport_apply", "sk_transport_apply_hadamard", "sk_eot_grad_x",
-           "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version")
+           "sk_ot_hvp_x", "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version")
 
 
 def library() -> ctypes.CDLL:
@@ -298,3 +301,24 @@ def solve_tol(x, y, a, b, eps: float, tol: float, max_iters: int, mode: str = "a
                                           _ptr(f), _ptr(g), _ptr(cost), ctypes.byref(done), ctypes.byref(err),
                                           ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return f, g, cost, done.value, err.value
+
+
+def ot_hvp_x(x, y, a, b, f, g, eps: float, V, cg_tol: float = 1e-6, cg_max_iters: int = 500, workspace=None):
+    """Hessian of OT_eps in x applied to V (n x d) at the pair (f, g), matrix-free.
+    Blocking. Returns (HV, cg_iters, cg_relative_residual)."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    for t, cnt, name in ((a, n, "a"), (b, m, "b"), (f, n, "f"), (g, m, "g")):
+        _vec(t, cnt, name, dev)
+    if V.dtype != torch.float32 or V.device != dev or tuple(V.shape) != (n, d):
+        raise ValueError(f"V must be float32 of shape ({n}, {d}) on {dev}")
+    V = V.contiguous()
+    out = torch.empty((n, d), dtype=torch.float32, device=dev)
+    iters = ctypes.c_int32(0)
+    resid = ctypes.c_double(0.0)
+    ws, wptr, wbytes = _workspace(SK_OP_HVP, dt, n, m, d, 0, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_ot_hvp_x(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), _ptr(f), _ptr(g), float(eps),
+                                _ptr(V), _ptr(out), float(cg_tol), int(cg_max_iters), ctypes.byref(iters),
+                                ctypes.byref(resid), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return out, iters.value, resid.value

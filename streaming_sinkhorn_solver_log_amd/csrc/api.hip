@@ -578,6 +578,109 @@ TolWs layout_tol(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   return L;
 }
 
+// ---------------------------------------------------------------- Hessian-vector product
+// HVP of OT_eps in x at a pair (f, g) (review, Summary and Strengths:
+// Theorem 5 reduces it to a Schur solve over streaming plan products).
+// Implicit differentiation of the marginal constraints, for a tangent V:
+//   dC_ij = 2 (x_i - y_j).v_i,  s_i = x_i.v_i,  r = P 1,  c = P^T 1
+//   u = (P o dC) 1 = 2 (s o r - rowdot(P Y, V)),  w = (P o dC)^T 1 = 2 (P^T s - rowdot(Y, P^T V))
+//   [diag(r) P; P^T diag(c)] [df; dg] = [u; w]:  S dg = w - P^T (u / r),
+//   S = diag(c) - P^T diag(1/r) P  (conjugate gradients; S 1 = 0 and the
+//   right side is orthogonal to 1, so its mean is removed), df = (u - P dg) / r
+//   (H V)_i = 2 r_i v_i - (2/eps) [(df_i - 2 s_i) (P Y)_i + (P (dg o Y))_i + 2 ((P o V Y^T) Y)_i]
+// Every plan product is a matrix-free application; the last term is the
+// Hadamard-weighted application with W = V Y^T (rank d).
+
+constexpr int kHvpMaxD = 64;
+
+__global__ void k_to_f32(const void* __restrict__ src, int bf16, int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(src)[i] << 16)
+                  : static_cast<const float*>(src)[i];
+}
+
+__global__ void k_fill(float* __restrict__ p, float v, int64_t cnt) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// out_i = A_i . B_i (rows of length d)
+__global__ void k_rowdot(const float* __restrict__ A, const float* __restrict__ B, int64_t rows, int64_t d,
+                         float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += (int64_t)gridDim.x * blockDim.x) {
+    float t = 0.0f;
+    for (int64_t k = 0; k < d; ++k) t = fmaf(A[i * d + k], B[i * d + k], t);
+    out[i] = t;
+  }
+}
+
+// out = 2 (p * q - t), elementwise (u and w of the derivation)
+__global__ void k_two_pq_minus_t(const float* __restrict__ p, const float* __restrict__ q, const float* __restrict__ t,
+                                 int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = 2.0f * ((q ? p[i] * q[i] : p[i]) - t[i]);
+}
+
+// out = p / q, elementwise
+__global__ void k_div(const float* __restrict__ p, const float* __restrict__ q, int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = p[i] / q[i];
+}
+
+// out = c * p - t, elementwise (the Schur product)
+__global__ void k_cp_minus_t(const float* __restrict__ c, const float* __restrict__ p, const float* __restrict__ t,
+                             int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = c[i] * p[i] - t[i];
+}
+
+// out[slot] = sum_i p_i q_i in float64; one block
+__global__ __launch_bounds__(1024) void k_dot(const float* __restrict__ p, const float* __restrict__ q, int64_t cnt,
+                                              double* __restrict__ out) {
+  __shared__ double red[16];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) acc += (double)p[i] * (double)(q ? q[i] : 1.0f);
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += red[k];
+    out[0] = t;
+  }
+}
+
+// p -= mean(p), the mean from a device sum
+__global__ void k_sub_mean(float* __restrict__ p, const double* __restrict__ sum, int64_t cnt) {
+  const float mean = (float)(sum[0] / (double)cnt);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] -= mean;
+}
+
+// y += alpha x; with xpby: y = x + alpha y
+__global__ void k_axpy(float alpha, const float* __restrict__ x, float* __restrict__ y, int64_t cnt, int xpby) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = xpby ? fmaf(alpha, y[i], x[i]) : fmaf(alpha, x[i], y[i]);
+}
+
+// out_jk = s_j * Y_jk
+__global__ void k_scale_rows(const float* __restrict__ sv, const float* __restrict__ Y, int64_t rows, int64_t d,
+                             float* __restrict__ out) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < rows * d; t += (int64_t)gridDim.x * blockDim.x)
+    out[t] = sv[t / d] * Y[t];
+}
+
+__global__ void k_hvp_out(const float* __restrict__ r, const float* __restrict__ V, const float* __restrict__ df,
+                          const float* __restrict__ sv, const float* __restrict__ PY, const float* __restrict__ PDY,
+                          const float* __restrict__ HY, int64_t n, int64_t d, float two_over_eps,
+                          float* __restrict__ out) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n * d; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / d;
+    const float inner = (df[i] - 2.0f * sv[i]) * PY[t] + PDY[t] + 2.0f * HY[t];
+    out[t] = 2.0f * r[i] * V[t] - two_over_eps * inner;
+  }
+}
+
 // ---------------------------------------------------------------- Hadamard-weighted application
 // (P o W) V with W = A B^T (review, Summary item ii names Hadamard-weighted
 // transport applications; W is not defined on the pages, and the low-rank
@@ -640,6 +743,54 @@ HadWs layout_hadamard(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   return L;
 }
 
+struct HvpWs {
+  float *xf, *yf, *ones, *r, *c, *PY, *PtV, *sv, *Pts, *u, *w, *tn, *tm, *tm2, *q, *res, *pp, *Sp, *df, *DY, *PDY,
+      *HY;
+  double* dots;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve cv{static_cast<char*>(ws)};
+  HvpWs L{};
+  const int64_t big = n > m ? n : m;
+  L.xf = cv.take<float>(n * d);
+  L.yf = cv.take<float>(m * d);
+  L.ones = cv.take<float>(big);
+  L.r = cv.take<float>(n);
+  L.c = cv.take<float>(m);
+  L.PY = cv.take<float>(n * d);
+  L.PtV = cv.take<float>(m * d);
+  L.sv = cv.take<float>(n);
+  L.Pts = cv.take<float>(m);
+  L.u = cv.take<float>(n);
+  L.w = cv.take<float>(m);
+  L.tn = cv.take<float>(n);
+  L.tm = cv.take<float>(m);
+  L.tm2 = cv.take<float>(m);
+  L.q = cv.take<float>(m);
+  L.res = cv.take<float>(m);
+  L.pp = cv.take<float>(m);
+  L.Sp = cv.take<float>(m);
+  L.df = cv.take<float>(n);
+  L.DY = cv.take<float>(m * d);
+  L.PDY = cv.take<float>(n * d);
+  L.HY = cv.take<float>(n * d);
+  L.dots = cv.take<double>(4);
+  size_t need = 0;
+  for (int64_t kk = 1; kk <= kHvpMaxD; ++kk) {
+    const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0), a1 = apply_bytes(dtype, n, m, d, kk, 1);
+    need = a0 > need ? a0 : need;
+    need = a1 > need ? a1 : need;
+  }
+  const size_t had = layout_hadamard(nullptr, dtype, n, m, d).bytes;  // the Hadamard application's own layout
+  L.inner_bytes = had > need ? had : need;
+  L.inner = cv.take<char>(L.inner_bytes);
+  L.bytes = cv.off;
+  return L;
+}
+
 extern "C" {
 
 int sk_version(void) { return SK_VERSION; }
@@ -664,6 +815,9 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
     case SK_OP_SOLVE_TOL:
       if (solve_path(dtype, d) == Path::None) return 0;
       return layout_tol(nullptr, dtype, n, m, d).bytes;
+    case SK_OP_HVP:
+      if (aux_path(dtype, d) == Path::None || d > kHvpMaxD) return 0;
+      return layout_hvp(nullptr, dtype, n, m, d).bytes;
     case SK_OP_APPLY_HADAMARD:
       if (aux_path(dtype, d) == Path::None || k < 1 || k > kHadamardCols) return 0;
       return layout_hadamard(nullptr, dtype, n, m, d).bytes;
@@ -893,6 +1047,105 @@ int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t
     k_hadamard_combine<<<grid_for(orows * k), 256, 0, s>>>(L.Z, Wo, orows, r, k, s0, gs, s0 > 0 ? 1 : 0, out);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hadamard combine");
   }
+  return SK_OK;
+}
+
+int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                const float* b, const float* f, const float* g, double eps, const float* V, float* out,
+                double cg_tol, int32_t cg_max_iters, int32_t* cg_iters, double* cg_resid, void* ws,
+                size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !V || !out || !cg_iters || !cg_resid) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
+  if (d > kHvpMaxD) return fail(SK_ERR_UNSUPPORTED, "the HVP supports d <= %d (d=%lld)", kHvpMaxD, (long long)d);
+  if (!(cg_tol > 0.0) || !isfinite(cg_tol)) return fail(SK_ERR_INVALID_ARG, "cg_tol must be finite and > 0");
+  if (cg_max_iters < 1) return fail(SK_ERR_INVALID_ARG, "cg_max_iters must be >= 1");
+  if (!aligned(V, 16)) return fail(SK_ERR_INVALID_ARG, "V must be 16-byte aligned");
+  const HvpWs L = layout_hvp(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  auto apply = [&](const float* vals, int64_t k, int transpose, float* o) {
+    return sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner,
+                              L.inner_bytes, stream);
+  };
+  double host = 0.0;
+  auto dot = [&](const float* p, const float* q, int64_t cnt, double& v) -> int {
+    k_dot<<<1, 1024, 0, s>>>(p, q, cnt, L.dots);
+    if ((e = hipGetLastError()) != hipSuccess ||
+        (e = hipMemcpyAsync(&host, L.dots, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "hvp reduction");
+    v = host;
+    return SK_OK;
+  };
+  const int64_t big = n > m ? n : m;
+  k_to_f32<<<grid_for(n * d), 256, 0, s>>>(x, dtype == SK_BF16, n * d, L.xf);
+  k_to_f32<<<grid_for(m * d), 256, 0, s>>>(y, dtype == SK_BF16, m * d, L.yf);
+  k_fill<<<grid_for(big), 256, 0, s>>>(L.ones, 1.0f, big);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp prep");
+  // marginals of the pair and the plan products the derivation needs
+  if ((rc = apply(L.ones, 1, 0, L.r)) || (rc = apply(L.ones, 1, 1, L.c)) || (rc = apply(L.yf, d, 0, L.PY)) ||
+      (rc = apply(V, d, 1, L.PtV)))
+    return rc;
+  k_rowdot<<<grid_for(n), 256, 0, s>>>(L.xf, V, n, d, L.sv);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  if ((rc = apply(L.sv, 1, 1, L.Pts))) return rc;
+  k_rowdot<<<grid_for(n), 256, 0, s>>>(L.PY, V, n, d, L.tn);
+  k_two_pq_minus_t<<<grid_for(n), 256, 0, s>>>(L.sv, L.r, L.tn, n, L.u);
+  k_rowdot<<<grid_for(m), 256, 0, s>>>(L.yf, L.PtV, m, d, L.tm);
+  k_two_pq_minus_t<<<grid_for(m), 256, 0, s>>>(L.Pts, nullptr, L.tm, m, L.w);
+  k_div<<<grid_for(n), 256, 0, s>>>(L.u, L.r, n, L.tn);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  // right side of the Schur system, w - P^T (u / r), with its mean removed
+  if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
+  if ((e = launch_sub(L.w, L.tm, L.res, m, s)) != hipSuccess) return hip_fail(e, "hvp");
+  k_dot<<<1, 1024, 0, s>>>(L.res, nullptr, m, L.dots);
+  k_sub_mean<<<grid_for(m), 256, 0, s>>>(L.res, L.dots, m);
+  k_fill<<<grid_for(m), 256, 0, s>>>(L.q, 0.0f, m);
+  if ((e = hipGetLastError()) != hipSuccess ||
+      (e = hipMemcpyAsync(L.pp, L.res, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "hvp");
+  // conjugate gradients on S = diag(c) - P^T diag(1/r) P (positive semidefinite)
+  double rr = 0.0;
+  if ((rc = dot(L.res, L.res, m, rr))) return rc;
+  const double zn = sqrt(rr);
+  int32_t it = 0;
+  while (it < cg_max_iters && sqrt(rr) > cg_tol * zn) {
+    if ((rc = apply(L.pp, 1, 0, L.tn))) return rc;
+    k_div<<<grid_for(n), 256, 0, s>>>(L.tn, L.r, n, L.tn);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+    if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
+    k_cp_minus_t<<<grid_for(m), 256, 0, s>>>(L.c, L.pp, L.tm, m, L.Sp);
+    double pSp = 0.0;
+    if ((rc = dot(L.pp, L.Sp, m, pSp))) return rc;
+    if (!(pSp > 0.0)) break;  // no curvature left along the search direction
+    const double alpha = rr / pSp;
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)alpha, L.pp, L.q, m, 0);
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)-alpha, L.Sp, L.res, m, 0);
+    double rn = 0.0;
+    if ((rc = dot(L.res, L.res, m, rn))) return rc;
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)(rn / rr), L.res, L.pp, m, 1);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+    rr = rn;
+    ++it;
+  }
+  *cg_iters = it;
+  *cg_resid = zn > 0.0 ? sqrt(rr) / zn : 0.0;
+  // df = (u - P dg) / r
+  if ((rc = apply(L.q, 1, 0, L.tn))) return rc;
+  if ((e = launch_sub(L.u, L.tn, L.tn, n, s)) != hipSuccess) return hip_fail(e, "hvp");
+  k_div<<<grid_for(n), 256, 0, s>>>(L.tn, L.r, n, L.df);
+  k_scale_rows<<<grid_for(m * d), 256, 0, s>>>(L.q, L.yf, m, d, L.DY);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  if ((rc = apply(L.DY, d, 0, L.PDY))) return rc;
+  // (P o V Y^T) Y: the Hadamard-weighted application of rank d
+  if ((rc = sk_transport_apply_hadamard(x, y, dtype, n, m, d, a, b, f, g, eps, 0, V, L.yf, d, L.yf, d, L.HY,
+                                        L.inner, L.inner_bytes, stream)))
+    return rc;
+  k_hvp_out<<<grid_for(n * d), 256, 0, s>>>(L.r, V, L.df, L.sv, L.PY, L.PDY, L.HY, n, d, (float)(2.0 / eps), out);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
   return SK_OK;
 }
 

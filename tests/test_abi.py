@@ -40,6 +40,7 @@ def lib():
                                          SZ, P]
     L.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, D, I32, P, P, P, P, P, P,
                                         SZ, P]
+    L.sk_ot_hvp_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, P, P, D, I32, P, P, P, SZ, P]
     L.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64, P,
                                               P, SZ, P]
     L.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
@@ -52,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"sk_sinkhorn_solve", "sk_transport_apply", "sk_eot_grad_x",
                           "sk_sinkhorn_divergence", "sk_transport_apply_hadamard", "sk_sinkhorn_solve_tol",
-                          "sk_workspace_bytes",
+                          "sk_ot_hvp_x", "sk_workspace_bytes",
                           "sk_last_error", "sk_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -76,6 +77,8 @@ def test_workspace_sizes(lib):
             assert lib.sk_workspace_bytes(had, 0, n, m, d, 16) >= lib.sk_workspace_bytes(apply, 0, n, m, d, 16)
             assert lib.sk_workspace_bytes(had, 0, n, m, d, 65) == 0
             assert lib.sk_workspace_bytes(_header_int("SK_OP_SOLVE_TOL"), 0, n, m, d, 0) > s
+            assert lib.sk_workspace_bytes(_header_int("SK_OP_HVP"), 0, n, m, d, 0) > 0
+    assert lib.sk_workspace_bytes(_header_int("SK_OP_HVP"), 0, 100, 100, 65, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 0, 5, 3, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 5, 5, 0, 0) == 0
     assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 0) == 0
@@ -170,3 +173,14 @@ def test_solve_tol_rejects_invalid_arguments(lib):
         args = list(base)
         args[idx] = val
         assert lib.sk_sinkhorn_solve_tol(*args) == code, (idx, val)
+
+
+def test_hvp_rejects_invalid_arguments(lib):
+    inv, uns, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_UNSUPPORTED"), _header_int("SK_ERR_WORKSPACE")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 1e-6, 100, FAKE, FAKE, FAKE, 1 << 30,
+            None]
+    for idx, val, code in [(8, None, inv), (11, None, inv), (12, None, inv), (13, 0.0, inv), (14, 0, inv),
+                           (15, None, inv), (5, 65, uns), (11, FAKE + 4, inv), (17, None, wsp), (18, 64, wsp)]:
+        args = list(base)
+        args[idx] = val
+        assert lib.sk_ot_hvp_x(*args) == code, (idx, val)

@@ -534,3 +534,34 @@ def test_solve_tol_reaches_tolerance(sk, key, n, m):
     # with tol = 0 it runs to max_iters
     _, _, _, done0, err0 = sk.solve_tol(x, y, a, b, w.eps, 0.0, 35, check_every=10)
     assert done0 == 35 and np.isfinite(err0)
+
+
+HVP_CASES = [
+    # (config key, n, m, eps override or None)
+    (1, 300, 400, 0.1),      # float32 d = 3
+    (6, 500, 450, 0.05),     # float32 d = 3, mixture
+    (3, 300, 350, None),     # bf16 d = 64
+    (2, 200, 260, 0.02),     # float32 d = 3, smaller eps
+]
+
+
+@pytest.mark.parametrize("key,n,m,eps", HVP_CASES)
+def test_hvp_matches_dense_oracle(sk, key, n, m, eps):
+    """Streaming Hessian-vector product (Schur CG over matrix-free applications)
+    against the oracle's dense Moore-Penrose solve at the same (converged) pair."""
+    from dataclasses import replace
+    w = W.CONFIGS[key].scaled(n, m, 300)
+    if eps is not None:
+        w = replace(w, eps=eps)
+    say(f"hvp cfg={key} n={n} m={m} d={w.d} {w.dtype} eps={w.eps}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, "alternating")
+    V = np.random.default_rng([key, n, 3]).standard_normal((n, w.d)).astype(np.float32)
+    HV, iters, resid = sk.ot_hvp_x(x, y, a, b, f, g, w.eps, torch.from_numpy(V).to(DEV), cg_tol=1e-6)
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    ref = oracle.hvp_x(inp.x64(), inp.y64(), inp.a, inp.b, t(f), t(g), w.eps, V)
+    err = np.abs(t(HV) - ref).max() / np.abs(ref).max()
+    say(f"  CG iterations {iters}, residual {resid:.2e}; rel err {err:.3e}")
+    # CG to 1e-6 over float32 applications (1e-5 each) through the Schur system
+    assert resid <= 1e-6 and err <= (1e-4 if w.dtype == "f32" else 1e-3)
