@@ -321,6 +321,32 @@ def measure_divergence(case, steps, warmup):
             "solve_iters_per_s": 3 * w.iters / (med * 1e-3)}
 
 
+def measure_hvp(case, steps, warmup):
+    """Hessian-vector products of OT_eps in x at the workload's solved pair
+    (CG to a relative residual of 1e-6), timed on the host (the call blocks)."""
+    sk, w, torch = case.sk, case.w, case.torch
+    f, g, _ = sk.solve(case.x, case.y, case.a, case.b, w.eps, w.iters, w.mode, workspace=case.ws)
+    dt = sk.SK_BF16 if w.dtype == "bf16" else sk.SK_F32
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_HVP, dt, w.n, w.m, w.d) + 256, dtype=torch.uint8,
+                     device=case.x.device)
+    gen = torch.Generator(device=case.x.device).manual_seed(11)
+    V = torch.randn(w.n, w.d, generator=gen, device=case.x.device)
+    for _ in range(warmup):
+        sk.ot_hvp_x(case.x, case.y, case.a, case.b, f, g, w.eps, V, workspace=ws)
+    torch.cuda.synchronize()
+    sec, its = [], 0
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        _, its, resid = sk.ot_hvp_x(case.x, case.y, case.a, case.b, f, g, w.eps, V, workspace=ws)
+        torch.cuda.synchronize()
+        sec.append(time.perf_counter() - t0)
+    med = statistics.median(sec)
+    return {"metric": "Hessian-vector products/s of OT_eps in x", "value": 1.0 / med, "unit": "HVP/s",
+            "seconds_per_hvp": med, "cg_iters": its, "cg_residual": resid, "higher_is_better": True,
+            "n_gpus": 1, "data": "synthetic", "steps": steps, "warmup": warmup,
+            "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "cg_tol": 1e-6}}
+
+
 def measure_tol(case, tol, check_every=10, max_iters=20000):
     """Iterations and wall time to reach a marginal error of tol (blocking solve
     with a check every `check_every` iterations)."""
@@ -437,6 +463,8 @@ def main():
     ap.add_argument("--tol", type=float, default=0.0,
                     help="solve the workload to this marginal error (checked every 10 iterations, at most "
                          "20000) and report the iterations and time it took")
+    ap.add_argument("--hvp", action="store_true",
+                    help="time one Hessian-vector product of OT_eps in x at the workload's solved pair")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -469,6 +497,9 @@ def main():
     case = Case(key, torch, sk, dev)
     if args.divergence:
         print(json.dumps(measure_divergence(case, args.steps, args.warmup)), flush=True)
+        return
+    if args.hvp:
+        print(json.dumps(measure_hvp(case, args.steps, args.warmup)), flush=True)
         return
     if args.tol > 0:
         print(json.dumps(measure_tol(case, args.tol)), flush=True)

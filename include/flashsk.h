@@ -173,7 +173,8 @@ int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t
  * the pages print no formula). At the pair (f, g), for a tangent V (n x d):
  *   dC_ij = 2 (x_i - y_j).v_i; (df, dg) keep both marginals of P fixed:
  *   [diag(r) P; P^T diag(c)] [df; dg] = [(P o dC) 1; (P o dC)^T 1],
- *   r = P 1, c = P^T 1, solved by conjugate gradients on the Schur
+ *   r = P 1, c = P^T 1, solved by conjugate gradients (preconditioned by
+ *   diag(c)) on the Schur
  *   complement diag(c) - P^T diag(1/r) P (relative residual cg_tol, at most
  *   cg_max_iters iterations); dP_ij = P_ij (df_i + dg_j - dC_ij)/eps;
  *   out_i = 2 r_i v_i - 2 sum_j dP_ij y_j.

@@ -585,8 +585,9 @@ TolWs layout_tol(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
 //   dC_ij = 2 (x_i - y_j).v_i,  s_i = x_i.v_i,  r = P 1,  c = P^T 1
 //   u = (P o dC) 1 = 2 (s o r - rowdot(P Y, V)),  w = (P o dC)^T 1 = 2 (P^T s - rowdot(Y, P^T V))
 //   [diag(r) P; P^T diag(c)] [df; dg] = [u; w]:  S dg = w - P^T (u / r),
-//   S = diag(c) - P^T diag(1/r) P  (conjugate gradients; S 1 = 0 and the
-//   right side is orthogonal to 1, so its mean is removed), df = (u - P dg) / r
+//   S = diag(c) - P^T diag(1/r) P  (conjugate gradients preconditioned by
+//   diag(c), which maps the spectrum of S into [0, 1]; S 1 = 0 and the right
+//   side is orthogonal to 1, so its mean is removed), df = (u - P dg) / r
 //   (H V)_i = 2 r_i v_i - (2/eps) [(df_i - 2 s_i) (P Y)_i + (P (dg o Y))_i + 2 ((P o V Y^T) Y)_i]
 // Every plan product is a matrix-free application; the last term is the
 // Hadamard-weighted application with W = V Y^T (rank d).
@@ -647,6 +648,36 @@ __global__ __launch_bounds__(1024) void k_dot(const float* __restrict__ p, const
     double t = 0.0;
     for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += red[k];
     out[0] = t;
+  }
+}
+
+// out[0] = p1 . q1, out[1] = p2 . q2 in float64; one block
+__global__ __launch_bounds__(1024) void k_dot2(const float* __restrict__ p1, const float* __restrict__ q1,
+                                               const float* __restrict__ p2, const float* __restrict__ q2,
+                                               int64_t cnt, double* __restrict__ out) {
+  __shared__ double red[2][16];
+  double a1 = 0.0, a2 = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+    a1 += (double)p1[i] * (double)q1[i];
+    a2 += (double)p2[i] * (double)q2[i];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    a1 += __shfl_xor(a1, o);
+    a2 += __shfl_xor(a2, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = a1;
+    red[1][threadIdx.x >> 6] = a2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t1 = 0.0, t2 = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) {
+      t1 += red[0][k];
+      t2 += red[1][k];
+    }
+    out[0] = t1;
+    out[1] = t2;
   }
 }
 
@@ -744,8 +775,8 @@ HadWs layout_hadamard(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
 }
 
 struct HvpWs {
-  float *xf, *yf, *ones, *r, *c, *PY, *PtV, *sv, *Pts, *u, *w, *tn, *tm, *tm2, *q, *res, *pp, *Sp, *df, *DY, *PDY,
-      *HY;
+  float *xf, *yf, *ones, *r, *c, *PY, *PtV, *sv, *Pts, *u, *w, *tn, *tm, *tm2, *q, *res, *pp, *Sp, *zv, *df, *DY,
+      *PDY, *HY;
   double* dots;
   void* inner;
   size_t inner_bytes, bytes;
@@ -773,6 +804,7 @@ HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   L.res = cv.take<float>(m);
   L.pp = cv.take<float>(m);
   L.Sp = cv.take<float>(m);
+  L.zv = cv.take<float>(m);
   L.df = cv.take<float>(n);
   L.DY = cv.take<float>(m * d);
   L.PDY = cv.take<float>(n * d);
@@ -1070,14 +1102,16 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
     return sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner,
                               L.inner_bytes, stream);
   };
-  double host = 0.0;
-  auto dot = [&](const float* p, const float* q, int64_t cnt, double& v) -> int {
-    k_dot<<<1, 1024, 0, s>>>(p, q, cnt, L.dots);
+  double host[2] = {0.0, 0.0};
+  auto dot2 = [&](const float* p1, const float* q1, const float* p2, const float* q2, int64_t cnt, double& v1,
+                  double& v2) -> int {
+    k_dot2<<<1, 1024, 0, s>>>(p1, q1, p2, q2, cnt, L.dots);
     if ((e = hipGetLastError()) != hipSuccess ||
-        (e = hipMemcpyAsync(&host, L.dots, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(host, L.dots, 2 * sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
         (e = hipStreamSynchronize(s)) != hipSuccess)
       return hip_fail(e, "hvp reduction");
-    v = host;
+    v1 = host[0];
+    v2 = host[1];
     return SK_OK;
   };
   const int64_t big = n > m ? n : m;
@@ -1104,12 +1138,13 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
   k_dot<<<1, 1024, 0, s>>>(L.res, nullptr, m, L.dots);
   k_sub_mean<<<grid_for(m), 256, 0, s>>>(L.res, L.dots, m);
   k_fill<<<grid_for(m), 256, 0, s>>>(L.q, 0.0f, m);
+  k_div<<<grid_for(m), 256, 0, s>>>(L.res, L.c, m, L.zv);
   if ((e = hipGetLastError()) != hipSuccess ||
-      (e = hipMemcpyAsync(L.pp, L.res, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      (e = hipMemcpyAsync(L.pp, L.zv, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
     return hip_fail(e, "hvp");
-  // conjugate gradients on S = diag(c) - P^T diag(1/r) P (positive semidefinite)
-  double rr = 0.0;
-  if ((rc = dot(L.res, L.res, m, rr))) return rc;
+  // preconditioned conjugate gradients on S = diag(c) - P^T diag(1/r) P
+  double rr = 0.0, rz = 0.0;
+  if ((rc = dot2(L.res, L.res, L.res, L.zv, m, rr, rz))) return rc;
   const double zn = sqrt(rr);
   int32_t it = 0;
   while (it < cg_max_iters && sqrt(rr) > cg_tol * zn) {
@@ -1118,17 +1153,19 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
     if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
     k_cp_minus_t<<<grid_for(m), 256, 0, s>>>(L.c, L.pp, L.tm, m, L.Sp);
-    double pSp = 0.0;
-    if ((rc = dot(L.pp, L.Sp, m, pSp))) return rc;
+    double pSp = 0.0, unused = 0.0;
+    if ((rc = dot2(L.pp, L.Sp, L.pp, L.Sp, m, pSp, unused))) return rc;
     if (!(pSp > 0.0)) break;  // no curvature left along the search direction
-    const double alpha = rr / pSp;
+    const double alpha = rz / pSp;
     k_axpy<<<grid_for(m), 256, 0, s>>>((float)alpha, L.pp, L.q, m, 0);
     k_axpy<<<grid_for(m), 256, 0, s>>>((float)-alpha, L.Sp, L.res, m, 0);
-    double rn = 0.0;
-    if ((rc = dot(L.res, L.res, m, rn))) return rc;
-    k_axpy<<<grid_for(m), 256, 0, s>>>((float)(rn / rr), L.res, L.pp, m, 1);
+    k_div<<<grid_for(m), 256, 0, s>>>(L.res, L.c, m, L.zv);
+    double rn = 0.0, rzn = 0.0;
+    if ((rc = dot2(L.res, L.res, L.res, L.zv, m, rn, rzn))) return rc;
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)(rzn / rz), L.zv, L.pp, m, 1);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
     rr = rn;
+    rz = rzn;
     ++it;
   }
   *cg_iters = it;
