@@ -1,0 +1,642 @@
+// compose.hip -- operations composed from the core entry points: the debiased
+// Sinkhorn divergence, the Hadamard-weighted transport application, the solve
+// to a marginal tolerance and the Hessian-vector product (declared in
+// include/flashsk.h). Each validates its arguments on the host, lays out the
+// caller's workspace, and calls the core entry points plus a few elementwise
+// and reduction kernels of its own.
+#include <math.h>
+
+#include "flashsk.h"
+#include "sk_api.h"
+
+namespace sk {
+namespace {
+
+using namespace api;
+
+// ---------------------------------------------------------------- divergence
+// Debiased Sinkhorn divergence S = OT(a,b) - OT(a,a)/2 - OT(b,b)/2 and its
+// gradients, composed from the solve and gradient entry points below (the
+// review names a "debiased-Sinkhorn" sweep among the OTDD drivers,
+// Weaknesses, "Downstream drivers absent"; the textbook form is used).
+
+__global__ void k_div_combine(const double* __restrict__ c, double* __restrict__ out) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) out[0] = c[0] - 0.5 * c[1] - 0.5 * c[2];
+}
+
+// out = p - q, elementwise (out may alias p)
+__global__ void k_sub(const float* p, const float* __restrict__ q, float* out, int64_t cnt) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = p[i] - q[i];
+}
+
+hipError_t launch_sub(const float* p, const float* q, float* out, int64_t cnt, hipStream_t s) {
+  const int64_t blocks = (cnt + 255) / 256;
+  k_sub<<<(int)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(p, q, out, cnt);
+  return hipGetLastError();
+}
+
+struct DivWs {
+  float *f_ab, *g_ab, *f_aa, *g_aa, *f_bb, *g_bb, *tmp;
+  double* costs;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+size_t div_inner_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  size_t need = 0;
+  auto take = [&](size_t v) { need = v > need ? v : need; };
+  take(solve_bytes(dtype, n, m, d));
+  take(solve_bytes(dtype, n, n, d));
+  take(solve_bytes(dtype, m, m, d));
+  if (aux_path(dtype, d) != Path::None) {
+    take(grad_bytes(dtype, n, m, d));
+    take(grad_bytes(dtype, n, n, d));
+    take(grad_bytes(dtype, m, n, d));
+    take(grad_bytes(dtype, m, m, d));
+  }
+  return need;
+}
+
+DivWs layout_div(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  DivWs L{};
+  L.f_ab = c.take<float>(n);
+  L.g_ab = c.take<float>(m);
+  L.f_aa = c.take<float>(n);
+  L.g_aa = c.take<float>(n);
+  L.f_bb = c.take<float>(m);
+  L.g_bb = c.take<float>(m);
+  L.tmp = c.take<float>((size_t)(n > m ? n : m) * d);
+  L.costs = c.take<double>(3);
+  L.inner_bytes = div_inner_bytes(dtype, n, m, d);
+  L.inner = c.take<char>(L.inner_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
+// ---------------------------------------------------------------- run to tolerance
+// Marginal error of a pair (f0, g0) from the next iteration (review,
+// Weaknesses: iterations to convergence grow sharply at small eps; the
+// survey's next step is a streamed marginal check). F(g0) normalizes the
+// rows exactly, so the row sums of P(f0, g0) are a_i exp((f0_i - F(g0)_i)/eps)
+// and ||P 1 - a||_1 = sum_i a_i |expm1((f0_i - F(g0)_i)/eps)|. The next
+// iteration computes F(g0): f1 itself (alternating) or 2 f1 - f0 (averaged,
+// whose G(f0) = 2 g1 - g0 gives the column term the same way; after an
+// alternating g-step the columns are exact).
+
+// out (+)= sum_i w_i |expm1((p0_i - M_i) inv_eps)|, M = p1 or 2 p1 - p0; one block
+__global__ __launch_bounds__(1024) void k_marginal_error(const float* __restrict__ w, const float* __restrict__ p0,
+                                                         const float* __restrict__ p1, int64_t cnt, double inv_eps,
+                                                         int averaged, int accumulate, double* __restrict__ out) {
+  __shared__ double red[16];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const float m = averaged ? 2.0f * p1[i] - p0[i] : p1[i];
+    acc += (double)w[i] * fabs(expm1((double)(p0[i] - m) * inv_eps));
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int q = 0; q < (int)(blockDim.x >> 6); ++q) t += red[q];
+    out[0] = accumulate ? out[0] + t : t;
+  }
+}
+
+struct TolWs {
+  float *f0, *g0;
+  double* err;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+TolWs layout_tol(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  TolWs L{};
+  L.f0 = c.take<float>(n);
+  L.g0 = c.take<float>(m);
+  L.err = c.take<double>(1);
+  L.inner_bytes = solve_bytes(dtype, n, m, d);
+  L.inner = c.take<char>(L.inner_bytes);
+  L.bytes = c.off;
+  return L;
+}
+
+// ---------------------------------------------------------------- Hessian-vector product
+// HVP of OT_eps in x at a pair (f, g) (review, Summary and Strengths:
+// Theorem 5 reduces it to a Schur solve over streaming plan products).
+// Implicit differentiation of the marginal constraints, for a tangent V:
+//   dC_ij = 2 (x_i - y_j).v_i,  s_i = x_i.v_i,  r = P 1,  c = P^T 1
+//   u = (P o dC) 1 = 2 (s o r - rowdot(P Y, V)),  w = (P o dC)^T 1 = 2 (P^T s - rowdot(Y, P^T V))
+//   [diag(r) P; P^T diag(c)] [df; dg] = [u; w]:  S dg = w - P^T (u / r),
+//   S = diag(c) - P^T diag(1/r) P  (conjugate gradients preconditioned by
+//   diag(c), which maps the spectrum of S into [0, 1]; S 1 = 0 and the right
+//   side is orthogonal to 1, so its mean is removed), df = (u - P dg) / r
+//   (H V)_i = 2 r_i v_i - (2/eps) [(df_i - 2 s_i) (P Y)_i + (P (dg o Y))_i + 2 ((P o V Y^T) Y)_i]
+// Every plan product is a matrix-free application; the last term is the
+// Hadamard-weighted application with W = V Y^T (rank d).
+
+__global__ void k_to_f32(const void* __restrict__ src, int bf16, int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(src)[i] << 16)
+                  : static_cast<const float*>(src)[i];
+}
+
+__global__ void k_fill(float* __restrict__ p, float v, int64_t cnt) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// out_i = A_i . B_i (rows of length d)
+__global__ void k_rowdot(const float* __restrict__ A, const float* __restrict__ B, int64_t rows, int64_t d,
+                         float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += (int64_t)gridDim.x * blockDim.x) {
+    float t = 0.0f;
+    for (int64_t k = 0; k < d; ++k) t = fmaf(A[i * d + k], B[i * d + k], t);
+    out[i] = t;
+  }
+}
+
+// out = 2 (p * q - t), elementwise (u and w of the derivation)
+__global__ void k_two_pq_minus_t(const float* __restrict__ p, const float* __restrict__ q, const float* __restrict__ t,
+                                 int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = 2.0f * ((q ? p[i] * q[i] : p[i]) - t[i]);
+}
+
+// out = p / q, elementwise
+__global__ void k_div(const float* __restrict__ p, const float* __restrict__ q, int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = p[i] / q[i];
+}
+
+// out = c * p - t, elementwise (the Schur product)
+__global__ void k_cp_minus_t(const float* __restrict__ c, const float* __restrict__ p, const float* __restrict__ t,
+                             int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = c[i] * p[i] - t[i];
+}
+
+// out[slot] = sum_i p_i q_i in float64; one block
+__global__ __launch_bounds__(1024) void k_dot(const float* __restrict__ p, const float* __restrict__ q, int64_t cnt,
+                                              double* __restrict__ out) {
+  __shared__ double red[16];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) acc += (double)p[i] * (double)(q ? q[i] : 1.0f);
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += red[k];
+    out[0] = t;
+  }
+}
+
+// out[0] = p1 . q1, out[1] = p2 . q2 in float64; one block
+__global__ __launch_bounds__(1024) void k_dot2(const float* __restrict__ p1, const float* __restrict__ q1,
+                                               const float* __restrict__ p2, const float* __restrict__ q2,
+                                               int64_t cnt, double* __restrict__ out) {
+  __shared__ double red[2][16];
+  double a1 = 0.0, a2 = 0.0;
+  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) {
+    a1 += (double)p1[i] * (double)q1[i];
+    a2 += (double)p2[i] * (double)q2[i];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    a1 += __shfl_xor(a1, o);
+    a2 += __shfl_xor(a2, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = a1;
+    red[1][threadIdx.x >> 6] = a2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t1 = 0.0, t2 = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) {
+      t1 += red[0][k];
+      t2 += red[1][k];
+    }
+    out[0] = t1;
+    out[1] = t2;
+  }
+}
+
+// p -= mean(p), the mean from a device sum
+__global__ void k_sub_mean(float* __restrict__ p, const double* __restrict__ sum, int64_t cnt) {
+  const float mean = (float)(sum[0] / (double)cnt);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] -= mean;
+}
+
+// y += alpha x; with xpby: y = x + alpha y
+__global__ void k_axpy(float alpha, const float* __restrict__ x, float* __restrict__ y, int64_t cnt, int xpby) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = xpby ? fmaf(alpha, y[i], x[i]) : fmaf(alpha, x[i], y[i]);
+}
+
+// out_jk = s_j * Y_jk
+__global__ void k_scale_rows(const float* __restrict__ sv, const float* __restrict__ Y, int64_t rows, int64_t d,
+                             float* __restrict__ out) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < rows * d; t += (int64_t)gridDim.x * blockDim.x)
+    out[t] = sv[t / d] * Y[t];
+}
+
+__global__ void k_hvp_out(const float* __restrict__ r, const float* __restrict__ V, const float* __restrict__ df,
+                          const float* __restrict__ sv, const float* __restrict__ PY, const float* __restrict__ PDY,
+                          const float* __restrict__ HY, int64_t n, int64_t d, float two_over_eps,
+                          float* __restrict__ out) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n * d; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / d;
+    const float inner = (df[i] - 2.0f * sv[i]) * PY[t] + PDY[t] + 2.0f * HY[t];
+    out[t] = 2.0f * r[i] * V[t] - two_over_eps * inner;
+  }
+}
+
+// ---------------------------------------------------------------- Hadamard-weighted application
+// (P o W) V with W = A B^T (review, Summary item ii names Hadamard-weighted
+// transport applications; W is not defined on the pages, and the low-rank
+// form is the one that streams):
+//   ((P o W) V)_i = sum_s A_is sum_j P_ij (B_js V_j) = sum_s A_is (P U_s)_i,
+// U_s = diag(B_s) V. Ranks go in groups whose values fit one application
+// (group size x k <= 64 columns).
+
+// U[row, q k + c] = Wv[row, s0 + q] * V[row, c] for q < gs
+__global__ void k_hadamard_values(const float* __restrict__ V, const float* __restrict__ Wv, int64_t rows,
+                                  int64_t r, int64_t k, int64_t s0, int64_t gs, float* __restrict__ U) {
+  const int64_t total = rows * gs * k;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / (gs * k), rem = t % (gs * k), q = rem / k, c = rem % k;
+    U[t] = Wv[row * r + s0 + q] * V[row * k + c];
+  }
+}
+
+// out[row, c] (+)= sum_q Wo[row, s0 + q] * Z[row, q k + c]
+__global__ void k_hadamard_combine(const float* __restrict__ Z, const float* __restrict__ Wo, int64_t rows,
+                                   int64_t r, int64_t k, int64_t s0, int64_t gs, int accumulate,
+                                   float* __restrict__ out) {
+  const int64_t total = rows * k;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / k, c = t % k;
+    float acc = accumulate ? out[t] : 0.0f;
+    for (int64_t q = 0; q < gs; ++q) acc = fmaf(Wo[row * r + s0 + q], Z[row * gs * k + q * k + c], acc);
+    out[t] = acc;
+  }
+}
+
+int grid_for(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
+}
+
+struct HadWs {
+  float *U, *Z;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+HadWs layout_hadamard(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  HadWs L{};
+  const int64_t big = n > m ? n : m;
+  L.U = c.take<float>((size_t)big * kHadamardCols);
+  L.Z = c.take<float>((size_t)big * kHadamardCols);
+  size_t need = 0;
+  for (int64_t kk = 1; kk <= kHadamardCols; ++kk) {  // any group width may occur
+    const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0), a1 = apply_bytes(dtype, n, m, d, kk, 1);
+    need = a0 > need ? a0 : need;
+    need = a1 > need ? a1 : need;
+  }
+  L.inner_bytes = need;
+  L.inner = c.take<char>(need);
+  L.bytes = c.off;
+  return L;
+}
+
+struct HvpWs {
+  float *xf, *yf, *ones, *r, *c, *PY, *PtV, *sv, *Pts, *u, *w, *tn, *tm, *tm2, *q, *res, *pp, *Sp, *zv, *df, *DY,
+      *PDY, *HY;
+  double* dots;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
+  Carve cv{static_cast<char*>(ws)};
+  HvpWs L{};
+  const int64_t big = n > m ? n : m;
+  L.xf = cv.take<float>(n * d);
+  L.yf = cv.take<float>(m * d);
+  L.ones = cv.take<float>(big);
+  L.r = cv.take<float>(n);
+  L.c = cv.take<float>(m);
+  L.PY = cv.take<float>(n * d);
+  L.PtV = cv.take<float>(m * d);
+  L.sv = cv.take<float>(n);
+  L.Pts = cv.take<float>(m);
+  L.u = cv.take<float>(n);
+  L.w = cv.take<float>(m);
+  L.tn = cv.take<float>(n);
+  L.tm = cv.take<float>(m);
+  L.tm2 = cv.take<float>(m);
+  L.q = cv.take<float>(m);
+  L.res = cv.take<float>(m);
+  L.pp = cv.take<float>(m);
+  L.Sp = cv.take<float>(m);
+  L.zv = cv.take<float>(m);
+  L.df = cv.take<float>(n);
+  L.DY = cv.take<float>(m * d);
+  L.PDY = cv.take<float>(n * d);
+  L.HY = cv.take<float>(n * d);
+  L.dots = cv.take<double>(4);
+  size_t need = 0;
+  for (int64_t kk = 1; kk <= kHvpMaxD; ++kk) {
+    const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0), a1 = apply_bytes(dtype, n, m, d, kk, 1);
+    need = a0 > need ? a0 : need;
+    need = a1 > need ? a1 : need;
+  }
+  const size_t had = layout_hadamard(nullptr, dtype, n, m, d).bytes;  // the Hadamard application's own layout
+  L.inner_bytes = had > need ? had : need;
+  L.inner = cv.take<char>(L.inner_bytes);
+  L.bytes = cv.off;
+  return L;
+}
+
+}  // namespace
+
+namespace api {
+size_t divergence_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  return layout_div(nullptr, dtype, n, m, d).bytes;
+}
+size_t hadamard_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  return layout_hadamard(nullptr, dtype, n, m, d).bytes;
+}
+size_t solve_tol_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  return layout_tol(nullptr, dtype, n, m, d).bytes;
+}
+size_t hvp_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) { return layout_hvp(nullptr, dtype, n, m, d).bytes; }
+}  // namespace api
+}  // namespace sk
+
+using namespace sk;
+using namespace sk::api;
+
+extern "C" {
+
+int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                          const float* a, const float* b, double eps, int32_t max_iters, int mode,
+                          uint32_t flags, double tol, int32_t check_every, float* f, float* g, double* cost,
+                          int32_t* iters_done, double* err, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, solve_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !cost || !iters_done || !err) return fail(SK_ERR_INVALID_ARG, "null output pointer");
+  if (max_iters < 1) return fail(SK_ERR_INVALID_ARG, "max_iters must be >= 1");
+  if (check_every < 1) return fail(SK_ERR_INVALID_ARG, "check_every must be >= 1");
+  if (!(tol >= 0.0) || !isfinite(tol)) return fail(SK_ERR_INVALID_ARG, "tol must be finite and >= 0");
+  if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
+  if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  const TolWs L = layout_tol(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t keep = flags & SK_NO_CENTER;
+  const double inv_eps = 1.0 / eps;
+  int32_t done = 0;
+  double e_host = INFINITY;
+  uint32_t fl = flags;
+  hipError_t e;
+  while (done < max_iters) {
+    // iterations up to the next check, then the checking iteration itself
+    const int32_t left = max_iters - done;
+    const int32_t run = (check_every - 1 < left - 1) ? check_every - 1 : left - 1;
+    if (run > 0) {
+      if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, run, mode, fl, f, g, cost, L.inner,
+                                  L.inner_bytes, stream)))
+        return rc;
+      done += run;
+      fl = keep | SK_WARM_START;
+    }
+    if (done > 0 || (fl & SK_WARM_START)) {
+      if ((e = hipMemcpyAsync(L.f0, f, n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+          (e = hipMemcpyAsync(L.g0, g, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "copy");
+    } else {
+      // cold start: the starting pair is zero
+      if ((e = hipMemsetAsync(L.f0, 0, n * sizeof(float), s)) != hipSuccess ||
+          (e = hipMemsetAsync(L.g0, 0, m * sizeof(float), s)) != hipSuccess)
+        return hip_fail(e, "clear");
+    }
+    // alternating: the columns of the checked pair are exact only if this call's
+    // own g-step produced it, so a check on the starting pair is skipped
+    const bool measurable = mode == SK_SYMMETRIC || done > 0;
+    if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, 1, mode, fl, f, g, cost, L.inner,
+                                L.inner_bytes, stream)))
+      return rc;
+    done += 1;
+    fl = keep | SK_WARM_START;
+    if (!measurable) continue;
+    const int avg = mode == SK_SYMMETRIC ? 1 : 0;
+    k_marginal_error<<<1, 1024, 0, s>>>(a, L.f0, f, n, inv_eps, avg, 0, L.err);
+    if (avg) k_marginal_error<<<1, 1024, 0, s>>>(b, L.g0, g, m, inv_eps, 1, 1, L.err);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "marginal error");
+    if ((e = hipMemcpyAsync(&e_host, L.err, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "marginal error");
+    if (e_host <= tol) break;
+  }
+  *iters_done = done;
+  *err = e_host;
+  return SK_OK;
+}
+
+int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                                const float* a, const float* b, const float* f, const float* g, double eps,
+                                int transpose, const float* A, const float* B, int64_t r, const float* V,
+                                int64_t k, float* out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !A || !B || !V || !out) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
+  if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
+  if (k < 1 || r < 1) return fail(SK_ERR_INVALID_ARG, "k and r must be >= 1");
+  if (k > kHadamardCols) return fail(SK_ERR_UNSUPPORTED, "k=%lld > 64 is not supported", (long long)k);
+  if (!aligned(V, 16)) return fail(SK_ERR_INVALID_ARG, "V must be 16-byte aligned");
+  const HadWs L = layout_hadamard(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // value side: the points V is indexed by; output side: the other one
+  const int64_t vrows = transpose ? n : m, orows = transpose ? m : n;
+  const float* Wv = transpose ? A : B;
+  const float* Wo = transpose ? B : A;
+  const int64_t gmax = kHadamardCols / k;
+  for (int64_t s0 = 0; s0 < r; s0 += gmax) {
+    const int64_t gs = (r - s0) < gmax ? (r - s0) : gmax;
+    k_hadamard_values<<<grid_for(vrows * gs * k), 256, 0, s>>>(V, Wv, vrows, r, k, s0, gs, L.U);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "hadamard values");
+    if ((rc = sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, L.U, gs * k, L.Z, L.inner,
+                                 L.inner_bytes, stream)))
+      return rc;
+    k_hadamard_combine<<<grid_for(orows * k), 256, 0, s>>>(L.Z, Wo, orows, r, k, s0, gs, s0 > 0 ? 1 : 0, out);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hadamard combine");
+  }
+  return SK_OK;
+}
+
+int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                const float* b, const float* f, const float* g, double eps, const float* V, float* out,
+                double cg_tol, int32_t cg_max_iters, int32_t* cg_iters, double* cg_resid, void* ws,
+                size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !V || !out || !cg_iters || !cg_resid) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
+  if (d > kHvpMaxD) return fail(SK_ERR_UNSUPPORTED, "the HVP supports d <= %d (d=%lld)", kHvpMaxD, (long long)d);
+  if (!(cg_tol > 0.0) || !isfinite(cg_tol)) return fail(SK_ERR_INVALID_ARG, "cg_tol must be finite and > 0");
+  if (cg_max_iters < 1) return fail(SK_ERR_INVALID_ARG, "cg_max_iters must be >= 1");
+  if (!aligned(V, 16)) return fail(SK_ERR_INVALID_ARG, "V must be 16-byte aligned");
+  const HvpWs L = layout_hvp(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  auto apply = [&](const float* vals, int64_t k, int transpose, float* o) {
+    return sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner,
+                              L.inner_bytes, stream);
+  };
+  double host[2] = {0.0, 0.0};
+  auto dot2 = [&](const float* p1, const float* q1, const float* p2, const float* q2, int64_t cnt, double& v1,
+                  double& v2) -> int {
+    k_dot2<<<1, 1024, 0, s>>>(p1, q1, p2, q2, cnt, L.dots);
+    if ((e = hipGetLastError()) != hipSuccess ||
+        (e = hipMemcpyAsync(host, L.dots, 2 * sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "hvp reduction");
+    v1 = host[0];
+    v2 = host[1];
+    return SK_OK;
+  };
+  const int64_t big = n > m ? n : m;
+  k_to_f32<<<grid_for(n * d), 256, 0, s>>>(x, dtype == SK_BF16, n * d, L.xf);
+  k_to_f32<<<grid_for(m * d), 256, 0, s>>>(y, dtype == SK_BF16, m * d, L.yf);
+  k_fill<<<grid_for(big), 256, 0, s>>>(L.ones, 1.0f, big);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp prep");
+  // marginals of the pair and the plan products the derivation needs
+  if ((rc = apply(L.ones, 1, 0, L.r)) || (rc = apply(L.ones, 1, 1, L.c)) || (rc = apply(L.yf, d, 0, L.PY)) ||
+      (rc = apply(V, d, 1, L.PtV)))
+    return rc;
+  k_rowdot<<<grid_for(n), 256, 0, s>>>(L.xf, V, n, d, L.sv);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  if ((rc = apply(L.sv, 1, 1, L.Pts))) return rc;
+  k_rowdot<<<grid_for(n), 256, 0, s>>>(L.PY, V, n, d, L.tn);
+  k_two_pq_minus_t<<<grid_for(n), 256, 0, s>>>(L.sv, L.r, L.tn, n, L.u);
+  k_rowdot<<<grid_for(m), 256, 0, s>>>(L.yf, L.PtV, m, d, L.tm);
+  k_two_pq_minus_t<<<grid_for(m), 256, 0, s>>>(L.Pts, nullptr, L.tm, m, L.w);
+  k_div<<<grid_for(n), 256, 0, s>>>(L.u, L.r, n, L.tn);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  // right side of the Schur system, w - P^T (u / r), with its mean removed
+  if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
+  if ((e = launch_sub(L.w, L.tm, L.res, m, s)) != hipSuccess) return hip_fail(e, "hvp");
+  k_dot<<<1, 1024, 0, s>>>(L.res, nullptr, m, L.dots);
+  k_sub_mean<<<grid_for(m), 256, 0, s>>>(L.res, L.dots, m);
+  k_fill<<<grid_for(m), 256, 0, s>>>(L.q, 0.0f, m);
+  k_div<<<grid_for(m), 256, 0, s>>>(L.res, L.c, m, L.zv);
+  if ((e = hipGetLastError()) != hipSuccess ||
+      (e = hipMemcpyAsync(L.pp, L.zv, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "hvp");
+  // preconditioned conjugate gradients on S = diag(c) - P^T diag(1/r) P
+  double rr = 0.0, rz = 0.0;
+  if ((rc = dot2(L.res, L.res, L.res, L.zv, m, rr, rz))) return rc;
+  const double zn = sqrt(rr);
+  int32_t it = 0;
+  while (it < cg_max_iters && sqrt(rr) > cg_tol * zn) {
+    if ((rc = apply(L.pp, 1, 0, L.tn))) return rc;
+    k_div<<<grid_for(n), 256, 0, s>>>(L.tn, L.r, n, L.tn);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+    if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
+    k_cp_minus_t<<<grid_for(m), 256, 0, s>>>(L.c, L.pp, L.tm, m, L.Sp);
+    double pSp = 0.0, unused = 0.0;
+    if ((rc = dot2(L.pp, L.Sp, L.pp, L.Sp, m, pSp, unused))) return rc;
+    if (!(pSp > 0.0)) break;  // no curvature left along the search direction
+    const double alpha = rz / pSp;
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)alpha, L.pp, L.q, m, 0);
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)-alpha, L.Sp, L.res, m, 0);
+    k_div<<<grid_for(m), 256, 0, s>>>(L.res, L.c, m, L.zv);
+    double rn = 0.0, rzn = 0.0;
+    if ((rc = dot2(L.res, L.res, L.res, L.zv, m, rn, rzn))) return rc;
+    k_axpy<<<grid_for(m), 256, 0, s>>>((float)(rzn / rz), L.zv, L.pp, m, 1);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+    rr = rn;
+    rz = rzn;
+    ++it;
+  }
+  *cg_iters = it;
+  *cg_resid = zn > 0.0 ? sqrt(rr) / zn : 0.0;
+  // df = (u - P dg) / r
+  if ((rc = apply(L.q, 1, 0, L.tn))) return rc;
+  if ((e = launch_sub(L.u, L.tn, L.tn, n, s)) != hipSuccess) return hip_fail(e, "hvp");
+  k_div<<<grid_for(n), 256, 0, s>>>(L.tn, L.r, n, L.df);
+  k_scale_rows<<<grid_for(m * d), 256, 0, s>>>(L.q, L.yf, m, d, L.DY);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  if ((rc = apply(L.DY, d, 0, L.PDY))) return rc;
+  // (P o V Y^T) Y: the Hadamard-weighted application of rank d
+  if ((rc = sk_transport_apply_hadamard(x, y, dtype, n, m, d, a, b, f, g, eps, 0, V, L.yf, d, L.yf, d, L.HY,
+                                        L.inner, L.inner_bytes, stream)))
+    return rc;
+  k_hvp_out<<<grid_for(n * d), 256, 0, s>>>(L.r, V, L.df, L.sv, L.PY, L.PDY, L.HY, n, d, (float)(2.0 / eps), out);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  return SK_OK;
+}
+
+int sk_sinkhorn_divergence(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                           const float* a, const float* b, double eps, int32_t iters, int mode,
+                           uint32_t flags, double* div, float* grad_a, float* grad_b, float* grad_x,
+                           float* grad_y, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, solve_path(dtype, d));
+  if (rc) return rc;
+  if (!div) return fail(SK_ERR_INVALID_ARG, "null output pointer");
+  if (iters < 0) return fail(SK_ERR_INVALID_ARG, "iters must be >= 0");
+  if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
+  if (flags & ~SK_NO_CENTER) return fail(SK_ERR_INVALID_ARG, "flags 0x%x: only SK_NO_CENTER applies", flags);
+  if ((grad_x || grad_y) && aux_path(dtype, d) == Path::None)
+    return fail(SK_ERR_UNSUPPORTED, "gradients at d=%lld are not supported by this build", (long long)d);
+  const DivWs L = layout_div(ws, dtype, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // every sub-call below passes the same validation, so none fails before
+  // enqueuing anything unless the HIP runtime does
+  if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, iters, mode, flags, L.f_ab, L.g_ab,
+                              L.costs, L.inner, L.inner_bytes, stream)))
+    return rc;
+  if ((rc = sk_sinkhorn_solve(x, x, dtype, n, n, d, a, a, eps, iters, SK_SYMMETRIC, flags, L.f_aa, L.g_aa,
+                              L.costs + 1, L.inner, L.inner_bytes, stream)))
+    return rc;
+  if ((rc = sk_sinkhorn_solve(y, y, dtype, m, m, d, b, b, eps, iters, SK_SYMMETRIC, flags, L.f_bb, L.g_bb,
+                              L.costs + 2, L.inner, L.inner_bytes, stream)))
+    return rc;
+  k_div_combine<<<1, 64, 0, s>>>(L.costs, div);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "divergence");
+  if (grad_a && (e = launch_sub(L.f_ab, L.f_aa, grad_a, n, s)) != hipSuccess) return hip_fail(e, "grad_a");
+  if (grad_b && (e = launch_sub(L.g_ab, L.g_bb, grad_b, m, s)) != hipSuccess) return hip_fail(e, "grad_b");
+  if (grad_x) {
+    if ((rc = sk_eot_grad_x(x, y, dtype, n, m, d, a, b, L.g_ab, eps, grad_x, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((rc = sk_eot_grad_x(x, x, dtype, n, n, d, a, a, L.g_aa, eps, L.tmp, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((e = launch_sub(grad_x, L.tmp, grad_x, n * d, s)) != hipSuccess) return hip_fail(e, "grad_x");
+  }
+  if (grad_y) {
+    if ((rc = sk_eot_grad_x(y, x, dtype, m, n, d, b, a, L.f_ab, eps, grad_y, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((rc = sk_eot_grad_x(y, y, dtype, m, m, d, b, b, L.g_bb, eps, L.tmp, L.inner, L.inner_bytes, stream)))
+      return rc;
+    if ((e = launch_sub(grad_y, L.tmp, grad_y, m * d, s)) != hipSuccess) return hip_fail(e, "grad_y");
+  }
+  return SK_OK;
+}
+
+}  // extern "C"

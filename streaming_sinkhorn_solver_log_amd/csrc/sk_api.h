@@ -1,0 +1,60 @@
+// sk_api.h -- helpers shared by the C-ABI entry points (api.hip) and the
+// operations composed from them (compose.hip). Library-internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "flashsk.h"
+
+namespace sk {
+namespace api {
+
+constexpr size_t kAlign = 256;                  // workspace alignment
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // largest n or m
+constexpr int64_t kHadamardCols = 64;           // value columns per application
+constexpr int kHvpMaxD = 64;                    // largest d of the Hessian-vector product
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only sizes.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += round_up(count * sizeof(T) > 0 ? count * sizeof(T) : 1, kAlign);
+    return p;
+  }
+};
+
+enum class Path { Valu, Mfma, Gemm, None };
+
+// Thread-local error message (sk_last_error): fail() formats it and returns code.
+void clear_error();
+const char* last_error();
+int fail(int code, const char* fmt, ...);
+int hip_fail(hipError_t e, const char* where);
+
+Path solve_path(int dtype, int64_t d);
+Path aux_path(int dtype, int64_t d);
+// Host validation common to every entry point (pointers, dtype, sizes, eps, path).
+int check_common(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                 const float* a, const float* b, double eps, Path path);
+int check_ws(void* ws, size_t ws_bytes, size_t need);
+
+// Workspace bytes of the core entry points (api.hip).
+size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose);
+size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+// Workspace bytes of the composed operations (compose.hip).
+size_t divergence_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+size_t hadamard_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+size_t solve_tol_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+size_t hvp_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+
+}  // namespace api
+}  // namespace sk
