@@ -347,7 +347,7 @@ def measure_hvp(case, steps, warmup):
             "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "cg_tol": 1e-6}}
 
 
-def measure_tol(case, tol, check_every=10, max_iters=20000):
+def measure_tol(case, tol, check_every=10, max_iters=20000, eps_start=0.0):
     """Iterations and wall time to reach a marginal error of tol (blocking solve
     with a check every `check_every` iterations)."""
     sk, w, torch = case.sk, case.w, case.torch
@@ -358,11 +358,12 @@ def measure_tol(case, tol, check_every=10, max_iters=20000):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     _, _, cost, done, err = sk.solve_tol(case.x, case.y, case.a, case.b, w.eps, tol, max_iters, w.mode,
-                                         check_every, workspace=ws)
+                                         check_every, eps_start=eps_start, workspace=ws)
     sec = time.perf_counter() - t0
     return {"metric": "iterations to a marginal error of tol", "value": done, "unit": "iterations",
             "higher_is_better": False, "seconds": sec, "iters_per_s": done / sec, "err": err, "tol": tol,
             "converged": err <= tol, "cost": float(cost), "check_every": check_every, "max_iters": max_iters,
+            "eps_start": eps_start,
             "n_gpus": 1, "data": "synthetic",
             "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "mode": w.mode}}
 
@@ -463,6 +464,8 @@ def main():
     ap.add_argument("--tol", type=float, default=0.0,
                     help="solve the workload to this marginal error (checked every 10 iterations, at most "
                          "20000) and report the iterations and time it took")
+    ap.add_argument("--eps-start", type=float, default=0.0,
+                    help="with --tol: eps-scaling from this eps (one iteration per halving)")
     ap.add_argument("--hvp", action="store_true",
                     help="time one Hessian-vector product of OT_eps in x at the workload's solved pair")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -502,7 +505,7 @@ def main():
         print(json.dumps(measure_hvp(case, args.steps, args.warmup)), flush=True)
         return
     if args.tol > 0:
-        print(json.dumps(measure_tol(case, args.tol)), flush=True)
+        print(json.dumps(measure_tol(case, args.tol, eps_start=args.eps_start)), flush=True)
         return
     if args.hadamard:
         print(json.dumps(measure_hadamard(case, args.hadamard, args.steps, args.warmup)), flush=True)

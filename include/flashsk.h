@@ -105,6 +105,9 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
  * g-step the column sums are b, so in that schedule a check of the starting
  * pair itself is skipped). It stops after that iteration once err <= tol, or
  * after max_iters iterations (err is then the last one measured, or +Inf).
+ *   eps_start  eps-scaling: when eps_start > eps, one iteration at each of
+ *              eps_start, eps_start/2, ... while above eps runs first (these
+ *              count in iters_done); 0 (or <= eps) disables it.
  *   max_iters, check_every   >= 1.
  *   tol        >= 0, finite. float32 potentials put a floor near
  *              1e-7 * max|f| / eps under the measurable error.
@@ -117,9 +120,10 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
  * Workspace: sk_workspace_bytes(SK_OP_SOLVE_TOL, dtype, n, m, d, 0).
  */
 int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
-                          const float* a, const float* b, double eps, int32_t max_iters, int mode,
-                          uint32_t flags, double tol, int32_t check_every, float* f, float* g, double* cost,
-                          int32_t* iters_done, double* err, void* ws, size_t ws_bytes, void* stream);
+                          const float* a, const float* b, double eps, double eps_start, int32_t max_iters,
+                          int mode, uint32_t flags, double tol, int32_t check_every, float* f, float* g,
+                          double* cost, int32_t* iters_done, double* err, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Matrix-free transport application (review, Summary item ii: transport-vector

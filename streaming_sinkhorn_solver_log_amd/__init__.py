@@ -68,8 +68,8 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64,
                                                 P, P, SZ, P]
     lib.sk_transport_apply_hadamard.restype = INT
-    lib.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, D, I32, P, P, P, P, P,
-                                          P, SZ, P]
+    lib.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, D, I32, INT, U32, D, I32, P, P, P, P,
+                                          P, P, SZ, P]
     lib.sk_sinkhorn_solve_tol.restype = INT
     lib.sk_ot_hvp_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, P, P, D, I32, P, P, P, SZ, P]
     lib.sk_ot_hvp_x.restype = INT
@@ -272,9 +272,11 @@ def transport_apply_hadamard(x, y, a, b, f, g, eps: float, A, B, V, transpose: b
 
 
 def solve_tol(x, y, a, b, eps: float, tol: float, max_iters: int, mode: str = "alternating",
-              check_every: int = 10, f0=None, g0=None, center: bool = True, workspace=None):
+              check_every: int = 10, f0=None, g0=None, center: bool = True, eps_start: float = 0.0,
+              workspace=None):
     """Sinkhorn until the marginal error ||P1 - a||_1 + ||P^T 1 - b||_1 of the
-    pair checked every `check_every` iterations is <= tol (or max_iters).
+    pair checked every `check_every` iterations is <= tol (or max_iters), after
+    an optional eps-scaling from eps_start (one iteration per halving).
     Blocking. Returns (f, g, cost, iters_done, err)."""
     n, m, d, dt = _points(x, y)
     dev = x.device
@@ -297,7 +299,8 @@ def solve_tol(x, y, a, b, eps: float, tol: float, max_iters: int, mode: str = "a
     ws, wptr, wbytes = _workspace(SK_OP_SOLVE_TOL, dt, n, m, d, 0, dev, workspace)
     with torch.cuda.device(dev):
         _check(_lib.sk_sinkhorn_solve_tol(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
-                                          int(max_iters), mode_code, flags, float(tol), int(check_every),
+                                          float(eps_start), int(max_iters), mode_code, flags, float(tol),
+                                          int(check_every),
                                           _ptr(f), _ptr(g), _ptr(cost), ctypes.byref(done), ctypes.byref(err),
                                           ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return f, g, cost, done.value, err.value

@@ -387,9 +387,10 @@ using namespace sk::api;
 extern "C" {
 
 int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
-                          const float* a, const float* b, double eps, int32_t max_iters, int mode,
-                          uint32_t flags, double tol, int32_t check_every, float* f, float* g, double* cost,
-                          int32_t* iters_done, double* err, void* ws, size_t ws_bytes, void* stream) {
+                          const float* a, const float* b, double eps, double eps_start, int32_t max_iters,
+                          int mode, uint32_t flags, double tol, int32_t check_every, float* f, float* g,
+                          double* cost, int32_t* iters_done, double* err, void* ws, size_t ws_bytes,
+                          void* stream) {
   clear_error();
   int rc = check_common(x, y, dtype, n, m, d, a, b, eps, solve_path(dtype, d));
   if (rc) return rc;
@@ -397,6 +398,7 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
   if (max_iters < 1) return fail(SK_ERR_INVALID_ARG, "max_iters must be >= 1");
   if (check_every < 1) return fail(SK_ERR_INVALID_ARG, "check_every must be >= 1");
   if (!(tol >= 0.0) || !isfinite(tol)) return fail(SK_ERR_INVALID_ARG, "tol must be finite and >= 0");
+  if (!(eps_start >= 0.0) || !isfinite(eps_start)) return fail(SK_ERR_INVALID_ARG, "eps_start must be finite and >= 0");
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
   if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   const TolWs L = layout_tol(ws, dtype, n, m, d);
@@ -408,6 +410,15 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
   double e_host = INFINITY;
   uint32_t fl = flags;
   hipError_t e;
+  // eps-scaling: one iteration at each of eps_start, eps_start / 2, ... above eps
+  for (double ek = eps_start; ek > eps && done < max_iters; ek *= 0.5) {
+    if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, ek, 1, mode, fl, f, g, cost, L.inner, L.inner_bytes,
+                                stream)))
+      return rc;
+    ++done;
+    fl = keep | SK_WARM_START;
+  }
+  int32_t done_at_eps = 0;
   while (done < max_iters) {
     // iterations up to the next check, then the checking iteration itself
     const int32_t left = max_iters - done;
@@ -417,6 +428,7 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
                                   L.inner_bytes, stream)))
         return rc;
       done += run;
+      done_at_eps += run;
       fl = keep | SK_WARM_START;
     }
     if (done > 0 || (fl & SK_WARM_START)) {
@@ -430,12 +442,14 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
         return hip_fail(e, "clear");
     }
     // alternating: the columns of the checked pair are exact only if this call's
-    // own g-step produced it, so a check on the starting pair is skipped
-    const bool measurable = mode == SK_SYMMETRIC || done > 0;
+    // own g-step at eps produced it, so a check on the starting pair (or the
+    // last pair of the eps-scaling) is skipped
+    const bool measurable = mode == SK_SYMMETRIC || done_at_eps > 0;
     if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, 1, mode, fl, f, g, cost, L.inner,
                                 L.inner_bytes, stream)))
       return rc;
     done += 1;
+    done_at_eps += 1;
     fl = keep | SK_WARM_START;
     if (!measurable) continue;
     const int avg = mode == SK_SYMMETRIC ? 1 : 0;

@@ -38,8 +38,8 @@ def lib():
     L.sk_eot_grad_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, D, P, P, SZ, P]
     L.sk_sinkhorn_divergence.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P, P, P,
                                          SZ, P]
-    L.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, D, I32, P, P, P, P, P, P,
-                                        SZ, P]
+    L.sk_sinkhorn_solve_tol.argtypes = [P, P, INT, I64, I64, I64, P, P, D, D, I32, INT, U32, D, I32, P, P, P, P, P,
+                                        P, SZ, P]
     L.sk_ot_hvp_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, P, P, D, I32, P, P, P, SZ, P]
     L.sk_transport_apply_hadamard.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, INT, P, P, I64, P, I64, P,
                                               P, SZ, P]
@@ -165,11 +165,11 @@ def test_hadamard_apply_rejects_invalid_arguments(lib):
 
 def test_solve_tol_rejects_invalid_arguments(lib):
     inv, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_WORKSPACE")
-    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 100, 0, 0, 1e-4, 10, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-            1 << 30, None]
-    for idx, val, code in [(9, 0, inv), (13, 0, inv), (12, -1.0, inv), (12, float("nan"), inv), (10, 3, inv),
-                           (11, 0x40, inv), (17, None, inv), (18, None, inv), (14, None, inv), (19, None, wsp),
-                           (20, 32, wsp), (8, 0.0, inv)]:
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 0.0, 100, 0, 0, 1e-4, 10, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, 1 << 30, None]
+    for idx, val, code in [(10, 0, inv), (14, 0, inv), (13, -1.0, inv), (13, float("nan"), inv), (11, 3, inv),
+                           (12, 0x40, inv), (18, None, inv), (19, None, inv), (15, None, inv), (20, None, wsp),
+                           (21, 32, wsp), (8, 0.0, inv), (9, -1.0, inv), (9, float("inf"), inv)]:
         args = list(base)
         args[idx] = val
         assert lib.sk_sinkhorn_solve_tol(*args) == code, (idx, val)

@@ -565,3 +565,19 @@ def test_hvp_matches_dense_oracle(sk, key, n, m, eps):
     say(f"  CG iterations {iters}, residual {resid:.2e}; rel err {err:.3e}")
     # CG to 1e-6 over float32 applications (1e-5 each) through the Schur system
     assert resid <= 1e-6 and err <= (1e-4 if w.dtype == "f32" else 1e-3)
+
+
+def test_solve_tol_with_eps_scaling(sk):
+    """eps-scaling (one iteration per halving from eps_start) then the tolerance
+    phase at eps: the returned pair meets the tolerance by the oracle's marginals."""
+    w = W.CONFIGS[6].scaled(900, 800)
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    tol = 1e-4
+    _, _, _, plain, _ = sk.solve_tol(x, y, a, b, w.eps, tol, 5000, check_every=10)
+    f, g, _, done, err = sk.solve_tol(x, y, a, b, w.eps, tol, 5000, check_every=10, eps_start=2.0)
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    r, c = oracle.marginals(inp.x64(), inp.y64(), inp.a, inp.b, t(f), t(g), w.eps)
+    ref = np.abs(r - inp.a).sum() + np.abs(c - inp.b).sum()
+    say(f"eps-scaling from 2.0 to {w.eps}: {done} iterations (without: {plain}); err {err:.2e}, oracle {ref:.2e}")
+    assert done < 5000 and err <= tol and ref <= tol
