@@ -581,3 +581,29 @@ def test_solve_tol_with_eps_scaling(sk):
     ref = np.abs(r - inp.a).sum() + np.abs(c - inp.b).sum()
     say(f"eps-scaling from 2.0 to {w.eps}: {done} iterations (without: {plain}); err {err:.2e}, oracle {ref:.2e}")
     assert done < 5000 and err <= tol and ref <= tol
+
+
+@pytest.mark.parametrize("key", [3, 2])
+def test_hvp_and_hadamard_properties_at_full_size(sk, key):
+    """At full size (no dense oracle): the Hessian is symmetric, <U, H V> =
+    <V, H U>, and the Hadamard-weighted application with W = 1 1^T is the plain
+    application bit for bit."""
+    w = W.CONFIGS[key]
+    say(f"full-size HVP symmetry / Hadamard identity cfg={key} n={w.n} m={w.m} d={w.d}")
+    inp = W.make_inputs(w, k=16)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, "alternating")
+    gen = torch.Generator(device=DEV).manual_seed(key)
+    U = torch.randn(w.n, w.d, generator=gen, device=DEV)
+    V = torch.randn(w.n, w.d, generator=gen, device=DEV)
+    HV, iv, rv = sk.ot_hvp_x(x, y, a, b, f, g, w.eps, V)
+    HU, iu, ru = sk.ot_hvp_x(x, y, a, b, f, g, w.eps, U)
+    l, r = float((U.double() * HV.double()).sum()), float((V.double() * HU.double()).sum())
+    scale = float(U.double().norm() * HV.double().norm())
+    say(f"  CG {iv}/{iu} iterations (residuals {rv:.1e}, {ru:.1e}); <U,HV>={l:.6e} <V,HU>={r:.6e}")
+    assert abs(l - r) <= 1e-4 * scale
+    Vv = torch.from_numpy(inp.V).to(DEV)
+    ones_n, ones_m = torch.ones(w.n, 1, device=DEV), torch.ones(w.m, 1, device=DEV)
+    plain = sk.transport_apply(x, y, a, b, f, g, w.eps, Vv)
+    had = sk.transport_apply_hadamard(x, y, a, b, f, g, w.eps, ones_n, ones_m, Vv)
+    assert torch.equal(plain, had)
