@@ -207,12 +207,31 @@ def alu_slots_per_pair(w):
     return 3 + (1 if w.dtype == "bf16" else 0)
 
 
+# Measured rate of a register-only loop with the half-pass's own instruction
+# mix (bench.py --peaks, stored in profiles/unit_peaks.json): the practical
+# ceiling of the register-resident half-pass on this chip.
+UNIT_PEAKS_FILE = os.path.join(ROOT, "profiles", "unit_peaks.json")
+MIX_PROBE = {("f32", 3): "mix_f32_points_d3", ("bf16", 64): "mix_bf16_points_d64"}
+
+
+def measured_mix_rate(w):
+    name = MIX_PROBE.get((w.dtype, w.d))
+    if name is None or not os.path.exists(UNIT_PEAKS_FILE):
+        return None, None
+    with open(UNIT_PEAKS_FILE) as fh:
+        return name, json.load(fh)["peaks"][name]["rate"]
+
+
 def _pass_roofline(w, pass_ms):
     pairs = w.n * w.m
     sec = pass_ms * 1e-3
     rate = pairs / sec
     alu_peak = VALU_PEAK / alu_slots_per_pair(w)  # pairs/s when the VALU issue binds
     also = {"exp_frac": rate / EXP_PEAK}
+    probe, mix_rate = measured_mix_rate(w)
+    if mix_rate:
+        also["measured_mix_probe"] = probe
+        also["measured_mix_frac"] = rate / mix_rate
     if w.d >= 32:
         peak = BF16_MFMA_PEAK if w.dtype == "bf16" else F32_MFMA_PEAK
         mfma_flops = 2.0 * w.d * pairs
@@ -448,6 +467,50 @@ def cpu_baseline(case, target_s=15.0):
                       f"{tf + tg:.1f} s measured"}
 
 
+# Unit-rate microbenchmarks (streaming_sinkhorn_solver_log_amd/peaks/peaks.hip):
+# (index, name, unit of the work count, model peak per second or None, model)
+PEAK_CASES = [
+    (0, "exp2", "exp/s", EXP_PEAK, "v_exp_f32 at 2 issue slots"),
+    (1, "fma_f32", "op/s", VALU_PEAK, "non-packed fp32 VALU, 1 slot"),
+    (2, "add_f32", "op/s", VALU_PEAK, "non-packed fp32 VALU, 1 slot"),
+    (3, "exp2_add", "score/s", VALU_PEAK / 3, "exp2 (2 slots) + add (1 slot) per score"),
+    (4, "mfma_bf16_32x32x16", "flop/s", BF16_MFMA_PEAK, "published dense bf16"),
+    (5, "mfma_f32_32x32x2", "flop/s", F32_MFMA_PEAK, "published fp32 matrix"),
+    (6, "mix_f32_points_d3", "score/s", VALU_PEAK / 3,
+     "2 bf16 MFMAs per 1024 scores + exp2 + add: VALU roof if the MFMAs hide fully"),
+    (7, "hbm_read", "B/s", HBM_PEAK, "published HBM3E"),
+    (8, "l2_read", "B/s", None, "1 MiB read by every workgroup"),
+    (9, "mall_read", "B/s", None, "64 MiB streamed 32 times"),
+    (10, "mix_bf16_points_d64", "score/s", VALU_PEAK / 4,
+     "4 bf16 MFMAs per 1024 scores + mul + exp2 + add: VALU roof if the MFMAs hide fully"),
+]
+
+
+def measure_peaks():
+    import ctypes
+
+    from streaming_sinkhorn_solver_log_amd.build import PEAKS_LIB
+    if not os.path.exists(PEAKS_LIB):
+        raise RuntimeError(f"{PEAKS_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.skp_measure.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_int)]
+    lib.skp_measure.restype = ctypes.c_int
+    res = {}
+    cus = ctypes.c_int(0)
+    for which, name, unit, peak, model in PEAK_CASES:
+        work, ms = ctypes.c_double(0), ctypes.c_double(0)
+        rc = lib.skp_measure(which, ctypes.byref(work), ctypes.byref(ms), ctypes.byref(cus))
+        if rc != 0:
+            raise RuntimeError(f"peaks benchmark {name} failed with HIP error {-rc}")
+        rate = work.value / (ms.value * 1e-3)
+        res[name] = {"rate": rate, "unit": unit, "ms": ms.value, "model_peak": peak,
+                     "frac": rate / peak if peak else None, "model": model,
+                     "per_cu_per_clk": rate / (CU * CLK)}
+        print(f"[peaks] {name}: {rate:.4g} {unit} ({ms.value:.3f} ms)", file=sys.stderr, flush=True)
+    return {"peaks": res, "cus": cus.value, "clock_assumed_hz": CLK}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +531,8 @@ def main():
                     help="with --tol: eps-scaling from this eps (one iteration per halving)")
     ap.add_argument("--hvp", action="store_true",
                     help="time one Hessian-vector product of OT_eps in x at the workload's solved pair")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only run the unit-rate microbenchmarks (exp2, VALU, MFMA, HBM/L2/MALL reads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -486,6 +551,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.peaks:
+        print(json.dumps(measure_peaks()), flush=True)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)

@@ -1,4 +1,5 @@
-"""Builds libflashsk.so in-tree from csrc/*.hip with hipcc for gfx950.
+"""Builds libflashsk.so in-tree from csrc/*.hip with hipcc for gfx950, and the
+unit-rate microbenchmarks peaks/libskpeaks.so that `bench.py --peaks` runs.
 
 Usage: python -m streaming_sinkhorn_solver_log_amd.build   (or build_library()).
 """
@@ -16,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflashsk.so")
 OBJ_DIR = os.path.join(PKG, "_build")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "peaks", "libskpeaks.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -52,5 +55,18 @@ def build_library(jobs: int = 8) -> str:
     return LIB
 
 
+def build_peaks() -> str:
+    """Compiles the microbenchmark library (separate from libflashsk.so)."""
+    tmp = PEAKS_LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, "-shared", PEAKS_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PEAKS_SRC}:\n{err}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
+
+
 if __name__ == "__main__":
     print(build_library())
+    print(build_peaks())

@@ -184,3 +184,13 @@ def test_hvp_rejects_invalid_arguments(lib):
         args = list(base)
         args[idx] = val
         assert lib.sk_ot_hvp_x(*args) == code, (idx, val)
+
+
+def test_peaks_library_exports_measure_entry():
+    """The unit-rate microbenchmark library bench.py --peaks loads exports its
+    one entry point (loading it makes no GPU call)."""
+    path = os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "peaks", "libskpeaks.so")
+    if not os.path.exists(path):
+        pytest.skip("libskpeaks.so not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    assert hasattr(L, "skp_measure")
