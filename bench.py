@@ -482,32 +482,50 @@ PEAK_CASES = [
     (8, "l2_read", "B/s", None, "1 MiB read by every workgroup"),
     (9, "mall_read", "B/s", None, "64 MiB streamed 32 times"),
     (10, "mix_bf16_points_d64", "score/s", VALU_PEAK / 4,
-     "4 bf16 MFMAs per 1024 scores + mul + exp2 + add: VALU roof if the MFMAs hide fully"),
+     "5 bf16 MFMAs per 1024 scores + mul + exp2 + add: VALU roof if the MFMAs hide fully"),
+    (11, "mul_exp2_add", "score/s", VALU_PEAK / 4, "mul + exp2 (2 slots) + add per score"),
 ]
 
 
-def measure_peaks():
+def measure_peaks(wgs_list=None):
+    """Unit-rate microbenchmarks at 8 workgroups per CU; with wgs_list, the
+    half-pass mix probes and their parts at each of those workgroup counts."""
     import ctypes
 
     from streaming_sinkhorn_solver_log_amd.build import PEAKS_LIB
     if not os.path.exists(PEAKS_LIB):
         raise RuntimeError(f"{PEAKS_LIB} is missing: run __graft_entry__.build() first")
     lib = ctypes.CDLL(PEAKS_LIB)
-    lib.skp_measure.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
-                                ctypes.POINTER(ctypes.c_int)]
+    lib.skp_measure.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.skp_measure.restype = ctypes.c_int
     res = {}
     cus = ctypes.c_int(0)
-    for which, name, unit, peak, model in PEAK_CASES:
+
+    def run(which, name, wgs):
         work, ms = ctypes.c_double(0), ctypes.c_double(0)
-        rc = lib.skp_measure(which, ctypes.byref(work), ctypes.byref(ms), ctypes.byref(cus))
+        rc = lib.skp_measure(which, wgs, ctypes.byref(work), ctypes.byref(ms), ctypes.byref(cus))
         if rc != 0:
-            raise RuntimeError(f"peaks benchmark {name} failed with HIP error {-rc}")
-        rate = work.value / (ms.value * 1e-3)
-        res[name] = {"rate": rate, "unit": unit, "ms": ms.value, "model_peak": peak,
+            raise RuntimeError(f"peaks benchmark {name} failed with code {rc}")
+        return work.value / (ms.value * 1e-3), ms.value
+
+    if wgs_list:
+        for which, name, unit, peak, model in PEAK_CASES:
+            if which not in (3, 4, 6, 10, 11):
+                continue
+            res[name] = {"unit": unit, "by_wgs_per_cu": {}}
+            for wgs in wgs_list:
+                rate, ms = run(which, name, wgs)
+                res[name]["by_wgs_per_cu"][str(wgs)] = {"rate": rate, "ms": ms}
+                print(f"[peaks] {name} at {wgs} workgroups/CU: {rate:.4g} {unit} ({ms:.3f} ms)",
+                      file=sys.stderr, flush=True)
+        return {"peaks_by_occupancy": res, "cus": cus.value}
+    for which, name, unit, peak, model in PEAK_CASES:
+        rate, ms = run(which, name, 0)
+        res[name] = {"rate": rate, "unit": unit, "ms": ms, "model_peak": peak,
                      "frac": rate / peak if peak else None, "model": model,
                      "per_cu_per_clk": rate / (CU * CLK)}
-        print(f"[peaks] {name}: {rate:.4g} {unit} ({ms.value:.3f} ms)", file=sys.stderr, flush=True)
+        print(f"[peaks] {name}: {rate:.4g} {unit} ({ms:.3f} ms)", file=sys.stderr, flush=True)
     return {"peaks": res, "cus": cus.value, "clock_assumed_hz": CLK}
 
 
@@ -533,6 +551,8 @@ def main():
                     help="time one Hessian-vector product of OT_eps in x at the workload's solved pair")
     ap.add_argument("--peaks", action="store_true",
                     help="only run the unit-rate microbenchmarks (exp2, VALU, MFMA, HBM/L2/MALL reads)")
+    ap.add_argument("--peaks-wgs", default="", metavar="N,N,...",
+                    help="with --peaks: run the half-pass mix probes at these workgroups per CU instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -552,7 +572,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.peaks:
-        print(json.dumps(measure_peaks()), flush=True)
+        wgs = [int(v) for v in args.peaks_wgs.split(",") if v.strip()]
+        print(json.dumps(measure_peaks(wgs)), flush=True)
         return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB

@@ -69,22 +69,24 @@ __global__ __launch_bounds__(kThreads) void k_add(float* out, int iters, float c
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// The half-pass mix: per score one exp2 and one add into a running sum
-// (16 scores per step, four partial sums).
-__global__ __launch_bounds__(kThreads) void k_exp_add(float* out, int iters) {
+// The half-pass VALU mix alone: per score one exp2 (after a multiply by e when
+// SCALED) and one add into a running sum (16 scores per step, four sums).
+template <bool SCALED>
+__global__ __launch_bounds__(kThreads) void k_exp_add(float* out, int iters, float e) {
   float x[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) x[k] = -0.05f * (k + threadIdx.x % 3);
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  auto ex = [&](float v) { return __builtin_amdgcn_exp2f(SCALED ? v * e : v); };
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) opaque(x[k]);
 #pragma unroll
     for (int k = 0; k < 16; k += 4) {
-      s0 += __builtin_amdgcn_exp2f(x[k]);
-      s1 += __builtin_amdgcn_exp2f(x[k + 1]);
-      s2 += __builtin_amdgcn_exp2f(x[k + 2]);
-      s3 += __builtin_amdgcn_exp2f(x[k + 3]);
+      s0 += ex(x[k]);
+      s1 += ex(x[k + 1]);
+      s2 += ex(x[k + 2]);
+      s3 += ex(x[k + 3]);
     }
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = (s0 + s1) + (s2 + s3);
@@ -126,11 +128,13 @@ __global__ __launch_bounds__(kThreads) void k_mfma_f32(float* out, int iters) {
 }
 
 // The half-pass instruction mix with everything but the MFMAs and the VALU
-// taken out: per step NKB chained bf16 MFMAs produce 1024 scores while the
+// taken out: per step NMFMA chained bf16 MFMAs produce 1024 scores while the
 // previous step's 1024 are folded as exp2(score) (times e first when SCALED)
-// into four running sums -- the register-resident half-pass pattern.
-template <int NKB, bool SCALED>
-__global__ __launch_bounds__(kThreads) void k_mfma_exp(float* out, int iters, float e) {
+// into four running sums -- the register-resident half-pass pattern. The
+// occupancy hint keeps the accumulators in VGPRs, as in the half-pass kernel
+// (accumulators in AGPRs would add one v_accvgpr_read per score).
+template <int NMFMA, bool SCALED>
+__global__ __launch_bounds__(kThreads, 2) void k_mfma_exp(float* out, int iters, float e) {
   bf16x8 A, B;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void k_mfma_exp(float* out, int iters, fl
   auto chain = [&]() {
     f32x16 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int q = 1; q < NKB; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
+    for (int q = 1; q < NMFMA; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
     return acc;
   };
   auto fold = [&](const f32x16& acc) {
@@ -229,11 +233,12 @@ void launch_one(void* p) {
     case 0: k_exp<<<c.blocks, kThreads>>>(c.out, c.iters); break;
     case 1: k_fma<<<c.blocks, kThreads>>>(c.out, c.iters, 0.999f, 1e-4f); break;
     case 2: k_add<<<c.blocks, kThreads>>>(c.out, c.iters, 1e-7f); break;
-    case 3: k_exp_add<<<c.blocks, kThreads>>>(c.out, c.iters); break;
+    case 3: k_exp_add<false><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
+    case 11: k_exp_add<true><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
     case 4: k_mfma_bf16<<<c.blocks, kThreads>>>(c.out, c.iters); break;
     case 5: k_mfma_f32<<<c.blocks, kThreads>>>(c.out, c.iters); break;
     case 6: k_mfma_exp<2, false><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
-    case 10: k_mfma_exp<4, true><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
+    case 10: k_mfma_exp<5, true><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
     case 8: k_read_window<<<c.blocks, kThreads>>>(c.buf, c.count, c.passes, c.out); break;
     default: k_read<<<c.blocks, kThreads>>>(c.buf, c.count, c.passes, c.out); break;
   }
@@ -245,12 +250,16 @@ extern "C" {
 
 // Benchmark `which`: 0 exp2, 1 fma, 2 add, 3 exp2 + add, 4 bf16 MFMA, 5 fp32 MFMA,
 // 6 two chained bf16 MFMAs per 1024 scores overlapped with exp2 + add (the
-// float32-point half-pass mix at d <= 5), 7 HBM read, 8 L2-resident read,
-// 9 MALL-resident read, 10 four chained bf16 MFMAs per 1024 scores with
-// multiply + exp2 + add (the bf16-point half-pass mix at d = 64). Writes the work done (operations or bytes) and the
-// kernel time in ms; returns 0 or a negative HIP error.
-int skp_measure(int which, double* work, double* ms_out, int* cus) {
-  if (which > 10 || which < 0) return -1;
+// float32-record half-pass mix at d <= 5), 7 HBM read, 8 L2-resident read,
+// 9 MALL-resident read, 10 five chained bf16 MFMAs per 1024 scores with
+// multiply + exp2 + add (the bf16-point half-pass mix at d = 64: four data
+// chunks and the bias chunk), 11 multiply + exp2 + add.
+// wgs_per_cu: workgroups of 256 threads per CU in the grid (0: 8, i.e. up to
+// 8 waves per SIMD where registers allow). Writes the work done (operations,
+// scores or bytes) and the kernel time in ms; returns 0, -1 for an invalid
+// argument or a negative HIP error.
+int skp_measure(int which, int wgs_per_cu, double* work, double* ms_out, int* cus) {
+  if (which > 11 || which < 0 || wgs_per_cu < 0 || wgs_per_cu > 32) return -1;
   hipError_t e;
   if (g_cus == 0) {
     int dev = 0;
@@ -260,9 +269,9 @@ int skp_measure(int which, double* work, double* ms_out, int* cus) {
   *cus = g_cus;
   Ctx c{};
   c.which = which;
-  c.blocks = g_cus * 8;  // 8 workgroups of 4 waves per CU: 8 waves per SIMD where registers allow
+  c.blocks = g_cus * (wgs_per_cu ? wgs_per_cu : 8);
   int64_t buf_bytes = 0;
-  if (which <= 6 || which == 10) {
+  if (which <= 6 || which >= 10) {
     c.iters = (which == 4 || which == 5) ? 20000 : (which == 6 || which == 10 ? 8000 : 40000);
   } else {
     // HBM: 4 GiB read once (16x the MALL); L2: 1 MiB read by every workgroup
@@ -299,7 +308,7 @@ int skp_measure(int which, double* work, double* ms_out, int* cus) {
   const double threads = (double)outs, waves = threads / 64.0;
   switch (which) {
     case 0: case 1: case 2: *work = threads * c.iters * 8; break;   // lane operations
-    case 3: *work = threads * c.iters * 16; break;                   // scores (exp2 + add each)
+    case 3: case 11: *work = threads * c.iters * 16; break;          // scores
     case 4: *work = waves * c.iters * 4 * 32768.0; break;            // flops
     case 5: *work = waves * c.iters * 4 * 4096.0; break;             // flops
     case 6: case 10: *work = waves * c.iters * 1024.0; break;        // scores
