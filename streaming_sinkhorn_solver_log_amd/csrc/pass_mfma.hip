@@ -88,13 +88,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// One 16-byte-per-lane global-to-LDS load: lane l's 16 bytes land at
+// One 16-byte-per-lane global-to-LDS load from a wave-uniform base address
+// (SGPR pair) plus a per-lane 32-bit byte offset: lane l's 16 bytes land at
 // lds_addr + 16 l. Written as inline assembly so that the compiler does not
 // treat the in-flight load as aliasing every later LDS read (it would wait for
-// all of them); completion is waited for explicitly with vmcnt.
-__device__ __forceinline__ void load_to_lds(const void* src, const void* lds_dst) {
+// all of them); completion is waited for explicitly with vmcnt. The uniform
+// base keeps the per-stage address arithmetic on the scalar unit.
+__device__ __forceinline__ void load_to_lds(const void* base, unsigned lane_off, const void* lds_dst) {
   const unsigned m0 = (unsigned)(uintptr_t)lds_dst;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(m0) : "memory");
 }
 
 // This wave's share of stage [c0, c0 + 128): blocks wave, wave + 4, ... of the
@@ -108,15 +110,17 @@ __device__ __attribute__((always_inline)) inline void issue_stage(
   constexpr int NB = kStageTiles * NBT;
   static_assert(NB % 4 == 0, "blocks of a stage split evenly over four waves");
   const int li = lane & 31, h = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: block choice on the scalar unit
+  // lane (li, h) reads its half h of column (tile start + li)
+  const unsigned off_rec = (unsigned)(li * (NKB * 32) + h * (NKB * 16));
+  const unsigned off_bias = (unsigned)(li * 32 + h * 16);
 #pragma unroll
   for (int q = 0; q < NB / 4; ++q) {
-    const int b = wave + 4 * q;
+    const int b = wv + 4 * q;
     const int tt = b / NBT, kb = b % NBT;
-    const int col = c0 + tt * 32 + li;
-    const void* src = (kb < NKB)
-        ? static_cast<const void*>(cols + (int64_t)col * (NKB * 32) + h * (NKB * 16) + kb * 16)
-        : static_cast<const void*>(bias + 2 * (int64_t)col + h);
-    load_to_lds(src, &L.blk[slot][tt][kb][0]);
+    const int64_t c = (int64_t)c0 + tt * 32;  // first column of the tile
+    if (kb < NKB) load_to_lds(cols + c * (NKB * 32) + kb * 16, off_rec, &L.blk[slot][tt][kb][0]);
+    else load_to_lds(reinterpret_cast<const unsigned char*>(bias) + c * 32, off_bias, &L.blk[slot][tt][kb][0]);
   }
 }
 
@@ -150,6 +154,18 @@ __device__ __attribute__((always_inline)) inline void sweep(
   constexpr int PER = kStageTiles * kBlocks<NKB, MERGED> / 4;  // loads per wave per stage
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
   const int nstages = (j1 - j0 + kStageCols - 1) / kStageCols;
+  // Software pipeline over the whole sweep: the MFMAs of tile g are issued
+  // before the exp/sum work of tile g - 1, across stage boundaries (tile g's
+  // scores live in acc[g & 1]; a stage holds an even number of tiles). The
+  // slot read before the first tile holds -inf scores, which add nothing.
+  static_assert(kStageTiles % 2 == 0, "tile parity carries across stages");
+  f32x16 acc[2][RB];
+  if constexpr (NKB <= 4) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[1][rb][r] = -INFINITY;
+  }
 #pragma unroll
   for (int q = 0; q < R - 1; ++q)
     if (q < nstages) issue_stage<NKB, MERGED>(L, q, cols, p.bias_col, j0 + q * kStageCols, wave, lane);
@@ -173,18 +189,12 @@ __device__ __attribute__((always_inline)) inline void sweep(
       if constexpr (!MERGED) ct.aug = L.blk[slot][tt][NKB][lane];
     };
     if constexpr (NKB <= 4) {
-      // MFMAs of tile tt + 1 are issued before the exp/sum work of tile tt
-      f32x16 acc[2][RB];
       ColTile<NKB> ct;
-      stage_tile(ct, 0);
-      tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc[0]);
 #pragma unroll
       for (int tt = 0; tt < kStageTiles; ++tt) {
-        if (tt + 1 < kStageTiles) {
-          stage_tile(ct, tt + 1);
-          tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc[(tt + 1) & 1]);
-        }
-        tile_valu<RB, SHIFTED, SCALED>(acc[tt & 1], p.escale, M, S);
+        stage_tile(ct, tt);
+        tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc[tt & 1]);
+        tile_valu<RB, SHIFTED, SCALED>(acc[(tt + 1) & 1], p.escale, M, S);
       }
     } else {
       // wide records: registers do not allow a second tile of accumulators
@@ -192,12 +202,14 @@ __device__ __attribute__((always_inline)) inline void sweep(
       for (int tt = 0; tt < kStageTiles; ++tt) {
         ColTile<NKB> ct;
         stage_tile(ct, tt);
-        f32x16 acc[RB];
-        tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc);
-        tile_valu<RB, SHIFTED, SCALED>(acc, p.escale, M, S);
+        f32x16 one[RB];
+        tile_scores<NKB, RB, MERGED>(ct, B, Baug, one);
+        tile_valu<RB, SHIFTED, SCALED>(one, p.escale, M, S);
       }
     }
   }
+  if constexpr (NKB <= 4)
+    if (nstages > 0) tile_valu<RB, SHIFTED, SCALED>(acc[1], p.escale, M, S);  // the last tile
   __syncthreads();
 }
 
@@ -261,8 +273,15 @@ __device__ __forceinline__ void row_sums(const MfmaPassArgs& p, const float (&M)
 // term by 1, so the sum cannot overflow; a row block with a sum below 2^-60
 // (shift far too high) is recomputed by an exact online-max sweep over all
 // columns, by the workgroup that completes it.
+// Waves per SIMD the register allocation must allow: 4 for the one-block
+// layouts (d = 3 float32, small bf16), 3 up to four K blocks (d = 64 bf16:
+// at most 168 VGPRs), 2 for wide records (their LDS ring allows two
+// workgroups per CU anyway).
+template <int NKB, bool MERGED>
+constexpr int kMinWaves = (MERGED || NKB == 1) ? 4 : (NKB <= 4 ? 3 : 2);
+
 template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED>
-__global__ __launch_bounds__(kThreads, 2) void k_lse_mfma(const MfmaPassArgs p) {
+__global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma(const MfmaPassArgs p) {
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
   static_assert(ROWS <= kThreads, "the partial merge finishes one row per thread");
