@@ -482,7 +482,7 @@ PEAK_CASES = [
     (8, "l2_read", "B/s", None, "1 MiB read by every workgroup"),
     (9, "mall_read", "B/s", None, "64 MiB streamed 32 times"),
     (10, "mix_bf16_points_d64", "score/s", VALU_PEAK / 4,
-     "5 bf16 MFMAs per 1024 scores + mul + exp2 + add: VALU roof if the MFMAs hide fully"),
+     "4 bf16 MFMAs per 1024 scores + mul + exp2 + add: VALU roof if the MFMAs hide fully"),
     (11, "mul_exp2_add", "score/s", VALU_PEAK / 4, "mul + exp2 (2 slots) + add per score"),
 ]
 

@@ -113,6 +113,7 @@ struct SideM {
   float* alpha;
   float* lw;
   bf16x8* bias[2];
+  float* hacc[2];  // the same biases as float32 in accumulator units (padded)
   float* hval[2];
   float* dmax[2];
   float* L;
@@ -146,6 +147,8 @@ SideM carve_side_m(Carve& c, int64_t cnt, int nkb, int row_blocks) {
   s.lw = c.take<float>(cnt);
   s.bias[0] = c.take<bf16x8>((size_t)padded * 2);
   s.bias[1] = c.take<bf16x8>((size_t)padded * 2);
+  s.hacc[0] = c.take<float>(padded);
+  s.hacc[1] = c.take<float>(padded);
   s.hval[0] = c.take<float>(cnt);
   s.hval[1] = c.take<float>(cnt);
   s.dmax[0] = c.take<float>(row_blocks);
@@ -415,6 +418,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
       pf.bias_stride = 2 * sp.nkb;
     }
     pf.Lout = L.xm.L; pf.Lin = L.xm.L; pf.hval_in = L.xm.hval[cur]; pf.hval_out = L.xm.hval[nxt];
+    pf.hcol = L.ym.hacc[cur]; pf.hout = L.xm.hacc[nxt];
     pf.dmax_in = L.ym.dmax[cur]; pf.n_dmax_in = sp.g.row_blocks; pf.dmax_out = L.xm.dmax[nxt];
     pf.exact_count = L.c.exact_count;
     pf.part = L.c.part; pf.counters = L.c.counters;
@@ -432,6 +436,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
       pg.bias_stride = 2 * sp.nkb;
     }
     pg.Lout = L.ym.L; pg.Lin = L.ym.L; pg.hval_in = L.ym.hval[cur]; pg.hval_out = L.ym.hval[nxt];
+    pg.hcol = L.xm.hacc[cur]; pg.hout = L.ym.hacc[nxt];
     pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
     pg.row_blocks = sp.g.row_blocks; pg.stages = sp.g.stages;
@@ -536,6 +541,8 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
                     L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
     MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw,
                     L.ym.bias[0], L.ym.bias[1], L.ym.hval[0], m};
+    px.hacc = L.xm.hacc[0]; px.hacc_alt = L.xm.hacc[1];
+    py.hacc = L.ym.hacc[0]; py.hacc_alt = L.ym.hacc[1];
     // counters and the exact-fallback count are zeroed together (adjacent)
     e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, sp.merged, center, L.c.centroid, L.c.shift,
                          L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);

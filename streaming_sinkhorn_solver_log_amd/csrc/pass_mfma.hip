@@ -48,12 +48,23 @@ namespace {
 
 using namespace dev;
 
-template <int RB, bool SHIFTED, bool SCALED>
+// bf16 points with a separate bias record: the column bias enters as the
+// first MFMA's float32 accumulator input (h~ from MfmaPassArgs::hcol) and the
+// row shift as the exponent's offset, exp2(e * acc - shift), folded into the
+// multiply by e that bf16 points need anyway: one MFMA per tile and row block
+// fewer than a bias K block. float32 records keep the bias block (an offset
+// would cost them an add per pair).
+template <bool SCALED, bool MERGED>
+constexpr bool kFloatBias = SCALED && !MERGED;
+
+template <int RB, bool SHIFTED, bool SCALED, bool FB>
 __device__ __attribute__((always_inline)) inline void tile_valu(const f32x16 (&acc)[RB], float e,
-                                                                float (&M)[RB], float (&S)[RB]) {
+                                                                const float (&off)[RB], float (&M)[RB],
+                                                                float (&S)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if constexpr (SHIFTED) sum_update<SCALED>(acc[rb], e, S[rb]);
+    if constexpr (SHIFTED && FB) sum_update_off(acc[rb], e, off[rb], S[rb]);
+    else if constexpr (SHIFTED) sum_update<SCALED>(acc[rb], e, S[rb]);
     else lse_update(acc[rb], e, M[rb], S[rb]);
   }
 }
@@ -64,8 +75,11 @@ __device__ __attribute__((always_inline)) inline void tile_valu(const f32x16 (&a
 // stages. A tile's image in LDS is NKB + 1 blocks of 1 KB; block kb holds, at
 // lane l's 16 bytes, exactly the A operand lane l needs (its half l / 32 of
 // K block kb of column tile + l % 32; block NKB is the bias chunk), so the
-// compute waves read it back with conflict-free 16-byte reads. The four waves
-// of the workgroup share the loads (one per block) and one barrier per stage.
+// compute waves read it back with conflict-free 16-byte reads. With float
+// biases (kFloatBias) the last block is instead the tile's 32 float32 biases
+// (one global_load_lds_dword; lanes 32-63 load a second copy), read back as
+// broadcast 16-byte reads. The four waves of the workgroup share the loads
+// (one per block) and one barrier per stage.
 constexpr int kStageTiles = 4;
 constexpr int kStageCols = kStageTiles * 32;
 template <int NKB>
@@ -76,10 +90,41 @@ constexpr int kRing = NKB >= 4 ? 2 : 3;  // stages in flight (LDS: ring x 4 x bl
 template <int NKB, bool MERGED>
 constexpr int kBlocks = MERGED ? NKB : NKB + 1;
 
-template <int NKB, bool MERGED>
+template <int NKB, bool MERGED, bool FB>
 struct StageRing {
   bf16x8 blk[kRing<NKB>][kStageTiles][kBlocks<NKB, MERGED>][64];
 };
+template <int NKB, bool MERGED>
+struct StageRing<NKB, MERGED, true> {
+  bf16x8 blk[kRing<NKB>][kStageTiles][NKB][64];
+  float hb[kRing<NKB>][kStageTiles][64];  // column biases of the tile, twice
+};
+
+// Column operands of one tile with float biases: the data K blocks and the
+// tile's biases in LDS, which each row block loads straight into its
+// accumulator (no registers held for them).
+template <int NKB>
+struct ColTileF {
+  bf16x8 a[NKB];
+  const float* hb;
+};
+
+// The accumulator input of a tile: lane (h, li) gets the biases of columns
+// 8q + 4h + t in register 4q + t (the accumulator layout), four broadcast
+// 16-byte LDS reads.
+__device__ __forceinline__ f32x16 bias_tile(const float* hb, int half) {
+  const float4* hb4 = reinterpret_cast<const float4*>(hb);
+  f32x16 c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = hb4[2 * q + half];  // columns 8q + 4h .. 8q + 4h + 3
+    c[4 * q + 0] = v.x;
+    c[4 * q + 1] = v.y;
+    c[4 * q + 2] = v.z;
+    c[4 * q + 3] = v.w;
+  }
+  return c;
+}
 
 // s_waitcnt vmcnt(N), other counters not waited on (gfx9 encoding).
 template <int N>
@@ -99,13 +144,19 @@ __device__ __forceinline__ void load_to_lds(const void* base, unsigned lane_off,
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(m0) : "memory");
 }
 
+// As load_to_lds with 4 bytes per lane: lane l's 4 bytes land at lds_addr + 4 l.
+__device__ __forceinline__ void load_to_lds_dword(const void* base, unsigned lane_off, const void* lds_dst) {
+  const unsigned m0 = (unsigned)(uintptr_t)lds_dst;
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(m0) : "memory");
+}
+
 // This wave's share of stage [c0, c0 + 128): blocks wave, wave + 4, ... of the
 // stage's blocks. Columns past the range read the padding (masked) or the
 // next range; they are never summed.
-template <int NKB, bool MERGED>
+template <int NKB, bool MERGED, bool FB>
 __device__ __attribute__((always_inline)) inline void issue_stage(
-    StageRing<NKB, MERGED>& L, int slot, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
-    int c0, int wave, int lane) {
+    StageRing<NKB, MERGED, FB>& L, int slot, const unsigned char* __restrict__ cols, const bf16x8* __restrict__ bias,
+    const float* __restrict__ hcol, int c0, int wave, int lane) {
   constexpr int NBT = kBlocks<NKB, MERGED>;
   constexpr int NB = kStageTiles * NBT;
   static_assert(NB % 4 == 0, "blocks of a stage split evenly over four waves");
@@ -119,13 +170,32 @@ __device__ __attribute__((always_inline)) inline void issue_stage(
     const int b = wv + 4 * q;
     const int tt = b / NBT, kb = b % NBT;
     const int64_t c = (int64_t)c0 + tt * 32;  // first column of the tile
-    if (kb < NKB) load_to_lds(cols + c * (NKB * 32) + kb * 16, off_rec, &L.blk[slot][tt][kb][0]);
-    else load_to_lds(reinterpret_cast<const unsigned char*>(bias) + c * 32, off_bias, &L.blk[slot][tt][kb][0]);
+    if (kb < NKB) {
+      load_to_lds(cols + c * (NKB * 32) + kb * 16, off_rec, &L.blk[slot][tt][kb][0]);
+    } else if constexpr (FB) {
+      load_to_lds_dword(reinterpret_cast<const unsigned char*>(hcol) + c * 4, (unsigned)(li * 4), &L.hb[slot][tt][0]);
+    } else {
+      load_to_lds(reinterpret_cast<const unsigned char*>(bias) + c * 32, off_bias, &L.blk[slot][tt][kb][0]);
+    }
   }
 }
 
 // Score tile against the RB row blocks: data K blocks, then (separate layout)
 // the bias block.
+template <int NKB, int RB, bool MERGED>
+__device__ __attribute__((always_inline)) inline void tile_scores(
+    const ColTileF<NKB>& ct, const bf16x8 (&B)[RB][NKB], const bf16x8 (&)[RB], f32x16 (&acc)[RB]) {
+  // float biases: the first MFMA adds them as its accumulator input
+  const int half = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    f32x16 a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.a[0], B[rb][0], bias_tile(ct.hb, half), 0, 0, 0);
+#pragma unroll
+    for (int kb = 1; kb < NKB; ++kb) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ct.a[kb], B[rb][kb], a, 0, 0, 0);
+    acc[rb] = a;
+  }
+}
+
 template <int NKB, int RB, bool MERGED>
 __device__ __attribute__((always_inline)) inline void tile_scores(
     const ColTile<NKB>& ct, const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB], f32x16 (&acc)[RB]) {
@@ -143,13 +213,16 @@ __device__ __attribute__((always_inline)) inline void tile_scores(
 }
 
 // One sweep of the workgroup over columns [j0, j1), j0 a multiple of 128.
-// SHIFTED: the row shift is folded into the row side's bias block and the sums
-// need no running maximum; otherwise online max/sum-exp. Ends with a barrier
-// (LDS reusable).
+// SHIFTED: the row shift is folded into the row side's bias block (float
+// biases: off = -shift in the exponent) and the sums need no running maximum;
+// otherwise online max/sum-exp. Ends with a barrier (LDS reusable).
 template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED>
 __device__ __attribute__((always_inline)) inline void sweep(
-    const MfmaPassArgs& p, StageRing<NKB, MERGED>& L, int j0, int j1, const bf16x8 (&B)[RB][NKB],
-    const bf16x8 (&Baug)[RB], float (&M)[RB], float (&S)[RB], int lane, int wave) {
+    const MfmaPassArgs& p, StageRing<NKB, MERGED, kFloatBias<SCALED, MERGED>>& L, int j0, int j1,
+    const bf16x8 (&B)[RB][NKB], const bf16x8 (&Baug)[RB], const float (&off)[RB], float (&M)[RB],
+    float (&S)[RB], int lane, int wave) {
+  constexpr bool FB = kFloatBias<SCALED, MERGED>;
+  using Tile = std::conditional_t<FB, ColTileF<NKB>, ColTile<NKB>>;
   constexpr int R = kRing<NKB>;
   constexpr int PER = kStageTiles * kBlocks<NKB, MERGED> / 4;  // loads per wave per stage
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
@@ -168,7 +241,7 @@ __device__ __attribute__((always_inline)) inline void sweep(
   }
 #pragma unroll
   for (int q = 0; q < R - 1; ++q)
-    if (q < nstages) issue_stage<NKB, MERGED>(L, q, cols, p.bias_col, j0 + q * kStageCols, wave, lane);
+    if (q < nstages) issue_stage<NKB, MERGED, FB>(L, q, cols, p.bias_col, p.hcol, j0 + q * kStageCols, wave, lane);
   for (int st = 0; st < nstages; ++st) {
     // this wave's loads of stage st are done once at most the later stages'
     // loads are outstanding; the barrier then covers every wave's loads
@@ -181,35 +254,40 @@ __device__ __attribute__((always_inline)) inline void sweep(
     __syncthreads();
     // slot (st - 1) % R is free: every wave finished stage st - 1 before the barrier
     if (st + R - 1 < nstages)
-      issue_stage<NKB, MERGED>(L, (st + R - 1) % R, cols, p.bias_col, j0 + (st + R - 1) * kStageCols, wave, lane);
+      issue_stage<NKB, MERGED, FB>(L, (st + R - 1) % R, cols, p.bias_col, p.hcol, j0 + (st + R - 1) * kStageCols,
+                                   wave, lane);
     const int slot = st % R;
-    auto stage_tile = [&](ColTile<NKB>& ct, int tt) {
+    auto stage_tile = [&](Tile& ct, int tt) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = L.blk[slot][tt][kb][lane];
-      if constexpr (!MERGED) ct.aug = L.blk[slot][tt][NKB][lane];
+      if constexpr (FB) {
+        ct.hb = &L.hb[slot][tt][0];
+      } else if constexpr (!MERGED) {
+        ct.aug = L.blk[slot][tt][NKB][lane];
+      }
     };
     if constexpr (NKB <= 4) {
-      ColTile<NKB> ct;
+      Tile ct;
 #pragma unroll
       for (int tt = 0; tt < kStageTiles; ++tt) {
         stage_tile(ct, tt);
         tile_scores<NKB, RB, MERGED>(ct, B, Baug, acc[tt & 1]);
-        tile_valu<RB, SHIFTED, SCALED>(acc[(tt + 1) & 1], p.escale, M, S);
+        tile_valu<RB, SHIFTED, SCALED, FB>(acc[(tt + 1) & 1], p.escale, off, M, S);
       }
     } else {
       // wide records: registers do not allow a second tile of accumulators
 #pragma unroll
       for (int tt = 0; tt < kStageTiles; ++tt) {
-        ColTile<NKB> ct;
+        Tile ct;
         stage_tile(ct, tt);
         f32x16 one[RB];
         tile_scores<NKB, RB, MERGED>(ct, B, Baug, one);
-        tile_valu<RB, SHIFTED, SCALED>(one, p.escale, M, S);
+        tile_valu<RB, SHIFTED, SCALED, FB>(one, p.escale, off, M, S);
       }
     }
   }
   if constexpr (NKB <= 4)
-    if (nstages > 0) tile_valu<RB, SHIFTED, SCALED>(acc[1], p.escale, M, S);  // the last tile
+    if (nstages > 0) tile_valu<RB, SHIFTED, SCALED, FB>(acc[1], p.escale, off, M, S);  // the last tile
   __syncthreads();
 }
 
@@ -286,7 +364,8 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
   constexpr int ROWS = 4 * RB * 32;
   static_assert(ROWS <= kThreads, "the partial merge finishes one row per thread");
   __shared__ float red[kThreads / 64];
-  __shared__ __attribute__((aligned(16))) StageRing<NKB, MERGED> lds;
+  constexpr bool FB = kFloatBias<SCALED, MERGED>;
+  __shared__ __attribute__((aligned(16))) StageRing<NKB, MERGED, FB> lds;
   // Row side of the bias block: (1, 1, 1, -shift parts) meeting the column's
   // (bias parts, 1, 1, 1). Separate layout: its own K block (Baug); merged
   // layout: the free last chunk of the row record (half 1, K block NKB - 1).
@@ -329,7 +408,7 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
     const int row_base = r * ROWS + wave * (RB * 32);
 
     bf16x8 B[RB][NKB], Baug[RB];
-    float M[RB], S[RB], shift_row[RB];
+    float M[RB], S[RB], shift_row[RB], off[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int i = min(row_base + rb * 32 + li, p.nr - 1);
@@ -338,18 +417,20 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
       for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
       if constexpr (SHIFTED) {
         shift_row[rb] = p.Lin[i] + dmax;  // log2 units
-        set_row_aug(B[rb], Baug[rb], -shift_row[rb] / p.escale, half);
+        if constexpr (!FB) set_row_aug(B[rb], Baug[rb], -shift_row[rb] / p.escale, half);
+        off[rb] = -shift_row[rb];
         M[rb] = 0.0f;
       } else {
         shift_row[rb] = 0.0f;
-        set_row_aug(B[rb], Baug[rb], 0.0f, half);
+        if constexpr (!FB) set_row_aug(B[rb], Baug[rb], 0.0f, half);
+        off[rb] = 0.0f;
         M[rb] = -INFINITY;
       }
       S[rb] = 0.0f;
     }
 
-    sweep<NKB, RB, SHIFTED, SCALED, MERGED>(p, lds, s0 * kStageCols, min(p.nc, s1 * kStageCols), B, Baug, M,
-                                             S, lane, wave);
+    sweep<NKB, RB, SHIFTED, SCALED, MERGED>(p, lds, s0 * kStageCols, min(p.nc, s1 * kStageCols), B, Baug, off,
+                                             M, S, lane, wave);
     float Lm[RB], Ls[RB];
     row_sums<RB, SHIFTED>(p, M, S, shift_row, Lm, Ls);
 
@@ -419,11 +500,11 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
         if (threadIdx.x == 0 && p.exact_count) atomicAdd(p.exact_count, 1u);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          set_row_aug(B[rb], Baug[rb], 0.0f, half);
+          if constexpr (!FB) set_row_aug(B[rb], Baug[rb], 0.0f, half);
           M[rb] = -INFINITY;
           S[rb] = 0.0f;
         }
-        sweep<NKB, RB, false, SCALED, MERGED>(p, lds, 0, p.nc, B, Baug, M, S, lane, wave);
+        sweep<NKB, RB, false, SCALED, MERGED>(p, lds, 0, p.nc, B, Baug, off, M, S, lane, wave);
         row_sums<RB, false>(p, M, S, shift_row, Lm, Ls);
         dh = -INFINITY;
 #pragma unroll
@@ -487,7 +568,7 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
                                                         const float* pot, float* pot_zero,
                                                         float* alpha, float* lw, bf16x8* bias, int bias_stride,
                                                         bf16x8* bias_alt, float* hval, float log2e_over_eps,
-                                                        float bias_scale) {
+                                                        float bias_scale, float* hacc) {
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n) return;
   float nrm = 0.0f;
@@ -510,6 +591,7 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
   const float h = kLog2e * l + (pv - nrm) * log2e_over_eps;
   hval[r] = h;
   write_bias_chunk(bias + r * bias_stride, h * bias_scale);
+  if (hacc) hacc[r] = masked_bias(h * bias_scale);
   if (bias_alt) {
     bias[r * bias_stride + 1] = bf16x8{};
     bias_alt[2 * r + 1] = bf16x8{};
@@ -518,9 +600,10 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
 
 // Masked padding columns [n, n_pad) of a side. Separate layout: zero records,
 // masked bias records in both buffers. Merged layout: zero records whose
-// last chunk is a masked bias chunk.
+// last chunk is a masked bias chunk. Float bias buffers (if given): masked.
 __global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, int nkb, int merged,
-                                                     bf16x8* col_rec, bf16x8* bias0, bf16x8* bias1) {
+                                                     bf16x8* col_rec, bf16x8* bias0, bf16x8* bias1,
+                                                     float* hacc0, float* hacc1) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per = (int64_t)nkb * 2;
   bf16x8 masked = {};
@@ -534,6 +617,10 @@ __global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, i
     const bf16x8 v = ((q & 1) == 0) ? masked : bf16x8{};
     bias0[q] = v;
     bias1[q] = v;
+  }
+  if (t < n_pad - n) {
+    if (hacc0) hacc0[n + t] = kMaskedBias;
+    if (hacc1) hacc1[n + t] = kMaskedBias;
   }
 }
 
@@ -665,13 +752,14 @@ hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int 
     const int64_t npad = mfma_padded_count(side->n);
     const int64_t pad_work = (npad - side->n) * nkb * 2;
     k_pad_columns<<<(int)((pad_work + 255) / 256), 256, 0, s>>>(side->n, npad, nkb, merged ? 1 : 0,
-                                                                side->col_rec, side->bias, side->bias_alt);
+                                                                side->col_rec, side->bias, side->bias_alt,
+                                                                side->hacc, side->hacc_alt);
     // merged: the bias chunk is the last chunk of the column record
     bf16x8* bias0 = merged ? side->col_rec + (2 * nkb - 1) : side->bias;
     k_prep_side_mfma<<<(int)((side->n + 255) / 256), 256, 0, s>>>(
         side->pts, dtype, side->n, d, sh, side->w, side->pot, side->pot_zero, side->alpha, side->lw,
         bias0, merged ? 2 * nkb : 2, merged ? nullptr : side->bias_alt, side->hval, log2e_over_eps,
-        mfma_bias_scale(dtype, c2));
+        mfma_bias_scale(dtype, c2), side->hacc);
   }
   return hipGetLastError();
 }

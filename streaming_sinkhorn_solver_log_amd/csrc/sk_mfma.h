@@ -38,6 +38,13 @@ struct MfmaPassArgs {
   // points keep exact records (escale = c2, biases stored divided by c2).
   float escale, bias_scale, neg_eps_ln2, log2e_over_eps;
   int symmetric;
+  // Column biases as float32 in accumulator units (h~ = h * bias_scale,
+  // masked like the bias records), padded like them; the bf16-point kernels
+  // with a separate bias record add them as the first MFMA's accumulator
+  // input instead of multiplying the bias record. hout: the rows' values for
+  // the other side's next pass (may be null).
+  const float* hcol;
+  float* hout;
 };
 
 // Weighted sums over the columns of the half-pass scores, on the matrix cores:
@@ -80,6 +87,8 @@ struct MfmaPrepSide {
   bf16x8* bias_alt;  // the second bias buffer (its padding is initialized too)
   float* hval;       // n biases (log2 units) of the starting potential
   int64_t n;
+  float* hacc = nullptr;      // padded float biases in accumulator units (or null)
+  float* hacc_alt = nullptr;  // the second float bias buffer (its padding is initialized too)
 };
 
 int mfma_nkb(int dtype, int d);  // K blocks per record, 0 if the resident kernel does not serve d

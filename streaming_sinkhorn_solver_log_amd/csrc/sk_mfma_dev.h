@@ -23,10 +23,13 @@ __device__ __forceinline__ void split3(float v, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)(r1 - (float)mid);
 }
 
+// A column bias with -inf (zero weight) replaced by the masked value; NaN kept.
+__device__ __forceinline__ float masked_bias(float htilde) { return htilde < kMaskedBias ? kMaskedBias : htilde; }
+
 // Bias chunk of one column: (hi, mid, lo, 1, 1, 1, 0, 0). The three ones meet
 // the row side's (-M) parts in the shifted sweep.
 __device__ __forceinline__ void write_bias_chunk(bf16x8* dst, float htilde) {
-  float v = htilde < kMaskedBias ? kMaskedBias : htilde;  // -inf (zero weight) -> masked; NaN kept
+  const float v = masked_bias(htilde);
   bf16x8 h0 = {};
   __bf16 a, b, c;
   split3(v, a, b, c);
@@ -70,6 +73,7 @@ __device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, f
   p.pot[i] = v;
   const float h = fmaf(kLog2e, p.lw[i], (v - al) * p.log2e_over_eps);
   write_bias_chunk(p.bias_out + (int64_t)i * p.bias_stride, h * p.bias_scale);
+  if (p.hout) p.hout[i] = masked_bias(h * p.bias_scale);
   const float dh = h - p.hval_in[i];
   p.hval_out[i] = h;
   p.Lout[i] = L;
@@ -109,6 +113,21 @@ __device__ __forceinline__ void lse_update(const f32x16& acc, float e, float& M,
   }
   S = fmaf(S, scale, (s0 + s1) + (s2 + s3));
   M = valid ? Mn : M;
+}
+
+// Shifted update with the row shift outside the accumulator: every term is
+// exp2(e * acc + off), off = -(row shift) in log2 units.
+__device__ __forceinline__ void sum_update_off(const f32x16& acc, float e, float off, float& S) {
+  auto ex = [&](float a) { return fast_exp2(fmaf(a, e, off)); };
+  float s0 = ex(acc[0]), s1 = ex(acc[1]), s2 = ex(acc[2]), s3 = ex(acc[3]);
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    s0 += ex(acc[r + 0]);
+    s1 += ex(acc[r + 1]);
+    s2 += ex(acc[r + 2]);
+    s3 += ex(acc[r + 3]);
+  }
+  S += (s0 + s1) + (s2 + s3);
 }
 
 // Shifted update: the row shift is already inside acc (bias block), so every

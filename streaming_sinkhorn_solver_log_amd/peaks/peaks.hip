@@ -238,7 +238,7 @@ void launch_one(void* p) {
     case 4: k_mfma_bf16<<<c.blocks, kThreads>>>(c.out, c.iters); break;
     case 5: k_mfma_f32<<<c.blocks, kThreads>>>(c.out, c.iters); break;
     case 6: k_mfma_exp<2, false><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
-    case 10: k_mfma_exp<5, true><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
+    case 10: k_mfma_exp<4, true><<<c.blocks, kThreads>>>(c.out, c.iters, 1.0f); break;
     case 8: k_read_window<<<c.blocks, kThreads>>>(c.buf, c.count, c.passes, c.out); break;
     default: k_read<<<c.blocks, kThreads>>>(c.buf, c.count, c.passes, c.out); break;
   }
@@ -251,9 +251,10 @@ extern "C" {
 // Benchmark `which`: 0 exp2, 1 fma, 2 add, 3 exp2 + add, 4 bf16 MFMA, 5 fp32 MFMA,
 // 6 two chained bf16 MFMAs per 1024 scores overlapped with exp2 + add (the
 // float32-record half-pass mix at d <= 5), 7 HBM read, 8 L2-resident read,
-// 9 MALL-resident read, 10 five chained bf16 MFMAs per 1024 scores with
-// multiply + exp2 + add (the bf16-point half-pass mix at d = 64: four data
-// chunks and the bias chunk), 11 multiply + exp2 + add.
+// 9 MALL-resident read, 10 four chained bf16 MFMAs per 1024 scores with
+// multiply + exp2 + add (the bf16-point half-pass mix at d = 64: four data K
+// blocks, the bias entering as accumulator input, the multiply an fma with
+// the row shift), 11 multiply + exp2 + add.
 // wgs_per_cu: workgroups of 256 threads per CU in the grid (0: 8, i.e. up to
 // 8 waves per SIMD where registers allow). Writes the work done (operations,
 // scores or bytes) and the kernel time in ms; returns 0, -1 for an invalid
