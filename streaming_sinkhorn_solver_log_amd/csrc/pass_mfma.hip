@@ -239,6 +239,11 @@ __device__ __attribute__((always_inline)) inline void sweep(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[1][rb][r] = -INFINITY;
   }
+  // Every earlier load (row records, shifts) completes here. Otherwise the
+  // compiler waits for them at their first use inside the stage loop, with a
+  // full vmcnt(0) that would also wait, every stage, for the loads just
+  // issued for the stages ahead.
+  wait_vmcnt<0>();
 #pragma unroll
   for (int q = 0; q < R - 1; ++q)
     if (q < nstages) issue_stage<NKB, MERGED, FB>(L, q, cols, p.bias_col, p.hcol, j0 + q * kStageCols, wave, lane);
