@@ -153,18 +153,32 @@ def test_zero_iterations_and_warm_start_resume(sk):
     assert np.abs(g3.cpu().numpy() - gr3).max() <= tol_pot(w, gr3)
 
 
-def test_zero_weights(sk):
-    w = W.CONFIGS[1].scaled(600, 500, 10)
-    say("zero weights")
+def _zero_weight_workload(case):
+    from dataclasses import replace
+    if case == "f32_d3":
+        return W.CONFIGS[1].scaled(600, 500, 10), None
+    if case in ("bf16_d64", "bf16_d64_symmetric"):  # float32 column biases, four K blocks
+        return W.CONFIGS[3].scaled(700, 611, 10), ("symmetric" if case.endswith("symmetric") else None)
+    # bf16_d16: float32 column biases, one K block
+    return replace(W.CONFIGS[4], d=16, dtype="bf16", eps=0.2, name="gauss_d16_bf16").scaled(650, 555, 10), None
+
+
+@pytest.mark.parametrize("case", ["f32_d3", "bf16_d64", "bf16_d64_symmetric", "bf16_d16"])
+def test_zero_weights(sk, case):
+    # zero weights give -inf column biases: masked columns that add nothing
+    w, mode = _zero_weight_workload(case)
+    mode = mode or w.mode
+    say(f"zero weights {case} n={w.n} m={w.m} d={w.d} mode={mode}")
     inp = W.make_inputs(w)
     inp.a[::7] = 0.0
     inp.b[3::11] = 0.0
     x, y, a, b = dev(inp)
-    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters)
-    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters)
-    assert np.abs(f.cpu().numpy() - fr).max() <= tol_pot(w, fr)
-    assert np.abs(g.cpu().numpy() - gr).max() <= tol_pot(w, gr)
-    assert abs(float(cost) - cr) <= 1e-5 * abs(cr)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, mode)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, mode)
+    ef, eg = np.abs(f.cpu().numpy() - fr).max(), np.abs(g.cpu().numpy() - gr).max()
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} tol={tol_pot(w, fr):.3e}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
 
 
 def test_repeatable_and_swap_symmetric(sk):
