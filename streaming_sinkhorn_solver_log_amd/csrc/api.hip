@@ -193,8 +193,8 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
   if (sp.path == Path::Mfma) {
     sp.nkb = mfma_nkb(dtype, (int)d);
     sp.merged = alternating && mfma_merged(dtype, (int)d, sp.nkb);
-    sp.f = plan_mfma_pass(n, m, sp.nkb, sp.merged);
-    sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged);
+    sp.f = plan_mfma_pass(n, m, sp.nkb, sp.merged, dtype == SK_BF16);
+    sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged, dtype == SK_BF16);
   } else if (sp.path == Path::Gemm) {
     sp.nkb = gemm_nkb(dtype, (int)d);
     sp.wide = dtype == SK_F32;
@@ -423,7 +423,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pf.exact_count = L.c.exact_count;
     pf.part = L.c.part; pf.counters = L.c.counters;
     pf.nr = (int)n; pf.nc = (int)m; pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
-    pf.row_blocks = sp.f.row_blocks; pf.stages = sp.f.stages;
+    pf.row_blocks = sp.f.row_blocks; pf.stages = sp.f.stages; pf.chunks = sp.f.chunks;
     pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
     pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
     if ((e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
@@ -439,7 +439,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pg.hcol = L.xm.hacc[cur]; pg.hout = L.ym.hacc[nxt];
     pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
-    pg.row_blocks = sp.g.row_blocks; pg.stages = sp.g.stages;
+    pg.row_blocks = sp.g.row_blocks; pg.stages = sp.g.stages; pg.chunks = sp.g.chunks;
     if ((e = launch_pass(sp, pg, shifted, scaled, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
     cur = nxt;
   }

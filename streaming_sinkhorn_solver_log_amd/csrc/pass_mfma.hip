@@ -328,7 +328,18 @@ struct UnitMap {
   }
 };
 
-__host__ __device__ inline int64_t chunks_for(int64_t T, int64_t W) { return (W % 8 == 0 && T >= 8) ? 8 : 1; }
+// Column chunks of a pass: the fewest (1, 2, 4 or 8) whose share of the
+// column bytes fits one XCD's 4 MB L2, so that the XCDs sweeping a chunk keep
+// it cached. More chunks than needed cost more row-block segments per
+// workgroup (row loads, partials, merges): measured at n = m = 50k, eight
+// chunks instead of one made the d = 3 half-pass 8% slower.
+int64_t chunks_for(int64_t T, int64_t W, int64_t col_bytes) {
+  constexpr int64_t kL2Bytes = int64_t(4) << 20;
+  if (W % 8 != 0) return 1;
+  int64_t c = 1;
+  while (c < 8 && c < T && col_bytes / c > kL2Bytes) c *= 2;
+  return c;
+}
 
 // Row results of one row block: (Lm, Ls) per row with L = Lm + log2 Ls (log2
 // units), in lanes of half 0.
@@ -389,7 +400,7 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
   const int li = lane & 31;
   const int64_t W = gridDim.x, w = blockIdx.x;
   const int64_t T = p.stages;
-  const UnitMap um{p.row_blocks, T, chunks_for(T, W), (int64_t)p.row_blocks * T, W};
+  const UnitMap um{p.row_blocks, T, p.chunks > 0 ? p.chunks : 1, (int64_t)p.row_blocks * T, W};
   const int64_t v = (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;  // XCD-contiguous numbering
   const int64_t u_end = um.begin(v + 1);
 
@@ -695,7 +706,7 @@ bool mfma_merged(int dtype, int d, int nkb) {
 
 int64_t mfma_padded_count(int64_t n) { return (n + 31) / 32 * 32 + 5 * 32; }
 
-PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged) {
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scaled) {
   PassPlan pl{};
   pl.rows_per_block = 4 * mfma_rb(nkb) * 32;
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
@@ -706,8 +717,12 @@ PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged) {
   if (grid > units / min_units) grid = units / min_units;
   if (grid < 1) grid = 1;
   pl.grid = (int)grid;
+  // column bytes a sweep streams: the records, plus (separate layout) the
+  // float32 biases (bf16 points) or the 32-byte bias records
+  const int64_t col_bytes = nc * ((int64_t)nkb * 32 + (merged ? 0 : (scaled ? 4 : 32)));
+  pl.chunks = (int)chunks_for(pl.stages, grid, col_bytes);
   // partial slots per row: the most contributors any row block has
-  const UnitMap um{pl.row_blocks, pl.stages, chunks_for(pl.stages, grid), units, grid};
+  const UnitMap um{pl.row_blocks, pl.stages, pl.chunks, units, grid};
   int64_t most = 1;
   for (int64_t r = 0; r < pl.row_blocks; ++r) {
     int64_t n = 0;

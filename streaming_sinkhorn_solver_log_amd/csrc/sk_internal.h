@@ -83,6 +83,7 @@ struct PassPlan {
   int cols_per_split;
   int grid;            // balanced plan: workgroups (one resident wave of them)
   int stages;          // balanced plan: 128-column stages per row block
+  int chunks;          // balanced plan: column chunks, each swept by the workgroups of 8 / chunks XCDs
 };
 
 PassPlan plan_valu_pass(int64_t nr, int64_t nc, int d);

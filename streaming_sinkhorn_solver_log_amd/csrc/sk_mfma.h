@@ -33,6 +33,7 @@ struct MfmaPassArgs {
   int nr, nc;
   int splits, cols_per_split;  // GEMM-tiled pass: column splits
   int row_blocks, stages;      // register-resident pass: balanced split of row blocks x stages
+  int chunks;                  // register-resident pass: column chunks (PassPlan::chunks)
   // Exponent of a pair in log2 units = escale * (acc - M). float32 points have
   // c2 folded into their row records (escale = 1, biases in log2 units); bf16
   // points keep exact records (escale = c2, biases stored divided by c2).
@@ -99,7 +100,7 @@ bool mfma_merged(int dtype, int d, int nkb);
 int mfma_rb(int nkb);
 // Points per side including the masked padding columns (records, bias buffers).
 int64_t mfma_padded_count(int64_t n);
-PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged);
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scaled);
 hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, bool merged,
                            const PassPlan& pl, hipStream_t s);
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
