@@ -50,7 +50,7 @@ class SinkhornError(RuntimeError):
 def _load_library() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m streaming_sinkhorn_solver_log_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python streaming_sinkhorn_solver_log_amd/build.py` "
             "(hipcc, gfx950). There is no fallback implementation.")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, U32, D, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,

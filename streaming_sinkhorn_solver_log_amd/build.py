@@ -1,7 +1,8 @@
 """Builds libflashsk.so in-tree from csrc/*.hip with hipcc for gfx950, and the
 unit-rate microbenchmarks peaks/libskpeaks.so that `bench.py --peaks` runs.
 
-Usage: python -m streaming_sinkhorn_solver_log_amd.build   (or build_library()).
+Usage: python streaming_sinkhorn_solver_log_amd/build.py   (or build_library()).
+Run it as a script: importing the package needs the library it builds.
 """
 from __future__ import annotations
 
