@@ -31,90 +31,94 @@ namespace {
 
 using namespace dev;
 
-// Workgroup tile: 2 x 2 waves, each wave WRT x WCT accumulator tiles of
-// 32 x 32, i.e. 64 WRT rows and 64 WCT columns per workgroup.
-template <int WRT, int WCT>
+// Workgroup tile: WGR x 2 waves (row waves x column waves), each wave
+// WRT x WCT accumulator tiles of 32 x 32, i.e. 32 WRT WGR rows and 64 WCT
+// columns per workgroup.
+template <int WRT, int WCT, int WGR>
 struct Geo {
-  static constexpr int kRows = 64 * WRT;
+  static constexpr int kWRT = WRT, kWCT = WCT, kWGR = WGR;
+  static constexpr int kNT = 128 * WGR;  // threads
+  static constexpr int kRows = 32 * WRT * WGR;
   static constexpr int kCols = 64 * WCT;
-  static constexpr int kRowLoads = kRows * 8 / kThreads;  // 16-byte chunks per thread per stage
-  static constexpr int kColLoads = kCols * 8 / kThreads;
-  static constexpr int kOcc = (WRT * WCT > 4) ? 1 : 2;  // workgroups per CU
+  static constexpr int kRowLoads = kRows * 8 / kNT;  // 16-byte chunks per thread per stage
+  static constexpr int kColLoads = kCols * 8 / kNT;
+  static constexpr int kOcc = (WRT * WCT * WGR > 8) ? 1 : 2;  // workgroups per CU
+  static_assert(kRows * 8 % kNT == 0 && kCols * 8 % kNT == 0, "stage loads split evenly");
 };
 
-template <int WRT, int WCT>
+template <class G>
 struct TileLds {
-  unsigned char rows[2][Geo<WRT, WCT>::kRows * kGRow];
-  unsigned char cols[2][Geo<WRT, WCT>::kCols * kGRow];
+  unsigned char rows[2][G::kRows * kGRow];
+  unsigned char cols[2][G::kCols * kGRow];
 };
 
-template <int WRT, int WCT>
+template <class G>
 struct TileRegs {
-  u32x4 r[Geo<WRT, WCT>::kRowLoads];
-  u32x4 c[Geo<WRT, WCT>::kColLoads];
+  u32x4 r[G::kRowLoads];
+  u32x4 c[G::kColLoads];
 };
 
 // Stage (kc) of the K dimension for rows [r0, r0 + kRows) and columns
 // [c0, c0 + kCols): per record, 4 x 16 bytes in each half, record bytes
 // [h * NKB * 16 + kc * 64, +64). Row indices clamp to the last row, column
 // indices to the last padded (masked) column.
-template <int WRT, int WCT>
+template <class G>
 __device__ __attribute__((always_inline)) inline void tile_load(
-    TileRegs<WRT, WCT>& g, const unsigned char* __restrict__ rows, const unsigned char* __restrict__ cols,
+    TileRegs<G>& g, const unsigned char* __restrict__ rows, const unsigned char* __restrict__ cols,
     int nkb, int nr, int col_last, int r0, int c0, int kc) {
   const int64_t rsb = (int64_t)nkb * 32;
 #pragma unroll
-  for (int q = 0; q < Geo<WRT, WCT>::kRowLoads; ++q) {
-    const int ch = threadIdx.x + q * kThreads;  // record (ch >> 3), half ((ch >> 2) & 1), part (ch & 3)
+  for (int q = 0; q < G::kRowLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;  // record (ch >> 3), half ((ch >> 2) & 1), part (ch & 3)
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
     const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
     g.r[q] = *reinterpret_cast<const u32x4*>(rows + (int64_t)min(r0 + rec, nr - 1) * rsb + off);
   }
 #pragma unroll
-  for (int q = 0; q < Geo<WRT, WCT>::kColLoads; ++q) {
-    const int ch = threadIdx.x + q * kThreads;
+  for (int q = 0; q < G::kColLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
     const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
     g.c[q] = *reinterpret_cast<const u32x4*>(cols + (int64_t)min(c0 + rec, col_last) * rsb + off);
   }
 }
 
-template <int WRT, int WCT>
-__device__ __attribute__((always_inline)) inline void tile_store(const TileRegs<WRT, WCT>& g,
-                                                                  TileLds<WRT, WCT>& L, int buf) {
+template <class G>
+__device__ __attribute__((always_inline)) inline void tile_store(const TileRegs<G>& g, TileLds<G>& L, int buf) {
 #pragma unroll
-  for (int q = 0; q < Geo<WRT, WCT>::kRowLoads; ++q) {
-    const int ch = threadIdx.x + q * kThreads;
+  for (int q = 0; q < G::kRowLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
     *reinterpret_cast<u32x4*>(&L.rows[buf][rec * kGRow + hh * 64 + part * 16]) = g.r[q];
   }
 #pragma unroll
-  for (int q = 0; q < Geo<WRT, WCT>::kColLoads; ++q) {
-    const int ch = threadIdx.x + q * kThreads;
+  for (int q = 0; q < G::kColLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
     *reinterpret_cast<u32x4*>(&L.cols[buf][rec * kGRow + hh * 64 + part * 16]) = g.c[q];
   }
 }
 
 // One sweep of the workgroup over columns [j0, j1). Wave (wr, wc)
-// accumulates rows wr * kRows/2 + rb * 32 + li against columns
+// accumulates rows wr * kRows/WGR + rb * 32 + li against columns
 // wc * kCols/2 + ct * 32 of each block. Ends with a barrier.
-template <bool SHIFTED, bool SCALED, int WRT, int WCT>
+template <bool SHIFTED, bool SCALED, class G, int WRT, int WCT>
 __device__ __attribute__((always_inline)) inline void gemm_sweep(
-    const MfmaPassArgs& p, TileLds<WRT, WCT>& L, int nkb, int col_last, int r0, int j0, int j1,
+    const MfmaPassArgs& p, TileLds<G>& L, int nkb, int col_last, int r0, int j0, int j1,
     const bf16x8 (&Baug)[WRT], float (&M)[WRT], float (&S)[WRT], int wr, int wc, int li, int half) {
-  using G = Geo<WRT, WCT>;
+  static_assert(G::kRows == 32 * WRT * (G::kNT / 128) && G::kCols == 64 * WCT, "wave tile matches the geometry");
+  constexpr int kWaveRows = G::kRows / (G::kNT / 128);
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
   const int nkc = nkb / kGKb;
   const int nblocks = (j1 - j0 + G::kCols - 1) / G::kCols;
   const int nstages = nblocks * nkc;
-  auto load_stage = [&](TileRegs<WRT, WCT>& g, int st) {
-    tile_load<WRT, WCT>(g, rows, cols, nkb, p.nr, col_last, r0, j0 + (st / nkc) * G::kCols, st % nkc);
+  auto load_stage = [&](TileRegs<G>& g, int st) {
+    tile_load<G>(g, rows, cols, nkb, p.nr, col_last, r0, j0 + (st / nkc) * G::kCols, st % nkc);
   };
-  TileRegs<WRT, WCT> g;
+  TileRegs<G> g;
   load_stage(g, 0);
-  tile_store<WRT, WCT>(g, L, 0);
+  tile_store<G>(g, L, 0);
   if (nstages > 1) load_stage(g, 1);
   __syncthreads();
   f32x16 acc[WRT][WCT];
@@ -137,7 +141,7 @@ __device__ __attribute__((always_inline)) inline void gemm_sweep(
 #pragma unroll
       for (int rb = 0; rb < WRT; ++rb)
         B[rb] = *reinterpret_cast<const bf16x8*>(
-            &L.rows[buf][(wr * (G::kRows / 2) + rb * 32 + li) * kGRow + half * 64 + kb * 16]);
+            &L.rows[buf][(wr * kWaveRows + rb * 32 + li) * kGRow + half * 64 + kb * 16]);
 #pragma unroll
       for (int rb = 0; rb < WRT; ++rb)
 #pragma unroll
@@ -165,18 +169,34 @@ __device__ __attribute__((always_inline)) inline void gemm_sweep(
     }
     // stage st + 1 into the other buffer (its previous stage was consumed
     // before the last barrier), then fetch stage st + 2
-    if (st + 1 < nstages) tile_store<WRT, WCT>(g, L, buf ^ 1);
+    if (st + 1 < nstages) tile_store<G>(g, L, buf ^ 1);
     if (st + 2 < nstages) load_stage(g, st + 2);
     __syncthreads();
   }
 }
 
-template <bool SHIFTED, bool SCALED, int WRT, int WCT>
-__global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(const MfmaPassArgs p, int nkb,
-                                                                           int col_last) {
-  using G = Geo<WRT, WCT>;
-  __shared__ __attribute__((aligned(16))) TileLds<WRT, WCT> lds;
-  __shared__ float red[kThreads / 64];
+// Workgroup-wide maximum over NT threads (every thread must call it).
+template <int NT>
+__device__ inline float wg_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+template <bool SHIFTED, bool SCALED, int WRT, int WCT, int WGR>
+__global__ __launch_bounds__((Geo<WRT, WCT, WGR>::kNT), (Geo<WRT, WCT, WGR>::kOcc)) void k_lse_gemm(
+    const MfmaPassArgs p, int nkb, int col_last) {
+  using G = Geo<WRT, WCT, WGR>;
+  constexpr int kNT = G::kNT;
+  constexpr int kWaveRows = G::kRows / WGR;
+  __shared__ __attribute__((aligned(16))) TileLds<G> lds;
+  __shared__ float red[kNT / 64];
   __shared__ float sm_m[2][G::kRows];  // per column-wave partials of each row
   __shared__ float sm_s[2][G::kRows];
   // Wide tiles keep their accumulators in AGPRs: an (empty) use of one lets
@@ -208,11 +228,11 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
   float shift_row[WRT];
   if constexpr (SHIFTED) {
     float dm = -INFINITY;
-    for (int q = threadIdx.x; q < p.n_dmax_in; q += kThreads) dm = fmaxf(dm, p.dmax_in[q]);
-    const float dmax = block_max(dm, red);
+    for (int q = threadIdx.x; q < p.n_dmax_in; q += kNT) dm = fmaxf(dm, p.dmax_in[q]);
+    const float dmax = wg_max<kNT>(dm, red);
 #pragma unroll
     for (int rb = 0; rb < WRT; ++rb) {
-      const int i = min(row0 + wr * (G::kRows / 2) + rb * 32 + li, p.nr - 1);
+      const int i = min(row0 + wr * kWaveRows + rb * 32 + li, p.nr - 1);
       shift_row[rb] = p.Lin[i] + dmax;
       Baug[rb] = row_aug(half, -shift_row[rb] / p.escale);
       M[rb] = 0.0f;
@@ -246,8 +266,8 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
         lm = p.escale * Mt;
       }
       if (half == 0) {
-        sm_m[wc][wr * (G::kRows / 2) + rb * 32 + li] = lm;
-        sm_s[wc][wr * (G::kRows / 2) + rb * 32 + li] = ls;
+        sm_m[wc][wr * kWaveRows + rb * 32 + li] = lm;
+        sm_s[wc][wr * kWaveRows + rb * 32 + li] = ls;
       }
     }
     __syncthreads();
@@ -260,11 +280,11 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
     lm = mt;
   };
 
-  gemm_sweep<SHIFTED, SCALED, WRT, WCT>(p, lds, nkb, col_last, row0, j0, j1, Baug, M, S, wr, wc, li, half);
+  gemm_sweep<SHIFTED, SCALED, G, WRT, WCT>(p, lds, nkb, col_last, row0, j0, j1, Baug, M, S, wr, wc, li, half);
   merge_rows(SHIFTED);
 
   // thread t owns rows t, t + 256, ... of the block
-  constexpr int kRowsPerThread = (G::kRows + kThreads - 1) / kThreads;
+  constexpr int kRowsPerThread = (G::kRows + kNT - 1) / kNT;
   float dh = -INFINITY;
   bool need_exact = false;
   float Lr[kRowsPerThread];
@@ -274,7 +294,7 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
   if (p.splits == 1) {
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
-      const int r = threadIdx.x + u * kThreads, i = row0 + r;
+      const int r = threadIdx.x + u * kNT, i = row0 + r;
       if (r < G::kRows && i < p.nr) {
         float lm, ls;
         row_result(r, lm, ls);
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
   } else {
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
-      const int r = threadIdx.x + u * kThreads, i = row0 + r;
+      const int r = threadIdx.x + u * kNT, i = row0 + r;
       if (r < G::kRows && i < p.nr) {
         float lm, ls;
         row_result(r, lm, ls);
@@ -295,7 +315,7 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
     if (!arrive_last(p.counters + rblk, p.splits)) return;
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
-      const int r = threadIdx.x + u * kThreads, i = row0 + r;
+      const int r = threadIdx.x + u * kNT, i = row0 + r;
       if (r < G::kRows && i < p.nr) {
         float Mt = -INFINITY;
         for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
@@ -316,7 +336,7 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
   if (!need_exact) {
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {
-      const int r = threadIdx.x + u * kThreads, i = row0 + r;
+      const int r = threadIdx.x + u * kNT, i = row0 + r;
       if (r < G::kRows && i < p.nr) dh = fmaxf(dh, finish_row_mfma(p, i, Lr[u]));
     }
   }
@@ -329,11 +349,11 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
         M[rb] = -INFINITY;
         S[rb] = 0.0f;
       }
-      gemm_sweep<false, SCALED, WRT, WCT>(p, lds, nkb, col_last, row0, 0, p.nc, Baug, M, S, wr, wc, li, half);
+      gemm_sweep<false, SCALED, G, WRT, WCT>(p, lds, nkb, col_last, row0, 0, p.nc, Baug, M, S, wr, wc, li, half);
       merge_rows(false);
 #pragma unroll
       for (int u = 0; u < kRowsPerThread; ++u) {
-        const int r = threadIdx.x + u * kThreads, i = row0 + r;
+        const int r = threadIdx.x + u * kNT, i = row0 + r;
         if (r < G::kRows && i < p.nr) {
           float lm, ls;
           row_result(r, lm, ls);
@@ -342,7 +362,7 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
       }
     }
   }
-  const float bmax = block_max(dh, red);
+  const float bmax = wg_max<kNT>(dh, red);
   if (threadIdx.x == 0) p.dmax_out[rblk] = bmax;
 }
 
@@ -351,8 +371,19 @@ __global__ __launch_bounds__(kThreads, (Geo<WRT, WCT>::kOcc)) void k_lse_gemm(co
 // float32 records, whose long K loop favours fewer operand reads per MFMA
 // (0.75 instead of 1 LDS fragment per MFMA; measured 3.4-3.7 ms against
 // 4.2 ms at d = 512).
-using NarrowGeo = Geo<2, 2>;
-using WideGeo = Geo<2, 4>;
+#ifndef SK_GEMM_NARROW
+#define SK_GEMM_NARROW 2, 4, 4
+#endif
+#ifndef SK_GEMM_WIDE
+#define SK_GEMM_WIDE 2, 4, 4
+#endif
+using NarrowGeo = Geo<SK_GEMM_NARROW>;
+using WideGeo = Geo<SK_GEMM_WIDE>;
+
+template <class G, bool SHIFTED, bool SCALED>
+void launch_geo(const MfmaPassArgs& a, int nkb, int col_last, dim3 grid, hipStream_t s) {
+  k_lse_gemm<SHIFTED, SCALED, G::kWRT, G::kWCT, G::kWGR><<<grid, G::kNT, 0, s>>>(a, nkb, col_last);
+}
 
 }  // namespace
 
@@ -395,8 +426,11 @@ int gemm_resident(bool wide) {
     int cus = 0, per_cu = 0;
     // the instantiations of one shape share the LDS footprint that binds occupancy
     const hipError_t e =
-        wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_gemm<true, false, 2, 4>, kThreads, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_gemm<true, true, 2, 2>, kThreads, 0);
+        wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &per_cu, k_lse_gemm<true, false, WideGeo::kWRT, WideGeo::kWCT, WideGeo::kWGR>, WideGeo::kNT, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &per_cu, k_lse_gemm<true, true, NarrowGeo::kWRT, NarrowGeo::kWCT, NarrowGeo::kWGR>,
+                   NarrowGeo::kNT, 0);
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
@@ -436,19 +470,19 @@ hipError_t launch_lse_gemm(const MfmaPassArgs& args, int nkb, bool shifted, bool
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
   if (wide) {
     if (shifted) {
-      if (scaled) k_lse_gemm<true, true, 2, 4><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-      else k_lse_gemm<true, false, 2, 4><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+      if (scaled) launch_geo<WideGeo, true, true>(a, nkb, col_last, grid, s);
+      else launch_geo<WideGeo, true, false>(a, nkb, col_last, grid, s);
     } else {
-      if (scaled) k_lse_gemm<false, true, 2, 4><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-      else k_lse_gemm<false, false, 2, 4><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+      if (scaled) launch_geo<WideGeo, false, true>(a, nkb, col_last, grid, s);
+      else launch_geo<WideGeo, false, false>(a, nkb, col_last, grid, s);
     }
   } else {
     if (shifted) {
-      if (scaled) k_lse_gemm<true, true, 2, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-      else k_lse_gemm<true, false, 2, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+      if (scaled) launch_geo<NarrowGeo, true, true>(a, nkb, col_last, grid, s);
+      else launch_geo<NarrowGeo, true, false>(a, nkb, col_last, grid, s);
     } else {
-      if (scaled) k_lse_gemm<false, true, 2, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-      else k_lse_gemm<false, false, 2, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+      if (scaled) launch_geo<NarrowGeo, false, true>(a, nkb, col_last, grid, s);
+      else launch_geo<NarrowGeo, false, false>(a, nkb, col_last, grid, s);
     }
   }
   return hipGetLastError();
