@@ -20,9 +20,11 @@
 // in that column order. pack_values writes them so, once per call.
 //
 // Precision: entries and values are split into bf16 parts (float32 points:
-// three and three, the six products of relative order up to 2^-16 give
-// float32 accuracy; bf16 points: two parts of the entries and two of the
-// values for P V, or one exact part of the bf16 points for the gradient).
+// three and three; the entries' leading parts are truncations, of relative
+// order 1, 2^-7, 2^-14, the values' are rounded, 1, 2^-8, 2^-16, and the six
+// products kept leave out terms of order 2^-22 and below: float32 accuracy;
+// bf16 points: two parts of the entries (2^-16) and two of the values for
+// P V, or one exact part of the bf16 points for the gradient).
 //
 // Stabilization: a running row maximum mu (acc units), raised only when a
 // tile's maximum exceeds it by more than 2^8 in value (lazy rescaling: terms
@@ -103,29 +105,55 @@ __device__ __attribute__((always_inline)) inline float pv_shift(const f32x16 (&a
   return -e * mu;
 }
 
-// Plan entries of one score tile (terms <= 2^8), their sum, and their bf16 parts
-// as the B operands of two K blocks.
-template <int PP>
+// Two floats' upper 16 bits packed as a bf16 pair (a in the low half): the
+// truncated bf16 parts, one v_perm_b32.
+__device__ __forceinline__ unsigned pack_hi16(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+// a and b rounded to bf16 (nearest even), packed (a in the low half).
+__device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(unsigned, v);
+}
+__device__ __forceinline__ float trunc_bf16(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFF0000u); }
+
+// Plan entries of one score tile (terms <= 2^8), their sum (SUM), and their
+// bf16 parts as the B operands of two K blocks. All parts but the last are
+// truncations (v - part is then exact), the last is rounded to nearest: two
+// parts carry 16 bits (relative error <= 2^-16), three carry float32's 24.
+template <int PP, bool SUM>
 __device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& acc, float e, float off,
                                                                bf16x8 (&P)[PP][2]) {
-  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  u32x4 W[PP][2];
+  float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float v = fast_exp2(fmaf(acc[r], e, off));
-    if ((r & 3) == 0) s0 += v;
-    else if ((r & 3) == 1) s1 += v;
-    else if ((r & 3) == 2) s2 += v;
-    else s3 += v;
-    const __bf16 a = (__bf16)v;
-    P[0][r >> 3][r & 7] = a;
-    if constexpr (PP >= 2) {
-      const float r1 = v - (float)a;
-      const __bf16 b = (__bf16)r1;
-      P[1][r >> 3][r & 7] = b;
-      if constexpr (PP >= 3) P[2][r >> 3][r & 7] = (__bf16)(r1 - (float)b);
+  for (int r = 0; r < 16; r += 2) {
+    const float v0 = fast_exp2(fmaf(acc[r], e, off));
+    const float v1 = fast_exp2(fmaf(acc[r + 1], e, off));
+    if constexpr (SUM) {
+      s0 = r == 0 ? v0 : s0 + v0;
+      s1 = r == 0 ? v1 : s1 + v1;
+    }
+    const int kb = r >> 3, w = (r & 7) >> 1;
+    if constexpr (PP == 1) {
+      W[0][kb][w] = pack_bf16_rne(v0, v1);
+    } else {
+      W[0][kb][w] = pack_hi16(v0, v1);
+      const float r0 = v0 - trunc_bf16(v0), r1 = v1 - trunc_bf16(v1);
+      if constexpr (PP == 2) {
+        W[1][kb][w] = pack_bf16_rne(r0, r1);
+      } else {
+        W[1][kb][w] = pack_hi16(r0, r1);
+        W[2][kb][w] = pack_bf16_rne(r0 - trunc_bf16(r0), r1 - trunc_bf16(r1));
+      }
     }
   }
-  return (s0 + s1) + (s2 + s3);
+#pragma unroll
+  for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) P[pp][kb] = __builtin_bit_cast(bf16x8, W[pp][kb]);
+  return s0 + s1;
 }
 
 // O[ob] += V[ob] x P over the products (pp, vp) of combined order below max(PP, VP).
@@ -272,25 +300,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
     for (int ob = 0; ob < NOB; ++ob) O[rb][ob] = f32x16{};
   }
 
-  auto tile_work = [&](const ColTile<NKB>& ct, const VTile<NOB, VP>& vt) {
-    f32x16 acc[RB];
-    tile_mfma<NKB, RB>(ct, B, Baug, acc);
+  // Plan entries of a scored tile, then their products with the tile's values.
+  auto entries_work = [&](const f32x16 (&acc)[RB], const VTile<NOB, VP>& vt) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const f32x16 a1[1] = {acc[rb]};
       const float off = pv_shift<1, NOB>(a1, e, mu[rb], S[rb], O[rb]);
       bf16x8 P[PP][2];
-      S[rb] += pv_probs<PP>(acc[rb], e, off, P);
+      if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb], e, off, P);
+      else pv_probs<PP, false>(acc[rb], e, off, P);  // the application never divides by S
       pv_mfma<NOB, PP, VP>(vt, P, O[rb]);
     }
   };
 
-  // Tiles past the range read the padding (masked columns, zero values) or the
-  // next range; the loop below reads at most one tile past its last one.
   const int ntiles = (j1 - j0 + 31) / 32;
   const int64_t t0 = j0 / 32;
   ColTile<NKB> c0, c1;
   VTile<NOB, VP> v0, v1;
+  // Each tile is scored, then used; loads run one tile ahead (the loop reads
+  // at most one tile past its last one: padding or the next range).
+  auto tile_work = [&](const ColTile<NKB>& ct, const VTile<NOB, VP>& vt) {
+    f32x16 acc[RB];
+    tile_mfma<NKB, RB>(ct, B, Baug, acc);
+    entries_work(acc, vt);
+  };
   load_tile<NKB>(c0, cols, p.bias_col, j0, li, half);
   load_vtile<NOB, VP>(v0, p, t0, ob0, lane);
   for (int t = 0; t < ntiles; t += 2) {
@@ -392,7 +425,8 @@ __global__ __launch_bounds__(kThreads, NOB >= 4 ? 1 : 2) void k_pv_gemm(const Pv
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           bf16x8 P[PP][2];
-          S[rb] += pv_probs<PP>(acc[rb][ct], e, off, P);
+          if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb][ct], e, off, P);
+          else pv_probs<PP, false>(acc[rb][ct], e, off, P);
 #pragma unroll
           for (int ob = 0; ob < NOB; ++ob) {
             VTile<1, VP> vt;
