@@ -27,8 +27,8 @@
 // P V, or one exact part of the bf16 points for the gradient).
 //
 // Stabilization: a running row maximum mu (acc units), raised only when a
-// tile's maximum exceeds it by more than 2^8 in value (lazy rescaling: terms
-// stay below 256, the accumulators are rescaled rarely). The maximum is taken
+// tile's maximum exceeds it by more than 2^16 in value (lazy rescaling: terms
+// stay below 2^16, the accumulators are rescaled rarely). The maximum is taken
 // over both halves of the wave, so one shift holds for a whole MFMA sum.
 #include "sk_internal.h"
 #include "sk_mfma.h"
@@ -44,7 +44,7 @@ namespace {
 using namespace dev;
 
 constexpr float kMuInit = -1.0e29f;  // no column seen yet (above any masked score)
-constexpr float kLazy = 8.0f;        // raise mu when a term would exceed 2^8
+constexpr float kLazy = 16.0f;       // raise mu when a term would exceed 2^16
 
 template <int NOB, int VP>
 struct VTile {
@@ -56,20 +56,21 @@ __device__ __forceinline__ const bf16x8* vfrag_at(const PvArgs& p, int64_t tile,
   return p.vfrag + ((((tile * p.nobt + ob) * vp_parts + vp) * 2 + kb) << 6);
 }
 
-// Lane l supplies value index l % 32 of each block; lanes past the value
-// width hold zeros in the fragments, so they skip the load (for k = 16 half
-// the bytes, for the d = 3 gradient 29 of 32).
+// Lane l supplies value index l % 32 of each block. Lanes past the value
+// width read the fragment of the first lane of their half instead of their
+// own (zero) one: the same cache lines as the live lanes, and no registers to
+// clear. What they hold only reaches output rows past the value width, which
+// are never stored.
 template <int NOB, int VP>
 __device__ __attribute__((always_inline)) inline void load_vtile(VTile<NOB, VP>& vt, const PvArgs& p,
                                                                  int64_t tile, int ob0, int lane) {
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob) {
-    const bool live = (ob0 + ob) * 32 + (lane & 31) < p.kv;
+    const int src = (ob0 + ob) * 32 + (lane & 31) < p.kv ? lane : (lane & 32);
 #pragma unroll
     for (int vp = 0; vp < VP; ++vp)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        vt.v[ob][vp][kb] = live ? vfrag_at(p, tile, ob0 + ob, VP, vp, kb)[lane] : bf16x8{};
+      for (int kb = 0; kb < 2; ++kb) vt.v[ob][vp][kb] = vfrag_at(p, tile, ob0 + ob, VP, vp, kb)[src];
   }
 }
 
@@ -118,7 +119,7 @@ __device__ __forceinline__ unsigned pack_bf16_rne(float a, float b) {
 }
 __device__ __forceinline__ float trunc_bf16(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFF0000u); }
 
-// Plan entries of one score tile (terms <= 2^8), their sum (SUM), and their
+// Plan entries of one score tile (terms <= 2^16), their sum (SUM), and their
 // bf16 parts as the B operands of two K blocks. All parts but the last are
 // truncations (v - part is then exact), the last is rounded to nearest: two
 // parts carry 16 bits (relative error <= 2^-16), three carry float32's 24.
