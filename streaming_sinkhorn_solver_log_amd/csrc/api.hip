@@ -96,6 +96,13 @@ bool debug_enabled() {
   return v;
 }
 
+// FLASHSK_FORCE_EXACT=1 (read on every solve): every shifted half-pass
+// recomputes its row blocks exactly, so tests can check that path.
+bool force_exact_enabled() {
+  const char* e = getenv("FLASHSK_FORCE_EXACT");
+  return e && e[0] == '1';
+}
+
 // ---------------------------------------------------------------- workspace layouts
 // Vector-ALU layout of one side: packed float32 points and per-point vectors.
 struct Side {
@@ -405,6 +412,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
   int cur = 0;
   hipError_t e;
   const bool scaled = dtype == SK_BF16;
+  const int force_exact = force_exact_enabled() ? 1 : 0;
   for (int t = 0; t < iters; ++t) {
     const int nxt = sym ? 1 - cur : cur;
     // Each side's first pass has no previous log-sum-exp to shift by: exact sweep.
@@ -426,6 +434,7 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pf.row_blocks = sp.f.row_blocks; pf.stages = sp.f.stages; pf.chunks = sp.f.chunks;
     pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
     pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
+    pf.force_exact = force_exact;
     if ((e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
     MfmaPassArgs pg = pf;
     pg.rows = L.ym.row_rec; pg.cols = L.xm.col_rec; pg.bias_col = L.xm.bias[cur];

@@ -332,7 +332,7 @@ __global__ __launch_bounds__((Geo<WRT, WCT, WGR>::kNT), (Geo<WRT, WCT, WGR>::kOc
     }
     if (threadIdx.x == 0) atomicExch(p.counters + rblk, 0u);
   }
-  if constexpr (SHIFTED) need_exact = __syncthreads_or(bad);
+  if constexpr (SHIFTED) need_exact = __syncthreads_or(bad || p.force_exact != 0);
   if (!need_exact) {
 #pragma unroll
     for (int u = 0; u < kRowsPerThread; ++u) {

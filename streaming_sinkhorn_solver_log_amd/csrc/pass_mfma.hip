@@ -461,6 +461,7 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             bad |= (row_base + rb * 32 + li < p.nr) && !(Ls[rb] >= kShiftedFloor);
+        bad |= p.force_exact != 0;
         need_exact = __syncthreads_or(bad);
       }
       if (!need_exact && half == 0) {
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
         Lr = Mt + fast_log2(St);
         bad = SHIFTED && !(St >= kShiftedFloor);
       }
-      if constexpr (SHIFTED) need_exact = __syncthreads_or(bad);
+      if constexpr (SHIFTED) need_exact = __syncthreads_or(bad || p.force_exact != 0);
       if (!need_exact && mine) dh = finish_row_mfma(p, i, Lr);
       if (threadIdx.x == 0) atomicExch(p.counters + r, 0u);
     }

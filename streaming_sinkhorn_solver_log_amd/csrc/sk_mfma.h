@@ -46,6 +46,9 @@ struct MfmaPassArgs {
   // the other side's next pass (may be null).
   const float* hcol;
   float* hout;
+  // Nonzero: every shifted row block takes the exact recomputation, as if its
+  // shifted sum had fallen below the floor (a test hook; normally 0).
+  int force_exact;
 };
 
 // Weighted sums over the columns of the half-pass scores, on the matrix cores:

@@ -98,6 +98,39 @@ def test_solve_matches_oracle(sk, key, n, m, iters):
     assert abs(float(cost) - cr) <= tol_rel(w) * max(abs(cr), 1e-30)
 
 
+FORCED_EXACT_CASES = [
+    (6, 3000, 2500),   # float32 d = 3, merged records (register-resident kernel)
+    (2, 1500, 2000),   # float32 d = 3, symmetric schedule (separate bias records)
+    (3, 2000, 3000),   # bf16 d = 64, float32 column biases
+    (7, 700, 900),     # bf16 d = 512, GEMM-tiled kernel
+    (4, 300, 700),     # float32 d = 512, GEMM-tiled kernel
+]
+
+
+@pytest.mark.parametrize("key,n,m", FORCED_EXACT_CASES)
+def test_forced_exact_fallback(sk, key, n, m, monkeypatch):
+    """The shifted sweep's exact recomputation of a row block (taken when its shifted
+    sum falls below the floor, which the benchmark workloads never reach), forced from
+    the host on every shifted pass: the solve still matches the oracle, and its rounding
+    differs from the shifted sweep's, so the recomputation really ran."""
+    w = W.CONFIGS[key].scaled(n, m, 4)
+    say(f"forced exact fallback cfg={key} n={n} m={m} d={w.d} {w.dtype} mode={w.mode}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f0, g0, _ = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    monkeypatch.setenv("FLASHSK_FORCE_EXACT", "1")
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("FLASHSK_FORCE_EXACT")
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    ef = np.abs(f.cpu().numpy().astype(np.float64) - fr).max()
+    eg = np.abs(g.cpu().numpy().astype(np.float64) - gr).max()
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} tol={tol_pot(w, fr):.3e}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
+    assert not (torch.equal(f, f0) and torch.equal(g, g0)), "the forced recomputation did not run"
+
+
 CUSTOM_DIMS = [("f32", 16), ("f32", 20), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7),
                ("f32", 64), ("bf16", 200), ("f32", 130)]
 
