@@ -174,9 +174,13 @@ Common carve_common(Carve& c, size_t part_f2, int n_counters, int64_t d) {
   return k;
 }
 
-size_t part_f2(const PassPlan& f, int64_t n, const PassPlan& g, int64_t m) {
-  const size_t pf = f.splits > 1 ? (size_t)f.splits * n : 0;
-  const size_t pg = g.splits > 1 ? (size_t)g.splits * m : 0;
+size_t part_f2_of(const PassPlan& pl, int64_t nr) { return pl.splits > 1 ? (size_t)pl.splits * nr : 0; }
+
+// Split partials of the two half-passes: shared when they run one after the
+// other, side by side when they share a launch (fused).
+size_t part_f2(const PassPlan& f, int64_t n, const PassPlan& g, int64_t m, bool fused = false) {
+  const size_t pf = part_f2_of(f, n), pg = part_f2_of(g, m);
+  if (fused) return pf + pg;
   return pf > pg ? pf : pg;
 }
 
@@ -184,7 +188,8 @@ struct SolvePlan {
   Path path;
   int nkb;      // matrix-core records: K blocks per record
   bool merged;  // register-resident pass with the bias chunk inside the column records
-  bool wide;    // GEMM-tiled pass with the 128 x 256 workgroup tile
+  bool wide;    // GEMM-tiled pass over float32 (six-part) records
+  bool fused;   // averaged schedule, register-resident pass: F and G in one launch
   PassPlan f, g;
 };
 
@@ -197,11 +202,16 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
   sp.nkb = 0;
   sp.merged = false;
   sp.wide = false;
+  sp.fused = false;
   if (sp.path == Path::Mfma) {
     sp.nkb = mfma_nkb(dtype, (int)d);
     sp.merged = alternating && mfma_merged(dtype, (int)d, sp.nkb);
-    sp.f = plan_mfma_pass(n, m, sp.nkb, sp.merged, dtype == SK_BF16);
-    sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged, dtype == SK_BF16);
+    // the averaged schedule's two half-passes read only the previous pair:
+    // one launch runs both, each on half of the resident workgroups
+    sp.fused = !alternating;
+    const int share = sp.fused ? 2 : 1;
+    sp.f = plan_mfma_pass(n, m, sp.nkb, sp.merged, dtype == SK_BF16, share);
+    sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged, dtype == SK_BF16, share);
   } else if (sp.path == Path::Gemm) {
     sp.nkb = gemm_nkb(dtype, (int)d);
     sp.wide = dtype == SK_F32;
@@ -221,6 +231,13 @@ struct SolveWs {
   size_t bytes;
 };
 
+// Row-block arrival counters: one set shared by passes that run one after the
+// other, one per pass when they share a launch.
+int solve_counters(const SolvePlan& sp) {
+  if (sp.fused) return sp.f.row_blocks + sp.g.row_blocks;
+  return sp.f.row_blocks > sp.g.row_blocks ? sp.f.row_blocks : sp.g.row_blocks;
+}
+
 SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_t d) {
   Carve c{static_cast<char*>(ws)};
   SolveWs L{};
@@ -231,8 +248,7 @@ SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_
     L.x = carve_side(c, n, valu_dp((int)d));
     L.y = carve_side(c, m, valu_dp((int)d));
   }
-  const int ncnt = sp.f.row_blocks > sp.g.row_blocks ? sp.f.row_blocks : sp.g.row_blocks;
-  L.c = carve_common(c, part_f2(sp.f, n, sp.g, m), ncnt, d);
+  L.c = carve_common(c, part_f2(sp.f, n, sp.g, m, sp.fused), solve_counters(sp), d);
   L.bytes = c.off;
   return L;
 }
@@ -435,7 +451,8 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pf.escale = mfma_escale(dtype, sc.c2); pf.bias_scale = mfma_bias_scale(dtype, sc.c2);
     pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps; pf.symmetric = sym;
     pf.force_exact = force_exact;
-    if ((e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
+    if (!sp.fused && (e = launch_pass(sp, pf, shifted, scaled, sp.f, s)) != hipSuccess)
+      return hip_fail(e, "f half-pass");
     MfmaPassArgs pg = pf;
     pg.rows = L.ym.row_rec; pg.cols = L.xm.col_rec; pg.bias_col = L.xm.bias[cur];
     pg.alpha = L.ym.alpha; pg.lw = L.ym.lw; pg.pot = g; pg.bias_out = L.ym.bias[nxt]; pg.bias_stride = 2;
@@ -449,7 +466,15 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
     pg.dmax_in = L.xm.dmax[cur]; pg.n_dmax_in = sp.f.row_blocks; pg.dmax_out = L.ym.dmax[nxt];
     pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
     pg.row_blocks = sp.g.row_blocks; pg.stages = sp.g.stages; pg.chunks = sp.g.chunks;
-    if ((e = launch_pass(sp, pg, shifted, scaled, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
+    if (sp.fused) {
+      // both passes in one launch, each with its own partials and counters
+      pg.part = L.c.part + part_f2_of(sp.f, n);
+      pg.counters = L.c.counters + sp.f.row_blocks;
+      if ((e = launch_lse_mfma_pair(pf, sp.f, pg, &sp.g, sp.nkb, shifted, scaled, sp.merged, s)) != hipSuccess)
+        return hip_fail(e, "f and g half-passes");
+    } else if ((e = launch_pass(sp, pg, shifted, scaled, sp.g, s)) != hipSuccess) {
+      return hip_fail(e, "g half-pass");
+    }
     cur = nxt;
   }
   return SK_OK;
@@ -539,7 +564,7 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   const bool warm = (flags & SK_WARM_START) != 0;
   const bool center = (flags & SK_NO_CENTER) == 0;
   const bool sym = (mode == SK_SYMMETRIC);
-  const int ncnt = sp.f.row_blocks > sp.g.row_blocks ? sp.f.row_blocks : sp.g.row_blocks;
+  const int ncnt = solve_counters(sp);
   const float* f_start = warm ? f : nullptr;
   const float* g_start = warm ? g : nullptr;
   float* f_zero = warm ? nullptr : f;

@@ -374,8 +374,14 @@ __device__ __forceinline__ void row_sums(const MfmaPassArgs& p, const float (&M)
 template <int NKB, bool MERGED>
 constexpr int kMinWaves = (MERGED || NKB == 1) ? 4 : (NKB <= 4 ? 3 : 2);
 
-template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED>
-__global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma(const MfmaPassArgs p) {
+// PAIR: two independent half-passes (the averaged schedule's F and G maps,
+// both of the previous pair) share one launch: workgroups below w0 run p0's
+// pass over its own plan, the others p1's. Otherwise p1 and w0 are unused.
+template <int NKB, int RB, bool SHIFTED, bool SCALED, bool MERGED, bool PAIR>
+__global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma(const MfmaPassArgs p0,
+                                                                                 const MfmaPassArgs p1, int w0) {
+  const bool second = PAIR && (int)blockIdx.x >= w0;
+  const MfmaPassArgs& p = second ? p1 : p0;
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
   static_assert(ROWS <= kThreads, "the partial merge finishes one row per thread");
@@ -398,7 +404,8 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int li = lane & 31;
-  const int64_t W = gridDim.x, w = blockIdx.x;
+  const int64_t W = PAIR ? (second ? (int64_t)gridDim.x - w0 : w0) : (int64_t)gridDim.x;
+  const int64_t w = second ? (int64_t)blockIdx.x - w0 : (int64_t)blockIdx.x;
   const int64_t T = p.stages;
   const UnitMap um{p.row_blocks, T, p.chunks > 0 ? p.chunks : 1, (int64_t)p.row_blocks * T, W};
   const int64_t v = (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;  // XCD-contiguous numbering
@@ -642,14 +649,31 @@ __global__ __launch_bounds__(256) void k_pad_columns(int64_t n, int64_t n_pad, i
 }
 
 template <int NKB, int RB, bool MERGED>
-hipError_t run_lse(const MfmaPassArgs& a, bool shifted, bool scaled, const PassPlan& pl, hipStream_t s) {
-  const dim3 grid(pl.grid);
+hipError_t run_lse(const MfmaPassArgs& a, const PassPlan& pl, const MfmaPassArgs& a1, const PassPlan* pl1,
+                   bool shifted, bool scaled, hipStream_t s) {
+  const int w0 = pl.grid;
+  const dim3 grid(pl.grid + (pl1 ? pl1->grid : 0));
+  if (pl1) {
+    // the averaged schedule, which never uses the merged layout
+    if constexpr (MERGED) {
+      return hipErrorInvalidValue;
+    } else {
+      if (shifted) {
+        if (scaled) k_lse_mfma<NKB, RB, true, true, false, true><<<grid, kThreads, 0, s>>>(a, a1, w0);
+        else k_lse_mfma<NKB, RB, true, false, false, true><<<grid, kThreads, 0, s>>>(a, a1, w0);
+      } else {
+        if (scaled) k_lse_mfma<NKB, RB, false, true, false, true><<<grid, kThreads, 0, s>>>(a, a1, w0);
+        else k_lse_mfma<NKB, RB, false, false, false, true><<<grid, kThreads, 0, s>>>(a, a1, w0);
+      }
+      return hipGetLastError();
+    }
+  }
   if (shifted) {
-    if (scaled) k_lse_mfma<NKB, RB, true, true, MERGED><<<grid, kThreads, 0, s>>>(a);
-    else k_lse_mfma<NKB, RB, true, false, MERGED><<<grid, kThreads, 0, s>>>(a);
+    if (scaled) k_lse_mfma<NKB, RB, true, true, MERGED, false><<<grid, kThreads, 0, s>>>(a, a, w0);
+    else k_lse_mfma<NKB, RB, true, false, MERGED, false><<<grid, kThreads, 0, s>>>(a, a, w0);
   } else {
-    if (scaled) k_lse_mfma<NKB, RB, false, true, MERGED><<<grid, kThreads, 0, s>>>(a);
-    else k_lse_mfma<NKB, RB, false, false, MERGED><<<grid, kThreads, 0, s>>>(a);
+    if (scaled) k_lse_mfma<NKB, RB, false, true, MERGED, false><<<grid, kThreads, 0, s>>>(a, a, w0);
+    else k_lse_mfma<NKB, RB, false, false, MERGED, false><<<grid, kThreads, 0, s>>>(a, a, w0);
   }
   return hipGetLastError();
 }
@@ -669,12 +693,12 @@ int resident_workgroups(int nkb, bool merged) {
     int per_cu = 0, cus = 0;
     hipError_t e = hipErrorInvalidValue;
     switch (nkb * 2 + (merged ? 1 : 0)) {
-      case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true, false>, kThreads, 0); break;
-      case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true, true>, kThreads, 0); break;
-      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false, false>, kThreads, 0); break;
-      case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false, true>, kThreads, 0); break;
-      case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<4, 2, true, true, false>, kThreads, 0); break;
-      case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<8, 1, true, true, false>, kThreads, 0); break;
+      case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true, false, false>, kThreads, 0); break;
+      case 3: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<1, 2, true, true, true, false>, kThreads, 0); break;
+      case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false, false, false>, kThreads, 0); break;
+      case 5: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<2, 2, true, false, true, false>, kThreads, 0); break;
+      case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<4, 2, true, true, false, false>, kThreads, 0); break;
+      case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_lse_mfma<8, 1, true, true, false, false>, kThreads, 0); break;
       default: break;
     }
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
@@ -707,13 +731,16 @@ bool mfma_merged(int dtype, int d, int nkb) {
 
 int64_t mfma_padded_count(int64_t n) { return (n + 31) / 32 * 32 + 5 * 32; }
 
-PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scaled) {
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scaled, int share) {
   PassPlan pl{};
   pl.rows_per_block = 4 * mfma_rb(nkb) * 32;
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
   pl.stages = (int)((nc + kStageCols - 1) / kStageCols);
   const int64_t units = (int64_t)pl.row_blocks * pl.stages;
+  // a pass sharing its launch with another gets 1/share of the resident
+  // workgroups (a multiple of 8, so both keep the XCD-contiguous numbering)
   int64_t grid = resident_workgroups(nkb, merged);
+  if (share > 1) grid = grid / share / 8 * 8 > 0 ? grid / share / 8 * 8 : 1;
   const int64_t min_units = 4;  // at least 512 columns of one row block per workgroup
   if (grid > units / min_units) grid = units / min_units;
   if (grid < 1) grid = 1;
@@ -737,18 +764,24 @@ PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scale
 
 hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, bool merged,
                            const PassPlan& pl, hipStream_t s) {
+  return launch_lse_mfma_pair(a, pl, a, nullptr, nkb, shifted, scaled, merged, s);
+}
+
+hipError_t launch_lse_mfma_pair(const MfmaPassArgs& a0, const PassPlan& pl0, const MfmaPassArgs& a1,
+                                const PassPlan* pl1, int nkb, bool shifted, bool scaled, bool merged,
+                                hipStream_t s) {
   if (merged) {
     switch (nkb) {
-      case 1: return run_lse<1, 2, true>(a, shifted, scaled, pl, s);
-      case 2: return run_lse<2, 2, true>(a, shifted, scaled, pl, s);
+      case 1: return run_lse<1, 2, true>(a0, pl0, a1, pl1, shifted, scaled, s);
+      case 2: return run_lse<2, 2, true>(a0, pl0, a1, pl1, shifted, scaled, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (nkb) {
-    case 1: return run_lse<1, 2, false>(a, shifted, scaled, pl, s);
-    case 2: return run_lse<2, 2, false>(a, shifted, scaled, pl, s);
-    case 4: return run_lse<4, 2, false>(a, shifted, scaled, pl, s);
-    case 8: return run_lse<8, 1, false>(a, shifted, scaled, pl, s);
+    case 1: return run_lse<1, 2, false>(a0, pl0, a1, pl1, shifted, scaled, s);
+    case 2: return run_lse<2, 2, false>(a0, pl0, a1, pl1, shifted, scaled, s);
+    case 4: return run_lse<4, 2, false>(a0, pl0, a1, pl1, shifted, scaled, s);
+    case 8: return run_lse<8, 1, false>(a0, pl0, a1, pl1, shifted, scaled, s);
     default: return hipErrorInvalidValue;
   }
 }

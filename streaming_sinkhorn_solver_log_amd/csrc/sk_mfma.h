@@ -103,9 +103,14 @@ bool mfma_merged(int dtype, int d, int nkb);
 int mfma_rb(int nkb);
 // Points per side including the masked padding columns (records, bias buffers).
 int64_t mfma_padded_count(int64_t n);
-PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scaled);
+// share > 1: the pass shares its launch with share - 1 others (launch_lse_mfma_pair).
+PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scaled, int share = 1);
 hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, bool merged,
                            const PassPlan& pl, hipStream_t s);
+// Two independent half-passes of the same kernel in one launch (pl1 null: one).
+hipError_t launch_lse_mfma_pair(const MfmaPassArgs& a0, const PassPlan& pl0, const MfmaPassArgs& a1,
+                                const PassPlan* pl1, int nkb, bool shifted, bool scaled, bool merged,
+                                hipStream_t s);
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
                             int nkb, bool merged, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,
