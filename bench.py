@@ -54,8 +54,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 _CSRC = os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "csrc")
 KERNEL_SOURCES = ["pass_mfma.hip", "sk_mfma_dev.h", "sk_mfma.h", "sk_sync.h", "sk_internal.h"]
 # shifted half-pass kernel of each workload (the launch that dominates a solve)
-HALF_PASS_KERNEL = {"embed_d64_50k_bf16": "k_lse_mfma<4, 2, true, true, false>",
-                    "mix8_d3_50k": "k_lse_mfma<2, 2, true, false, true>"}
+HALF_PASS_KERNEL = {"embed_d64_50k_bf16": "k_lse_mfma<4, 2, true, true, false, false>",
+                    "mix8_d3_50k": "k_lse_mfma<2, 2, true, false, true, false>"}
 
 
 def source_digest():
