@@ -150,6 +150,56 @@ def test_solve_other_dimensions(sk, dtype, d):
     assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
 
 
+# Every edge of the kernel choice by dimension: record widths of 1, 2, 4 and 8
+# MFMA K blocks (float32 points take six bf16 slots per coordinate, bf16 points
+# one), the merged layout's limit (float32 d <= 4, bf16 d <= 8, alternating
+# schedule), the first GEMM-tiled widths (float32 d = 22, bf16 d = 129) and the
+# largest supported d; ragged n and m; both schedules.
+BOUNDARY_DIMS = [
+    ("f32", 1, "alternating"), ("f32", 2, "symmetric"), ("f32", 4, "alternating"), ("f32", 5, "alternating"),
+    ("f32", 6, "symmetric"), ("f32", 10, "alternating"), ("f32", 11, "alternating"), ("f32", 21, "symmetric"),
+    ("f32", 22, "alternating"), ("f32", 300, "symmetric"),
+    ("bf16", 1, "alternating"), ("bf16", 8, "alternating"), ("bf16", 9, "symmetric"), ("bf16", 16, "alternating"),
+    ("bf16", 17, "alternating"), ("bf16", 33, "symmetric"), ("bf16", 65, "alternating"),
+    ("bf16", 128, "alternating"), ("bf16", 129, "symmetric"), ("bf16", 4096, "alternating"),
+]
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(BOUNDARY_DIMS)))
+def test_dimension_boundaries(sk, i, case):
+    """Solve, gradient and both applications at every dimension boundary of the
+    kernel choice, on ragged shapes, against the oracle (the applications and the
+    gradient with the GPU's potentials fed to both sides)."""
+    from dataclasses import replace
+    dtype, d, mode = case
+    n, m = 97 + (241 * i) % 900, 131 + (367 * i) % 1100
+    while n * m * d > 3e8:
+        n, m = n // 2 + 1, m // 2 + 1
+    w = replace(W.CONFIGS[4], d=d, dtype=dtype, eps=0.2, mode=mode, name=f"edge_d{d}_{dtype}").scaled(n, m, 3)
+    say(f"dimension edge {dtype} d={d} {mode} n={n} m={m}")
+    inp = W.make_inputs(w, k=5)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    fn, gn = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    ef, eg = np.abs(fn - fr).max(), np.abs(gn - gr).max()
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr), (ef, eg, tol_pot(w, fr))
+    assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
+    x64, y64 = inp.x64(), inp.y64()
+    grad = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()
+    ref = oracle.grad_x(x64, y64, inp.a, inp.b, gn, w.eps)
+    e_g = np.abs(grad - ref).max() / np.abs(ref).max()
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+    PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy()
+    ref1 = oracle.apply(x64, y64, inp.a, inp.b, fn, gn, w.eps, inp.V)
+    PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy()
+    ref2 = oracle.apply(x64, y64, inp.a, inp.b, fn, gn, w.eps, inp.U, transpose=True)
+    e1 = np.abs(PV - ref1).max() / np.abs(ref1).max()
+    e2 = np.abs(PtU - ref2).max() / np.abs(ref2).max()
+    say(f"  max|df|={ef:.2e} max|dg|={eg:.2e} grad {e_g:.2e} P.V {e1:.2e} P^T.U {e2:.2e}")
+    assert e_g <= tol_rel(w) and e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
 def test_solve_bf16_points_small_d(sk):
     w = bf16_variant(W.CONFIGS[1].scaled(900, 1100, 20))
     say("solve bf16 d=3")
