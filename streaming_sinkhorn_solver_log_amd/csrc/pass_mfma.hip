@@ -411,13 +411,13 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
   const int64_t v = (W % 8 == 0) ? (w % 8) * (W / 8) + w / 8 : w;  // XCD-contiguous numbering
   const int64_t u_end = um.begin(v + 1);
 
-  float dmax = 0.0f;
-  if constexpr (SHIFTED) {
-    // largest change of a column bias since this side's previous pass
-    float dm = -INFINITY;
+  // Largest change of a column bias since this side's previous pass: the
+  // loads start here, the workgroup maximum is taken after the first row
+  // segment's loads are issued (their latencies overlap).
+  float dmax = 0.0f, dm = -INFINITY;
+  bool dmax_ready = !SHIFTED;
+  if constexpr (SHIFTED)
     for (int q = threadIdx.x; q < p.n_dmax_in; q += kThreads) dm = fmaxf(dm, p.dmax_in[q]);
-    dmax = block_max(dm, red);
-  }
 
   for (int64_t u = um.begin(v); u < u_end;) {
     const int64_t c = um.chunk_of(u);
@@ -431,15 +431,23 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
     const int row_base = r * ROWS + wave * (RB * 32);
 
     bf16x8 B[RB][NKB], Baug[RB];
-    float M[RB], S[RB], shift_row[RB], off[RB];
+    float M[RB], S[RB], shift_row[RB], off[RB], lin[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int i = min(row_base + rb * 32 + li, p.nr - 1);
       const bf16x8* rec = reinterpret_cast<const bf16x8*>(rows + (int64_t)i * RSB) + half * NKB;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) B[rb][kb] = rec[kb];
+      if constexpr (SHIFTED) lin[rb] = p.Lin[i];
+    }
+    if (!dmax_ready) {  // the workgroup's first segment (uniform)
+      dmax = block_max(dm, red);
+      dmax_ready = true;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       if constexpr (SHIFTED) {
-        shift_row[rb] = p.Lin[i] + dmax;  // log2 units
+        shift_row[rb] = lin[rb] + dmax;  // log2 units
         if constexpr (!FB) set_row_aug(B[rb], Baug[rb], -shift_row[rb] / p.escale, half);
         off[rb] = -shift_row[rb];
         M[rb] = 0.0f;
@@ -500,7 +508,9 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
       bool bad = false;
       const int i = r * ROWS + (int)threadIdx.x;
       const bool mine = (int)threadIdx.x < ROWS && i < p.nr;
+      RowIn rin{};
       if (mine) {
+        rin = load_row_in(p, i);
         float Mt = -INFINITY;
         for (int s2 = 0; s2 < contributors; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
         const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
@@ -514,7 +524,7 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
         bad = SHIFTED && !(St >= kShiftedFloor);
       }
       if constexpr (SHIFTED) need_exact = __syncthreads_or(bad || p.force_exact != 0);
-      if (!need_exact && mine) dh = finish_row_mfma(p, i, Lr);
+      if (!need_exact && mine) dh = finish_row_mfma(p, i, Lr, rin);
       if (threadIdx.x == 0) atomicExch(p.counters + r, 0u);
     }
 

@@ -64,20 +64,31 @@ __device__ __forceinline__ bf16x8 row_aug(int half, float neg_m) {
   return r;
 }
 
+// What the potential update of row i reads besides its log2-sum-exp; loaded
+// ahead of the partial merge, so that the two latencies overlap.
+struct RowIn {
+  float alpha, lw, pot, hval;
+};
+__device__ __forceinline__ RowIn load_row_in(const MfmaPassArgs& p, int i) {
+  return RowIn{p.alpha[i], p.lw[i], p.symmetric ? p.pot[i] : 0.0f, p.hval_in[i]};
+}
+
 // Potential update of row i from its log2-sum-exp L; returns the change of the
 // row's bias (log2 units) since the previous pass of this side.
-__device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, float L) {
-  const float al = p.alpha[i];
-  float v = fmaf(p.neg_eps_ln2, L, al);
-  if (p.symmetric) v = 0.5f * (p.pot[i] + v);
+__device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, float L, const RowIn& r) {
+  float v = fmaf(p.neg_eps_ln2, L, r.alpha);
+  if (p.symmetric) v = 0.5f * (r.pot + v);
   p.pot[i] = v;
-  const float h = fmaf(kLog2e, p.lw[i], (v - al) * p.log2e_over_eps);
+  const float h = fmaf(kLog2e, r.lw, (v - r.alpha) * p.log2e_over_eps);
   write_bias_chunk(p.bias_out + (int64_t)i * p.bias_stride, h * p.bias_scale);
   if (p.hout) p.hout[i] = masked_bias(h * p.bias_scale);
-  const float dh = h - p.hval_in[i];
+  const float dh = h - r.hval;
   p.hval_out[i] = h;
   p.Lout[i] = L;
   return dh;
+}
+__device__ __forceinline__ float finish_row_mfma(const MfmaPassArgs& p, int i, float L) {
+  return finish_row_mfma(p, i, L, load_row_in(p, i));
 }
 
 // max(a, b, c): one v_maximum3_f32 (IEEE maximum: a NaN operand gives NaN, so
