@@ -196,7 +196,7 @@ __device__ __forceinline__ void pv_store(const PvArgs& p, int i, int cc, float m
 // otherwise the partials (mu, S, T) go to the split buffer and the last
 // workgroup of the row block merges them in split order (bitwise repeatable).
 // Lanes of inactive waves hold nothing but take part in the barriers.
-template <int RB, int NOB>
+template <int RB, int NOB, int NT = kThreads>
 __device__ __attribute__((always_inline)) inline void pv_finish(
     const PvArgs& p, bool active, int row_base, int rows_per_wg, const f32x16 (&O)[RB][NOB],
     const float (&mu)[RB], const float (&S)[RB], int li, int half) {
@@ -244,7 +244,7 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
   unsigned* counter = p.counters + (int64_t)z * p.row_blocks + blockIdx.x;
   if (!arrive_last(counter, p.splits)) return;
   const int row0 = blockIdx.x * rows_per_wg;
-  for (int q = threadIdx.x; q < rows_per_wg * CW; q += kThreads) {
+  for (int q = threadIdx.x; q < rows_per_wg * CW; q += NT) {
     const int i = row0 + q / CW;
     const int c = q % CW;
     if (i >= p.nr || cbase + c >= p.kv) continue;
@@ -488,6 +488,145 @@ __global__ __launch_bounds__(kThreads, NOB >= 4 ? 1 : 2) void k_pv_gemm(const Pv
   pv_finish<2, NOB>(p, wc == 0, r0 + wr * 64, kGRows, O, mu, S, li, half);
 }
 
+// GEMM-tiled variant for one value block (applications with k <= 32): the
+// 256 x 256 workgroup tile of 8 waves of the large-d half-pass (4 row waves x
+// 2 column waves, each 64 rows x 128 columns), K streamed through LDS; each
+// column block's scores feed the value products of the wave's rows, and the
+// two column waves of a row group merge their partials through LDS at the end.
+using PvGeo = Geo<2, 4, 4>;
+
+template <int PP, int VP>
+__global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int nkb, int col_last) {
+  using G = PvGeo;
+  constexpr int WRT = 2, WCT = 4, kWaveRows = 64;
+  __shared__ __attribute__((aligned(16))) TileLds<G> lds;
+  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
+  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const int ob0 = blockIdx.z;
+  const int j0 = blockIdx.y * p.cols_per_split;
+  const int j1 = min(p.nc, j0 + p.cols_per_split);
+  const int r0 = blockIdx.x * G::kRows;
+  const float e = p.escale;
+
+  bf16x8 Baug[WRT];
+  float mu[WRT], S[WRT];
+  f32x16 O[WRT][1];
+#pragma unroll
+  for (int rb = 0; rb < WRT; ++rb) {
+    Baug[rb] = row_aug(half, 0.0f);
+    mu[rb] = kMuInit;
+    S[rb] = 0.0f;
+    O[rb][0] = f32x16{};
+  }
+
+  const int nkc = nkb / kGKb;
+  const int nblocks = (j1 - j0 + G::kCols - 1) / G::kCols;
+  const int nstages = nblocks * nkc;
+  auto load_stage = [&](TileRegs<G>& g, int st) {
+    tile_load<G>(g, rows, cols, nkb, p.nr, col_last, r0, j0 + (st / nkc) * G::kCols, st % nkc);
+  };
+  TileRegs<G> g;
+  load_stage(g, 0);
+  tile_store<G>(g, lds, 0);
+  if (nstages > 1) load_stage(g, 1);
+  __syncthreads();
+  f32x16 acc[WRT][WCT];
+  for (int st = 0; st < nstages; ++st) {
+    const int blk = st / nkc, kc = st % nkc;
+    const int buf = st & 1;
+    if (kc == 0) {
+#pragma unroll
+      for (int rb = 0; rb < WRT; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) acc[rb][ct] = f32x16{};
+    }
+#pragma unroll
+    for (int kb = 0; kb < kGKb; ++kb) {
+      bf16x8 A[WCT], B[WRT];
+#pragma unroll
+      for (int ct = 0; ct < WCT; ++ct)
+        A[ct] = *reinterpret_cast<const bf16x8*>(
+            &lds.cols[buf][(wc * (G::kCols / 2) + ct * 32 + li) * kGRow + half * 64 + kb * 16]);
+#pragma unroll
+      for (int rb = 0; rb < WRT; ++rb)
+        B[rb] = *reinterpret_cast<const bf16x8*>(
+            &lds.rows[buf][(wr * kWaveRows + rb * 32 + li) * kGRow + half * 64 + kb * 16]);
+#pragma unroll
+      for (int rb = 0; rb < WRT; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct)
+          acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ct], B[rb], acc[rb][ct], 0, 0, 0);
+    }
+    // the next stage's operands go to LDS before the epilogue, so their
+    // staging registers are free during it
+    if (st + 1 < nstages) tile_store<G>(g, lds, buf ^ 1);
+    if (kc == nkc - 1) {
+      const int cb = j0 + blk * G::kCols + wc * (G::kCols / 2);
+#pragma unroll
+      for (int ct = 0; ct < WCT; ++ct) {
+        const bf16x8 Aaug = p.bias_col[2 * (int64_t)min(cb + ct * 32 + li, col_last) + half];
+#pragma unroll
+        for (int rb = 0; rb < WRT; ++rb)
+          acc[rb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aaug, Baug[rb], acc[rb][ct], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < WRT; ++rb) {
+        const float off = pv_shift<WCT, 1>(acc[rb], e, mu[rb], S[rb], O[rb]);
+#pragma unroll
+        for (int ct = 0; ct < WCT; ++ct) {
+          bf16x8 P[PP][2];
+          if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb][ct], e, off, P);
+          else pv_probs<PP, false>(acc[rb][ct], e, off, P);
+          // a column block can overhang the padded columns by up to 7 tiles:
+          // those columns are masked, so any zero-valued tile serves, here
+          // the last padded one
+          VTile<1, VP> vt;
+          load_vtile<1, VP>(vt, p, min((cb >> 5) + ct, col_last >> 5), ob0, lane);
+          pv_mfma<1, PP, VP>(vt, P, O[rb]);
+        }
+      }
+    }
+    if (st + 2 < nstages) load_stage(g, st + 2);
+    __syncthreads();
+  }
+
+  // Column wave 1 hands (mu, S, O) to column wave 0 of the same rows (same
+  // lane layout) through the staging buffers, free after the last barrier.
+  constexpr int PER = WRT * (2 + 16);  // floats per lane
+  static_assert(G::kNT / 128 * PER * 64 * 4 <= (int)sizeof(TileLds<G>), "merge area exceeds the staging buffers");
+  float* xl = reinterpret_cast<float*>(&lds) + wr * PER * 64 + lane;
+  if (wc == 1) {
+#pragma unroll
+    for (int rb = 0; rb < WRT; ++rb) {
+      xl[(rb * 18) * 64] = mu[rb];
+      xl[(rb * 18 + 1) * 64] = S[rb];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xl[(rb * 18 + 2 + r) * 64] = O[rb][0][r];
+    }
+  }
+  __syncthreads();
+  if (wc == 0) {
+#pragma unroll
+    for (int rb = 0; rb < WRT; ++rb) {
+      const float mo = xl[(rb * 18) * 64];
+      const float so = xl[(rb * 18 + 1) * 64];
+      const float mt = fmaxf(mu[rb], mo);
+      const float f0 = fast_exp2(e * (mu[rb] - mt)), f1 = fast_exp2(e * (mo - mt));
+      S[rb] = S[rb] * f0 + so * f1;
+      mu[rb] = mt;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[rb][0][r] = O[rb][0][r] * f0 + xl[(rb * 18 + 2 + r) * 64] * f1;
+    }
+  }
+  __syncthreads();
+  pv_finish<WRT, 1, G::kNT>(p, wc == 0, r0 + wr * kWaveRows, G::kRows, O, mu, S, li, half);
+}
+
 // Value fragment (tile t, value block ob, part vp, K block kb) in lane l
 // (h = l / 32): the values of index 32 ob + l % 32 at the eight points
 // 32 t + 16 kb + 8 (e / 4) + 4 h + e % 4, e = 0..7 -- the column order of a
@@ -551,6 +690,13 @@ hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStr
   return hipErrorInvalidValue;
 }
 
+hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, const dim3& grid, hipStream_t s) {
+  const int col_last = (int)(mfma_padded_count(a.nc) - 1);
+  if (pp == 3 && vp == 3) k_pv_gemm8<3, 3><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 template <int NOB>
 hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& grid, hipStream_t s) {
   if (pp == 3 && vp == 3) k_pv_gemm<NOB, 3, 3><<<grid, kThreads, 0, s>>>(a, nkb);
@@ -608,16 +754,48 @@ int pv_gemm_resident(int nob) {
 }
 }  // namespace
 
+namespace {
+bool pv_tile8(bool gemm, int nob, int vp) { return gemm && nob == 1 && vp == 3; }
+
+// Resident workgroups of the 8-wave GEMM-tiled kernel (per device, computed once).
+int pv_gemm8_resident() {
+  constexpr int kDevices = 16;
+  static std::atomic<int> cached[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev] : nullptr;
+  int v = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (v == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm8<3, 3>, PvGeo::kNT, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    v = per_cu * cus;
+    if (slot) slot->store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+}  // namespace
+
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks) {
   PassPlan pl{};
-  pl.rows_per_block = gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32;
+  // GEMM-tiled with one value block and float32 (three-part) values: the
+  // 256 x 256 tile of 8 waves (k_pv_gemm8). Its epilogue spills, which only
+  // the long K loop of the six-part float32 records amortizes (d = 512:
+  // P V 10.1 -> 6.2 ms); bf16 records stay on the 128 x 128 tile (d = 512:
+  // 1.0 ms there, 1.3 ms on the larger one).
+  const bool tile8 = pv_tile8(gemm, nob, vp);
+  pl.rows_per_block = tile8 ? PvGeo::kRows : (gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32);
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
   if (gemm) {
     int64_t max_splits = nc / 512 > 1 ? nc / 512 : 1;
     if (max_splits > 64) max_splits = 64;
     int64_t cps = 0;
     const int64_t units = (int64_t)pl.row_blocks * (nchunks > 0 ? nchunks : 1);
-    pl.splits = (int)round_filling_splits(units, nc, kGCols, max_splits, pv_gemm_resident(nob), cps);
+    pl.splits = (int)round_filling_splits(units, nc, tile8 ? PvGeo::kCols : kGCols, max_splits,
+                                          tile8 ? pv_gemm8_resident() : pv_gemm_resident(nob), cps);
     pl.cols_per_split = (int)cps;
     return pl;
   }
@@ -640,6 +818,7 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
                      const PassPlan& pl, hipStream_t s) {
   const dim3 grid(pl.row_blocks, pl.splits, a.nchunks);
   if (gemm) {
+    if (pv_tile8(gemm, nob, vp)) return run_pv_gemm8(a, nkb, pp, vp, grid, s);
     if (nob == 1) return run_pv_gemm<1>(a, nkb, pp, vp, grid, s);
     if (nob == 2) return run_pv_gemm<2>(a, nkb, pp, vp, grid, s);
     if (nob == 4) return run_pv_gemm<4>(a, nkb, pp, vp, grid, s);

@@ -53,5 +53,74 @@ __device__ __attribute__((always_inline)) inline void gemm_store(const GemmRegs&
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256 tiles of 8 waves
+// Workgroup tile: WGR x 2 waves (row waves x column waves), each wave
+// WRT x WCT accumulator tiles of 32 x 32, i.e. 32 WRT WGR rows and 64 WCT
+// columns per workgroup.
+template <int WRT, int WCT, int WGR>
+struct Geo {
+  static constexpr int kWRT = WRT, kWCT = WCT, kWGR = WGR;
+  static constexpr int kNT = 128 * WGR;  // threads
+  static constexpr int kRows = 32 * WRT * WGR;
+  static constexpr int kCols = 64 * WCT;
+  static constexpr int kRowLoads = kRows * 8 / kNT;  // 16-byte chunks per thread per stage
+  static constexpr int kColLoads = kCols * 8 / kNT;
+  static constexpr int kOcc = (WRT * WCT * WGR > 8) ? 1 : 2;  // workgroups per CU
+  static_assert(kRows * 8 % kNT == 0 && kCols * 8 % kNT == 0, "stage loads split evenly");
+};
+
+template <class G>
+struct TileLds {
+  unsigned char rows[2][G::kRows * kGRow];
+  unsigned char cols[2][G::kCols * kGRow];
+};
+
+template <class G>
+struct TileRegs {
+  u32x4 r[G::kRowLoads];
+  u32x4 c[G::kColLoads];
+};
+
+// Stage (kc) of the K dimension for rows [r0, r0 + kRows) and columns
+// [c0, c0 + kCols): per record, 4 x 16 bytes in each half, record bytes
+// [h * NKB * 16 + kc * 64, +64). Row indices clamp to the last row, column
+// indices to the last padded (masked) column.
+template <class G>
+__device__ __attribute__((always_inline)) inline void tile_load(
+    TileRegs<G>& g, const unsigned char* __restrict__ rows, const unsigned char* __restrict__ cols,
+    int nkb, int nr, int col_last, int r0, int c0, int kc) {
+  const int64_t rsb = (int64_t)nkb * 32;
+#pragma unroll
+  for (int q = 0; q < G::kRowLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;  // record (ch >> 3), half ((ch >> 2) & 1), part (ch & 3)
+    const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+    const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
+    g.r[q] = *reinterpret_cast<const u32x4*>(rows + (int64_t)min(r0 + rec, nr - 1) * rsb + off);
+  }
+#pragma unroll
+  for (int q = 0; q < G::kColLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;
+    const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+    const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
+    g.c[q] = *reinterpret_cast<const u32x4*>(cols + (int64_t)min(c0 + rec, col_last) * rsb + off);
+  }
+}
+
+template <class G>
+__device__ __attribute__((always_inline)) inline void tile_store(const TileRegs<G>& g, TileLds<G>& L, int buf) {
+#pragma unroll
+  for (int q = 0; q < G::kRowLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;
+    const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+    *reinterpret_cast<u32x4*>(&L.rows[buf][rec * kGRow + hh * 64 + part * 16]) = g.r[q];
+  }
+#pragma unroll
+  for (int q = 0; q < G::kColLoads; ++q) {
+    const int ch = threadIdx.x + q * G::kNT;
+    const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+    *reinterpret_cast<u32x4*>(&L.cols[buf][rec * kGRow + hh * 64 + part * 16]) = g.c[q];
+  }
+}
+
 }  // namespace dev
 }  // namespace sk
