@@ -344,6 +344,7 @@ APPLY_CASES = [
     (3, 500, 3000, 7),
     (5, 300, 1300, 16),  # bf16 d = 1024, GEMM-tiled
     (4, 600, 700, 40),   # float32 d = 512, two value blocks
+    (4, 300, 1300, 16),  # float32 d = 512, 8-wave tile: the last column block overhangs the padding
 ]
 
 
