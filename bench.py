@@ -44,7 +44,7 @@ BF16_MFMA_PEAK = 2.5e15             # dense bf16 MFMA flop/s
 F32_MFMA_PEAK = 157.3e12
 HBM_PEAK = 8.0e12
 
-WORKLOADS = {w.name: key for key, w in W.CONFIGS.items()}
+WORKLOADS = {w.name: key for key, w in W.CASES.items()}
 
 # HBM traffic of the half-pass kernels, from rocprofv3 FETCH_SIZE / WRITE_SIZE
 # runs scaled by the same counters' reading for a device copy of known size
@@ -133,7 +133,7 @@ def _dev_points(arr, dtype, torch, dev):
 
 class Case:
     def __init__(self, key, torch, sk, dev, k=16):
-        self.w = w = W.CONFIGS[key]
+        self.w = w = W.CASES[key]
         inp = W.make_inputs(w, k=k)
         self.inp = inp
         self.x = _dev_points(inp.x, w.dtype, torch, dev)
@@ -562,7 +562,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

@@ -52,7 +52,7 @@ extern "C" {
 /* return codes */
 #define SK_OK 0
 #define SK_ERR_INVALID_ARG (-1) /* a size, pointer, eps, mode or flag is invalid  */
-#define SK_ERR_UNSUPPORTED (-2) /* a valid combination this build does not handle */
+#define SK_ERR_UNSUPPORTED (-2) /* a valid combination the library does not handle */
 #define SK_ERR_WORKSPACE (-3)   /* ws is NULL, misaligned or too small            */
 #define SK_ERR_HIP (-4)         /* the HIP runtime reported an error              */
 

@@ -69,7 +69,7 @@ int check_common(const void* x, const void* y, int dtype, int64_t n, int64_t m, 
   if (!aligned(x, 16) || !aligned(y, 16)) return fail(SK_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
   if (n > kMaxRows || m > kMaxRows || n * d > ((int64_t)1 << 31) - 1 || m * d > ((int64_t)1 << 31) - 1)
     return fail(SK_ERR_UNSUPPORTED, "n*d and m*d must be below 2^31");
-  if (path == Path::None) return fail(SK_ERR_UNSUPPORTED, "dimension d=%lld is not supported by this build", (long long)d);
+  if (path == Path::None) return fail(SK_ERR_UNSUPPORTED, "dimension d=%lld is not supported by this library", (long long)d);
   return SK_OK;
 }
 

@@ -77,8 +77,8 @@ DivWs layout_div(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
 
 // ---------------------------------------------------------------- run to tolerance
 // Marginal error of a pair (f0, g0) from the next iteration (review,
-// Weaknesses: iterations to convergence grow sharply at small eps; the
-// survey's next step is a streamed marginal check). F(g0) normalizes the
+// Weaknesses: iterations to convergence grow sharply at small eps, so a
+// solve stops on a streamed marginal check). F(g0) normalizes the
 // rows exactly, so the row sums of P(f0, g0) are a_i exp((f0_i - F(g0)_i)/eps)
 // and ||P 1 - a||_1 = sum_i a_i |expm1((f0_i - F(g0)_i)/eps)|. The next
 // iteration computes F(g0): f1 itself (alternating) or 2 f1 - f0 (averaged,
@@ -616,7 +616,7 @@ int sk_sinkhorn_divergence(const void* x, const void* y, int dtype, int64_t n, i
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
   if (flags & ~SK_NO_CENTER) return fail(SK_ERR_INVALID_ARG, "flags 0x%x: only SK_NO_CENTER applies", flags);
   if ((grad_x || grad_y) && aux_path(dtype, d) == Path::None)
-    return fail(SK_ERR_UNSUPPORTED, "gradients at d=%lld are not supported by this build", (long long)d);
+    return fail(SK_ERR_UNSUPPORTED, "gradients at d=%lld are not supported by this library", (long long)d);
   const DivWs L = layout_div(ws, dtype, n, m, d);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -21,7 +21,7 @@ CASES = [(1, 40, 33, 6), (2, 37, 45, 5), (3, 24, 20, 4)]
 def compute():
     out = []
     for key, n, m, iters in CASES:
-        w = W.CONFIGS[key].scaled(n, m, iters)
+        w = W.CASES[key].scaled(n, m, iters)
         inp = W.make_inputs(w)
         f, g, cost = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, iters, w.mode)
         grad = oracle.grad_x(inp.x64(), inp.y64(), inp.a, inp.b, g, w.eps)

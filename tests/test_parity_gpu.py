@@ -84,7 +84,7 @@ SOLVE_CASES = [
 
 @pytest.mark.parametrize("key,n,m,iters", SOLVE_CASES)
 def test_solve_matches_oracle(sk, key, n, m, iters):
-    w = W.CONFIGS[key].scaled(n, m, iters)
+    w = W.CASES[key].scaled(n, m, iters)
     say(f"solve cfg={key} n={n} m={m} d={w.d} iters={w.iters} mode={w.mode} eps={w.eps}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -113,7 +113,7 @@ def test_forced_exact_fallback(sk, key, n, m, monkeypatch):
     sum falls below the floor, which the benchmark workloads never reach), forced from
     the host on every shifted pass: the solve still matches the oracle, and its rounding
     differs from the shifted sweep's, so the recomputation really ran."""
-    w = W.CONFIGS[key].scaled(n, m, 4)
+    w = W.CASES[key].scaled(n, m, 4)
     say(f"forced exact fallback cfg={key} n={n} m={m} d={w.d} {w.dtype} mode={w.mode}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -138,7 +138,7 @@ CUSTOM_DIMS = [("f32", 16), ("f32", 20), ("f32", 32), ("bf16", 100), ("bf16", 8)
 @pytest.mark.parametrize("dtype,d", CUSTOM_DIMS)
 def test_solve_other_dimensions(sk, dtype, d):
     from dataclasses import replace
-    w = replace(W.CONFIGS[4], d=d, dtype=dtype, eps=0.2, name=f"gauss_d{d}_{dtype}").scaled(900, 1100, 10)
+    w = replace(W.CASES[4], d=d, dtype=dtype, eps=0.2, name=f"gauss_d{d}_{dtype}").scaled(900, 1100, 10)
     say(f"solve d={d} {dtype}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -175,7 +175,7 @@ def test_dimension_boundaries(sk, i, case):
     n, m = 97 + (241 * i) % 900, 131 + (367 * i) % 1100
     while n * m * d > 3e8:
         n, m = n // 2 + 1, m // 2 + 1
-    w = replace(W.CONFIGS[4], d=d, dtype=dtype, eps=0.2, mode=mode, name=f"edge_d{d}_{dtype}").scaled(n, m, 3)
+    w = replace(W.CASES[4], d=d, dtype=dtype, eps=0.2, mode=mode, name=f"edge_d{d}_{dtype}").scaled(n, m, 3)
     say(f"dimension edge {dtype} d={d} {mode} n={n} m={m}")
     inp = W.make_inputs(w, k=5)
     x, y, a, b = dev(inp)
@@ -201,7 +201,7 @@ def test_dimension_boundaries(sk, i, case):
 
 
 def test_solve_bf16_points_small_d(sk):
-    w = bf16_variant(W.CONFIGS[1].scaled(900, 1100, 20))
+    w = bf16_variant(W.CASES[1].scaled(900, 1100, 20))
     say("solve bf16 d=3")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -213,7 +213,7 @@ def test_solve_bf16_points_small_d(sk):
 
 
 def test_zero_iterations_and_warm_start_resume(sk):
-    w = W.CONFIGS[6].scaled(1300, 1200, 12)
+    w = W.CASES[6].scaled(1300, 1200, 12)
     say("iters=0 and warm-start resume")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -239,11 +239,11 @@ def test_zero_iterations_and_warm_start_resume(sk):
 def _zero_weight_workload(case):
     from dataclasses import replace
     if case == "f32_d3":
-        return W.CONFIGS[1].scaled(600, 500, 10), None
+        return W.CASES[1].scaled(600, 500, 10), None
     if case in ("bf16_d64", "bf16_d64_symmetric"):  # float32 column biases, four K blocks
-        return W.CONFIGS[3].scaled(700, 611, 10), ("symmetric" if case.endswith("symmetric") else None)
+        return W.CASES[3].scaled(700, 611, 10), ("symmetric" if case.endswith("symmetric") else None)
     # bf16_d16: float32 column biases, one K block
-    return replace(W.CONFIGS[4], d=16, dtype="bf16", eps=0.2, name="gauss_d16_bf16").scaled(650, 555, 10), None
+    return replace(W.CASES[4], d=16, dtype="bf16", eps=0.2, name="gauss_d16_bf16").scaled(650, 555, 10), None
 
 
 @pytest.mark.parametrize("case", ["f32_d3", "bf16_d64", "bf16_d64_symmetric", "bf16_d16"])
@@ -265,7 +265,7 @@ def test_zero_weights(sk, case):
 
 
 def test_repeatable_and_swap_symmetric(sk):
-    w = W.CONFIGS[2].scaled(1200, 1200, 15)
+    w = W.CASES[2].scaled(1200, 1200, 15)
     say("bitwise repeatability, swap symmetry")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -280,7 +280,7 @@ def test_repeatable_and_swap_symmetric(sk):
 def test_bitwise_repeatable_all_kernels(sk, key, n, m):
     """Every kernel family (register-resident, LDS-staged, GEMM-tiled half-pass; gradient;
     transport application) gives bitwise identical results on repeated calls."""
-    w = W.CONFIGS[key].scaled(n, m, 4)
+    w = W.CASES[key].scaled(n, m, 4)
     say(f"repeatability cfg={key} n={n} m={m} d={w.d} {w.dtype}")
     inp = W.make_inputs(w, k=16)
     x, y, a, b = dev(inp)
@@ -299,7 +299,7 @@ def test_bitwise_repeatable_all_kernels(sk, key, n, m):
 
 
 def test_translation_invariance(sk):
-    w = W.CONFIGS[1].scaled(800, 900, 10)
+    w = W.CASES[1].scaled(800, 900, 10)
     say("translation invariance")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -323,7 +323,7 @@ GRAD_CASES = [
 
 @pytest.mark.parametrize("key,n,m", GRAD_CASES)
 def test_grad_matches_oracle(sk, key, n, m):
-    w = W.CONFIGS[key].scaled(n, m, 10)
+    w = W.CASES[key].scaled(n, m, 10)
     say(f"grad cfg={key} n={n} m={m}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -350,7 +350,7 @@ APPLY_CASES = [
 
 @pytest.mark.parametrize("key,n,m,k", APPLY_CASES)
 def test_apply_matches_oracle(sk, key, n, m, k):
-    w = W.CONFIGS[key].scaled(n, m, 10)
+    w = W.CASES[key].scaled(n, m, 10)
     say(f"apply cfg={key} n={n} m={m} k={k}")
     inp = W.make_inputs(w, k=k)
     x, y, a, b = dev(inp)
@@ -373,7 +373,7 @@ AUX_DIMS = [("f32", 16), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7), ("
 @pytest.mark.parametrize("dtype,d", AUX_DIMS)
 def test_grad_apply_other_dimensions(sk, dtype, d):
     from dataclasses import replace
-    w = replace(W.CONFIGS[4], d=d, dtype=dtype, eps=0.2, name=f"gauss_d{d}_{dtype}").scaled(700, 1300, 5)
+    w = replace(W.CASES[4], d=d, dtype=dtype, eps=0.2, name=f"gauss_d{d}_{dtype}").scaled(700, 1300, 5)
     say(f"grad/apply d={d} {dtype}")
     inp = W.make_inputs(w, k=40)
     x, y, a, b = dev(inp)
@@ -396,7 +396,7 @@ def test_grad_apply_other_dimensions(sk, dtype, d):
 @pytest.mark.parametrize("key,scale", [(1, 0.5), (3, 0.3), (4, 2.0)])
 def test_apply_arbitrary_potentials(sk, key, scale):
     """Plan entries spread over many orders of magnitude (potentials not from a solve)."""
-    w = W.CONFIGS[key].scaled(700, 900, 1)
+    w = W.CASES[key].scaled(700, 900, 1)
     say(f"apply cfg={key} arbitrary potentials scale={scale}")
     inp = W.make_inputs(w, k=16)
     x, y, a, b = dev(inp)
@@ -434,7 +434,7 @@ SPLIT_SHAPES = [
 def test_work_split_regimes(sk, key, n, m):
     """Shapes at the edges of the balanced work split, checked on sampled rows of the
     last half-pass: F(g) for rows of x and G(f) for rows of y."""
-    w = W.CONFIGS[key].scaled(n, m, 3)
+    w = W.CASES[key].scaled(n, m, 3)
     say(f"work split cfg={key} n={n} m={m} d={w.d} {w.dtype}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -461,7 +461,7 @@ def test_full_size_sampled_rows(sk, key):
     """Every configuration at full size, in the benchmark's launch configuration:
     the solve, the gradient and both applications, checked on sampled rows and
     columns that the oracle computes one by one."""
-    w = W.CONFIGS[key]
+    w = W.CASES[key]
     say(f"full size cfg={key} n={w.n} m={w.m} d={w.d} {w.dtype} iters={w.iters} mode={w.mode}")
     inp = W.make_inputs(w, k=16)
     x, y, a, b = dev(inp)
@@ -520,7 +520,7 @@ def test_divergence_matches_oracle(sk, key, n, m, iters):
     same solves run through the solve entry point (bitwise repeatable), the
     gradients in x and y against the oracle fed those potentials, and S and the
     weight gradients end to end against the oracle's own solves."""
-    w = W.CONFIGS[key].scaled(n, m, iters)
+    w = W.CASES[key].scaled(n, m, iters)
     say(f"divergence cfg={key} n={n} m={m} iters={iters} {w.dtype} d={w.d}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -570,7 +570,7 @@ def test_hadamard_apply_matches_oracle(sk, key, n, m, r, k):
     """(P o A B^T) V and its transpose against the oracle's entrywise definition,
     both sides fed the same float32 potentials; the bound is relative to
     |P| |W| |V| (signed weights may cancel)."""
-    w = W.CONFIGS[key].scaled(n, m, 8)
+    w = W.CASES[key].scaled(n, m, 8)
     say(f"hadamard apply cfg={key} n={n} m={m} r={r} k={k}")
     inp = W.make_inputs(w, k=k)
     x, y, a, b = dev(inp)
@@ -595,7 +595,7 @@ def test_hadamard_apply_matches_oracle(sk, key, n, m, r, k):
 def test_solve_tol_error_matches_oracle(sk, mode):
     """The marginal error the tolerance solve measures equals the oracle's
     ||P1 - a||_1 + ||P^T 1 - b||_1 at the checked pair (far from convergence)."""
-    w = W.CONFIGS[6].scaled(900, 700, 3)
+    w = W.CASES[6].scaled(900, 700, 3)
     say(f"solve_tol error parity mode={mode}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -618,7 +618,7 @@ def test_solve_tol_error_matches_oracle(sk, mode):
 
 @pytest.mark.parametrize("key,n,m", [(1, 600, 500), (3, 400, 700), (6, 800, 700)])
 def test_solve_tol_reaches_tolerance(sk, key, n, m):
-    w = W.CONFIGS[key].scaled(n, m)
+    w = W.CASES[key].scaled(n, m)
     say(f"solve_tol convergence cfg={key} n={n} m={m} {w.dtype}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
@@ -648,7 +648,7 @@ def test_hvp_matches_dense_oracle(sk, key, n, m, eps):
     """Streaming Hessian-vector product (Schur CG over matrix-free applications)
     against the oracle's dense Moore-Penrose solve at the same (converged) pair."""
     from dataclasses import replace
-    w = W.CONFIGS[key].scaled(n, m, 300)
+    w = W.CASES[key].scaled(n, m, 300)
     if eps is not None:
         w = replace(w, eps=eps)
     say(f"hvp cfg={key} n={n} m={m} d={w.d} {w.dtype} eps={w.eps}")
@@ -668,7 +668,7 @@ def test_hvp_matches_dense_oracle(sk, key, n, m, eps):
 def test_solve_tol_with_eps_scaling(sk):
     """eps-scaling (one iteration per halving from eps_start) then the tolerance
     phase at eps: the returned pair meets the tolerance by the oracle's marginals."""
-    w = W.CONFIGS[6].scaled(900, 800)
+    w = W.CASES[6].scaled(900, 800)
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
     tol = 1e-4
@@ -686,7 +686,7 @@ def test_hvp_and_hadamard_properties_at_full_size(sk, key):
     """At full size (no dense oracle): the Hessian is symmetric, <U, H V> =
     <V, H U>, and the Hadamard-weighted application with W = 1 1^T is the plain
     application bit for bit."""
-    w = W.CONFIGS[key]
+    w = W.CASES[key]
     say(f"full-size HVP symmetry / Hadamard identity cfg={key} n={w.n} m={w.m} d={w.d}")
     inp = W.make_inputs(w, k=16)
     x, y, a, b = dev(inp)

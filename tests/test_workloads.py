@@ -22,9 +22,9 @@ def test_bf16_rounding_is_round_to_nearest_even():
     assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
 
 
-@pytest.mark.parametrize("key", sorted(W.CONFIGS))
+@pytest.mark.parametrize("key", sorted(W.CASES))
 def test_inputs_are_deterministic_and_shaped(key):
-    w = W.CONFIGS[key].scaled(257, 131)
+    w = W.CASES[key].scaled(257, 131)
     i1, i2 = W.make_inputs(w), W.make_inputs(w)
     for a1, a2 in [(i1.x, i2.x), (i1.y, i2.y), (i1.a, i2.a), (i1.b, i2.b)]:
         assert a1.tobytes() == a2.tobytes()
@@ -39,6 +39,6 @@ def test_inputs_are_deterministic_and_shaped(key):
 
 
 def test_bf16_variant_shares_points_with_f32_config():
-    a = W.make_inputs(W.CONFIGS[4].scaled(64))
-    b = W.make_inputs(W.CONFIGS[7].scaled(64))
+    a = W.make_inputs(W.CASES[4].scaled(64))
+    b = W.make_inputs(W.CASES[7].scaled(64))
     assert np.array_equal(W.f32_to_bf16_bits(a.x), b.x)

@@ -50,7 +50,7 @@ class Workload:
 
 # The five point-cloud configurations, the n=m=50k d=3 shape (key 6) and the bf16
 # variant of the d=512 configuration (key 7, same seed and points as key 4).
-CONFIGS = {
+CASES = {
     1: Workload(1, "tiny_d3", 1024, 1024, 3, "f32", "unit_vs_gauss", "uniform", 0.05, 50, "alternating"),
     2: Workload(2, "mix8_d3_10k", 10_000, 10_000, 3, "f32", "mixture8", "uniform", 0.01, 100, "symmetric", grad=True),
     3: Workload(3, "embed_d64_50k_bf16", 50_000, 50_000, 64, "bf16", "gauss_over_sqrt_d", "dirichlet1", 0.1, 100, "alternating"),
