@@ -361,7 +361,7 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   MfmaPrepSide py{y, b, g, nullptr, L.y.row_rec, L.y.col_rec, L.y.alpha, L.y.lw,
                   L.y.bias[0], L.y.bias[1], L.y.hval[0], m};
   hipError_t e = launch_prep_mfma(px, py, dtype, (int)d, ap.nkb, false, true, L.c.centroid, L.c.shift,
-                                  L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);
+                                  L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, ap.path == Path::Gemm, s);
   if (e != hipSuccess) return hip_fail(e, "prep");
   const float* shift = dtype == SK_F32 ? L.c.shift : nullptr;
   e = launch_pack_values(vsrc, vsrc_bf16, ap.nc, ap.kv, grad ? shift : nullptr, ap.vp, ap.nobt,
@@ -579,7 +579,7 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
     py.hacc = L.ym.hacc[0]; py.hacc_alt = L.ym.hacc[1];
     // counters and the exact-fallback count are zeroed together (adjacent)
     e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, sp.merged, center, L.c.centroid, L.c.shift,
-                         L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, s);
+                         L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, sp.path == Path::Gemm, s);
     if (e != hipSuccess) return hip_fail(e, "prep");
     if ((rc = solve_mfma(L, sp, dtype, n, m, iters, sym, f, g, sc, s))) return rc;
     if (debug_enabled()) {

@@ -556,8 +556,10 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
 // ---------------------------------------------------------------- record prep
 // Slot s of a record: data slots first (coordinate-major), then zeros.
 // bf16 storage: one slot per coordinate. float32 storage: six slots per coordinate.
+// Records of the GEMM-tiled kernels (interleave) are stored K block by K
+// block: chunk (half h, K block kb) at position 2 kb + h instead of h nkb + kb.
 __global__ __launch_bounds__(256) void k_pack_records(const void* pts, int dtype, int64_t n, int d,
-                                                      const float* shift, int nkb, float c2,
+                                                      const float* shift, int nkb, float c2, int interleave,
                                                       bf16x8* row_rec, bf16x8* col_rec) {
   const int chunks = nkb * 2;  // 16-byte chunks per record
   const int64_t total = n * chunks;
@@ -588,8 +590,9 @@ __global__ __launch_bounds__(256) void k_pack_records(const void* pts, int dtype
         cv[e] = (w == 1 || w == 4) ? u2 : (w == 3 ? u3 : u1);
       }
     }
-    row_rec[c] = rv;
-    col_rec[c] = cv;
+    const int64_t at = interleave ? r * chunks + (q % nkb) * 2 + q / nkb : c;
+    row_rec[at] = rv;
+    col_rec[at] = cv;
   }
 }
 
@@ -799,7 +802,7 @@ hipError_t launch_lse_mfma_pair(const MfmaPassArgs& a0, const PassPlan& pl0, con
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
                             int nkb, bool merged, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,
-                            float c2, hipStream_t s) {
+                            float c2, bool interleave, hipStream_t s) {
   const float* sh = nullptr;
   if (center && dtype == 0) {
     hipError_t e = launch_centroid(xs.pts, xs.n, ys.pts, ys.n, dtype, d, centroid_part, shift, s);
@@ -811,7 +814,7 @@ hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int 
   for (const MfmaPrepSide* side : {&xs, &ys}) {
     const int64_t chunks = side->n * nkb * 2;
     const int blocks = (int)((chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096);
-    k_pack_records<<<blocks, 256, 0, s>>>(side->pts, dtype, side->n, d, sh, nkb, c2,
+    k_pack_records<<<blocks, 256, 0, s>>>(side->pts, dtype, side->n, d, sh, nkb, c2, interleave ? 1 : 0,
                                           side->row_rec, side->col_rec);
     const int64_t npad = mfma_padded_count(side->n);
     const int64_t pad_work = (npad - side->n) * nkb * 2;

@@ -8,12 +8,23 @@ namespace sk {
 namespace dev {
 
 // ---------------------------------------------------------------- GEMM-tiled staging
+constexpr int kGKb = 4;       // K blocks (16 slots) per LDS stage
+constexpr int kGRow = kGKb * 2 * 16 + 16;  // LDS bytes per record per stage (both halves + pad)
+
+// The GEMM-tiled kernels read records stored K block by K block: the 16-byte
+// chunk of half h and K block kb sits at chunk position 2 kb + h (the
+// register-resident kernels keep each half's run together instead), so the
+// four K blocks of a stage are 128 contiguous bytes of a record, one cache
+// line, and eight threads load it whole.
+__device__ __forceinline__ int64_t gemm_chunk_off(int hh, int kc, int part) {
+  return (int64_t)((kc * kGKb + part) * 2 + hh) * 16;
+}
+
+
 // Workgroups of 2 x 2 waves own 128 rows and sweep columns in blocks of 128;
 // both operands stream through LDS in chunks of 4 K blocks.
 constexpr int kGRows = 128;   // rows per workgroup
 constexpr int kGCols = 128;   // columns per block
-constexpr int kGKb = 4;       // K blocks (16 slots) per LDS stage
-constexpr int kGRow = kGKb * 2 * 16 + 16;  // LDS bytes per record per stage (both halves + pad)
 
 struct GemmLds {
   unsigned char rows[2][kGRows * kGRow];
@@ -27,7 +38,7 @@ struct GemmRegs {
 
 // Stage s of the flattened (column block, K chunk) sequence: chunk (kc) of the
 // K dimension for rows [r0, r0+128) and columns [c0, c0+128). A chunk is, per
-// record, 4 x 16 bytes in each half: record bytes [h*NKB*16 + kc*64, +64).
+// record, the 128 bytes [kc * 128, +128) (both halves of 4 K blocks).
 __device__ __attribute__((always_inline)) inline void gemm_load(
     GemmRegs& g, const unsigned char* __restrict__ rows, const unsigned char* __restrict__ cols,
     int nkb, int nr, int r0, int c0, int kc) {
@@ -36,7 +47,7 @@ __device__ __attribute__((always_inline)) inline void gemm_load(
   for (int q = 0; q < 4; ++q) {
     const int ch = threadIdx.x + q * kThreads;  // 0..1023: record (ch >> 3), half ((ch >> 2) & 1), part (ch & 3)
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
-    const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
+    const int64_t off = gemm_chunk_off(hh, kc, part);
     g.r[q] = *reinterpret_cast<const u32x4*>(rows + (int64_t)min(r0 + rec, nr - 1) * rsb + off);
     g.c[q] = *reinterpret_cast<const u32x4*>(cols + (int64_t)(c0 + rec) * rsb + off);
   }
@@ -82,9 +93,9 @@ struct TileRegs {
 };
 
 // Stage (kc) of the K dimension for rows [r0, r0 + kRows) and columns
-// [c0, c0 + kCols): per record, 4 x 16 bytes in each half, record bytes
-// [h * NKB * 16 + kc * 64, +64). Row indices clamp to the last row, column
-// indices to the last padded (masked) column.
+// [c0, c0 + kCols): per record, the 128 bytes [kc * 128, +128) (both halves
+// of 4 K blocks). Row indices clamp to the last row, column indices to the
+// last padded (masked) column.
 template <class G>
 __device__ __attribute__((always_inline)) inline void tile_load(
     TileRegs<G>& g, const unsigned char* __restrict__ rows, const unsigned char* __restrict__ cols,
@@ -94,14 +105,14 @@ __device__ __attribute__((always_inline)) inline void tile_load(
   for (int q = 0; q < G::kRowLoads; ++q) {
     const int ch = threadIdx.x + q * G::kNT;  // record (ch >> 3), half ((ch >> 2) & 1), part (ch & 3)
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
-    const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
+    const int64_t off = gemm_chunk_off(hh, kc, part);
     g.r[q] = *reinterpret_cast<const u32x4*>(rows + (int64_t)min(r0 + rec, nr - 1) * rsb + off);
   }
 #pragma unroll
   for (int q = 0; q < G::kColLoads; ++q) {
     const int ch = threadIdx.x + q * G::kNT;
     const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
-    const int64_t off = (int64_t)hh * nkb * 16 + (int64_t)kc * 64 + part * 16;
+    const int64_t off = gemm_chunk_off(hh, kc, part);
     g.c[q] = *reinterpret_cast<const u32x4*>(cols + (int64_t)min(c0 + rec, col_last) * rsb + off);
   }
 }

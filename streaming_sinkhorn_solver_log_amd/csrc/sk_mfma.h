@@ -111,10 +111,11 @@ hipError_t launch_lse_mfma(const MfmaPassArgs& a, int nkb, bool shifted, bool sc
 hipError_t launch_lse_mfma_pair(const MfmaPassArgs& a0, const PassPlan& pl0, const MfmaPassArgs& a1,
                                 const PassPlan* pl1, int nkb, bool shifted, bool scaled, bool merged,
                                 hipStream_t s);
+// interleave: records for the GEMM-tiled kernels (K block by K block).
 hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int dtype, int d,
                             int nkb, bool merged, bool center, double* centroid_part, float* shift,
                             unsigned* counters, int n_counters, float log2e_over_eps,
-                            float c2, hipStream_t s);
+                            float c2, bool interleave, hipStream_t s);
 // escale and bias_scale of a storage type (see MfmaPassArgs).
 inline float mfma_escale(int dtype, float c2) { return dtype == 1 ? c2 : 1.0f; }
 inline float mfma_bias_scale(int dtype, float c2) { return dtype == 1 ? 1.0f / c2 : 1.0f; }
