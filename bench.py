@@ -193,9 +193,9 @@ class Case:
 def pass_roofline(w, pass_ms):
     """Roofline of the half-pass kernel. Per pair the VALU must issue one exp2,
     one add (and a multiply for bf16 points); these share the issue port, so
-    the ALU roof is VALU_PEAK / slots per pair. The matrix-core roof is the
-    bf16 MFMA work per pair (2d flops, or 12d for the six-product float32
-    split); the longer ideal time is the bound."""
+    the ALU roof is VALU_PEAK / slots per pair. The matrix-core roof is 2d
+    flops per pair at the points' dtype's MFMA peak; the longer ideal time is
+    the bound."""
     r = _pass_roofline(w, pass_ms)
     r["traffic"] = kernel_traffic(w.name)
     return r
@@ -234,14 +234,16 @@ def _pass_roofline(w, pass_ms):
         also["measured_mix_probe"] = probe
         also["measured_mix_frac"] = rate / mix_rate
     if w.d >= 32:
-        # The matrix cores run bf16 MFMAs in both cases: 2d flops per pair for
-        # bf16 points, six bf16 products (12d flops) for float32 points, whose
-        # float32-MFMA equivalent is reported beside it.
-        peak = BF16_MFMA_PEAK
-        mfma_flops = (2.0 if w.dtype == "bf16" else 12.0) * w.d * pairs
+        # A contraction is priced at its own dtype's peak: 2d flops per pair
+        # at the bf16 or float32 MFMA peak. float32 points run as six bf16
+        # products per coordinate pair (12d issued flops), so their fraction
+        # of the float32 peak can exceed 1; the issued bf16 work's fraction of
+        # the bf16 peak is reported beside it.
+        peak = BF16_MFMA_PEAK if w.dtype == "bf16" else F32_MFMA_PEAK
+        mfma_flops = 2.0 * w.d * pairs
         mfma_frac = mfma_flops / sec / peak
         if w.dtype != "bf16":
-            also["f32_mfma_equivalent_frac"] = 2.0 * w.d * pairs / sec / F32_MFMA_PEAK
+            also["bf16_issued_frac"] = 12.0 * w.d * pairs / sec / BF16_MFMA_PEAK
         # the binding roof is whichever ideal time is longer
         if mfma_flops / peak >= pairs / alu_peak:
             also["alu_frac"] = rate / alu_peak
