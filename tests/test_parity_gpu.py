@@ -200,6 +200,53 @@ def test_dimension_boundaries(sk, i, case):
     assert e_g <= tol_rel(w) and e1 <= tol_rel(w) and e2 <= tol_rel(w)
 
 
+def _random_case(seed):
+    """A seeded random shape: n, m in [1, 2600], d over every kernel family,
+    either dtype and schedule, eps in [0.05, 1], k in [1, 64]."""
+    from dataclasses import replace
+    rng = np.random.default_rng([20, seed])
+    dtype = ["f32", "bf16"][int(rng.integers(2))]
+    d = int(rng.choice([1, 2, 3, 4, 5, 7, 9, 13, 16, 21, 24, 31, 40, 64, 70, 100, 128, 150, 257, 520]))
+    n, m = int(rng.integers(1, 2600)), int(rng.integers(1, 2600))
+    while n * m * d > 6e7:
+        n, m = max(1, n // 2), max(1, m // 2)
+    mode = ["alternating", "symmetric"][int(rng.integers(2))]
+    eps = float(np.round(rng.uniform(0.05, 1.0), 3))
+    k = int(rng.integers(1, 65))
+    iters = int(rng.integers(1, 6))
+    w = replace(W.CASES[4], d=d, dtype=dtype, eps=eps, mode=mode, name=f"rand{seed}").scaled(n, m, iters)
+    return w, k
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(sk, seed):
+    """Solve, gradient, P V and P^T U on seeded random shapes against the oracle
+    (the gradient and the applications with the GPU's potentials fed to both sides)."""
+    w, k = _random_case(seed)
+    say(f"random seed={seed} {w.dtype} d={w.d} n={w.n} m={w.m} {w.mode} eps={w.eps} iters={w.iters} k={k}")
+    inp = W.make_inputs(w, k=k)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    fn, gn = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    ef, eg = np.abs(fn - fr).max(), np.abs(gn - gr).max()
+    x64, y64 = inp.x64(), inp.y64()
+    grad = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()
+    ref = oracle.grad_x(x64, y64, inp.a, inp.b, gn, w.eps)
+    e_g = np.abs(grad - ref).max() / max(np.abs(ref).max(), 1e-30)
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+    PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy()
+    ref1 = oracle.apply(x64, y64, inp.a, inp.b, fn, gn, w.eps, inp.V)
+    PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy()
+    ref2 = oracle.apply(x64, y64, inp.a, inp.b, fn, gn, w.eps, inp.U, transpose=True)
+    e1 = np.abs(PV - ref1).max() / np.abs(ref1).max()
+    e2 = np.abs(PtU - ref2).max() / np.abs(ref2).max()
+    say(f"  max|df|={ef:.2e} max|dg|={eg:.2e} (tol {tol_pot(w, fr):.1e}) grad {e_g:.2e} P.V {e1:.2e} P^T.U {e2:.2e}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * max(abs(cr), 1e-30)
+    assert e_g <= tol_rel(w) and e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
 def test_solve_bf16_points_small_d(sk):
     w = bf16_variant(W.CASES[1].scaled(900, 1100, 20))
     say("solve bf16 d=3")
