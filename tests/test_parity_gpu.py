@@ -345,6 +345,43 @@ def test_bitwise_repeatable_all_kernels(sk, key, n, m):
                 assert torch.equal(r, t)
 
 
+def test_side_streams_and_caller_workspace(sk):
+    """Work is ordered on the caller's current stream only: two problems of
+    different kernel families issued on two side streams without any host
+    synchronization in between give bitwise the default-stream results, also
+    when every call takes a caller workspace pre-filled with 0xFF (the library
+    initializes every counter and partial it relies on)."""
+    cases = [(3, 6000, 5000), (6, 3000, 2500)]
+    probs, refs = [], []
+    for key, n, m in cases:
+        w = W.CASES[key].scaled(n, m, 6)
+        say(f"side streams cfg={key} n={n} m={m} d={w.d} {w.dtype}")
+        inp = W.make_inputs(w, k=16)
+        x, y, a, b = dev(inp)
+        V = torch.from_numpy(inp.V).to(DEV)
+        f, g, c = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+        refs.append((f, g, c, sk.eot_grad_x(x, y, a, b, g, w.eps),
+                     sk.transport_apply(x, y, a, b, f, g, w.eps, V)))
+        probs.append((w, x, y, a, b, V))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = []
+    for (w, x, y, a, b, V), s in zip(probs, streams):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            ws = torch.full((1 << 26,), 255, dtype=torch.uint8, device=DEV)
+            f, g, c = sk.solve(x, y, a, b, w.eps, w.iters, w.mode, workspace=ws)
+            ws.fill_(255)
+            gr = sk.eot_grad_x(x, y, a, b, g, w.eps, workspace=ws)
+            ws.fill_(255)
+            pv = sk.transport_apply(x, y, a, b, f, g, w.eps, V, workspace=ws)
+            outs.append((f, g, c, gr, pv))
+    torch.cuda.synchronize()
+    for ref, out in zip(refs, outs):
+        for r, t in zip(ref, out):
+            assert torch.equal(r, t)
+
+
 def test_translation_invariance(sk):
     w = W.CASES[1].scaled(800, 900, 10)
     say("translation invariance")
