@@ -67,6 +67,7 @@ extern "C" {
 /* solve flags */
 #define SK_WARM_START 1u /* f and g hold the starting potentials (else zeros)  */
 #define SK_NO_CENTER 2u  /* do not translate float32 clouds to a common origin */
+#define SK_CHECK_FINITE 4u /* screen the inputs first (see sk_sinkhorn_solve)    */
 
 /* operations, for sk_workspace_bytes */
 #define SK_OP_SOLVE 0
@@ -84,10 +85,17 @@ extern "C" {
  *              half-pass); iters = 0 returns the starting potentials and
  *              their cost.
  *   mode       SK_ALTERNATING or SK_SYMMETRIC.
- *   flags      SK_WARM_START, SK_NO_CENTER.
+ *   flags      SK_WARM_START, SK_NO_CENTER, SK_CHECK_FINITE.
  *   f, g       out (in/out with SK_WARM_START): n and m float32 potentials.
  *   cost       out: one double, <a, f> + <b, g> at the final pair.
- * Requirements: n, m, d >= 1; eps finite and > 0; iters >= 0.
+ * Requirements: n, m, d >= 1; eps finite and > 0; iters >= 0. The values
+ * themselves are not checked by default: a NaN or infinity in x, y, a, b (or
+ * in f, g under SK_WARM_START) propagates into the results. SK_CHECK_FINITE
+ * screens them on the device first and waits for the verdict (one host
+ * synchronization of `stream`): a NaN or infinity, a negative weight, or an
+ * a or b with no positive weight returns SK_ERR_INVALID_ARG before anything
+ * that writes f, g or cost is enqueued (the screening writes one workspace
+ * word). Nonzero weights are never renormalized.
  */
 int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                       const float* a, const float* b, double eps, int32_t iters, int mode,

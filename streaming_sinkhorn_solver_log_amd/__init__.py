@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(_PKG, "libflashsk.so")
 SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0, -1, -2, -3, -4
 SK_F32, SK_BF16 = 0, 1
 SK_ALTERNATING, SK_SYMMETRIC = 0, 1
-SK_WARM_START, SK_NO_CENTER = 1, 2
+SK_WARM_START, SK_NO_CENTER, SK_CHECK_FINITE = 1, 2, 4
 SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD, SK_OP_SOLVE_TOL, SK_OP_HVP = range(7)
 
 _ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
@@ -151,14 +151,16 @@ def _workspace(op, dtype, n, m, d, k, device, ws):
 
 
 def solve(x, y, a, b, eps: float, iters: int, mode: str = "alternating", f0=None, g0=None,
-          center: bool = True, workspace=None):
-    """Fixed-budget Sinkhorn; returns (f, g, cost) with cost a 0-d float64 tensor."""
+          center: bool = True, workspace=None, check_finite: bool = False):
+    """Fixed-budget Sinkhorn; returns (f, g, cost) with cost a 0-d float64 tensor.
+    check_finite: screen x, y, a, b (and f0, g0) on the device first and raise
+    SinkhornError on a NaN, an infinity or a bad weight (waits for the stream)."""
     n, m, d, dt = _points(x, y)
     dev = x.device
     _vec(a, n, "a", dev)
     _vec(b, m, "b", dev)
     mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
-    flags = 0 if center else SK_NO_CENTER
+    flags = (0 if center else SK_NO_CENTER) | (SK_CHECK_FINITE if check_finite else 0)
     if (f0 is None) != (g0 is None):
         raise ValueError("give both f0 and g0 for a warm start, or neither")
     if f0 is not None:

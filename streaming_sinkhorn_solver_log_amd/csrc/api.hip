@@ -9,6 +9,7 @@
 
 #include "flashsk.h"
 #include "sk_internal.h"
+#include "sk_check.h"
 #include "sk_mfma.h"
 #include "sk_gemm.h"
 #include "sk_api.h"
@@ -544,6 +545,24 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
   }
 }
 
+// SK_CHECK_FINITE: screens the inputs on the device and waits for the
+// verdict, so that a bad input fails before the solve enqueues anything that
+// writes f, g or cost. `word` is a workspace word the solve re-initializes.
+static int screen_inputs(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                         const float* a, const float* b, bool warm, const float* f, const float* g,
+                         unsigned* word, hipStream_t s) {
+  hipError_t e = launch_check_inputs(x, y, dtype, n, m, d, a, b, warm ? f : nullptr, warm ? g : nullptr, word, s);
+  unsigned bits = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bits, word, sizeof(bits), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "input check");
+  if (bits & kBadPoints) return fail(SK_ERR_INVALID_ARG, "x or y holds a NaN or an infinity");
+  if (bits & kBadWeights) return fail(SK_ERR_INVALID_ARG, "a or b holds a negative, NaN or infinite weight");
+  if (!(bits & kPositiveA) || !(bits & kPositiveB)) return fail(SK_ERR_INVALID_ARG, "a or b has no positive weight");
+  if (bits & kBadPotentials) return fail(SK_ERR_INVALID_ARG, "the starting f or g holds a NaN or an infinity");
+  return SK_OK;
+}
+
 int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                       const float* a, const float* b, double eps, int32_t iters, int mode,
                       uint32_t flags, float* f, float* g, double* cost, void* ws, size_t ws_bytes,
@@ -554,12 +573,16 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   if (!f || !g || !cost) return fail(SK_ERR_INVALID_ARG, "null output pointer");
   if (iters < 0) return fail(SK_ERR_INVALID_ARG, "iters must be >= 0");
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
-  if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & ~(SK_WARM_START | SK_NO_CENTER | SK_CHECK_FINITE))
+    return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   const SolvePlan sp = plan_solve(dtype, n, m, d, mode == SK_ALTERNATING);
   const size_t need = layout_solve(nullptr, sp, n, m, d).bytes;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   const SolveWs L = layout_solve(ws, sp, n, m, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((flags & SK_CHECK_FINITE) && (rc = screen_inputs(x, y, dtype, n, m, d, a, b, (flags & SK_WARM_START) != 0,
+                                                       f, g, L.c.counters, s)))
+    return rc;
   const Scalars sc = scalars(eps);
   const bool warm = (flags & SK_WARM_START) != 0;
   const bool center = (flags & SK_NO_CENTER) == 0;

@@ -9,6 +9,7 @@
 // under a common translation, and smaller norms make the expansion better
 // conditioned in float32.
 #include "sk_internal.h"
+#include "sk_check.h"
 
 #include <math.h>
 
@@ -113,6 +114,40 @@ __global__ __launch_bounds__(256) void k_zero_u32(unsigned* p, int64_t count) {
   if (i < count) p[i] = 0u;
 }
 
+// Input screening for SK_CHECK_FINITE: ORs into *bad the bits of
+// InputCheckBits that some element violates (one atomic per workgroup).
+__device__ __forceinline__ bool finite_bits(unsigned u, unsigned expmask) { return (u & expmask) != expmask; }
+
+__global__ __launch_bounds__(256) void k_check_inputs(const void* x, const void* y, int dtype, int64_t nx,
+                                                      int64_t ny, const float* a, int64_t n, const float* b,
+                                                      int64_t m, const float* f, const float* g,
+                                                      unsigned* bad) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool pts = false, wts = false, apos = false, bpos = false, pot = false;
+  for (int64_t i = t0; i < nx + ny; i += stride) {
+    const void* src = i < nx ? x : y;
+    const int64_t k = i < nx ? i : i - nx;
+    if (dtype == 1) pts |= !finite_bits(static_cast<const unsigned short*>(src)[k], 0x7F80u);
+    else pts |= !finite_bits(__float_as_uint(static_cast<const float*>(src)[k]), 0x7F800000u);
+  }
+  for (int64_t i = t0; i < n + m; i += stride) {
+    const float w = i < n ? a[i] : b[i - n];
+    // NaN fails both comparisons: !(w >= 0) catches it with the negatives
+    wts |= !(w >= 0.0f) || !finite_bits(__float_as_uint(w), 0x7F800000u);
+    if (i < n) apos |= w > 0.0f;
+    else bpos |= w > 0.0f;
+    if (f) {
+      const float v = i < n ? f[i] : g[i - n];
+      pot |= !finite_bits(__float_as_uint(v), 0x7F800000u);
+    }
+  }
+  const unsigned bits = (__syncthreads_or(pts) ? kBadPoints : 0u) | (__syncthreads_or(wts) ? kBadWeights : 0u) |
+                        (__syncthreads_or(apos) ? kPositiveA : 0u) | (__syncthreads_or(bpos) ? kPositiveB : 0u) |
+                        (__syncthreads_or(pot) ? kBadPotentials : 0u);
+  if (threadIdx.x == 0 && bits) atomicOr(bad, bits);
+}
+
 // cost = sum_i a_i f_i + sum_j b_j g_j in float64, one workgroup, fixed order.
 __global__ __launch_bounds__(1024) void k_cost(const float* a, const float* f, int64_t n,
                                                const float* b, const float* g, int64_t m,
@@ -159,6 +194,14 @@ hipError_t launch_prep(const PrepSide& xs, const PrepSide& ys, int dtype, int d,
 hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
                        int64_t m, double* cost, hipStream_t s) {
   k_cost<<<1, 1024, 0, s>>>(a, f, n, b, g, m, cost);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_inputs(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                               const float* a, const float* b, const float* f, const float* g,
+                               unsigned* bad, hipStream_t s) {
+  k_zero_u32<<<1, 256, 0, s>>>(bad, 1);
+  k_check_inputs<<<1024, 256, 0, s>>>(x, y, dtype, n * d, m * d, a, n, b, m, f, g, bad);
   return hipGetLastError();
 }
 

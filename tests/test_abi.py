@@ -194,3 +194,17 @@ def test_peaks_library_exports_measure_entry():
         pytest.skip("libskpeaks.so not built; run __graft_entry__.build()")
     L = ctypes.CDLL(path)
     assert hasattr(L, "skp_measure")
+
+
+def test_check_finite_flag_matches_the_binding(lib):
+    """SK_CHECK_FINITE is a known flag bit (unknown bits are still refused) and
+    the Python binding uses the header's value."""
+    flag = _header_int("SK_CHECK_FINITE")
+    assert flag not in (_header_int("SK_WARM_START"), _header_int("SK_NO_CENTER"))
+    src = open(os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "__init__.py")).read()
+    values = re.search(r"^SK_WARM_START, SK_NO_CENTER, SK_CHECK_FINITE = (.*)$", src, re.M).group(1)
+    assert [int(v) for v in values.split(",")][2] == flag
+    inv = _header_int("SK_ERR_INVALID_ARG")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 3, 0, flag | 0x80, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.sk_sinkhorn_solve(*base) == inv
+    assert b"flag" in lib.sk_last_error()

@@ -382,6 +382,45 @@ def test_side_streams_and_caller_workspace(sk):
             assert torch.equal(r, t)
 
 
+def test_check_finite_screens_inputs(sk):
+    """SK_CHECK_FINITE: clean inputs give bitwise the unchecked result; a NaN
+    or an infinity in the points, a negative or NaN weight, an all-zero
+    marginal or a non-finite warm start is refused with SK_ERR_INVALID_ARG."""
+    nan, inf = float("nan"), float("inf")
+    for key in (1, 3):  # float32 d = 3, bf16 d = 64
+        w = W.CASES[key].scaled(700, 900, 5)
+        say(f"check_finite cfg={key} {w.dtype} d={w.d}")
+        inp = W.make_inputs(w)
+        x, y, a, b = dev(inp)
+        ref = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+        out = sk.solve(x, y, a, b, w.eps, w.iters, w.mode, check_finite=True)
+        for r, t in zip(ref, out):
+            assert torch.equal(r, t)
+        f0, g0 = ref[0].clone(), ref[1].clone()
+
+        def put(t, idx, v):
+            t = t.clone()
+            t[idx] = v
+            return t
+        bad = {
+            "nan in x": dict(x=put(x, (17, 1 % w.d), nan)),
+            "inf in y": dict(y=put(y, (899, 0), -inf)),
+            "negative a": dict(a=put(a, 3, -1e-6)),
+            "nan in b": dict(b=put(b, 0, nan)),
+            "all-zero a": dict(a=torch.zeros_like(a)),
+            "inf in f0": dict(f0=put(f0, 5, inf), g0=g0),
+        }
+        for name, over in bad.items():
+            args = dict(x=x, y=y, a=a, b=b)
+            args.update(over)
+            with pytest.raises(sk.SinkhornError) as err:
+                sk.solve(args.pop("x"), args.pop("y"), args.pop("a"), args.pop("b"), w.eps, w.iters, w.mode,
+                         check_finite=True, **args)
+            assert err.value.code == sk.SK_ERR_INVALID_ARG, name
+        # the same warm start, finite, is accepted
+        sk.solve(x, y, a, b, w.eps, 1, w.mode, f0=f0, g0=g0, check_finite=True)
+
+
 def test_translation_invariance(sk):
     w = W.CASES[1].scaled(800, 900, 10)
     say("translation invariance")
