@@ -387,7 +387,7 @@ def test_check_finite_screens_inputs(sk):
     or an infinity in the points, a negative or NaN weight, an all-zero
     marginal or a non-finite warm start is refused with SK_ERR_INVALID_ARG."""
     nan, inf = float("nan"), float("inf")
-    for key in (1, 3):  # float32 d = 3, bf16 d = 64
+    for key in (1, 3, 4):  # float32 d = 3, bf16 d = 64, float32 d = 512 (GEMM-tiled)
         w = W.CASES[key].scaled(700, 900, 5)
         say(f"check_finite cfg={key} {w.dtype} d={w.d}")
         inp = W.make_inputs(w)
