@@ -132,8 +132,9 @@ def _dev_points(arr, dtype, torch, dev):
 
 
 class Case:
-    def __init__(self, key, torch, sk, dev, k=16):
-        self.w = w = W.CASES[key]
+    def __init__(self, key, torch, sk, dev, k=16, mode=None):
+        from dataclasses import replace
+        self.w = w = W.CASES[key] if mode is None else replace(W.CASES[key], mode=mode)
         inp = W.make_inputs(w, k=k)
         self.inp = inp
         self.x = _dev_points(inp.x, w.dtype, torch, dev)
@@ -193,9 +194,11 @@ class Case:
 def pass_roofline(w, pass_ms):
     """Roofline of the half-pass kernel. Per pair the VALU must issue one exp2,
     one add (and a multiply for bf16 points); these share the issue port, so
-    the ALU roof is VALU_PEAK / slots per pair. The matrix-core roof is 2d
-    flops per pair at the points' dtype's MFMA peak; the longer ideal time is
-    the bound."""
+    the ALU roof is VALU_PEAK / slots per pair, or the measured rate of that
+    VALU work alone where the chip beats the model. The matrix-core roof is
+    the bf16 MFMA peak for the products the pass issues (2d flops per pair for
+    bf16 points, 12d for float32 points); the longer ideal time is the bound,
+    and the other fraction is reported beside it."""
     r = _pass_roofline(w, pass_ms)
     r["traffic"] = kernel_traffic(w.name)
     return r
@@ -208,49 +211,66 @@ def alu_slots_per_pair(w):
     return 3 + (1 if w.dtype == "bf16" else 0)
 
 
-# Measured rate of a register-only loop with the half-pass's own instruction
-# mix (bench.py --peaks, stored in profiles/unit_peaks.json): the practical
-# ceiling of the register-resident half-pass on this chip.
+# Measured rates of register-only loops (bench.py --peaks, stored in
+# profiles/unit_peaks.json). VALU_PROBE: the half-pass's VALU work per pair
+# alone (exp2 + add, or mul + exp2 + add); the chip runs it slightly faster
+# than the issue-slot model, so the ALU roof is the larger of the two.
+# MIX_PROBE: the same VALU work with the pass's MFMAs interleaved.
 UNIT_PEAKS_FILE = os.path.join(ROOT, "profiles", "unit_peaks.json")
+VALU_PROBE = {"f32": "exp2_add", "bf16": "mul_exp2_add"}
 MIX_PROBE = {("f32", 3): "mix_f32_points_d3", ("bf16", 64): "mix_bf16_points_d64"}
+
+
+def _unit_peak(name):
+    if name is None or not os.path.exists(UNIT_PEAKS_FILE):
+        return None
+    with open(UNIT_PEAKS_FILE) as fh:
+        return json.load(fh)["peaks"].get(name, {}).get("rate")
 
 
 def measured_mix_rate(w):
     name = MIX_PROBE.get((w.dtype, w.d))
-    if name is None or not os.path.exists(UNIT_PEAKS_FILE):
-        return None, None
-    with open(UNIT_PEAKS_FILE) as fh:
-        return name, json.load(fh)["peaks"][name]["rate"]
+    return name, _unit_peak(name)
+
+
+def alu_roof(w):
+    """(pairs/s, how it was priced): the issue-slot model or, when the chip
+    beats it, the measured rate of the same VALU work with nothing else."""
+    model = VALU_PEAK / alu_slots_per_pair(w)
+    probe = _unit_peak(VALU_PROBE[w.dtype])
+    if probe and probe > model:
+        return probe, f"measured {VALU_PROBE[w.dtype]} probe ({probe:.4g} pairs/s > model {model:.4g})"
+    return model, f"issue-slot model ({alu_slots_per_pair(w)} slots per pair)"
 
 
 def _pass_roofline(w, pass_ms):
     pairs = w.n * w.m
     sec = pass_ms * 1e-3
     rate = pairs / sec
-    alu_peak = VALU_PEAK / alu_slots_per_pair(w)  # pairs/s when the VALU issue binds
-    also = {"exp_frac": rate / EXP_PEAK}
+    alu_peak, alu_basis = alu_roof(w)
+    also = {"exp_frac": rate / EXP_PEAK, "alu_roof_basis": alu_basis}
     probe, mix_rate = measured_mix_rate(w)
     if mix_rate:
         also["measured_mix_probe"] = probe
         also["measured_mix_frac"] = rate / mix_rate
     if w.d >= 32:
-        # A contraction is priced at its own dtype's peak: 2d flops per pair
-        # at the bf16 or float32 MFMA peak. float32 points run as six bf16
-        # products per coordinate pair (12d issued flops), so their fraction
-        # of the float32 peak can exceed 1; the issued bf16 work's fraction of
-        # the bf16 peak is reported beside it.
-        peak = BF16_MFMA_PEAK if w.dtype == "bf16" else F32_MFMA_PEAK
-        mfma_flops = 2.0 * w.d * pairs
-        mfma_frac = mfma_flops / sec / peak
+        # The contraction: 2d flops per pair. bf16 points issue exactly that on
+        # the bf16 matrix cores. float32 points issue six bf16 products per
+        # coordinate pair (12d flops per pair) for float32 accuracy, so their
+        # ceiling is the bf16 peak for that issued work; the fraction of the
+        # float32 MFMA peak at 2d flops per pair is kept beside it.
+        issued = (2.0 if w.dtype == "bf16" else 12.0) * w.d * pairs
+        mfma_frac = issued / sec / BF16_MFMA_PEAK
         if w.dtype != "bf16":
-            also["bf16_issued_frac"] = 12.0 * w.d * pairs / sec / BF16_MFMA_PEAK
+            also["f32_contraction_TFLOPs"] = 2.0 * w.d * pairs / sec / 1e12
+            also["f32_contraction_frac_of_f32_mfma_peak"] = 2.0 * w.d * pairs / sec / F32_MFMA_PEAK
         # the binding roof is whichever ideal time is longer
-        if mfma_flops / peak >= pairs / alu_peak:
+        if issued / BF16_MFMA_PEAK >= pairs / alu_peak:
             also["alu_frac"] = rate / alu_peak
-            return {"bound": "mfma", "achieved": mfma_flops / sec / 1e12, "peak": peak / 1e12,
+            return {"bound": "mfma", "achieved": issued / sec / 1e12, "peak": BF16_MFMA_PEAK / 1e12,
                     "unit": "TFLOP/s", "frac": mfma_frac, "traffic": None, "also": also}
         also["mfma_frac"] = mfma_frac
-        also["mfma_TFLOPs"] = mfma_flops / sec / 1e12
+        also["mfma_TFLOPs"] = issued / sec / 1e12
     return {"bound": "alu", "achieved": rate / 1e9, "peak": alu_peak / 1e9, "unit": "Gpair/s",
             "frac": rate / alu_peak, "traffic": None, "also": also}
 
@@ -262,9 +282,10 @@ def op_roofline(w, ms, value_width):
     the VALU. The longer ideal time is the bound."""
     pairs = w.n * w.m
     sec = ms * 1e-3
-    peak = BF16_MFMA_PEAK if w.dtype == "bf16" else F32_MFMA_PEAK
-    flops = 2.0 * (w.d + value_width) * pairs
-    alu_peak = VALU_PEAK / alu_slots_per_pair(w)
+    # float32 points issue six bf16 products per coordinate (scores and values)
+    peak = BF16_MFMA_PEAK
+    flops = (2.0 if w.dtype == "bf16" else 12.0) * (w.d + value_width) * pairs
+    alu_peak, _ = alu_roof(w)
     t_mfma, t_alu = flops / peak, pairs / alu_peak
     r = {"ms": ms, "mfma_frac": t_mfma / sec, "alu_frac": t_alu / sec}
     r["bound"] = "mfma" if t_mfma >= t_alu else "alu"
@@ -475,6 +496,31 @@ def cpu_baseline(case, target_s=15.0):
                       f"{tf + tg:.1f} s measured"}
 
 
+def cpu_single_thread_tiny(min_s=2.0):
+    """Scaling context for the CPU baseline: the float64 oracle on one host
+    thread, whole iterations of the tiny configuration (n = m = 1024, d = 3)."""
+    import oracle
+
+    oracle.build(force=False)
+    w = W.CASES[1]
+    inp = W.make_inputs(w)
+    x64, y64 = inp.x64(), inp.y64()
+    before = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        its, t0 = 0, time.perf_counter()
+        while True:
+            oracle.solve(x64, y64, inp.a, inp.b, w.eps, 1, w.mode)
+            its += 1
+            sec = time.perf_counter() - t0
+            if sec >= min_s:
+                break
+    finally:
+        oracle.set_threads(before)
+    return {"value": its / sec, "unit": "iters/s", "cores": 1, "kind": "oracle",
+            "sample": f"{its} whole iteration(s) of {w.name} (n=m={w.n}, d={w.d}) on one thread, {sec:.1f} s"}
+
+
 # Unit-rate microbenchmarks (streaming_sinkhorn_solver_log_amd/peaks/peaks.hip):
 # (index, name, unit of the work count, model peak per second or None, model)
 PEAK_CASES = [
@@ -636,9 +682,19 @@ def main():
         out["d3"] = {"workload": c3.w.name, "iters_per_s": r3["iters_per_s"], "ms_per_step": r3["ms_per_step"],
                      "roofline": r3["roofline"], "detail": {k: v for k, v in r3.items() if k != "roofline"}}
         del c3
+        # the same shape in the averaged schedule: both half-passes in one launch
+        print("[bench] d=3 point, symmetric schedule", file=sys.stderr, flush=True)
+        c3s = Case(6, torch, sk, dev, mode="symmetric")
+        r3s = measure(c3s, args.steps, args.warmup)
+        out["d3"]["symmetric"] = {"iters_per_s": r3s["iters_per_s"], "ms_per_step": r3s["ms_per_step"],
+                                  "solve_only_iters_per_s": r3s["solve_only_iters_per_s"],
+                                  "half_pass_ms": r3s["half_pass_ms"],
+                                  "half_pass_frac": r3s["roofline"]["frac"]}
+        del c3s
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        out["cpu_baseline"]["single_thread_tiny"] = cpu_single_thread_tiny()
     print(json.dumps(out), flush=True)
 
 

@@ -135,17 +135,22 @@ def workspace_bytes(op: int, dtype: int, n: int, m: int, d: int, k: int = 0) -> 
 
 
 def _workspace(op, dtype, n, m, d, k, device, ws):
-    """A 256-byte aligned region of at least the required size: the caller's
-    uint8 tensor if large enough, else a new one. A new tensor is allocated on
-    the current stream, which the library's launches use too, so the caching
-    allocator cannot hand it to other work before they finish."""
+    """A 256-byte aligned region of at least the required size. With ws=None a
+    new uint8 tensor is allocated on the current stream, which the library's
+    launches use too, so the caching allocator cannot hand it to other work
+    before they finish. A caller's workspace is used as given: it must be a
+    contiguous uint8 tensor on the device holding the required bytes after
+    its first 256-byte aligned address, else ValueError."""
     need = workspace_bytes(op, dtype, n, m, d, k)
     if need == 0:
         need = 256  # invalid sizes: the library reports the reason
-    if ws is not None and (ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous()):
-        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
-    if ws is None or ws.numel() < need + (-ws.data_ptr()) % 256:
+    if ws is None:
         ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    elif ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    elif ws.numel() < need + (-ws.data_ptr()) % 256:
+        raise ValueError(f"workspace holds {ws.numel()} bytes; this call needs {need} bytes after a "
+                         f"256-byte aligned start ({need + (-ws.data_ptr()) % 256} from this tensor's start)")
     off = (-ws.data_ptr()) % 256
     return ws, ws.data_ptr() + off, ws.numel() - off
 

@@ -19,6 +19,7 @@ import torch
 
 import oracle
 import workloads as W
+from tests.golden import fullsize as FS
 
 pytestmark = pytest.mark.gpu
 
@@ -544,10 +545,47 @@ def test_apply_arbitrary_potentials(sk, key, scale):
     assert eg <= tol_rel(w)
 
 
+def _check_last_iteration(sk, w, inp, x, y, a, b, T, mode, rows, cols, tag):
+    """(f_T, g_T) = solve(T) and (f', g') = solve(T + 1) from the same cold start.
+    Runs are bitwise deterministic, so the first T iterations of the second solve
+    are the first solve; its last iteration runs the shifted sweep (every pass after
+    a side's first), in the launch configuration of a T + 1 iteration solve. On
+    sampled rows and columns, f' and g' are compared with the oracle's maps at the
+    GPU's own pair:
+      alternating: f' = F(g_T) and g' = G(f');
+      symmetric:   f' = (f_T + F(g_T)) / 2 and g' = (g_T + G(f_T)) / 2.
+    The cost of the returned pair is compared with <a, f'> + <b, g'> in float64."""
+    fT, gT, _ = sk.solve(x, y, a, b, w.eps, T, mode)
+    f1, g1, cost = sk.solve(x, y, a, b, w.eps, T + 1, mode)
+    assert torch.isfinite(f1).all() and torch.isfinite(g1).all()
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    fT, gT, f1n, g1n = t(fT), t(gT), t(f1), t(g1)
+    x64, y64 = inp.x64(), inp.y64()
+    Fr = oracle.F(x64[rows], y64, inp.b, gT, w.eps)
+    if mode == "alternating":
+        fr = Fr
+        gr = oracle.G(x64, y64[cols], inp.a, f1n, w.eps)
+    else:
+        fr = 0.5 * (fT[rows] + Fr)
+        gr = 0.5 * (gT[cols] + oracle.G(x64, y64[cols], inp.a, fT, w.eps))
+    ef = np.abs(f1n[rows] - fr).max()
+    eg = np.abs(g1n[cols] - gr).max()
+    tf, tg = tol_pot(w, fr), tol_pot(w, gr)
+    s64 = float(np.dot(inp.a.astype(np.float64), f1n) + np.dot(inp.b.astype(np.float64), g1n))
+    scale = float(np.abs(inp.a * f1n).sum() + np.abs(inp.b * g1n).sum())
+    ec = abs(float(cost) - s64)
+    say(f"  {tag}: iteration {T + 1} ({mode}) sampled max|df|={ef:.3e} (tol {tf:.1e}) "
+        f"max|dg|={eg:.3e} (tol {tg:.1e}); cost {float(cost):.10g} vs <a,f>+<b,g> {s64:.10g}")
+    assert ef <= tf and eg <= tg
+    assert ec <= 1e-9 * max(scale, 1e-300)
+    return f1, g1, f1n, g1n
+
+
 SPLIT_SHAPES = [
     (6, 200_000, 700),    # far more row blocks than resident workgroups; 6 stages -> one column chunk
     (6, 700, 200_000),    # few row blocks, many stages: every row block merged from many partials
     (3, 130_000, 900),    # bf16 d = 64, wide row range
+    (3, 900, 130_000),    # bf16 d = 64, several column chunks per row block
     (1, 300, 300),        # a single workgroup per side
     (1, 33, 4000),
 ]
@@ -555,62 +593,42 @@ SPLIT_SHAPES = [
 
 @pytest.mark.parametrize("key,n,m", SPLIT_SHAPES)
 def test_work_split_regimes(sk, key, n, m):
-    """Shapes at the edges of the balanced work split, checked on sampled rows of the
-    last half-pass: F(g) for rows of x and G(f) for rows of y."""
+    """Shapes at the edges of the balanced work split: the last iteration of a
+    4-iteration solve (shifted sweep) on sampled rows and columns."""
     w = W.CASES[key].scaled(n, m, 3)
     say(f"work split cfg={key} n={n} m={m} d={w.d} {w.dtype}")
     inp = W.make_inputs(w)
     x, y, a, b = dev(inp)
-    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, "alternating")
-    assert torch.isfinite(f).all() and torch.isfinite(g).all()
-    f1, g1, _ = sk.solve(x, y, a, b, w.eps, 1, "alternating", f0=f, g0=g)
     rng = np.random.default_rng(1)
     rows = np.sort(rng.choice(n, min(n, 64), replace=False))
     cols = np.sort(rng.choice(m, min(m, 64), replace=False))
-    x64, y64 = inp.x64(), inp.y64()
-    f1n = f1.cpu().numpy().astype(np.float64)
-    fr = oracle.F(x64[rows], y64, inp.b, g.cpu().numpy().astype(np.float64), w.eps)
-    gr = oracle.G(x64, y64[cols], inp.a, f1n, w.eps)
-    tf = 1e-3 * max(np.abs(fr).max(), w.eps) if w.dtype == "bf16" else 1e-4 * w.eps
-    tg = 1e-3 * max(np.abs(gr).max(), w.eps) if w.dtype == "bf16" else 1e-4 * w.eps
-    ef = np.abs(f1n[rows] - fr).max()
-    eg = np.abs(g1.cpu().numpy()[cols] - gr).max()
-    say(f"  sampled max|df|={ef:.3e} (tol {tf:.1e}) max|dg|={eg:.3e} (tol {tg:.1e})")
-    assert ef <= tf and eg <= tg
+    _check_last_iteration(sk, w, inp, x, y, a, b, w.iters, "alternating", rows, cols, "work split")
 
 
 @pytest.mark.parametrize("key", [2, 3, 4, 5, 6, 7])
 def test_full_size_sampled_rows(sk, key):
     """Every configuration at full size, in the benchmark's launch configuration:
-    the solve, the gradient and both applications, checked on sampled rows and
-    columns that the oracle computes one by one."""
+    the last iteration of the configured solve (the shifted sweep: at n = m = 50k
+    and d = 64 over two column chunks, at n = m = 10k both half-passes of the
+    averaged schedule in one launch, at d >= 512 the GEMM-tiled passes), then the
+    gradient and both applications at the returned pair, checked on sampled rows
+    and columns that the oracle computes one by one."""
     w = W.CASES[key]
     say(f"full size cfg={key} n={w.n} m={w.m} d={w.d} {w.dtype} iters={w.iters} mode={w.mode}")
     inp = W.make_inputs(w, k=16)
     x, y, a, b = dev(inp)
-    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
-    assert torch.isfinite(f).all() and torch.isfinite(g).all()
-    # one more alternating iteration from (f, g): its f is F(g) and its g is G(F(g))
-    f1, g1, _ = sk.solve(x, y, a, b, w.eps, 1, "alternating", f0=f, g0=g)
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(w.n, 96, replace=False))
     cols = np.sort(rng.choice(w.m, 96, replace=False))
-    gT = g.cpu().numpy().astype(np.float64)
-    f1n = f1.cpu().numpy().astype(np.float64)
-    g1n = g1.cpu().numpy().astype(np.float64)
+    f1, g1, f1n, g1n = _check_last_iteration(sk, w, inp, x, y, a, b, w.iters - 1, w.mode, rows, cols,
+                                             "full size")
     x64, y64 = inp.x64(), inp.y64()
-    fr = oracle.F(x64[rows], y64, inp.b, gT, w.eps)
-    gr = oracle.G(x64, y64[cols], inp.a, f1n, w.eps)
-    ef = np.abs(f1n[rows] - fr).max()
-    eg = np.abs(g1n[cols] - gr).max()
-    tf, tg = tol_pot(w, fr), tol_pot(w, gr)
-    say(f"  sampled max|df|={ef:.3e} (tol {tf:.1e}) max|dg|={eg:.3e} (tol {tg:.1e})")
-    assert ef <= tf and eg <= tg
-    # the last half-pass was the g-pass: the plan's column sums are b
-    colsum = sk.transport_apply(x, y, a, b, f1, g1, w.eps, torch.ones(w.n, device=DEV), transpose=True)
-    rel = ((colsum - b).abs() / b).max().item()
-    say(f"  column-sum rel err {rel:.3e}")
-    assert rel <= max(1e-4, tol_rel(w))
+    if w.mode == "alternating":
+        # the last half-pass was the g-pass: the plan's column sums are b
+        colsum = sk.transport_apply(x, y, a, b, f1, g1, w.eps, torch.ones(w.n, device=DEV), transpose=True)
+        rel = ((colsum - b).abs() / b).max().item()
+        say(f"  column-sum rel err {rel:.3e}")
+        assert rel <= max(1e-4, tol_rel(w))
     # gradient (final g) and the applications (GPU potentials fed to both sides)
     a_s = inp.a[rows]
     grad = sk.eot_grad_x(x, y, a, b, g1, w.eps).cpu().numpy()[rows]
@@ -625,6 +643,66 @@ def test_full_size_sampled_rows(sk, key):
     e2 = np.abs(PtU - ref2).max() / np.abs(ref2).max()
     say(f"  sampled rel err grad {e_g:.3e}  P.V {e1:.3e}  P^T.U {e2:.3e} (tol {tol_rel(w):.0e})")
     assert e_g <= tol_rel(w) and e1 <= tol_rel(w) and e2 <= tol_rel(w)
+
+
+@pytest.mark.parametrize("key", FS.KEYS)
+def test_full_size_against_stored_oracle(sk, key):
+    """End to end at full size: the configured solve against the float64 oracle's
+    own solve of the same inputs (stored by tests/golden/make_oracle_fullsize.py,
+    keyed by digests of the inputs and of the oracle source): every entry of f and
+    g, and the cost. Then the gradient and applications from the GPU's own
+    potentials against the oracle's from its own; their bounds add, to the
+    tolerance of a single evaluation, what the potential differences measured
+    here can move a plan entry: |dP_ij| <= P_ij (exp((|df_i| + |dg_j|)/eps) - 1),
+    and a softmax weight of the gradient at most by exp(2 |dg|_inf / eps) - 1."""
+    w = W.CASES[key]
+    ref = FS.load(w)
+    if ref is None:
+        pytest.skip(f"no stored reference for {w.name} (tests/golden/make_oracle_fullsize.py)")
+    inp = W.make_inputs(w)
+    meta = ref["meta"]
+    assert meta["input_sha256"] == FS.input_digest(inp), "inputs changed: the stored reference is stale"
+    assert meta["oracle_sha256"] == FS.oracle_digest(), "oracle changed: the stored reference is stale"
+    say(f"stored oracle cfg={key} n={w.n} m={w.m} d={w.d} {w.dtype} iters={w.iters} mode={w.mode}")
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    t = lambda v: v.cpu().numpy().astype(np.float64)  # noqa: E731
+    fn, gn = t(f), t(g)
+    fr, gr, cr = ref["f"], ref["g"], float(ref["cost"])
+    dfv, dgv = np.abs(fn - fr), np.abs(gn - gr)
+    ef, eg = dfv.max(), dgv.max()
+    # gauge-free view (the (c, -c) direction is neutral under both maps)
+    c = float(np.dot(inp.a, fn - fr))
+    eq = max(np.abs(fn - fr - c).max(), np.abs(gn - gr + c).max())
+    ec = abs(float(cost) - cr) / abs(cr)
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} (tol {tol_pot(w, fr):.1e}; gauge-free {eq:.3e}) "
+        f"cost {float(cost):.10g} vs {cr:.10g} rel {ec:.2e} (tol {tol_rel(w):.0e})")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert ec <= tol_rel(w)
+    x64, y64 = inp.x64(), inp.y64()
+    if "grad" in ref:
+        rows = ref["grad_rows"]
+        grad = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()[rows].astype(np.float64)
+        gref = ref["grad"]
+        dg = gn - gr  # the softmax over j ignores a constant shift of g
+        spread = np.expm1(2.0 * 0.5 * (dg.max() - dg.min()) / w.eps)
+        reach = np.abs(y64).max(axis=0)[None, :] + np.abs(x64[rows])
+        bound = tol_rel(w) * np.abs(gref).max() + 2.0 * inp.a[rows, None] * spread * reach
+        worst = (np.abs(grad - gref) / bound).max()
+        say(f"  gradient rows {len(rows)}: max|d|={np.abs(grad - gref).max():.3e}, worst share of bound {worst:.3f}")
+        assert worst <= 1.0
+    if "pv" in ref:
+        inpk = W.make_inputs(w, k=w.apply_k)
+        V, U = torch.from_numpy(inpk.V).to(DEV), torch.from_numpy(inpk.U).to(DEV)
+        rows, cols = ref["pv_rows"], ref["ptu_cols"]
+        PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy()[rows]
+        PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy()[cols]
+        b1 = tol_rel(w) * np.abs(ref["pv"]).max() + np.expm1((dfv[rows, None] + eg) / w.eps) * ref["pv_abs"]
+        b2 = tol_rel(w) * np.abs(ref["ptu"]).max() + np.expm1((dgv[cols, None] + ef) / w.eps) * ref["ptu_abs"]
+        w1 = (np.abs(PV - ref["pv"]) / b1).max()
+        w2 = (np.abs(PtU - ref["ptu"]) / b2).max()
+        say(f"  P.V rows {len(rows)} worst share of bound {w1:.3f}; P^T.U cols {len(cols)} {w2:.3f}")
+        assert w1 <= 1.0 and w2 <= 1.0
 
 
 DIV_CASES = [
