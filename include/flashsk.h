@@ -122,9 +122,11 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
  *   iters_done out (host): iterations run.
  *   err        out (host): the last error measured (of the pair before the
  *              last iteration; the returned pair is one iteration further).
- * BLOCKING: synchronizes `stream` at every check. Between checks the solve
- * restarts from the current pair (SK_WARM_START), so the pairs differ from an
- * uninterrupted sk_sinkhorn_solve of the same length by rounding only.
+ *   flags      SK_WARM_START, SK_NO_CENTER, SK_CHECK_FINITE (as for the solve).
+ * BLOCKING: synchronizes `stream` at every check. The iterations at eps run in
+ * one workspace lifetime (one prep; every pass after each side's first uses
+ * the shifted sweep), so without eps-scaling the returned pair is bitwise the
+ * one sk_sinkhorn_solve returns for iters = iters_done.
  * Workspace: sk_workspace_bytes(SK_OP_SOLVE_TOL, dtype, n, m, d, 0).
  */
 int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
@@ -211,7 +213,8 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
  * each OT the cost <a,f> + <b,g> of a fixed-budget solve of `iters`
  * iterations: the cross term with `mode`, the two self terms with
  * SK_SYMMETRIC (which keeps their f = g).
- *   flags      SK_NO_CENTER only (warm starts do not apply).
+ *   flags      SK_NO_CENTER, SK_CHECK_FINITE (screens x, y, a, b once, as
+ *              for the solve); warm starts do not apply.
  *   div        out: one double, S.
  *   grad_a     out (n, or NULL): f_ab - f_aa, the gradient of S in a along
  *              mass-preserving directions (off the simplex it holds up to an

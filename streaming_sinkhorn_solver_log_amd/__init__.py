@@ -221,18 +221,19 @@ def eot_grad_x(x, y, a, b, g, eps: float, workspace=None):
 
 
 def sinkhorn_divergence(x, y, a, b, eps: float, iters: int, mode: str = "alternating", grads: bool = True,
-                        center: bool = True, workspace=None):
+                        center: bool = True, workspace=None, check_finite: bool = False):
     """Debiased Sinkhorn divergence S = OT(a,b) - OT(a,a)/2 - OT(b,b)/2 (flashsk.h).
 
     Returns (S, grad_a, grad_b, grad_x, grad_y): S a 0-d float64 tensor, the
-    gradients float32 (None when grads=False).
+    gradients float32 (None when grads=False). check_finite: screen x, y, a, b
+    on the device first (as for solve).
     """
     n, m, d, dt = _points(x, y)
     dev = x.device
     _vec(a, n, "a", dev)
     _vec(b, m, "b", dev)
     mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
-    flags = 0 if center else SK_NO_CENTER
+    flags = (0 if center else SK_NO_CENTER) | (SK_CHECK_FINITE if check_finite else 0)
     S = torch.empty((), dtype=torch.float64, device=dev)
     ga = gb = gx = gy = None
     if grads:
@@ -280,7 +281,7 @@ def transport_apply_hadamard(x, y, a, b, f, g, eps: float, A, B, V, transpose: b
 
 def solve_tol(x, y, a, b, eps: float, tol: float, max_iters: int, mode: str = "alternating",
               check_every: int = 10, f0=None, g0=None, center: bool = True, eps_start: float = 0.0,
-              workspace=None):
+              workspace=None, check_finite: bool = False):
     """Sinkhorn until the marginal error ||P1 - a||_1 + ||P^T 1 - b||_1 of the
     pair checked every `check_every` iterations is <= tol (or max_iters), after
     an optional eps-scaling from eps_start (one iteration per halving).
@@ -290,7 +291,7 @@ def solve_tol(x, y, a, b, eps: float, tol: float, max_iters: int, mode: str = "a
     _vec(a, n, "a", dev)
     _vec(b, m, "b", dev)
     mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
-    flags = 0 if center else SK_NO_CENTER
+    flags = (0 if center else SK_NO_CENTER) | (SK_CHECK_FINITE if check_finite else 0)
     if (f0 is None) != (g0 is None):
         raise ValueError("give both f0 and g0 for a warm start, or neither")
     if f0 is not None:

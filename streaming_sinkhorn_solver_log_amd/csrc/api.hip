@@ -37,23 +37,11 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(SK_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
-namespace {
-bool force_valu() {
-  static const bool v = [] {
-    const char* e = getenv("FLASHSK_PATH");
-    return e && strcmp(e, "valu") == 0;
-  }();
-  return v;
-}
-}  // namespace
-
 // Kernel family of a call: the matrix-core kernels with register-resident row
 // records when they fit (bf16: d <= 128, float32: d <= 21), else the GEMM-tiled
-// matrix-core kernels (d <= 4096). FLASHSK_PATH=valu selects the vector-ALU
-// kernels where they apply (d <= 64, for comparisons).
+// matrix-core kernels (d <= 4096).
 Path solve_path(int dtype, int64_t d) {
   if (d < 1) return Path::None;
-  if (force_valu() && d <= 64) return Path::Valu;
   if (d <= 4096 && mfma_nkb(dtype, (int)d) > 0) return Path::Mfma;
   if (d <= 4096) return Path::Gemm;
   return Path::None;
@@ -81,6 +69,24 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
   return SK_OK;
 }
 
+// SK_CHECK_FINITE: screens the inputs on the device and waits for the
+// verdict, so that a bad input fails before the solve enqueues anything that
+// writes f, g or cost. `word` is a workspace word the caller re-initializes
+// (f, g: warm-start potentials, or null).
+int screen_inputs(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                  const float* b, const float* f, const float* g, unsigned* word, hipStream_t s) {
+  hipError_t e = launch_check_inputs(x, y, dtype, n, m, d, a, b, f, g, word, s);
+  unsigned bits = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bits, word, sizeof(bits), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "input check");
+  if (bits & kBadPoints) return fail(SK_ERR_INVALID_ARG, "x or y holds a NaN or an infinity");
+  if (bits & kBadWeights) return fail(SK_ERR_INVALID_ARG, "a or b holds a negative, NaN or infinite weight");
+  if (!(bits & kPositiveA) || !(bits & kPositiveB)) return fail(SK_ERR_INVALID_ARG, "a or b has no positive weight");
+  if (bits & kBadPotentials) return fail(SK_ERR_INVALID_ARG, "the starting f or g holds a NaN or an infinity");
+  return SK_OK;
+}
+
 }  // namespace api
 
 namespace {
@@ -105,15 +111,6 @@ bool force_exact_enabled() {
 }
 
 // ---------------------------------------------------------------- workspace layouts
-// Vector-ALU layout of one side: packed float32 points and per-point vectors.
-struct Side {
-  float* pts;
-  float* alpha;
-  float* lw;
-  float* h[2];
-  float* L;
-};
-
 // Matrix-core layout of one side: row-form and column-form records, bias records.
 struct SideM {
   bf16x8* row_rec;
@@ -134,17 +131,6 @@ struct Common {
   double* centroid;
   float* shift;
 };
-
-Side carve_side(Carve& c, int64_t cnt, int dp) {
-  Side s;
-  s.pts = c.take<float>((size_t)cnt * dp);
-  s.alpha = c.take<float>(cnt);
-  s.lw = c.take<float>(cnt);
-  s.h[0] = c.take<float>(cnt);
-  s.h[1] = c.take<float>(cnt);
-  s.L = c.take<float>(cnt);
-  return s;
-}
 
 SideM carve_side_m(Carve& c, int64_t cnt, int nkb, int row_blocks) {
   SideM s;
@@ -218,16 +204,12 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
     sp.wide = dtype == SK_F32;
     sp.f = plan_gemm_pass(n, m, sp.wide);
     sp.g = plan_gemm_pass(m, n, sp.wide);
-  } else {
-    sp.f = plan_valu_pass(n, m, (int)d);
-    sp.g = plan_valu_pass(m, n, (int)d);
   }
   return sp;
 }
 
 struct SolveWs {
-  Side x, y;     // vector-ALU path
-  SideM xm, ym;  // matrix-core path
+  SideM xm, ym;
   Common c;
   size_t bytes;
 };
@@ -242,36 +224,9 @@ int solve_counters(const SolvePlan& sp) {
 SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_t d) {
   Carve c{static_cast<char*>(ws)};
   SolveWs L{};
-  if (sp.path == Path::Mfma || sp.path == Path::Gemm) {
-    L.xm = carve_side_m(c, n, sp.nkb, sp.f.row_blocks);
-    L.ym = carve_side_m(c, m, sp.nkb, sp.g.row_blocks);
-  } else {
-    L.x = carve_side(c, n, valu_dp((int)d));
-    L.y = carve_side(c, m, valu_dp((int)d));
-  }
+  L.xm = carve_side_m(c, n, sp.nkb, sp.f.row_blocks);
+  L.ym = carve_side_m(c, m, sp.nkb, sp.g.row_blocks);
   L.c = carve_common(c, part_f2(sp.f, n, sp.g, m, sp.fused), solve_counters(sp), d);
-  L.bytes = c.off;
-  return L;
-}
-
-// Gradient and transport application: vector-ALU layout plus wider partials.
-size_t wide_part_floats(const PassPlan& pl, int64_t nr, int64_t rec) {
-  return pl.splits > 1 ? (size_t)pl.splits * nr * rec : 0;
-}
-
-struct AuxWs {
-  Side x, y;
-  Common c;
-  size_t bytes;
-};
-
-AuxWs layout_aux(void* ws, int64_t n, int64_t m, int64_t d, const PassPlan& pl, int64_t nr,
-                 int64_t rec) {
-  Carve c{static_cast<char*>(ws)};
-  AuxWs L{};
-  L.x = carve_side(c, n, valu_dp((int)d));
-  L.y = carve_side(c, m, valu_dp((int)d));
-  L.c = carve_common(c, (wide_part_floats(pl, nr, rec) + 1) / 2, pl.row_blocks, d);
   L.bytes = c.off;
   return L;
 }
@@ -313,8 +268,6 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
     ap.nobt = ap.nchunks * ap.nob;
     ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks);
-  } else {
-    ap.pl = plan_valu_pass(ap.nr, ap.nc, (int)d);
   }
   return ap;
 }
@@ -343,9 +296,8 @@ AuxWsM layout_aux_m(void* ws, const AuxPlan& ap, int64_t n, int64_t m, int64_t d
   return L;
 }
 
-// Workspace of a transport application (vector-ALU partials: k floats per split).
-size_t aux_bytes(const AuxPlan& ap, int64_t n, int64_t m, int64_t d, int64_t k) {
-  if (ap.path == Path::Valu) return layout_aux(nullptr, n, m, d, ap.pl, ap.nr, k).bytes;
+// Workspace of a transport application or gradient.
+size_t aux_bytes(const AuxPlan& ap, int64_t n, int64_t m, int64_t d) {
   return layout_aux_m(nullptr, ap, n, m, d).bytes;
 }
 
@@ -384,53 +336,22 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   return SK_OK;
 }
 
-hipError_t prep_valu(const Side& X, const Side& Y, const Common& C, const void* x, const void* y,
-                     int dtype, int64_t n, int64_t m, int64_t d, const float* a, const float* b,
-                     const float* f_start, const float* g_start, float* f_zero, float* g_zero,
-                     bool center, int n_counters, const Scalars& sc, hipStream_t s) {
-  PrepSide px{x, a, f_start, f_zero, X.pts, X.alpha, X.lw, X.h[0], n};
-  PrepSide py{y, b, g_start, g_zero, Y.pts, Y.alpha, Y.lw, Y.h[0], m};
-  return launch_prep(px, py, dtype, (int)d, valu_dp((int)d), center, C.centroid, C.shift,
-                     C.counters, n_counters, sc.log2e_over_eps, s);
-}
-
-int solve_valu(const SolveWs& L, const SolvePlan& sp, int64_t n, int64_t m, int64_t d,
-               int iters, bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
-  int cur = 0;
-  hipError_t e;
-  for (int t = 0; t < iters; ++t) {
-    const int nxt = sym ? 1 - cur : cur;
-    PassArgs pf{};
-    pf.rows = L.x.pts; pf.cols = L.y.pts; pf.hcol = L.y.h[cur];
-    pf.alpha = L.x.alpha; pf.lw = L.x.lw; pf.pot = f; pf.hout = L.x.h[nxt]; pf.Lout = L.x.L;
-    pf.part = L.c.part; pf.counters = L.c.counters; pf.nr = (int)n; pf.nc = (int)m;
-    pf.splits = sp.f.splits; pf.cols_per_split = sp.f.cols_per_split;
-    pf.c2 = sc.c2; pf.neg_eps_ln2 = sc.neg_eps_ln2; pf.log2e_over_eps = sc.log2e_over_eps;
-    pf.symmetric = sym;
-    if ((e = launch_lse_valu(pf, (int)d, sp.f, s)) != hipSuccess) return hip_fail(e, "f half-pass");
-    PassArgs pg = pf;
-    pg.rows = L.y.pts; pg.cols = L.x.pts; pg.hcol = L.x.h[cur];  // alternating: the new f's bias
-    pg.alpha = L.y.alpha; pg.lw = L.y.lw; pg.pot = g; pg.hout = L.y.h[nxt]; pg.Lout = L.y.L;
-    pg.nr = (int)m; pg.nc = (int)n; pg.splits = sp.g.splits; pg.cols_per_split = sp.g.cols_per_split;
-    if ((e = launch_lse_valu(pg, (int)d, sp.g, s)) != hipSuccess) return hip_fail(e, "g half-pass");
-    cur = nxt;
-  }
-  return SK_OK;
-}
-
 hipError_t launch_pass(const SolvePlan& sp, const MfmaPassArgs& a, bool shifted, bool scaled,
                        const PassPlan& pl, hipStream_t s) {
   if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, sp.wide, pl, s);
   return launch_lse_mfma(a, sp.nkb, shifted, scaled, sp.merged, pl, s);
 }
 
-int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int64_t m, int iters,
-               bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
-  int cur = 0;
+// Iterations t0 .. t0 + iters - 1 of a solve whose prep has run (t counts the
+// iterations since the prep: each side's first pass, t = 0, is the exact
+// sweep, every later one the shifted sweep). `cur` selects the bias buffers the
+// next iteration reads (the averaged schedule alternates them).
+int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int64_t m, int t0, int iters,
+               int& cur, bool sym, float* f, float* g, const Scalars& sc, hipStream_t s) {
   hipError_t e;
   const bool scaled = dtype == SK_BF16;
   const int force_exact = force_exact_enabled() ? 1 : 0;
-  for (int t = 0; t < iters; ++t) {
+  for (int t = t0; t < t0 + iters; ++t) {
     const int nxt = sym ? 1 - cur : cur;
     // Each side's first pass has no previous log-sum-exp to shift by: exact sweep.
     const bool shifted = t > 0;
@@ -481,6 +402,62 @@ int solve_mfma(const SolveWs& L, const SolvePlan& sp, int dtype, int64_t n, int6
   return SK_OK;
 }
 
+// The state of one solve between its launches: plan, workspace layout and the
+// position in the schedule. solve_begin validates the workspace, screens the
+// inputs when asked, and runs the prep; solve_iterate then adds iterations, so
+// a caller can stop between them (to measure an error) and continue with the
+// same records, biases and shifted-sweep state.
+struct SolveState {
+  SolvePlan sp;
+  SolveWs L;
+  Scalars sc;
+  int dtype;
+  int64_t n, m, d;
+  bool sym;
+  int t;    // iterations since the prep
+  int cur;  // bias buffers the next iteration reads
+};
+
+int solve_begin(SolveState& st, const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                const float* a, const float* b, double eps, int mode, uint32_t flags, float* f, float* g,
+                void* ws, size_t ws_bytes, hipStream_t s) {
+  st.sp = plan_solve(dtype, n, m, d, mode == SK_ALTERNATING);
+  int rc = check_ws(ws, ws_bytes, layout_solve(nullptr, st.sp, n, m, d).bytes);
+  if (rc) return rc;
+  st.L = layout_solve(ws, st.sp, n, m, d);
+  st.sc = scalars(eps);
+  st.dtype = dtype;
+  st.n = n;
+  st.m = m;
+  st.d = d;
+  st.sym = mode == SK_SYMMETRIC;
+  st.t = 0;
+  st.cur = 0;
+  const bool warm = (flags & SK_WARM_START) != 0;
+  if ((flags & SK_CHECK_FINITE) &&
+      (rc = screen_inputs(x, y, dtype, n, m, d, a, b, warm ? f : nullptr, warm ? g : nullptr, st.L.c.counters, s)))
+    return rc;
+  const SolveWs& L = st.L;
+  MfmaPrepSide px{x, a, warm ? f : nullptr, warm ? nullptr : f, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw,
+                  L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
+  MfmaPrepSide py{y, b, warm ? g : nullptr, warm ? nullptr : g, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw,
+                  L.ym.bias[0], L.ym.bias[1], L.ym.hval[0], m};
+  px.hacc = L.xm.hacc[0]; px.hacc_alt = L.xm.hacc[1];
+  py.hacc = L.ym.hacc[0]; py.hacc_alt = L.ym.hacc[1];
+  // counters and the exact-fallback count are zeroed together (adjacent)
+  hipError_t e = launch_prep_mfma(px, py, dtype, (int)d, st.sp.nkb, st.sp.merged, (flags & SK_NO_CENTER) == 0,
+                                  L.c.centroid, L.c.shift, L.c.counters, solve_counters(st.sp) + 1,
+                                  st.sc.log2e_over_eps, st.sc.c2, st.sp.path == Path::Gemm, s);
+  if (e != hipSuccess) return hip_fail(e, "prep");
+  return SK_OK;
+}
+
+int solve_iterate(SolveState& st, int iters, float* f, float* g, hipStream_t s) {
+  const int rc = solve_mfma(st.L, st.sp, st.dtype, st.n, st.m, st.t, iters, st.cur, st.sym, f, g, st.sc, s);
+  st.t += iters;
+  return rc;
+}
+
 }  // namespace
 
 namespace api {
@@ -493,13 +470,54 @@ size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
 }
 
 size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
-  return aux_bytes(plan_aux(dtype, n, m, d, k, false, transpose), n, m, d, k);
+  return aux_bytes(plan_aux(dtype, n, m, d, k, false, transpose), n, m, d);
 }
 
 size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
-  const AuxPlan ap = plan_aux(dtype, n, m, d, d, true, 0);
-  if (ap.path == Path::Valu) return layout_aux(nullptr, n, m, d, ap.pl, n, 2 + valu_dclass((int)d)).bytes;
-  return layout_aux_m(nullptr, ap, n, m, d).bytes;
+  return aux_bytes(plan_aux(dtype, n, m, d, d, true, 0), n, m, d);
+}
+
+int solve_to_tolerance(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                       const float* b, double eps, int mode, uint32_t flags, int32_t max_iters, int32_t check_every,
+                       double tol, float* f, float* g, double* cost, TolScratch scratch, int32_t* iters_done,
+                       double* err, void* ws, size_t ws_bytes, hipStream_t s) {
+  SolveState st;
+  int rc = solve_begin(st, x, y, dtype, n, m, d, a, b, eps, mode, flags & ~SK_CHECK_FINITE, f, g, ws, ws_bytes, s);
+  if (rc) return rc;
+  const double inv_eps = 1.0 / eps;
+  const bool avg = mode == SK_SYMMETRIC;
+  int32_t done = 0;
+  double e_host = INFINITY;
+  hipError_t e;
+  while (done < max_iters) {
+    // iterations up to the next check, then the checking iteration itself
+    const int32_t left = max_iters - done;
+    const int32_t run = (check_every - 1 < left - 1) ? check_every - 1 : left - 1;
+    if (run > 0) {
+      if ((rc = solve_iterate(st, run, f, g, s))) return rc;
+      done += run;
+    }
+    // alternating: the columns of the checked pair are exact only once this
+    // loop's own g-step produced it, so a check of the starting pair is skipped
+    const bool measurable = avg || done > 0;
+    if (measurable && ((e = hipMemcpyAsync(scratch.f0, f, n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+                       (e = hipMemcpyAsync(scratch.g0, g, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess))
+      return hip_fail(e, "copy");
+    if ((rc = solve_iterate(st, 1, f, g, s))) return rc;
+    done += 1;
+    if (!measurable) continue;
+    if ((e = launch_marginal_error(a, scratch.f0, f, n, inv_eps, avg, false, scratch.err, s)) != hipSuccess ||
+        (avg && (e = launch_marginal_error(b, scratch.g0, g, m, inv_eps, true, true, scratch.err, s)) != hipSuccess))
+      return hip_fail(e, "marginal error");
+    if ((e = hipMemcpyAsync(&e_host, scratch.err, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "marginal error");
+    if (e_host <= tol) break;
+  }
+  if ((e = launch_cost(a, f, n, b, g, m, cost, s)) != hipSuccess) return hip_fail(e, "cost");
+  *iters_done = done;
+  *err = e_host;
+  return SK_OK;
 }
 
 }  // namespace api
@@ -545,24 +563,6 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
   }
 }
 
-// SK_CHECK_FINITE: screens the inputs on the device and waits for the
-// verdict, so that a bad input fails before the solve enqueues anything that
-// writes f, g or cost. `word` is a workspace word the solve re-initializes.
-static int screen_inputs(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
-                         const float* a, const float* b, bool warm, const float* f, const float* g,
-                         unsigned* word, hipStream_t s) {
-  hipError_t e = launch_check_inputs(x, y, dtype, n, m, d, a, b, warm ? f : nullptr, warm ? g : nullptr, word, s);
-  unsigned bits = 0;
-  if (e == hipSuccess) e = hipMemcpyAsync(&bits, word, sizeof(bits), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return hip_fail(e, "input check");
-  if (bits & kBadPoints) return fail(SK_ERR_INVALID_ARG, "x or y holds a NaN or an infinity");
-  if (bits & kBadWeights) return fail(SK_ERR_INVALID_ARG, "a or b holds a negative, NaN or infinite weight");
-  if (!(bits & kPositiveA) || !(bits & kPositiveB)) return fail(SK_ERR_INVALID_ARG, "a or b has no positive weight");
-  if (bits & kBadPotentials) return fail(SK_ERR_INVALID_ARG, "the starting f or g holds a NaN or an infinity");
-  return SK_OK;
-}
-
 int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                       const float* a, const float* b, double eps, int32_t iters, int mode,
                       uint32_t flags, float* f, float* g, double* cost, void* ws, size_t ws_bytes,
@@ -575,50 +575,19 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
   if (flags & ~(SK_WARM_START | SK_NO_CENTER | SK_CHECK_FINITE))
     return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
-  const SolvePlan sp = plan_solve(dtype, n, m, d, mode == SK_ALTERNATING);
-  const size_t need = layout_solve(nullptr, sp, n, m, d).bytes;
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  const SolveWs L = layout_solve(ws, sp, n, m, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((flags & SK_CHECK_FINITE) && (rc = screen_inputs(x, y, dtype, n, m, d, a, b, (flags & SK_WARM_START) != 0,
-                                                       f, g, L.c.counters, s)))
-    return rc;
-  const Scalars sc = scalars(eps);
-  const bool warm = (flags & SK_WARM_START) != 0;
-  const bool center = (flags & SK_NO_CENTER) == 0;
-  const bool sym = (mode == SK_SYMMETRIC);
-  const int ncnt = solve_counters(sp);
-  const float* f_start = warm ? f : nullptr;
-  const float* g_start = warm ? g : nullptr;
-  float* f_zero = warm ? nullptr : f;
-  float* g_zero = warm ? nullptr : g;
-  hipError_t e;
-  if (sp.path == Path::Mfma || sp.path == Path::Gemm) {
-    MfmaPrepSide px{x, a, f_start, f_zero, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw,
-                    L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
-    MfmaPrepSide py{y, b, g_start, g_zero, L.ym.row_rec, L.ym.col_rec, L.ym.alpha, L.ym.lw,
-                    L.ym.bias[0], L.ym.bias[1], L.ym.hval[0], m};
-    px.hacc = L.xm.hacc[0]; px.hacc_alt = L.xm.hacc[1];
-    py.hacc = L.ym.hacc[0]; py.hacc_alt = L.ym.hacc[1];
-    // counters and the exact-fallback count are zeroed together (adjacent)
-    e = launch_prep_mfma(px, py, dtype, (int)d, sp.nkb, sp.merged, center, L.c.centroid, L.c.shift,
-                         L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, sp.path == Path::Gemm, s);
-    if (e != hipSuccess) return hip_fail(e, "prep");
-    if ((rc = solve_mfma(L, sp, dtype, n, m, iters, sym, f, g, sc, s))) return rc;
-    if (debug_enabled()) {
-      unsigned cnt = 0;
-      if (hipMemcpyAsync(&cnt, L.c.exact_count, sizeof(cnt), hipMemcpyDeviceToHost, s) == hipSuccess &&
-          hipStreamSynchronize(s) == hipSuccess)
-        fprintf(stderr, "[flashsk] solve n=%lld m=%lld d=%lld iters=%d: %u workgroup(s) used the exact fallback\n",
-                (long long)n, (long long)m, (long long)d, iters, cnt);
-    }
-  } else {
-    e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, f_start, g_start, f_zero, g_zero,
-                  center, ncnt, sc, s);
-    if (e != hipSuccess) return hip_fail(e, "prep");
-    if ((rc = solve_valu(L, sp, n, m, d, iters, sym, f, g, sc, s))) return rc;
+  SolveState st;
+  if ((rc = solve_begin(st, x, y, dtype, n, m, d, a, b, eps, mode, flags, f, g, ws, ws_bytes, s))) return rc;
+  if ((rc = solve_iterate(st, iters, f, g, s))) return rc;
+  if (debug_enabled()) {
+    unsigned cnt = 0;
+    if (hipMemcpyAsync(&cnt, st.L.c.exact_count, sizeof(cnt), hipMemcpyDeviceToHost, s) == hipSuccess &&
+        hipStreamSynchronize(s) == hipSuccess)
+      fprintf(stderr, "[flashsk] solve n=%lld m=%lld d=%lld iters=%d: %u workgroup(s) used the exact fallback\n",
+              (long long)n, (long long)m, (long long)d, iters, cnt);
   }
-  if ((e = launch_cost(a, f, n, b, g, m, cost, s)) != hipSuccess) return hip_fail(e, "cost");
+  hipError_t e = launch_cost(a, f, n, b, g, m, cost, s);
+  if (e != hipSuccess) return hip_fail(e, "cost");
   return SK_OK;
 }
 
@@ -634,29 +603,10 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
   if (k < 1) return fail(SK_ERR_INVALID_ARG, "k must be >= 1");
   if (k > 64) return fail(SK_ERR_UNSUPPORTED, "k=%lld > 64 is not supported", (long long)k);
   const AuxPlan ap = plan_aux(dtype, n, m, d, k, false, transpose);
-  const size_t need = aux_bytes(ap, n, m, d, k);
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Scalars sc = scalars(eps);
-  if (ap.path != Path::Valu) {
-    const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
-    return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, transpose, V, false, out, sc, s);
-  }
-  const PassPlan& pl = ap.pl;
-  const int64_t nr = ap.nr, nc = ap.nc;
-  const AuxWs L = layout_aux(ws, n, m, d, pl, nr, k);
-  hipError_t e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, f, g, nullptr, nullptr, true,
-                           pl.row_blocks, sc, s);
-  if (e != hipSuccess) return hip_fail(e, "prep");
-  const Side& R = transpose ? L.y : L.x;
-  const Side& Cs = transpose ? L.x : L.y;
-  ApplyArgs aa{};
-  aa.rows = R.pts; aa.cols = Cs.pts; aa.hrow = R.h[0]; aa.hcol = Cs.h[0]; aa.V = V; aa.out = out;
-  aa.part = reinterpret_cast<float*>(L.c.part); aa.counters = L.c.counters;
-  aa.nr = (int)nr; aa.nc = (int)nc; aa.k = (int)k; aa.splits = pl.splits;
-  aa.cols_per_split = pl.cols_per_split; aa.c2 = sc.c2;
-  if ((e = launch_apply_valu(aa, (int)d, pl, s)) != hipSuccess) return hip_fail(e, "apply");
-  return SK_OK;
+  if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
+  const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
+  return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, transpose, V, false, out, scalars(eps),
+                   static_cast<hipStream_t>(stream));
 }
 
 int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
@@ -667,28 +617,10 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
   if (rc) return rc;
   if (!g || !grad_x) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
   const AuxPlan ap = plan_aux(dtype, n, m, d, d, true, 0);
-  const size_t need = grad_bytes(dtype, n, m, d);
-  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Scalars sc = scalars(eps);
-  if (ap.path != Path::Valu) {
-    const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
-    return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, nullptr, g, true, 0, y, dtype == SK_BF16,
-                     grad_x, sc, s);
-  }
-  const PassPlan& pl = ap.pl;
-  const int64_t rec = 2 + valu_dclass((int)d);
-  const AuxWs L = layout_aux(ws, n, m, d, pl, n, rec);
-  hipError_t e = prep_valu(L.x, L.y, L.c, x, y, dtype, n, m, d, a, b, nullptr, g, nullptr, nullptr,
-                           true, pl.row_blocks, sc, s);
-  if (e != hipSuccess) return hip_fail(e, "prep");
-  GradArgs ga{};
-  ga.rows = L.x.pts; ga.cols = L.y.pts; ga.hcol = L.y.h[0]; ga.wrow = a; ga.out = grad_x;
-  ga.part = reinterpret_cast<float*>(L.c.part); ga.counters = L.c.counters;
-  ga.nr = (int)n; ga.nc = (int)m; ga.d = (int)d; ga.splits = pl.splits;
-  ga.cols_per_split = pl.cols_per_split; ga.c2 = sc.c2;
-  if ((e = launch_grad_valu(ga, pl, s)) != hipSuccess) return hip_fail(e, "grad");
-  return SK_OK;
+  if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
+  const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
+  return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, nullptr, g, true, 0, y, dtype == SK_BF16, grad_x,
+                   scalars(eps), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -39,6 +39,7 @@ hipError_t launch_sub(const float* p, const float* q, float* out, int64_t cnt, h
 struct DivWs {
   float *f_ab, *g_ab, *f_aa, *g_aa, *f_bb, *g_bb, *tmp;
   double* costs;
+  unsigned* word;
   void* inner;
   size_t inner_bytes, bytes;
 };
@@ -69,6 +70,7 @@ DivWs layout_div(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   L.g_bb = c.take<float>(m);
   L.tmp = c.take<float>((size_t)(n > m ? n : m) * d);
   L.costs = c.take<double>(3);
+  L.word = c.take<unsigned>(1);
   L.inner_bytes = div_inner_bytes(dtype, n, m, d);
   L.inner = c.take<char>(L.inner_bytes);
   L.bytes = c.off;
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(1024) void k_marginal_error(const float* __restrict
 struct TolWs {
   float *f0, *g0;
   double* err;
+  unsigned* word;
   void* inner;
   size_t inner_bytes, bytes;
 };
@@ -118,6 +121,7 @@ TolWs layout_tol(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   L.f0 = c.take<float>(n);
   L.g0 = c.take<float>(m);
   L.err = c.take<double>(1);
+  L.word = c.take<unsigned>(1);
   L.inner_bytes = solve_bytes(dtype, n, m, d);
   L.inner = c.take<char>(L.inner_bytes);
   L.bytes = c.off;
@@ -368,6 +372,11 @@ HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
 }  // namespace
 
 namespace api {
+hipError_t launch_marginal_error(const float* w, const float* p0, const float* p1, int64_t cnt, double inv_eps,
+                                 bool averaged, bool accumulate, double* out, hipStream_t s) {
+  k_marginal_error<<<1, 1024, 0, s>>>(w, p0, p1, cnt, inv_eps, averaged ? 1 : 0, accumulate ? 1 : 0, out);
+  return hipGetLastError();
+}
 size_t divergence_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
   return layout_div(nullptr, dtype, n, m, d).bytes;
 }
@@ -400,16 +409,18 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
   if (!(tol >= 0.0) || !isfinite(tol)) return fail(SK_ERR_INVALID_ARG, "tol must be finite and >= 0");
   if (!(eps_start >= 0.0) || !isfinite(eps_start)) return fail(SK_ERR_INVALID_ARG, "eps_start must be finite and >= 0");
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
-  if (flags & ~(SK_WARM_START | SK_NO_CENTER)) return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & ~(SK_WARM_START | SK_NO_CENTER | SK_CHECK_FINITE))
+    return fail(SK_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   const TolWs L = layout_tol(ws, dtype, n, m, d);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((flags & SK_CHECK_FINITE) &&
+      (rc = screen_inputs(x, y, dtype, n, m, d, a, b, (flags & SK_WARM_START) ? f : nullptr,
+                          (flags & SK_WARM_START) ? g : nullptr, L.word, s)))
+    return rc;
   const uint32_t keep = flags & SK_NO_CENTER;
-  const double inv_eps = 1.0 / eps;
+  uint32_t fl = flags & (SK_WARM_START | SK_NO_CENTER);
   int32_t done = 0;
-  double e_host = INFINITY;
-  uint32_t fl = flags;
-  hipError_t e;
   // eps-scaling: one iteration at each of eps_start, eps_start / 2, ... above eps
   for (double ek = eps_start; ek > eps && done < max_iters; ek *= 0.5) {
     if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, ek, 1, mode, fl, f, g, cost, L.inner, L.inner_bytes,
@@ -418,50 +429,15 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
     ++done;
     fl = keep | SK_WARM_START;
   }
-  int32_t done_at_eps = 0;
-  while (done < max_iters) {
-    // iterations up to the next check, then the checking iteration itself
-    const int32_t left = max_iters - done;
-    const int32_t run = (check_every - 1 < left - 1) ? check_every - 1 : left - 1;
-    if (run > 0) {
-      if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, run, mode, fl, f, g, cost, L.inner,
-                                  L.inner_bytes, stream)))
-        return rc;
-      done += run;
-      done_at_eps += run;
-      fl = keep | SK_WARM_START;
-    }
-    if (done > 0 || (fl & SK_WARM_START)) {
-      if ((e = hipMemcpyAsync(L.f0, f, n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
-          (e = hipMemcpyAsync(L.g0, g, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
-        return hip_fail(e, "copy");
-    } else {
-      // cold start: the starting pair is zero
-      if ((e = hipMemsetAsync(L.f0, 0, n * sizeof(float), s)) != hipSuccess ||
-          (e = hipMemsetAsync(L.g0, 0, m * sizeof(float), s)) != hipSuccess)
-        return hip_fail(e, "clear");
-    }
-    // alternating: the columns of the checked pair are exact only if this call's
-    // own g-step at eps produced it, so a check on the starting pair (or the
-    // last pair of the eps-scaling) is skipped
-    const bool measurable = mode == SK_SYMMETRIC || done_at_eps > 0;
-    if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, 1, mode, fl, f, g, cost, L.inner,
-                                L.inner_bytes, stream)))
+  int32_t at_eps = 0;
+  double e_host = INFINITY;
+  if (done < max_iters) {
+    // the tolerance phase: one prep, the shifted sweep kept across checks
+    if ((rc = solve_to_tolerance(x, y, dtype, n, m, d, a, b, eps, mode, fl, max_iters - done, check_every, tol, f, g,
+                                 cost, TolScratch{L.f0, L.g0, L.err}, &at_eps, &e_host, L.inner, L.inner_bytes, s)))
       return rc;
-    done += 1;
-    done_at_eps += 1;
-    fl = keep | SK_WARM_START;
-    if (!measurable) continue;
-    const int avg = mode == SK_SYMMETRIC ? 1 : 0;
-    k_marginal_error<<<1, 1024, 0, s>>>(a, L.f0, f, n, inv_eps, avg, 0, L.err);
-    if (avg) k_marginal_error<<<1, 1024, 0, s>>>(b, L.g0, g, m, inv_eps, 1, 1, L.err);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "marginal error");
-    if ((e = hipMemcpyAsync(&e_host, L.err, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
-        (e = hipStreamSynchronize(s)) != hipSuccess)
-      return hip_fail(e, "marginal error");
-    if (e_host <= tol) break;
   }
-  *iters_done = done;
+  *iters_done = done + at_eps;
   *err = e_host;
   return SK_OK;
 }
@@ -614,12 +590,16 @@ int sk_sinkhorn_divergence(const void* x, const void* y, int dtype, int64_t n, i
   if (!div) return fail(SK_ERR_INVALID_ARG, "null output pointer");
   if (iters < 0) return fail(SK_ERR_INVALID_ARG, "iters must be >= 0");
   if (mode != SK_ALTERNATING && mode != SK_SYMMETRIC) return fail(SK_ERR_INVALID_ARG, "mode %d is not SK_ALTERNATING or SK_SYMMETRIC", mode);
-  if (flags & ~SK_NO_CENTER) return fail(SK_ERR_INVALID_ARG, "flags 0x%x: only SK_NO_CENTER applies", flags);
+  if (flags & ~(SK_NO_CENTER | SK_CHECK_FINITE))
+    return fail(SK_ERR_INVALID_ARG, "flags 0x%x: only SK_NO_CENTER and SK_CHECK_FINITE apply", flags);
   if ((grad_x || grad_y) && aux_path(dtype, d) == Path::None)
     return fail(SK_ERR_UNSUPPORTED, "gradients at d=%lld are not supported by this library", (long long)d);
   const DivWs L = layout_div(ws, dtype, n, m, d);
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((flags & SK_CHECK_FINITE) && (rc = screen_inputs(x, y, dtype, n, m, d, a, b, nullptr, nullptr, L.word, s)))
+    return rc;
+  flags &= SK_NO_CENTER;
   // every sub-call below passes the same validation, so none fails before
   // enqueuing anything unless the HIP runtime does
   if ((rc = sk_sinkhorn_solve(x, y, dtype, n, m, d, a, b, eps, iters, mode, flags, L.f_ab, L.g_ab,

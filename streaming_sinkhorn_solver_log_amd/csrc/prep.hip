@@ -79,36 +79,6 @@ __global__ __launch_bounds__(256) void k_centroid_final(const double* part, int 
   }
 }
 
-// One thread per point of either side: packed float32 point (row stride dp,
-// zero padded), |p|^2, ln w, and the bias of the starting potential.
-__global__ __launch_bounds__(256) void k_prep_f32(PrepSide xs, PrepSide ys, int dtype, int d,
-                                                  int dp, const float* shift,
-                                                  float log2e_over_eps, unsigned* counters,
-                                                  int n_counters) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid < n_counters) counters[gid] = 0u;
-  const bool is_x = gid < xs.n;
-  const PrepSide& s = is_x ? xs : ys;
-  const int64_t r = is_x ? gid : gid - xs.n;
-  if (r >= s.n) return;
-  float nrm = 0.0f;
-  for (int k = 0; k < dp; ++k) {
-    float v = 0.0f;
-    if (k < d) {
-      v = load_point(s.pts, dtype, r * d + k);
-      if (shift) v -= shift[k];
-    }
-    s.packed[r * dp + k] = v;
-    nrm = fmaf(v, v, nrm);
-  }
-  const float lw = logf(s.w[r]);
-  const float pot = s.pot ? s.pot[r] : 0.0f;
-  if (s.pot_init) s.pot_init[r] = 0.0f;
-  s.alpha[r] = nrm;
-  s.lw[r] = lw;
-  s.h[r] = kLog2e * lw + (pot - nrm) * log2e_over_eps;
-}
-
 __global__ __launch_bounds__(256) void k_zero_u32(unsigned* p, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < count) p[i] = 0u;
@@ -176,18 +146,6 @@ hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, i
 
 hipError_t launch_zero_u32(unsigned* p, int64_t count, hipStream_t s) {
   if (count > 0) k_zero_u32<<<(int)((count + 255) / 256), 256, 0, s>>>(p, count);
-  return hipGetLastError();
-}
-
-hipError_t launch_prep(const PrepSide& xs, const PrepSide& ys, int dtype, int d, int dp,
-                       bool center, double* centroid_part, float* shift, unsigned* counters,
-                       int n_counters, float log2e_over_eps, hipStream_t s) {
-  if (center) (void)launch_centroid(xs.pts, xs.n, ys.pts, ys.n, dtype, d, centroid_part, shift, s);
-  const int64_t total = xs.n + ys.n;
-  const int64_t work = total > n_counters ? total : n_counters;
-  const int blocks = (int)((work + 255) / 256);
-  k_prep_f32<<<blocks, 256, 0, s>>>(xs, ys, dtype, d, dp, center ? shift : nullptr,
-                                    log2e_over_eps, counters, n_counters);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ struct Carve {
   }
 };
 
-enum class Path { Valu, Mfma, Gemm, None };
+enum class Path { Mfma, Gemm, None };
 
 // Thread-local error message (sk_last_error): fail() formats it and returns code.
 void clear_error();
@@ -45,6 +45,35 @@ Path aux_path(int dtype, int64_t d);
 int check_common(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                  const float* a, const float* b, double eps, Path path);
 int check_ws(void* ws, size_t ws_bytes, size_t need);
+// SK_CHECK_FINITE screening: launches the input check, waits for its verdict
+// (one synchronization of s) and returns SK_ERR_INVALID_ARG on a NaN or an
+// infinity in x, y (or f, g when non-null), a negative or non-finite weight,
+// or a marginal with no positive weight. `word` is a workspace word.
+int screen_inputs(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                  const float* b, const float* f, const float* g, unsigned* word, hipStream_t s);
+
+// Device scratch of the tolerance loop: the pair before the checking
+// iteration and the error it measures.
+struct TolScratch {
+  float* f0;
+  float* g0;
+  double* err;
+};
+// The tolerance phase of sk_sinkhorn_solve_tol at a fixed eps (arguments
+// validated by the caller; SK_CHECK_FINITE is the caller's to apply): one
+// prep, then iterations in one workspace lifetime (every pass after each
+// side's first runs the shifted sweep), the marginal error of the pair before
+// every check_every-th iteration measured from that iteration, until it is
+// <= tol or max_iters iterations have run. ws: solve_bytes(dtype, n, m, d).
+int solve_to_tolerance(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                       const float* b, double eps, int mode, uint32_t flags, int32_t max_iters, int32_t check_every,
+                       double tol, float* f, float* g, double* cost, TolScratch scratch, int32_t* iters_done,
+                       double* err, void* ws, size_t ws_bytes, hipStream_t s);
+// out (+)= sum_i w_i |expm1((p0_i - M_i) inv_eps)| in float64 with M = p1
+// (or 2 p1 - p0 when averaged): the L1 marginal error of the pair (p0, .)
+// from the map value the following iteration computed (compose.hip).
+hipError_t launch_marginal_error(const float* w, const float* p0, const float* p1, int64_t cnt, double inv_eps,
+                                 bool averaged, bool accumulate, double* out, hipStream_t s);
 
 // Workspace bytes of the core entry points (api.hip).
 size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d);

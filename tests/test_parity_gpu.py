@@ -866,6 +866,52 @@ def test_hvp_matches_dense_oracle(sk, key, n, m, eps):
     assert resid <= 1e-6 and err <= (1e-4 if w.dtype == "f32" else 1e-3)
 
 
+@pytest.mark.parametrize("key,n,m,mode", [(6, 1500, 1300, "alternating"), (2, 900, 1100, "symmetric"),
+                                           (3, 1200, 1000, "alternating"), (4, 300, 500, "symmetric")])
+def test_solve_tol_continues_the_solve(sk, key, n, m, mode):
+    """The tolerance solve runs its iterations in one workspace lifetime (one
+    prep, shifted sweeps across the checks): with tol = 0 it returns bitwise the
+    pair and cost of a plain solve of the same length, cold and warm, whatever
+    the check interval."""
+    w = W.CASES[key].scaled(n, m, 23)
+    say(f"solve_tol continuity cfg={key} n={n} m={m} d={w.d} {w.dtype} {mode}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    ref = sk.solve(x, y, a, b, w.eps, 23, mode)
+    for every in (1, 4, 10, 23, 40):
+        f, g, c, done, err = sk.solve_tol(x, y, a, b, w.eps, 0.0, 23, mode, check_every=every)
+        assert done == 23 and torch.equal(f, ref[0]) and torch.equal(g, ref[1]) and torch.equal(c, ref[2]), every
+    f0, g0, _ = sk.solve(x, y, a, b, w.eps, 5, mode)
+    ref_w = sk.solve(x, y, a, b, w.eps, 12, mode, f0=f0, g0=g0)
+    f, g, c, done, err = sk.solve_tol(x, y, a, b, w.eps, 0.0, 12, mode, check_every=5, f0=f0, g0=g0)
+    assert done == 12 and torch.equal(f, ref_w[0]) and torch.equal(g, ref_w[1]) and torch.equal(c, ref_w[2])
+
+
+def test_check_finite_in_composed_operations(sk):
+    """SK_CHECK_FINITE reaches the tolerance solve and the divergence: clean
+    inputs give bitwise the unchecked results, a NaN point or a negative
+    weight is refused with SK_ERR_INVALID_ARG."""
+    w = W.CASES[1].scaled(600, 700, 6)
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    r1 = sk.solve_tol(x, y, a, b, w.eps, 1e-3, 40)
+    r2 = sk.solve_tol(x, y, a, b, w.eps, 1e-3, 40, check_finite=True)
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1]) and r1[3] == r2[3]
+    d1 = sk.sinkhorn_divergence(x, y, a, b, w.eps, w.iters)
+    d2 = sk.sinkhorn_divergence(x, y, a, b, w.eps, w.iters, check_finite=True)
+    assert all(torch.equal(p, q) for p, q in zip(d1, d2))
+    xb = x.clone()
+    xb[3, 1] = float("nan")
+    ab = a.clone()
+    ab[7] = -1e-6
+    for args in ((xb, y, a, b), (x, y, ab, b)):
+        with pytest.raises(sk.SinkhornError) as e1:
+            sk.solve_tol(*args, w.eps, 1e-3, 40, check_finite=True)
+        with pytest.raises(sk.SinkhornError) as e2:
+            sk.sinkhorn_divergence(*args, w.eps, w.iters, check_finite=True)
+        assert e1.value.code == sk.SK_ERR_INVALID_ARG and e2.value.code == sk.SK_ERR_INVALID_ARG
+
+
 def test_solve_tol_with_eps_scaling(sk):
     """eps-scaling (one iteration per halving from eps_start) then the tolerance
     phase at eps: the returned pair meets the tolerance by the oracle's marginals."""
