@@ -235,6 +235,28 @@ int sk_sinkhorn_divergence(const void* x, const void* y, int dtype, int64_t n, i
                            uint32_t flags, double* div, float* grad_a, float* grad_b, float* grad_x,
                            float* grad_y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Allocation-free solve, for callers that cannot allocate device memory or
+ * hand over a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Arguments, results and errors as for
+ * sk_sinkhorn_solve without ws and ws_bytes. Its scratch is a device array of
+ * sk_noalloc_scratch_bytes() bytes (64 MiB) inside the library, one per GPU,
+ * held from the library's load until the process ends; the call allocates
+ * nothing. A size whose solve workspace (sk_workspace_bytes(SK_OP_SOLVE, ...))
+ * exceeds it returns SK_ERR_UNSUPPORTED before anything is enqueued.
+ *   flags      SK_WARM_START, SK_NO_CENTER (SK_CHECK_FINITE, which waits for
+ *              the stream, is refused with SK_ERR_INVALID_ARG).
+ * Every call on a GPU uses that GPU's one array, which keeps the last call's
+ * contents (the solve initializes all it reads): calls that overlap on one
+ * GPU (on other streams or threads) race, and the caller must order them.
+ */
+int sk_sinkhorn_solve_noalloc(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                              const float* a, const float* b, double eps, int32_t iters, int mode,
+                              uint32_t flags, float* f, float* g, double* cost, void* stream);
+
+/* Bytes of the scratch array sk_sinkhorn_solve_noalloc uses on each GPU. */
+size_t sk_noalloc_scratch_bytes(void);
+
 /* Workspace bytes needed by `op` for these sizes (0 on invalid sizes). */
 size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, int64_t k);
 

@@ -73,6 +73,10 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_sinkhorn_solve_tol.restype = INT
     lib.sk_ot_hvp_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, P, P, D, I32, P, P, P, SZ, P]
     lib.sk_ot_hvp_x.restype = INT
+    lib.sk_sinkhorn_solve_noalloc.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P]
+    lib.sk_sinkhorn_solve_noalloc.restype = INT
+    lib.sk_noalloc_scratch_bytes.argtypes = []
+    lib.sk_noalloc_scratch_bytes.restype = SZ
     lib.sk_workspace_bytes.argtypes = [INT, INT, I64, I64, I64, I64]
     lib.sk_workspace_bytes.restype = SZ
     lib.sk_last_error.argtypes = []
@@ -84,7 +88,8 @@ def _load_library() -> ctypes.CDLL:
 
 _lib = _load_library()
 EXPORTS = ("sk_sinkhorn_solve", "sk_sinkhorn_solve_tol", "sk_transport_apply", "sk_transport_apply_hadamard", "sk_eot_grad_x",
-           "sk_ot_hvp_x", "sk_sinkhorn_divergence", "sk_workspace_bytes", "sk_last_error", "sk_version")
+           "sk_ot_hvp_x", "sk_sinkhorn_divergence", "sk_sinkhorn_solve_noalloc", "sk_noalloc_scratch_bytes",
+           "sk_workspace_bytes", "sk_last_error", "sk_version")
 
 
 def library() -> ctypes.CDLL:
@@ -181,6 +186,34 @@ def solve(x, y, a, b, eps: float, iters: int, mode: str = "alternating", f0=None
         _check(_lib.sk_sinkhorn_solve(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
                                       int(iters), mode_code, flags, _ptr(f), _ptr(g), _ptr(cost),
                                       ctypes.c_void_p(wptr), wbytes, _stream(dev)))
+    return f, g, cost
+
+
+def solve_noalloc(x, y, a, b, eps: float, iters: int, mode: str = "alternating", f0=None, g0=None,
+                  center: bool = True):
+    """solve() on the library's own per-GPU scratch (sk_sinkhorn_solve_noalloc):
+    no workspace is allocated or passed. Outputs are still new tensors here;
+    callers that cannot allocate call the C entry point with their own."""
+    n, m, d, dt = _points(x, y)
+    dev = x.device
+    _vec(a, n, "a", dev)
+    _vec(b, m, "b", dev)
+    mode_code = {"alternating": SK_ALTERNATING, "symmetric": SK_SYMMETRIC}[mode]
+    flags = 0 if center else SK_NO_CENTER
+    if (f0 is None) != (g0 is None):
+        raise ValueError("give both f0 and g0 for a warm start, or neither")
+    if f0 is not None:
+        f = _vec(f0, n, "f0", dev).clone()
+        g = _vec(g0, m, "g0", dev).clone()
+        flags |= SK_WARM_START
+    else:
+        f = torch.empty(n, dtype=torch.float32, device=dev)
+        g = torch.empty(m, dtype=torch.float32, device=dev)
+    cost = torch.empty((), dtype=torch.float64, device=dev)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_sinkhorn_solve_noalloc(_ptr(x), _ptr(y), dt, n, m, d, _ptr(a), _ptr(b), float(eps),
+                                              int(iters), mode_code, flags, _ptr(f), _ptr(g), _ptr(cost),
+                                              _stream(dev)))
     return f, g, cost
 
 

@@ -208,3 +208,26 @@ def test_check_finite_flag_matches_the_binding(lib):
     base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 3, 0, flag | 0x80, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.sk_sinkhorn_solve(*base) == inv
     assert b"flag" in lib.sk_last_error()
+
+
+def test_noalloc_solve_validates_before_any_device_call(lib):
+    """The allocation-free solve refuses bad arguments, SK_CHECK_FINITE and sizes
+    beyond its scratch on the host, before it looks up its device array."""
+    P, I64, I32, U32, D, INT = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_double,
+                                ctypes.c_int)
+    fn = lib.sk_sinkhorn_solve_noalloc
+    fn.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P]
+    fn.restype = INT
+    lib.sk_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    assert lib.sk_noalloc_scratch_bytes() == 64 << 20
+    inv, uns = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_UNSUPPORTED")
+    base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, 0.1, 3, 0, 0, FAKE, FAKE, FAKE, None]
+    cases = [(0, None, inv), (8, -1.0, inv), (9, -1, inv), (10, 7, inv), (11, _header_int("SK_CHECK_FINITE"), inv),
+             (12, None, inv), (3, 20_000, uns)]
+    for idx, val, code in cases:
+        args = list(base)
+        args[idx] = val
+        if idx == 3:  # float32 d = 512 at 20k x 20k needs far more than the scratch
+            args[4], args[5] = 20_000, 512
+        assert fn(*args) == code, (idx, val)
+        assert len(lib.sk_last_error()) > 0
