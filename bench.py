@@ -416,6 +416,41 @@ def measure_tol(case, tol, check_every=10, max_iters=20000, eps_start=0.0):
             "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "mode": w.mode}}
 
 
+def measure_low_eps(case, eps_list=(1e-2, 3e-3, 1e-3, 3e-4), tols=(1e-3, 1e-4, 1e-5), eps_start=1.0,
+                    check_every=10, max_iters=20000):
+    """Iterations and time to a marginal tolerance on the workload's points at
+    each eps, with and without eps-scaling (one iteration per halving from
+    eps_start), in the workload's schedule; each run blocks on its checks."""
+    from dataclasses import replace
+    sk, torch = case.sk, case.torch
+    dt = sk.SK_BF16 if case.w.dtype == "bf16" else sk.SK_F32
+    w0 = case.w
+    ws = torch.empty(sk.workspace_bytes(sk.SK_OP_SOLVE_TOL, dt, w0.n, w0.m, w0.d) + 256, dtype=torch.uint8,
+                     device=case.x.device)
+    sk.solve_tol(case.x, case.y, case.a, case.b, w0.eps, 1e-3, 20, w0.mode, check_every, workspace=ws)  # warm-up
+    rows = []
+    for eps in eps_list:
+        w = replace(w0, eps=eps)
+        for es in (0.0, eps_start):
+            for tol in tols:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                f, _, cost, done, err = sk.solve_tol(case.x, case.y, case.a, case.b, eps, tol, max_iters, w.mode,
+                                                     check_every, eps_start=es, workspace=ws)
+                sec = time.perf_counter() - t0
+                floor = 2.0 ** -24 * float(f.abs().max()) / eps
+                rows.append({"eps": eps, "eps_start": es, "tol": tol, "iters": done, "converged": err <= tol,
+                             "err": err, "seconds": sec, "iters_per_s": done / sec, "cost": float(cost),
+                             "f32_floor_estimate": floor})
+                print(f"[low-eps] eps={eps:g} eps_start={es:g} tol={tol:g}: {done} iterations, err {err:.3e}, "
+                      f"{sec:.3f} s, floor ~{floor:.1e}", file=sys.stderr, flush=True)
+    return {"metric": "iterations to a marginal error of tol at low eps", "unit": "iterations",
+            "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "check_every": check_every,
+            "max_iters": max_iters,
+            "config": {"workload": w0.name, "n": w0.n, "m": w0.m, "d": w0.d, "mode": w0.mode},
+            "rows": rows}
+
+
 def measure_hadamard(case, r, steps, warmup):
     """(P o A B^T) V and (P o A B^T)^T U with the workload's potentials (one
     solve first) and k = 16: ceil(r / 4) matrix-free applications each."""
@@ -601,6 +636,9 @@ def main():
                          "20000) and report the iterations and time it took")
     ap.add_argument("--eps-start", type=float, default=0.0,
                     help="with --tol: eps-scaling from this eps (one iteration per halving)")
+    ap.add_argument("--low-eps-study", action="store_true",
+                    help="iterations and time to marginal tolerances 1e-3..1e-5 at eps 1e-2..3e-4, with and "
+                         "without eps-scaling, on the workload's points")
     ap.add_argument("--hvp", action="store_true",
                     help="time one Hessian-vector product of OT_eps in x at the workload's solved pair")
     ap.add_argument("--peaks", action="store_true",
@@ -646,6 +684,9 @@ def main():
         return
     if args.hvp:
         print(json.dumps(measure_hvp(case, args.steps, args.warmup)), flush=True)
+        return
+    if args.low_eps_study:
+        print(json.dumps(measure_low_eps(case)), flush=True)
         return
     if args.tol > 0:
         print(json.dumps(measure_tol(case, args.tol, eps_start=args.eps_start)), flush=True)

@@ -2,8 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
 benchmark's CPU-baseline leg; the product package never imports it. The
-arithmetic lives in ``sk_oracle.c`` (plain float64 loops, OpenMP over rows);
-this file only marshals numpy arrays and builds the shared object.
+per-pair arithmetic lives in ``sk_oracle.c`` (plain float64 loops, OpenMP over
+rows) and this file marshals numpy arrays to it; the composed references
+(divergence, run to tolerance, dense Hessian-vector product and Newton step)
+are written here in float64 numpy on top of those routines or from their
+dense definitions, each with its derivation in its docstring.
 
 Every function takes the stored point values exactly (float32, or bf16 decoded
 exactly) promoted to float64, and weights as stored (float32) promoted to
@@ -272,6 +275,50 @@ def objectives(x, y, a, b, f, g, eps):
     _load().sko_objectives(_p(x), _p(y), n, m, d, _p(a), _p(b), _p(f), _p(g), float(eps),
                            ctypes.byref(pr), ctypes.byref(du))
     return pr.value, du.value
+
+
+def solve_tol(x, y, a, b, eps, tol, max_iters, mode="alternating", check_every=10, eps_start=0.0):
+    """Sinkhorn until the L1 marginal error ||P 1 - a||_1 + ||P^T 1 - b||_1 of a
+    checked pair is <= tol, composed from solve() and marginals() (both in
+    sk_oracle.c; the error is summed from the dense plan here, in float64).
+
+    Schedule, as the library's tolerance solve states it: optional eps-scaling
+    first (one iteration at each of eps_start, eps_start/2, ... while above
+    eps); then iterations at eps, and after every check_every-th of them the
+    pair before that iteration is checked (in the alternating schedule a pair
+    not produced by an iteration at eps is skipped); the run stops after that
+    iteration once the error is <= tol, or after max_iters iterations in all.
+    Returns (f, g, iters_done, err) with err the last error measured (inf if none).
+    """
+    x, y, n, m, d = _shapes(x, y)
+    a, b = _c(a), _c(b)
+    f, g = np.zeros(n), np.zeros(m)
+    done = 0
+    ek = float(eps_start)
+    while ek > eps and done < max_iters:
+        f, g, _ = solve(x, y, a, b, ek, 1, mode, f, g)
+        done += 1
+        ek *= 0.5
+    at_eps = 0
+    err = float("inf")
+    while done < max_iters:
+        run = min(check_every - 1, max_iters - done - 1)
+        if run > 0:
+            f, g, _ = solve(x, y, a, b, eps, run, mode, f, g)
+            done += run
+            at_eps += run
+        checked = (f.copy(), g.copy())
+        measurable = mode == "symmetric" or at_eps > 0
+        f, g, _ = solve(x, y, a, b, eps, 1, mode, f, g)
+        done += 1
+        at_eps += 1
+        if not measurable:
+            continue
+        r, c = marginals(x, y, a, b, checked[0], checked[1], eps)
+        err = float(np.abs(r - a).sum() + np.abs(c - b).sum())
+        if err <= tol:
+            break
+    return f, g, done, err
 
 
 def time_row_map(x, y, w, pot, eps, repeats: int = 1) -> float:

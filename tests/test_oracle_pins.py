@@ -436,3 +436,68 @@ def test_hvp_is_symmetric():
     lhs = (U * oracle.hvp_x(x, y, a, b, f, g, eps, V)).sum()
     rhs = (V * oracle.hvp_x(x, y, a, b, f, g, eps, U)).sum()
     assert lhs == pytest.approx(rhs, rel=1e-10)
+
+
+# ---------------------------------------------------------------- run to tolerance
+def _scaling_solve_tol(K, a, b, tol, max_iters, check_every, mode):
+    """The stopping rule of the tolerance solve on primal matrix scaling
+    (u = a / (K v), v = b / (K^T u); P = diag(u) K diag(v)): after every
+    check_every-th iteration, the marginal error of the pair before it."""
+    u, v = a.copy(), b.copy()
+    done = 0
+    err = float("inf")
+    while done < max_iters:
+        run = min(check_every - 1, max_iters - done - 1)
+        for _ in range(run):
+            u, v = _scaling_iterates_from(K, a, b, u, v, mode)
+        done += run
+        uc, vc = u.copy(), v.copy()
+        u, v = _scaling_iterates_from(K, a, b, u, v, mode)
+        done += 1
+        if mode == "alternating" and done == 1:
+            continue
+        P = uc[:, None] * K * vc[None, :]
+        err = np.abs(P.sum(1) - a).sum() + np.abs(P.sum(0) - b).sum()
+        if err <= tol:
+            break
+    return u, v, done, err
+
+
+def _scaling_iterates_from(K, a, b, u, v, mode):
+    if mode == "alternating":
+        u = a / (K @ v)
+        return u, b / (K.T @ u)
+    return np.sqrt(u * a / (K @ v)), np.sqrt(v * b / (K.T @ u))
+
+
+@pytest.mark.parametrize("mode,eps,tol,every", [("alternating", 0.05, 1e-6, 10), ("symmetric", 0.05, 1e-5, 7),
+                                                ("alternating", 0.02, 1e-8, 1), ("alternating", 0.1, 1e-3, 4)])
+def test_solve_tol_matches_primal_scaling_with_the_same_stopping_rule(mode, eps, tol, every):
+    """The oracle's run to tolerance stops at the same iteration as primal matrix
+    scaling under the same rule, with the same pair and error (the scaling form
+    of the iteration: Fused & Furious, section II.B)."""
+    x, y = _cloud(31, 9, 2), _cloud(32, 11, 2)
+    a, b = _weights(33, 9), _weights(34, 11)
+    K = np.exp(-_pairwise_by_expansion(x, y) / eps)
+    u, v, n_s, e_s = _scaling_solve_tol(K, a, b, tol, 5000, every, mode)
+    f, g, n_o, e_o = oracle.solve_tol(x, y, a, b, eps, tol, 5000, mode, every)
+    assert n_o == n_s < 5000
+    assert e_o == pytest.approx(e_s, rel=1e-6, abs=1e-14) and e_o <= tol
+    np.testing.assert_allclose(np.exp(f / eps), u / a, rtol=1e-9)
+    np.testing.assert_allclose(np.exp(g / eps), v / b, rtol=1e-9)
+
+
+def test_solve_tol_eps_scaling_schedule():
+    """eps-scaling runs one iteration per halving above eps before the checks:
+    from eps_start = 0.8 to eps = 0.1 that is 0.8, 0.4, 0.2 (three iterations),
+    whose pair then starts the run at eps."""
+    x, y = _cloud(41, 8, 3), _cloud(42, 10, 3)
+    a, b = _weights(43, 8), _weights(44, 10)
+    f3, g3, _ = oracle.solve(x, y, a, b, 0.8, 1)
+    f3, g3, _ = oracle.solve(x, y, a, b, 0.4, 1, "alternating", f3, g3)
+    f3, g3, _ = oracle.solve(x, y, a, b, 0.2, 1, "alternating", f3, g3)
+    fr, gr, _ = oracle.solve(x, y, a, b, 0.1, 20, "alternating", f3, g3)
+    f, g, done, err = oracle.solve_tol(x, y, a, b, 0.1, 0.0, 23, "alternating", 10, eps_start=0.8)
+    assert done == 23 and np.isfinite(err)
+    np.testing.assert_allclose(f, fr, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g, gr, rtol=0, atol=1e-13)
