@@ -141,7 +141,10 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
  * (f, g) as they are (no renormalization),
  *   transpose = 0:  out (n x k) = P V,    V is m x k
  *   transpose = 1:  out (m x k) = P^T V,  V is n x k
- * Requirements: 1 <= k <= 64 (SK_ERR_UNSUPPORTED above), as for the solve otherwise.
+ * Requirements: 1 <= k <= 4096 (SK_ERR_UNSUPPORTED above), as for the solve
+ * otherwise. Widths above 64 on large d (bf16 d > 128, float32 d > 21) run on
+ * the wide kernel (scores once per 512 values); on small d the scores are
+ * recomputed once per 64 values.
  */
 int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                        const float* a, const float* b, const float* f, const float* g, double eps,
@@ -196,8 +199,11 @@ int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t
  * plan products are matrix-free applications (O((n + m) d) memory).
  *   V, out     n x d float32 (V 16-byte aligned).
  *   cg_iters, cg_resid   out (host): CG iterations and final relative residual.
- * BLOCKING: synchronizes `stream` once per CG iteration.
- * Requirements: d <= 64 (SK_ERR_UNSUPPORTED above), as for the solve otherwise.
+ * The term (P o dC) Y is one weighted application (each plan entry times
+ * v_i.y_j, on the matrix cores), and the CG scalars stay on the device.
+ * BLOCKING: synchronizes `stream` once per batch of 8 CG iterations (an
+ * iteration after convergence in a batch changes nothing).
+ * Requirements: d <= 4096 (SK_ERR_UNSUPPORTED above), as for the solve otherwise.
  * Workspace: sk_workspace_bytes(SK_OP_HVP, dtype, n, m, d, 0).
  */
 int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,

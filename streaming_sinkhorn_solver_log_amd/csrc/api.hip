@@ -249,22 +249,27 @@ struct AuxPlan {
   Path path;
   int nkb;
   int kv, nobt, nob, nchunks, pp, vp;
+  int wq;  // weighted application: tangent record arrays (0: unweighted)
   int64_t nr, nc;
   PassPlan pl;
 };
 
-AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool grad, int transpose) {
+// weighted: the application of the plan entries times t_i.y_j to the values
+// y (rows x, columns y), which runs on the GEMM-tiled wide kernel at any d.
+AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool grad, int transpose,
+                 bool weighted = false) {
   AuxPlan ap{};
-  ap.path = aux_path(dtype, d);
+  ap.path = weighted ? (d <= 4096 ? Path::Gemm : Path::None) : aux_path(dtype, d);
+  ap.wq = weighted ? (dtype == SK_BF16 ? 2 : 1) : 0;
   ap.nr = transpose ? m : n;
   ap.nc = transpose ? n : m;
   ap.kv = (int)kv;
   if (ap.path == Path::Mfma || ap.path == Path::Gemm) {
     const bool gemm = ap.path == Path::Gemm;
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
-    pv_parts(dtype, grad, ap.pp, ap.vp);
+    pv_parts(dtype, grad || weighted, ap.pp, ap.vp);
     const int blocks = (int)((kv + 31) / 32);
-    ap.nob = pv_nob(gemm, blocks);
+    ap.nob = weighted ? pv_nob_weighted(blocks) : pv_nob(gemm, blocks);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
     ap.nobt = ap.nchunks * ap.nob;
     ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks);
@@ -276,6 +281,8 @@ struct AuxWsM {
   SideM x, y;
   bf16x8* vfrag;
   int64_t vtiles;
+  bf16x8* wrec;  // weighted application: tangent records of the rows
+  float* qoff;
   Common c;
   size_t bytes;
 };
@@ -292,6 +299,10 @@ AuxWsM layout_aux_m(void* ws, const AuxPlan& ap, int64_t n, int64_t m, int64_t d
   const size_t part_floats = ap.pl.splits > 1
       ? round_up(2 * slots_rows, 4) + slots_rows * 32 * ap.nob : 0;
   L.c = carve_common(c, (part_floats + 1) / 2, ap.nchunks * ap.pl.row_blocks, d);
+  if (ap.wq > 0) {
+    L.wrec = c.take<bf16x8>((size_t)ap.wq * ap.nr * ap.nkb * 2);
+    L.qoff = c.take<float>(ap.nr);
+  }
   L.bytes = c.off;
   return L;
 }
@@ -307,7 +318,7 @@ size_t aux_bytes(const AuxPlan& ap, int64_t n, int64_t m, int64_t d) {
 int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, int dtype, int64_t n,
               int64_t m, int64_t d, const float* a, const float* b, const float* f, const float* g,
               bool grad, int transpose, const void* vsrc, bool vsrc_bf16, float* out,
-              const Scalars& sc, hipStream_t s) {
+              const Scalars& sc, hipStream_t s, const float* tangent = nullptr) {
   const int ncnt = ap.nchunks * ap.pl.row_blocks;
   MfmaPrepSide px{x, a, f, nullptr, L.x.row_rec, L.x.col_rec, L.x.alpha, L.x.lw,
                   L.x.bias[0], L.x.bias[1], L.x.hval[0], n};
@@ -331,6 +342,15 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   pa.nr = (int)ap.nr; pa.nc = (int)ap.nc; pa.row_blocks = ap.pl.row_blocks; pa.nchunks = ap.nchunks;
   pa.splits = ap.pl.splits; pa.cols_per_split = ap.pl.cols_per_split;
   pa.escale = mfma_escale(dtype, sc.c2);
+  if (ap.wq > 0) {
+    const int64_t stride = (int64_t)ap.nr * ap.nkb * 2;
+    e = launch_pack_tangent(tangent, dtype == SK_BF16, ap.nr, (int)d, ap.nkb, shift, L.wrec, stride,
+                            dtype == SK_F32 ? L.qoff : nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "tangent records");
+    pa.wrec = L.wrec;
+    pa.wrec_stride = stride;
+    pa.qoff = dtype == SK_F32 ? L.qoff : nullptr;
+  }
   e = launch_pv(pa, ap.path == Path::Gemm, ap.nkb, ap.nob, ap.pp, ap.vp, ap.pl, s);
   if (e != hipSuccess) return hip_fail(e, grad ? "grad" : "apply");
   return SK_OK;
@@ -477,6 +497,22 @@ size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
   return aux_bytes(plan_aux(dtype, n, m, d, d, true, 0), n, m, d);
 }
 
+size_t apply_weighted_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
+  return aux_bytes(plan_aux(dtype, n, m, d, d, false, 0, true), n, m, d);
+}
+
+int apply_weighted(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                   const float* b, const float* f, const float* g, double eps, const float* T, float* out, void* ws,
+                   size_t ws_bytes, hipStream_t s) {
+  const AuxPlan ap = plan_aux(dtype, n, m, d, d, false, 0, true);
+  if (ap.path == Path::None) return fail(SK_ERR_UNSUPPORTED, "d=%lld is beyond the weighted application", (long long)d);
+  int rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d));
+  if (rc) return rc;
+  const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
+  // values: the column points as given (the centering only enters the records)
+  return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, 0, y, dtype == SK_BF16, out, scalars(eps), s, T);
+}
+
 int solve_to_tolerance(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
                        const float* b, double eps, int mode, uint32_t flags, int32_t max_iters, int32_t check_every,
                        double tol, float* f, float* g, double* cost, TolScratch scratch, int32_t* iters_done,
@@ -540,7 +576,7 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
       if (solve_path(dtype, d) == Path::None) return 0;
       return solve_bytes(dtype, n, m, d);
     case SK_OP_APPLY: {
-      if (aux_path(dtype, d) == Path::None || k < 1 || k > 64) return 0;
+      if (aux_path(dtype, d) == Path::None || k < 1 || k > kMaxValueCols) return 0;
       const size_t a0 = apply_bytes(dtype, n, m, d, k, 0), a1 = apply_bytes(dtype, n, m, d, k, 1);
       return a0 > a1 ? a0 : a1;
     }
@@ -601,7 +637,8 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
   if (!f || !g || !V || !out) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
   if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
   if (k < 1) return fail(SK_ERR_INVALID_ARG, "k must be >= 1");
-  if (k > 64) return fail(SK_ERR_UNSUPPORTED, "k=%lld > 64 is not supported", (long long)k);
+  if (k > kMaxValueCols)
+    return fail(SK_ERR_UNSUPPORTED, "k=%lld > %lld is not supported", (long long)k, (long long)kMaxValueCols);
   const AuxPlan ap = plan_aux(dtype, n, m, d, k, false, transpose);
   if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
   const AuxWsM L = layout_aux_m(ws, ap, n, m, d);

@@ -260,6 +260,57 @@ __global__ void k_hvp_out(const float* __restrict__ r, const float* __restrict__
   }
 }
 
+// Conjugate-gradient state on the device (float64): the scalars of the
+// iteration never visit the host, which reads them once per batch.
+// (rr, rz) and (rn, rzn) are adjacent: k_dot2 writes each pair at once.
+enum CgSlot { kRr = 0, kRz, kZn, kPsp, kRn, kRzn, kIt, kDone, kCgSlots };
+
+__global__ void k_cg_init(double* st, double tol) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    st[kZn] = sqrt(st[kRr]);
+    st[kIt] = 0.0;
+    st[kDone] = (sqrt(st[kRr]) > tol * st[kZn]) ? 0.0 : 1.0;
+  }
+}
+
+// q += alpha p, res -= alpha Sp, z = res / c (alpha = rz / pSp), unless done
+// or without curvature along p.
+__global__ void k_cg_step1(const double* __restrict__ st, float* __restrict__ q, float* __restrict__ res,
+                           const float* __restrict__ pp, const float* __restrict__ Sp, const float* __restrict__ c,
+                           float* __restrict__ z, int64_t cnt) {
+  if (st[kDone] != 0.0 || !(st[kPsp] > 0.0)) return;
+  const float alpha = (float)(st[kRz] / st[kPsp]);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x) {
+    q[i] = fmaf(alpha, pp[i], q[i]);
+    const float r = fmaf(-alpha, Sp[i], res[i]);
+    res[i] = r;
+    z[i] = r / c[i];
+  }
+}
+
+// p = z + beta p (beta = rzn / rz), unless done or without curvature.
+__global__ void k_cg_step2(const double* __restrict__ st, const float* __restrict__ z, float* __restrict__ pp,
+                           int64_t cnt) {
+  if (st[kDone] != 0.0 || !(st[kPsp] > 0.0)) return;
+  const float beta = (float)(st[kRzn] / st[kRz]);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    pp[i] = fmaf(beta, pp[i], z[i]);
+}
+
+// End of an iteration: count it and test the relative residual; no curvature
+// along p ends the iteration without counting.
+__global__ void k_cg_finish(double* st, double tol) {
+  if (threadIdx.x != 0 || blockIdx.x != 0 || st[kDone] != 0.0) return;
+  if (!(st[kPsp] > 0.0)) {
+    st[kDone] = 1.0;
+    return;
+  }
+  st[kRz] = st[kRzn];
+  st[kRr] = st[kRn];
+  st[kIt] += 1.0;
+  if (!(sqrt(st[kRr]) > tol * st[kZn])) st[kDone] = 1.0;
+}
+
 // ---------------------------------------------------------------- Hadamard-weighted application
 // (P o W) V with W = A B^T (review, Summary item ii names Hadamard-weighted
 // transport applications; W is not defined on the pages, and the low-rank
@@ -355,15 +406,14 @@ HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   L.DY = cv.take<float>(m * d);
   L.PDY = cv.take<float>(n * d);
   L.HY = cv.take<float>(n * d);
-  L.dots = cv.take<double>(4);
-  size_t need = 0;
-  for (int64_t kk = 1; kk <= kHvpMaxD; ++kk) {
+  L.dots = cv.take<double>(kCgSlots);
+  size_t need = apply_weighted_bytes(dtype, n, m, d);
+  for (int64_t kk : {(int64_t)1, d}) {
     const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0), a1 = apply_bytes(dtype, n, m, d, kk, 1);
     need = a0 > need ? a0 : need;
     need = a1 > need ? a1 : need;
   }
-  const size_t had = layout_hadamard(nullptr, dtype, n, m, d).bytes;  // the Hadamard application's own layout
-  L.inner_bytes = had > need ? had : need;
+  L.inner_bytes = need;
   L.inner = cv.take<char>(L.inner_bytes);
   L.bytes = cv.off;
   return L;
@@ -496,18 +546,6 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
     return sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner,
                               L.inner_bytes, stream);
   };
-  double host[2] = {0.0, 0.0};
-  auto dot2 = [&](const float* p1, const float* q1, const float* p2, const float* q2, int64_t cnt, double& v1,
-                  double& v2) -> int {
-    k_dot2<<<1, 1024, 0, s>>>(p1, q1, p2, q2, cnt, L.dots);
-    if ((e = hipGetLastError()) != hipSuccess ||
-        (e = hipMemcpyAsync(host, L.dots, 2 * sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
-        (e = hipStreamSynchronize(s)) != hipSuccess)
-      return hip_fail(e, "hvp reduction");
-    v1 = host[0];
-    v2 = host[1];
-    return SK_OK;
-  };
   const int64_t big = n > m ? n : m;
   k_to_f32<<<grid_for(n * d), 256, 0, s>>>(x, dtype == SK_BF16, n * d, L.xf);
   k_to_f32<<<grid_for(m * d), 256, 0, s>>>(y, dtype == SK_BF16, m * d, L.yf);
@@ -529,41 +567,49 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
   // right side of the Schur system, w - P^T (u / r), with its mean removed
   if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
   if ((e = launch_sub(L.w, L.tm, L.res, m, s)) != hipSuccess) return hip_fail(e, "hvp");
-  k_dot<<<1, 1024, 0, s>>>(L.res, nullptr, m, L.dots);
-  k_sub_mean<<<grid_for(m), 256, 0, s>>>(L.res, L.dots, m);
+  k_dot<<<1, 1024, 0, s>>>(L.res, nullptr, m, L.dots + kPsp);
+  k_sub_mean<<<grid_for(m), 256, 0, s>>>(L.res, L.dots + kPsp, m);
   k_fill<<<grid_for(m), 256, 0, s>>>(L.q, 0.0f, m);
   k_div<<<grid_for(m), 256, 0, s>>>(L.res, L.c, m, L.zv);
   if ((e = hipGetLastError()) != hipSuccess ||
       (e = hipMemcpyAsync(L.pp, L.zv, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
     return hip_fail(e, "hvp");
-  // preconditioned conjugate gradients on S = diag(c) - P^T diag(1/r) P
-  double rr = 0.0, rz = 0.0;
-  if ((rc = dot2(L.res, L.res, L.res, L.zv, m, rr, rz))) return rc;
-  const double zn = sqrt(rr);
-  int32_t it = 0;
-  while (it < cg_max_iters && sqrt(rr) > cg_tol * zn) {
-    if ((rc = apply(L.pp, 1, 0, L.tn))) return rc;
-    k_div<<<grid_for(n), 256, 0, s>>>(L.tn, L.r, n, L.tn);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
-    if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
-    k_cp_minus_t<<<grid_for(m), 256, 0, s>>>(L.c, L.pp, L.tm, m, L.Sp);
-    double pSp = 0.0, unused = 0.0;
-    if ((rc = dot2(L.pp, L.Sp, L.pp, L.Sp, m, pSp, unused))) return rc;
-    if (!(pSp > 0.0)) break;  // no curvature left along the search direction
-    const double alpha = rz / pSp;
-    k_axpy<<<grid_for(m), 256, 0, s>>>((float)alpha, L.pp, L.q, m, 0);
-    k_axpy<<<grid_for(m), 256, 0, s>>>((float)-alpha, L.Sp, L.res, m, 0);
-    k_div<<<grid_for(m), 256, 0, s>>>(L.res, L.c, m, L.zv);
-    double rn = 0.0, rzn = 0.0;
-    if ((rc = dot2(L.res, L.res, L.res, L.zv, m, rn, rzn))) return rc;
-    k_axpy<<<grid_for(m), 256, 0, s>>>((float)(rzn / rz), L.zv, L.pp, m, 1);
-    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
-    rr = rn;
-    rz = rzn;
-    ++it;
+  // preconditioned conjugate gradients on S = diag(c) - P^T diag(1/r) P, the
+  // scalars on the device; the host looks once per batch of iterations
+  k_dot2<<<1, 1024, 0, s>>>(L.res, L.res, L.res, L.zv, m, L.dots + kRr);  // rr, then rz
+  k_cg_init<<<1, 64, 0, s>>>(L.dots, cg_tol);
+  if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  double host[kCgSlots];
+  int32_t launched = 0;
+  constexpr int32_t kBatch = 8;
+  bool done = false;
+  while (!done && launched < cg_max_iters) {
+    const int32_t batch = (cg_max_iters - launched) < kBatch ? cg_max_iters - launched : kBatch;
+    for (int32_t t = 0; t < batch; ++t) {
+      if ((rc = apply(L.pp, 1, 0, L.tn))) return rc;
+      k_div<<<grid_for(n), 256, 0, s>>>(L.tn, L.r, n, L.tn);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+      if ((rc = apply(L.tn, 1, 1, L.tm))) return rc;
+      k_cp_minus_t<<<grid_for(m), 256, 0, s>>>(L.c, L.pp, L.tm, m, L.Sp);
+      k_dot<<<1, 1024, 0, s>>>(L.pp, L.Sp, m, L.dots + kPsp);
+      k_cg_step1<<<grid_for(m), 256, 0, s>>>(L.dots, L.q, L.res, L.pp, L.Sp, L.c, L.zv, m);
+      k_dot2<<<1, 1024, 0, s>>>(L.res, L.res, L.res, L.zv, m, L.dots + kRn);  // rn, rzn
+      k_cg_step2<<<grid_for(m), 256, 0, s>>>(L.dots, L.zv, L.pp, m);
+      k_cg_finish<<<1, 64, 0, s>>>(L.dots, cg_tol);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+    }
+    launched += batch;
+    if ((e = hipMemcpyAsync(host, L.dots, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "hvp");
+    done = host[kDone] != 0.0;
   }
-  *cg_iters = it;
-  *cg_resid = zn > 0.0 ? sqrt(rr) / zn : 0.0;
+  if (launched == 0 &&
+      ((e = hipMemcpyAsync(host, L.dots, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+       (e = hipStreamSynchronize(s)) != hipSuccess))
+    return hip_fail(e, "hvp");
+  *cg_iters = (int32_t)host[kIt];
+  *cg_resid = host[kZn] > 0.0 ? sqrt(host[kRr]) / host[kZn] : 0.0;
   // df = (u - P dg) / r
   if ((rc = apply(L.q, 1, 0, L.tn))) return rc;
   if ((e = launch_sub(L.u, L.tn, L.tn, n, s)) != hipSuccess) return hip_fail(e, "hvp");
@@ -571,10 +617,8 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
   k_scale_rows<<<grid_for(m * d), 256, 0, s>>>(L.q, L.yf, m, d, L.DY);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
   if ((rc = apply(L.DY, d, 0, L.PDY))) return rc;
-  // (P o V Y^T) Y: the Hadamard-weighted application of rank d
-  if ((rc = sk_transport_apply_hadamard(x, y, dtype, n, m, d, a, b, f, g, eps, 0, V, L.yf, d, L.yf, d, L.HY,
-                                        L.inner, L.inner_bytes, stream)))
-    return rc;
+  // (P o V Y^T) Y: the plan entries weighted by v_i . y_j, applied to Y
+  if ((rc = apply_weighted(x, y, dtype, n, m, d, a, b, f, g, eps, V, L.HY, L.inner, L.inner_bytes, s))) return rc;
   k_hvp_out<<<grid_for(n * d), 256, 0, s>>>(L.r, V, L.df, L.sv, L.PY, L.PDY, L.HY, n, d, (float)(2.0 / eps), out);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
   return SK_OK;

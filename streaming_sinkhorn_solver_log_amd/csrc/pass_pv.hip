@@ -157,6 +157,38 @@ __device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& ac
   return s0 + s1;
 }
 
+// Weighted plan entries of one score tile: 2^{e acc + off} * q (q: the
+// weights in the accumulator layout), split into PP bf16 parts as pv_probs
+// does (the weights may be negative: the truncated parts keep the sign and
+// the remainders stay exact).
+template <int PP>
+__device__ __attribute__((always_inline)) inline void pv_probs_w(const f32x16& acc, const f32x16& q, float qo, float e,
+                                                               float off, bf16x8 (&P)[PP][2]) {
+  u32x4 W[PP][2];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float v0 = fast_exp2(fmaf(acc[r], e, off)) * (q[r] + qo);
+    const float v1 = fast_exp2(fmaf(acc[r + 1], e, off)) * (q[r + 1] + qo);
+    const int kb = r >> 3, w = (r & 7) >> 1;
+    if constexpr (PP == 1) {
+      W[0][kb][w] = pack_bf16_rne(v0, v1);
+    } else {
+      W[0][kb][w] = pack_hi16(v0, v1);
+      const float r0 = v0 - trunc_bf16(v0), r1 = v1 - trunc_bf16(v1);
+      if constexpr (PP == 2) {
+        W[1][kb][w] = pack_bf16_rne(r0, r1);
+      } else {
+        W[1][kb][w] = pack_hi16(r0, r1);
+        W[2][kb][w] = pack_bf16_rne(r0 - trunc_bf16(r0), r1 - trunc_bf16(r1));
+      }
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) P[pp][kb] = __builtin_bit_cast(bf16x8, W[pp][kb]);
+}
+
 // O[ob] += V[ob] x P over the products (pp, vp) of combined order below max(PP, VP).
 template <int NOB, int PP, int VP>
 __device__ __attribute__((always_inline)) inline void pv_mfma(const VTile<NOB, VP>& vt, const bf16x8 (&P)[PP][2],
@@ -345,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
 // the value products of each wave's 64 x 64 quarter; the two column waves of
 // a row pair merge their partials through LDS at the end.
 template <int NOB, int PP, int VP>
-__global__ __launch_bounds__(kThreads, NOB >= 4 ? 1 : 2) void k_pv_gemm(const PvArgs p, int nkb) {
+__global__ __launch_bounds__(kThreads, 2) void k_pv_gemm(const PvArgs p, int nkb) {
   __shared__ __attribute__((aligned(16))) GemmLds lds;
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
   const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
@@ -627,6 +659,296 @@ __global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int 
   pv_finish<WRT, 1, G::kNT>(p, wc == 0, r0 + wr * kWaveRows, G::kRows, O, mu, S, li, half);
 }
 
+// GEMM-tiled variant for wide value chunks (the gradient at large d: value
+// width d up to 4 * NOBW * 32 per chunk). Each 64 x 128 score block is
+// computed once: the four waves form it together (wave w: row tile w & 1,
+// column tiles 2 (w >> 1) and 2 (w >> 1) + 1; K streamed through LDS), agree
+// on the rows' lazy shift through LDS, and write the plan entries' bf16 parts
+// to LDS; each wave then applies all 64 x 128 entries to its own NOBW value
+// blocks. The score work is thereby done once per value chunk instead of once
+// per NOB = 4 blocks (k_pv_gemm).
+using PvwGeo = Geo<1, 2, 2>;  // staging: 256 threads, 64 rows x 128 columns per stage
+constexpr int kPvwRows = 64;
+
+template <int PP, int WQ>
+struct PvwLds {
+  TileLds<PvwGeo> st;          // staged score operands (double buffered)
+  bf16x8 P[2][4][PP][2][64];   // entries: row tile, column tile, part, K block, lane
+  float tmax[2][2][32];        // per column half and row tile: each row's maximum over the block
+  float ssum[2][2][32];        // per column half and row tile: partial row sums (gradient)
+  // staged tangent records of the rows (weighted application)
+  unsigned char wrows[WQ > 0 ? WQ : 1][2][WQ > 0 ? kPvwRows * kGRow : 16];
+};
+
+// Stage (kc) of the tangent records of rows [r0, r0 + 64): WQ arrays, each
+// like the row records (tile_load's row half).
+template <int WQ>
+__device__ __attribute__((always_inline)) inline void wrec_load(u32x4 (&wr)[WQ > 0 ? WQ : 1][PvwGeo::kRowLoads],
+                                                                const PvArgs& p, int nkb, int r0, int kc) {
+  if constexpr (WQ > 0) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wrec);
+    const int64_t rsb = (int64_t)nkb * 32;
+#pragma unroll
+    for (int qq = 0; qq < WQ; ++qq)
+#pragma unroll
+      for (int q = 0; q < PvwGeo::kRowLoads; ++q) {
+        const int ch = threadIdx.x + q * PvwGeo::kNT;
+        const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+        wr[qq][q] = *reinterpret_cast<const u32x4*>(base + qq * p.wrec_stride * 16 +
+                                                     (int64_t)min(r0 + rec, p.nr - 1) * rsb +
+                                                     gemm_chunk_off(hh, kc, part));
+      }
+  }
+}
+
+template <int PP, int WQ>
+__device__ __attribute__((always_inline)) inline void wrec_store(const u32x4 (&wr)[WQ > 0 ? WQ : 1][PvwGeo::kRowLoads],
+                                                                 PvwLds<PP, WQ>& L, int buf) {
+  if constexpr (WQ > 0) {
+#pragma unroll
+    for (int qq = 0; qq < WQ; ++qq)
+#pragma unroll
+      for (int q = 0; q < PvwGeo::kRowLoads; ++q) {
+        const int ch = threadIdx.x + q * PvwGeo::kNT;
+        const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
+        *reinterpret_cast<u32x4*>(&L.wrows[qq][buf][rec * kGRow + hh * 64 + part * 16]) = wr[qq][q];
+      }
+  }
+}
+
+template <int PP, int VP, int NOBW, int WQ>
+__global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb, int col_last) {
+  using G = PvwGeo;
+  __shared__ __attribute__((aligned(16))) PvwLds<PP, WQ> lds;
+  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
+  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int li = lane & 31;
+  const int srt = wave & 1;   // row tile of this wave's scores
+  const int sch = wave >> 1;  // column half of this wave's scores
+  const int ob0 = blockIdx.z * (4 * NOBW) + wave * NOBW;  // this wave's first value block
+  const int j0 = blockIdx.y * p.cols_per_split;
+  const int j1 = min(p.nc, j0 + p.cols_per_split);
+  const int r0 = blockIdx.x * kPvwRows;
+  const float e = p.escale;
+  const bf16x8 Baug = row_aug(half, 0.0f);
+
+  float mu[2] = {kMuInit, kMuInit};  // lazy row maxima (acc units) of the lane's row in each row tile
+  float Sp = 0.0f;                   // partial row sum over this wave's score tiles
+  f32x16 O[2][NOBW];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ob = 0; ob < NOBW; ++ob) O[rt][ob] = f32x16{};
+
+  const int nkc = nkb / kGKb;
+  const int nblocks = (j1 - j0 + G::kCols - 1) / G::kCols;
+  const int nstages = nblocks * nkc;
+  auto load_stage = [&](TileRegs<G>& g, int st) {
+    tile_load<G>(g, rows, cols, nkb, p.nr, col_last, r0, j0 + (st / nkc) * G::kCols, st % nkc);
+  };
+  TileRegs<G> g;
+  u32x4 wr[WQ > 0 ? WQ : 1][G::kRowLoads];
+  if (nstages > 0) {
+    load_stage(g, 0);
+    wrec_load<WQ>(wr, p, nkb, r0, 0);
+    tile_store<G>(g, lds.st, 0);
+    wrec_store<PP, WQ>(wr, lds, 0);
+    if (nstages > 1) {
+      load_stage(g, 1);
+      wrec_load<WQ>(wr, p, nkb, r0, 1 % nkc);
+    }
+  }
+  float qoff[2] = {0.0f, 0.0f};
+  if constexpr (WQ > 0) {
+    if (p.qoff) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) qoff[rt] = p.qoff[min(r0 + rt * 32 + li, p.nr - 1)];
+    }
+  }
+  __syncthreads();
+  f32x16 acc[2], accq[2];
+  for (int st = 0; st < nstages; ++st) {
+    const int blk = st / nkc, kc = st % nkc;
+    const int buf = st & 1;
+    if (kc == 0) {
+      acc[0] = f32x16{};
+      acc[1] = f32x16{};
+      if constexpr (WQ > 0) {
+        accq[0] = f32x16{};
+        accq[1] = f32x16{};
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < kGKb; ++kb) {
+      const bf16x8 B = *reinterpret_cast<const bf16x8*>(&lds.st.rows[buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(
+            &lds.st.cols[buf][((2 * sch + ct) * 32 + li) * kGRow + half * 64 + kb * 16]);
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[ct], 0, 0, 0);
+        if constexpr (WQ > 0) {
+#pragma unroll
+          for (int qq = 0; qq < WQ; ++qq) {
+            const bf16x8 Bw =
+                *reinterpret_cast<const bf16x8*>(&lds.wrows[qq][buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
+            accq[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bw, accq[ct], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // the next stage's operands go to LDS before the epilogue, so their
+    // staging registers are free during it
+    if (st + 1 < nstages) {
+      tile_store<G>(g, lds.st, buf ^ 1);
+      wrec_store<PP, WQ>(wr, lds, buf ^ 1);
+    }
+    if (kc == nkc - 1) {
+      const int cb = j0 + blk * G::kCols;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bf16x8 Aaug = p.bias_col[2 * (int64_t)min(cb + (2 * sch + ct) * 32 + li, col_last) + half];
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Aaug, Baug, acc[ct], 0, 0, 0);
+      }
+      float tm = max3(max16(acc[0]), max16(acc[1]), kMuInit);
+      tm = max3(tm, __shfl_xor(tm, 32), tm);
+      if (half == 0) lds.tmax[sch][srt][li] = tm;
+      __syncthreads();
+      // the same lazy shift in every wave: raise a row's maximum only when a
+      // term would exceed 2^16
+      float sc[2];
+      bool raised = false;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float t = fmaxf(lds.tmax[0][rt][li], lds.tmax[1][rt][li]);
+        const bool raise = e * (t - mu[rt]) > kLazy;
+        const float mn = raise ? t : mu[rt];
+        sc[rt] = fast_exp2(e * (mu[rt] - mn));
+        mu[rt] = mn;
+        raised |= raise;
+      }
+      if (__any(raised)) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int ob = 0; ob < NOBW; ++ob)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[rt][ob][r] *= sc[rt];
+        Sp *= sc[srt];
+      }
+      const float off = -e * mu[srt];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        bf16x8 P[PP][2];
+        if constexpr (WQ > 0) pv_probs_w<PP>(acc[ct], accq[ct], qoff[srt], e, off, P);
+        else if (p.grad) Sp += pv_probs<PP, true>(acc[ct], e, off, P);
+        else pv_probs<PP, false>(acc[ct], e, off, P);
+#pragma unroll
+        for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) lds.P[srt][2 * sch + ct][pp][kb][lane] = P[pp][kb];
+      }
+      __syncthreads();
+      // a column block can overhang the padded columns by up to 3 tiles:
+      // those columns are masked, so any zero-valued tile serves, here the
+      // last padded one
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        bf16x8 Pf[2][PP][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Pf[rt][pp][kb] = lds.P[rt][ct][pp][kb][lane];
+        const int64_t tile = min((cb >> 5) + ct, col_last >> 5);
+#pragma unroll
+        for (int ob = 0; ob < NOBW; ++ob) {
+          VTile<1, VP> vt;
+          load_vtile<1, VP>(vt, p, tile, ob0 + ob, lane);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            f32x16 (&Oo)[1] = *reinterpret_cast<f32x16(*)[1]>(&O[rt][ob]);
+            pv_mfma<1, PP, VP>(vt, Pf[rt], Oo);
+          }
+        }
+      }
+    }
+    if (st + 2 < nstages) {
+      load_stage(g, st + 2);
+      wrec_load<WQ>(wr, p, nkb, r0, (st + 2) % nkc);
+    }
+    __syncthreads();
+  }
+
+  // Row sums: the two column halves' partials (both halves of each wave).
+  const float Sw = Sp + __shfl_xor(Sp, 32);
+  if (half == 0) lds.ssum[sch][srt][li] = Sw;
+  __syncthreads();
+  float S[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) S[rt] = lds.ssum[0][rt][li] + lds.ssum[1][rt][li];
+
+  constexpr int CW = 4 * NOBW * 32;  // value columns per chunk
+  const int z = blockIdx.z;
+  const int cbase = z * CW + wave * NOBW * 32;  // this wave's first value column
+  if (p.splits == 1) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int i = r0 + rt * 32 + li;
+      if (i >= p.nr) continue;
+#pragma unroll
+      for (int ob = 0; ob < NOBW; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cc = cbase + ob * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (cc < p.kv) pv_store(p, i, cc, mu[rt], S[rt], O[rt][ob][r]);
+        }
+    }
+    return;
+  }
+  // Split partials (mu, S, values), merged in split order by the last
+  // workgroup of the row block (bitwise repeatable).
+  const int64_t nslots = (int64_t)p.nchunks * p.splits;
+  float2* part_ms = reinterpret_cast<float2*>(p.part);
+  float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);
+  const int64_t slot = (int64_t)z * p.splits + blockIdx.y;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int i = r0 + rt * 32 + li;
+    if (i >= p.nr) continue;
+    if (wave == 0 && half == 0) store_coherent(&part_ms[slot * p.nr + i], make_float2(mu[rt], S[rt]));
+    float* T = part_t + (slot * p.nr + i) * CW + wave * NOBW * 32;
+#pragma unroll
+    for (int ob = 0; ob < NOBW; ++ob)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) store_coherent(T + ob * 32 + 8 * q + 4 * half + u, O[rt][ob][4 * q + u]);
+  }
+  unsigned* counter = p.counters + (int64_t)z * p.row_blocks + blockIdx.x;
+  if (!arrive_last(counter, p.splits)) return;
+  for (int q = threadIdx.x; q < kPvwRows * CW; q += kThreads) {
+    const int i = r0 + q / CW;
+    const int c = q % CW;
+    if (i >= p.nr || z * CW + c >= p.kv) continue;
+    float Mt = kMuInit;
+    for (int s2 = 0; s2 < p.splits; ++s2)
+      Mt = fmaxf(Mt, load_coherent(&part_ms[((int64_t)z * p.splits + s2) * p.nr + i].x));
+    float St2 = 0.0f, Tt = 0.0f;
+    for (int s2 = 0; s2 < p.splits; ++s2) {
+      const int64_t sl = ((int64_t)z * p.splits + s2) * p.nr + i;
+      const float f = fast_exp2(p.escale * (load_coherent(&part_ms[sl].x) - Mt));
+      St2 = fmaf(load_coherent(&part_ms[sl].y), f, St2);
+      Tt = fmaf(load_coherent(&part_t[sl * CW + c]), f, Tt);
+    }
+    pv_store(p, i, z * CW + c, Mt, St2, Tt);
+  }
+  if (threadIdx.x == 0) atomicExch(counter, 0u);
+}
+
 // Value fragment (tile t, value block ob, part vp, K block kb) in lane l
 // (h = l / 32): the values of index 32 ob + l % 32 at the eight points
 // 32 t + 16 kb + 8 (e / 4) + 4 h + e % 4, e = 0..7 -- the column order of a
@@ -668,6 +990,51 @@ __global__ __launch_bounds__(256) void k_pack_values(const void* src, int src_bf
   }
 }
 
+// Tangent records of the rows for the weighted application, in the GEMM-tiled
+// record order: float32 points, one record in the row form of the six-slot
+// split (scale 1, so its product with a column record is t_i.y_j to float32
+// accuracy); bf16 points, two records holding the bf16 parts of t (t - hi
+// rounded again), whose products with the exact bf16 column records sum to
+// t_i.y_j within 2^-16. qoff_i = t_i.shift adds back the centering of float32
+// columns (q uses the points as given).
+__global__ __launch_bounds__(256) void k_pack_tangent(const float* __restrict__ T, int bf16pts, int64_t n, int d,
+                                                      int nkb, const float* __restrict__ shift, bf16x8* out,
+                                                      int64_t part_stride, float* __restrict__ qoff) {
+  const int chunks = nkb * 2;
+  const int64_t total = n * chunks;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = c / chunks;
+    const int q = (int)(c % chunks);
+    bf16x8 a = {}, b = {};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int s2 = q * 8 + e;
+      if (bf16pts) {
+        if (s2 < d) {
+          const float v = T[r * d + s2];
+          const __bf16 hi = (__bf16)v;
+          a[e] = hi;
+          b[e] = (__bf16)(v - (float)hi);
+        }
+      } else if (s2 < 6 * d) {
+        const int k = s2 / 6, w = s2 % 6;
+        __bf16 v1, v2, v3;
+        split3(T[r * d + k], v1, v2, v3);
+        a[e] = (w == 2 || w == 4) ? v2 : (w == 5 ? v3 : v1);
+      }
+    }
+    const int64_t at = r * chunks + (q % nkb) * 2 + q / nkb;
+    out[at] = a;
+    if (bf16pts) out[part_stride + at] = b;
+    if (qoff && q == 0) {
+      float acc = 0.0f;
+      for (int k = 0; k < d; ++k) acc = fmaf(T[r * d + k], shift ? shift[k] : 0.0f, acc);
+      qoff[r] = acc;
+    }
+  }
+}
+
 // Row blocks per wave of the resident kernel: two where registers allow.
 constexpr int pv_rb(int nkb, int nob, int vp) { return (nkb <= 4 && nob * vp <= 2) ? 2 : 1; }
 
@@ -697,6 +1064,24 @@ hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, const dim3& gr
   return hipGetLastError();
 }
 
+template <int NOBW>
+hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, int wq, const dim3& grid, hipStream_t s) {
+  const int col_last = (int)(mfma_padded_count(a.nc) - 1);
+  if (wq == 0) {
+    if (pp == 3 && vp == 3) k_pv_wide<3, 3, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else if (pp == 2 && vp == 1) k_pv_wide<2, 1, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else return hipErrorInvalidValue;
+  } else if (wq == 1 && pp == 3 && vp == 3) {  // float32 points: one six-slot tangent record
+    k_pv_wide<3, 3, NOBW, 1><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+  } else if (wq == 2 && pp == 2 && vp == 1) {  // bf16 points: two bf16 parts of the tangent
+    k_pv_wide<2, 1, NOBW, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int NOB>
 hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& grid, hipStream_t s) {
   if (pp == 3 && vp == 3) k_pv_gemm<NOB, 3, 3><<<grid, kThreads, 0, s>>>(a, nkb);
@@ -719,10 +1104,9 @@ void pv_parts(int dtype, bool grad, int& pp, int& vp) {
 }
 
 int pv_nob(bool gemm, int nobt) {
-  // The GEMM-tiled kernel recomputes the scores once per chunk of value blocks,
-  // so it carries up to 4 blocks per chunk (one workgroup per CU then; 8 would
-  // spill).
-  if (gemm) return nobt >= 4 ? 4 : (nobt >= 2 ? 2 : 1);
+  // GEMM-tiled, more than two value blocks: the wide kernel, whose four waves
+  // carry NOBW blocks each (a chunk of 4 NOBW blocks, up to 512 values).
+  if (gemm && nobt > 2) return 4 * (nobt <= 4 ? 1 : (nobt <= 8 ? 2 : 4));
   return nobt >= 2 ? 2 : 1;
 }
 
@@ -732,8 +1116,8 @@ int pv_gemm_resident(int nob) {
   // Per device and value blocks per chunk, computed once; concurrent first
   // calls compute the same value.
   constexpr int kDevices = 16;
-  static std::atomic<int> cached[kDevices][5];
-  if (nob < 1 || nob > 4) return 256;
+  static std::atomic<int> cached[kDevices][17];
+  if (nob < 1 || nob > 16) return 256;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev][nob] : nullptr;
@@ -743,7 +1127,9 @@ int pv_gemm_resident(int nob) {
     hipError_t e = hipErrorInvalidValue;
     if (nob == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<1, 3, 3>, kThreads, 0);
     if (nob == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<2, 3, 3>, kThreads, 0);
-    if (nob == 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<4, 3, 3>, kThreads, 0);
+    if (nob == 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 1, 1>, kThreads, 0);
+    if (nob == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 2, 1>, kThreads, 0);
+    if (nob == 16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 4, 1>, kThreads, 0);
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
@@ -787,15 +1173,16 @@ PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, in
   // P V 10.1 -> 6.2 ms); bf16 records stay on the 128 x 128 tile (d = 512:
   // 1.0 ms there, 1.3 ms on the larger one).
   const bool tile8 = pv_tile8(gemm, nob, vp);
-  pl.rows_per_block = tile8 ? PvGeo::kRows : (gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32);
+  const bool wide = gemm && nob >= 4;
+  pl.rows_per_block = tile8 ? PvGeo::kRows : (wide ? kPvwRows : (gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32));
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
   if (gemm) {
     int64_t max_splits = nc / 512 > 1 ? nc / 512 : 1;
     if (max_splits > 64) max_splits = 64;
     int64_t cps = 0;
     const int64_t units = (int64_t)pl.row_blocks * (nchunks > 0 ? nchunks : 1);
-    pl.splits = (int)round_filling_splits(units, nc, tile8 ? PvGeo::kCols : kGCols, max_splits,
-                                          tile8 ? pv_gemm8_resident() : pv_gemm_resident(nob), cps);
+    pl.splits = (int)round_filling_splits(units, nc, tile8 ? PvGeo::kCols : (wide ? PvwGeo::kCols : kGCols),
+                                          max_splits, tile8 ? pv_gemm8_resident() : pv_gemm_resident(nob), cps);
     pl.cols_per_split = (int)cps;
     return pl;
   }
@@ -821,7 +1208,10 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
     if (pv_tile8(gemm, nob, vp)) return run_pv_gemm8(a, nkb, pp, vp, grid, s);
     if (nob == 1) return run_pv_gemm<1>(a, nkb, pp, vp, grid, s);
     if (nob == 2) return run_pv_gemm<2>(a, nkb, pp, vp, grid, s);
-    if (nob == 4) return run_pv_gemm<4>(a, nkb, pp, vp, grid, s);
+    const int wq = a.wrec ? (pp == 3 ? 1 : 2) : 0;
+    if (nob == 4) return run_pv_wide<1>(a, nkb, pp, vp, wq, grid, s);
+    if (nob == 8) return run_pv_wide<2>(a, nkb, pp, vp, wq, grid, s);
+    if (nob == 16) return run_pv_wide<4>(a, nkb, pp, vp, wq, grid, s);
     return hipErrorInvalidValue;
   }
   const int rb = pv_rb(nkb, nob, vp);
@@ -843,6 +1233,15 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
     case 812: return run_pv_mfma<8, 1, 2>(a, pp, vp, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_pack_tangent(const float* T, bool bf16pts, int64_t n, int d, int nkb, const float* shift,
+                               bf16x8* out, int64_t part_stride, float* qoff, hipStream_t s) {
+  const int64_t total = n * nkb * 2;
+  const int64_t blocks = (total + 255) / 256;
+  k_pack_tangent<<<(int)(blocks < 8192 ? blocks : 8192), 256, 0, s>>>(T, bf16pts ? 1 : 0, n, d, nkb, shift, out,
+                                                                      part_stride, qoff);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,

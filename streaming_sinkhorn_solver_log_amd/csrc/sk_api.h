@@ -14,7 +14,8 @@ namespace api {
 constexpr size_t kAlign = 256;                  // workspace alignment
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // largest n or m
 constexpr int64_t kHadamardCols = 64;           // value columns per application
-constexpr int kHvpMaxD = 64;                    // largest d of the Hessian-vector product
+constexpr int kHvpMaxD = 4096;                  // largest d of the Hessian-vector product
+constexpr int64_t kMaxValueCols = 4096;         // largest value width of a transport application
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -79,6 +80,13 @@ hipError_t launch_marginal_error(const float* w, const float* p0, const float* p
 size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose);
 size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+// Weighted application (rows x, columns y, any d <= 4096, arguments validated
+// by the caller): out_i = sum_j P_ij (t_i . y_j) y_j, out and T n x d float32;
+// the (P o T Y^T) Y term of the Hessian-vector product.
+size_t apply_weighted_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+int apply_weighted(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                   const float* b, const float* f, const float* g, double eps, const float* T, float* out, void* ws,
+                   size_t ws_bytes, hipStream_t s);
 // Workspace bytes of the composed operations (compose.hip).
 size_t divergence_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 size_t hadamard_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);

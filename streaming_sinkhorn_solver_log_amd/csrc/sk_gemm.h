@@ -24,6 +24,13 @@ int pv_nob(bool gemm, int nobt);  // value blocks per launch chunk
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
                      const PassPlan& pl, hipStream_t s);
+// Tangent records of n rows (T n x d float32) for the weighted application:
+// one record array (float32 points) or two (bf16 points, part_stride bf16x8
+// apart), GEMM-tiled order; qoff (or null) = T . shift per row.
+hipError_t launch_pack_tangent(const float* T, bool bf16pts, int64_t n, int d, int nkb, const float* shift,
+                               bf16x8* out, int64_t part_stride, float* qoff, hipStream_t s);
+// Value blocks per chunk of the weighted application (always the wide kernel).
+inline int pv_nob_weighted(int nobt) { return 4 * (nobt <= 4 ? 1 : (nobt <= 8 ? 2 : 4)); }
 // Value fragments of nv points (src nv x kv, float32 or bf16 bits) for vp parts.
 hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
                               int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s);

@@ -76,6 +76,13 @@ struct PvArgs {
   int nr, nc, row_blocks, nchunks;
   int splits, cols_per_split;
   float escale;
+  // Weighted application (wide kernel, apply mode): each plan entry is
+  // multiplied by q_ij = acc'_ij + qoff_i, acc'_ij the product of row i's
+  // tangent records (wq arrays of nr records, wrec_stride bf16x8 apart) with
+  // column j's records. Null wrec: unweighted.
+  const bf16x8* wrec;
+  int64_t wrec_stride;
+  const float* qoff;       // nr per-row offsets of q (or null)
 };
 
 struct MfmaPrepSide {

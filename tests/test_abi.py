@@ -78,11 +78,13 @@ def test_workspace_sizes(lib):
             assert lib.sk_workspace_bytes(had, 0, n, m, d, 65) == 0
             assert lib.sk_workspace_bytes(_header_int("SK_OP_SOLVE_TOL"), 0, n, m, d, 0) > s
             assert lib.sk_workspace_bytes(_header_int("SK_OP_HVP"), 0, n, m, d, 0) > 0
-    assert lib.sk_workspace_bytes(_header_int("SK_OP_HVP"), 0, 100, 100, 65, 0) == 0
+    assert lib.sk_workspace_bytes(_header_int("SK_OP_HVP"), 0, 100, 100, 65, 0) > 0
+    assert lib.sk_workspace_bytes(_header_int("SK_OP_HVP"), 0, 100, 100, 4097, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 0, 5, 3, 0) == 0
     assert lib.sk_workspace_bytes(solve, 0, 5, 5, 0, 0) == 0
     assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 0) == 0
-    assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 65) == 0
+    assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 65) > 0
+    assert lib.sk_workspace_bytes(apply, 0, 5, 5, 3, 4097) == 0
     assert lib.sk_workspace_bytes(99, 0, 5, 5, 3, 0) == 0
 
 
@@ -126,7 +128,7 @@ def test_solve_rejects_invalid_arguments(lib, kw, code):
 def test_apply_and_grad_reject_invalid_arguments(lib):
     inv, uns, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_UNSUPPORTED"), _header_int("SK_ERR_WORKSPACE")
     base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, FAKE, FAKE, 0.1, 0, FAKE, 4, FAKE, FAKE, 1 << 30, None]
-    for idx, val, code in [(11, 2, inv), (13, 0, inv), (13, 65, uns), (12, None, inv), (14, None, inv),
+    for idx, val, code in [(11, 2, inv), (13, 0, inv), (13, 4097, uns), (12, None, inv), (14, None, inv),
                            (8, None, inv), (10, 0.0, inv), (15, None, wsp), (16, 8, wsp)]:
         args = list(base)
         args[idx] = val
@@ -180,7 +182,7 @@ def test_hvp_rejects_invalid_arguments(lib):
     base = [FAKE, FAKE, 0, 10, 12, 3, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 1e-6, 100, FAKE, FAKE, FAKE, 1 << 30,
             None]
     for idx, val, code in [(8, None, inv), (11, None, inv), (12, None, inv), (13, 0.0, inv), (14, 0, inv),
-                           (15, None, inv), (5, 65, uns), (11, FAKE + 4, inv), (17, None, wsp), (18, 64, wsp)]:
+                           (15, None, inv), (5, 4097, uns), (11, FAKE + 4, inv), (17, None, wsp), (18, 64, wsp)]:
         args = list(base)
         args[idx] = val
         assert lib.sk_ot_hvp_x(*args) == code, (idx, val)

@@ -469,6 +469,10 @@ APPLY_CASES = [
     (5, 300, 1300, 16),  # bf16 d = 1024, GEMM-tiled
     (4, 600, 700, 40),   # float32 d = 512, two value blocks
     (4, 300, 1300, 16),  # float32 d = 512, 8-wave tile: the last column block overhangs the padding
+    (4, 300, 700, 130),  # float32 d = 512, wide kernel (two value blocks per wave)
+    (7, 250, 900, 600),  # bf16 d = 512, wide kernel, two value chunks
+    (3, 400, 500, 100),  # bf16 d = 64, register-resident kernel over two value chunks
+    (1, 200, 333, 97),   # float32 d = 3, widths past 64
 ]
 
 
@@ -841,6 +845,9 @@ HVP_CASES = [
     (6, 500, 450, 0.05),     # float32 d = 3, mixture
     (3, 300, 350, None),     # bf16 d = 64
     (2, 200, 260, 0.02),     # float32 d = 3, smaller eps
+    (4, 120, 150, None),     # float32 d = 512 (GEMM-tiled records)
+    (7, 110, 130, None),     # bf16 d = 512
+    (5, 60, 200, None),      # bf16 d = 1024, rectangular
 ]
 
 
