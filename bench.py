@@ -395,6 +395,23 @@ def measure_hvp(case, steps, warmup):
             "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "cg_tol": 1e-6}}
 
 
+def measure_newton(case, steps, sk_tol=1e-4):
+    """Newton-CG on the workload's x (float32 points): wall time, costs and
+    gradient norms of `steps` steps (blocking)."""
+    sk, w, torch = case.sk, case.w, case.torch
+    sk.ot_newton_x(case.x, case.y, case.a, case.b, w.eps, newton_iters=1, sk_tol=sk_tol, sk_max_iters=5000)
+    torch.cuda.synchronize()
+    print("[newton] warm-up done", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    _, costs, norms, done = sk.ot_newton_x(case.x, case.y, case.a, case.b, w.eps, newton_iters=steps,
+                                           sk_tol=sk_tol, sk_max_iters=5000)
+    sec = time.perf_counter() - t0
+    return {"metric": "Newton-CG steps/s on x -> OT_eps(mu_x, nu)", "value": done / sec if done else 0.0,
+            "unit": "steps/s", "seconds": sec, "steps": done, "costs": costs, "grad_norms": norms,
+            "higher_is_better": True, "n_gpus": 1, "data": "synthetic",
+            "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "sk_tol": sk_tol}}
+
+
 def measure_tol(case, tol, check_every=10, max_iters=20000, eps_start=0.0):
     """Iterations and wall time to reach a marginal error of tol (blocking solve
     with a check every `check_every` iterations)."""
@@ -639,6 +656,8 @@ def main():
     ap.add_argument("--low-eps-study", action="store_true",
                     help="iterations and time to marginal tolerances 1e-3..1e-5 at eps 1e-2..3e-4, with and "
                          "without eps-scaling, on the workload's points")
+    ap.add_argument("--newton", type=int, default=0, metavar="K",
+                    help="time K steps of Newton-CG on the workload's x (float32 points)")
     ap.add_argument("--hvp", action="store_true",
                     help="time one Hessian-vector product of OT_eps in x at the workload's solved pair")
     ap.add_argument("--peaks", action="store_true",
@@ -684,6 +703,9 @@ def main():
         return
     if args.hvp:
         print(json.dumps(measure_hvp(case, args.steps, args.warmup)), flush=True)
+        return
+    if args.newton:
+        print(json.dumps(measure_newton(case, args.newton)), flush=True)
         return
     if args.low_eps_study:
         print(json.dumps(measure_low_eps(case)), flush=True)

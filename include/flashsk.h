@@ -66,7 +66,7 @@ extern "C" {
 
 /* solve flags */
 #define SK_WARM_START 1u /* f and g hold the starting potentials (else zeros)  */
-#define SK_NO_CENTER 2u  /* do not translate float32 clouds to a common origin */
+#define SK_NO_CENTER 2u  /* do not translate the clouds toward the origin     */
 #define SK_CHECK_FINITE 4u /* screen the inputs first (see sk_sinkhorn_solve)    */
 
 /* operations, for sk_workspace_bytes */
@@ -77,6 +77,7 @@ extern "C" {
 #define SK_OP_APPLY_HADAMARD 4
 #define SK_OP_SOLVE_TOL 5
 #define SK_OP_HVP 6
+#define SK_OP_NEWTON 7 /* float32 points only */
 
 /*
  * Fixed-budget Sinkhorn solve (FlashSinkhorn abstract; review, Summary and
@@ -210,6 +211,39 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
                 const float* b, const float* f, const float* g, double eps, const float* V, float* out,
                 double cg_tol, int32_t cg_max_iters, int32_t* cg_iters, double* cg_resid, void* ws,
                 size_t ws_bytes, void* stream);
+
+/*
+ * Newton-CG on the points x of the first measure: minimizes
+ *   F(x) = OT_eps(sum_i a_i delta_{x_i}, sum_j b_j delta_{y_j})
+ * over x (n x d) with y, a, b, eps fixed (the replication review's Summary and
+ * Strengths: the streaming HVP makes Newton-CG on OT_eps possible in
+ * O((n + m) d) memory; the pages print no algorithm, so the textbook
+ * line-search Newton-CG is used). Each iterate's potentials are solved to the
+ * marginal error sk_tol (sk_sinkhorn_solve_tol, alternating, a check every 10
+ * iterations, at most sk_max_iters; warm from the previous iterate's), F is
+ * <a, f> + <b, g>, its gradient sk_eot_grad_x and its Hessian sk_ot_hvp_x
+ * (inner Schur CG to 1e-6, at most 500 iterations). The CG on H p = -grad
+ * stops at the forcing term min(1/2, sqrt|grad|) |grad|, at cg_max_iters, or
+ * at the first direction of non-positive curvature (the first one gives
+ * p = -grad); the step t halves from 1 until the Armijo condition
+ * F(x + t p) <= F(x) + 1e-4 t grad.p holds (at most 30 halvings, else stop).
+ *   x0         n x d float32 start (may equal x).
+ *   y          m x d float32 (the points are float32 on both sides).
+ *   newton_iters   at most this many steps; grad_tol >= 0 stops earlier once
+ *              |grad|_2 <= grad_tol.
+ *   x          out: n x d float32, the last iterate.
+ *   costs      out (host, newton_iters + 1 doubles, or NULL): F at iterates 0..steps.
+ *   grad_norms out (host, newton_iters + 1 doubles, or NULL): |grad|_2 at the
+ *              iterates whose gradient was formed (0..steps).
+ *   steps_done out (host): steps taken.
+ * BLOCKING (host decisions on every CG and line-search step).
+ * Requirements: d <= 4096 (SK_ERR_UNSUPPORTED above); sk_tol > 0; as for the
+ * solve otherwise. Workspace: sk_workspace_bytes(SK_OP_NEWTON, SK_F32, n, m, d, 0).
+ */
+int sk_ot_newton_x(const float* x0, const float* y, int64_t n, int64_t m, int64_t d, const float* a,
+                   const float* b, double eps, double sk_tol, int32_t sk_max_iters, int32_t newton_iters,
+                   double grad_tol, int32_t cg_max_iters, float* x, double* costs, double* grad_norms,
+                   int32_t* steps_done, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Debiased Sinkhorn divergence (the replication review names a

@@ -14,6 +14,7 @@ the package fails loudly if the shared library is missing.
     out = transport_apply_hadamard(x, y, a, b, f, g, eps, A, B, V)   # (P o A B^T) V
     grad = eot_grad_x(x, y, a, b, g, eps)
     HV, cg_iters, cg_resid = ot_hvp_x(x, y, a, b, f, g, eps, V)       # blocking
+    x, costs, gnorms, steps = ot_newton_x(x0, y, a, b, eps)          # Newton-CG, blocking
     S, ga, gb, gx, gy = sinkhorn_divergence(x, y, a, b, eps, iters)  # debiased
 
 x, y: (n, d) and (m, d) float32 or bfloat16 CUDA tensors; a, b, f, g, V, U:
@@ -33,7 +34,7 @@ SK_OK, SK_ERR_INVALID_ARG, SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE, SK_ERR_HIP = 0,
 SK_F32, SK_BF16 = 0, 1
 SK_ALTERNATING, SK_SYMMETRIC = 0, 1
 SK_WARM_START, SK_NO_CENTER, SK_CHECK_FINITE = 1, 2, 4
-SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD, SK_OP_SOLVE_TOL, SK_OP_HVP = range(7)
+SK_OP_SOLVE, SK_OP_APPLY, SK_OP_GRAD, SK_OP_DIVERGENCE, SK_OP_APPLY_HADAMARD, SK_OP_SOLVE_TOL, SK_OP_HVP, SK_OP_NEWTON = range(8)
 
 _ERR_NAMES = {SK_ERR_INVALID_ARG: "SK_ERR_INVALID_ARG", SK_ERR_UNSUPPORTED: "SK_ERR_UNSUPPORTED",
               SK_ERR_WORKSPACE: "SK_ERR_WORKSPACE", SK_ERR_HIP: "SK_ERR_HIP"}
@@ -73,6 +74,8 @@ def _load_library() -> ctypes.CDLL:
     lib.sk_sinkhorn_solve_tol.restype = INT
     lib.sk_ot_hvp_x.argtypes = [P, P, INT, I64, I64, I64, P, P, P, P, D, P, P, D, I32, P, P, P, SZ, P]
     lib.sk_ot_hvp_x.restype = INT
+    lib.sk_ot_newton_x.argtypes = [P, P, I64, I64, I64, P, P, D, D, I32, I32, D, I32, P, P, P, P, P, SZ, P]
+    lib.sk_ot_newton_x.restype = INT
     lib.sk_sinkhorn_solve_noalloc.argtypes = [P, P, INT, I64, I64, I64, P, P, D, I32, INT, U32, P, P, P, P]
     lib.sk_sinkhorn_solve_noalloc.restype = INT
     lib.sk_noalloc_scratch_bytes.argtypes = []
@@ -88,7 +91,8 @@ def _load_library() -> ctypes.CDLL:
 
 _lib = _load_library()
 EXPORTS = ("sk_sinkhorn_solve", "sk_sinkhorn_solve_tol", "sk_transport_apply", "sk_transport_apply_hadamard", "sk_eot_grad_x",
-           "sk_ot_hvp_x", "sk_sinkhorn_divergence", "sk_sinkhorn_solve_noalloc", "sk_noalloc_scratch_bytes",
+           "sk_ot_hvp_x", "sk_ot_newton_x", "sk_sinkhorn_divergence", "sk_sinkhorn_solve_noalloc",
+           "sk_noalloc_scratch_bytes",
            "sk_workspace_bytes", "sk_last_error", "sk_version")
 
 
@@ -366,3 +370,30 @@ def ot_hvp_x(x, y, a, b, f, g, eps: float, V, cg_tol: float = 1e-6, cg_max_iters
                                 _ptr(V), _ptr(out), float(cg_tol), int(cg_max_iters), ctypes.byref(iters),
                                 ctypes.byref(resid), ctypes.c_void_p(wptr), wbytes, _stream(dev)))
     return out, iters.value, resid.value
+
+
+def ot_newton_x(x0, y, a, b, eps: float, newton_iters: int = 10, sk_tol: float = 1e-5, sk_max_iters: int = 20000,
+                grad_tol: float = 0.0, cg_max_iters: int = 100, workspace=None):
+    """Line-search Newton-CG on the points x of the first measure, minimizing
+    OT_eps(sum_i a_i delta_{x_i}, sum_j b_j delta_{y_j}) (flashsk.h,
+    sk_ot_newton_x); x0 (n, d) and y (m, d) float32. Blocking. Returns
+    (x, costs, grad_norms, steps): the last iterate, and float64 arrays of
+    the cost and gradient norm at iterates 0..steps."""
+    n, m, d, dt = _points(x0, y)
+    if dt != SK_F32:
+        raise TypeError("Newton-CG takes float32 points")
+    dev = x0.device
+    _vec(a, n, "a", dev)
+    _vec(b, m, "b", dev)
+    x = torch.empty_like(x0)
+    costs = (ctypes.c_double * (newton_iters + 1))()
+    norms = (ctypes.c_double * (newton_iters + 1))()
+    steps = ctypes.c_int32(0)
+    ws, wptr, wbytes = _workspace(SK_OP_NEWTON, dt, n, m, d, 0, dev, workspace)
+    with torch.cuda.device(dev):
+        _check(_lib.sk_ot_newton_x(_ptr(x0), _ptr(y), n, m, d, _ptr(a), _ptr(b), float(eps), float(sk_tol),
+                                   int(sk_max_iters), int(newton_iters), float(grad_tol), int(cg_max_iters),
+                                   _ptr(x), costs, norms, ctypes.byref(steps), ctypes.c_void_p(wptr), wbytes,
+                                   _stream(dev)))
+    k = steps.value
+    return x, [costs[i] for i in range(k + 1)], [norms[i] for i in range(k + 1)], k

@@ -269,7 +269,7 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
     pv_parts(dtype, grad || weighted, ap.pp, ap.vp);
     const int blocks = (int)((kv + 31) / 32);
-    ap.nob = weighted ? pv_nob_weighted(blocks) : pv_nob(gemm, blocks);
+    ap.nob = weighted ? pv_wide_nob(blocks, ap.vp, true) : pv_nob(gemm, blocks, ap.vp);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
     ap.nobt = ap.nchunks * ap.nob;
     ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks);
@@ -327,7 +327,7 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   hipError_t e = launch_prep_mfma(px, py, dtype, (int)d, ap.nkb, false, true, L.c.centroid, L.c.shift,
                                   L.c.counters, ncnt + 1, sc.log2e_over_eps, sc.c2, ap.path == Path::Gemm, s);
   if (e != hipSuccess) return hip_fail(e, "prep");
-  const float* shift = dtype == SK_F32 ? L.c.shift : nullptr;
+  const float* shift = L.c.shift;  // centering shift of both clouds (exact for bf16 points)
   e = launch_pack_values(vsrc, vsrc_bf16, ap.nc, ap.kv, grad ? shift : nullptr, ap.vp, ap.nobt,
                          L.vtiles, L.vfrag, s);
   if (e != hipSuccess) return hip_fail(e, "value packing");
@@ -344,12 +344,11 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   pa.escale = mfma_escale(dtype, sc.c2);
   if (ap.wq > 0) {
     const int64_t stride = (int64_t)ap.nr * ap.nkb * 2;
-    e = launch_pack_tangent(tangent, dtype == SK_BF16, ap.nr, (int)d, ap.nkb, shift, L.wrec, stride,
-                            dtype == SK_F32 ? L.qoff : nullptr, s);
+    e = launch_pack_tangent(tangent, dtype == SK_BF16, ap.nr, (int)d, ap.nkb, shift, L.wrec, stride, L.qoff, s);
     if (e != hipSuccess) return hip_fail(e, "tangent records");
     pa.wrec = L.wrec;
     pa.wrec_stride = stride;
-    pa.qoff = dtype == SK_F32 ? L.qoff : nullptr;
+    pa.qoff = L.qoff;
   }
   e = launch_pv(pa, ap.path == Path::Gemm, ap.nkb, ap.nob, ap.pp, ap.vp, ap.pl, s);
   if (e != hipSuccess) return hip_fail(e, grad ? "grad" : "apply");
@@ -592,6 +591,9 @@ size_t sk_workspace_bytes(int op, int dtype, int64_t n, int64_t m, int64_t d, in
     case SK_OP_APPLY_HADAMARD:
       if (aux_path(dtype, d) == Path::None || k < 1 || k > kHadamardCols) return 0;
       return hadamard_ws_bytes(dtype, n, m, d);
+    case SK_OP_NEWTON:
+      if (dtype != SK_F32 || aux_path(dtype, d) == Path::None || d > kHvpMaxD) return 0;
+      return newton_ws_bytes(n, m, d);
     case SK_OP_DIVERGENCE:
       if (solve_path(dtype, d) == Path::None) return 0;
       return divergence_ws_bytes(dtype, n, m, d);

@@ -419,6 +419,69 @@ HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   return L;
 }
 
+// ---------------------------------------------------------------- Newton-CG
+// Line-search Newton-CG on x -> OT_eps(mu_x, nu) (the replication review's
+// Summary and Strengths: the streaming HVP makes Newton-CG on OT_eps possible
+// in O((n + m) d) memory; the pages print no algorithm, so the textbook one is
+// used): at each iterate the potentials are solved to a marginal tolerance,
+// the gradient is the barycentric gradient, the inner CG on H p = -grad stops
+// at the forcing term min(1/2, sqrt|g|) |g| or at the first direction of
+// non-positive curvature (which falls back to -grad on the first inner
+// iteration), and an Armijo backtracking (c1 = 1e-4, up to 30 halvings)
+// chooses the step; each trial solve starts from the current potentials.
+
+// out = x + t p, elementwise
+__global__ void k_step(const float* __restrict__ x, const float* __restrict__ p, float t, int64_t cnt,
+                       float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = fmaf(t, p[i], x[i]);
+}
+
+// dv = -r + beta dv, elementwise (the next conjugate direction)
+__global__ void k_cg_dir(const float* __restrict__ r, float beta, int64_t cnt, float* __restrict__ dv) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    dv[i] = fmaf(beta, dv[i], -r[i]);
+}
+
+// out = -p, elementwise
+__global__ void k_neg(const float* __restrict__ p, int64_t cnt, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cnt; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = -p[i];
+}
+
+struct NewtonWs {
+  float *f, *g, *ft, *gt, *grad, *z, *r, *dv, *Hd, *p, *xt;
+  double *cost, *dots;
+  void* inner;
+  size_t inner_bytes, bytes;
+};
+
+NewtonWs layout_newton(void* ws, int64_t n, int64_t m, int64_t d) {
+  Carve c{static_cast<char*>(ws)};
+  NewtonWs L{};
+  L.f = c.take<float>(n);
+  L.g = c.take<float>(m);
+  L.ft = c.take<float>(n);
+  L.gt = c.take<float>(m);
+  L.grad = c.take<float>(n * d);
+  L.z = c.take<float>(n * d);
+  L.r = c.take<float>(n * d);
+  L.dv = c.take<float>(n * d);
+  L.Hd = c.take<float>(n * d);
+  L.p = c.take<float>(n * d);
+  L.xt = c.take<float>(n * d);
+  L.cost = c.take<double>(2);
+  L.dots = c.take<double>(2);
+  size_t need = solve_tol_ws_bytes(SK_F32, n, m, d);
+  const size_t gb = grad_bytes(SK_F32, n, m, d), hb = hvp_ws_bytes(SK_F32, n, m, d);
+  need = gb > need ? gb : need;
+  need = hb > need ? hb : need;
+  L.inner_bytes = need;
+  L.inner = c.take<char>(need);
+  L.bytes = c.off;
+  return L;
+}
+
 }  // namespace
 
 namespace api {
@@ -437,6 +500,7 @@ size_t solve_tol_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
   return layout_tol(nullptr, dtype, n, m, d).bytes;
 }
 size_t hvp_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d) { return layout_hvp(nullptr, dtype, n, m, d).bytes; }
+size_t newton_ws_bytes(int64_t n, int64_t m, int64_t d) { return layout_newton(nullptr, n, m, d).bytes; }
 }  // namespace api
 }  // namespace sk
 
@@ -621,6 +685,131 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
   if ((rc = apply_weighted(x, y, dtype, n, m, d, a, b, f, g, eps, V, L.HY, L.inner, L.inner_bytes, s))) return rc;
   k_hvp_out<<<grid_for(n * d), 256, 0, s>>>(L.r, V, L.df, L.sv, L.PY, L.PDY, L.HY, n, d, (float)(2.0 / eps), out);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "hvp");
+  return SK_OK;
+}
+
+int sk_ot_newton_x(const float* x0, const float* y, int64_t n, int64_t m, int64_t d, const float* a,
+                   const float* b, double eps, double sk_tol, int32_t sk_max_iters, int32_t newton_iters,
+                   double grad_tol, int32_t cg_max_iters, float* x, double* costs, double* grad_norms,
+                   int32_t* steps_done, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int rc = check_common(x0, y, SK_F32, n, m, d, a, b, eps, aux_path(SK_F32, d));
+  if (rc) return rc;
+  if (!x || !steps_done) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(x, 16)) return fail(SK_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  if (d > kHvpMaxD) return fail(SK_ERR_UNSUPPORTED, "Newton-CG supports d <= %d (d=%lld)", kHvpMaxD, (long long)d);
+  if (!(sk_tol > 0.0) || !isfinite(sk_tol)) return fail(SK_ERR_INVALID_ARG, "sk_tol must be finite and > 0");
+  if (sk_max_iters < 1 || cg_max_iters < 1 || newton_iters < 0)
+    return fail(SK_ERR_INVALID_ARG, "sk_max_iters and cg_max_iters must be >= 1, newton_iters >= 0");
+  if (!(grad_tol >= 0.0) || !isfinite(grad_tol)) return fail(SK_ERR_INVALID_ARG, "grad_tol must be finite and >= 0");
+  const NewtonWs L = layout_newton(ws, n, m, d);
+  if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const int64_t nd = n * d;
+  double host[2];
+  int32_t its = 0;
+  double err = 0.0;
+  auto dot = [&](const float* p, const float* q, double& out) -> int {
+    k_dot<<<1, 1024, 0, s>>>(p, q, nd, L.dots);
+    if ((e = hipGetLastError()) != hipSuccess ||
+        (e = hipMemcpyAsync(host, L.dots, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "newton reduction");
+    out = host[0];
+    return SK_OK;
+  };
+  // potentials at xx to the marginal tolerance, warm from (fw, gw) if warm; cost to host
+  auto solve_at = [&](const float* xx, float* fw, float* gw, bool warm, double& cost) -> int {
+    int r2 = sk_sinkhorn_solve_tol(xx, y, SK_F32, n, m, d, a, b, eps, 0.0, sk_max_iters, SK_ALTERNATING,
+                                   warm ? SK_WARM_START : 0u, sk_tol, 10, fw, gw, L.cost, &its, &err, L.inner,
+                                   L.inner_bytes, stream);
+    if (r2) return r2;
+    if ((e = hipMemcpyAsync(host, L.cost, sizeof(double), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess)
+      return hip_fail(e, "newton cost");
+    cost = host[0];
+    return SK_OK;
+  };
+  if (x != x0 && (e = hipMemcpyAsync(x, x0, nd * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+    return hip_fail(e, "newton copy");
+  double cost = 0.0;
+  if ((rc = solve_at(x, L.f, L.g, false, cost))) return rc;
+  if (costs) costs[0] = cost;
+  int32_t steps = 0;
+  for (int32_t k = 0; k <= newton_iters; ++k) {
+    if ((rc = sk_eot_grad_x(x, y, SK_F32, n, m, d, a, b, L.g, eps, L.grad, L.inner, L.inner_bytes, stream)))
+      return rc;
+    double gg = 0.0;
+    if ((rc = dot(L.grad, L.grad, gg))) return rc;
+    const double gn = sqrt(gg);
+    if (grad_norms) grad_norms[k] = gn;
+    if (k == newton_iters || gn <= grad_tol) break;
+    // truncated CG on H p = -grad
+    const double tolk = (sqrt(gn) < 0.5 ? sqrt(gn) : 0.5) * gn;
+    k_fill<<<grid_for(nd), 256, 0, s>>>(L.z, 0.0f, nd);
+    k_neg<<<grid_for(nd), 256, 0, s>>>(L.grad, nd, L.dv);
+    if ((e = hipGetLastError()) != hipSuccess ||
+        (e = hipMemcpyAsync(L.r, L.grad, nd * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "newton");
+    double rr = gg;
+    const float* p = L.z;
+    for (int32_t j = 0; j < cg_max_iters; ++j) {
+      int32_t hits = 0;
+      double hres = 0.0;
+      if ((rc = sk_ot_hvp_x(x, y, SK_F32, n, m, d, a, b, L.f, L.g, eps, L.dv, L.Hd, 1e-6, 500, &hits, &hres, L.inner,
+                            L.inner_bytes, stream)))
+        return rc;
+      double curv = 0.0;
+      if ((rc = dot(L.dv, L.Hd, curv))) return rc;
+      if (!(curv > 0.0)) {
+        if (j == 0) {
+          k_neg<<<grid_for(nd), 256, 0, s>>>(L.grad, nd, L.p);
+          if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "newton");
+          p = L.p;
+        }
+        break;
+      }
+      const double alpha = rr / curv;
+      k_axpy<<<grid_for(nd), 256, 0, s>>>((float)alpha, L.dv, L.z, nd, 0);
+      k_axpy<<<grid_for(nd), 256, 0, s>>>((float)alpha, L.Hd, L.r, nd, 0);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "newton");
+      double rr_new = 0.0;
+      if ((rc = dot(L.r, L.r, rr_new))) return rc;
+      if (sqrt(rr_new) < tolk) break;
+      k_cg_dir<<<grid_for(nd), 256, 0, s>>>(L.r, (float)(rr_new / rr), nd, L.dv);
+      if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "newton");
+      rr = rr_new;
+    }
+    // Armijo backtracking along p
+    double slope = 0.0;
+    if ((rc = dot(L.grad, p, slope))) return rc;
+    double t = 1.0, ct = 0.0;
+    bool accepted = false;
+    for (int h = 0; h <= 30; ++h) {
+      k_step<<<grid_for(nd), 256, 0, s>>>(x, p, (float)t, nd, L.xt);
+      if ((e = hipGetLastError()) != hipSuccess ||
+          (e = hipMemcpyAsync(L.ft, L.f, n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+          (e = hipMemcpyAsync(L.gt, L.g, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "newton");
+      if ((rc = solve_at(L.xt, L.ft, L.gt, true, ct))) return rc;
+      if (ct <= cost + 1e-4 * t * slope) {
+        accepted = true;
+        break;
+      }
+      t *= 0.5;
+    }
+    if (!accepted) break;
+    if ((e = hipMemcpyAsync(x, L.xt, nd * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(L.f, L.ft, n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(L.g, L.gt, m * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "newton");
+    cost = ct;
+    ++steps;
+    if (costs) costs[steps] = cost;
+  }
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "newton");
+  *steps_done = steps;
   return SK_OK;
 }
 

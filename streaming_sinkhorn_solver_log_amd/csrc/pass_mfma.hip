@@ -574,7 +574,8 @@ __global__ __launch_bounds__(256) void k_pack_records(const void* pts, int dtype
       if (dtype == 1) {
         if (s < d) {
           const unsigned short bits = static_cast<const unsigned short*>(pts)[r * d + s];
-          const __bf16 v = __builtin_bit_cast(__bf16, bits);
+          __bf16 v = __builtin_bit_cast(__bf16, bits);
+          if (shift) v = (__bf16)(__uint_as_float((unsigned)bits << 16) - shift[s]);  // exact (prep.hip)
           rv[e] = v;
           cv[e] = v;
         }
@@ -614,6 +615,7 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
     if (dtype == 1) {
       const unsigned short bits = static_cast<const unsigned short*>(pts)[r * d + k];
       v = __uint_as_float(static_cast<unsigned>(bits) << 16);
+      if (shift) v -= shift[k];
     } else {
       v = static_cast<const float*>(pts)[r * d + k];
       if (shift) v -= shift[k];
@@ -804,8 +806,9 @@ hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int 
                             unsigned* counters, int n_counters, float log2e_over_eps,
                             float c2, bool interleave, hipStream_t s) {
   const float* sh = nullptr;
-  if (center && dtype == 0) {
-    hipError_t e = launch_centroid(xs.pts, xs.n, ys.pts, ys.n, dtype, d, centroid_part, shift, s);
+  if (center) {
+    hipError_t e = dtype == 0 ? launch_centroid(xs.pts, xs.n, ys.pts, ys.n, dtype, d, centroid_part, shift, s)
+                              : launch_bf16_shift(xs.pts, xs.n, ys.pts, ys.n, d, centroid_part, shift, s);
     if (e != hipSuccess) return e;
     sh = shift;
   }

@@ -212,12 +212,9 @@ __device__ __forceinline__ void pv_store(const PvArgs& p, int i, int cc, float m
   const int64_t o = (int64_t)i * p.kv + cc;
   if (p.grad) {
     float xv;
-    if (p.xbf16) {
-      xv = __uint_as_float((unsigned)static_cast<const unsigned short*>(p.xrow)[o] << 16);
-    } else {
-      xv = static_cast<const float*>(p.xrow)[o];
-      if (p.shift) xv -= p.shift[cc];
-    }
+    if (p.xbf16) xv = __uint_as_float((unsigned)static_cast<const unsigned short*>(p.xrow)[o] << 16);
+    else xv = static_cast<const float*>(p.xrow)[o];
+    if (p.shift) xv -= p.shift[cc];
     p.out[o] = 2.0f * p.wrow[i] * (xv - T / S);
   } else {
     p.out[o] = T * fast_exp2(fmaf(p.escale, mu, p.hrow[i]));
@@ -770,9 +767,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
   }
   __syncthreads();
   f32x16 acc[2], accq[2];
+  // value fragments of the block's column tiles, one tile ahead (the first
+  // tile's loads go out with the block's last K chunk), where the registers
+  // allow it; three-part values at four blocks per wave load at their use
+  constexpr bool PF = !(VP == 3 && NOBW == 4);
+  VTile<NOBW, VP> vb0, vb1;
   for (int st = 0; st < nstages; ++st) {
     const int blk = st / nkc, kc = st % nkc;
     const int buf = st & 1;
+    if (PF && kc == nkc - 1)
+      load_vtile<NOBW, VP>(vb0, p, min(((j0 + blk * G::kCols) >> 5), col_last >> 5), ob0, lane);
     if (kc == 0) {
       acc[0] = f32x16{};
       acc[1] = f32x16{};
@@ -854,8 +858,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
       // a column block can overhang the padded columns by up to 3 tiles:
       // those columns are masked, so any zero-valued tile serves, here the
       // last padded one
+      constexpr int KMAX = PP > VP ? PP : VP;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
+        VTile<NOBW, VP>& cur = (ct & 1) ? vb1 : vb0;
+        VTile<NOBW, VP>& nxt = (ct & 1) ? vb0 : vb1;
+        if constexpr (PF) {
+          if (ct + 1 < 4) load_vtile<NOBW, VP>(nxt, p, min((cb >> 5) + ct + 1, col_last >> 5), ob0, lane);
+        } else {
+          load_vtile<NOBW, VP>(cur, p, min((cb >> 5) + ct, col_last >> 5), ob0, lane);
+        }
         bf16x8 Pf[2][PP][2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -863,17 +875,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
           for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) Pf[rt][pp][kb] = lds.P[rt][ct][pp][kb][lane];
-        const int64_t tile = min((cb >> 5) + ct, col_last >> 5);
 #pragma unroll
-        for (int ob = 0; ob < NOBW; ++ob) {
-          VTile<1, VP> vt;
-          load_vtile<1, VP>(vt, p, tile, ob0 + ob, lane);
+        for (int ob = 0; ob < NOBW; ++ob)
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            f32x16 (&Oo)[1] = *reinterpret_cast<f32x16(*)[1]>(&O[rt][ob]);
-            pv_mfma<1, PP, VP>(vt, Pf[rt], Oo);
-          }
-        }
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+              for (int vp = 0; vp < VP; ++vp)
+                if (pp + vp < KMAX) {
+#pragma unroll
+                  for (int kb = 0; kb < 2; ++kb)
+                    O[rt][ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[ob][vp][kb], Pf[rt][pp][kb],
+                                                                        O[rt][ob], 0, 0, 0);
+                }
       }
     }
     if (st + 2 < nstages) {
@@ -975,12 +990,9 @@ __global__ __launch_bounds__(256) void k_pack_values(const void* src, int src_bf
       const int64_t j = t * 32 + kb * 16 + 8 * (e >> 2) + 4 * h + (e & 3);
       float v = 0.0f;
       if (j < nv && cc < kv) {
-        if (src_bf16) {
-          v = __uint_as_float((unsigned)static_cast<const unsigned short*>(src)[j * kv + cc] << 16);
-        } else {
-          v = static_cast<const float*>(src)[j * kv + cc];
-          if (shift) v -= shift[cc];
-        }
+        if (src_bf16) v = __uint_as_float((unsigned)static_cast<const unsigned short*>(src)[j * kv + cc] << 16);
+        else v = static_cast<const float*>(src)[j * kv + cc];
+        if (shift) v -= shift[cc];
       }
       __bf16 a, b, c;
       split3(v, a, b, c);
@@ -1067,18 +1079,21 @@ hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, const dim3& gr
 template <int NOBW>
 hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, int wq, const dim3& grid, hipStream_t s) {
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
-  if (wq == 0) {
-    if (pp == 3 && vp == 3) k_pv_wide<3, 3, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-    else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-    else if (pp == 2 && vp == 1) k_pv_wide<2, 1, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-    else return hipErrorInvalidValue;
-  } else if (wq == 1 && pp == 3 && vp == 3) {  // float32 points: one six-slot tangent record
-    k_pv_wide<3, 3, NOBW, 1><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-  } else if (wq == 2 && pp == 2 && vp == 1) {  // bf16 points: two bf16 parts of the tangent
-    k_pv_wide<2, 1, NOBW, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-  } else {
-    return hipErrorInvalidValue;
+  if constexpr (NOBW <= 2) {
+    if (wq == 1 && pp == 3 && vp == 3) {  // float32 points: one six-slot tangent record
+      k_pv_wide<3, 3, NOBW, 1><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+      return hipGetLastError();
+    }
+    if (wq == 2 && pp == 2 && vp == 1) {  // bf16 points: two bf16 parts of the tangent
+      k_pv_wide<2, 1, NOBW, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+      return hipGetLastError();
+    }
   }
+  if (wq != 0) return hipErrorInvalidValue;
+  if (pp == 3 && vp == 3) k_pv_wide<3, 3, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+  else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+  else if (pp == 2 && vp == 1) k_pv_wide<2, 1, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -1103,10 +1118,10 @@ void pv_parts(int dtype, bool grad, int& pp, int& vp) {
   }
 }
 
-int pv_nob(bool gemm, int nobt) {
+int pv_nob(bool gemm, int nobt, int vp) {
   // GEMM-tiled, more than two value blocks: the wide kernel, whose four waves
   // carry NOBW blocks each (a chunk of 4 NOBW blocks, up to 512 values).
-  if (gemm && nobt > 2) return 4 * (nobt <= 4 ? 1 : (nobt <= 8 ? 2 : 4));
+  if (gemm && nobt > 2) return pv_wide_nob(nobt, vp, false);
   return nobt >= 2 ? 2 : 1;
 }
 
@@ -1129,7 +1144,7 @@ int pv_gemm_resident(int nob) {
     if (nob == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<2, 3, 3>, kThreads, 0);
     if (nob == 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 1, 1>, kThreads, 0);
     if (nob == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 2, 1>, kThreads, 0);
-    if (nob == 16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 4, 1>, kThreads, 0);
+    if (nob == 16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<2, 1, 4, 0>, kThreads, 0);
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;

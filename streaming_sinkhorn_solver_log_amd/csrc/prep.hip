@@ -135,7 +135,82 @@ __global__ __launch_bounds__(1024) void k_cost(const float* a, const float* f, i
   if (threadIdx.x == 0) *cost = red[0];
 }
 
+// Exact shift of bf16 clouds. Translating bf16 points by their centroid would
+// change their values (x - t is rarely a bf16 number), so the shift of
+// coordinate k is taken where the difference stays exact: when every point of
+// both clouds has the same sign in k, t_k is the largest multiple of U_k (the
+// bf16 spacing at the largest |value|) not above the smallest |value|, with
+// that sign. Then each x - t_k is a multiple of the spacing at x and smaller
+// than |x|, so it has at most 8 significant bits: exactly a bf16 number. A
+// coordinate whose values change sign keeps t_k = 0.
+// Ordered integer image of a float: a < b as floats iff ord(a) < ord(b) as
+// signed integers, so atomicMin / atomicMax on the images reduce floats.
+__device__ __forceinline__ int float_ord(float v) {
+  const int b = __float_as_int(v);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float ord_float(int o) { return __int_as_float(o >= 0 ? o : o ^ 0x7FFFFFFF); }
+
+__global__ __launch_bounds__(256) void k_bf16_shift_init(int* mm, int d) {
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    mm[k] = float_ord(INFINITY);
+    mm[d + k] = float_ord(-INFINITY);
+  }
+}
+
+// mm[k] = ord(min), mm[d + k] = ord(max) of coordinate k over both clouds:
+// each workgroup reduces a contiguous range of rows, each thread a fixed set
+// of coordinates (coalesced along the rows), then one atomic per coordinate.
+__global__ __launch_bounds__(256) void k_bf16_shift_partial(const unsigned short* x, int64_t n,
+                                                             const unsigned short* y, int64_t m, int d,
+                                                             int rows_per_block, int* mm) {
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  const int kt = d < 256 ? d : 256;  // coordinates per row sweep
+  const int rstep = 256 / kt;        // rows per sweep
+  const int k0 = threadIdx.x % kt, rr = threadIdx.x / kt;
+  if (rr >= rstep) return;
+  for (int k = k0; k < d; k += kt) {
+    float lo = INFINITY, hi = -INFINITY;
+    for (int64_t r = r0 + rr; r < r0 + rows_per_block && r < n + m; r += rstep) {
+      const unsigned short bits = r < n ? x[r * d + k] : y[(r - n) * d + k];
+      const float v = __uint_as_float((unsigned)bits << 16);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+    atomicMin(&mm[k], float_ord(lo));
+    atomicMax(&mm[d + k], float_ord(hi));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_bf16_shift_final(const int* mm, int d, float* shift) {
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float lo = ord_float(mm[k]), hi = ord_float(mm[d + k]);
+    float t = 0.0f;
+    if (lo > 0.0f || hi < 0.0f) {
+      const float small = lo > 0.0f ? lo : -hi, big = lo > 0.0f ? hi : -lo;
+      int e = 0;
+      frexpf(big, &e);                   // big = m 2^e, m in [0.5, 1)
+      const float U = ldexpf(1.0f, e - 8);  // bf16 spacing in [2^(e-1), 2^e)
+      t = floorf(small / U) * U;
+      if (hi < 0.0f) t = -t;
+    }
+    shift[k] = t;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_bf16_shift(const void* x, int64_t n, const void* y, int64_t m, int d, double* part, float* shift,
+                             hipStream_t s) {
+  int* mm = reinterpret_cast<int*>(part);  // 2 d ints of the centroid scratch
+  const int rows = 64;
+  const int64_t blocks = (n + m + rows - 1) / rows;
+  k_bf16_shift_init<<<1, 256, 0, s>>>(mm, d);
+  k_bf16_shift_partial<<<(int)blocks, 256, 0, s>>>(static_cast<const unsigned short*>(x), n,
+                                                    static_cast<const unsigned short*>(y), m, d, rows, mm);
+  k_bf16_shift_final<<<1, 256, 0, s>>>(mm, d, shift);
+  return hipGetLastError();
+}
 
 hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, int dtype, int d,
                            double* centroid_part, float* shift, hipStream_t s) {

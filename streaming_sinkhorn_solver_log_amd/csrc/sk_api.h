@@ -92,6 +92,7 @@ size_t divergence_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 size_t hadamard_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 size_t solve_tol_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 size_t hvp_ws_bytes(int dtype, int64_t n, int64_t m, int64_t d);
+size_t newton_ws_bytes(int64_t n, int64_t m, int64_t d);
 
 }  // namespace api
 }  // namespace sk

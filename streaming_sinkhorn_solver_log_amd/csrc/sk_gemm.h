@@ -20,7 +20,7 @@ hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool sc
 // Transport application / gradient kernels. pv_parts: bf16 parts of the plan
 // entries (pp) and of the values (vp) for a storage type and operation.
 void pv_parts(int dtype, bool grad, int& pp, int& vp);
-int pv_nob(bool gemm, int nobt);  // value blocks per launch chunk
+int pv_nob(bool gemm, int nobt, int vp);  // value blocks per launch chunk
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
                      const PassPlan& pl, hipStream_t s);
@@ -29,8 +29,14 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
 // apart), GEMM-tiled order; qoff (or null) = T . shift per row.
 hipError_t launch_pack_tangent(const float* T, bool bf16pts, int64_t n, int d, int nkb, const float* shift,
                                bf16x8* out, int64_t part_stride, float* qoff, hipStream_t s);
-// Value blocks per chunk of the weighted application (always the wide kernel).
-inline int pv_nob_weighted(int nobt) { return 4 * (nobt <= 4 ? 1 : (nobt <= 8 ? 2 : 4)); }
+// Value blocks per chunk of the wide kernel (the weighted application always
+// runs on it): 4 NOBW, NOBW <= 4, and <= 2 in the weighted mode (its
+// registers would spill at 4).
+inline int pv_wide_nob(int nobt, int vp, bool weighted) {
+  (void)vp;
+  const int w = nobt <= 4 ? 1 : (nobt <= 8 || weighted ? 2 : 4);
+  return 4 * w;
+}
 // Value fragments of nv points (src nv x kv, float32 or bf16 bits) for vp parts.
 hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
                               int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s);

@@ -25,6 +25,10 @@ struct PassPlan {
 
 hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, int dtype, int d,
                            double* centroid_part, float* shift, hipStream_t s);
+// Exact per-coordinate shift of two bf16 clouds (see prep.hip): part holds
+// kCentroidBlocks x 2 x d doubles of scratch.
+hipError_t launch_bf16_shift(const void* x, int64_t n, const void* y, int64_t m, int d, double* part, float* shift,
+                             hipStream_t s);
 hipError_t launch_zero_u32(unsigned* p, int64_t count, hipStream_t s);
 hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
                        int64_t m, double* cost, hipStream_t s);

@@ -233,3 +233,21 @@ def test_noalloc_solve_validates_before_any_device_call(lib):
             args[4], args[5] = 20_000, 512
         assert fn(*args) == code, (idx, val)
         assert len(lib.sk_last_error()) > 0
+
+
+def test_newton_rejects_invalid_arguments(lib):
+    P, I64, I32, D, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
+    fn = lib.sk_ot_newton_x
+    fn.argtypes = [P, P, I64, I64, I64, P, P, D, D, I32, I32, D, I32, P, P, P, P, P, SZ, P]
+    fn.restype = ctypes.c_int
+    inv, uns, wsp = _header_int("SK_ERR_INVALID_ARG"), _header_int("SK_ERR_UNSUPPORTED"), _header_int("SK_ERR_WORKSPACE")
+    base = [FAKE, FAKE, 10, 12, 3, FAKE, FAKE, 0.1, 1e-5, 100, 5, 0.0, 50, FAKE, None, None, FAKE, FAKE, 1 << 30,
+            None]
+    for idx, val, code in [(0, None, inv), (13, None, inv), (16, None, inv), (8, 0.0, inv), (9, 0, inv),
+                           (10, -1, inv), (11, -1.0, inv), (12, 0, inv), (4, 4097, uns), (7, 0.0, inv),
+                           (17, None, wsp), (18, 64, wsp)]:
+        args = list(base)
+        args[idx] = val
+        assert fn(*args) == code, (idx, val)
+    assert lib.sk_workspace_bytes(_header_int("SK_OP_NEWTON"), 1, 10, 12, 3, 0) == 0  # float32 points only
+    assert lib.sk_workspace_bytes(_header_int("SK_OP_NEWTON"), 0, 10, 12, 3, 0) > 0

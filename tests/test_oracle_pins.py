@@ -501,3 +501,54 @@ def test_solve_tol_eps_scaling_schedule():
     assert done == 23 and np.isfinite(err)
     np.testing.assert_allclose(f, fr, rtol=0, atol=1e-13)
     np.testing.assert_allclose(g, gr, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- Newton-CG
+def _newton_instance(seed=5, n=10, m=24, d=2):
+    rng = np.random.default_rng(seed)
+    y = rng.uniform(0, 1, (m, d))
+    x0 = rng.uniform(0, 1, (n, d))
+    return x0, y, np.full(n, 1.0 / n), np.full(m, 1.0 / m)
+
+
+def test_newton_reaches_a_stationary_point_with_decreasing_cost():
+    """Line-search Newton-CG on x -> OT_eps(mu_x, nu): the costs decrease
+    (Armijo), the gradient norm falls below 1e-8, the last steps converge
+    superlinearly, and the limit is a fixed point of the barycentric map,
+    r_i x_i = (P Y)_i, checked with the plan's own row sums and application
+    (not with the gradient routine)."""
+    x0, y, a, b = _newton_instance()
+    eps = 0.1
+    x, costs, norms, steps = oracle.newton_x(x0, y, a, b, eps, 12, sk_tol=1e-13, grad_tol=1e-9)
+    assert np.all(np.diff(costs) < 1e-15)
+    assert norms[-1] < 1e-8 and steps < 12
+    tail = norms[-4:]  # the full Newton steps at the end
+    # superlinear there: |g_{k+1}| <= e |g_k|^1.3
+    assert all(np.log(tail[i + 1]) <= 1.3 * np.log(tail[i]) + 1.0 for i in range(len(tail) - 1))
+    f, g, _, _ = oracle.solve_tol(x, y, a, b, eps, 1e-13, 10 ** 7, "alternating", 10)
+    r, _ = oracle.marginals(x, y, a, b, f, g, eps)
+    PY = oracle.apply(x, y, a, b, f, g, eps, y)
+    assert np.abs(r[:, None] * x - PY).max() < 1e-9
+
+
+def test_newton_step_solves_the_newton_system_by_finite_differences():
+    """Near the minimizer the first inner CG direction p satisfies H p = -grad,
+    H p taken here as a central difference of the converged gradient (not the
+    Hessian-vector routine the step uses)."""
+    x0, y, a, b = _newton_instance()
+    eps = 0.1
+    xs, _, _, _ = oracle.newton_x(x0, y, a, b, eps, 12, sk_tol=1e-13, grad_tol=1e-9)
+    xk = xs + 0.01 * np.random.default_rng(9).standard_normal(xs.shape)
+
+    def conv_grad(xx):
+        f, g, _, _ = oracle.solve_tol(xx, y, a, b, eps, 1e-14, 10 ** 7, "alternating", 10)
+        return oracle.grad_x(xx, y, a, b, g, eps)
+    g0 = conv_grad(xk)
+    x1, _, _, steps = oracle.newton_x(xk, y, a, b, eps, 1, sk_tol=1e-13)
+    assert steps == 1
+    p = x1 - xk  # the full step (t = 1 near the minimizer)
+    h = 1e-4
+    Hp = (conv_grad(xk + h * p) - conv_grad(xk - h * p)) / (2 * h)
+    # the inner CG stops at the forcing term min(1/2, sqrt|g|) |g|
+    gn = np.linalg.norm(g0)
+    assert np.linalg.norm(Hp + g0) <= 1.05 * min(0.5, np.sqrt(gn)) * gn + 1e-7

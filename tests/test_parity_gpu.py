@@ -20,6 +20,7 @@ import torch
 import oracle
 import workloads as W
 from tests.golden import fullsize as FS
+from tests.golden import newton_cases as NC
 
 pytestmark = pytest.mark.gpu
 
@@ -432,6 +433,45 @@ def test_translation_invariance(sk):
     f2, g2, c2 = sk.solve(x + t, y + t, a, b, w.eps, w.iters)
     assert (f1 - f2).abs().max().item() <= 1e-4 * w.eps
     assert abs(float(c1) - float(c2)) <= 1e-5 * abs(float(c1))
+
+
+@pytest.mark.parametrize("mode", ["alternating", "symmetric"])
+def test_bf16_clouds_far_from_the_origin(sk, mode):
+    """bf16 points near 200 in every coordinate: the library translates them by
+    an exactly representable shift (bf16 differences stay bf16), so the
+    |x|^2 + |y|^2 - 2 x.y expansion keeps its accuracy. Solve, gradient and
+    application against the oracle on the same stored values; without the
+    shift (center=False) the float32 expansion is visibly worse."""
+    rng = np.random.default_rng([31, 5])
+    n, m, d, eps, iters = 700, 900, 8, 1.0, 10
+    xs = W.f32_to_bf16_bits((200.0 + 1.5 * rng.standard_normal((n, d))).astype(np.float32))
+    ys = W.f32_to_bf16_bits((201.0 + 1.5 * rng.standard_normal((m, d))).astype(np.float32))
+    a = np.full(n, np.float32(1.0 / n), dtype=np.float32)
+    b = np.full(m, np.float32(1.0 / m), dtype=np.float32)
+    x64, y64 = W.bf16_bits_to_f32(xs).astype(np.float64), W.bf16_bits_to_f32(ys).astype(np.float64)
+    x, y = dev_points(xs, "bf16"), dev_points(ys, "bf16")
+    at, bt = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    say(f"bf16 far from the origin, {mode}")
+    f, g, cost = sk.solve(x, y, at, bt, eps, iters, mode)
+    fr, gr, cr = oracle.solve(x64, y64, a, b, eps, iters, mode)
+    fn, gn = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    ef, eg = np.abs(fn - fr).max(), np.abs(gn - gr).max()
+    tol = 1e-3 * max(np.abs(fr).max(), eps)
+    f0, g0, _ = sk.solve(x, y, at, bt, eps, iters, mode, center=False)
+    e0 = np.abs(f0.cpu().numpy().astype(np.float64) - fr).max()
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} (tol {tol:.1e}); without the shift max|df|={e0:.3e}")
+    assert ef <= tol and eg <= tol
+    assert abs(float(cost) - cr) <= 1e-3 * abs(cr)
+    assert e0 > 10 * ef
+    grad = sk.eot_grad_x(x, y, at, bt, g, eps).cpu().numpy()
+    ref = oracle.grad_x(x64, y64, a, b, gn, eps)
+    e_g = np.abs(grad - ref).max() / np.abs(ref).max()
+    V = torch.from_numpy(rng.standard_normal((m, 5)).astype(np.float32)).to(DEV)
+    PV = sk.transport_apply(x, y, at, bt, f, g, eps, V).cpu().numpy()
+    ref1 = oracle.apply(x64, y64, a, b, fn, gn, eps, V.cpu().numpy())
+    e1 = np.abs(PV - ref1).max() / np.abs(ref1).max()
+    say(f"  grad rel err {e_g:.3e}, P.V rel err {e1:.3e}")
+    assert e_g <= 1e-3 and e1 <= 1e-3
 
 
 GRAD_CASES = [
@@ -997,3 +1037,54 @@ def test_hvp_and_hadamard_properties_at_full_size(sk, key):
     plain = sk.transport_apply(x, y, a, b, f, g, w.eps, Vv)
     had = sk.transport_apply_hadamard(x, y, a, b, f, g, w.eps, ones_n, ones_m, Vv)
     assert torch.equal(plain, had)
+
+
+def _newton_reference():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_newton.json")
+    with open(path) as fh:
+        return json.load(fh)
+
+
+@pytest.mark.parametrize("case", range(len(NC.CASES)))
+def test_newton_matches_float64_newton(sk, case):
+    """Newton-CG on x -> OT_eps(mu_x, nu) against the float64 oracle's Newton-CG
+    (same algorithm; dense Moore-Penrose Hessian-vector products; stored by
+    tests/golden/make_oracle_newton.py) from the same float32 start: the same
+    cost after the first step, and the same stationary point. Later iterates
+    may part slightly: the inner CG stops on a threshold (the forcing term),
+    which float32 and float64 residuals can cross at different inner steps."""
+    ref = _newton_reference()
+    assert ref["oracle_sha256"] == NC.oracle_digest(), "oracle changed: the stored Newton references are stale"
+    seed, n, m, d, eps = NC.CASES[case]
+    r = ref["cases"][case]
+    assert (r["seed"], r["n"], r["m"], r["d"], r["eps"]) == (seed, n, m, d, eps)
+    x0, y, a, b = NC.inputs(seed, n, m, d)
+    say(f"newton seed={seed} n={n} m={m} d={d} eps={eps}")
+    t = lambda v: torch.from_numpy(v).to(DEV)  # noqa: E731
+    # the marginal tolerance of each solve stays above the float32 floor of the
+    # measured error (2^-24 max|f| / eps, about 1e-6 here)
+    x, costs, norms, steps = sk.ot_newton_x(t(x0), t(y), t(a), t(b), eps, newton_iters=NC.NEWTON_ITERS, sk_tol=1e-5,
+                                            sk_max_iters=4000, grad_tol=NC.GRAD_TOL)
+    costs_o, norms_o = np.array(r["costs"]), np.array(r["grad_norms"])
+    xo = np.array(r["x"]).reshape(n, d)
+    say(f"  GPU {steps} steps, costs {np.array(costs)}, |grad| {np.array(norms)}")
+    say(f"  float64 {r['steps']} steps, costs {costs_o}, |grad| {norms_o}")
+    k = min(1, steps, r["steps"])
+    assert np.allclose(costs[:k + 1], costs_o[:k + 1], rtol=1e-5, atol=0)
+    assert norms[-1] <= 1e-4
+    assert abs(costs[-1] - costs_o[-1]) <= 1e-5 * abs(costs_o[-1])
+    assert np.abs(x.cpu().numpy() - xo).max() <= 2e-3
+
+
+def test_newton_decreases_the_cost_at_full_shape(sk):
+    """At n = m = 2000 (no dense reference): every step lowers the cost (Armijo)
+    and the gradient norm falls by two orders of magnitude."""
+    w = W.CASES[6].scaled(2000, 2000)
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    xs, costs, norms, steps = sk.ot_newton_x(x, y, a, b, 0.05, newton_iters=8, sk_tol=1e-4, sk_max_iters=4000)
+    say(f"newton n=m=2000 d=3: {steps} steps, costs {np.array(costs)}, |grad| {np.array(norms)}")
+    assert steps >= 3 and np.all(np.diff(costs) < 0)
+    assert norms[-1] <= 1e-2 * norms[0]
