@@ -338,7 +338,7 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   pa.nobt = ap.nobt; pa.kv = ap.kv; pa.out = out;
   pa.hrow = R.hval[0]; pa.wrow = a; pa.xrow = x; pa.xbf16 = dtype == SK_BF16; pa.shift = shift;
   pa.grad = grad ? 1 : 0;
-  pa.part = reinterpret_cast<float*>(L.c.part); pa.counters = L.c.counters;
+  pa.part = reinterpret_cast<float*>(L.c.part);
   pa.nr = (int)ap.nr; pa.nc = (int)ap.nc; pa.row_blocks = ap.pl.row_blocks; pa.nchunks = ap.nchunks;
   pa.splits = ap.pl.splits; pa.cols_per_split = ap.pl.cols_per_split;
   pa.escale = mfma_escale(dtype, sc.c2);

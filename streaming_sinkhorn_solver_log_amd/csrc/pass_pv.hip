@@ -222,12 +222,11 @@ __device__ __forceinline__ void pv_store(const PvArgs& p, int i, int cc, float m
 }
 
 // End of a workgroup: with one split, every lane writes its rows' outputs;
-// otherwise the partials (mu, S, T) go to the split buffer and the last
-// workgroup of the row block merges them in split order (bitwise repeatable).
-// Lanes of inactive waves hold nothing but take part in the barriers.
-template <int RB, int NOB, int NT = kThreads>
+// otherwise the partials (mu, S, T) go to the split buffer, which k_pv_merge
+// combines after the launch. Lanes of inactive waves hold nothing.
+template <int RB, int NOB>
 __device__ __attribute__((always_inline)) inline void pv_finish(
-    const PvArgs& p, bool active, int row_base, int rows_per_wg, const f32x16 (&O)[RB][NOB],
+    const PvArgs& p, bool active, int row_base, const f32x16 (&O)[RB][NOB],
     const float (&mu)[RB], const float (&S)[RB], int li, int half) {
   constexpr int CW = NOB * 32;
   const int sp = blockIdx.y, z = blockIdx.z;
@@ -255,41 +254,20 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
   float2* part_ms = reinterpret_cast<float2*>(p.part);
   float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);  // 16-byte aligned value partials
   const int64_t slot = (int64_t)z * p.splits + sp;
-  if (active) {
+  if (!active) return;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = row_base + rb * 32 + li;
-      if (i >= p.nr) continue;
-      if (half == 0) store_coherent(&part_ms[slot * p.nr + i], make_float2(mu[rb], St[rb]));
-      float* T = part_t + (slot * p.nr + i) * CW;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = row_base + rb * 32 + li;
+    if (i >= p.nr) continue;
+    if (half == 0) part_ms[slot * p.nr + i] = make_float2(mu[rb], St[rb]);
+    float* T = part_t + (slot * p.nr + i) * CW;
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob)
+    for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) store_coherent(T + ob * 32 + 8 * q + 4 * half + e, O[rb][ob][4 * q + e]);
-    }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(T + ob * 32 + 8 * q + 4 * half) =
+            make_float4(O[rb][ob][4 * q], O[rb][ob][4 * q + 1], O[rb][ob][4 * q + 2], O[rb][ob][4 * q + 3]);
   }
-  unsigned* counter = p.counters + (int64_t)z * p.row_blocks + blockIdx.x;
-  if (!arrive_last(counter, p.splits)) return;
-  const int row0 = blockIdx.x * rows_per_wg;
-  for (int q = threadIdx.x; q < rows_per_wg * CW; q += NT) {
-    const int i = row0 + q / CW;
-    const int c = q % CW;
-    if (i >= p.nr || cbase + c >= p.kv) continue;
-    float Mt = kMuInit;
-    for (int s2 = 0; s2 < p.splits; ++s2)
-      Mt = fmaxf(Mt, load_coherent(&part_ms[((int64_t)z * p.splits + s2) * p.nr + i].x));
-    float St2 = 0.0f, Tt = 0.0f;
-    for (int s2 = 0; s2 < p.splits; ++s2) {
-      const int64_t sl = ((int64_t)z * p.splits + s2) * p.nr + i;
-      const float f = fast_exp2(p.escale * (load_coherent(&part_ms[sl].x) - Mt));
-      St2 = fmaf(load_coherent(&part_ms[sl].y), f, St2);
-      Tt = fmaf(load_coherent(&part_t[sl * CW + c]), f, Tt);
-    }
-    pv_store(p, i, cbase + c, Mt, St2, Tt);
-  }
-  if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
 
 // Register-resident rows (record widths up to 8 K blocks): each wave keeps RB
@@ -366,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
       tile_work(c1, v1);
     }
   }
-  pv_finish<RB, NOB>(p, true, row_base, ROWS, O, mu, S, li, half);
+  pv_finish<RB, NOB>(p, true, row_base, O, mu, S, li, half);
 }
 
 // GEMM-tiled variant for wide records: the score block of a 2 x 2-wave
@@ -514,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_gemm(const PvArgs p, int nkb
     }
     __syncthreads();
   }
-  pv_finish<2, NOB>(p, wc == 0, r0 + wr * 64, kGRows, O, mu, S, li, half);
+  pv_finish<2, NOB>(p, wc == 0, r0 + wr * 64, O, mu, S, li, half);
 }
 
 // GEMM-tiled variant for one value block (applications with k <= 32): the
@@ -653,7 +631,7 @@ __global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int 
     }
   }
   __syncthreads();
-  pv_finish<WRT, 1, G::kNT>(p, wc == 0, r0 + wr * kWaveRows, G::kRows, O, mu, S, li, half);
+  pv_finish<WRT, 1>(p, wc == 0, r0 + wr * kWaveRows, O, mu, S, li, half);
 }
 
 // GEMM-tiled variant for wide value chunks (the gradient at large d: value
@@ -772,45 +750,70 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
   // allow it; three-part values at four blocks per wave load at their use
   constexpr bool PF = !(VP == 3 && NOBW == 4);
   VTile<NOBW, VP> vb0, vb1;
-  for (int st = 0; st < nstages; ++st) {
-    const int blk = st / nkc, kc = st % nkc;
-    const int buf = st & 1;
-    if (PF && kc == nkc - 1)
-      load_vtile<NOBW, VP>(vb0, p, min(((j0 + blk * G::kCols) >> 5), col_last >> 5), ob0, lane);
-    if (kc == 0) {
-      acc[0] = f32x16{};
-      acc[1] = f32x16{};
-      if constexpr (WQ > 0) {
-        accq[0] = f32x16{};
-        accq[1] = f32x16{};
-      }
+  // Blocks of 128 columns, each a run of K chunks then the epilogue; the K
+  // loop leaves the value accumulators alone, so they stay in their
+  // registers across it.
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const int cb = j0 + blk * G::kCols;
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+    if constexpr (WQ > 0) {
+      accq[0] = f32x16{};
+      accq[1] = f32x16{};
     }
+    for (int kc = 0; kc < nkc; ++kc) {
+      const int st = blk * nkc + kc;
+      const int buf = st & 1;
+      if (PF && kc == nkc - 1) {
+        load_vtile<NOBW, VP>(vb0, p, min(cb >> 5, col_last >> 5), ob0, lane);
+        // keep the loads here, a whole K chunk and the epilogue ahead of their
+        // use (the scheduler would otherwise sink them next to the MFMAs)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the stage's operand fragments are read from LDS up front, so one LDS
+      // latency precedes the stage's MFMAs rather than one per MFMA
+      bf16x8 Bs[kGKb], As[kGKb][2];
 #pragma unroll
-    for (int kb = 0; kb < kGKb; ++kb) {
-      const bf16x8 B = *reinterpret_cast<const bf16x8*>(&lds.st.rows[buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
+      for (int kb = 0; kb < kGKb; ++kb) {
+        Bs[kb] = *reinterpret_cast<const bf16x8*>(&lds.st.rows[buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(
-            &lds.st.cols[buf][((2 * sch + ct) * 32 + li) * kGRow + half * 64 + kb * 16]);
-        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[ct], 0, 0, 0);
-        if constexpr (WQ > 0) {
+        for (int ct = 0; ct < 2; ++ct)
+          As[kb][ct] = *reinterpret_cast<const bf16x8*>(
+              &lds.st.cols[buf][((2 * sch + ct) * 32 + li) * kGRow + half * 64 + kb * 16]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int qq = 0; qq < WQ; ++qq) {
-            const bf16x8 Bw =
-                *reinterpret_cast<const bf16x8*>(&lds.wrows[qq][buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
-            accq[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bw, accq[ct], 0, 0, 0);
+      for (int kb = 0; kb < kGKb; ++kb) {
+        const bf16x8 B = Bs[kb];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const bf16x8 A = As[kb][ct];
+          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[ct], 0, 0, 0);
+          if constexpr (WQ > 0) {
+#pragma unroll
+            for (int qq = 0; qq < WQ; ++qq) {
+              const bf16x8 Bw =
+                  *reinterpret_cast<const bf16x8*>(&lds.wrows[qq][buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
+              accq[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bw, accq[ct], 0, 0, 0);
+            }
           }
         }
       }
+      // the next stage's operands go to LDS before the epilogue, so their
+      // staging registers are free during it
+      if (st + 1 < nstages) {
+        tile_store<G>(g, lds.st, buf ^ 1);
+        wrec_store<PP, WQ>(wr, lds, buf ^ 1);
+      }
+      if (kc + 1 < nkc) {
+        if (st + 2 < nstages) {
+          load_stage(g, st + 2);
+          wrec_load<WQ>(wr, p, nkb, r0, (st + 2) % nkc);
+        }
+        __syncthreads();
+      }
     }
-    // the next stage's operands go to LDS before the epilogue, so their
-    // staging registers are free during it
-    if (st + 1 < nstages) {
-      tile_store<G>(g, lds.st, buf ^ 1);
-      wrec_store<PP, WQ>(wr, lds, buf ^ 1);
-    }
-    if (kc == nkc - 1) {
-      const int cb = j0 + blk * G::kCols;
+    {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const bf16x8 Aaug = p.bias_col[2 * (int64_t)min(cb + (2 * sch + ct) * 32 + li, col_last) + half];
@@ -864,7 +867,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
         VTile<NOBW, VP>& cur = (ct & 1) ? vb1 : vb0;
         VTile<NOBW, VP>& nxt = (ct & 1) ? vb0 : vb1;
         if constexpr (PF) {
-          if (ct + 1 < 4) load_vtile<NOBW, VP>(nxt, p, min((cb >> 5) + ct + 1, col_last >> 5), ob0, lane);
+          if (ct + 1 < 4) {
+            load_vtile<NOBW, VP>(nxt, p, min((cb >> 5) + ct + 1, col_last >> 5), ob0, lane);
+            __builtin_amdgcn_sched_barrier(0);  // issued one tile of MFMAs ahead of their use
+          }
         } else {
           load_vtile<NOBW, VP>(cur, p, min((cb >> 5) + ct, col_last >> 5), ob0, lane);
         }
@@ -891,10 +897,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
                 }
       }
     }
+    const int st = blk * nkc + nkc - 1;
     if (st + 2 < nstages) {
       load_stage(g, st + 2);
       wrec_load<WQ>(wr, p, nkb, r0, (st + 2) % nkc);
     }
+    // the value accumulators cross the back edge in the accumulation
+    // registers (else the compiler carries a vector-register copy of all
+    // of them and moves it on every trip)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ob = 0; ob < NOBW; ++ob) asm volatile("" : "+a"(O[rt][ob]));
     __syncthreads();
   }
 
@@ -924,8 +938,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
     }
     return;
   }
-  // Split partials (mu, S, values), merged in split order by the last
-  // workgroup of the row block (bitwise repeatable).
+  // Split partials (mu, S, values), combined by k_pv_merge after the launch.
   const int64_t nslots = (int64_t)p.nchunks * p.splits;
   float2* part_ms = reinterpret_cast<float2*>(p.part);
   float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);
@@ -934,34 +947,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
   for (int rt = 0; rt < 2; ++rt) {
     const int i = r0 + rt * 32 + li;
     if (i >= p.nr) continue;
-    if (wave == 0 && half == 0) store_coherent(&part_ms[slot * p.nr + i], make_float2(mu[rt], S[rt]));
+    if (wave == 0 && half == 0) part_ms[slot * p.nr + i] = make_float2(mu[rt], S[rt]);
     float* T = part_t + (slot * p.nr + i) * CW + wave * NOBW * 32;
 #pragma unroll
     for (int ob = 0; ob < NOBW; ++ob)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) store_coherent(T + ob * 32 + 8 * q + 4 * half + u, O[rt][ob][4 * q + u]);
+        *reinterpret_cast<float4*>(T + ob * 32 + 8 * q + 4 * half) =
+            make_float4(O[rt][ob][4 * q], O[rt][ob][4 * q + 1], O[rt][ob][4 * q + 2], O[rt][ob][4 * q + 3]);
   }
-  unsigned* counter = p.counters + (int64_t)z * p.row_blocks + blockIdx.x;
-  if (!arrive_last(counter, p.splits)) return;
-  for (int q = threadIdx.x; q < kPvwRows * CW; q += kThreads) {
-    const int i = r0 + q / CW;
-    const int c = q % CW;
-    if (i >= p.nr || z * CW + c >= p.kv) continue;
+}
+
+// Split partials of the transport kernels, combined in split order (bitwise
+// repeatable): for element (i, c) of value chunk z, M = max_s M_s and, with
+// f_s = 2^(e (M_s - M)), S = sum_s S_s f_s and T = sum_s T_s f_s, then the
+// output as in a single-split launch. cw: value columns per chunk.
+__global__ __launch_bounds__(256) void k_pv_merge(const PvArgs p, int cw) {
+  const int64_t nslots = (int64_t)p.nchunks * p.splits;
+  const float2* part_ms = reinterpret_cast<const float2*>(p.part);
+  const float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);
+  const int64_t total = (int64_t)p.nchunks * p.nr * cw;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+    const int c = (int)(q % cw);
+    const int64_t t = q / cw;
+    const int i = (int)(t % p.nr);
+    const int z = (int)(t / p.nr);
+    const int cc = z * cw + c;
+    if (cc >= p.kv) continue;
+    const int64_t s0 = (int64_t)z * p.splits * p.nr + i;  // slot (z, 0) of row i
     float Mt = kMuInit;
-    for (int s2 = 0; s2 < p.splits; ++s2)
-      Mt = fmaxf(Mt, load_coherent(&part_ms[((int64_t)z * p.splits + s2) * p.nr + i].x));
-    float St2 = 0.0f, Tt = 0.0f;
+    for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, part_ms[s0 + (int64_t)s2 * p.nr].x);
+    float St = 0.0f, Tt = 0.0f;
     for (int s2 = 0; s2 < p.splits; ++s2) {
-      const int64_t sl = ((int64_t)z * p.splits + s2) * p.nr + i;
-      const float f = fast_exp2(p.escale * (load_coherent(&part_ms[sl].x) - Mt));
-      St2 = fmaf(load_coherent(&part_ms[sl].y), f, St2);
-      Tt = fmaf(load_coherent(&part_t[sl * CW + c]), f, Tt);
+      const int64_t sl = s0 + (int64_t)s2 * p.nr;
+      const float2 ms = part_ms[sl];
+      const float f = fast_exp2(p.escale * (ms.x - Mt));
+      St = fmaf(ms.y, f, St);
+      Tt = fmaf(part_t[sl * cw + c], f, Tt);
     }
-    pv_store(p, i, z * CW + c, Mt, St2, Tt);
+    pv_store(p, i, cc, Mt, St, Tt);
   }
-  if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
 
 // Value fragment (tile t, value block ob, part vp, K block kb) in lane l
@@ -1216,8 +1241,8 @@ PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, in
   return pl;
 }
 
-hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
-                     const PassPlan& pl, hipStream_t s) {
+hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+                          const PassPlan& pl, hipStream_t s) {
   const dim3 grid(pl.row_blocks, pl.splits, a.nchunks);
   if (gemm) {
     if (pv_tile8(gemm, nob, vp)) return run_pv_gemm8(a, nkb, pp, vp, grid, s);
@@ -1248,6 +1273,17 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
     case 812: return run_pv_mfma<8, 1, 2>(a, pp, vp, grid, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+                     const PassPlan& pl, hipStream_t s) {
+  hipError_t e = launch_pv_main(a, gemm, nkb, nob, pp, vp, pl, s);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int cw = nob * 32;
+  const int64_t total = (int64_t)a.nchunks * a.nr * cw;
+  const int64_t blocks = (total + 255) / 256;
+  k_pv_merge<<<(int)(blocks < 16384 ? blocks : 16384), 256, 0, s>>>(a, cw);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_tangent(const float* T, bool bf16pts, int64_t n, int d, int nkb, const float* shift,

@@ -72,7 +72,6 @@ struct PvArgs {
   const float* shift;      // grad: centering shift of float32 points (or null)
   int grad;
   float* part;             // split partials: (mu, S) pairs then values, per (chunk, split)
-  unsigned* counters;      // chunks x row_blocks, zero on entry and exit
   int nr, nc, row_blocks, nchunks;
   int splits, cols_per_split;
   float escale;
