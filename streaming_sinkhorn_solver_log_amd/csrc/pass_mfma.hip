@@ -126,30 +126,6 @@ __device__ __forceinline__ f32x16 bias_tile(const float* hb, int half) {
   return c;
 }
 
-// s_waitcnt vmcnt(N), other counters not waited on (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// One 16-byte-per-lane global-to-LDS load from a wave-uniform base address
-// (SGPR pair) plus a per-lane 32-bit byte offset: lane l's 16 bytes land at
-// lds_addr + 16 l. Written as inline assembly so that the compiler does not
-// treat the in-flight load as aliasing every later LDS read (it would wait for
-// all of them); completion is waited for explicitly with vmcnt. The uniform
-// base keeps the per-stage address arithmetic on the scalar unit.
-__device__ __forceinline__ void load_to_lds(const void* base, unsigned lane_off, const void* lds_dst) {
-  const unsigned m0 = (unsigned)(uintptr_t)lds_dst;
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(m0) : "memory");
-}
-
-// As load_to_lds with 4 bytes per lane: lane l's 4 bytes land at lds_addr + 4 l.
-__device__ __forceinline__ void load_to_lds_dword(const void* base, unsigned lane_off, const void* lds_dst) {
-  const unsigned m0 = (unsigned)(uintptr_t)lds_dst;
-  asm volatile("global_load_lds_dword %0, %1" ::"v"(lane_off), "s"(base), "{m0}"(m0) : "memory");
-}
-
 // This wave's share of stage [c0, c0 + 128): blocks wave, wave + 4, ... of the
 // stage's blocks. Columns past the range read the padding (masked) or the
 // next range; they are never summed.

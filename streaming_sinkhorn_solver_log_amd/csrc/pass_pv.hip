@@ -637,66 +637,92 @@ __global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int 
 // GEMM-tiled variant for wide value chunks (the gradient at large d: value
 // width d up to 4 * NOBW * 32 per chunk). Each 64 x 128 score block is
 // computed once: the four waves form it together (wave w: row tile w & 1,
-// column tiles 2 (w >> 1) and 2 (w >> 1) + 1; K streamed through LDS), agree
-// on the rows' lazy shift through LDS, and write the plan entries' bf16 parts
-// to LDS; each wave then applies all 64 x 128 entries to its own NOBW value
-// blocks. The score work is thereby done once per value chunk instead of once
-// per NOB = 4 blocks (k_pv_gemm).
-using PvwGeo = Geo<1, 2, 2>;  // staging: 256 threads, 64 rows x 128 columns per stage
+// column tiles 2 (w >> 1) and 2 (w >> 1) + 1), agree on the rows' lazy shift
+// through LDS, and write the plan entries' bf16 parts to LDS; each wave then
+// applies all 64 x 128 entries to its own NOBW value blocks. The score work is
+// thereby done once per value chunk instead of once per NOB = 4 blocks
+// (k_pv_gemm).
+//
+// The score operands stream through a ring of LDS stages that direct
+// global-to-LDS loads fill several stages ahead, one K chunk (4 K blocks, 128
+// bytes per record) of the 64 row and 128 column records (and of the rows'
+// tangent records) per stage. Each load instruction reads 8 whole 128-byte
+// record chunks (coalesced) into 1 KB of LDS; within record r's 128 bytes the
+// 16-byte piece c (K block c / 2, half c % 2) is stored at position c ^ (r % 8),
+// so that the 32 lanes of an MFMA operand read (records 32 t + li, one piece
+// each) hit distinct banks. Each stage's fragments are read right after the
+// barrier that publishes it, while the previous stage's MFMAs still run.
 constexpr int kPvwRows = 64;
+constexpr int kPvwCols = 128;
+
+template <int WQ>
+struct PvwStage {
+  static constexpr int kColOff = kPvwRows * 128;             // byte offsets within a stage
+  static constexpr int kTanOff = (kPvwRows + kPvwCols) * 128;
+  static constexpr int kBytes = (kPvwRows + kPvwCols + WQ * kPvwRows) * 128;
+  static constexpr int kPerWave = kBytes / 1024 / 4;         // 1 KB load instructions per wave
+  static constexpr int kRing = WQ > 0 ? 3 : 4;               // stages (tangent records take the room of one)
+  static_assert(kBytes % 4096 == 0, "stage loads split evenly over four waves");
+};
 
 template <int PP, int WQ>
 struct PvwLds {
-  TileLds<PvwGeo> st;          // staged score operands (double buffered)
+  unsigned char ring[PvwStage<WQ>::kRing][PvwStage<WQ>::kBytes];
   bf16x8 P[2][4][PP][2][64];   // entries: row tile, column tile, part, K block, lane
   float tmax[2][2][32];        // per column half and row tile: each row's maximum over the block
   float ssum[2][2][32];        // per column half and row tile: partial row sums (gradient)
-  // staged tangent records of the rows (weighted application)
-  unsigned char wrows[WQ > 0 ? WQ : 1][2][WQ > 0 ? kPvwRows * kGRow : 16];
 };
 
-// Stage (kc) of the tangent records of rows [r0, r0 + 64): WQ arrays, each
-// like the row records (tile_load's row half).
+// This wave's loads of a stage: K chunk kc of rows [r0, r0 + 64), columns
+// [c0, c0 + 128) and the rows' tangent records, into `dst`. Load q of the
+// stage fills slots [64 q, 64 q + 64): the wave-uniform part of its address
+// is on the scalar unit, each lane adds its record's offset. Row indices
+// clamp to the last row, column indices to the last padded (masked) column.
+// This wave's loads of a stage: K chunk kc of rows [r0, r0 + 64), columns
+// [c0, c0 + 128) and the rows' tangent records, into `dst`. Load q = 4 u +
+// wave covers records [8 q', 8 q' + 8) of its region (rows for u < 2, columns
+// for u < 6, then the tangent arrays); lane l reads piece (l % 8) ^ (l / 8) of
+// record 8 q' + l / 8, which lands at position l % 8 of that record's LDS
+// chunk. Row indices clamp to the last row, column indices to the last padded
+// (masked) column. The uniform part of each address is on the scalar unit.
 template <int WQ>
-__device__ __attribute__((always_inline)) inline void wrec_load(u32x4 (&wr)[WQ > 0 ? WQ : 1][PvwGeo::kRowLoads],
-                                                                const PvArgs& p, int nkb, int r0, int kc) {
-  if constexpr (WQ > 0) {
-    const unsigned char* base = reinterpret_cast<const unsigned char*>(p.wrec);
-    const int64_t rsb = (int64_t)nkb * 32;
+__device__ __attribute__((always_inline)) inline void pvw_issue_stage(
+    unsigned char* dst, const PvArgs& p, int nkb, int col_last, int r0, int c0, int kc, int wave, int lane) {
+  using Stg = PvwStage<WQ>;
+  static_assert(Stg::kPerWave == 6 + 2 * WQ, "load q = 4 u + wave: u < 2 rows, u < 6 columns, then tangents");
+  const int64_t rsb = (int64_t)nkb * 32;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 3;
+  const unsigned piece = (unsigned)((((lane & 7) ^ g)) * 16);
+  const int64_t kco = (int64_t)kc * 128;
+  const unsigned char* rows = static_cast<const unsigned char*>(p.rows) + (int64_t)r0 * rsb + kco;
+  const unsigned char* cols = static_cast<const unsigned char*>(p.cols) + (int64_t)c0 * rsb + kco;
 #pragma unroll
-    for (int qq = 0; qq < WQ; ++qq)
-#pragma unroll
-      for (int q = 0; q < PvwGeo::kRowLoads; ++q) {
-        const int ch = threadIdx.x + q * PvwGeo::kNT;
-        const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
-        wr[qq][q] = *reinterpret_cast<const u32x4*>(base + qq * p.wrec_stride * 16 +
-                                                     (int64_t)min(r0 + rec, p.nr - 1) * rsb +
-                                                     gemm_chunk_off(hh, kc, part));
-      }
-  }
-}
-
-template <int PP, int WQ>
-__device__ __attribute__((always_inline)) inline void wrec_store(const u32x4 (&wr)[WQ > 0 ? WQ : 1][PvwGeo::kRowLoads],
-                                                                 PvwLds<PP, WQ>& L, int buf) {
-  if constexpr (WQ > 0) {
-#pragma unroll
-    for (int qq = 0; qq < WQ; ++qq)
-#pragma unroll
-      for (int q = 0; q < PvwGeo::kRowLoads; ++q) {
-        const int ch = threadIdx.x + q * PvwGeo::kNT;
-        const int rec = ch >> 3, hh = (ch >> 2) & 1, part = ch & 3;
-        *reinterpret_cast<u32x4*>(&L.wrows[qq][buf][rec * kGRow + hh * 64 + part * 16]) = wr[qq][q];
-      }
+  for (int u = 0; u < Stg::kPerWave; ++u) {
+    const int q = 4 * u + wv;
+    if (u < 2) {
+      const int rec = min(r0 + 8 * q + g, p.nr - 1) - r0;
+      load_to_lds(rows, (unsigned)(rec * rsb) + piece, dst + q * 1024);
+    } else if (u < 6) {
+      const int q2 = q - 8;
+      const int rec = min(c0 + 8 * q2 + g, col_last) - c0;
+      load_to_lds(cols, (unsigned)(rec * rsb) + piece, dst + q * 1024);
+    } else {
+      const int q3 = q - 24;  // tangent array q3 / 8, records 8 (q3 % 8) ...
+      const unsigned char* tan = reinterpret_cast<const unsigned char*>(p.wrec) +
+                                 (int64_t)(q3 >> 3) * p.wrec_stride * 16 + (int64_t)r0 * rsb + kco;
+      const int rec = min(r0 + 8 * (q3 & 7) + g, p.nr - 1) - r0;
+      load_to_lds(tan, (unsigned)(rec * rsb) + piece, dst + q * 1024);
+    }
   }
 }
 
 template <int PP, int VP, int NOBW, int WQ>
 __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb, int col_last) {
-  using G = PvwGeo;
+  using Stg = PvwStage<WQ>;
+  constexpr int R = Stg::kRing;
+  constexpr int PER = Stg::kPerWave;
   __shared__ __attribute__((aligned(16))) PvwLds<PP, WQ> lds;
-  const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
-  const unsigned char* __restrict__ cols = static_cast<const unsigned char*>(p.cols);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
@@ -719,23 +745,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
     for (int ob = 0; ob < NOBW; ++ob) O[rt][ob] = f32x16{};
 
   const int nkc = nkb / kGKb;
-  const int nblocks = (j1 - j0 + G::kCols - 1) / G::kCols;
+  const int nblocks = (j1 - j0 + kPvwCols - 1) / kPvwCols;
   const int nstages = nblocks * nkc;
-  auto load_stage = [&](TileRegs<G>& g, int st) {
-    tile_load<G>(g, rows, cols, nkb, p.nr, col_last, r0, j0 + (st / nkc) * G::kCols, st % nkc);
+  auto issue = [&](int st) {
+    pvw_issue_stage<WQ>(lds.ring[st % R], p, nkb, col_last, r0, j0 + (st / nkc) * kPvwCols, st % nkc, wave, lane);
   };
-  TileRegs<G> g;
-  u32x4 wr[WQ > 0 ? WQ : 1][G::kRowLoads];
-  if (nstages > 0) {
-    load_stage(g, 0);
-    wrec_load<WQ>(wr, p, nkb, r0, 0);
-    tile_store<G>(g, lds.st, 0);
-    wrec_store<PP, WQ>(wr, lds, 0);
-    if (nstages > 1) {
-      load_stage(g, 1);
-      wrec_load<WQ>(wr, p, nkb, r0, 1 % nkc);
+  // Waits until this wave's loads of stage st have landed, the stages after
+  // it up to `last` (at most R - 2 of them) being still in flight.
+  auto wait_stage = [&](int st, int last) {
+    const int younger = min(last, nstages - 1) - st;
+    if (R > 3 && younger >= 2) wait_vmcnt<(R > 3 ? 2 * PER : 0)>();
+    else if (younger >= 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+  };
+  // operand fragments of a stage (row tile srt, column tiles 2 sch + ct)
+  bf16x8 Bs[kGKb], As[kGKb][2], Ws[WQ > 0 ? WQ : 1][kGKb];
+  auto read_frags = [&](int st) {
+    const unsigned char* rg = lds.ring[st % R];
+#pragma unroll
+    for (int kb = 0; kb < kGKb; ++kb) {
+      const int pos = (((2 * kb + half) ^ (li & 7)) * 16) + li * 128;  // piece 2 kb + h of record 32 t + li
+      Bs[kb] = *reinterpret_cast<const bf16x8*>(rg + srt * 32 * 128 + pos);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        As[kb][ct] = *reinterpret_cast<const bf16x8*>(rg + Stg::kColOff + (2 * sch + ct) * 32 * 128 + pos);
+      if constexpr (WQ > 0) {
+#pragma unroll
+        for (int qq = 0; qq < WQ; ++qq)
+          Ws[qq][kb] = *reinterpret_cast<const bf16x8*>(rg + Stg::kTanOff + qq * (kPvwRows * 128) + srt * 32 * 128 + pos);
+      }
     }
-  }
+  };
+  // Advances the ring past stage st: refills the slot of stage st - 1 (its
+  // readers all passed the previous barrier) with stage st + R - 1, waits for
+  // this wave's loads of stage st + 1, publishes it and reads its fragments
+  // while the MFMAs of stage st still run.
+  auto advance = [&](int st) {
+    if (st + R - 1 < nstages) issue(st + R - 1);
+    if (st + 1 < nstages) wait_stage(st + 1, st + R - 1);
+    __syncthreads();
+    if (st + 1 < nstages) read_frags(st + 1);
+  };
+
+  for (int s2 = 0; s2 < R - 1 && s2 < nstages; ++s2) issue(s2);
+  if (nstages > 0) wait_stage(0, R - 2);
   float qoff[2] = {0.0f, 0.0f};
   if constexpr (WQ > 0) {
     if (p.qoff) {
@@ -744,6 +797,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
     }
   }
   __syncthreads();
+  if (nstages > 0) read_frags(0);
   f32x16 acc[2], accq[2];
   // value fragments of the block's column tiles, one tile ahead (the first
   // tile's loads go out with the block's last K chunk), where the registers
@@ -754,7 +808,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
   // loop leaves the value accumulators alone, so they stay in their
   // registers across it.
   for (int blk = 0; blk < nblocks; ++blk) {
-    const int cb = j0 + blk * G::kCols;
+    const int cb = j0 + blk * kPvwCols;
     acc[0] = f32x16{};
     acc[1] = f32x16{};
     if constexpr (WQ > 0) {
@@ -762,56 +816,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
       accq[1] = f32x16{};
     }
     for (int kc = 0; kc < nkc; ++kc) {
-      const int st = blk * nkc + kc;
-      const int buf = st & 1;
       if (PF && kc == nkc - 1) {
         load_vtile<NOBW, VP>(vb0, p, min(cb >> 5, col_last >> 5), ob0, lane);
         // keep the loads here, a whole K chunk and the epilogue ahead of their
         // use (the scheduler would otherwise sink them next to the MFMAs)
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the stage's operand fragments are read from LDS up front, so one LDS
-      // latency precedes the stage's MFMAs rather than one per MFMA
-      bf16x8 Bs[kGKb], As[kGKb][2];
 #pragma unroll
       for (int kb = 0; kb < kGKb; ++kb) {
-        Bs[kb] = *reinterpret_cast<const bf16x8*>(&lds.st.rows[buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          As[kb][ct] = *reinterpret_cast<const bf16x8*>(
-              &lds.st.cols[buf][((2 * sch + ct) * 32 + li) * kGRow + half * 64 + kb * 16]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < kGKb; ++kb) {
-        const bf16x8 B = Bs[kb];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const bf16x8 A = As[kb][ct];
-          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(As[kb][ct], Bs[kb], acc[ct], 0, 0, 0);
           if constexpr (WQ > 0) {
 #pragma unroll
-            for (int qq = 0; qq < WQ; ++qq) {
-              const bf16x8 Bw =
-                  *reinterpret_cast<const bf16x8*>(&lds.wrows[qq][buf][(srt * 32 + li) * kGRow + half * 64 + kb * 16]);
-              accq[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bw, accq[ct], 0, 0, 0);
-            }
+            for (int qq = 0; qq < WQ; ++qq)
+              accq[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(As[kb][ct], Ws[qq][kb], accq[ct], 0, 0, 0);
           }
         }
       }
-      // the next stage's operands go to LDS before the epilogue, so their
-      // staging registers are free during it
-      if (st + 1 < nstages) {
-        tile_store<G>(g, lds.st, buf ^ 1);
-        wrec_store<PP, WQ>(wr, lds, buf ^ 1);
-      }
-      if (kc + 1 < nkc) {
-        if (st + 2 < nstages) {
-          load_stage(g, st + 2);
-          wrec_load<WQ>(wr, p, nkb, r0, (st + 2) % nkc);
-        }
-        __syncthreads();
-      }
+      if (kc + 1 < nkc) advance(blk * nkc + kc);
     }
     {
 #pragma unroll
@@ -897,19 +920,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
                 }
       }
     }
-    const int st = blk * nkc + nkc - 1;
-    if (st + 2 < nstages) {
-      load_stage(g, st + 2);
-      wrec_load<WQ>(wr, p, nkb, r0, (st + 2) % nkc);
-    }
+    advance(blk * nkc + nkc - 1);
     // the value accumulators cross the back edge in the accumulation
-    // registers (else the compiler carries a vector-register copy of all
-    // of them and moves it on every trip)
+    // registers (else the compiler carries a vector-register copy of all of
+    // them and moves it on every trip)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int ob = 0; ob < NOBW; ++ob) asm volatile("" : "+a"(O[rt][ob]));
-    __syncthreads();
   }
 
   // Row sums: the two column halves' partials (both halves of each wave).
@@ -1221,7 +1239,7 @@ PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, in
     if (max_splits > 64) max_splits = 64;
     int64_t cps = 0;
     const int64_t units = (int64_t)pl.row_blocks * (nchunks > 0 ? nchunks : 1);
-    pl.splits = (int)round_filling_splits(units, nc, tile8 ? PvGeo::kCols : (wide ? PvwGeo::kCols : kGCols),
+    pl.splits = (int)round_filling_splits(units, nc, tile8 ? PvGeo::kCols : (wide ? kPvwCols : kGCols),
                                           max_splits, tile8 ? pv_gemm8_resident() : pv_gemm_resident(nob), cps);
     pl.cols_per_split = (int)cps;
     return pl;
