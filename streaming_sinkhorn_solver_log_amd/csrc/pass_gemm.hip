@@ -141,15 +141,24 @@ __global__ __launch_bounds__((Geo<WRT, WCT, WGR>::kNT), (Geo<WRT, WCT, WGR>::kOc
   const int half = lane >> 5;
   const int li = lane & 31;
   // Workgroups are dispatched to the 8 XCDs round robin; the virtual index v
-  // gives each XCD a contiguous range, numbered split-major, so the
-  // workgroups of one XCD sweep the same columns.
+  // gives each XCD a contiguous range, in groups of kGroupRows row blocks:
+  // within a group, v runs over the row blocks, then the splits. The
+  // workgroups an XCD runs together thus cover a few row blocks times several
+  // column splits, and its L2 serves both operands' re-reads (numbered
+  // split-major, every resident workgroup had rows of its own, which the L2
+  // could not hold).
+  constexpr int kGroupRows = 4;
   int sp, rblk;
   {
     const int nwg = p.row_blocks * p.splits;
     const int h = blockIdx.x, xcd = h & 7, q = nwg >> 3, rem = nwg & 7;
     const int v = xcd * q + min(xcd, rem) + (h >> 3);
-    sp = v / p.row_blocks;
-    rblk = v - sp * p.row_blocks;
+    const int gsz = kGroupRows * p.splits;
+    const int grp = v / gsz;
+    const int gr = min(kGroupRows, p.row_blocks - grp * kGroupRows);  // row blocks in this group
+    const int off = v - grp * gsz;
+    sp = off / gr;
+    rblk = grp * kGroupRows + (off - sp * gr);
   }
   const int j0 = sp * p.cols_per_split;
   const int j1 = min(p.nc, j0 + p.cols_per_split);
