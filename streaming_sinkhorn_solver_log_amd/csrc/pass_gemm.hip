@@ -258,15 +258,8 @@ __global__ __launch_bounds__((Geo<WRT, WCT, WGR>::kNT), (Geo<WRT, WCT, WGR>::kOc
     for (int u = 0; u < kRowsPerThread; ++u) {
       const int r = threadIdx.x + u * kNT, i = row0 + r;
       if (r < G::kRows && i < p.nr) {
-        float Mt = -INFINITY;
-        for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
-        const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
-        float St = 0.0f;
-        for (int s2 = 0; s2 < p.splits; ++s2) {
-          const float Mp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].x);
-          const float Sp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].y);
-          St = fmaf(Sp, fast_exp2(Mp - Me), St);
-        }
+        float Mt, St;
+        merge_partials(p.part + i, p.nr, p.splits, Mt, St);
         Lr[u] = Mt + fast_log2(St);
         bad |= SHIFTED && !(St >= kShiftedFloor);
       }

@@ -487,15 +487,8 @@ __global__ __launch_bounds__(kThreads, (kMinWaves<NKB, MERGED>)) void k_lse_mfma
       RowIn rin{};
       if (mine) {
         rin = load_row_in(p, i);
-        float Mt = -INFINITY;
-        for (int s2 = 0; s2 < contributors; ++s2) Mt = fmaxf(Mt, load_coherent(&p.part[(int64_t)s2 * p.nr + i].x));
-        const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
-        float St = 0.0f;
-        for (int s2 = 0; s2 < contributors; ++s2) {
-          const float Mp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].x);
-          const float Sp = load_coherent(&p.part[(int64_t)s2 * p.nr + i].y);
-          St = fmaf(Sp, fast_exp2(Mp - Me), St);
-        }
+        float Mt, St;
+        merge_partials(p.part + i, p.nr, contributors, Mt, St);
         Lr = Mt + fast_log2(St);
         bad = SHIFTED && !(St >= kShiftedFloor);
       }

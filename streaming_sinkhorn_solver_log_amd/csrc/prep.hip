@@ -159,26 +159,40 @@ __global__ __launch_bounds__(256) void k_bf16_shift_init(int* mm, int d) {
 }
 
 // mm[k] = ord(min), mm[d + k] = ord(max) of coordinate k over both clouds:
-// each workgroup reduces a contiguous range of rows, each thread a fixed set
-// of coordinates (coalesced along the rows), then one atomic per coordinate.
+// each workgroup reduces a contiguous range of rows (each thread a fixed
+// coordinate of every rstep-th row, coalesced along the rows), combines its
+// threads through LDS, then one atomic per coordinate and workgroup.
 __global__ __launch_bounds__(256) void k_bf16_shift_partial(const unsigned short* x, int64_t n,
                                                              const unsigned short* y, int64_t m, int d,
                                                              int rows_per_block, int* mm) {
+  __shared__ float slo[256], shi[256];
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
   const int kt = d < 256 ? d : 256;  // coordinates per row sweep
   const int rstep = 256 / kt;        // rows per sweep
   const int k0 = threadIdx.x % kt, rr = threadIdx.x / kt;
-  if (rr >= rstep) return;
-  for (int k = k0; k < d; k += kt) {
+  for (int kb = 0; kb < d; kb += kt) {
+    const int k = kb + k0;
     float lo = INFINITY, hi = -INFINITY;
-    for (int64_t r = r0 + rr; r < r0 + rows_per_block && r < n + m; r += rstep) {
-      const unsigned short bits = r < n ? x[r * d + k] : y[(r - n) * d + k];
-      const float v = __uint_as_float((unsigned)bits << 16);
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
+    if (rr < rstep && k < d) {
+      for (int64_t r = r0 + rr; r < r0 + rows_per_block && r < n + m; r += rstep) {
+        const unsigned short bits = r < n ? x[r * d + k] : y[(r - n) * d + k];
+        const float v = __uint_as_float((unsigned)bits << 16);
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
     }
-    atomicMin(&mm[k], float_ord(lo));
-    atomicMax(&mm[d + k], float_ord(hi));
+    slo[threadIdx.x] = lo;
+    shi[threadIdx.x] = hi;
+    __syncthreads();
+    if (rr == 0 && k < d) {
+      for (int q = 1; q < rstep; ++q) {
+        lo = fminf(lo, slo[q * kt + k0]);
+        hi = fmaxf(hi, shi[q * kt + k0]);
+      }
+      atomicMin(&mm[k], float_ord(lo));
+      atomicMax(&mm[d + k], float_ord(hi));
+    }
+    __syncthreads();
   }
 }
 
@@ -203,8 +217,10 @@ __global__ __launch_bounds__(256) void k_bf16_shift_final(const int* mm, int d, 
 hipError_t launch_bf16_shift(const void* x, int64_t n, const void* y, int64_t m, int d, double* part, float* shift,
                              hipStream_t s) {
   int* mm = reinterpret_cast<int*>(part);  // 2 d ints of the centroid scratch
-  const int rows = 64;
-  const int64_t blocks = (n + m + rows - 1) / rows;
+  // about 512 workgroups: few atomics per coordinate, the whole GPU busy
+  const int64_t total = n + m;
+  const int rows = (int)(total / 512 > 64 ? (total + 511) / 512 : 64);
+  const int64_t blocks = (total + rows - 1) / rows;
   k_bf16_shift_init<<<1, 256, 0, s>>>(mm, d);
   k_bf16_shift_partial<<<(int)blocks, 256, 0, s>>>(static_cast<const unsigned short*>(x), n,
                                                     static_cast<const unsigned short*>(y), m, d, rows, mm);

@@ -13,6 +13,45 @@ namespace dev {
 constexpr float kMaskedBias = -1.0e30f;  // bias of a column that contributes nothing
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 64-bit coherent load of a split partial (M, S) (both words written with
+// store_coherent before their writer counted itself in).
+__device__ __forceinline__ float2 load_coherent2(const float2* p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(float2, v);
+}
+
+// A row's split partials (M_s, S_s) at part[s * stride], s = 0 .. count - 1,
+// combined in split order: M = max_s M_s and S = sum_s S_s 2^(M_s - M') with
+// M' = M (0 when every M_s is -inf). The loads go out eight at a time, so the
+// merge waits for about one memory round trip per eight partials instead of
+// one per partial (up to eight partials are loaded once).
+__device__ inline void merge_partials(const float2* part, int64_t stride, int count, float& M, float& S) {
+  constexpr int kB = 8;
+  float2 v[kB];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      v[u] = s0 + u < count ? load_coherent2(part + (int64_t)(s0 + u) * stride) : make_float2(-INFINITY, 0.0f);
+  };
+  float Mt = -INFINITY;
+  for (int s0 = 0; s0 < count; s0 += kB) {
+    load_batch(s0);
+#pragma unroll
+    for (int u = 0; u < kB; ++u) Mt = fmaxf(Mt, v[u].x);
+  }
+  const float Me = (Mt == -INFINITY) ? 0.0f : Mt;
+  float St = 0.0f;
+  for (int s0 = 0; s0 < count; s0 += kB) {
+    if (count > kB) load_batch(s0);  // else the batch is still in registers
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (s0 + u < count) St = fmaf(v[u].y, fast_exp2(v[u].x - Me), St);
+  }
+  M = Mt;
+  S = St;
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Three-part bf16 split of v (v ~= hi + mid + lo to float32 precision).
