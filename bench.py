@@ -433,6 +433,81 @@ def measure_tol(case, tol, check_every=10, max_iters=20000, eps_start=0.0):
             "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "eps": w.eps, "mode": w.mode}}
 
 
+def io_model(w, tile):
+    """Algorithmic operand bytes a GEMM-tiled half-pass moves into the CUs
+    with an R x C workgroup tile: every (row block, column block) pair reads
+    both blocks' records once, n m s (1/C + 1/R) bytes for s bytes a record
+    (IO bound of the pass: review, Summary, Theorem 2's n m d^2 / M term, M
+    ~ R + C records staged)."""
+    R, C = tile
+    s = (w.d if w.dtype == "bf16" else 6 * w.d) * 2  # bf16 slots of a record
+    s = -(-s // 128) * 128                           # whole 128-byte K chunks
+    return w.n * w.m * s * (1.0 / C + 1.0 / R)
+
+
+GEMM_TILES = {"256x256": (256, 256), "128x128": (128, 128), "128x256": (128, 256)}
+
+
+def measure_io_tile(case, reps=5):
+    """Shifted half-pass time at the tile FLASHSK_GEMM_TILE selects (large-d workloads)."""
+    sk, w, torch = case.sk, case.w, case.torch
+    tile = os.environ.get("FLASHSK_GEMM_TILE", "256x256")
+    if tile not in GEMM_TILES:
+        raise SystemExit(f"FLASHSK_GEMM_TILE={tile}: not one of {sorted(GEMM_TILES)}")
+
+    def run(iters):
+        out = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            sk.solve(case.x, case.y, case.a, case.b, w.eps, iters, "alternating", workspace=case.ws)
+            e.record()
+            e.synchronize()
+            out.append(s.elapsed_time(e))
+        return statistics.median(out)
+
+    run(2)
+    ms = (run(11) - run(1)) / 20.0
+    model = io_model(w, GEMM_TILES[tile])
+    return {"metric": "shifted half-pass time", "value": ms, "unit": "ms", "higher_is_better": False,
+            "tile": tile, "model_operand_bytes": model, "model_operand_TBps": model / (ms * 1e-3) / 1e12,
+            "config": {"workload": w.name, "n": w.n, "m": w.m, "d": w.d, "dtype": w.dtype}}
+
+
+def summarize_io(pairs):
+    """Markdown table of the re-read study from TILE=TIMING_JSON:FETCH_DIR:REQ_DIR triples."""
+    print("| tile | half-pass ms | model operand MB (n m s (1/R + 1/C)) | L2 requests (TCC_REQ) x 128 B, MB "
+          "| L2 hit rate | FETCH_SIZE MB (x copy scale) |")
+    print("|---|---|---|---|---|---|")
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            fscale = json.load(fh)["fetch_scale"]
+    except (OSError, ValueError, KeyError):
+        fscale = 1.0
+    for item in pairs:
+        tile, rest = item.split("=", 1)
+        tfile, fdir, rdir = rest.split(":")
+        with open(tfile) as fh:
+            t = json.loads(fh.read().strip().splitlines()[-1])
+        fetch, _ = _pmc_means(fdir)
+        req, _ = _pmc_means(rdir)
+        stem = "k_lse_gemm<true"
+        kf = next(v for k, v in fetch.items() if stem in k)
+        # TCC_REQ and TCC_HIT arrive as separate counter rows: take both by name
+        import csv
+        import glob
+        vals = {}
+        for f in glob.glob(os.path.join(rdir, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if stem in r["Kernel_Name"]:
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        reqs = sum(vals["TCC_REQ_sum"]) / len(vals["TCC_REQ_sum"])
+        hits = sum(vals["TCC_HIT_sum"]) / len(vals["TCC_HIT_sum"])
+        print(f"| {tile} | {t['value']:.3f} | {t['model_operand_bytes'] / 1e6:.0f} | {reqs * 128 / 1e6:.0f} | "
+              f"{hits / reqs:.2f} | {kf * fscale * 1.024e-3:.0f} |")
+
+
 def measure_low_eps(case, eps_list=(1e-2, 3e-3, 1e-3, 3e-4), tols=(1e-3, 1e-4, 1e-5), eps_start=1.0,
                     check_every=10, max_iters=20000):
     """Iterations and time to a marginal tolerance on the workload's points at
@@ -668,9 +743,18 @@ def main():
                     help="only run a 1 GiB device-to-device copy (scale for the HBM counters)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/hbm_traffic.json from four rocprofv3 --pmc output folders")
+    ap.add_argument("--io-study", action="store_true",
+                    help="time the shifted GEMM-tiled half-pass at the tile FLASHSK_GEMM_TILE selects "
+                         "(256x256, 128x128, 128x256) and print it with the re-read model")
+    ap.add_argument("--summarize-io", nargs="+", metavar="TILE=TIMING:FETCH_DIR:REQ_DIR",
+                    help="print the re-read study table from timing JSON files and rocprofv3 --pmc folders "
+                         "(FETCH_SIZE; TCC_REQ_sum TCC_HIT_sum)")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_io:
+        summarize_io(args.summarize_io)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -698,6 +782,9 @@ def main():
     key = WORKLOADS[args.workload]
     print(f"[bench] workload {args.workload}: building inputs", file=sys.stderr, flush=True)
     case = Case(key, torch, sk, dev)
+    if args.io_study:
+        print(json.dumps(measure_io_tile(case)), flush=True)
+        return
     if args.divergence:
         print(json.dumps(measure_divergence(case, args.steps, args.warmup)), flush=True)
         return

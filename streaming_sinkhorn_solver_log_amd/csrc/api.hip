@@ -175,7 +175,6 @@ struct SolvePlan {
   Path path;
   int nkb;      // matrix-core records: K blocks per record
   bool merged;  // register-resident pass with the bias chunk inside the column records
-  bool wide;    // GEMM-tiled pass over float32 (six-part) records
   bool fused;   // averaged schedule, register-resident pass: F and G in one launch
   PassPlan f, g;
 };
@@ -188,7 +187,6 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
   sp.path = solve_path(dtype, d);
   sp.nkb = 0;
   sp.merged = false;
-  sp.wide = false;
   sp.fused = false;
   if (sp.path == Path::Mfma) {
     sp.nkb = mfma_nkb(dtype, (int)d);
@@ -201,9 +199,8 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
     sp.g = plan_mfma_pass(m, n, sp.nkb, sp.merged, dtype == SK_BF16, share);
   } else if (sp.path == Path::Gemm) {
     sp.nkb = gemm_nkb(dtype, (int)d);
-    sp.wide = dtype == SK_F32;
-    sp.f = plan_gemm_pass(n, m, sp.wide);
-    sp.g = plan_gemm_pass(m, n, sp.wide);
+    sp.f = plan_gemm_pass(n, m);
+    sp.g = plan_gemm_pass(m, n);
   }
   return sp;
 }
@@ -357,7 +354,7 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
 
 hipError_t launch_pass(const SolvePlan& sp, const MfmaPassArgs& a, bool shifted, bool scaled,
                        const PassPlan& pl, hipStream_t s) {
-  if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, sp.wide, pl, s);
+  if (sp.path == Path::Gemm) return launch_lse_gemm(a, sp.nkb, shifted, scaled, pl, s);
   return launch_lse_mfma(a, sp.nkb, shifted, scaled, sp.merged, pl, s);
 }
 

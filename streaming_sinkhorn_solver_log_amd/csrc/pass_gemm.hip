@@ -25,6 +25,8 @@
 #include <atomic>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 namespace sk {
 namespace {
@@ -305,14 +307,13 @@ __global__ __launch_bounds__((Geo<WRT, WCT, WGR>::kNT), (Geo<WRT, WCT, WGR>::kOc
 // float32 records, whose long K loop favours fewer operand reads per MFMA
 // (0.75 instead of 1 LDS fragment per MFMA; measured 3.4-3.7 ms against
 // 4.2 ms at d = 512).
-#ifndef SK_GEMM_NARROW
-#define SK_GEMM_NARROW 2, 4, 4
-#endif
-#ifndef SK_GEMM_WIDE
-#define SK_GEMM_WIDE 2, 4, 4
-#endif
-using NarrowGeo = Geo<SK_GEMM_NARROW>;
-using WideGeo = Geo<SK_GEMM_WIDE>;
+// Workgroup tiles: 256 x 256 with eight waves (the default), and two smaller
+// ones for the re-read study of the pass (the operand re-read traffic scales
+// with 1/R + 1/C) and for tests: 128 x 128 (four waves, two workgroups per
+// CU) and 128 x 256 (four waves).
+using Tile256 = Geo<2, 4, 4>;
+using Tile128 = Geo<2, 2, 2>;
+using Tile128x256 = Geo<2, 4, 2>;
 
 template <class G, bool SHIFTED, bool SCALED>
 void launch_geo(const MfmaPassArgs& a, int nkb, int col_last, dim3 grid, hipStream_t s) {
@@ -347,25 +348,28 @@ int64_t round_filling_splits(int64_t units, int64_t nc, int64_t unit_cols, int64
 }
 
 namespace {
-int gemm_resident(bool wide) {
-  // Per device and tile shape, computed once; concurrent first calls compute
-  // the same value.
+template <class G>
+int occupancy_of() {
+  int per_cu = 0;
+  // the instantiations of one tile share the LDS footprint that binds occupancy
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, k_lse_gemm<true, true, G::kWRT, G::kWCT, G::kWGR>, G::kNT, 0);
+  return (e != hipSuccess || per_cu < 1) ? 1 : per_cu;
+}
+
+int gemm_resident(int tile) {
+  // Per device and tile, computed once; concurrent first calls compute the
+  // same value.
   constexpr int kDevices = 16;
-  static std::atomic<int> cached[kDevices][2];
+  static std::atomic<int> cached[kDevices][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev][wide ? 1 : 0] : nullptr;
+  std::atomic<int>* slot = (dev >= 0 && dev < kDevices) ? &cached[dev][tile] : nullptr;
   int v = slot ? slot->load(std::memory_order_relaxed) : 0;
   if (v == 0) {
-    int cus = 0, per_cu = 0;
-    // the instantiations of one shape share the LDS footprint that binds occupancy
-    const hipError_t e =
-        wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &per_cu, k_lse_gemm<true, false, WideGeo::kWRT, WideGeo::kWCT, WideGeo::kWGR>, WideGeo::kNT, 0)
-             : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                   &per_cu, k_lse_gemm<true, true, NarrowGeo::kWRT, NarrowGeo::kWCT, NarrowGeo::kWGR>,
-                   NarrowGeo::kNT, 0);
-    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    const int per_cu = tile == 1 ? occupancy_of<Tile128>() : (tile == 2 ? occupancy_of<Tile128x256>()
+                                                                         : occupancy_of<Tile256>());
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
     v = per_cu * cus;
@@ -375,16 +379,24 @@ int gemm_resident(bool wide) {
 }
 }  // namespace
 
-PassPlan plan_gemm_pass(int64_t nr, int64_t nc, bool wide) {
+int gemm_tile_choice() {
+  const char* v = getenv("FLASHSK_GEMM_TILE");
+  if (v && !strcmp(v, "128x128")) return 1;
+  if (v && !strcmp(v, "128x256")) return 2;
+  return 0;
+}
+
+PassPlan plan_gemm_pass(int64_t nr, int64_t nc) {
   PassPlan pl{};
-  const int rows = wide ? WideGeo::kRows : NarrowGeo::kRows;
-  const int cols = wide ? WideGeo::kCols : NarrowGeo::kCols;
+  pl.tile = gemm_tile_choice();
+  const int rows = pl.tile == 0 ? Tile256::kRows : (pl.tile == 1 ? Tile128::kRows : Tile128x256::kRows);
+  const int cols = pl.tile == 0 ? Tile256::kCols : (pl.tile == 1 ? Tile128::kCols : Tile128x256::kCols);
   pl.rows_per_block = rows;
   pl.row_blocks = (int)((nr + rows - 1) / rows);
   int64_t max_splits = nc / 512 > 1 ? nc / 512 : 1;
   if (max_splits > 64) max_splits = 64;
   int64_t cps = 0;
-  pl.splits = (int)round_filling_splits(pl.row_blocks, nc, cols, max_splits, gemm_resident(wide), cps);
+  pl.splits = (int)round_filling_splits(pl.row_blocks, nc, cols, max_splits, gemm_resident(pl.tile), cps);
   pl.cols_per_split = (int)cps;
   return pl;
 }
@@ -395,30 +407,29 @@ int gemm_nkb(int dtype, int d) {
   return (nkb + kGKb - 1) / kGKb * kGKb;  // whole K chunks
 }
 
-hipError_t launch_lse_gemm(const MfmaPassArgs& args, int nkb, bool shifted, bool scaled, bool wide,
-                           const PassPlan& pl, hipStream_t s) {
+namespace {
+template <class G>
+void launch_tile(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, int col_last, dim3 grid, hipStream_t s) {
+  if (shifted) {
+    if (scaled) launch_geo<G, true, true>(a, nkb, col_last, grid, s);
+    else launch_geo<G, true, false>(a, nkb, col_last, grid, s);
+  } else {
+    if (scaled) launch_geo<G, false, true>(a, nkb, col_last, grid, s);
+    else launch_geo<G, false, false>(a, nkb, col_last, grid, s);
+  }
+}
+}  // namespace
+
+hipError_t launch_lse_gemm(const MfmaPassArgs& args, int nkb, bool shifted, bool scaled, const PassPlan& pl,
+                           hipStream_t s) {
   MfmaPassArgs a = args;
   a.row_blocks = pl.row_blocks;
   a.splits = pl.splits;
   const dim3 grid((unsigned)(pl.row_blocks * pl.splits));
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
-  if (wide) {
-    if (shifted) {
-      if (scaled) launch_geo<WideGeo, true, true>(a, nkb, col_last, grid, s);
-      else launch_geo<WideGeo, true, false>(a, nkb, col_last, grid, s);
-    } else {
-      if (scaled) launch_geo<WideGeo, false, true>(a, nkb, col_last, grid, s);
-      else launch_geo<WideGeo, false, false>(a, nkb, col_last, grid, s);
-    }
-  } else {
-    if (shifted) {
-      if (scaled) launch_geo<NarrowGeo, true, true>(a, nkb, col_last, grid, s);
-      else launch_geo<NarrowGeo, true, false>(a, nkb, col_last, grid, s);
-    } else {
-      if (scaled) launch_geo<NarrowGeo, false, true>(a, nkb, col_last, grid, s);
-      else launch_geo<NarrowGeo, false, false>(a, nkb, col_last, grid, s);
-    }
-  }
+  if (pl.tile == 1) launch_tile<Tile128>(a, nkb, shifted, scaled, col_last, grid, s);
+  else if (pl.tile == 2) launch_tile<Tile128x256>(a, nkb, shifted, scaled, col_last, grid, s);
+  else launch_tile<Tile256>(a, nkb, shifted, scaled, col_last, grid, s);
   return hipGetLastError();
 }
 

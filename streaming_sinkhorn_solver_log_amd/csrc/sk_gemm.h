@@ -12,11 +12,14 @@ namespace sk {
 int64_t round_filling_splits(int64_t units, int64_t nc, int64_t unit_cols, int64_t max_splits,
                              int64_t resident, int64_t& cols_per_split);
 // GEMM-tiled half-pass for wide records (any NKB that is a multiple of 4).
-// wide: the 128 x 256 workgroup tile (float32 records), else 128 x 128.
+// The workgroup tile is 256 x 256 unless the environment variable
+// FLASHSK_GEMM_TILE names 128x128 or 128x256 (read at each plan; the plan
+// records it in PassPlan::tile, which the launch follows).
 int gemm_nkb(int dtype, int d);
-PassPlan plan_gemm_pass(int64_t nr, int64_t nc, bool wide);
-hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, bool wide,
-                           const PassPlan& pl, hipStream_t s);
+int gemm_tile_choice();
+PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
+hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, const PassPlan& pl,
+                           hipStream_t s);
 // Transport application / gradient kernels. pv_parts: bf16 parts of the plan
 // entries (pp) and of the values (vp) for a storage type and operation.
 void pv_parts(int dtype, bool grad, int& pp, int& vp);

@@ -21,6 +21,7 @@ struct PassPlan {
   int grid;            // balanced plan: workgroups (one resident wave of them)
   int stages;          // balanced plan: 128-column stages per row block
   int chunks;          // balanced plan: column chunks, each swept by the workgroups of 8 / chunks XCDs
+  int tile;            // GEMM-tiled half-pass: workgroup tile (0: 256 x 256, 1: 128 x 128, 2: 128 x 256)
 };
 
 hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, int dtype, int d,

@@ -133,6 +133,34 @@ def test_forced_exact_fallback(sk, key, n, m, monkeypatch):
     assert not (torch.equal(f, f0) and torch.equal(g, g0)), "the forced recomputation did not run"
 
 
+GEMM_TILE_CASES = [
+    ("128x128", 7, 700, 900),   # bf16 d = 512: more row blocks than the default tile, several splits
+    ("128x256", 7, 333, 1500),
+    ("128x128", 4, 300, 700),   # float32 d = 512
+    ("128x256", 5, 300, 1300),  # bf16 d = 1024, rectangular
+]
+
+
+@pytest.mark.parametrize("tile,key,n,m", GEMM_TILE_CASES)
+def test_gemm_tiles_match_oracle(sk, tile, key, n, m, monkeypatch):
+    """The smaller workgroup tiles of the GEMM-tiled half-pass (kept for the re-read
+    study of the pass) match the oracle like the default one."""
+    w = W.CASES[key].scaled(n, m, 5)
+    say(f"gemm tile {tile} cfg={key} n={n} m={m} d={w.d} {w.dtype}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    monkeypatch.setenv("FLASHSK_GEMM_TILE", tile)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("FLASHSK_GEMM_TILE")
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    ef = np.abs(f.cpu().numpy().astype(np.float64) - fr).max()
+    eg = np.abs(g.cpu().numpy().astype(np.float64) - gr).max()
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} tol={tol_pot(w, fr):.3e}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * abs(cr)
+
+
 CUSTOM_DIMS = [("f32", 16), ("f32", 20), ("f32", 32), ("bf16", 100), ("bf16", 8), ("f32", 7),
                ("f32", 64), ("bf16", 200), ("f32", 130)]
 
