@@ -105,6 +105,13 @@ bool debug_enabled() {
 
 // FLASHSK_FORCE_EXACT=1 (read on every solve): every shifted half-pass
 // recomputes its row blocks exactly, so tests can check that path.
+// The one-launch solve of small problems is on unless FLASHSK_SMALL_SOLVE=0
+// (read at each plan: tests and timings compare it with the streaming passes).
+bool small_enabled() {
+  const char* e = getenv("FLASHSK_SMALL_SOLVE");
+  return !(e && e[0] == '0');
+}
+
 bool force_exact_enabled() {
   const char* e = getenv("FLASHSK_FORCE_EXACT");
   return e && e[0] == '1';
@@ -182,12 +189,18 @@ struct SolvePlan {
 // The merged layout keeps one bias copy per side inside its column records, so
 // it serves the alternating schedule only (the averaged one reads the old
 // biases of both sides while writing the new ones).
-SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternating) {
+SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternating, bool allow_small = true) {
   SolvePlan sp;
   sp.path = solve_path(dtype, d);
   sp.nkb = 0;
   sp.merged = false;
   sp.fused = false;
+  if (allow_small && sp.path != Path::None && small_fits(n, m, d) && small_enabled()) {
+    sp.path = Path::Small;
+    sp.f = PassPlan{};
+    sp.g = PassPlan{};
+    return sp;
+  }
   if (sp.path == Path::Mfma) {
     sp.nkb = mfma_nkb(dtype, (int)d);
     sp.merged = alternating && mfma_merged(dtype, (int)d, sp.nkb);
@@ -208,6 +221,7 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
 struct SolveWs {
   SideM xm, ym;
   Common c;
+  void* tags;  // one-launch solve of small problems: its tagged potentials
   size_t bytes;
 };
 
@@ -221,6 +235,12 @@ int solve_counters(const SolvePlan& sp) {
 SolveWs layout_solve(void* ws, const SolvePlan& sp, int64_t n, int64_t m, int64_t d) {
   Carve c{static_cast<char*>(ws)};
   SolveWs L{};
+  if (sp.path == Path::Small) {  // the tagged potentials and the input screen's flag only
+    L.c = carve_common(c, 1, 1, d);
+    L.tags = c.take<char>(small_ws_bytes(n, m));
+    L.bytes = c.off;
+    return L;
+  }
   L.xm = carve_side_m(c, n, sp.nkb, sp.f.row_blocks);
   L.ym = carve_side_m(c, m, sp.nkb, sp.g.row_blocks);
   L.c = carve_common(c, part_f2(sp.f, n, sp.g, m, sp.fused), solve_counters(sp), d);
@@ -432,6 +452,12 @@ struct SolveState {
   bool sym;
   int t;    // iterations since the prep
   int cur;  // bias buffers the next iteration reads
+  // the one-launch path recomputes everything from the inputs and (f, g)
+  const void* x;
+  const void* y;
+  const float* a;
+  const float* b;
+  double eps;
 };
 
 int solve_begin(SolveState& st, const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
@@ -449,10 +475,22 @@ int solve_begin(SolveState& st, const void* x, const void* y, int dtype, int64_t
   st.sym = mode == SK_SYMMETRIC;
   st.t = 0;
   st.cur = 0;
+  st.x = x;
+  st.y = y;
+  st.a = a;
+  st.b = b;
+  st.eps = eps;
   const bool warm = (flags & SK_WARM_START) != 0;
   if ((flags & SK_CHECK_FINITE) &&
       (rc = screen_inputs(x, y, dtype, n, m, d, a, b, warm ? f : nullptr, warm ? g : nullptr, st.L.c.counters, s)))
     return rc;
+  if (st.sp.path == Path::Small) {
+    hipError_t e = hipSuccess;
+    if (!warm && ((e = launch_zero_u32(reinterpret_cast<unsigned*>(f), n, s)) != hipSuccess ||
+                  (e = launch_zero_u32(reinterpret_cast<unsigned*>(g), m, s)) != hipSuccess))
+      return hip_fail(e, "zero potentials");
+    return SK_OK;
+  }
   const SolveWs& L = st.L;
   MfmaPrepSide px{x, a, warm ? f : nullptr, warm ? nullptr : f, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw,
                   L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
@@ -469,6 +507,13 @@ int solve_begin(SolveState& st, const void* x, const void* y, int dtype, int64_t
 }
 
 int solve_iterate(SolveState& st, int iters, float* f, float* g, hipStream_t s) {
+  if (st.sp.path == Path::Small) {
+    const hipError_t e = launch_small_solve(st.x, st.y, st.dtype, st.n, st.m, st.d, st.a, st.b, st.eps, iters,
+                                            st.sym, f, g, st.L.tags, s);
+    if (e != hipSuccess) return hip_fail(e, "small-problem solve");
+    st.t += iters;
+    return SK_OK;
+  }
   const int rc = solve_mfma(st.L, st.sp, st.dtype, st.n, st.m, st.t, iters, st.cur, st.sym, f, g, st.sc, s);
   st.t += iters;
   return rc;
@@ -479,9 +524,11 @@ int solve_iterate(SolveState& st, int iters, float* f, float* g, hipStream_t s) 
 namespace api {
 
 size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
-  // the schedule is not known here: the larger of the two plans
-  const size_t a = layout_solve(nullptr, plan_solve(dtype, n, m, d, true), n, m, d).bytes;
-  const size_t b = layout_solve(nullptr, plan_solve(dtype, n, m, d, false), n, m, d).bytes;
+  // the schedule is not known here: the larger of the two plans, sized for
+  // the streaming passes also where the one-launch solve would run (so that
+  // the workspace serves either choice)
+  const size_t a = layout_solve(nullptr, plan_solve(dtype, n, m, d, true, false), n, m, d).bytes;
+  const size_t b = layout_solve(nullptr, plan_solve(dtype, n, m, d, false, false), n, m, d).bytes;
   return a > b ? a : b;
 }
 
@@ -614,7 +661,7 @@ int sk_sinkhorn_solve(const void* x, const void* y, int dtype, int64_t n, int64_
   SolveState st;
   if ((rc = solve_begin(st, x, y, dtype, n, m, d, a, b, eps, mode, flags, f, g, ws, ws_bytes, s))) return rc;
   if ((rc = solve_iterate(st, iters, f, g, s))) return rc;
-  if (debug_enabled()) {
+  if (debug_enabled() && st.sp.path != Path::Small) {
     unsigned cnt = 0;
     if (hipMemcpyAsync(&cnt, st.L.c.exact_count, sizeof(cnt), hipMemcpyDeviceToHost, s) == hipSuccess &&
         hipStreamSynchronize(s) == hipSuccess)

@@ -32,7 +32,9 @@ struct Carve {
   }
 };
 
-enum class Path { Mfma, Gemm, None };
+// Small: the whole fixed-budget solve of a small problem in one cooperative
+// launch (solve only; see small.hip).
+enum class Path { Mfma, Gemm, Small, None };
 
 // Thread-local error message (sk_last_error): fail() formats it and returns code.
 void clear_error();

@@ -31,6 +31,15 @@ hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, i
 hipError_t launch_bf16_shift(const void* x, int64_t n, const void* y, int64_t m, int d, double* part, float* shift,
                              hipStream_t s);
 hipError_t launch_zero_u32(unsigned* p, int64_t count, hipStream_t s);
+// Small problems (small.hip): whether the one-launch solve serves n, m, d, its
+// grid, its scratch (tags: small_ws_bytes, 8-byte aligned) and a batch of
+// iterations on it.
+bool small_fits(int64_t n, int64_t m, int64_t d);
+int small_grid(int64_t n, int64_t m);
+size_t small_ws_bytes(int64_t n, int64_t m);
+hipError_t launch_small_solve(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                              const float* a, const float* b, double eps, int iters, bool averaged, float* f,
+                              float* g, void* tags, hipStream_t s);
 hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
                        int64_t m, double* cost, hipStream_t s);
 

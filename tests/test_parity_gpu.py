@@ -133,6 +133,83 @@ def test_forced_exact_fallback(sk, key, n, m, monkeypatch):
     assert not (torch.equal(f, f0) and torch.equal(g, g0)), "the forced recomputation did not run"
 
 
+SMALL_CASES = [
+    # (config key, n, m, iters, mode or None, dtype or None, d or None): shapes the one-launch solve serves
+    (1, 1024, 1024, None, None, None, None),   # the tiny configuration itself
+    (2, 900, 1100, 40, None, None, None),      # symmetric schedule, eps = 0.01
+    (1, 1, 1, 5, None, None, None),
+    (1, 4096, 300, 10, "symmetric", None, None),
+    (1, 333, 4096, 10, None, None, None),
+    (1, 700, 650, 10, None, "bf16", None),
+    (4, 500, 600, 10, None, None, 7),          # d = 7: two float4 per staged point
+    (4, 600, 400, 10, "symmetric", "bf16", 6),
+]
+
+
+def _small_workload(key, n, m, iters, mode, dtype, d):
+    from dataclasses import replace
+    w = W.CASES[key]
+    if d is not None:
+        w = replace(w, d=d, eps=0.5, name=f"{w.name}_d{d}")
+    if dtype is not None:
+        w = replace(w, dtype=dtype, name=w.name + "_" + dtype)
+    if mode is not None:
+        w = replace(w, mode=mode)
+    return w.scaled(n, m, iters)
+
+
+@pytest.mark.parametrize("key,n,m,iters,mode,dtype,d", SMALL_CASES)
+def test_small_solve_matches_oracle_and_streaming(sk, key, n, m, iters, mode, dtype, d, monkeypatch):
+    """The one-launch solve of small problems against the oracle, and against the
+    streaming passes (FLASHSK_SMALL_SOLVE=0) on the same inputs."""
+    w = _small_workload(key, n, m, iters, mode, dtype, d)
+    say(f"small solve cfg={key} n={n} m={m} d={w.d} {w.dtype} iters={w.iters} mode={w.mode} eps={w.eps}")
+    inp = W.make_inputs(w)
+    x, y, a, b = dev(inp)
+    f, g, cost = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    monkeypatch.setenv("FLASHSK_SMALL_SOLVE", "0")
+    fs, gs, cs = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("FLASHSK_SMALL_SOLVE")
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), inp.a, inp.b, w.eps, w.iters, w.mode)
+    f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    ef, eg = np.abs(f64 - fr).max(), np.abs(g64 - gr).max()
+    es = max(np.abs(f64 - fs.cpu().numpy()).max(), np.abs(g64 - gs.cpu().numpy()).max())
+    say(f"  max|df|={ef:.3e} max|dg|={eg:.3e} vs streaming {es:.3e} tol={tol_pot(w, fr):.3e}")
+    assert ef <= tol_pot(w, fr) and eg <= tol_pot(w, gr)
+    assert es <= 2 * tol_pot(w, fr)
+    assert abs(float(cost) - cr) <= tol_rel(w) * max(abs(cr), 1e-30)
+
+
+@pytest.mark.parametrize("mode", ["alternating", "symmetric"])
+def test_small_solve_batches_and_zero_weights(sk, mode):
+    """The one-launch solve continued from its own output in batches is bitwise the
+    solve in one batch (its state is (f, g)); zero weights mask their points; it is
+    swap-symmetric in the averaged schedule and repeatable."""
+    w = W.CASES[1].scaled(800, 900, 12)
+    inp = W.make_inputs(w)
+    a_np, b_np = inp.a.copy(), inp.b.copy()
+    a_np[::7] = 0.0
+    b_np[3::5] = 0.0
+    a_np /= a_np.sum()
+    b_np /= b_np.sum()
+    x, y, _, _ = dev(inp)
+    a, b = torch.from_numpy(a_np).to(DEV), torch.from_numpy(b_np).to(DEV)
+    f, g, c = sk.solve(x, y, a, b, w.eps, 12, mode)
+    f1, g1, _ = sk.solve(x, y, a, b, w.eps, 5, mode)
+    f2, g2, c2 = sk.solve(x, y, a, b, w.eps, 7, mode, f0=f1, g0=g1)
+    assert torch.equal(f, f2) and torch.equal(g, g2) and float(c) == float(c2)
+    fa, ga, _ = sk.solve(x, y, a, b, w.eps, 12, mode)
+    assert torch.equal(f, fa) and torch.equal(g, ga)
+    fr, gr, cr = oracle.solve(inp.x64(), inp.y64(), a_np, b_np, w.eps, 12, mode)
+    assert np.abs(f.cpu().numpy() - fr).max() <= tol_pot(w, fr)
+    assert np.abs(g.cpu().numpy() - gr).max() <= tol_pot(w, gr)
+    assert abs(float(c) - cr) <= 1e-5 * abs(cr)
+    if mode == "symmetric":
+        gs, fs, _ = sk.solve(y, x, b, a, w.eps, 12, mode)
+        assert torch.equal(f, fs) and torch.equal(g, gs)
+
+
 GEMM_TILE_CASES = [
     ("128x128", 7, 700, 900),   # bf16 d = 512: more row blocks than the default tile, several splits
     ("128x256", 7, 333, 1500),
@@ -464,12 +541,15 @@ def test_translation_invariance(sk):
 
 
 @pytest.mark.parametrize("mode", ["alternating", "symmetric"])
-def test_bf16_clouds_far_from_the_origin(sk, mode):
+def test_bf16_clouds_far_from_the_origin(sk, mode, monkeypatch):
     """bf16 points near 200 in every coordinate: the library translates them by
     an exactly representable shift (bf16 differences stay bf16), so the
     |x|^2 + |y|^2 - 2 x.y expansion keeps its accuracy. Solve, gradient and
     application against the oracle on the same stored values; without the
-    shift (center=False) the float32 expansion is visibly worse."""
+    shift (center=False) the float32 expansion is visibly worse. The streaming
+    passes are forced (the one-launch small solve forms direct differences and
+    needs no shift)."""
+    monkeypatch.setenv("FLASHSK_SMALL_SOLVE", "0")
     rng = np.random.default_rng([31, 5])
     n, m, d, eps, iters = 700, 900, 8, 1.0, 10
     xs = W.f32_to_bf16_bits((200.0 + 1.5 * rng.standard_normal((n, d))).astype(np.float32))
