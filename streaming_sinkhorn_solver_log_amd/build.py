@@ -30,9 +30,19 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C-ABI
+# validation layer (device code is built as usual: each -fsanitize= applies to
+# the host pass only). The result, libflashsk_san.so, is loaded by
+# tests/test_sanitized_abi.py with the sanitizer runtime preloaded.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_LIB = os.path.join(PKG, "libflashsk_san.so")
+SAN_OBJ_DIR = os.path.join(PKG, "_build_san")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_OBJ_DIR if sanitize else OBJ_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(SAN_FLAGS if sanitize else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:
@@ -42,18 +52,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(jobs: int = 8) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build_library(jobs: int = 8, sanitize: bool = False) -> str:
+    out = SAN_LIB if sanitize else LIB
+    os.makedirs(SAN_OBJ_DIR if sanitize else OBJ_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+        objs = list(ex.map(lambda src: _compile(src, sanitize), srcs))
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *(SAN_FLAGS if sanitize else []),
+           "-Xarch_host", "-shared-libsan", "-o", tmp, *objs] if sanitize else \
+          [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (preloaded by the sanitized tests)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
 
 
 def build_peaks() -> str:
@@ -69,5 +88,8 @@ def build_peaks() -> str:
 
 
 if __name__ == "__main__":
-    print(build_library())
-    print(build_peaks())
+    if "--sanitize" in sys.argv[1:]:
+        print(build_library(sanitize=True))
+    else:
+        print(build_library())
+        print(build_peaks())

@@ -162,7 +162,8 @@ Common carve_common(Carve& c, size_t part_f2, int n_counters, int64_t d) {
   Common k;
   k.part = c.take<float2>(part_f2);
   k.counters = c.take<unsigned>((n_counters > 0 ? n_counters : 1) + 1);
-  k.exact_count = k.counters + (n_counters > 0 ? n_counters : 1);
+  // (a sizing pass carves from a null base: no pointer arithmetic on it)
+  k.exact_count = k.counters ? k.counters + (n_counters > 0 ? n_counters : 1) : nullptr;
   k.centroid = c.take<double>((size_t)kCentroidBlocks * 2 * d);
   k.shift = c.take<float>(d);
   return k;

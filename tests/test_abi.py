@@ -12,7 +12,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flashsk.h")
-LIB = os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "libflashsk.so")
+# FLASHSK_ABI_LIB: another build of the same library (the host-sanitized one,
+# tests/test_sanitized_abi.py)
+LIB = os.environ.get("FLASHSK_ABI_LIB") or os.path.join(ROOT, "streaming_sinkhorn_solver_log_amd", "libflashsk.so")
 
 
 def _declared():
