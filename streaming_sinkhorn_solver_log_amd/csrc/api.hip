@@ -196,7 +196,7 @@ SolvePlan plan_solve(int dtype, int64_t n, int64_t m, int64_t d, bool alternatin
   sp.nkb = 0;
   sp.merged = false;
   sp.fused = false;
-  if (allow_small && sp.path != Path::None && small_fits(n, m, d) && small_enabled()) {
+  if (allow_small && sp.path != Path::None && small_fits(n, m, d, alternating) && small_enabled()) {
     sp.path = Path::Small;
     sp.f = PassPlan{};
     sp.g = PassPlan{};
@@ -453,6 +453,7 @@ struct SolveState {
   bool sym;
   int t;    // iterations since the prep
   int cur;  // bias buffers the next iteration reads
+  bool cold;  // started from zero potentials (not SK_WARM_START)
   // the one-launch path recomputes everything from the inputs and (f, g)
   const void* x;
   const void* y;
@@ -482,16 +483,11 @@ int solve_begin(SolveState& st, const void* x, const void* y, int dtype, int64_t
   st.b = b;
   st.eps = eps;
   const bool warm = (flags & SK_WARM_START) != 0;
+  st.cold = !warm;
   if ((flags & SK_CHECK_FINITE) &&
       (rc = screen_inputs(x, y, dtype, n, m, d, a, b, warm ? f : nullptr, warm ? g : nullptr, st.L.c.counters, s)))
     return rc;
-  if (st.sp.path == Path::Small) {
-    hipError_t e = hipSuccess;
-    if (!warm && ((e = launch_zero_u32(reinterpret_cast<unsigned*>(f), n, s)) != hipSuccess ||
-                  (e = launch_zero_u32(reinterpret_cast<unsigned*>(g), m, s)) != hipSuccess))
-      return hip_fail(e, "zero potentials");
-    return SK_OK;
-  }
+  if (st.sp.path == Path::Small) return SK_OK;  // a cold start is zeroed by the first launch
   const SolveWs& L = st.L;
   MfmaPrepSide px{x, a, warm ? f : nullptr, warm ? nullptr : f, L.xm.row_rec, L.xm.col_rec, L.xm.alpha, L.xm.lw,
                   L.xm.bias[0], L.xm.bias[1], L.xm.hval[0], n};
@@ -510,7 +506,7 @@ int solve_begin(SolveState& st, const void* x, const void* y, int dtype, int64_t
 int solve_iterate(SolveState& st, int iters, float* f, float* g, hipStream_t s) {
   if (st.sp.path == Path::Small) {
     const hipError_t e = launch_small_solve(st.x, st.y, st.dtype, st.n, st.m, st.d, st.a, st.b, st.eps, iters,
-                                            st.sym, f, g, st.L.tags, s);
+                                            st.sym, f, g, st.cold && st.t == 0, st.L.tags, s);
     if (e != hipSuccess) return hip_fail(e, "small-problem solve");
     st.t += iters;
     return SK_OK;
@@ -688,6 +684,11 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
     return fail(SK_ERR_UNSUPPORTED, "k=%lld > %lld is not supported", (long long)k, (long long)kMaxValueCols);
   const AuxPlan ap = plan_aux(dtype, n, m, d, k, false, transpose);
   if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
+  if (small_aux_fits(n, m, d, k) && small_enabled()) {
+    const hipError_t e = launch_small_aux(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, false, V, k, out,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SK_OK : hip_fail(e, "small-problem transport application");
+  }
   const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
   return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, transpose, V, false, out, scalars(eps),
                    static_cast<hipStream_t>(stream));
@@ -702,6 +703,11 @@ int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m,
   if (!g || !grad_x) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
   const AuxPlan ap = plan_aux(dtype, n, m, d, d, true, 0);
   if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
+  if (small_aux_fits(n, m, d, d) && small_enabled()) {
+    const hipError_t e = launch_small_aux(x, y, dtype, n, m, d, a, b, nullptr, g, eps, 0, true, nullptr, 0, grad_x,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SK_OK : hip_fail(e, "small-problem gradient");
+  }
   const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
   return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, nullptr, g, true, 0, y, dtype == SK_BF16, grad_x,
                    scalars(eps), static_cast<hipStream_t>(stream));

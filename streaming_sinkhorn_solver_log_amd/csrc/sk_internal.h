@@ -33,13 +33,19 @@ hipError_t launch_bf16_shift(const void* x, int64_t n, const void* y, int64_t m,
 hipError_t launch_zero_u32(unsigned* p, int64_t count, hipStream_t s);
 // Small problems (small.hip): whether the one-launch solve serves n, m, d, its
 // grid, its scratch (tags: small_ws_bytes, 8-byte aligned) and a batch of
-// iterations on it.
-bool small_fits(int64_t n, int64_t m, int64_t d);
+// iterations on it (cold: from zero potentials, which it writes when iters = 0).
+bool small_fits(int64_t n, int64_t m, int64_t d, bool alternating);
 int small_grid(int64_t n, int64_t m);
 size_t small_ws_bytes(int64_t n, int64_t m);
 hipError_t launch_small_solve(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                               const float* a, const float* b, double eps, int iters, bool averaged, float* f,
-                              float* g, void* tags, hipStream_t s);
+                              float* g, bool cold, void* tags, hipStream_t s);
+// Small problems' transport applications (V: m x k, or n x k transposed) and
+// barycentric gradient (grad: V, k, f unused) in one launch, no workspace.
+bool small_aux_fits(int64_t n, int64_t m, int64_t d, int64_t k);
+hipError_t launch_small_aux(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
+                            const float* a, const float* b, const float* f, const float* g, double eps,
+                            int transpose, bool grad, const float* V, int64_t k, float* out, hipStream_t s);
 hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
                        int64_t m, double* cost, hipStream_t s);
 

@@ -138,6 +138,8 @@ SMALL_CASES = [
     (1, 1024, 1024, None, None, None, None),   # the tiny configuration itself
     (2, 900, 1100, 40, None, None, None),      # symmetric schedule, eps = 0.01
     (1, 1, 1, 5, None, None, None),
+    (1, 2048, 2000, 5, None, None, None),      # alternating at its pair limit: points staged per half-pass
+    (1, 1448, 1448, 6, "symmetric", None, None),  # averaged at its pair limit: both sides resident
     (1, 4096, 300, 10, "symmetric", None, None),
     (1, 333, 4096, 10, None, None, None),
     (1, 700, 650, 10, None, "bf16", None),
@@ -695,6 +697,66 @@ def test_apply_arbitrary_potentials(sk, key, scale):
     eg = np.abs(gr - refg).max() / np.abs(refg).max()
     say(f"  grad rel err {eg:.3e}")
     assert eg <= tol_rel(w)
+
+
+SMALL_AUX_CASES = [
+    # (config key, n, m, k, dtype or None, d or None, potentials): shapes the one-launch
+    # gradient and applications serve; "solve" = a 10-iteration solve's pair,
+    # "random" = potentials spread over orders of magnitude
+    (1, 1024, 1024, 16, None, None, "solve"),   # the tiny configuration, k = 16
+    (1, 1, 40, 3, None, None, "solve"),
+    (1, 333, 4096, 5, None, None, "solve"),     # eight column chunks (P V), ragged rows
+    (1, 2048, 2000, 13, None, None, "solve"),   # at the pair limit; k padded to 16
+    (1, 700, 650, 8, "bf16", None, "solve"),
+    (4, 500, 600, 1, None, 7, "solve"),         # d = 7: two float4 per staged point
+    (4, 600, 400, 12, "bf16", 6, "solve"),
+    (1, 700, 900, 16, None, None, "random"),
+]
+
+
+@pytest.mark.parametrize("key,n,m,k,dtype,d,pots", SMALL_AUX_CASES)
+def test_small_aux_matches_oracle_and_streaming(sk, key, n, m, k, dtype, d, pots, monkeypatch):
+    """The one-launch gradient and transport applications of small problems
+    against the oracle, and against the streaming kernels (FLASHSK_SMALL_SOLVE=0)
+    on the same inputs and potentials."""
+    w = _small_workload(key, n, m, 10, None, dtype, d)
+    say(f"small aux cfg={key} n={n} m={m} d={w.d} {w.dtype} k={k} potentials={pots}")
+    inp = W.make_inputs(w, k=k)
+    x, y, a, b = dev(inp)
+    if pots == "solve":
+        f, g, _ = sk.solve(x, y, a, b, w.eps, w.iters, w.mode)
+    else:
+        fs, gs = W.random_potentials(w.n, w.m, 0.5, seed=11)
+        f, g = torch.from_numpy(fs).to(DEV), torch.from_numpy(gs).to(DEV)
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+
+    def run():
+        return (sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy(),
+                sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy(),
+                sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy())
+
+    small = run()
+    monkeypatch.setenv("FLASHSK_SMALL_SOLVE", "0")
+    stream = run()
+    torch.cuda.synchronize()
+    monkeypatch.delenv("FLASHSK_SMALL_SOLVE")
+    f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    refs = (oracle.grad_x(inp.x64(), inp.y64(), inp.a, inp.b, g64, w.eps),
+            oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.V),
+            oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.U, transpose=True))
+    for name, sm, st, ref in zip(("grad", "P.V", "P^T.U"), small, stream, refs):
+        if pots == "random" and name != "grad":
+            # row-wise relative error: each row has its own scale here
+            den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+            es = (np.abs(sm - ref).max(axis=1) / den).max()
+            et = (np.abs(sm - st).max(axis=1) / den).max()
+            tol = 1e-3 if w.dtype == "bf16" else 1e-4
+        else:
+            den = np.abs(ref).max()
+            es, et = np.abs(sm - ref).max() / den, np.abs(sm - st).max() / den
+            tol = tol_rel(w)
+        say(f"  {name}: rel err {es:.3e} vs streaming {et:.3e} (tol {tol:.0e})")
+        assert es <= tol and et <= 2 * tol
 
 
 def _check_last_iteration(sk, w, inp, x, y, a, b, T, mode, rows, cols, tag):
