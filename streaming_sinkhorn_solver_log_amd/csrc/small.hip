@@ -471,6 +471,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_aux(const void* rows, c
     if (ch > 0) __syncthreads();  // the previous chunk is read before it is replaced
     stage(c0, nchunks == 1);
     __syncthreads();
+#pragma unroll 4
     for (int64_t j = lane; j < cnt; j += kGroup) mx = fmaxf(mx, score2<DQ>(pts, j, p, k));
   }
   const float M = wave_max(mx);
@@ -486,6 +487,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_small_aux(const void* rows, c
       stage(c0, true);
       __syncthreads();
     }
+#pragma unroll 4
     for (int64_t j = lane; j < cnt; j += kGroup) {
       const float t = score2<DQ>(pts, j, p, k);
       const float e = t > -INFINITY ? __builtin_amdgcn_exp2f(t - M) : 0.0f;
