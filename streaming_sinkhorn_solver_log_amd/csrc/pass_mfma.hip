@@ -537,6 +537,22 @@ __global__ __launch_bounds__(256) void k_pack_records(const void* pts, int dtype
     const int64_t r = c / chunks;
     const int q = (int)(c % chunks);
     bf16x8 rv = {}, cv = {};
+    if (dtype == 1 && (d & 7) == 0 && q * 8 < d) {
+      // eight whole coordinates: one 16-byte load (rows are 16-byte aligned)
+      const bf16x8 v = reinterpret_cast<const bf16x8*>(static_cast<const unsigned short*>(pts) + r * d)[q];
+      if (shift) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          rv[e] = (__bf16)((float)v[e] - shift[q * 8 + e]);  // exact (prep.hip)
+      } else {
+        rv = v;
+      }
+      cv = rv;
+      const int64_t at = interleave ? r * chunks + (q % nkb) * 2 + q / nkb : c;
+      row_rec[at] = rv;
+      col_rec[at] = cv;
+      continue;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int s = q * 8 + e;
@@ -569,17 +585,24 @@ __global__ __launch_bounds__(256) void k_pack_records(const void* pts, int dtype
 // Norms (of the values the records represent), log-weights, starting potentials
 // and the initial bias chunks (at bias + r * bias_stride). Separate layout
 // (bias_alt non-null): the half-1 chunks of both bias buffers are zeroed here
-// once; the passes only rewrite half-0 chunks. One thread per point.
+// once; the passes only rewrite half-0 chunks. G threads per point: one for
+// small d, a wave for large d (coordinates k = lane, lane + 64, ...: coalesced
+// loads, the norm summed over the wave).
+template <int G>
 __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dtype, int64_t n, int d,
                                                         const float* shift, const float* w,
                                                         const float* pot, float* pot_zero,
                                                         float* alpha, float* lw, bf16x8* bias, int bias_stride,
                                                         bf16x8* bias_alt, float* hval, float log2e_over_eps,
                                                         float bias_scale, float* hacc) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n) return;
+  static_assert(G == 1 || G == 64, "a thread or a wave per point");
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = t / G;
+  const int sub = (int)(t % G);
+  if (r >= n) return;  // G = 64: the whole wave
   float nrm = 0.0f;
-  for (int k = 0; k < d; ++k) {
+#pragma unroll 4
+  for (int k = sub; k < d; k += G) {
     float v;
     if (dtype == 1) {
       const unsigned short bits = static_cast<const unsigned short*>(pts)[r * d + k];
@@ -590,6 +613,11 @@ __global__ __launch_bounds__(256) void k_prep_side_mfma(const void* pts, int dty
       if (shift) v -= shift[k];
     }
     nrm = fmaf(v, v, nrm);
+  }
+  if constexpr (G > 1) {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) nrm += __shfl_xor(nrm, o, G);
+    if (sub != 0) return;
   }
   const float l = logf(w[r]);
   const float pv = pot ? pot[r] : 0.0f;
@@ -795,10 +823,17 @@ hipError_t launch_prep_mfma(const MfmaPrepSide& xs, const MfmaPrepSide& ys, int 
                                                                 side->hacc, side->hacc_alt);
     // merged: the bias chunk is the last chunk of the column record
     bf16x8* bias0 = merged ? side->col_rec + (2 * nkb - 1) : side->bias;
-    k_prep_side_mfma<<<(int)((side->n + 255) / 256), 256, 0, s>>>(
-        side->pts, dtype, side->n, d, sh, side->w, side->pot, side->pot_zero, side->alpha, side->lw,
-        bias0, merged ? 2 * nkb : 2, merged ? nullptr : side->bias_alt, side->hval, log2e_over_eps,
-        mfma_bias_scale(dtype, c2), side->hacc);
+    if (d >= 32) {
+      k_prep_side_mfma<64><<<(int)((side->n * 64 + 255) / 256), 256, 0, s>>>(
+          side->pts, dtype, side->n, d, sh, side->w, side->pot, side->pot_zero, side->alpha, side->lw,
+          bias0, merged ? 2 * nkb : 2, merged ? nullptr : side->bias_alt, side->hval, log2e_over_eps,
+          mfma_bias_scale(dtype, c2), side->hacc);
+    } else {
+      k_prep_side_mfma<1><<<(int)((side->n + 255) / 256), 256, 0, s>>>(
+          side->pts, dtype, side->n, d, sh, side->w, side->pot, side->pot_zero, side->alpha, side->lw,
+          bias0, merged ? 2 * nkb : 2, merged ? nullptr : side->bias_alt, side->hval, log2e_over_eps,
+          mfma_bias_scale(dtype, c2), side->hacc);
+    }
   }
   return hipGetLastError();
 }

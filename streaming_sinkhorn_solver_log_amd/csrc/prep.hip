@@ -27,7 +27,10 @@ __device__ inline float load_point(const void* pts, int dtype, int64_t idx) {
 // range as a flat, coalesced stream: thread t < T (T = the largest multiple of
 // d not above 256) owns coordinate t % d and every (T / d)-th row; the T
 // per-thread sums are then added per coordinate in a fixed order. Wider
-// points give each thread whole coordinates.
+// points: block (b, c) covers coordinates [256 c, 256 c + 256), a thread one
+// coordinate of every row of the range (coalesced along the coordinates).
+// Either way each thread keeps four running sums, so that its loads are in
+// flight together.
 __global__ __launch_bounds__(256) void k_centroid_partial(const void* x, int64_t n, const void* y,
                                                            int64_t m, int dtype, int d,
                                                            double* part) {
@@ -43,12 +46,19 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const void* x, int64_t
     if (d <= 256) {
       const int T = (256 / d) * d;
       const int step = T / d;  // rows advanced per sweep of the block
-      double s = 0.0;
+      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
       if (t < T) {
         const int k = t % d;
-        for (int64_t r = r0 + t / d; r < r1; r += step) s += load_point(pts, dtype, r * d + k);
+        int64_t r = r0 + t / d;
+        for (; r + 3 * step < r1; r += 4 * step) {
+          s0 += load_point(pts, dtype, r * d + k);
+          s1 += load_point(pts, dtype, (r + step) * d + k);
+          s2 += load_point(pts, dtype, (r + 2 * step) * d + k);
+          s3 += load_point(pts, dtype, (r + 3 * step) * d + k);
+        }
+        for (; r < r1; r += step) s0 += load_point(pts, dtype, r * d + k);
       }
-      acc[t] = s;
+      acc[t] = (s0 + s1) + (s2 + s3);
       __syncthreads();
       if (t < d) {
         double tot = 0.0;
@@ -57,26 +67,41 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const void* x, int64_t
       }
       __syncthreads();
     } else {
-      for (int k = t; k < d; k += blockDim.x) {
-        double s = 0.0;
-        for (int64_t r = r0; r < r1; ++r) s += load_point(pts, dtype, r * d + k);
-        out[k] = s;
+      const int k = blockIdx.y * 256 + t;
+      if (k < d) {
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+        int64_t r = r0;
+        for (; r + 3 < r1; r += 4) {
+          s0 += load_point(pts, dtype, r * d + k);
+          s1 += load_point(pts, dtype, (r + 1) * d + k);
+          s2 += load_point(pts, dtype, (r + 2) * d + k);
+          s3 += load_point(pts, dtype, (r + 3) * d + k);
+        }
+        for (; r < r1; ++r) s0 += load_point(pts, dtype, r * d + k);
+        out[k] = (s0 + s1) + (s2 + s3);
       }
     }
   }
 }
 
-// shift_k = (mean_x + mean_y)_k / 2, summed over the partials in a fixed order.
+// shift_k = (mean_x + mean_y)_k / 2: a wave per coordinate, lane l summing the
+// partials of blocks l, l + 64, ... in order, then the lanes in a fixed tree.
 __global__ __launch_bounds__(256) void k_centroid_final(const double* part, int nb, int64_t n,
                                                         int64_t m, int d, float* shift) {
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    double sx = 0.0, sy = 0.0;
-    for (int b = 0; b < nb; ++b) {
-      sx += part[((int64_t)b * 2 + 0) * d + k];
-      sy += part[((int64_t)b * 2 + 1) * d + k];
-    }
-    shift[k] = static_cast<float>(0.5 * (sx / (double)n + sy / (double)m));
+  const int k = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64);
+  const int lane = threadIdx.x & 63;
+  if (k >= d) return;  // whole waves
+  double sx = 0.0, sy = 0.0;
+  for (int b = lane; b < nb; b += 64) {
+    sx += part[((int64_t)b * 2 + 0) * d + k];
+    sy += part[((int64_t)b * 2 + 1) * d + k];
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sx += __shfl_xor(sx, o);
+    sy += __shfl_xor(sy, o);
+  }
+  if (lane == 0) shift[k] = static_cast<float>(0.5 * (sx / (double)n + sy / (double)m));
 }
 
 __global__ __launch_bounds__(256) void k_zero_u32(unsigned* p, int64_t count) {
@@ -143,30 +168,18 @@ __global__ __launch_bounds__(1024) void k_cost(const float* a, const float* f, i
 // that sign. Then each x - t_k is a multiple of the spacing at x and smaller
 // than |x|, so it has at most 8 significant bits: exactly a bf16 number. A
 // coordinate whose values change sign keeps t_k = 0.
-// Ordered integer image of a float: a < b as floats iff ord(a) < ord(b) as
-// signed integers, so atomicMin / atomicMax on the images reduce floats.
-__device__ __forceinline__ int float_ord(float v) {
-  const int b = __float_as_int(v);
-  return b >= 0 ? b : b ^ 0x7FFFFFFF;
-}
-__device__ __forceinline__ float ord_float(int o) { return __int_as_float(o >= 0 ? o : o ^ 0x7FFFFFFF); }
 
-__global__ __launch_bounds__(256) void k_bf16_shift_init(int* mm, int d) {
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    mm[k] = float_ord(INFINITY);
-    mm[d + k] = float_ord(-INFINITY);
-  }
-}
-
-// mm[k] = ord(min), mm[d + k] = ord(max) of coordinate k over both clouds:
-// each workgroup reduces a contiguous range of rows (each thread a fixed
-// coordinate of every rstep-th row, coalesced along the rows), combines its
-// threads through LDS, then one atomic per coordinate and workgroup.
+// Per-block minima and maxima of every coordinate over both clouds
+// (mm[b][0..d) and mm[b][d..2d), floats), reduced by k_bf16_shift_final:
+// each workgroup takes a contiguous range of rows, each thread a fixed
+// coordinate of every rstep-th row (coalesced along the rows), combined
+// through LDS.
 __global__ __launch_bounds__(256) void k_bf16_shift_partial(const unsigned short* x, int64_t n,
                                                              const unsigned short* y, int64_t m, int d,
-                                                             int rows_per_block, int* mm) {
+                                                             int rows_per_block, float* mm) {
   __shared__ float slo[256], shi[256];
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  float* out = mm + (int64_t)blockIdx.x * 2 * d;
   const int kt = d < 256 ? d : 256;  // coordinates per row sweep
   const int rstep = 256 / kt;        // rows per sweep
   const int k0 = threadIdx.x % kt, rr = threadIdx.x / kt;
@@ -174,6 +187,7 @@ __global__ __launch_bounds__(256) void k_bf16_shift_partial(const unsigned short
     const int k = kb + k0;
     float lo = INFINITY, hi = -INFINITY;
     if (rr < rstep && k < d) {
+#pragma unroll 8
       for (int64_t r = r0 + rr; r < r0 + rows_per_block && r < n + m; r += rstep) {
         const unsigned short bits = r < n ? x[r * d + k] : y[(r - n) * d + k];
         const float v = __uint_as_float((unsigned)bits << 16);
@@ -189,49 +203,125 @@ __global__ __launch_bounds__(256) void k_bf16_shift_partial(const unsigned short
         lo = fminf(lo, slo[q * kt + k0]);
         hi = fmaxf(hi, shi[q * kt + k0]);
       }
-      atomicMin(&mm[k], float_ord(lo));
-      atomicMax(&mm[d + k], float_ord(hi));
+      out[k] = lo;
+      out[d + k] = hi;
     }
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(256) void k_bf16_shift_final(const int* mm, int d, float* shift) {
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float lo = ord_float(mm[k]), hi = ord_float(mm[d + k]);
-    float t = 0.0f;
-    if (lo > 0.0f || hi < 0.0f) {
-      const float small = lo > 0.0f ? lo : -hi, big = lo > 0.0f ? hi : -lo;
-      int e = 0;
-      frexpf(big, &e);                   // big = m 2^e, m in [0.5, 1)
-      const float U = ldexpf(1.0f, e - 8);  // bf16 spacing in [2^(e-1), 2^e)
-      t = floorf(small / U) * U;
-      if (hi < 0.0f) t = -t;
+// The same for d a multiple of 8: each thread reads 8 coordinates of a row at
+// once (16 bytes; rows of 8-coordinate groups are 16-byte aligned as the
+// points are).
+__global__ __launch_bounds__(256) void k_bf16_shift_partial8(const uint4* x, int64_t n, const uint4* y, int64_t m,
+                                                              int d8, int rows_per_block, float* mm) {
+  __shared__ float slo[8][256], shi[8][256];
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  float* out = mm + (int64_t)blockIdx.x * 16 * d8;
+  const int gt = d8 < 256 ? d8 : 256;  // coordinate groups per row sweep
+  const int rstep = 256 / gt;          // rows per sweep
+  const int g0 = threadIdx.x % gt, rr = threadIdx.x / gt;
+  for (int gb = 0; gb < d8; gb += gt) {
+    const int g = gb + g0;
+    float lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = INFINITY;
+      hi[e] = -INFINITY;
     }
-    shift[k] = t;
+    if (rr < rstep && g < d8) {
+#pragma unroll 4
+      for (int64_t r = r0 + rr; r < r0 + rows_per_block && r < n + m; r += rstep) {
+        const uint4 v = r < n ? x[r * d8 + g] : y[(r - n) * d8 + g];
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a0 = __uint_as_float(w[q] << 16), a1 = __uint_as_float(w[q] & 0xFFFF0000u);
+          lo[2 * q] = fminf(lo[2 * q], a0);
+          hi[2 * q] = fmaxf(hi[2 * q], a0);
+          lo[2 * q + 1] = fminf(lo[2 * q + 1], a1);
+          hi[2 * q + 1] = fmaxf(hi[2 * q + 1], a1);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      slo[e][threadIdx.x] = lo[e];
+      shi[e][threadIdx.x] = hi[e];
+    }
+    __syncthreads();
+    if (rr == 0 && g < d8) {
+      for (int q = 1; q < rstep; ++q) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lo[e] = fminf(lo[e], slo[e][q * gt + g0]);
+          hi[e] = fmaxf(hi[e], shi[e][q * gt + g0]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        out[8 * g + e] = lo[e];
+        out[8 * d8 + 8 * g + e] = hi[e];
+      }
+    }
+    __syncthreads();
   }
+}
+
+// The shift of each coordinate from the nb blocks' minima and maxima: a wave
+// per coordinate (lanes over the blocks, then a shuffle tree).
+__global__ __launch_bounds__(256) void k_bf16_shift_final(const float* mm, int nb, int d, float* shift) {
+  const int k = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64);
+  const int lane = threadIdx.x & 63;
+  if (k >= d) return;  // whole waves
+  float lo = INFINITY, hi = -INFINITY;
+  for (int b = lane; b < nb; b += 64) {
+    lo = fminf(lo, mm[(int64_t)b * 2 * d + k]);
+    hi = fmaxf(hi, mm[(int64_t)b * 2 * d + d + k]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  if (lane != 0) return;
+  float t = 0.0f;
+  if (lo > 0.0f || hi < 0.0f) {
+    const float small = lo > 0.0f ? lo : -hi, big = lo > 0.0f ? hi : -lo;
+    int e = 0;
+    frexpf(big, &e);                   // big = m 2^e, m in [0.5, 1)
+    const float U = ldexpf(1.0f, e - 8);  // bf16 spacing in [2^(e-1), 2^e)
+    t = floorf(small / U) * U;
+    if (hi < 0.0f) t = -t;
+  }
+  shift[k] = t;
 }
 
 }  // namespace
 
 hipError_t launch_bf16_shift(const void* x, int64_t n, const void* y, int64_t m, int d, double* part, float* shift,
                              hipStream_t s) {
-  int* mm = reinterpret_cast<int*>(part);  // 2 d ints of the centroid scratch
-  // about 512 workgroups: few atomics per coordinate, the whole GPU busy
+  // per-block minima and maxima in the centroid scratch (kCentroidBlocks x 2 d
+  // doubles hold kCentroidBlocks x 2 d floats)
+  float* mm = reinterpret_cast<float*>(part);
   const int64_t total = n + m;
-  const int rows = (int)(total / 512 > 64 ? (total + 511) / 512 : 64);
-  const int64_t blocks = (total + rows - 1) / rows;
-  k_bf16_shift_init<<<1, 256, 0, s>>>(mm, d);
-  k_bf16_shift_partial<<<(int)blocks, 256, 0, s>>>(static_cast<const unsigned short*>(x), n,
-                                                    static_cast<const unsigned short*>(y), m, d, rows, mm);
-  k_bf16_shift_final<<<1, 256, 0, s>>>(mm, d, shift);
+  const int rows = (int)((total + kCentroidBlocks - 1) / kCentroidBlocks);
+  const int blocks = (int)((total + rows - 1) / rows);
+  if (d % 8 == 0)
+    k_bf16_shift_partial8<<<blocks, 256, 0, s>>>(static_cast<const uint4*>(x), n, static_cast<const uint4*>(y), m,
+                                                 d / 8, rows, mm);
+  else
+    k_bf16_shift_partial<<<blocks, 256, 0, s>>>(static_cast<const unsigned short*>(x), n,
+                                                static_cast<const unsigned short*>(y), m, d, rows, mm);
+  k_bf16_shift_final<<<(d * 64 + 255) / 256, 256, 0, s>>>(mm, blocks, d, shift);
   return hipGetLastError();
 }
 
 hipError_t launch_centroid(const void* x, int64_t n, const void* y, int64_t m, int dtype, int d,
                            double* centroid_part, float* shift, hipStream_t s) {
-  k_centroid_partial<<<kCentroidBlocks, 256, 0, s>>>(x, n, y, m, dtype, d, centroid_part);
-  k_centroid_final<<<1, 256, 0, s>>>(centroid_part, kCentroidBlocks, n, m, d, shift);
+  const dim3 grid(kCentroidBlocks, d > 256 ? (d + 255) / 256 : 1);
+  k_centroid_partial<<<grid, 256, 0, s>>>(x, n, y, m, dtype, d, centroid_part);
+  k_centroid_final<<<(d * 64 + 255) / 256, 256, 0, s>>>(centroid_part, kCentroidBlocks, n, m, d, shift);
   return hipGetLastError();
 }
 

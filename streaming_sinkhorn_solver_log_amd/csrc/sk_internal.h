@@ -49,6 +49,6 @@ hipError_t launch_small_aux(const void* x, const void* y, int dtype, int64_t n, 
 hipError_t launch_cost(const float* a, const float* f, int64_t n, const float* b, const float* g,
                        int64_t m, double* cost, hipStream_t s);
 
-constexpr int kCentroidBlocks = 64;
+constexpr int kCentroidBlocks = 256;
 
 }  // namespace sk
