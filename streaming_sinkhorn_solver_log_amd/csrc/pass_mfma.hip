@@ -749,14 +749,18 @@ PassPlan plan_mfma_pass(int64_t nr, int64_t nc, int nkb, bool merged, bool scale
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
   pl.stages = (int)((nc + kStageCols - 1) / kStageCols);
   const int64_t units = (int64_t)pl.row_blocks * pl.stages;
-  // a pass sharing its launch with another gets 1/share of the resident
+  // A pass sharing its launch with another gets 1/share of the resident
   // workgroups (a multiple of 8, so both keep the XCD-contiguous numbering)
   // where its units are few; with at least 32 units a workgroup each keeps
-  // all of them (the launch then runs two rounds, which balance better:
-  // n = m = 50k, d = 3, averaged: 541 -> 524 us per iteration; at 10k the
-  // shared grid is faster, 35 against 40 us)
+  // all of them, and a pass of its own with at least 64 gets twice the
+  // resident count: the launch then runs two rounds, and workgroups of the
+  // second fill the slots the first frees unevenly (n = m = 50k: averaged
+  // d = 3, 541 -> 515 us per iteration; alternating d = 64, 399 -> 392 us and
+  // d = 3, 241 -> 236 us per half-pass; at 10k the shared grid is faster, 35
+  // against 40 us per iteration).
   int64_t grid = resident_workgroups(nkb, merged);
   if (share > 1 && units < 32 * grid) grid = grid / share / 8 * 8 > 0 ? grid / share / 8 * 8 : 1;
+  else if (share == 1 && units >= 64 * grid) grid *= 2;
   const int64_t min_units = 4;  // at least 512 columns of one row block per workgroup
   if (grid > units / min_units) grid = units / min_units;
   if (grid < 1) grid = 1;
