@@ -993,9 +993,13 @@ __global__ __launch_bounds__(256) void k_pv_merge(const PvArgs p, int cw) {
     const int cc = z * cw + c;
     if (cc >= p.kv) continue;
     const int64_t s0 = (int64_t)z * p.splits * p.nr + i;  // slot (z, 0) of row i
+    // (unrolled so that the partials' loads are in flight together; the sums
+    // still run in split order)
     float Mt = kMuInit;
+#pragma unroll 8
     for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, part_ms[s0 + (int64_t)s2 * p.nr].x);
     float St = 0.0f, Tt = 0.0f;
+#pragma unroll 8
     for (int s2 = 0; s2 < p.splits; ++s2) {
       const int64_t sl = s0 + (int64_t)s2 * p.nr;
       const float2 ms = part_ms[sl];
