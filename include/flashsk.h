@@ -146,6 +146,13 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
  * otherwise. Widths above 64 on large d (bf16 d > 128, float32 d > 21) run on
  * the wide kernel (scores once per 512 values); on small d the scores are
  * recomputed once per 64 values.
+ * Precision of the plan entries in the value products: float32 points, three
+ * bf16 parts of each entry and value (float32 accuracy); bf16 points with
+ * d <= 128, one float16 per entry (relative error <= 2^-11, inside the 1e-3
+ * bound of bf16 inputs) and two float16 parts of each value after an exact
+ * power-of-two scale per value column (values below 2^-29 of their column's
+ * largest magnitude fall into float16's subnormal range); bf16 points with
+ * larger d, two bf16 parts of each entry (2^-16) and of each value.
  */
 int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                        const float* a, const float* b, const float* f, const float* g, double eps,
@@ -158,7 +165,9 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
  *   grad_x_i = 2 a_i (x_i - sum_j pi_ij y_j),
  *   pi_ij = softmax over j of (log b_j + (g_j - C_ij)/eps),
  * using g only. This is the exact derivative of x -> <a, F_x(g)> + <b, g>;
- * it equals the derivative of the cost at a converged pair.
+ * it equals the derivative of the cost at a converged pair. The weights pi
+ * enter the weighted sum with the precision sk_transport_apply states (their
+ * normalizing sum is accumulated in float32), the points y exactly.
  * Requirements as for the solve.
  */
 int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,

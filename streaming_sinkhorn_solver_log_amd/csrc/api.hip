@@ -266,7 +266,7 @@ Scalars scalars(double eps) {
 struct AuxPlan {
   Path path;
   int nkb;
-  int kv, nobt, nob, nchunks, pp, vp;
+  int kv, nobt, nob, nchunks, pp, vp;  // pp = 1: half-precision form
   int wq;  // weighted application: tangent record arrays (0: unweighted)
   int64_t nr, nc;
   PassPlan pl;
@@ -275,7 +275,7 @@ struct AuxPlan {
 // weighted: the application of the plan entries times t_i.y_j to the values
 // y (rows x, columns y), which runs on the GEMM-tiled wide kernel at any d.
 AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool grad, int transpose,
-                 bool weighted = false) {
+                 bool weighted = false, bool precise = false) {
   AuxPlan ap{};
   ap.path = weighted ? (d <= 4096 ? Path::Gemm : Path::None) : aux_path(dtype, d);
   ap.wq = weighted ? (dtype == SK_BF16 ? 2 : 1) : 0;
@@ -285,7 +285,7 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
   if (ap.path == Path::Mfma || ap.path == Path::Gemm) {
     const bool gemm = ap.path == Path::Gemm;
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
-    pv_parts(dtype, grad || weighted, ap.pp, ap.vp);
+    pv_parts(dtype, grad || weighted, gemm || weighted, precise, ap.pp, ap.vp);
     const int blocks = (int)((kv + 31) / 32);
     ap.nob = weighted ? pv_wide_nob(blocks, ap.vp, true) : pv_nob(gemm, blocks, ap.vp);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
@@ -298,6 +298,7 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
 struct AuxWsM {
   SideM x, y;
   bf16x8* vfrag;
+  unsigned* vmax;  // half-precision form: column maxima of the values
   int64_t vtiles;
   bf16x8* wrec;  // weighted application: tangent records of the rows
   float* qoff;
@@ -312,6 +313,7 @@ AuxWsM layout_aux_m(void* ws, const AuxPlan& ap, int64_t n, int64_t m, int64_t d
   L.y = carve_side_m(c, m, ap.nkb, 1);
   L.vtiles = mfma_padded_count(ap.nc) / 32;
   L.vfrag = c.take<bf16x8>((size_t)L.vtiles * ap.nobt * ap.vp * 2 * 64);
+  if (ap.pp == 1) L.vmax = c.take<unsigned>((size_t)ap.kv);
   // (mu, S) pairs, padded to 16 bytes, then the value partials
   const size_t slots_rows = (size_t)ap.nchunks * ap.pl.splits * ap.nr;
   const size_t part_floats = ap.pl.splits > 1
@@ -347,12 +349,13 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   if (e != hipSuccess) return hip_fail(e, "prep");
   const float* shift = L.c.shift;  // centering shift of both clouds (exact for bf16 points)
   e = launch_pack_values(vsrc, vsrc_bf16, ap.nc, ap.kv, grad ? shift : nullptr, ap.vp, ap.nobt,
-                         L.vtiles, L.vfrag, s);
+                         L.vtiles, ap.pp == 1 ? L.vmax : nullptr, L.vfrag, s);
   if (e != hipSuccess) return hip_fail(e, "value packing");
   const SideM& R = transpose ? L.y : L.x;
   const SideM& C = transpose ? L.x : L.y;
   PvArgs pa{};
   pa.rows = R.row_rec; pa.cols = C.col_rec; pa.bias_col = C.bias[0]; pa.vfrag = L.vfrag;
+  pa.vmax = ap.pp == 1 ? L.vmax : nullptr;
   pa.nobt = ap.nobt; pa.kv = ap.kv; pa.out = out;
   pa.hrow = R.hval[0]; pa.wrow = a; pa.xrow = x; pa.xbf16 = dtype == SK_BF16; pa.shift = shift;
   pa.grad = grad ? 1 : 0;
@@ -529,8 +532,8 @@ size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
   return a > b ? a : b;
 }
 
-size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose) {
-  return aux_bytes(plan_aux(dtype, n, m, d, k, false, transpose), n, m, d);
+size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose, bool precise) {
+  return aux_bytes(plan_aux(dtype, n, m, d, k, false, transpose, false, precise), n, m, d);
 }
 
 size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d) {
@@ -594,6 +597,29 @@ int solve_to_tolerance(const void* x, const void* y, int dtype, int64_t n, int64
   *iters_done = done;
   *err = e_host;
   return SK_OK;
+}
+
+int transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                    const float* b, const float* f, const float* g, double eps, int transpose, const float* V,
+                    int64_t k, float* out, void* ws, size_t ws_bytes, void* stream, bool precise) {
+  clear_error();
+  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
+  if (rc) return rc;
+  if (!f || !g || !V || !out) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
+  if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
+  if (k < 1) return fail(SK_ERR_INVALID_ARG, "k must be >= 1");
+  if (k > kMaxValueCols)
+    return fail(SK_ERR_UNSUPPORTED, "k=%lld > %lld is not supported", (long long)k, (long long)kMaxValueCols);
+  const AuxPlan ap = plan_aux(dtype, n, m, d, k, false, transpose, false, precise);
+  if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
+  if (small_aux_fits(n, m, d, k) && small_enabled()) {
+    const hipError_t e = launch_small_aux(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, false, V, k, out,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SK_OK : hip_fail(e, "small-problem transport application");
+  }
+  const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
+  return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, transpose, V, false, out, scalars(eps),
+                   static_cast<hipStream_t>(stream));
 }
 
 }  // namespace api
@@ -674,24 +700,8 @@ int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64
                        const float* a, const float* b, const float* f, const float* g, double eps,
                        int transpose, const float* V, int64_t k, float* out, void* ws,
                        size_t ws_bytes, void* stream) {
-  clear_error();
-  int rc = check_common(x, y, dtype, n, m, d, a, b, eps, aux_path(dtype, d));
-  if (rc) return rc;
-  if (!f || !g || !V || !out) return fail(SK_ERR_INVALID_ARG, "null pointer argument");
-  if (transpose != 0 && transpose != 1) return fail(SK_ERR_INVALID_ARG, "transpose must be 0 or 1");
-  if (k < 1) return fail(SK_ERR_INVALID_ARG, "k must be >= 1");
-  if (k > kMaxValueCols)
-    return fail(SK_ERR_UNSUPPORTED, "k=%lld > %lld is not supported", (long long)k, (long long)kMaxValueCols);
-  const AuxPlan ap = plan_aux(dtype, n, m, d, k, false, transpose);
-  if ((rc = check_ws(ws, ws_bytes, aux_bytes(ap, n, m, d)))) return rc;
-  if (small_aux_fits(n, m, d, k) && small_enabled()) {
-    const hipError_t e = launch_small_aux(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, false, V, k, out,
-                                          static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SK_OK : hip_fail(e, "small-problem transport application");
-  }
-  const AuxWsM L = layout_aux_m(ws, ap, n, m, d);
-  return run_aux_m(ap, L, x, y, dtype, n, m, d, a, b, f, g, false, transpose, V, false, out, scalars(eps),
-                   static_cast<hipStream_t>(stream));
+  return sk::api::transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, V, k, out, ws, ws_bytes,
+                                  stream, false);
 }
 
 int sk_eot_grad_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,

@@ -409,7 +409,7 @@ HvpWs layout_hvp(void* ws, int dtype, int64_t n, int64_t m, int64_t d) {
   L.dots = cv.take<double>(kCgSlots);
   size_t need = apply_weighted_bytes(dtype, n, m, d);
   for (int64_t kk : {(int64_t)1, d}) {
-    const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0), a1 = apply_bytes(dtype, n, m, d, kk, 1);
+    const size_t a0 = apply_bytes(dtype, n, m, d, kk, 0, true), a1 = apply_bytes(dtype, n, m, d, kk, 1, true);
     need = a0 > need ? a0 : need;
     need = a1 > need ? a1 : need;
   }
@@ -606,9 +606,11 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // the CG's applications keep two bf16 parts per plan entry (bf16 points):
+  // the Schur system amplifies the rounding of a single float16 part
   auto apply = [&](const float* vals, int64_t k, int transpose, float* o) {
-    return sk_transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner,
-                              L.inner_bytes, stream);
+    return transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner, L.inner_bytes,
+                           stream, true);
   };
   const int64_t big = n > m ? n : m;
   k_to_f32<<<grid_for(n * d), 256, 0, s>>>(x, dtype == SK_BF16, n * d, L.xf);

@@ -23,8 +23,19 @@
 // three and three; the entries' leading parts are truncations, of relative
 // order 1, 2^-7, 2^-14, the values' are rounded, 1, 2^-8, 2^-16, and the six
 // products kept leave out terms of order 2^-22 and below: float32 accuracy;
-// bf16 points: two parts of the entries (2^-16) and two of the values for
-// P V, or one exact part of the bf16 points for the gradient).
+// bf16 points on the GEMM-tiled kernels: two parts of the entries (2^-16)
+// and two of the values for P V, or one exact part of the bf16 points for
+// the gradient). The register-resident kernel takes bf16 points in the
+// half-precision form (PP = 1): as the attention output of FlashAttention
+// feeds its probabilities to the second product in 16-bit form, each entry
+// is one float16 (11 significant bits, rounded to nearest: relative error
+// <= 2^-11, within the 1e-3 bound of bf16 inputs), and the values are two
+// float16 parts (22 bits) after an exact power-of-two scale per value column
+// that puts the column's largest magnitude in [2^13, 2^14). float16's range
+// is kept by the stabilization below: the entries of a row are biased so the
+// running maximum term is 2^8 and stay below 2^15; terms 2^22 below the
+// maximum reach float16's subnormals, where the absolute error 2^-33 of the
+// maximum per term is negligible.
 //
 // Stabilization: a running row maximum mu (acc units), raised only when a
 // tile's maximum exceeds it by more than 2^16 in value (lazy rescaling: terms
@@ -45,6 +56,25 @@ using namespace dev;
 
 constexpr float kMuInit = -1.0e29f;  // no column seen yet (above any masked score)
 constexpr float kLazy = 16.0f;       // raise mu when a term would exceed 2^16
+// Half-precision form: terms 2^(e (acc - mu) + kHalfBias), raised when one
+// would exceed 2^15 (float16's largest power of two).
+constexpr float kHalfBias = 8.0f;
+constexpr float kHalfLazy = 15.0f - kHalfBias;
+constexpr int kVmaxCols = 4096;  // value columns of one application (the C-ABI allows k <= 4096)
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Power-of-two exponent k of a value column's scale 2^k: the column's largest
+// magnitude (float bits, as k_value_max writes them) times 2^k lies in
+// [2^13, 2^14); 0 for an all-zero column, clamped so the scale is a normal float.
+__device__ __forceinline__ int half_scale_exp(unsigned maxbits) {
+  if (maxbits == 0u) return 0;
+  const int be = (int)(maxbits >> 23);  // biased exponent (0: subnormal, 255: inf / nan)
+  const int ex = (be == 0 ? 1 : be) - 126;  // max = m 2^ex, m in [0.5, 1) for normal values
+  const int k = 14 - ex;
+  return k < -126 ? -126 : (k > 126 ? 126 : k);
+}
 
 template <int NOB, int VP>
 struct VTile {
@@ -83,8 +113,9 @@ __device__ __forceinline__ float max16(const f32x16& a) {
   return max3(max3(m1, m2, m3), max3(m4, m5, a[15]), a[15]);
 }
 
-// Lazy running maximum of a row over NT score tiles; returns the exponent offset -e*mu.
-template <int NT, int NOB>
+// Lazy running maximum of a row over NT score tiles; returns the exponent
+// offset -e*mu (H: -e*mu + kHalfBias).
+template <int NT, int NOB, bool H = false>
 __device__ __attribute__((always_inline)) inline float pv_shift(const f32x16 (&acc)[NT], float e, float& mu,
                                                                 float& S, f32x16 (&O)[NOB]) {
   float tm = max16(acc[0]);
@@ -92,7 +123,7 @@ __device__ __attribute__((always_inline)) inline float pv_shift(const f32x16 (&a
   for (int t = 1; t < NT; ++t) tm = max3(tm, max16(acc[t]), tm);
   const float to = __shfl_xor(tm, 32);
   tm = max3(tm, to, to);
-  const bool raise = e * (tm - mu) > kLazy;
+  const bool raise = e * (tm - mu) > (H ? kHalfLazy : kLazy);
   if (__any(raise)) {
     const float mn = raise ? tm : mu;
     const float sc = fast_exp2(e * (mu - mn));
@@ -103,7 +134,7 @@ __device__ __attribute__((always_inline)) inline float pv_shift(const f32x16 (&a
       for (int r = 0; r < 16; ++r) O[ob][r] *= sc;
     mu = mn;
   }
-  return -e * mu;
+  return H ? fmaf(-e, mu, kHalfBias) : -e * mu;
 }
 
 // Two floats' upper 16 bits packed as a bf16 pair (a in the low half): the
@@ -157,6 +188,42 @@ __device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& ac
   return s0 + s1;
 }
 
+// Half-precision form of pv_probs: the entries (terms < 2^15) as one float16
+// part each, rounded to nearest (v_cvt_pk_f16_f32), and their float32 sum (SUM).
+template <bool SUM>
+__device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& acc, float e, float off,
+                                                                 f16x8 (&P)[2]) {
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float v0 = fast_exp2(fmaf(acc[r], e, off));
+    const float v1 = fast_exp2(fmaf(acc[r + 1], e, off));
+    if constexpr (SUM) {
+      s0 = r == 0 ? v0 : s0 + v0;
+      s1 = r == 0 ? v1 : s1 + v1;
+    }
+    const f16x2 h = {(_Float16)v0, (_Float16)v1};
+    P[r >> 3][r & 7] = h[0];
+    P[r >> 3][(r & 7) + 1] = h[1];
+  }
+  return s0 + s1;
+}
+
+// O[ob] += V[ob] x P in float16: the entries' one part against each of the VP
+// value parts (fragments hold float16 bits in the half-precision form).
+template <int NOB, int VP>
+__device__ __attribute__((always_inline)) inline void pv_mfma_h(const VTile<NOB, VP>& vt, const f16x8 (&P)[2],
+                                                                f32x16 (&O)[NOB]) {
+#pragma unroll
+  for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+    for (int vp = 0; vp < VP; ++vp)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        O[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vt.v[ob][vp][kb]), P[kb], O[ob],
+                                                       0, 0, 0);
+}
+
 // Weighted plan entries of one score tile: 2^{e acc + off} * q (q: the
 // weights in the accumulator layout), split into PP bf16 parts as pv_probs
 // does (the weights may be negative: the truncated parts keep the sign and
@@ -208,8 +275,12 @@ __device__ __attribute__((always_inline)) inline void pv_mfma(const VTile<NOB, V
 }
 
 // Output element (row i, value index cc) from the merged (mu, S, T) of the row.
+// Half-precision form (vmax non-null): T carries the column's value scale
+// 2^k and, in the application, the entries' bias 2^kHalfBias (the gradient's
+// S carries the same bias and it cancels).
 __device__ __forceinline__ void pv_store(const PvArgs& p, int i, int cc, float mu, float S, float T) {
   const int64_t o = (int64_t)i * p.kv + cc;
+  if (p.vmax) T = ldexpf(T, -half_scale_exp(p.vmax[cc]));
   if (p.grad) {
     float xv;
     if (p.xbf16) xv = __uint_as_float((unsigned)static_cast<const unsigned short*>(p.xrow)[o] << 16);
@@ -217,7 +288,8 @@ __device__ __forceinline__ void pv_store(const PvArgs& p, int i, int cc, float m
     if (p.shift) xv -= p.shift[cc];
     p.out[o] = 2.0f * p.wrow[i] * (xv - T / S);
   } else {
-    p.out[o] = T * fast_exp2(fmaf(p.escale, mu, p.hrow[i]));
+    const float h = fmaf(p.escale, mu, p.hrow[i]);
+    p.out[o] = T * fast_exp2(p.vmax ? h - kHalfBias : h);
   }
 }
 
@@ -308,16 +380,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
     for (int ob = 0; ob < NOB; ++ob) O[rb][ob] = f32x16{};
   }
 
-  // Plan entries of a scored tile, then their products with the tile's values.
+  // Plan entries of a scored tile, then their products with the tile's values
+  // (PP = 1: the half-precision form).
+  constexpr bool H = PP == 1;
   auto entries_work = [&](const f32x16 (&acc)[RB], const VTile<NOB, VP>& vt) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const f32x16 a1[1] = {acc[rb]};
-      const float off = pv_shift<1, NOB>(a1, e, mu[rb], S[rb], O[rb]);
-      bf16x8 P[PP][2];
-      if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb], e, off, P);
-      else pv_probs<PP, false>(acc[rb], e, off, P);  // the application never divides by S
-      pv_mfma<NOB, PP, VP>(vt, P, O[rb]);
+      const float off = pv_shift<1, NOB, H>(a1, e, mu[rb], S[rb], O[rb]);
+      if constexpr (H) {
+        f16x8 P[2];
+        if (p.grad) S[rb] += pv_probs_h<true>(acc[rb], e, off, P);
+        else pv_probs_h<false>(acc[rb], e, off, P);
+        pv_mfma_h<NOB, VP>(vt, P, O[rb]);
+      } else {
+        bf16x8 P[PP][2];
+        if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb], e, off, P);
+        else pv_probs<PP, false>(acc[rb], e, off, P);  // the application never divides by S
+        pv_mfma<NOB, PP, VP>(vt, P, O[rb]);
+      }
     }
   };
 
@@ -1011,13 +1092,50 @@ __global__ __launch_bounds__(256) void k_pv_merge(const PvArgs p, int cw) {
   }
 }
 
+// Largest magnitude of each value column (as float bits; (src - shift) for
+// the gradient's points) into vmax, which k_value_max_init zeroed. Maxima of
+// non-negative floats order as their bits, so the atomics are exact and the
+// result does not depend on their order.
+__global__ __launch_bounds__(256) void k_value_max_init(int kv, unsigned* vmax) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < kv) vmax[i] = 0u;
+}
+
+// The grid's thread count is a multiple of kv, so each thread stays on one
+// column; a workgroup combines its threads' maxima in LDS, then issues one
+// global atomic per column.
+__global__ __launch_bounds__(256) void k_value_max(const void* src, int src_bf16, int64_t nv, int kv,
+                                                   const float* shift, unsigned* vmax) {
+  __shared__ unsigned smax[kVmaxCols];
+  for (int c = threadIdx.x; c < kv; c += 256) smax[c] = 0u;
+  __syncthreads();
+  const int64_t total = nv * kv;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cc = (int)(idx % kv);
+  unsigned m = 0u;
+  for (; idx < total; idx += stride) {
+    float v = src_bf16 ? __uint_as_float((unsigned)static_cast<const unsigned short*>(src)[idx] << 16)
+                       : static_cast<const float*>(src)[idx];
+    if (shift) v -= shift[cc];
+    const unsigned bits = __float_as_uint(v) & 0x7FFFFFFFu;
+    m = bits > m ? bits : m;
+  }
+  if (m) atomicMax(&smax[cc], m);
+  __syncthreads();
+  for (int c = threadIdx.x; c < kv; c += 256)
+    if (smax[c]) atomicMax(&vmax[c], smax[c]);
+}
+
 // Value fragment (tile t, value block ob, part vp, K block kb) in lane l
 // (h = l / 32): the values of index 32 ob + l % 32 at the eight points
 // 32 t + 16 kb + 8 (e / 4) + 4 h + e % 4, e = 0..7 -- the column order of a
-// score accumulator. Part vp of the three-part bf16 split; zeros past nv / kv.
+// score accumulator. Part vp of the three-part bf16 split, or with vmax (the
+// half-precision form) of the two-part float16 split of the value times its
+// column's scale 2^k (exact); zeros past nv / kv.
 __global__ __launch_bounds__(256) void k_pack_values(const void* src, int src_bf16, int64_t nv, int kv,
                                                      const float* shift, int vp_parts, int nobt,
-                                                     int64_t ntiles, bf16x8* out) {
+                                                     int64_t ntiles, const unsigned* vmax, bf16x8* out) {
   const int64_t total = ntiles * nobt * vp_parts * 2 * 64;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
@@ -1031,7 +1149,9 @@ __global__ __launch_bounds__(256) void k_pack_values(const void* src, int src_bf
     const int64_t t = q / nobt;
     const int h = lane >> 5;
     const int cc = ob * 32 + (lane & 31);
+    const int k = (vmax && cc < kv) ? half_scale_exp(vmax[cc]) : 0;
     bf16x8 r = {};
+    f16x8 rh = {};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int64_t j = t * 32 + kb * 16 + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -1041,11 +1161,17 @@ __global__ __launch_bounds__(256) void k_pack_values(const void* src, int src_bf
         else v = static_cast<const float*>(src)[j * kv + cc];
         if (shift) v -= shift[cc];
       }
-      __bf16 a, b, c;
-      split3(v, a, b, c);
-      r[e] = vp == 0 ? a : (vp == 1 ? b : c);
+      if (vmax) {
+        const float vs = ldexpf(v, k);
+        const _Float16 hi = (_Float16)vs;
+        rh[e] = vp == 0 ? hi : (_Float16)(vs - (float)hi);
+      } else {
+        __bf16 a, b, c;
+        split3(v, a, b, c);
+        r[e] = vp == 0 ? a : (vp == 1 ? b : c);
+      }
     }
-    out[idx] = r;
+    out[idx] = vmax ? __builtin_bit_cast(bf16x8, rh) : r;
   }
 }
 
@@ -1111,7 +1237,8 @@ bool try_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t 
 template <int NKB, int RB, int NOB>
 hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t s) {
   if (try_pv_mfma<NKB, RB, NOB, 3, 3>(a, pp, vp, grid, s) || try_pv_mfma<NKB, RB, NOB, 2, 2>(a, pp, vp, grid, s) ||
-      try_pv_mfma<NKB, RB, NOB, 2, 1>(a, pp, vp, grid, s))
+      try_pv_mfma<NKB, RB, NOB, 2, 1>(a, pp, vp, grid, s) || try_pv_mfma<NKB, RB, NOB, 1, 2>(a, pp, vp, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 1, 1>(a, pp, vp, grid, s))
     return hipGetLastError();
   return hipErrorInvalidValue;
 }
@@ -1155,10 +1282,13 @@ hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& gri
 
 }  // namespace
 
-void pv_parts(int dtype, bool grad, int& pp, int& vp) {
+void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp) {
   if (dtype == 0) {
     pp = 3;
     vp = 3;
+  } else if (!gemm && !precise) {
+    pp = 1;  // half-precision form
+    vp = grad ? 1 : 2;
   } else {
     pp = 2;
     vp = grad ? 1 : 2;
@@ -1318,11 +1448,28 @@ hipError_t launch_pack_tangent(const float* T, bool bf16pts, int64_t n, int d, i
 }
 
 hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
-                              int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s) {
+                              int vp, int nobt, int64_t ntiles, unsigned* vmax, bf16x8* out, hipStream_t s) {
+  if (vmax) {
+    k_value_max_init<<<(kv + 255) / 256, 256, 0, s>>>(kv, vmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (kv < 1 || kv > kVmaxCols) return hipErrorInvalidValue;
+    // a grid whose thread count is a multiple of kv: blocks a multiple of kv / gcd(kv, 256)
+    int g = kv, r = 256;
+    while (r) { const int t = g % r; g = r; r = t; }
+    const int64_t unit = kv / g;
+    const int64_t total = nv * kv;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 256) blocks = 256;
+    blocks = blocks / unit * unit;
+    if (blocks < unit) blocks = unit;
+    k_value_max<<<(int)blocks, 256, 0, s>>>(src, src_bf16 ? 1 : 0, nv, kv, shift, vmax);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t total = ntiles * nobt * vp * 2 * 64;
   const int64_t blocks = (total + 255) / 256;
   k_pack_values<<<(int)(blocks < 8192 ? blocks : 8192), 256, 0, s>>>(src, src_bf16 ? 1 : 0, nv, kv, shift,
-                                                                     vp, nobt, ntiles, out);
+                                                                     vp, nobt, ntiles, vmax, out);
   return hipGetLastError();
 }
 

@@ -80,7 +80,15 @@ hipError_t launch_marginal_error(const float* w, const float* p0, const float* p
 
 // Workspace bytes of the core entry points (api.hip).
 size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d);
-size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose);
+size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose, bool precise = false);
+// sk_transport_apply with precise = true: bf16 points keep two bf16 parts per
+// plan entry (relative error 2^-16) instead of the one float16 part of the
+// register-resident kernel; for the applications inside the Hessian-vector
+// product's CG, whose Schur system amplifies entry rounding.
+// ws: apply_bytes(..., precise).
+int transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
+                    const float* b, const float* f, const float* g, double eps, int transpose, const float* V,
+                    int64_t k, float* out, void* ws, size_t ws_bytes, void* stream, bool precise);
 size_t grad_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 // Weighted application (rows x, columns y, any d <= 4096, arguments validated
 // by the caller): out_i = sum_j P_ij (t_i . y_j) y_j, out and T n x d float32;

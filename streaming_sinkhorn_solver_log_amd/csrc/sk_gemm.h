@@ -21,8 +21,11 @@ PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
 hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, const PassPlan& pl,
                            hipStream_t s);
 // Transport application / gradient kernels. pv_parts: bf16 parts of the plan
-// entries (pp) and of the values (vp) for a storage type and operation.
-void pv_parts(int dtype, bool grad, int& pp, int& vp);
+// entries (pp) and of the values (vp) for a storage type and operation; pp = 1
+// is the half-precision form of the register-resident kernel (bf16 points,
+// not GEMM-tiled, unless precise: one float16 part per entry, vp float16
+// parts of the values scaled per column).
+void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp);
 int pv_nob(bool gemm, int nobt, int vp);  // value blocks per launch chunk
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
@@ -40,8 +43,10 @@ inline int pv_wide_nob(int nobt, int vp, bool weighted) {
   const int w = nobt <= 4 ? 1 : (nobt <= 8 || weighted ? 2 : 4);
   return 4 * w;
 }
-// Value fragments of nv points (src nv x kv, float32 or bf16 bits) for vp parts.
+// Value fragments of nv points (src nv x kv, float32 or bf16 bits) for vp parts;
+// with vmax (kv words, kv <= 4096) the half-precision form, whose column
+// maxima it writes there first.
 hipError_t launch_pack_values(const void* src, bool src_bf16, int64_t nv, int kv, const float* shift,
-                              int vp, int nobt, int64_t ntiles, bf16x8* out, hipStream_t s);
+                              int vp, int nobt, int64_t ntiles, unsigned* vmax, bf16x8* out, hipStream_t s);
 
 }  // namespace sk

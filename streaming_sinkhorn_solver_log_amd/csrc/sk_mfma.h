@@ -62,6 +62,7 @@ struct PvArgs {
   const void* cols;        // nc column-form records (padded)
   const bf16x8* bias_col;  // nc bias records of the columns (padded)
   const bf16x8* vfrag;     // value fragments of the columns (padded)
+  const unsigned* vmax;    // half-precision form: kv column maxima (float bits), else null
   int nobt;                // value blocks (of 32) per tile in vfrag
   int kv;                  // value width; out is nr x kv, row-major
   float* out;
