@@ -345,7 +345,7 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
 // Register-resident rows (record widths up to 8 K blocks): each wave keeps RB
 // blocks of 32 row records and streams column tiles and their value fragments
 // from memory, one tile ahead.
-template <int NKB, int RB, int NOB, int PP, int VP>
+template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD>
 __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
@@ -390,12 +390,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
       const float off = pv_shift<1, NOB, H>(a1, e, mu[rb], S[rb], O[rb]);
       if constexpr (H) {
         f16x8 P[2];
-        if (p.grad) S[rb] += pv_probs_h<true>(acc[rb], e, off, P);
+        if constexpr (GRAD) S[rb] += pv_probs_h<true>(acc[rb], e, off, P);
         else pv_probs_h<false>(acc[rb], e, off, P);
         pv_mfma_h<NOB, VP>(vt, P, O[rb]);
       } else {
         bf16x8 P[PP][2];
-        if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb], e, off, P);
+        if constexpr (GRAD) S[rb] += pv_probs<PP, true>(acc[rb], e, off, P);
         else pv_probs<PP, false>(acc[rb], e, off, P);  // the application never divides by S
         pv_mfma<NOB, PP, VP>(vt, P, O[rb]);
       }
@@ -1223,13 +1223,22 @@ __global__ __launch_bounds__(256) void k_pack_tangent(const float* __restrict__ 
 // Row blocks per wave of the resident kernel: two where registers allow.
 constexpr int pv_rb(int nkb, int nob, int vp) { return (nkb <= 4 && nob * vp <= 2) ? 2 : 1; }
 
+// The gradient / application choice is a template argument (no branch in the
+// tile loop); bf16 points use one value part for the gradient (the points)
+// and two for applications, float32 points three for both.
 template <int NKB, int RB, int NOB, int PP, int VP>
 bool try_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t s) {
   if constexpr (pv_rb(NKB, NOB, VP) != RB) {
     return false;
   } else {
     if (pp != PP || vp != VP) return false;
-    k_pv_mfma<NKB, RB, NOB, PP, VP><<<grid, kThreads, 0, s>>>(a);
+    if (a.grad) {
+      if constexpr (VP != 2) k_pv_mfma<NKB, RB, NOB, PP, VP, true><<<grid, kThreads, 0, s>>>(a);
+      else return false;
+    } else {
+      if constexpr (VP != 1) k_pv_mfma<NKB, RB, NOB, PP, VP, false><<<grid, kThreads, 0, s>>>(a);
+      else return false;
+    }
     return true;
   }
 }

@@ -699,6 +699,48 @@ def test_apply_arbitrary_potentials(sk, key, scale):
     assert eg <= tol_rel(w)
 
 
+@pytest.mark.parametrize("eps", [0.1, 0.004])
+def test_half_precision_form_column_scales(sk, eps):
+    """bf16 points at d = 64 run the transport kernels in half precision (one
+    float16 per plan entry, values as two float16 parts after a power-of-two
+    scale per value column). Value columns spanning 10^-30 .. 10^30, a zero
+    column and a column mixing magnitudes 2^-40 .. 1 must each keep the 1e-3
+    bound relative to their own largest output; at eps = 0.004 the plan is
+    nearly a permutation, so single entries carry the rounding (2^-11 of an
+    entry at most). Shape: several 32-column tiles with ragged rows, columns
+    and value width (k = 21)."""
+    from dataclasses import replace
+    w = replace(W.CASES[3].scaled(700, 900, 1), eps=eps)
+    say(f"half-precision form eps={eps} n={w.n} m={w.m} d={w.d} {w.dtype}")
+    inp = W.make_inputs(w, k=21)
+    x, y, a, b = dev(inp)
+    f, g, _ = sk.solve(x, y, a, b, w.eps, 30, w.mode)
+    f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng([eps > 0.01, 21])
+    scales = 10.0 ** np.linspace(-30, 30, 21)
+    for Vn, nrows in ((inp.V, w.m), (inp.U, w.n)):
+        Vn *= scales[None, :].astype(np.float32)
+        Vn[:, 3] = 0.0
+        Vn[:, 7] = (rng.standard_normal(nrows) * 2.0 ** rng.integers(-40, 1, nrows)).astype(np.float32)
+    V, U = torch.from_numpy(inp.V).to(DEV), torch.from_numpy(inp.U).to(DEV)
+    PV = sk.transport_apply(x, y, a, b, f, g, w.eps, V).cpu().numpy().astype(np.float64)
+    PtU = sk.transport_apply(x, y, a, b, f, g, w.eps, U, transpose=True).cpu().numpy().astype(np.float64)
+    ref1 = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.V)
+    ref2 = oracle.apply(inp.x64(), inp.y64(), inp.a, inp.b, f64, g64, w.eps, inp.U, transpose=True)
+    for out, ref, what in ((PV, ref1, "P.V"), (PtU, ref2, "P^T.U")):
+        assert np.all(out[:, 3] == 0.0)
+        den = np.abs(ref).max(axis=0)
+        live = den > 0
+        col = np.abs(out - ref).max(axis=0)[live] / den[live]
+        say(f"  {what}: worst column rel err {col.max():.3e} (column {int(np.argmax(col))})")
+        assert col.max() <= tol_rel(w)
+    gr = sk.eot_grad_x(x, y, a, b, g, w.eps).cpu().numpy()
+    refg = oracle.grad_x(inp.x64(), inp.y64(), inp.a, inp.b, g64, w.eps)
+    eg = np.abs(gr - refg).max() / np.abs(refg).max()
+    say(f"  grad rel err {eg:.3e}")
+    assert eg <= tol_rel(w)
+
+
 SMALL_AUX_CASES = [
     # (config key, n, m, k, dtype or None, d or None, potentials): shapes the one-launch
     # gradient and applications serve; "solve" = a 10-iteration solve's pair,
