@@ -266,7 +266,8 @@ Scalars scalars(double eps) {
 struct AuxPlan {
   Path path;
   int nkb;
-  int kv, nobt, nob, nchunks, pp, vp;  // pp = 1: half-precision form
+  int kv, nobt, nob, nchunks, pp, vp;
+  bool half;  // float16 parts of entries and values (else bf16 parts)
   int wq;  // weighted application: tangent record arrays (0: unweighted)
   int64_t nr, nc;
   PassPlan pl;
@@ -285,7 +286,7 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
   if (ap.path == Path::Mfma || ap.path == Path::Gemm) {
     const bool gemm = ap.path == Path::Gemm;
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
-    pv_parts(dtype, grad || weighted, gemm || weighted, precise, ap.pp, ap.vp);
+    pv_parts(dtype, grad || weighted, gemm || weighted, precise, ap.pp, ap.vp, ap.half);
     const int blocks = (int)((kv + 31) / 32);
     ap.nob = weighted ? pv_wide_nob(blocks, ap.vp, true) : pv_nob(gemm, blocks, ap.vp);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
@@ -313,7 +314,7 @@ AuxWsM layout_aux_m(void* ws, const AuxPlan& ap, int64_t n, int64_t m, int64_t d
   L.y = carve_side_m(c, m, ap.nkb, 1);
   L.vtiles = mfma_padded_count(ap.nc) / 32;
   L.vfrag = c.take<bf16x8>((size_t)L.vtiles * ap.nobt * ap.vp * 2 * 64);
-  if (ap.pp == 1) L.vmax = c.take<unsigned>((size_t)ap.kv);
+  if (ap.half) L.vmax = c.take<unsigned>((size_t)ap.kv);
   // (mu, S) pairs, padded to 16 bytes, then the value partials
   const size_t slots_rows = (size_t)ap.nchunks * ap.pl.splits * ap.nr;
   const size_t part_floats = ap.pl.splits > 1
@@ -349,13 +350,13 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
   if (e != hipSuccess) return hip_fail(e, "prep");
   const float* shift = L.c.shift;  // centering shift of both clouds (exact for bf16 points)
   e = launch_pack_values(vsrc, vsrc_bf16, ap.nc, ap.kv, grad ? shift : nullptr, ap.vp, ap.nobt,
-                         L.vtiles, ap.pp == 1 ? L.vmax : nullptr, L.vfrag, s);
+                         L.vtiles, ap.half ? L.vmax : nullptr, L.vfrag, s);
   if (e != hipSuccess) return hip_fail(e, "value packing");
   const SideM& R = transpose ? L.y : L.x;
   const SideM& C = transpose ? L.x : L.y;
   PvArgs pa{};
   pa.rows = R.row_rec; pa.cols = C.col_rec; pa.bias_col = C.bias[0]; pa.vfrag = L.vfrag;
-  pa.vmax = ap.pp == 1 ? L.vmax : nullptr;
+  pa.vmax = ap.half ? L.vmax : nullptr;
   pa.nobt = ap.nobt; pa.kv = ap.kv; pa.out = out;
   pa.hrow = R.hval[0]; pa.wrow = a; pa.xrow = x; pa.xbf16 = dtype == SK_BF16; pa.shift = shift;
   pa.grad = grad ? 1 : 0;
@@ -371,7 +372,7 @@ int run_aux_m(const AuxPlan& ap, const AuxWsM& L, const void* x, const void* y, 
     pa.wrec_stride = stride;
     pa.qoff = L.qoff;
   }
-  e = launch_pv(pa, ap.path == Path::Gemm, ap.nkb, ap.nob, ap.pp, ap.vp, ap.pl, s);
+  e = launch_pv(pa, ap.path == Path::Gemm, ap.nkb, ap.nob, ap.pp, ap.vp, ap.half, ap.pl, s);
   if (e != hipSuccess) return hip_fail(e, grad ? "grad" : "apply");
   return SK_OK;
 }

@@ -25,13 +25,16 @@
 // products kept leave out terms of order 2^-22 and below: float32 accuracy;
 // bf16 points on the GEMM-tiled kernels: two parts of the entries (2^-16)
 // and two of the values for P V, or one exact part of the bf16 points for
-// the gradient). The register-resident kernel takes bf16 points in the
-// half-precision form (PP = 1): as the attention output of FlashAttention
-// feeds its probabilities to the second product in 16-bit form, each entry
-// is one float16 (11 significant bits, rounded to nearest: relative error
-// <= 2^-11, within the 1e-3 bound of bf16 inputs), and the values are two
-// float16 parts (22 bits) after an exact power-of-two scale per value column
-// that puts the column's largest magnitude in [2^13, 2^14). float16's range
+// the gradient). The register-resident kernel runs in the half-precision form
+// (H): as the attention output of FlashAttention feeds its probabilities to
+// the second product in 16-bit form, the entries are float16 parts (rounded
+// to nearest; bf16 points: one part, 11 significant bits, relative error
+// <= 2^-11, within the 1e-3 bound of bf16 inputs; float32 points: two parts,
+// the second the rounded remainder, 22 bits), and the values are float16
+// parts (bf16 points: two for applications, one, exact, for the gradient's
+// points; float32 points: two) after an exact power-of-two scale per value
+// column that puts the column's largest magnitude in [2^13, 2^14); products
+// of combined order below the larger part count are kept. float16's range
 // is kept by the stabilization below: the entries of a row are biased so the
 // running maximum term is 2^8 and stay below 2^15; terms 2^22 below the
 // maximum reach float16's subnormals, where the absolute error 2^-33 of the
@@ -188,11 +191,13 @@ __device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& ac
   return s0 + s1;
 }
 
-// Half-precision form of pv_probs: the entries (terms < 2^15) as one float16
-// part each, rounded to nearest (v_cvt_pk_f16_f32), and their float32 sum (SUM).
-template <bool SUM>
+// Half-precision form of pv_probs: the entries (terms < 2^15) as PP float16
+// parts each, rounded to nearest (v_cvt_pk_f16_f32; the second part is the
+// rounded remainder v - part 1, exact in float32), and their float32 sum (SUM).
+template <int PP, bool SUM>
 __device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& acc, float e, float off,
-                                                                 f16x8 (&P)[2]) {
+                                                                 f16x8 (&P)[PP][2]) {
+  static_assert(PP == 1 || PP == 2, "one or two float16 parts");
   float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
@@ -203,25 +208,35 @@ __device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& 
       s1 = r == 0 ? v1 : s1 + v1;
     }
     const f16x2 h = {(_Float16)v0, (_Float16)v1};
-    P[r >> 3][r & 7] = h[0];
-    P[r >> 3][(r & 7) + 1] = h[1];
+    P[0][r >> 3][r & 7] = h[0];
+    P[0][r >> 3][(r & 7) + 1] = h[1];
+    if constexpr (PP == 2) {
+      const f16x2 l = {(_Float16)(v0 - (float)h[0]), (_Float16)(v1 - (float)h[1])};
+      P[1][r >> 3][r & 7] = l[0];
+      P[1][r >> 3][(r & 7) + 1] = l[1];
+    }
   }
   return s0 + s1;
 }
 
-// O[ob] += V[ob] x P in float16: the entries' one part against each of the VP
-// value parts (fragments hold float16 bits in the half-precision form).
-template <int NOB, int VP>
-__device__ __attribute__((always_inline)) inline void pv_mfma_h(const VTile<NOB, VP>& vt, const f16x8 (&P)[2],
+// O[ob] += V[ob] x P in float16 over the products (pp, vp) of combined order
+// below max(PP, VP) (fragments hold float16 bits in the half-precision form).
+template <int NOB, int PP, int VP>
+__device__ __attribute__((always_inline)) inline void pv_mfma_h(const VTile<NOB, VP>& vt, const f16x8 (&P)[PP][2],
                                                                 f32x16 (&O)[NOB]) {
+  constexpr int KMAX = PP > VP ? PP : VP;
 #pragma unroll
   for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-    for (int vp = 0; vp < VP; ++vp)
+    for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        O[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vt.v[ob][vp][kb]), P[kb], O[ob],
-                                                       0, 0, 0);
+      for (int vp = 0; vp < VP; ++vp)
+        if (pp + vp < KMAX) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            O[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vt.v[ob][vp][kb]), P[pp][kb],
+                                                           O[ob], 0, 0, 0);
+        }
 }
 
 // Weighted plan entries of one score tile: 2^{e acc + off} * q (q: the
@@ -345,7 +360,7 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
 // Register-resident rows (record widths up to 8 K blocks): each wave keeps RB
 // blocks of 32 row records and streams column tiles and their value fragments
 // from memory, one tile ahead.
-template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD>
+template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD, bool H>
 __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
@@ -381,18 +396,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
   }
 
   // Plan entries of a scored tile, then their products with the tile's values
-  // (PP = 1: the half-precision form).
-  constexpr bool H = PP == 1;
+  // (H: the half-precision form).
   auto entries_work = [&](const f32x16 (&acc)[RB], const VTile<NOB, VP>& vt) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const f32x16 a1[1] = {acc[rb]};
       const float off = pv_shift<1, NOB, H>(a1, e, mu[rb], S[rb], O[rb]);
       if constexpr (H) {
-        f16x8 P[2];
-        if constexpr (GRAD) S[rb] += pv_probs_h<true>(acc[rb], e, off, P);
-        else pv_probs_h<false>(acc[rb], e, off, P);
-        pv_mfma_h<NOB, VP>(vt, P, O[rb]);
+        f16x8 P[PP][2];
+        if constexpr (GRAD) S[rb] += pv_probs_h<PP, true>(acc[rb], e, off, P);
+        else pv_probs_h<PP, false>(acc[rb], e, off, P);
+        pv_mfma_h<NOB, PP, VP>(vt, P, O[rb]);
       } else {
         bf16x8 P[PP][2];
         if constexpr (GRAD) S[rb] += pv_probs<PP, true>(acc[rb], e, off, P);
@@ -1223,31 +1237,30 @@ __global__ __launch_bounds__(256) void k_pack_tangent(const float* __restrict__ 
 // Row blocks per wave of the resident kernel: two where registers allow.
 constexpr int pv_rb(int nkb, int nob, int vp) { return (nkb <= 4 && nob * vp <= 2) ? 2 : 1; }
 
-// The gradient / application choice is a template argument (no branch in the
-// tile loop); bf16 points use one value part for the gradient (the points)
-// and two for applications, float32 points three for both.
-template <int NKB, int RB, int NOB, int PP, int VP>
-bool try_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t s) {
+// The form, the part counts and the gradient / application choice are
+// template arguments (no branch in the tile loop). Instantiated: the half
+// form's bf16-point application (1, 2) and gradient (1, 1) and float32-point
+// application and gradient (2, 2); the bf16-part form's applications (3, 3)
+// and (2, 2), which the Hessian-vector product's CG uses.
+template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD, bool H>
+bool try_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& grid, hipStream_t s) {
   if constexpr (pv_rb(NKB, NOB, VP) != RB) {
     return false;
   } else {
-    if (pp != PP || vp != VP) return false;
-    if (a.grad) {
-      if constexpr (VP != 2) k_pv_mfma<NKB, RB, NOB, PP, VP, true><<<grid, kThreads, 0, s>>>(a);
-      else return false;
-    } else {
-      if constexpr (VP != 1) k_pv_mfma<NKB, RB, NOB, PP, VP, false><<<grid, kThreads, 0, s>>>(a);
-      else return false;
-    }
+    if (pp != PP || vp != VP || half != H || (a.grad != 0) != GRAD) return false;
+    k_pv_mfma<NKB, RB, NOB, PP, VP, GRAD, H><<<grid, kThreads, 0, s>>>(a);
     return true;
   }
 }
 
 template <int NKB, int RB, int NOB>
-hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, const dim3& grid, hipStream_t s) {
-  if (try_pv_mfma<NKB, RB, NOB, 3, 3>(a, pp, vp, grid, s) || try_pv_mfma<NKB, RB, NOB, 2, 2>(a, pp, vp, grid, s) ||
-      try_pv_mfma<NKB, RB, NOB, 2, 1>(a, pp, vp, grid, s) || try_pv_mfma<NKB, RB, NOB, 1, 2>(a, pp, vp, grid, s) ||
-      try_pv_mfma<NKB, RB, NOB, 1, 1>(a, pp, vp, grid, s))
+hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& grid, hipStream_t s) {
+  if (try_pv_mfma<NKB, RB, NOB, 1, 2, false, true>(a, pp, vp, half, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 1, 1, true, true>(a, pp, vp, half, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 2, 2, false, true>(a, pp, vp, half, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 2, 2, true, true>(a, pp, vp, half, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 3, 3, false, false>(a, pp, vp, half, grid, s) ||
+      try_pv_mfma<NKB, RB, NOB, 2, 2, false, false>(a, pp, vp, half, grid, s))
     return hipGetLastError();
   return hipErrorInvalidValue;
 }
@@ -1291,13 +1304,14 @@ hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& gri
 
 }  // namespace
 
-void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp) {
-  if (dtype == 0) {
+void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp, bool& half) {
+  half = !gemm && !precise;
+  if (half) {  // float16 parts
+    pp = dtype == 0 ? 2 : 1;
+    vp = (dtype != 0 && grad) ? 1 : 2;
+  } else if (dtype == 0) {
     pp = 3;
     vp = 3;
-  } else if (!gemm && !precise) {
-    pp = 1;  // half-precision form
-    vp = grad ? 1 : 2;
   } else {
     pp = 2;
     vp = grad ? 1 : 2;
@@ -1402,7 +1416,7 @@ PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, in
   return pl;
 }
 
-hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                           const PassPlan& pl, hipStream_t s) {
   const dim3 grid(pl.row_blocks, pl.splits, a.nchunks);
   if (gemm) {
@@ -1418,27 +1432,28 @@ hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, 
   const int rb = pv_rb(nkb, nob, vp);
   const int key = nkb * 100 + rb * 10 + nob;
   switch (key) {
-    case 111: return run_pv_mfma<1, 1, 1>(a, pp, vp, grid, s);
-    case 121: return run_pv_mfma<1, 2, 1>(a, pp, vp, grid, s);
-    case 122: return run_pv_mfma<1, 2, 2>(a, pp, vp, grid, s);
-    case 112: return run_pv_mfma<1, 1, 2>(a, pp, vp, grid, s);
-    case 221: return run_pv_mfma<2, 2, 1>(a, pp, vp, grid, s);
-    case 222: return run_pv_mfma<2, 2, 2>(a, pp, vp, grid, s);
-    case 211: return run_pv_mfma<2, 1, 1>(a, pp, vp, grid, s);
-    case 212: return run_pv_mfma<2, 1, 2>(a, pp, vp, grid, s);
-    case 421: return run_pv_mfma<4, 2, 1>(a, pp, vp, grid, s);
-    case 422: return run_pv_mfma<4, 2, 2>(a, pp, vp, grid, s);
-    case 411: return run_pv_mfma<4, 1, 1>(a, pp, vp, grid, s);
-    case 412: return run_pv_mfma<4, 1, 2>(a, pp, vp, grid, s);
-    case 811: return run_pv_mfma<8, 1, 1>(a, pp, vp, grid, s);
-    case 812: return run_pv_mfma<8, 1, 2>(a, pp, vp, grid, s);
+    case 111: return run_pv_mfma<1, 1, 1>(a, pp, vp, half, grid, s);
+    case 121: return run_pv_mfma<1, 2, 1>(a, pp, vp, half, grid, s);
+    case 122: return run_pv_mfma<1, 2, 2>(a, pp, vp, half, grid, s);
+    case 112: return run_pv_mfma<1, 1, 2>(a, pp, vp, half, grid, s);
+    case 221: return run_pv_mfma<2, 2, 1>(a, pp, vp, half, grid, s);
+    case 222: return run_pv_mfma<2, 2, 2>(a, pp, vp, half, grid, s);
+    case 211: return run_pv_mfma<2, 1, 1>(a, pp, vp, half, grid, s);
+    case 212: return run_pv_mfma<2, 1, 2>(a, pp, vp, half, grid, s);
+    case 421: return run_pv_mfma<4, 2, 1>(a, pp, vp, half, grid, s);
+    case 422: return run_pv_mfma<4, 2, 2>(a, pp, vp, half, grid, s);
+    case 411: return run_pv_mfma<4, 1, 1>(a, pp, vp, half, grid, s);
+    case 412: return run_pv_mfma<4, 1, 2>(a, pp, vp, half, grid, s);
+    case 811: return run_pv_mfma<8, 1, 1>(a, pp, vp, half, grid, s);
+    case 812: return run_pv_mfma<8, 1, 2>(a, pp, vp, half, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                      const PassPlan& pl, hipStream_t s) {
-  hipError_t e = launch_pv_main(a, gemm, nkb, nob, pp, vp, pl, s);
+  if (half && gemm) return hipErrorInvalidValue;
+  hipError_t e = launch_pv_main(a, gemm, nkb, nob, pp, vp, half, pl, s);
   if (e != hipSuccess || pl.splits == 1) return e;
   const int cw = nob * 32;
   const int64_t total = (int64_t)a.nchunks * a.nr * cw;

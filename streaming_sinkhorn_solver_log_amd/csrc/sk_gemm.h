@@ -20,15 +20,14 @@ int gemm_tile_choice();
 PassPlan plan_gemm_pass(int64_t nr, int64_t nc);
 hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool scaled, const PassPlan& pl,
                            hipStream_t s);
-// Transport application / gradient kernels. pv_parts: bf16 parts of the plan
-// entries (pp) and of the values (vp) for a storage type and operation; pp = 1
-// is the half-precision form of the register-resident kernel (bf16 points,
-// not GEMM-tiled, unless precise: one float16 part per entry, vp float16
-// parts of the values scaled per column).
-void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp);
+// Transport application / gradient kernels. pv_parts: parts of the plan
+// entries (pp) and of the values (vp) for a storage type and operation, and
+// the form: half (the register-resident kernel unless precise) = float16
+// parts, the values scaled per column; else bf16 parts.
+void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp, bool& half);
 int pv_nob(bool gemm, int nobt, int vp);  // value blocks per launch chunk
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
-hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp,
+hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                      const PassPlan& pl, hipStream_t s);
 // Tangent records of n rows (T n x d float32) for the weighted application:
 // one record array (float32 points) or two (bf16 points, part_stride bf16x8
