@@ -149,7 +149,7 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
  * Precision of the plan entries in the value products: bf16 points with
  * d <= 128, one float16 per entry (relative error <= 2^-11, inside the 1e-3
  * bound of bf16 inputs); float32 points with d <= 21, two float16 parts per
- * entry (2^-22); in both, two float16 parts of each value after an exact
+ * entry (2^-21); in both, two float16 parts of each value after an exact
  * power-of-two scale per value column (values below 2^-29 of their column's
  * largest magnitude fall into float16's subnormal range). Larger d: bf16
  * points two bf16 parts of each entry (2^-16) and value, float32 points

@@ -192,8 +192,10 @@ __device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& ac
 }
 
 // Half-precision form of pv_probs: the entries (terms < 2^15) as PP float16
-// parts each, rounded to nearest (v_cvt_pk_f16_f32; the second part is the
-// rounded remainder v - part 1, exact in float32), and their float32 sum (SUM).
+// parts each (v_cvt_pk_f16_f32), and their float32 sum (SUM). One part: the
+// entry rounded to nearest. Two parts: the entry truncated to float16's 11
+// significant bits (exact in float16 in its normal range), then the exact
+// float32 remainder rounded to nearest: relative error <= 2^-21.
 template <int PP, bool SUM>
 __device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& acc, float e, float off,
                                                                  f16x8 (&P)[PP][2]) {
@@ -207,11 +209,17 @@ __device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& 
       s0 = r == 0 ? v0 : s0 + v0;
       s1 = r == 0 ? v1 : s1 + v1;
     }
-    const f16x2 h = {(_Float16)v0, (_Float16)v1};
-    P[0][r >> 3][r & 7] = h[0];
-    P[0][r >> 3][(r & 7) + 1] = h[1];
-    if constexpr (PP == 2) {
-      const f16x2 l = {(_Float16)(v0 - (float)h[0]), (_Float16)(v1 - (float)h[1])};
+    if constexpr (PP == 1) {
+      const f16x2 h = {(_Float16)v0, (_Float16)v1};
+      P[0][r >> 3][r & 7] = h[0];
+      P[0][r >> 3][(r & 7) + 1] = h[1];
+    } else {
+      const float t0 = __uint_as_float(__float_as_uint(v0) & 0xFFFFE000u);
+      const float t1 = __uint_as_float(__float_as_uint(v1) & 0xFFFFE000u);
+      const f16x2 h = {(_Float16)t0, (_Float16)t1};
+      const f16x2 l = {(_Float16)(v0 - t0), (_Float16)(v1 - t1)};
+      P[0][r >> 3][r & 7] = h[0];
+      P[0][r >> 3][(r & 7) + 1] = h[1];
       P[1][r >> 3][r & 7] = l[0];
       P[1][r >> 3][(r & 7) + 1] = l[1];
     }
