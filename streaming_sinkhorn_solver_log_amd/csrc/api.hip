@@ -286,8 +286,11 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
   if (ap.path == Path::Mfma || ap.path == Path::Gemm) {
     const bool gemm = ap.path == Path::Gemm;
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
-    pv_parts(dtype, grad || weighted, gemm || weighted, precise, ap.pp, ap.vp, ap.half);
     const int blocks = (int)((kv + 31) / 32);
+    // the float16 form runs on the register-resident kernel and, for value
+    // widths above 64, on the wide kernel (not in the weighted application)
+    const bool half_kernel = !gemm || (!weighted && blocks > 2);
+    pv_parts(dtype, grad || weighted, half_kernel, precise, ap.pp, ap.vp, ap.half);
     ap.nob = weighted ? pv_wide_nob(blocks, ap.vp, true) : pv_nob(gemm, blocks, ap.vp);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
     ap.nobt = ap.nchunks * ap.nob;

@@ -820,8 +820,9 @@ __device__ __attribute__((always_inline)) inline void pvw_issue_stage(
   }
 }
 
-template <int PP, int VP, int NOBW, int WQ>
+template <int PP, int VP, int NOBW, int WQ, bool H>
 __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb, int col_last) {
+  static_assert(!(H && WQ > 0), "the weighted application keeps bf16 parts");
   using Stg = PvwStage<WQ>;
   constexpr int R = Stg::kRing;
   constexpr int PER = Stg::kPerWave;
@@ -950,13 +951,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
       if (half == 0) lds.tmax[sch][srt][li] = tm;
       __syncthreads();
       // the same lazy shift in every wave: raise a row's maximum only when a
-      // term would exceed 2^16
+      // term would exceed 2^16 (H: 2^15 with the bias 2^kHalfBias)
       float sc[2];
       bool raised = false;
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const float t = fmaxf(lds.tmax[0][rt][li], lds.tmax[1][rt][li]);
-        const bool raise = e * (t - mu[rt]) > kLazy;
+        const bool raise = e * (t - mu[rt]) > (H ? kHalfLazy : kLazy);
         const float mn = raise ? t : mu[rt];
         sc[rt] = fast_exp2(e * (mu[rt] - mn));
         mu[rt] = mn;
@@ -971,17 +972,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
             for (int r = 0; r < 16; ++r) O[rt][ob][r] *= sc[rt];
         Sp *= sc[srt];
       }
-      const float off = -e * mu[srt];
+      const float off = H ? fmaf(-e, mu[srt], kHalfBias) : -e * mu[srt];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        bf16x8 P[PP][2];
-        if constexpr (WQ > 0) pv_probs_w<PP>(acc[ct], accq[ct], qoff[srt], e, off, P);
-        else if (p.grad) Sp += pv_probs<PP, true>(acc[ct], e, off, P);
-        else pv_probs<PP, false>(acc[ct], e, off, P);
+        if constexpr (H) {
+          f16x8 P[PP][2];
+          if (p.grad) Sp += pv_probs_h<PP, true>(acc[ct], e, off, P);
+          else pv_probs_h<PP, false>(acc[ct], e, off, P);
 #pragma unroll
-        for (int pp = 0; pp < PP; ++pp)
+          for (int pp = 0; pp < PP; ++pp)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) lds.P[srt][2 * sch + ct][pp][kb][lane] = P[pp][kb];
+            for (int kb = 0; kb < 2; ++kb)
+              lds.P[srt][2 * sch + ct][pp][kb][lane] = __builtin_bit_cast(bf16x8, P[pp][kb]);
+        } else {
+          bf16x8 P[PP][2];
+          if constexpr (WQ > 0) pv_probs_w<PP>(acc[ct], accq[ct], qoff[srt], e, off, P);
+          else if (p.grad) Sp += pv_probs<PP, true>(acc[ct], e, off, P);
+          else pv_probs<PP, false>(acc[ct], e, off, P);
+#pragma unroll
+          for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) lds.P[srt][2 * sch + ct][pp][kb][lane] = P[pp][kb];
+        }
       }
       __syncthreads();
       // a column block can overhang the padded columns by up to 3 tiles:
@@ -1017,9 +1029,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
               for (int vp = 0; vp < VP; ++vp)
                 if (pp + vp < KMAX) {
 #pragma unroll
-                  for (int kb = 0; kb < 2; ++kb)
-                    O[rt][ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[ob][vp][kb], Pf[rt][pp][kb],
-                                                                        O[rt][ob], 0, 0, 0);
+                  for (int kb = 0; kb < 2; ++kb) {
+                    if constexpr (H)
+                      O[rt][ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, cur.v[ob][vp][kb]),
+                                                                         __builtin_bit_cast(f16x8, Pf[rt][pp][kb]),
+                                                                         O[rt][ob], 0, 0, 0);
+                    else
+                      O[rt][ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[ob][vp][kb], Pf[rt][pp][kb],
+                                                                          O[rt][ob], 0, 0, 0);
+                  }
                 }
       }
     }
@@ -1280,24 +1298,35 @@ hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, const dim3& gr
   return hipGetLastError();
 }
 
+// Instantiated: the weighted application (bf16 parts); the half form's
+// bf16-point gradient (1, 1) and application (1, 2) and float32-point ones
+// (2, 2); the bf16-part form's (3, 3) and (2, 2) applications (the Hessian-
+// vector product's CG).
 template <int NOBW>
-hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, int wq, const dim3& grid, hipStream_t s) {
+hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, bool half, int wq, const dim3& grid,
+                       hipStream_t s) {
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
   if constexpr (NOBW <= 2) {
-    if (wq == 1 && pp == 3 && vp == 3) {  // float32 points: one six-slot tangent record
-      k_pv_wide<3, 3, NOBW, 1><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    if (wq == 1 && pp == 3 && vp == 3 && !half) {  // float32 points: one six-slot tangent record
+      k_pv_wide<3, 3, NOBW, 1, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
       return hipGetLastError();
     }
-    if (wq == 2 && pp == 2 && vp == 1) {  // bf16 points: two bf16 parts of the tangent
-      k_pv_wide<2, 1, NOBW, 2><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    if (wq == 2 && pp == 2 && vp == 1 && !half) {  // bf16 points: two bf16 parts of the tangent
+      k_pv_wide<2, 1, NOBW, 2, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
       return hipGetLastError();
     }
   }
   if (wq != 0) return hipErrorInvalidValue;
-  if (pp == 3 && vp == 3) k_pv_wide<3, 3, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-  else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-  else if (pp == 2 && vp == 1) k_pv_wide<2, 1, NOBW, 0><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-  else return hipErrorInvalidValue;
+  if (half) {
+    if (pp == 1 && vp == 1) k_pv_wide<1, 1, NOBW, 0, true><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else if (pp == 1 && vp == 2) k_pv_wide<1, 2, NOBW, 0, true><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0, true><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else return hipErrorInvalidValue;
+  } else {
+    if (pp == 3 && vp == 3) k_pv_wide<3, 3, NOBW, 0, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    else return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1312,8 +1341,8 @@ hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& gri
 
 }  // namespace
 
-void pv_parts(int dtype, bool grad, bool gemm, bool precise, int& pp, int& vp, bool& half) {
-  half = !gemm && !precise;
+void pv_parts(int dtype, bool grad, bool half_kernel, bool precise, int& pp, int& vp, bool& half) {
+  half = half_kernel && !precise;
   if (half) {  // float16 parts
     pp = dtype == 0 ? 2 : 1;
     vp = (dtype != 0 && grad) ? 1 : 2;
@@ -1350,9 +1379,9 @@ int pv_gemm_resident(int nob) {
     hipError_t e = hipErrorInvalidValue;
     if (nob == 1) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<1, 3, 3>, kThreads, 0);
     if (nob == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm<2, 3, 3>, kThreads, 0);
-    if (nob == 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 1, 1>, kThreads, 0);
-    if (nob == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 2, 1>, kThreads, 0);
-    if (nob == 16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<2, 1, 4, 0>, kThreads, 0);
+    if (nob == 4) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 1, 1, false>, kThreads, 0);
+    if (nob == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<3, 3, 2, 1, false>, kThreads, 0);
+    if (nob == 16) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_wide<2, 2, 4, 0, false>, kThreads, 0);
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
@@ -1432,9 +1461,9 @@ hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, 
     if (nob == 1) return run_pv_gemm<1>(a, nkb, pp, vp, grid, s);
     if (nob == 2) return run_pv_gemm<2>(a, nkb, pp, vp, grid, s);
     const int wq = a.wrec ? (pp == 3 ? 1 : 2) : 0;
-    if (nob == 4) return run_pv_wide<1>(a, nkb, pp, vp, wq, grid, s);
-    if (nob == 8) return run_pv_wide<2>(a, nkb, pp, vp, wq, grid, s);
-    if (nob == 16) return run_pv_wide<4>(a, nkb, pp, vp, wq, grid, s);
+    if (nob == 4) return run_pv_wide<1>(a, nkb, pp, vp, half, wq, grid, s);
+    if (nob == 8) return run_pv_wide<2>(a, nkb, pp, vp, half, wq, grid, s);
+    if (nob == 16) return run_pv_wide<4>(a, nkb, pp, vp, half, wq, grid, s);
     return hipErrorInvalidValue;
   }
   const int rb = pv_rb(nkb, nob, vp);
@@ -1460,7 +1489,7 @@ hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, 
 
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                      const PassPlan& pl, hipStream_t s) {
-  if (half && gemm) return hipErrorInvalidValue;
+  if (half && gemm && nob < 4) return hipErrorInvalidValue;  // the GEMM-tiled kernels of 1-2 blocks: bf16 parts
   hipError_t e = launch_pv_main(a, gemm, nkb, nob, pp, vp, half, pl, s);
   if (e != hipSuccess || pl.splits == 1) return e;
   const int cw = nob * 32;
