@@ -751,10 +751,14 @@ __global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int 
 // bytes per record) of the 64 row and 128 column records (and of the rows'
 // tangent records) per stage. Each load instruction reads 8 whole 128-byte
 // record chunks (coalesced) into 1 KB of LDS; within record r's 128 bytes the
-// 16-byte piece c (K block c / 2, half c % 2) is stored at position c ^ (r % 8),
-// so that the 32 lanes of an MFMA operand read (records 32 t + li, one piece
-// each) hit distinct banks. Each stage's fragments are read right after the
-// barrier that publishes it, while the previous stage's MFMAs still run.
+// 16-byte piece c (K block c / 2, half c % 2) is stored at position
+// c ^ ((r / 2) % 8), so that an MFMA operand read (records 32 t + li, one
+// piece each) is free of bank conflicts: the LDS serves a 16-byte read 16
+// lanes at a time (256 bytes, all 64 banks), and of 16 consecutive records the
+// even ones start at bank 0 and the odd ones at bank 32, each group of eight
+// meeting every piece position once (with c ^ (r % 8), records r and r + 8
+// collided). Each stage's fragments are read right after the barrier that
+// publishes it, while the previous stage's MFMAs still run.
 constexpr int kPvwRows = 64;
 constexpr int kPvwCols = 128;
 
@@ -777,17 +781,14 @@ struct PvwLds {
 };
 
 // This wave's loads of a stage: K chunk kc of rows [r0, r0 + 64), columns
-// [c0, c0 + 128) and the rows' tangent records, into `dst`. Load q of the
-// stage fills slots [64 q, 64 q + 64): the wave-uniform part of its address
-// is on the scalar unit, each lane adds its record's offset. Row indices
-// clamp to the last row, column indices to the last padded (masked) column.
-// This wave's loads of a stage: K chunk kc of rows [r0, r0 + 64), columns
 // [c0, c0 + 128) and the rows' tangent records, into `dst`. Load q = 4 u +
 // wave covers records [8 q', 8 q' + 8) of its region (rows for u < 2, columns
-// for u < 6, then the tangent arrays); lane l reads piece (l % 8) ^ (l / 8) of
-// record 8 q' + l / 8, which lands at position l % 8 of that record's LDS
-// chunk. Row indices clamp to the last row, column indices to the last padded
-// (masked) column. The uniform part of each address is on the scalar unit.
+// for u < 6, then the tangent arrays; q' and q have the same parity); lane l
+// reads piece (l % 8) ^ ((r / 2) % 8) of record r = 8 q' + l / 8, i.e. piece
+// (l % 8) ^ (4 (q % 2) + l / 16), which lands at position l % 8 of that
+// record's LDS chunk. Row indices clamp to the last row, column indices to
+// the last padded (masked) column. The uniform part of each address is on the
+// scalar unit.
 template <int WQ>
 __device__ __attribute__((always_inline)) inline void pvw_issue_stage(
     unsigned char* dst, const PvArgs& p, int nkb, int col_last, int r0, int c0, int kc, int wave, int lane) {
@@ -796,7 +797,7 @@ __device__ __attribute__((always_inline)) inline void pvw_issue_stage(
   const int64_t rsb = (int64_t)nkb * 32;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int g = lane >> 3;
-  const unsigned piece = (unsigned)((((lane & 7) ^ g)) * 16);
+  const unsigned piece = (unsigned)(((lane & 7) ^ (((wv & 1) << 2) | (g >> 1))) * 16);
   const int64_t kco = (int64_t)kc * 128;
   const unsigned char* rows = static_cast<const unsigned char*>(p.rows) + (int64_t)r0 * rsb + kco;
   const unsigned char* cols = static_cast<const unsigned char*>(p.cols) + (int64_t)c0 * rsb + kco;
@@ -868,7 +869,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
     const unsigned char* rg = lds.ring[st % R];
 #pragma unroll
     for (int kb = 0; kb < kGKb; ++kb) {
-      const int pos = (((2 * kb + half) ^ (li & 7)) * 16) + li * 128;  // piece 2 kb + h of record 32 t + li
+      const int pos = (((2 * kb + half) ^ ((li >> 1) & 7)) * 16) + li * 128;  // piece 2 kb + h of record 32 t + li
       Bs[kb] = *reinterpret_cast<const bf16x8*>(rg + srt * 32 * 128 + pos);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
