@@ -350,18 +350,21 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
   float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);  // 16-byte aligned value partials
   const int64_t slot = (int64_t)z * p.splits + sp;
   if (!active) return;
+  // p.pcw (a multiple of 8, at most CW) value partials per row: the columns
+  // past a narrower value width are not written
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int i = row_base + rb * 32 + li;
     if (i >= p.nr) continue;
     if (half == 0) part_ms[slot * p.nr + i] = make_float2(mu[rb], St[rb]);
-    float* T = part_t + (slot * p.nr + i) * CW;
+    float* T = part_t + (slot * p.nr + i) * p.pcw;
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(T + ob * 32 + 8 * q + 4 * half) =
-            make_float4(O[rb][ob][4 * q], O[rb][ob][4 * q + 1], O[rb][ob][4 * q + 2], O[rb][ob][4 * q + 3]);
+        if (ob * 32 + 8 * q < p.pcw)
+          *reinterpret_cast<float4*>(T + ob * 32 + 8 * q + 4 * half) =
+              make_float4(O[rb][ob][4 * q], O[rb][ob][4 * q + 1], O[rb][ob][4 * q + 2], O[rb][ob][4 * q + 3]);
   }
 }
 
@@ -1491,12 +1494,18 @@ hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, 
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                      const PassPlan& pl, hipStream_t s) {
   if (half && gemm && nob < 4) return hipErrorInvalidValue;  // the GEMM-tiled kernels of 1-2 blocks: bf16 parts
-  hipError_t e = launch_pv_main(a, gemm, nkb, nob, pp, vp, half, pl, s);
-  if (e != hipSuccess || pl.splits == 1) return e;
+  // value partials per (slot, row): a single chunk of the register-resident
+  // or the 1-2 block GEMM-tiled kernels keeps only the value width (rounded
+  // to 8); the wide kernel writes whole chunks
+  PvArgs b = a;
   const int cw = nob * 32;
-  const int64_t total = (int64_t)a.nchunks * a.nr * cw;
+  const bool wide = gemm && nob >= 4;
+  b.pcw = (!wide && a.nchunks == 1 && ((a.kv + 7) & ~7) < cw) ? ((a.kv + 7) & ~7) : cw;
+  hipError_t e = launch_pv_main(b, gemm, nkb, nob, pp, vp, half, pl, s);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t total = (int64_t)b.nchunks * b.nr * b.pcw;
   const int64_t blocks = (total + 255) / 256;
-  k_pv_merge<<<(int)(blocks < 16384 ? blocks : 16384), 256, 0, s>>>(a, cw);
+  k_pv_merge<<<(int)(blocks < 16384 ? blocks : 16384), 256, 0, s>>>(b, b.pcw);
   return hipGetLastError();
 }
 

@@ -73,6 +73,7 @@ struct PvArgs {
   const float* shift;      // grad: centering shift of float32 points (or null)
   int grad;
   float* part;             // split partials: (mu, S) pairs then values, per (chunk, split)
+  int pcw;                 // value partials per (slot, row) (set by launch_pv)
   int nr, nc, row_blocks, nchunks;
   int splits, cols_per_split;
   float escale;
