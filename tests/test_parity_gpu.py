@@ -699,25 +699,35 @@ def test_apply_arbitrary_potentials(sk, key, scale):
     assert eg <= tol_rel(w)
 
 
-@pytest.mark.parametrize("eps", [0.1, 0.004])
-def test_half_precision_form_column_scales(sk, eps):
-    """bf16 points at d = 64 run the transport kernels in half precision (one
-    float16 per plan entry, values as two float16 parts after a power-of-two
-    scale per value column). Value columns spanning 10^-30 .. 10^30, a zero
-    column and a column mixing magnitudes 2^-40 .. 1 must each keep the 1e-3
+HALF_FORM_CASES = [
+    # (config key, eps, k): the transport kernels' float16 form
+    (3, 0.1, 21),     # bf16 d = 64, register-resident kernel
+    (3, 0.004, 21),   # nearly a permutation plan
+    (6, 0.05, 21),    # float32 d = 3 (two float16 parts per entry)
+    (7, 0.1, 100),    # bf16 d = 512, k > 64: the wide kernel
+    (4, 0.2, 100),    # float32 d = 512, the wide kernel
+]
+
+
+@pytest.mark.parametrize("key,eps,k", HALF_FORM_CASES)
+def test_half_precision_form_column_scales(sk, key, eps, k):
+    """The transport kernels' half-precision form (float16 parts of the plan
+    entries, values as two float16 parts after a power-of-two scale per value
+    column). Value columns spanning 10^-30 .. 10^30, a zero column and a
+    column mixing magnitudes 2^-40 .. 1 must each keep the configuration's
     bound relative to their own largest output; at eps = 0.004 the plan is
     nearly a permutation, so single entries carry the rounding (2^-11 of an
-    entry at most). Shape: several 32-column tiles with ragged rows, columns
-    and value width (k = 21)."""
+    entry at most for bf16 points). Shape: several 32-column tiles with
+    ragged rows, columns and value width."""
     from dataclasses import replace
-    w = replace(W.CASES[3].scaled(700, 900, 1), eps=eps)
-    say(f"half-precision form eps={eps} n={w.n} m={w.m} d={w.d} {w.dtype}")
-    inp = W.make_inputs(w, k=21)
+    w = replace(W.CASES[key].scaled(700, 900, 1), eps=eps)
+    say(f"half-precision form cfg={key} eps={eps} k={k} n={w.n} m={w.m} d={w.d} {w.dtype}")
+    inp = W.make_inputs(w, k=k)
     x, y, a, b = dev(inp)
     f, g, _ = sk.solve(x, y, a, b, w.eps, 30, w.mode)
     f64, g64 = f.cpu().numpy().astype(np.float64), g.cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng([eps > 0.01, 21])
-    scales = 10.0 ** np.linspace(-30, 30, 21)
+    rng = np.random.default_rng([key, k, eps > 0.01])
+    scales = 10.0 ** np.linspace(-30, 30, k)
     for Vn, nrows in ((inp.V, w.m), (inp.U, w.n)):
         Vn *= scales[None, :].astype(np.float32)
         Vn[:, 3] = 0.0
