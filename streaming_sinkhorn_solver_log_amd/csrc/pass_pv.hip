@@ -23,18 +23,20 @@
 // three and three; the entries' leading parts are truncations, of relative
 // order 1, 2^-7, 2^-14, the values' are rounded, 1, 2^-8, 2^-16, and the six
 // products kept leave out terms of order 2^-22 and below: float32 accuracy;
-// bf16 points on the GEMM-tiled kernels: two parts of the entries (2^-16)
-// and two of the values for P V, or one exact part of the bf16 points for
-// the gradient). The register-resident kernel runs in the half-precision form
-// (H): as the attention output of FlashAttention feeds its probabilities to
-// the second product in 16-bit form, the entries are float16 parts (rounded
-// to nearest; bf16 points: one part, 11 significant bits, relative error
-// <= 2^-11, within the 1e-3 bound of bf16 inputs; float32 points: two parts,
-// the second the rounded remainder, 22 bits), and the values are float16
-// parts (bf16 points: two for applications, one, exact, for the gradient's
-// points; float32 points: two) after an exact power-of-two scale per value
-// column that puts the column's largest magnitude in [2^13, 2^14); products
-// of combined order below the larger part count are kept. float16's range
+// bf16 points: two parts of the entries (2^-16) and two of the values for
+// P V, or one exact part of the bf16 points for the gradient). That is the
+// form of the 1-2 block GEMM-tiled kernels and of the Hessian-vector
+// product's applications; the register-resident kernel and the wide kernel
+// run in the half-precision form (H): as the attention output of
+// FlashAttention feeds its probabilities to the second product in 16-bit
+// form, the entries are float16 parts (bf16 points: one part rounded to
+// nearest, 11 significant bits, relative error <= 2^-11, within the 1e-3
+// bound of bf16 inputs; float32 points: two parts, the entry truncated to 11
+// bits and the rounded remainder, 2^-21), and the values are float16 parts
+// (bf16 points: two for applications, one, exact, for the gradient's points;
+// float32 points: two) after an exact power-of-two scale per value column
+// that puts the column's largest magnitude in [2^13, 2^14); products of
+// combined order below the larger part count are kept. float16's range
 // is kept by the stabilization below: the entries of a row are biased so the
 // running maximum term is 2^8 and stay below 2^15; terms 2^22 below the
 // maximum reach float16's subnormals, where the absolute error 2^-33 of the
