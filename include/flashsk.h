@@ -147,13 +147,15 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
  * the wide kernel (scores once per 512 values); on small d the scores are
  * recomputed once per 64 values.
  * Precision of the plan entries in the value products (bf16 d <= 128,
- * float32 d <= 21, and any d for k > 64): bf16 points, one float16 per entry
+ * float32 d <= 21, any d for k > 64, float32 points for k <= 32): bf16
+ * points, one float16 per entry
  * (relative error <= 2^-11, inside the 1e-3 bound of bf16 inputs); float32
  * points, two float16 parts per entry (2^-21); in both, two float16 parts of
  * each value after an exact power-of-two scale per value column (values
  * below 2^-29 of their column's largest magnitude fall into float16's
- * subnormal range). Larger d with k <= 64: bf16 points two bf16 parts of
- * each entry (2^-16) and value, float32 points three (float32 accuracy).
+ * subnormal range). Otherwise (larger d, k <= 64; float32 points with
+ * 32 < k <= 64): bf16 points two bf16 parts of each entry (2^-16) and value,
+ * float32 points three (float32 accuracy).
  */
 int sk_transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d,
                        const float* a, const float* b, const float* f, const float* g, double eps,

@@ -287,14 +287,16 @@ AuxPlan plan_aux(int dtype, int64_t n, int64_t m, int64_t d, int64_t kv, bool gr
     const bool gemm = ap.path == Path::Gemm;
     ap.nkb = gemm ? gemm_nkb(dtype, (int)d) : mfma_nkb(dtype, (int)d);
     const int blocks = (int)((kv + 31) / 32);
-    // the float16 form runs on the register-resident kernel and, for value
-    // widths above 64, on the wide kernel (not in the weighted application)
-    const bool half_kernel = !gemm || (!weighted && blocks > 2);
+    // the float16 form runs on the register-resident kernel and, on the
+    // GEMM path, on the wide kernel (value widths above 64) and, for float32
+    // points, the 8-wave kernel (one value block); not in the weighted
+    // application
+    const bool half_kernel = !gemm || (!weighted && (blocks > 2 || (blocks == 1 && dtype == SK_F32)));
     pv_parts(dtype, grad || weighted, half_kernel, precise, ap.pp, ap.vp, ap.half);
     ap.nob = weighted ? pv_wide_nob(blocks, ap.vp, true) : pv_nob(gemm, blocks, ap.vp);
     ap.nchunks = (blocks + ap.nob - 1) / ap.nob;
     ap.nobt = ap.nchunks * ap.nob;
-    ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks);
+    ap.pl = plan_pv(gemm, ap.nr, ap.nc, ap.nkb, ap.nob, ap.vp, ap.nchunks, ap.half);
   }
   return ap;
 }

@@ -610,7 +610,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_gemm(const PvArgs p, int nkb
 // two column waves of a row group merge their partials through LDS at the end.
 using PvGeo = Geo<2, 4, 4>;
 
-template <int PP, int VP>
+template <int PP, int VP, bool H>
 __global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int nkb, int col_last) {
   using G = PvGeo;
   constexpr int WRT = 2, WCT = 4, kWaveRows = 64;
@@ -691,18 +691,26 @@ __global__ __launch_bounds__(PvGeo::kNT, 1) void k_pv_gemm8(const PvArgs p, int 
       }
 #pragma unroll
       for (int rb = 0; rb < WRT; ++rb) {
-        const float off = pv_shift<WCT, 1>(acc[rb], e, mu[rb], S[rb], O[rb]);
+        const float off = pv_shift<WCT, 1, H>(acc[rb], e, mu[rb], S[rb], O[rb]);
 #pragma unroll
         for (int ct = 0; ct < WCT; ++ct) {
-          bf16x8 P[PP][2];
-          if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb][ct], e, off, P);
-          else pv_probs<PP, false>(acc[rb][ct], e, off, P);
           // a column block can overhang the padded columns by up to 7 tiles:
           // those columns are masked, so any zero-valued tile serves, here
           // the last padded one
           VTile<1, VP> vt;
-          load_vtile<1, VP>(vt, p, min((cb >> 5) + ct, col_last >> 5), ob0, lane);
-          pv_mfma<1, PP, VP>(vt, P, O[rb]);
+          if constexpr (H) {
+            f16x8 P[PP][2];
+            if (p.grad) S[rb] += pv_probs_h<PP, true>(acc[rb][ct], e, off, P);
+            else pv_probs_h<PP, false>(acc[rb][ct], e, off, P);
+            load_vtile<1, VP>(vt, p, min((cb >> 5) + ct, col_last >> 5), ob0, lane);
+            pv_mfma_h<1, PP, VP>(vt, P, O[rb]);
+          } else {
+            bf16x8 P[PP][2];
+            if (p.grad) S[rb] += pv_probs<PP, true>(acc[rb][ct], e, off, P);
+            else pv_probs<PP, false>(acc[rb][ct], e, off, P);
+            load_vtile<1, VP>(vt, p, min((cb >> 5) + ct, col_last >> 5), ob0, lane);
+            pv_mfma<1, PP, VP>(vt, P, O[rb]);
+          }
         }
       }
     }
@@ -1297,9 +1305,10 @@ hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& g
   return hipErrorInvalidValue;
 }
 
-hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, const dim3& grid, hipStream_t s) {
+hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, bool half, const dim3& grid, hipStream_t s) {
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
-  if (pp == 3 && vp == 3) k_pv_gemm8<3, 3><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
+  if (!half && pp == 3 && vp == 3) k_pv_gemm8<3, 3, false><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
+  else if (half && pp == 2 && vp == 2) k_pv_gemm8<2, 2, true><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -1399,7 +1408,11 @@ int pv_gemm_resident(int nob) {
 }  // namespace
 
 namespace {
-bool pv_tile8(bool gemm, int nob, int vp) { return gemm && nob == 1 && vp == 3; }
+// one value block on the GEMM path: the 8-wave tile for float32 points, in
+// the bf16-part (vp = 3) or the float16 form (bf16 points stay on the
+// 128 x 128 tile: 0.73 ms there at d = 512, n = m = 20k, the same in the
+// float16 form on the 8-wave tile, 1.3 ms in bf16 parts)
+bool pv_tile8(bool gemm, int nob, int vp, bool half) { return gemm && nob == 1 && (vp == 3 || half); }
 
 // Resident workgroups of the 8-wave GEMM-tiled kernel (per device, computed once).
 int pv_gemm8_resident() {
@@ -1411,7 +1424,7 @@ int pv_gemm8_resident() {
   int v = slot ? slot->load(std::memory_order_relaxed) : 0;
   if (v == 0) {
     int cus = 0, per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm8<3, 3>, PvGeo::kNT, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm8<3, 3, false>, PvGeo::kNT, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
@@ -1423,14 +1436,14 @@ int pv_gemm8_resident() {
 }
 }  // namespace
 
-PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks) {
+PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks, bool half) {
   PassPlan pl{};
-  // GEMM-tiled with one value block and float32 (three-part) values: the
-  // 256 x 256 tile of 8 waves (k_pv_gemm8). Its epilogue spills, which only
-  // the long K loop of the six-part float32 records amortizes (d = 512:
-  // P V 10.1 -> 6.2 ms); bf16 records stay on the 128 x 128 tile (d = 512:
-  // 1.0 ms there, 1.3 ms on the larger one).
-  const bool tile8 = pv_tile8(gemm, nob, vp);
+  // GEMM-tiled with one value block and float32 points: the 256 x 256 tile
+  // of 8 waves (k_pv_gemm8). Its epilogue spills, which only the long K loop
+  // of the six-part float32 records amortizes (d = 512: P V 10.1 -> 6.2 ms
+  // in bf16 parts, 5.3 -> 4.7 ms in the float16 form, which spills less);
+  // bf16 records stay on the 128 x 128 tile.
+  const bool tile8 = pv_tile8(gemm, nob, vp, half);
   const bool wide = gemm && nob >= 4;
   pl.rows_per_block = tile8 ? PvGeo::kRows : (wide ? kPvwRows : (gemm ? kGRows : 4 * pv_rb(nkb, nob, vp) * 32));
   pl.row_blocks = (int)((nr + pl.rows_per_block - 1) / pl.rows_per_block);
@@ -1463,7 +1476,7 @@ hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, 
                           const PassPlan& pl, hipStream_t s) {
   const dim3 grid(pl.row_blocks, pl.splits, a.nchunks);
   if (gemm) {
-    if (pv_tile8(gemm, nob, vp)) return run_pv_gemm8(a, nkb, pp, vp, grid, s);
+    if (pv_tile8(gemm, nob, vp, half)) return run_pv_gemm8(a, nkb, pp, vp, half, grid, s);
     if (nob == 1) return run_pv_gemm<1>(a, nkb, pp, vp, grid, s);
     if (nob == 2) return run_pv_gemm<2>(a, nkb, pp, vp, grid, s);
     const int wq = a.wrec ? (pp == 3 ? 1 : 2) : 0;
@@ -1495,7 +1508,7 @@ hipError_t launch_pv_main(const PvArgs& a, bool gemm, int nkb, int nob, int pp, 
 
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                      const PassPlan& pl, hipStream_t s) {
-  if (half && gemm && nob < 4) return hipErrorInvalidValue;  // the GEMM-tiled kernels of 1-2 blocks: bf16 parts
+  if (half && gemm && nob == 2) return hipErrorInvalidValue;  // k_pv_gemm: bf16 parts
   // value partials per (slot, row): a single chunk of the register-resident
   // or the 1-2 block GEMM-tiled kernels keeps only the value width (rounded
   // to 8); the wide kernel writes whole chunks

@@ -26,7 +26,7 @@ hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool sc
 // values scaled per column; else bf16 parts.
 void pv_parts(int dtype, bool grad, bool half_kernel, bool precise, int& pp, int& vp, bool& half);
 int pv_nob(bool gemm, int nobt, int vp);  // value blocks per launch chunk
-PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks);
+PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks, bool half);
 hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int vp, bool half,
                      const PassPlan& pl, hipStream_t s);
 // Tangent records of n rows (T n x d float32) for the weighted application:
