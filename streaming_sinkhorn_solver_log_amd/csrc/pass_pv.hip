@@ -1347,9 +1347,10 @@ hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, bool half, int 
 
 template <int NOB>
 hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& grid, hipStream_t s) {
+  // float32 points' applications and gradients of 33-64 values, bf16 points'
+  // applications of up to 64 values (their gradients run on the wide kernel)
   if (pp == 3 && vp == 3) k_pv_gemm<NOB, 3, 3><<<grid, kThreads, 0, s>>>(a, nkb);
   else if (pp == 2 && vp == 2) k_pv_gemm<NOB, 2, 2><<<grid, kThreads, 0, s>>>(a, nkb);
-  else if (pp == 2 && vp == 1) k_pv_gemm<NOB, 2, 1><<<grid, kThreads, 0, s>>>(a, nkb);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
