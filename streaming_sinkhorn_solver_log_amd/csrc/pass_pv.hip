@@ -370,11 +370,65 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
   }
 }
 
+// Shared column stages of the register-resident kernel: the four waves of a
+// workgroup sweep the same columns (each its own rows), so a stage of
+// kPvStageTiles column tiles -- per tile the NKB record blocks, the bias
+// chunk and the NOB x VP x 2 value fragments, 1 KB each, in the lane order
+// of the operands -- is loaded once into LDS by direct global-to-LDS loads
+// (the waves split the blocks) instead of once per wave: with every wave
+// loading its own copy the vector memory path (texture addresser) is the
+// bottleneck at d = 64. Two stages in flight, one barrier per stage.
+constexpr int kPvStageTiles = 4;
+template <int NKB, int NOB, int VP>
+struct PvStage {
+  static constexpr int kValBlocks = NOB * VP * 2;
+  static constexpr int kBlocks = NKB + 1 + kValBlocks;  // per tile
+  static_assert(kPvStageTiles * kBlocks % 4 == 0, "stage blocks split evenly over four waves");
+  bf16x8 blk[2][kPvStageTiles][kBlocks][64];
+};
+
+// This wave's share of stage (first tile t): blocks wave, wave + 4, ... of
+// the stage. Tiles past the sweep's last read the padding or the next range
+// (never used); value lanes past the value width read their half's first
+// lane's fragment, as load_vtile does.
+template <int NKB, int NOB, int VP>
+__device__ __attribute__((always_inline)) inline void pv_issue_stage(
+    PvStage<NKB, NOB, VP>& L, int slot, const PvArgs& p, const unsigned char* __restrict__ cols, int64_t t,
+    int ob0, int wave, int lane) {
+  using Stg = PvStage<NKB, NOB, VP>;
+  constexpr int NB = kPvStageTiles * Stg::kBlocks;
+  const int li = lane & 31, h = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned off_rec = (unsigned)(li * (NKB * 32) + h * (NKB * 16));
+  const unsigned off_bias = (unsigned)(li * 32 + h * 16);
+#pragma unroll
+  for (int q = 0; q < NB / 4; ++q) {
+    const int b = wv + 4 * q;
+    const int tt = b / Stg::kBlocks, kb = b % Stg::kBlocks;
+    const int64_t tile = t + tt;
+    if (kb < NKB) {
+      load_to_lds(cols + tile * 32 * (NKB * 32) + kb * 16, off_rec, &L.blk[slot][tt][kb][0]);
+    } else if (kb == NKB) {
+      load_to_lds(reinterpret_cast<const unsigned char*>(p.bias_col) + tile * 32 * 32, off_bias,
+                  &L.blk[slot][tt][kb][0]);
+    } else {
+      const int v = kb - NKB - 1;  // (ob * VP + vp) * 2 + k
+      const int ob = v / (VP * 2);
+      const int src = (ob0 + ob) * 32 + li < p.kv ? lane : (lane & 32);
+      load_to_lds(vfrag_at(p, tile, ob0 + ob, VP, (v / 2) % VP, v % 2), (unsigned)(src * 16),
+                  &L.blk[slot][tt][kb][0]);
+    }
+  }
+}
+
 // Register-resident rows (record widths up to 8 K blocks): each wave keeps RB
 // blocks of 32 row records and streams column tiles and their value fragments
 // from memory, one tile ahead.
 template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD, bool H>
 __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
+  // shared column stages for records of four K blocks (bf16 d = 33-64) with
+  // tiles of at most 9 blocks (two stages: 72 KB, two workgroups per CU)
+  constexpr bool kShared = NKB == 4 && NKB + 1 + NOB * VP * 2 <= 9;
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
@@ -431,6 +485,41 @@ __global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
 
   const int ntiles = (j1 - j0 + 31) / 32;
   const int64_t t0 = j0 / 32;
+  if constexpr (kShared) {
+    using Stg = PvStage<NKB, NOB, VP>;
+    __shared__ __attribute__((aligned(16))) Stg L;
+    const int nstages = (ntiles + kPvStageTiles - 1) / kPvStageTiles;
+    if (nstages > 0) pv_issue_stage<NKB, NOB, VP>(L, 0, p, cols, t0, ob0, wave, lane);
+    for (int st = 0; st < nstages; ++st) {
+      const int slot = st & 1;
+      wait_vmcnt<0>();  // this wave's loads of stage st
+      __syncthreads();  // everyone's; the other slot (stage st - 1) is free
+      if (st + 1 < nstages)
+        pv_issue_stage<NKB, NOB, VP>(L, slot ^ 1, p, cols, t0 + (st + 1) * kPvStageTiles, ob0, wave, lane);
+      const int nt = min(kPvStageTiles, ntiles - st * kPvStageTiles);
+#pragma unroll
+      for (int tt = 0; tt < kPvStageTiles; ++tt) {
+        if (tt < nt) {
+          ColTile<NKB> ct;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) ct.a[kb] = L.blk[slot][tt][kb][lane];
+          ct.aug = L.blk[slot][tt][NKB][lane];
+          f32x16 acc[RB];
+          tile_mfma<NKB, RB>(ct, B, Baug, acc);
+          VTile<NOB, VP> vt;
+#pragma unroll
+          for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+            for (int vp = 0; vp < VP; ++vp)
+#pragma unroll
+              for (int k = 0; k < 2; ++k) vt.v[ob][vp][k] = L.blk[slot][tt][NKB + 1 + (ob * VP + vp) * 2 + k][lane];
+          entries_work(acc, vt);
+        }
+      }
+    }
+    pv_finish<RB, NOB>(p, true, row_base, O, mu, S, li, half);
+    return;
+  }
   ColTile<NKB> c0, c1;
   VTile<NOB, VP> v0, v1;
   // Each tile is scored, then used; loads run one tile ahead (the loop reads
