@@ -378,12 +378,12 @@ __device__ __attribute__((always_inline)) inline void pv_finish(
 // (the waves split the blocks) instead of once per wave: with every wave
 // loading its own copy the vector memory path (texture addresser) is the
 // bottleneck at d = 64. Two stages in flight, one barrier per stage.
-constexpr int kPvStageTiles = 4;
+constexpr int kPvStageTiles = 2;
 template <int NKB, int NOB, int VP>
 struct PvStage {
   static constexpr int kValBlocks = NOB * VP * 2;
   static constexpr int kBlocks = NKB + 1 + kValBlocks;  // per tile
-  static_assert(kPvStageTiles * kBlocks % 4 == 0, "stage blocks split evenly over four waves");
+
   bf16x8 blk[2][kPvStageTiles][kBlocks][64];
 };
 
@@ -402,8 +402,9 @@ __device__ __attribute__((always_inline)) inline void pv_issue_stage(
   const unsigned off_rec = (unsigned)(li * (NKB * 32) + h * (NKB * 16));
   const unsigned off_bias = (unsigned)(li * 32 + h * 16);
 #pragma unroll
-  for (int q = 0; q < NB / 4; ++q) {
+  for (int q = 0; q < (NB + 3) / 4; ++q) {
     const int b = wv + 4 * q;
+    if (b >= NB) break;  // wave-uniform: the last round has fewer blocks than waves
     const int tt = b / Stg::kBlocks, kb = b % Stg::kBlocks;
     const int64_t tile = t + tt;
     if (kb < NKB) {
@@ -424,11 +425,17 @@ __device__ __attribute__((always_inline)) inline void pv_issue_stage(
 // Register-resident rows (record widths up to 8 K blocks): each wave keeps RB
 // blocks of 32 row records and streams column tiles and their value fragments
 // from memory, one tile ahead.
+// Shared column stages (see PvStage) for records of four K blocks (bf16
+// d = 33-64) with tiles of at most 9 blocks: two stages of two tiles, 36 KB;
+// three workgroups per CU with one value block (168 registers; two value
+// blocks would spill there).
+template <int NKB, int NOB, int VP>
+constexpr bool pv_shared() { return NKB == 4 && NKB + 1 + NOB * VP * 2 <= 9; }
+
 template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD, bool H>
-__global__ __launch_bounds__(kThreads, 2) void k_pv_mfma(const PvArgs p) {
-  // shared column stages for records of four K blocks (bf16 d = 33-64) with
-  // tiles of at most 9 blocks (two stages: 72 KB, two workgroups per CU)
-  constexpr bool kShared = NKB == 4 && NKB + 1 + NOB * VP * 2 <= 9;
+__global__ __launch_bounds__(kThreads, (pv_shared<NKB, NOB, VP>() && NOB == 1 ? 3 : 2)) void k_pv_mfma(
+    const PvArgs p) {
+  constexpr bool kShared = pv_shared<NKB, NOB, VP>();
   constexpr int RSB = NKB * 32;
   constexpr int ROWS = 4 * RB * 32;
   const unsigned char* __restrict__ rows = static_cast<const unsigned char*>(p.rows);
