@@ -383,7 +383,6 @@ template <int NKB, int NOB, int VP>
 struct PvStage {
   static constexpr int kValBlocks = NOB * VP * 2;
   static constexpr int kBlocks = NKB + 1 + kValBlocks;  // per tile
-
   bf16x8 blk[2][kPvStageTiles][kBlocks][64];
 };
 
