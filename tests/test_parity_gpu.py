@@ -623,6 +623,10 @@ APPLY_CASES = [
     (7, 250, 900, 600),  # bf16 d = 512, wide kernel, two value chunks
     (3, 400, 500, 100),  # bf16 d = 64, register-resident kernel over two value chunks
     (1, 200, 333, 97),   # float32 d = 3, widths past 64
+    (3, 300, 500, 1),    # bf16 d = 64, a single value column (float16 form, shared stages)
+    (3, 200, 300, 4096), # bf16 d = 64, the widest application: 64 value chunks
+    (6, 200, 300, 4096), # float32 d = 3, the widest application
+    (7, 100, 200, 4096), # bf16 d = 512, the widest application on the wide kernel
 ]
 
 
