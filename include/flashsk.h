@@ -150,7 +150,7 @@ int sk_sinkhorn_solve_tol(const void* x, const void* y, int dtype, int64_t n, in
  * float32 d <= 21, any d for k > 64, float32 points for k <= 32): bf16
  * points, one float16 per entry
  * (relative error <= 2^-11, inside the 1e-3 bound of bf16 inputs); float32
- * points, two float16 parts per entry (2^-21); in both, two float16 parts of
+ * points, two float16 parts per entry (2^-22); in both, two float16 parts of
  * each value after an exact power-of-two scale per value column (values
  * below 2^-29 of their column's largest magnitude fall into float16's
  * subnormal range). Otherwise (larger d, k <= 64; float32 points with

@@ -31,8 +31,8 @@
 // FlashAttention feeds its probabilities to the second product in 16-bit
 // form, the entries are float16 parts (bf16 points: one part rounded to
 // nearest, 11 significant bits, relative error <= 2^-11, within the 1e-3
-// bound of bf16 inputs; float32 points: two parts, the entry truncated to 11
-// bits and the rounded remainder, 2^-21), and the values are float16 parts
+// bound of bf16 inputs; float32 points: two parts, the entry and its
+// remainder each rounded, 2^-22), and the values are float16 parts
 // (bf16 points: two for applications, one, exact, for the gradient's points;
 // float32 points: two) after an exact power-of-two scale per value column
 // that puts the column's largest magnitude in [2^13, 2^14); products of
@@ -193,11 +193,23 @@ __device__ __attribute__((always_inline)) inline float pv_probs(const f32x16& ac
   return s0 + s1;
 }
 
+// Remainder v - (float)h of an entry and its float16 part h, lane half HI of
+// the packed pair hp: one v_fma_mix_f32 (h * -1 + v with h read as float16
+// from the selected half; exact, as the difference of v and a float16
+// rounding of it). The compiler writes this as a conversion back and a
+// subtraction, and converts v to float16 a second time for them.
+template <int HI>
+__device__ __forceinline__ float half_remainder(unsigned hp, float v) {
+  float r;
+  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hp), "v"(v));
+  else asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hp), "v"(v));
+  return r;
+}
+
 // Half-precision form of pv_probs: the entries (terms < 2^15) as PP float16
-// parts each (v_cvt_pk_f16_f32), and their float32 sum (SUM). One part: the
-// entry rounded to nearest. Two parts: the entry truncated to float16's 11
-// significant bits (exact in float16 in its normal range), then the exact
-// float32 remainder rounded to nearest: relative error <= 2^-21.
+// parts each (v_cvt_pk_f16_f32, rounded to nearest), and their float32 sum
+// (SUM). Two parts: the entry's float16 rounding and the rounded remainder,
+// relative error <= 2^-22.
 template <int PP, bool SUM>
 __device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& acc, float e, float off,
                                                                  f16x8 (&P)[PP][2]) {
@@ -211,17 +223,12 @@ __device__ __attribute__((always_inline)) inline float pv_probs_h(const f32x16& 
       s0 = r == 0 ? v0 : s0 + v0;
       s1 = r == 0 ? v1 : s1 + v1;
     }
-    if constexpr (PP == 1) {
-      const f16x2 h = {(_Float16)v0, (_Float16)v1};
-      P[0][r >> 3][r & 7] = h[0];
-      P[0][r >> 3][(r & 7) + 1] = h[1];
-    } else {
-      const float t0 = __uint_as_float(__float_as_uint(v0) & 0xFFFFE000u);
-      const float t1 = __uint_as_float(__float_as_uint(v1) & 0xFFFFE000u);
-      const f16x2 h = {(_Float16)t0, (_Float16)t1};
-      const f16x2 l = {(_Float16)(v0 - t0), (_Float16)(v1 - t1)};
-      P[0][r >> 3][r & 7] = h[0];
-      P[0][r >> 3][(r & 7) + 1] = h[1];
+    const f16x2 h = {(_Float16)v0, (_Float16)v1};
+    P[0][r >> 3][r & 7] = h[0];
+    P[0][r >> 3][(r & 7) + 1] = h[1];
+    if constexpr (PP == 2) {
+      const unsigned hp = __builtin_bit_cast(unsigned, h);
+      const f16x2 l = {(_Float16)half_remainder<0>(hp, v0), (_Float16)half_remainder<1>(hp, v1)};
       P[1][r >> 3][r & 7] = l[0];
       P[1][r >> 3][(r & 7) + 1] = l[1];
     }
