@@ -1382,8 +1382,8 @@ constexpr int pv_rb(int nkb, int nob, int vp) { return (nkb <= 4 && nob * vp <= 
 // The form, the part counts and the gradient / application choice are
 // template arguments (no branch in the tile loop). Instantiated: the half
 // form's bf16-point application (1, 2) and gradient (1, 1) and float32-point
-// application and gradient (2, 2); the bf16-part form's applications (3, 3)
-// and (2, 2), which the Hessian-vector product's CG uses.
+// application and gradient (2, 2); the bf16-part form's bf16-point
+// application (2, 2), which the Hessian-vector product's CG uses.
 template <int NKB, int RB, int NOB, int PP, int VP, bool GRAD, bool H>
 bool try_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& grid, hipStream_t s) {
   if constexpr (pv_rb(NKB, NOB, VP) != RB) {
@@ -1401,7 +1401,6 @@ hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& g
       try_pv_mfma<NKB, RB, NOB, 1, 1, true, true>(a, pp, vp, half, grid, s) ||
       try_pv_mfma<NKB, RB, NOB, 2, 2, false, true>(a, pp, vp, half, grid, s) ||
       try_pv_mfma<NKB, RB, NOB, 2, 2, true, true>(a, pp, vp, half, grid, s) ||
-      try_pv_mfma<NKB, RB, NOB, 3, 3, false, false>(a, pp, vp, half, grid, s) ||
       try_pv_mfma<NKB, RB, NOB, 2, 2, false, false>(a, pp, vp, half, grid, s))
     return hipGetLastError();
   return hipErrorInvalidValue;
@@ -1409,15 +1408,14 @@ hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& g
 
 hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, bool half, const dim3& grid, hipStream_t s) {
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
-  if (!half && pp == 3 && vp == 3) k_pv_gemm8<3, 3, false><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
-  else if (half && pp == 2 && vp == 2) k_pv_gemm8<2, 2, true><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
+  if (half && pp == 2 && vp == 2) k_pv_gemm8<2, 2, true><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 // Instantiated: the weighted application (bf16 parts); the half form's
 // bf16-point gradient (1, 1) and application (1, 2) and float32-point ones
-// (2, 2); the bf16-part form's (3, 3) and (2, 2) applications (the Hessian-
+// (2, 2); the bf16-part form's bf16-point application (2, 2) (the Hessian-
 // vector product's CG).
 template <int NOBW>
 hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, bool half, int wq, const dim3& grid,
@@ -1440,8 +1438,7 @@ hipError_t run_pv_wide(const PvArgs& a, int nkb, int pp, int vp, bool half, int 
     else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0, true><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
     else return hipErrorInvalidValue;
   } else {
-    if (pp == 3 && vp == 3) k_pv_wide<3, 3, NOBW, 0, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
-    else if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
+    if (pp == 2 && vp == 2) k_pv_wide<2, 2, NOBW, 0, false><<<grid, kThreads, 0, s>>>(a, nkb, col_last);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1460,7 +1457,10 @@ hipError_t run_pv_gemm(const PvArgs& a, int nkb, int pp, int vp, const dim3& gri
 }  // namespace
 
 void pv_parts(int dtype, bool grad, bool half_kernel, bool precise, int& pp, int& vp, bool& half) {
-  half = half_kernel && !precise;
+  // precise: bf16 points keep two bf16 parts (2^-16) rather than one float16
+  // part; float32 points' two float16 parts (2^-22) already match the
+  // three-part bf16 split
+  half = half_kernel && !(precise && dtype != 0);
   if (half) {  // float16 parts
     pp = dtype == 0 ? 2 : 1;
     vp = (dtype != 0 && grad) ? 1 : 2;
@@ -1511,11 +1511,11 @@ int pv_gemm_resident(int nob) {
 }  // namespace
 
 namespace {
-// one value block on the GEMM path: the 8-wave tile for float32 points, in
-// the bf16-part (vp = 3) or the float16 form (bf16 points stay on the
-// 128 x 128 tile: 0.73 ms there at d = 512, n = m = 20k, the same in the
-// float16 form on the 8-wave tile, 1.3 ms in bf16 parts)
-bool pv_tile8(bool gemm, int nob, int vp, bool half) { return gemm && nob == 1 && (vp == 3 || half); }
+// one value block on the GEMM path: the 8-wave tile for float32 points in
+// the float16 form (bf16 points stay on the 128 x 128 tile: 0.73 ms there
+// at d = 512, n = m = 20k, the same in the float16 form on the 8-wave tile,
+// 1.3 ms in bf16 parts)
+bool pv_tile8(bool gemm, int nob, int vp, bool half) { return gemm && nob == 1 && vp == 2 && half; }
 
 // Resident workgroups of the 8-wave GEMM-tiled kernel (per device, computed once).
 int pv_gemm8_resident() {
@@ -1527,7 +1527,7 @@ int pv_gemm8_resident() {
   int v = slot ? slot->load(std::memory_order_relaxed) : 0;
   if (v == 0) {
     int cus = 0, per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm8<3, 3, false>, PvGeo::kNT, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pv_gemm8<2, 2, true>, PvGeo::kNT, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)

@@ -82,9 +82,9 @@ hipError_t launch_marginal_error(const float* w, const float* p0, const float* p
 size_t solve_bytes(int dtype, int64_t n, int64_t m, int64_t d);
 size_t apply_bytes(int dtype, int64_t n, int64_t m, int64_t d, int64_t k, int transpose, bool precise = false);
 // sk_transport_apply with precise = true: bf16 points keep two bf16 parts per
-// plan entry (relative error 2^-16) instead of the one float16 part of the
-// register-resident kernel; for the applications inside the Hessian-vector
-// product's CG, whose Schur system amplifies entry rounding.
+// plan entry (relative error 2^-16) instead of one float16 part; for the
+// applications inside the Hessian-vector product's CG, whose Schur system
+// amplifies entry rounding (float32 points are the same either way).
 // ws: apply_bytes(..., precise).
 int transport_apply(const void* x, const void* y, int dtype, int64_t n, int64_t m, int64_t d, const float* a,
                     const float* b, const float* f, const float* g, double eps, int transpose, const float* V,

@@ -22,8 +22,8 @@ hipError_t launch_lse_gemm(const MfmaPassArgs& a, int nkb, bool shifted, bool sc
                            hipStream_t s);
 // Transport application / gradient kernels. pv_parts: parts of the plan
 // entries (pp) and of the values (vp) for a storage type and operation, and
-// the form: half (a kernel that has it, unless precise) = float16 parts, the
-// values scaled per column; else bf16 parts.
+// the form: half (a kernel that has it, unless precise with bf16 points) =
+// float16 parts, the values scaled per column; else bf16 parts.
 void pv_parts(int dtype, bool grad, bool half_kernel, bool precise, int& pp, int& vp, bool& half);
 int pv_nob(bool gemm, int nobt, int vp);  // value blocks per launch chunk
 PassPlan plan_pv(bool gemm, int64_t nr, int64_t nc, int nkb, int nob, int vp, int nchunks, bool half);
