@@ -1406,6 +1406,11 @@ hipError_t run_pv_mfma(const PvArgs& a, int pp, int vp, bool half, const dim3& g
   return hipErrorInvalidValue;
 }
 
+// Emitted though never launched: without it the compiler allocates
+// k_pv_gemm8<2, 2, true>'s registers differently and spills more in its
+// main loop (P V at n = m = 20k, d = 512 float32: 4.70 -> 5.51 ms).
+template __global__ void k_pv_gemm8<3, 3, false>(const PvArgs, int, int);
+
 hipError_t run_pv_gemm8(const PvArgs& a, int nkb, int pp, int vp, bool half, const dim3& grid, hipStream_t s) {
   const int col_last = (int)(mfma_padded_count(a.nc) - 1);
   if (half && pp == 2 && vp == 2) k_pv_gemm8<2, 2, true><<<grid, PvGeo::kNT, 0, s>>>(a, nkb, col_last);
