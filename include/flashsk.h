@@ -209,7 +209,9 @@ int sk_transport_apply_hadamard(const void* x, const void* y, int dtype, int64_t
  *   cg_max_iters iterations); dP_ij = P_ij (df_i + dg_j - dC_ij)/eps;
  *   out_i = 2 r_i v_i - 2 sum_j dP_ij y_j.
  * At a converged pair this is the Hessian of OT_eps in x applied to V. All
- * plan products are matrix-free applications (O((n + m) d) memory).
+ * plan products are matrix-free applications (O((n + m) d) memory); the
+ * CG's take two bf16 parts per plan entry for bf16 points (2^-16) and, for
+ * float32 points, the float16 form of sk_transport_apply (2^-22).
  *   V, out     n x d float32 (V 16-byte aligned).
  *   cg_iters, cg_resid   out (host): CG iterations and final relative residual.
  * The term (P o dC) Y is one weighted application (each plan entry times

@@ -606,8 +606,9 @@ int sk_ot_hvp_x(const void* x, const void* y, int dtype, int64_t n, int64_t m, i
   if ((rc = check_ws(ws, ws_bytes, L.bytes))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  // the CG's applications keep two bf16 parts per plan entry (bf16 points):
-  // the Schur system amplifies the rounding of a single float16 part
+  // the CG's applications keep two bf16 parts per plan entry for bf16 points
+  // (the Schur system amplifies the rounding of a single float16 part);
+  // float32 points' applications are the plain ones
   auto apply = [&](const float* vals, int64_t k, int transpose, float* o) {
     return transport_apply(x, y, dtype, n, m, d, a, b, f, g, eps, transpose, vals, k, o, L.inner, L.inner_bytes,
                            stream, true);
