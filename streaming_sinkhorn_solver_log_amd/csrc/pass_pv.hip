@@ -1218,13 +1218,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_pv_wide(const PvArgs p, int nkb
 // f_s = 2^(e (M_s - M)), S = sum_s S_s f_s and T = sum_s T_s f_s, then the
 // output as in a single-split launch. cw: value columns per chunk.
 __global__ __launch_bounds__(256) void k_pv_merge(const PvArgs p, int cw) {
+  // four consecutive value columns per thread (cw is a multiple of 8): one
+  // 16-byte partial load per split, the split weights formed once per four
   const int64_t nslots = (int64_t)p.nchunks * p.splits;
   const float2* part_ms = reinterpret_cast<const float2*>(p.part);
   const float* part_t = p.part + ((2 * nslots * p.nr + 3) & ~(int64_t)3);
-  const int64_t total = (int64_t)p.nchunks * p.nr * cw;
+  const int cq = cw >> 2;
+  const int64_t total = (int64_t)p.nchunks * p.nr * cq;
   for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
-    const int c = (int)(q % cw);
-    const int64_t t = q / cw;
+    const int c = (int)(q % cq) * 4;
+    const int64_t t = q / cq;
     const int i = (int)(t % p.nr);
     const int z = (int)(t / p.nr);
     const int cc = z * cw + c;
@@ -1235,16 +1238,23 @@ __global__ __launch_bounds__(256) void k_pv_merge(const PvArgs p, int cw) {
     float Mt = kMuInit;
 #pragma unroll 8
     for (int s2 = 0; s2 < p.splits; ++s2) Mt = fmaxf(Mt, part_ms[s0 + (int64_t)s2 * p.nr].x);
-    float St = 0.0f, Tt = 0.0f;
+    float St = 0.0f;
+    float Tt[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 8
     for (int s2 = 0; s2 < p.splits; ++s2) {
       const int64_t sl = s0 + (int64_t)s2 * p.nr;
       const float2 ms = part_ms[sl];
       const float f = fast_exp2(p.escale * (ms.x - Mt));
       St = fmaf(ms.y, f, St);
-      Tt = fmaf(part_t[sl * cw + c], f, Tt);
+      const float4 v = *reinterpret_cast<const float4*>(part_t + sl * cw + c);
+      Tt[0] = fmaf(v.x, f, Tt[0]);
+      Tt[1] = fmaf(v.y, f, Tt[1]);
+      Tt[2] = fmaf(v.z, f, Tt[2]);
+      Tt[3] = fmaf(v.w, f, Tt[3]);
     }
-    pv_store(p, i, cc, Mt, St, Tt);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (cc + u < p.kv) pv_store(p, i, cc + u, Mt, St, Tt[u]);
   }
 }
 
@@ -1626,7 +1636,7 @@ hipError_t launch_pv(const PvArgs& a, bool gemm, int nkb, int nob, int pp, int v
   b.pcw = (!wide && a.nchunks == 1 && ((a.kv + 7) & ~7) < cw) ? ((a.kv + 7) & ~7) : cw;
   hipError_t e = launch_pv_main(b, gemm, nkb, nob, pp, vp, half, pl, s);
   if (e != hipSuccess || pl.splits == 1) return e;
-  const int64_t total = (int64_t)b.nchunks * b.nr * b.pcw;
+  const int64_t total = (int64_t)b.nchunks * b.nr * (b.pcw / 4);  // four columns per thread
   const int64_t blocks = (total + 255) / 256;
   k_pv_merge<<<(int)(blocks < 16384 ? blocks : 16384), 256, 0, s>>>(b, b.pcw);
   return hipGetLastError();
